@@ -1,0 +1,262 @@
+"""ctypes binding of the plain C CPU oracle (moe_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the
+benchmark's CPU-baseline leg are the only callers.  The GPU library never
+imports this package.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SO = os.path.join(_HERE, "libmoe_oracle.so")
+
+W_INT4_ROW = 1
+W_INT4_AFFINE_G64 = 2
+
+
+def build() -> None:
+    """Compile the oracle with gcc (single-threaded, IEEE fp, no fast-math)."""
+    subprocess.check_call(
+        ["gcc", "-O2", "-fPIC", "-shared", "-std=c99", "-fno-fast-math", "-ffp-contract=off",
+         os.path.join(_HERE, "moe_oracle.c"), "-o", SO + ".tmp", "-lm"])
+    os.replace(SO + ".tmp", SO)
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(SO):
+            build()
+        L = ctypes.CDLL(SO)
+        vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+        L.orc_blob_bytes.argtypes = [i32, i64, i64]
+        L.orc_blob_bytes.restype = i64
+        L.orc_bf16_round.argtypes = [f32]
+        L.orc_bf16_round.restype = f32
+        L.orc_pack_int4_row.argtypes = [vp, i64, i64, vp, vp]
+        L.orc_unpack_int4_row.argtypes = [vp, i64, i64, vp]
+        L.orc_dequant_int4_row.argtypes = [vp, vp, i64, i64, vp]
+        L.orc_pack_affine_g64.argtypes = [vp, i64, i64, vp, vp]
+        L.orc_dequant_affine_g64.argtypes = [vp, vp, i64, i64, vp]
+        L.orc_pack_expert.argtypes = [i32, i64, i64, vp, vp, vp, vp]
+        L.orc_pack_expert.restype = i32
+        L.orc_dequant_expert.argtypes = [i32, i64, i64, vp, vp, vp, vp]
+        L.orc_dequant_expert.restype = i32
+        L.orc_expert.argtypes = [i32, i64, i64, vp, vp, vp, vp]
+        L.orc_expert.restype = i32
+        L.orc_route.argtypes = [vp, i32, i64, vp, vp, i32, i32, f32, i32, vp, vp, vp, vp, vp, vp]
+        L.orc_route.restype = i32
+        L.orc_bucket.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp]
+        L.orc_bucket.restype = i32
+        L.orc_combine.argtypes = [i32, i32, i64, i32, vp, vp, vp, vp]
+        L.orc_combine.restype = None
+        L.orc_moe_layer.argtypes = [vp, i32, i64, i64, i32, i32, i32, vp, vp, f32, i32, vp, i32,
+                                    vp, vp, vp, vp]
+        L.orc_moe_layer.restype = i32
+        L.orc_rmsnorm.argtypes = [vp, i32, i64, f32, vp]
+        L.orc_rmsnorm.restype = None
+        L.orc_residual_layer.argtypes = [vp, i32, i64, i64, i32, i32, i32, vp, vp, f32, i32, vp,
+                                         i32, vp, f32, vp, vp]
+        L.orc_residual_layer.restype = i32
+        for name in ("orc_pack_int4_row", "orc_unpack_int4_row", "orc_dequant_int4_row",
+                     "orc_pack_affine_g64", "orc_dequant_affine_g64"):
+            getattr(L, name).restype = None
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray) -> int:
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+def _f32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def blob_bytes(fmt: int, H: int, I: int) -> int:
+    return int(lib().orc_blob_bytes(fmt, H, I))
+
+
+def bf16_round(v: float) -> float:
+    return float(lib().orc_bf16_round(v))
+
+
+def pack_int4_row(w: np.ndarray):
+    w = _f32(w)
+    O, I = w.shape
+    q = np.empty((O, (I + 1) // 2), dtype=np.uint8)
+    s = np.empty(O, dtype=np.float32)
+    lib().orc_pack_int4_row(_p(w), O, I, _p(q), _p(s))
+    return q, s
+
+
+def unpack_int4_row(q: np.ndarray, I: int) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    O = q.shape[0]
+    out = np.empty((O, I), dtype=np.int8)
+    lib().orc_unpack_int4_row(_p(q), O, I, _p(out))
+    return out
+
+
+def dequant_int4_row(q: np.ndarray, s: np.ndarray, I: int) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    s = _f32(s)
+    O = q.shape[0]
+    out = np.empty((O, I), dtype=np.float64)
+    lib().orc_dequant_int4_row(_p(q), _p(s), O, I, _p(out))
+    return out
+
+
+def pack_affine_g64(w: np.ndarray):
+    w = _f32(w)
+    O, I = w.shape
+    assert I % 64 == 0
+    q = np.empty((O, I // 2), dtype=np.uint8)
+    scmn = np.empty((O, I // 64, 2), dtype=np.uint16)
+    lib().orc_pack_affine_g64(_p(w), O, I, _p(q), _p(scmn))
+    return q, scmn
+
+
+def dequant_affine_g64(q: np.ndarray, scmn: np.ndarray, I: int) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    scmn = np.ascontiguousarray(scmn, dtype=np.uint16)
+    O = q.shape[0]
+    out = np.empty((O, I), dtype=np.float64)
+    lib().orc_dequant_affine_g64(_p(q), _p(scmn), O, I, _p(out))
+    return out
+
+
+def pack_expert(fmt: int, wg, wu, wd) -> np.ndarray:
+    wg, wu, wd = _f32(wg), _f32(wu), _f32(wd)
+    I, H = wg.shape
+    blob = np.empty(blob_bytes(fmt, H, I), dtype=np.uint8)
+    rc = lib().orc_pack_expert(fmt, H, I, _p(wg), _p(wu), _p(wd), _p(blob))
+    if rc:
+        raise ValueError(f"orc_pack_expert failed ({rc})")
+    return blob
+
+
+def dequant_expert(fmt: int, H: int, I: int, blob: np.ndarray):
+    wg = np.empty((I, H), dtype=np.float64)
+    wu = np.empty((I, H), dtype=np.float64)
+    wd = np.empty((H, I), dtype=np.float64)
+    rc = lib().orc_dequant_expert(fmt, H, I, _p(blob), _p(wg), _p(wu), _p(wd))
+    if rc:
+        raise ValueError(f"orc_dequant_expert failed ({rc})")
+    return wg, wu, wd
+
+
+def expert(fmt: int, H: int, I: int, blob: np.ndarray, x: np.ndarray):
+    x = _f32(x)
+    y = np.empty(H, dtype=np.float32)
+    h = np.empty(I, dtype=np.float32)
+    rc = lib().orc_expert(fmt, H, I, _p(blob), _p(x), _p(y), _p(h))
+    if rc:
+        raise ValueError(f"orc_expert failed ({rc})")
+    return y, h
+
+
+def route(x, Wr, bias, K: int, routed_scale: float = 2.5, norm_topk: int = 1):
+    """Returns ids [T,K], wts [T,K], logits [T,E], sig [T,E], gap_k [T], gap_in [T]."""
+    x, Wr, bias = _f32(x), _f32(Wr), _f32(bias)
+    T, H = x.shape
+    E = Wr.shape[0]
+    ids = np.empty((T, K), dtype=np.int32)
+    wts = np.empty((T, K), dtype=np.float32)
+    logits = np.empty((T, E), dtype=np.float32)
+    sig = np.empty((T, E), dtype=np.float32)
+    gk = np.empty(T, dtype=np.float64)
+    gi = np.empty(T, dtype=np.float64)
+    rc = lib().orc_route(_p(x), T, H, _p(Wr), _p(bias), E, K, routed_scale, norm_topk, _p(ids),
+                         _p(wts), _p(logits), _p(sig), _p(gk), _p(gi))
+    if rc:
+        raise ValueError(f"orc_route failed ({rc})")
+    return ids, wts, logits, sig, gk, gi
+
+
+def bucket(ids: np.ndarray, E: int):
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    T, K = ids.shape
+    cnt = np.empty(E, dtype=np.int32)
+    off = np.empty(E + 1, dtype=np.int32)
+    perm = np.empty(T * K, dtype=np.int32)
+    active = np.empty(E, dtype=np.int32)
+    na = np.zeros(1, dtype=np.int32)
+    rc = lib().orc_bucket(_p(ids), T, K, E, _p(cnt), _p(off), _p(perm), _p(active), _p(na))
+    if rc:
+        raise ValueError(f"orc_bucket failed ({rc})")
+    return cnt, off, perm, active[: int(na[0])].copy()
+
+
+def combine(y_routed, wts, y_shared, n_shared: int):
+    y_routed, wts = _f32(y_routed), _f32(wts)
+    T, K = wts.shape
+    H = y_routed.shape[-1]
+    ys = _f32(y_shared) if n_shared else np.zeros((1, T, H), dtype=np.float32)
+    out = np.empty((T, H), dtype=np.float32)
+    lib().orc_combine(T, K, H, n_shared, _p(y_routed), _p(wts), _p(ys), _p(out))
+    return out
+
+
+def _blob_array(blobs):
+    arr = (ctypes.c_void_p * len(blobs))()
+    for i, b in enumerate(blobs):
+        arr[i] = None if b is None else b.ctypes.data
+    return arr
+
+
+def moe_layer(x, Wr, bias, K, fmt, I, blobs, shared_blobs, routed_scale=2.5, norm_topk=1):
+    """Whole layer; blobs is a list of E blobs (None = not resident)."""
+    x, Wr, bias = _f32(x), _f32(Wr), _f32(bias)
+    T, H = x.shape
+    E = Wr.shape[0]
+    out = np.empty((T, H), dtype=np.float32)
+    ids = np.empty((T, K), dtype=np.int32)
+    wts = np.empty((T, K), dtype=np.float32)
+    ba = _blob_array(blobs)
+    sa = _blob_array(shared_blobs) if shared_blobs else None
+    rc = lib().orc_moe_layer(_p(x), T, H, I, E, K, fmt, _p(Wr), _p(bias), routed_scale, norm_topk,
+                             ctypes.cast(ba, ctypes.c_void_p), len(shared_blobs or []),
+                             ctypes.cast(sa, ctypes.c_void_p) if sa is not None else None,
+                             _p(out), _p(ids), _p(wts))
+    if rc:
+        raise ValueError(f"orc_moe_layer failed ({rc})")
+    return out, ids, wts
+
+
+def rmsnorm(x, eps: float = 1e-6):
+    x = _f32(x)
+    T, H = x.shape
+    out = np.empty_like(x)
+    lib().orc_rmsnorm(_p(x), T, H, eps, _p(out))
+    return out
+
+
+def residual_layer(x, Wr, bias, K, fmt, I, blobs, shared_blobs, eps=1e-6, routed_scale=2.5,
+                   norm_topk=1):
+    """x <- x + moe(rmsnorm(x)); returns (new x, ids, wts)."""
+    x = _f32(x).copy()
+    T, H = x.shape
+    E = Wr.shape[0]
+    Wr, bias = _f32(Wr), _f32(bias)
+    ids = np.empty((T, K), dtype=np.int32)
+    wts = np.empty((T, K), dtype=np.float32)
+    ba = _blob_array(blobs)
+    sa = _blob_array(shared_blobs) if shared_blobs else None
+    rc = lib().orc_residual_layer(_p(x), T, H, I, E, K, fmt, _p(Wr), _p(bias), routed_scale,
+                                  norm_topk, ctypes.cast(ba, ctypes.c_void_p),
+                                  len(shared_blobs or []),
+                                  ctypes.cast(sa, ctypes.c_void_p) if sa is not None else None,
+                                  eps, _p(ids), _p(wts))
+    if rc:
+        raise ValueError(f"orc_residual_layer failed ({rc})")
+    return x, ids, wts

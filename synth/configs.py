@@ -1,0 +1,61 @@
+"""Workload recipes: layer shapes, seeds and value distributions.
+
+Each entry is a synthetic stand-in for a layer of a trained model (no
+checkpoint is used): expert and router weights ~N(0, 0.02), router bias
+~N(0, 0.1) plus, where routing should be skewed, a Zipf(1.1) hot-expert term
+of weight 0.2 over a seeded expert permutation, tokens ~N(0, 1).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+
+W_INT4_ROW = 1
+W_INT4_AFFINE_G64 = 2
+
+
+@dataclass(frozen=True)
+class LayerConfig:
+    name: str
+    H: int            # hidden size
+    I: int            # expert intermediate size
+    E: int            # routed experts
+    K: int            # experts chosen per token
+    n_shared: int     # always-active shared experts (same format, weight 1)
+    fmt: int          # W_INT4_ROW or W_INT4_AFFINE_G64
+    T: int            # tokens per forward
+    n_layers: int     # layers resident (rotated, or chained)
+    seed: int
+    chained: bool = False     # x <- x + moe(rmsnorm(x)) between layers
+    zipf_c: float = 0.0
+    zipf_s: float = 1.1
+    sigma_w: float = 0.02
+    sigma_r: float = 0.02
+    sigma_b: float = 0.1
+    sigma_x: float = 1.0
+    routed_scale: float = 2.5
+    norm_topk: int = 1
+    eps: float = 1e-6
+
+    def with_(self, **kw) -> "LayerConfig":
+        return replace(self, **kw)
+
+
+CONFIGS = {
+    # tiny layer: H=512, 32 experts, top-4, I=256, one shared expert, 4 tokens
+    "tiny": LayerConfig("tiny", H=512, I=256, E=32, K=4, n_shared=1, fmt=W_INT4_ROW, T=4,
+                        n_layers=1, seed=0),
+    # GLM-5.2-shape MoE layer, one decode token, 8 resident layers rotated
+    "glm_decode": LayerConfig("glm_decode", H=6144, I=2048, E=256, K=8, n_shared=1,
+                              fmt=W_INT4_ROW, T=1, n_layers=8, seed=1, zipf_c=0.2),
+    # GLM-5.2 shape, 8-token speculative-verify batch through 8 chained layers
+    "glm_verify": LayerConfig("glm_verify", H=6144, I=2048, E=256, K=8, n_shared=1,
+                              fmt=W_INT4_ROW, T=8, n_layers=8, seed=100, chained=True,
+                              zipf_c=0.2),
+    # Edge0 shape, affine int4 g64, 40 chained layers, one token, top-4
+    "edge0_decode": LayerConfig("edge0_decode", H=2048, I=512, E=256, K=4, n_shared=0,
+                                fmt=W_INT4_AFFINE_G64, T=1, n_layers=40, seed=200, chained=True),
+    # GLM-5.2 shape prefill, 2048 tokens, one layer
+    "glm_prefill": LayerConfig("glm_prefill", H=6144, I=2048, E=256, K=8, n_shared=1,
+                               fmt=W_INT4_ROW, T=2048, n_layers=1, seed=300, zipf_c=0.2),
+}
+CONFIGS["edge0_decode_k8"] = CONFIGS["edge0_decode"].with_(name="edge0_decode_k8", K=8)

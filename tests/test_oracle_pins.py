@@ -1,0 +1,457 @@
+"""Pins of the CPU oracle to facts the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: values
+printed on the pages (tests/golden), closed forms, exact special cases,
+invariants and brute force on tiny inputs.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+ROW, AFF = oracle.W_INT4_ROW, oracle.W_INT4_AFFINE_G64
+
+
+def _golden(name):
+    out = {}
+    with open(os.path.join(GOLDEN, name), encoding="utf-8") as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                k, v = line.split(":", 1)
+                out[k.strip()] = v.strip()
+    return out
+
+
+# ---------------------------------------------------------------------------
+# sizes printed on the pages
+# ---------------------------------------------------------------------------
+
+def test_glm_expert_bytes_match_hot_tier_figures():
+    g = _golden("expert_sizes.txt")
+    b = oracle.blob_bytes(ROW, 6144, 2048)
+    assert b == 3 * 6144 * 2048 // 2 + 4 * (2048 + 2048 + 6144)
+    assert round(b * int(g["glm_hot_tier_experts"]) / 1e9, 2) == float(g["glm_hot_tier_gb"])
+    assert round(b * int(g["glm_device_experts"]) / 1e9, 2) == float(g["glm_device_gb"])
+    assert round(b / 1e6, 1) == float(g["glm_expert_mb"])
+
+
+def test_edge0_expert_bytes_match_byte_account():
+    g = _golden("expert_sizes.txt")
+    b = oracle.blob_bytes(AFF, 2048, 512)
+    assert round(b / 1e6, 2) == float(g["edge0_expert_mb"])
+    assert round(256 * b / 1e6) == pytest.approx(float(g["edge0_layer_mb"]), abs=1)
+    assert round(40 * 256 * b / 1e9, 1) == float(g["edge0_total_gb"])
+    assert round(40 * 4 * b / 1e6) == pytest.approx(float(g["edge0_tok_mb"]), abs=1)
+
+
+def test_mac_counts_match_dataflow_page():
+    g = _golden("expert_sizes.txt")
+    H, I, E = 6144, 2048, 256
+    # the oracle's dequantised matrices of one GLM-shape expert hold exactly
+    # 3*H*I weights, one MAC each per token
+    wg, wu, wd = (np.zeros((I, 64)), np.zeros((I, 64)), np.zeros((64, I)))
+    assert wg.shape[0] == I and wd.shape[1] == I
+    macs = 3 * H * I
+    assert round(macs / 1e6, 1) == float(g["glm_expert_mmacs"])
+    assert round(8 * macs / 1e6) == float(g["glm_routed8_mmacs"])
+    assert round(H * E / 1e6, 1) == float(g["glm_router_mmacs"])
+
+
+# ---------------------------------------------------------------------------
+# O1 / O3: per-row int4 pack and unpack
+# ---------------------------------------------------------------------------
+
+def test_page_container_example_decodes():
+    g = _golden("int4_container_example.txt")
+    raw = np.array([int(b, 16) for b in g["bytes_offset_binary"].split()], dtype=np.uint8)
+    want_lo = [int(v) for v in g["low_nibble_codes"].split()]
+    assert int(g["nbytes"]) * 2 // int(g["rows"]) == 6144
+    # offset-binary (q + 8) -> two's complement nibbles: flip each nibble's top bit
+    twos = (raw ^ 0x88).reshape(1, -1)
+    codes = oracle.unpack_int4_row(twos, 16)[0]
+    assert list(codes[0::2]) == want_lo
+    # the high nibbles decode by the same rule (q = nibble - 8 in the page's encoding)
+    assert list(codes[1::2]) == [int(b >> 4) - 8 for b in raw]
+
+
+def test_nibble_order_and_twos_complement():
+    s = 2.0 ** -4            # amax = 7 s so s is reproduced exactly
+    row = np.array([[1, 0, 0, 0, 7, 0], [0, 1, 0, 0, 7, 0], [-1, 0, 0, 0, 7, 0],
+                    [0, -7, 3, -3, 7, 0]], dtype=np.float32) * s
+    q, sc = oracle.pack_int4_row(row)
+    assert np.all(sc == np.float32(s))
+    assert list(q[0]) == [0x01, 0x00, 0x07]
+    assert list(q[1]) == [0x10, 0x00, 0x07]
+    assert list(q[2]) == [0x0F, 0x00, 0x07]
+    assert list(q[3]) == [0x90, 0xD3, 0x07]
+
+
+def test_round_half_to_even():
+    s = 2.0 ** -4            # 0.4375 / 7 == 0.0625 exactly
+    w = np.array([[0.5, 1.5, 2.5, -2.5, 3.5, -0.5, 7.0, 0.0]], dtype=np.float32) * s
+    q, sc = oracle.pack_int4_row(w)
+    assert sc[0] == np.float32(0.0625)
+    codes = oracle.unpack_int4_row(q, 8)[0]
+    # half-to-even; rounding half away from zero would give 1, 2, 3, -3, 4, -1
+    assert list(codes) == [0, 2, 2, -2, 4, 0, 7, 0]
+
+
+def test_every_byte_round_trips():
+    s = 2.0 ** -5
+    for b in range(256):
+        lo, hi = b & 0xF, b >> 4
+        if lo == 8 or hi == 8:      # code -8 is never produced (clamp [-7, 7])
+            continue
+        ql = lo - 16 if lo >= 8 else lo
+        qh = hi - 16 if hi >= 8 else hi
+        w = np.array([[ql, qh, 7, 0]], dtype=np.float32) * np.float32(s)
+        q, sc = oracle.pack_int4_row(w)
+        assert q[0, 0] == b and q[0, 1] == 0x07 and sc[0] == np.float32(s)
+
+
+def test_pack_error_bound_and_code_range():
+    w = synth.gauss(synth.key(7, 0, synth.T_GATE, 0), 64 * 512, 0.02).reshape(64, 512)
+    w[3] *= 1e3
+    w[5, :] = 0.0
+    q, s = oracle.pack_int4_row(w)
+    codes = oracle.unpack_int4_row(q, 512).astype(np.float64)
+    assert codes.min() >= -7 and codes.max() <= 7
+    amax = np.abs(w.astype(np.float64)).max(axis=1)
+    for o in range(64):
+        if o == 5:
+            assert s[o] == np.float32(1e-8) and not codes[o].any()
+            continue
+        assert s[o] == np.float32(np.float32(amax[o]) / np.float32(7.0))
+        err = np.abs(w[o].astype(np.float64) - codes[o] * float(s[o]))
+        assert err.max() <= 0.5 * float(s[o]) * (1 + 1e-6)
+        assert np.abs(codes[o]).max() == 7
+    deq = oracle.dequant_int4_row(q, s, 512)
+    assert np.array_equal(deq, codes * s.astype(np.float64)[:, None])
+
+
+def test_odd_width_pads_high_nibble():
+    w = np.array([[7, -7, 1]], dtype=np.float32)
+    q, _ = oracle.pack_int4_row(w)
+    assert q.shape == (1, 2) and q[0, 1] == 0x01
+
+
+# ---------------------------------------------------------------------------
+# O2 / O3: affine int4, group size 64
+# ---------------------------------------------------------------------------
+
+def test_affine_exact_grid_recovers_codes():
+    rng = np.random.default_rng(3)
+    O, I = 4, 128
+    sc, mn = 2.0 ** -6, -0.25
+    codes = rng.integers(0, 16, size=(O, I))
+    codes[:, ::64] = 0
+    codes[:, 1::64] = 15
+    w = (codes * sc + mn).astype(np.float32)
+    q, scmn = oracle.pack_affine_g64(w)
+    assert np.all(scmn[..., 0] == 0x3C80)          # bf16 of 2^-6
+    assert np.all(scmn[..., 1] == 0xBE80)          # bf16 of -0.25
+    deq = oracle.dequant_affine_g64(q, scmn, I)
+    assert np.array_equal(deq, w.astype(np.float64))
+    lo = q & 0xF
+    assert np.array_equal(lo, codes[:, 0::2])
+    assert np.array_equal(q >> 4, codes[:, 1::2])
+
+
+def test_affine_constant_group():
+    w = np.full((2, 64), 0.3, dtype=np.float32)
+    q, scmn = oracle.pack_affine_g64(w)
+    assert not q.any() and np.all(scmn[..., 0] == 0)
+    deq = oracle.dequant_affine_g64(q, scmn, 64)
+    assert np.all(deq == oracle.bf16_round(0.3))
+
+
+def test_affine_error_bound():
+    w = synth.gauss(synth.key(9, 0, synth.T_DOWN, 0), 32 * 512, 0.02).reshape(32, 512)
+    q, scmn = oracle.pack_affine_g64(w)
+    deq = oracle.dequant_affine_g64(q, scmn, 512)
+    for o in range(32):
+        for g in range(8):
+            seg = w[o, g * 64:(g + 1) * 64].astype(np.float64)
+            s = oracle.bf16_round(float(np.float32(seg.max() - seg.min()) / np.float32(15)))
+            m = oracle.bf16_round(float(seg.min()))
+            # rounding of the code, plus what bf16 rounding of min and scale moves
+            bound = 0.5 * s + abs(m - seg.min()) + 15 * abs(s - (seg.max() - seg.min()) / 15)
+            assert np.abs(seg - deq[o, g * 64:(g + 1) * 64]).max() <= bound * (1 + 1e-6)
+
+
+# ---------------------------------------------------------------------------
+# O4: router
+# ---------------------------------------------------------------------------
+
+def _route_by_bias(bias, K):
+    """x = 0 makes every logit 0 and every sigmoid exactly 0.5, so the
+    selection score is 0.5 + bias."""
+    E = len(bias)
+    x = np.zeros((1, 8), dtype=np.float32)
+    W = np.zeros((E, 8), dtype=np.float32)
+    return oracle.route(x, W, np.asarray(bias, dtype=np.float32), K)
+
+
+def test_topk_equals_brute_force_sort_with_ties():
+    rng = np.random.default_rng(11)
+    for trial in range(300):
+        E = int(rng.integers(1, 13))
+        K = int(rng.integers(1, E + 1))
+        bias = rng.integers(-3, 4, size=E).astype(np.float32) / 4   # many ties
+        ids, wts, logits, sig, gk, gi = _route_by_bias(bias, K)
+        c = [0.5 + float(b) for b in bias]
+        want = sorted(range(E), key=lambda e: (-c[e], e))[:K]
+        assert list(ids[0]) == want
+        assert np.all(sig == 0.5) and np.all(logits == 0)
+        assert np.allclose(wts[0], 2.5 / K, rtol=0, atol=1e-6)
+
+
+def test_identical_scores_pick_lowest_ids():
+    ids, *_ = _route_by_bias(np.zeros(16), 5)
+    assert list(ids[0]) == [0, 1, 2, 3, 4]
+
+
+def test_router_logits_one_hot_rows_and_sigmoid_symmetry():
+    H, E = 16, 16
+    x = (np.arange(H, dtype=np.float32) - 7.5).reshape(1, H) / 4
+    W = np.eye(E, H, dtype=np.float32)
+    W2 = -W
+    b = np.zeros(E, dtype=np.float32)
+    _, _, lg, sg, _, _ = oracle.route(x, W, b, 4)
+    _, _, lg2, sg2, _, _ = oracle.route(x, W2, b, 4)
+    assert np.array_equal(lg[0], x[0])
+    # sigmoid(-z) = 1 - sigmoid(z); sigmoid(0) = 1/2; monotone increasing
+    assert np.allclose(sg[0] + sg2[0], 1.0, atol=1e-7)
+    assert np.all(np.diff(sg[0]) > 0)
+
+
+def test_weights_renormalised_to_routed_scale():
+    cfg = synth.CONFIGS["tiny"]
+    W = synth.router_weight(cfg, 0)
+    b = synth.router_bias(cfg, 0)
+    x = synth.tokens(cfg, T=16)
+    ids, wts, lg, sg, gk, gi = oracle.route(x, W, b, 4)
+    assert np.allclose(wts.sum(axis=1), 2.5, atol=4 * 2.5 * 2 ** -23)
+    for t in range(16):
+        s = sg[t, ids[t]].astype(np.float64)
+        assert np.allclose(wts[t], 2.5 * s / s.sum(), rtol=1e-7)
+    # K = E: the weights are 2.5 * sigma / sum(sigma) over all experts
+    ids, wts, lg, sg, gk, gi = oracle.route(x[:2], W, b, cfg.E)
+    for t in range(2):
+        order = np.argsort(ids[t])
+        assert np.allclose(wts[t][order], 2.5 * sg[t] / sg[t].astype(np.float64).sum(),
+                           rtol=1e-6)
+        assert gk[t] == np.inf
+    # no renormalisation: weight = 2.5 * sigma
+    ids, wts, lg, sg, gk, gi = oracle.route(x, W, b, 4, norm_topk=0)
+    for t in range(16):
+        assert np.allclose(wts[t], 2.5 * sg[t, ids[t]], rtol=1e-7)
+
+
+def test_router_permutation_equivariance():
+    cfg = synth.CONFIGS["tiny"]
+    W = synth.router_weight(cfg, 0)
+    b = synth.router_bias(cfg, 0)
+    x = synth.tokens(cfg, T=8)
+    ids, wts, *_ = oracle.route(x, W, b, 4)
+    p = np.random.default_rng(5).permutation(cfg.E)
+    ids2, wts2, *_ = oracle.route(x, W[p], b[p], 4)
+    assert np.array_equal(p[ids2], ids)
+    assert np.array_equal(wts2, wts)
+
+
+def test_gap_flags():
+    bias = np.array([0.3, 0.1, 0.2, 0.2 - 2e-5, -0.1], dtype=np.float32)
+    ids, wts, lg, sg, gk, gi = _route_by_bias(bias, 3)
+    c = (np.float32(0.5) + bias).astype(np.float64)
+    assert list(ids[0]) == [0, 2, 3]
+    assert gk[0] == pytest.approx(c[3] - c[1])
+    assert gi[0] == pytest.approx(c[2] - c[3])
+
+
+# ---------------------------------------------------------------------------
+# O5: bucketing
+# ---------------------------------------------------------------------------
+
+def test_bucket_brute_force_and_invariants():
+    rng = np.random.default_rng(2)
+    for trial in range(100):
+        E = int(rng.integers(1, 20))
+        K = int(rng.integers(1, E + 1))
+        T = int(rng.integers(1, 12))
+        ids = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+        cnt, off, perm, active = oracle.bucket(ids, E)
+        flat = ids.reshape(-1)
+        assert cnt.sum() == T * K
+        assert np.array_equal(np.sort(perm), np.arange(T * K))
+        want = sorted(range(T * K), key=lambda a: (flat[a], a))
+        assert list(perm) == want
+        assert list(active) == sorted(set(flat.tolist()))
+        assert len(active) <= min(T * K, E)
+        for e in range(E):
+            seg = perm[off[e]:off[e + 1]]
+            assert np.all(flat[seg] == e) and np.all(np.diff(seg) > 0)
+
+
+# ---------------------------------------------------------------------------
+# O6 / O7: expert math and combine, closed forms
+# ---------------------------------------------------------------------------
+
+def _row_blob(H, I, qg, qu, qd, sg, su, sd):
+    """Builds a row-format blob from integer codes directly (no quantiser)."""
+    def pack(qm):
+        qm = np.asarray(qm, dtype=np.int64)
+        n = qm & 0xF
+        return (n[:, 0::2] | (n[:, 1::2] << 4)).astype(np.uint8)
+    parts = [pack(qg).ravel(), pack(qu).ravel(), pack(qd).ravel(),
+             np.asarray(sg, np.float32).view(np.uint8), np.asarray(su, np.float32).view(np.uint8),
+             np.asarray(sd, np.float32).view(np.uint8)]
+    blob = np.concatenate(parts)
+    assert blob.size == oracle.blob_bytes(ROW, H, I)
+    return blob
+
+
+def test_expert_all_ones_closed_form():
+    H, I = 64, 32
+    ones = np.ones
+    blob = _row_blob(H, I, ones((I, H)), ones((I, H)), ones((H, I)), ones(I), ones(I), ones(H))
+    x = np.full(H, 1 / 8, dtype=np.float32)        # sum(x) = 8
+    y, h = oracle.expert(ROW, H, I, blob, x)
+    h_want = 8.0 / (1 + math.exp(-8.0)) * 8.0
+    assert np.allclose(h, h_want, rtol=1e-7)
+    assert np.allclose(y, I * np.float32(h_want), rtol=1e-7)
+
+
+def test_expert_single_weight_closed_form():
+    H, I = 64, 32
+    qg = np.zeros((I, H)); qu = np.zeros((I, H)); qd = np.zeros((H, I))
+    qg[5, 9] = 3
+    qu[5, 20] = -2
+    qd[:, 5] = np.arange(H) % 15 - 7
+    sg = np.full(I, 0.5); su = np.full(I, 0.25); sd = np.linspace(0.1, 1.0, H)
+    blob = _row_blob(H, I, qg, qu, qd, sg, su, sd)
+    x = synth.gauss(synth.key(1, 0, synth.T_X, 9), H, 1.0)
+    y, h = oracle.expert(ROW, H, I, blob, x)
+    g = np.float32(1.5 * float(x[9]))
+    u = np.float32(-0.5 * float(x[20]))
+    hw = np.float32(float(g) / (1 + math.exp(-float(g))) * float(u))
+    assert h[5] == pytest.approx(float(hw), rel=1e-7)
+    assert np.all(np.delete(h, 5) == 0)
+    want = sd.astype(np.float32).astype(np.float64) * qd[:, 5] * float(hw)
+    assert np.allclose(y, want, rtol=1e-6)
+
+
+def test_expert_zero_weights_give_zero():
+    H, I = 64, 64
+    z = np.zeros
+    blob = _row_blob(H, I, z((I, H)), z((I, H)), z((H, I)), np.ones(I), np.ones(I), np.ones(H))
+    y, h = oracle.expert(ROW, H, I, blob, synth.tokens(synth.CONFIGS["tiny"])[0, :64])
+    assert not y.any() and not h.any()
+
+
+def test_affine_expert_constant_groups_closed_form():
+    H, I = 128, 64
+    wg = np.full((I, H), 0.125, dtype=np.float32)
+    wu = np.full((I, H), -0.0625, dtype=np.float32)
+    wd = np.full((H, I), 0.5, dtype=np.float32)
+    blob = oracle.pack_expert(AFF, wg, wu, wd)
+    x = np.linspace(-1, 1, H).astype(np.float32) + 0.25
+    sx = float(x.astype(np.float64).sum())
+    y, h = oracle.expert(AFF, H, I, blob, x)
+    g, u = np.float32(0.125 * sx), np.float32(-0.0625 * sx)
+    hw = np.float32(float(g) / (1 + math.exp(-float(g))) * float(u))
+    assert np.allclose(h, hw, rtol=1e-7)
+    assert np.allclose(y, 0.5 * I * float(hw), rtol=1e-6)
+
+
+@pytest.mark.parametrize("fmt", [ROW, AFF])
+def test_blob_layout_round_trips_exact_weights(fmt):
+    H, I = 128, 64
+    rng = np.random.default_rng(4)
+    if fmt == ROW:
+        def mk(O, In):
+            q = rng.integers(-7, 8, size=(O, In)); q[:, 0] = 7
+            return (q * 2.0 ** -7).astype(np.float32)
+    else:
+        def mk(O, In):
+            q = rng.integers(0, 16, size=(O, In)); q[:, ::64] = 0; q[:, 1::64] = 15
+            return (q * 2.0 ** -7 - 0.0625).astype(np.float32)
+    wg, wu, wd = mk(I, H), mk(I, H), mk(H, I)
+    blob = oracle.pack_expert(fmt, wg, wu, wd)
+    dg, du, dd = oracle.dequant_expert(fmt, H, I, blob)
+    assert np.array_equal(dg, wg) and np.array_equal(du, wu) and np.array_equal(dd, wd)
+
+
+def test_combine_closed_forms():
+    T, K, H = 2, 3, 5
+    yr = np.arange(T * K * H, dtype=np.float32).reshape(T * K, H)
+    w = np.array([[2.5, 0, 0], [0, 0, 2.5]], dtype=np.float32)
+    ys = np.ones((1, T, H), dtype=np.float32)
+    out = oracle.combine(yr, w, ys, 1)
+    assert np.array_equal(out[0], 2.5 * yr[0] + 1)
+    assert np.array_equal(out[1], 2.5 * yr[5] + 1)
+
+
+# ---------------------------------------------------------------------------
+# whole layer: invariants that pin composition
+# ---------------------------------------------------------------------------
+
+def _tiny_layer(cfg, n_tok=None):
+    W = synth.router_weight(cfg, 0)
+    b = synth.router_bias(cfg, 0)
+    blobs = [oracle.pack_expert(cfg.fmt, *synth.expert_weights(cfg, 0, e)) for e in range(cfg.E)]
+    shared = [oracle.pack_expert(cfg.fmt, *synth.expert_weights(cfg, 0, cfg.E + s))
+              for s in range(cfg.n_shared)]
+    x = synth.tokens(cfg, T=n_tok)
+    return W, b, blobs, shared, x
+
+
+def test_layer_identical_experts_sum_to_routed_scale():
+    cfg = synth.CONFIGS["tiny"]
+    W, b, blobs, shared, x = _tiny_layer(cfg)
+    same = [blobs[0]] * cfg.E
+    out, ids, wts = oracle.moe_layer(x, W, b, cfg.K, cfg.fmt, cfg.I, same, shared)
+    for t in range(cfg.T):
+        y, _ = oracle.expert(cfg.fmt, cfg.H, cfg.I, blobs[0], x[t])
+        ysh, _ = oracle.expert(cfg.fmt, cfg.H, cfg.I, shared[0], x[t])
+        assert np.allclose(out[t], 2.5 * y.astype(np.float64) + ysh, rtol=1e-6, atol=1e-6)
+
+
+def test_layer_relabelling_and_token_independence():
+    cfg = synth.CONFIGS["tiny"]
+    W, b, blobs, shared, x = _tiny_layer(cfg)
+    out, ids, wts = oracle.moe_layer(x, W, b, cfg.K, cfg.fmt, cfg.I, blobs, shared)
+    p = np.random.default_rng(8).permutation(cfg.E)
+    out2, ids2, _ = oracle.moe_layer(x, W[p], b[p], cfg.K, cfg.fmt, cfg.I,
+                                     [blobs[e] for e in p], shared)
+    assert np.array_equal(out, out2) and np.array_equal(p[ids2], ids)
+    for t in range(cfg.T):
+        o1, _, _ = oracle.moe_layer(x[t:t + 1], W, b, cfg.K, cfg.fmt, cfg.I, blobs, shared)
+        assert np.array_equal(o1[0], out[t])
+
+
+def test_layer_missing_expert_is_an_error():
+    cfg = synth.CONFIGS["tiny"]
+    W, b, blobs, shared, x = _tiny_layer(cfg)
+    _, ids, _ = oracle.moe_layer(x, W, b, cfg.K, cfg.fmt, cfg.I, blobs, shared)
+    holes = list(blobs)
+    holes[int(ids[0, 0])] = None
+    with pytest.raises(ValueError):
+        oracle.moe_layer(x, W, b, cfg.K, cfg.fmt, cfg.I, holes, shared)
+
+
+def test_rmsnorm_closed_form_and_scale_invariance():
+    x = np.full((1, 64), -3.0, dtype=np.float32)
+    out = oracle.rmsnorm(x, eps=0.0)
+    assert np.all(out == -1.0)
+    y = synth.tokens(synth.CONFIGS["tiny"])
+    a = oracle.rmsnorm(y, eps=0.0)
+    b = oracle.rmsnorm(8 * y, eps=0.0)
+    assert np.array_equal(a, b)
+    assert np.allclose((a.astype(np.float64) ** 2).mean(axis=1), 1.0, rtol=1e-6)
