@@ -1,0 +1,210 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) int4-weight MoE FFN library.
+ *
+ * The library computes one MoE FFN step of a GLM-5.2-style decoder layer:
+ *   router:   logits = x . Wr^T (fp32), sigma = 1/(1+exp(-logits)),
+ *             choose top-K experts by sigma + bias (equal scores: lower id),
+ *             w_k = routed_scale * sigma_k / (sum_j sigma_j + 1e-20)
+ *   experts:  y_e(x) = Wd_e (silu(Wg_e x) * (Wu_e x)), weights int4
+ *   combine:  out = sum_s shared_s(x) + sum_k w_k y_{id_k}(x)
+ * Sources, cited by page title and section:
+ *   [GLM-C] "惊呆了！25GB 内存上运行 GLM 5.2 744B 模型" (reader.mx) §11 (routing
+ *           and expert execution: sigmoid + correction bias picks, the plain
+ *           sigmoid weighs; batch expert union; SwiGLU on gathered rows),
+ *           §06 (int4 pack: per-row absmax scale, two codes per byte, first
+ *           code in the low nibble), §13 (one contiguous g|u|d slab per
+ *           expert, a GPU hot tier of resident experts);
+ *   [FLOW]  GLM-5.2 dataflow page (devpress.csdn.net) §三 Step 6 (6a router
+ *           6144->256 top-8, 6b SwiGLU experts 6144->2048->6144, 6c the
+ *           always-active shared expert, 6d output = routed sum + shared);
+ *   [COLI]  "初始化与权重加载" (colibrì analysis) §1.1-1.2 (n_group,
+ *           topk_group, norm_topk, routed_scale; n_group must be 1), §2.2
+ *           (ESlot: an expert slot addressed by expert id);
+ *   [EDGE0] Edge0 write-up (magicnetworld.com) §三 (affine int4, group size
+ *           64), §七 (sigmoid-group weights with the 1e-20 term), §十四
+ *           (routing indices mapped through a slot table on the device).
+ *
+ * Conventions for every entry point:
+ *   - return MOE_OK (0) or a negative MOE_E_* code; nothing calls exit();
+ *   - argument, size and range checks are synchronous and leave no work
+ *     enqueued when they fail;
+ *   - "device pointer" means memory the HIP runtime can address from the
+ *     context's device (hipMalloc or a torch CUDA tensor's data_ptr());
+ *     "host or device pointer" accepts either (copied with hipMemcpyDefault);
+ *   - all GPU work is enqueued on the context's stream (see moe_set_stream)
+ *     and is asynchronous unless stated otherwise;
+ *   - a context is used by one host thread at a time (not thread-safe).
+ * There is no CPU fallback: without a gfx950 device, moe_layer_create
+ * fails with MOE_E_HIP.
+ */
+#ifndef MOE_INT4_H
+#define MOE_INT4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct moe_ctx moe_ctx;
+
+/* status codes */
+#define MOE_OK 0
+#define MOE_E_ARG (-1)          /* bad argument: null, range, aliasing */
+#define MOE_E_NOMEM (-2)        /* device allocation failed */
+#define MOE_E_SIZE (-3)         /* blob size differs from moe_expert_bytes() */
+#define MOE_E_SLOT (-4)         /* slot index out of range */
+#define MOE_E_NOT_RESIDENT (-5) /* a selected expert had no slot (moe_status) */
+#define MOE_E_HIP (-6)          /* a HIP runtime call failed */
+#define MOE_E_UNSUPPORTED (-7)  /* configuration outside what the kernels do */
+#define MOE_E_RANGE (-8)        /* fp16 activation overflow on the GEMM path (moe_status) */
+
+/* expert weight formats (layout of an expert blob, see moe_load_expert) */
+#define MOE_W_INT4_ROW 1        /* symmetric int4, one fp32 scale per output row */
+#define MOE_W_INT4_AFFINE_G64 2 /* affine int4, bf16 scale and min per 64 inputs */
+
+typedef struct moe_config {
+    int hidden;         /* H, multiple of 64 */
+    int inter;          /* I, multiple of 64 */
+    int n_experts;      /* E, 1..256 routed experts */
+    int top_k;          /* K, 1..min(8, E) */
+    int n_shared;       /* 0 or 1 always-active shared experts (weight 1) */
+    int n_layers;       /* layers whose router/shared/slot table are held */
+    int wfmt;           /* MOE_W_INT4_ROW or MOE_W_INT4_AFFINE_G64 */
+    int n_group;        /* expert groups of the router: must be 1 ([COLI] §1.2) */
+    int topk_group;     /* groups kept: must be 1 */
+    float routed_scale; /* routed scaling factor (GLM-5.2: 2.5) */
+    int norm_topk;      /* 1: renormalise chosen sigmas before scaling ([EDGE0] §七) */
+    int n_slots;        /* expert slots in the HBM pool */
+    int max_tokens;     /* largest T passed to moe_forward / moe_route */
+    float rms_eps;      /* eps of the RMSNorm used by moe_forward_residual */
+} moe_config;
+
+/* Creates a context on the current HIP device: allocates the slot pool
+ * (n_slots * moe_expert_bytes), per-layer router weights, bias, shared
+ * experts and slot table (all entries -1 = not resident), and a workspace
+ * sized for max_tokens.  stream: a hipStream_t (NULL = default stream).
+ * Errors: MOE_E_ARG (null/invalid field), MOE_E_UNSUPPORTED (n_group or
+ * topk_group != 1, E > 256, K > 8, H or I not a multiple of 64),
+ * MOE_E_NOMEM, MOE_E_HIP (no device or not gfx950). */
+int moe_layer_create(const moe_config *cfg, void *stream, moe_ctx **out);
+
+/* Frees every allocation of the context (synchronises its stream first). */
+void moe_destroy(moe_ctx *ctx);
+
+/* Changes the stream later calls enqueue on. */
+int moe_set_stream(moe_ctx *ctx, void *stream);
+
+/* Bytes of one expert blob for the context's format and shape:
+ *   MOE_W_INT4_ROW:        3*H*I/2 + 4*(2I + H)    (GLM 6144/2048: 18,915,328)
+ *   MOE_W_INT4_AFFINE_G64: 3*H*I/2 + 12*H*I/64     (Edge0 2048/512: 1,769,472)
+ * Returns 0 for a null context. */
+size_t moe_expert_bytes(const moe_ctx *ctx);
+
+/* Sets layer's router: W [E][H] fp32 row-major, bias [E] fp32; host or
+ * device pointers.  Synchronous: returns after the data is copied in.
+ * Errors: MOE_E_ARG (null, layer out of range). */
+int moe_set_router(moe_ctx *ctx, int layer, const float *W, const float *bias);
+
+/* Copies one expert blob (host or device pointer, nbytes ==
+ * moe_expert_bytes) into a pool slot ([GLM-C] §13 contiguous slab).
+ * Blob layout, little-endian, row-major, output rows:
+ *   MOE_W_INT4_ROW:  Qg[I][H/2] Qu[I][H/2] Qd[H][I/2] sg[I] su[I] sd[H]
+ *     Q bytes hold two's-complement codes in [-7, 7]; column 2j in the low
+ *     nibble of byte j, column 2j+1 in the high nibble; s fp32 row scales;
+ *     weight = code * s.
+ *   MOE_W_INT4_AFFINE_G64: Qg Qu Qd (as above, unsigned codes 0..15), then
+ *     Ag[I][H/64][2] Au[I][H/64][2] Ad[H][I/64][2] bf16 pairs (scale, min);
+ *     weight = code * scale + min for the group of 64 inputs it falls in.
+ * The slot keeps the bytes in the library's own order (64-row interleave);
+ * moe_read_slot gives the blob back.  Synchronous.  Does not map the slot.
+ * Errors: MOE_E_SLOT, MOE_E_SIZE, MOE_E_ARG, MOE_E_HIP. */
+int moe_load_expert(moe_ctx *ctx, int slot, const void *blob, size_t nbytes);
+
+/* Quantises and packs fp32 weights already in device memory straight into
+ * a slot: Wg [I][H], Wu [I][H], Wd [H][I] row-major device pointers.  Same
+ * quantiser as moe_pack_int4_rows / moe_pack_affine_g64.  Asynchronous. */
+int moe_pack_expert(moe_ctx *ctx, int slot, const float *Wg, const float *Wu, const float *Wd);
+
+/* Shared expert s of a layer, from a blob (host or device; synchronous) or
+ * from device fp32 weights (asynchronous).  Errors: MOE_E_ARG, MOE_E_SIZE. */
+int moe_set_shared(moe_ctx *ctx, int layer, int s, const void *blob, size_t nbytes);
+int moe_pack_shared(moe_ctx *ctx, int layer, int s, const float *Wg, const float *Wu,
+                    const float *Wd);
+
+/* Points (layer, expert_id) at a slot, or unmaps it with slot = -1
+ * ([COLI] §2.2 ESlot, [EDGE0] §十四 slot table).  Several layers or ids may
+ * share a slot.  Errors: MOE_E_ARG, MOE_E_SLOT. */
+int moe_map_expert(moe_ctx *ctx, int layer, int expert_id, int slot);
+
+/* Copies a slot back out in blob layout to dst (host or device pointer).
+ * Synchronous.  Errors: MOE_E_SLOT, MOE_E_SIZE, MOE_E_ARG. */
+int moe_read_slot(moe_ctx *ctx, int slot, void *dst, size_t nbytes);
+
+/* The MoE step: out[T][H] = moe(x[T][H]) for the given layer ([GLM-C] §11
+ * moe(); [FLOW] Step 6).  x, out: device pointers to fp32 row-major
+ * arrays that must not overlap; out is fully overwritten.  1 <= T <=
+ * max_tokens.  A selected expert whose slot entry is -1 contributes zero
+ * and is reported by moe_status.  Deterministic: the same inputs give
+ * bitwise the same outputs.  Errors: MOE_E_ARG. */
+int moe_forward(moe_ctx *ctx, const float *x, int T, int layer, float *out);
+
+/* One chained layer in place: x <- x + moe(rmsnorm(x)), unit-weight
+ * RMSNorm with eps = rms_eps ([GLM-C] §04 rmsnorm and layer order).
+ * x: device pointer [T][H].  Errors: MOE_E_ARG. */
+int moe_forward_residual(moe_ctx *ctx, float *x, int T, int layer);
+
+/* Router only: ids [T][K] int32 (descending score), w [T][K] fp32, device
+ * pointers.  Errors: MOE_E_ARG. */
+int moe_route(moe_ctx *ctx, const float *x, int T, int layer, int32_t *ids, float *w);
+
+/* Synchronises the stream and reports errors found on the device since the
+ * last call: MOE_E_NOT_RESIDENT (then up to cap missing (layer*E + id)
+ * codes go to missing_ids, *n_missing = their count), MOE_E_RANGE, or
+ * MOE_OK.  Clears the device status.  missing_ids/n_missing may be null. */
+int moe_status(moe_ctx *ctx, int32_t *missing_ids, int cap, int *n_missing);
+
+/* Which path moe_forward takes: tokens at or above this count use the MFMA
+ * grouped GEMM (row format only), below it the int4 GEMV kernels.
+ * Default 64.  0 restores the default. */
+int moe_set_gemm_min_tokens(moe_ctx *ctx, int min_tokens);
+
+/* Duration in milliseconds of the kernels of the last moe_forward (or
+ * moe_forward_residual, moe_route), measured with HIP events on the
+ * context's stream when timing is on.  Synchronises.  ms[i] receives
+ * kernel i's duration in launch order; *n receives the kernel count and
+ * names[i] (optional) a static string naming it.  Timing adds events
+ * between kernels; leave it off for production.  Errors: MOE_E_ARG. */
+int moe_set_timing(moe_ctx *ctx, int on);
+int moe_last_timings(moe_ctx *ctx, float *ms, const char **names, int cap, int *n);
+
+/* --- stand-alone steps, for callers that quantise or bucket themselves --- */
+
+/* Per-row symmetric int4 pack ([GLM-C] §05 quantize_rows, §06 pack_int4):
+ * s[o] = max(max_i |w[o][i]| / 7, 1e-8); code = rint(w / s) clamped to
+ * [-7, 7] (round half to even, fp32 division); q [O][I/2] in the blob's
+ * nibble order.  w, q, s: device pointers; I even.  Asynchronous on
+ * stream (hipStream_t).  Errors: MOE_E_ARG, MOE_E_HIP. */
+int moe_pack_int4_rows(const float *w, int64_t O, int64_t I, uint8_t *q, float *s, void *stream);
+
+/* Affine g64 pack ([EDGE0] §三): per row and group of 64 inputs, scale =
+ * bf16((max - min) / 15), min = bf16(min), code = rint((w - min) / scale)
+ * clamped to [0, 15] (0 when scale is 0); q [O][I/2], scmn [O][I/64][2]
+ * bf16 (scale, min).  Device pointers; I a multiple of 64. */
+int moe_pack_affine_g64(const float *w, int64_t O, int64_t I, uint8_t *q, uint16_t *scmn,
+                        void *stream);
+
+/* Token -> expert bucketing of ids [T][K] (device) ([GLM-C] §11 batch
+ * expert union): cnt [E], off [E+1] (exclusive scan), perm [T*K] =
+ * assignment indices t*K+k in a stable sort by expert id, active [E] =
+ * ids with cnt > 0 ascending and n_active [1].  Device pointers.
+ * T*K <= 65536.  Errors: MOE_E_ARG. */
+int moe_bucket(const int32_t *ids, int T, int K, int E, int32_t *cnt, int32_t *off,
+               int32_t *perm, int32_t *active, int32_t *n_active, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_INT4_H */

@@ -1,0 +1,341 @@
+// k_large.hip -- router and bucketing for large token counts (prefill):
+// per-token statistics, an fp32 router GEMM, one-wavefront-per-token top-K,
+// and a single-workgroup stable counting sort of the T*K assignments.
+//
+// Cited by page title and section: "惊呆了！25GB 内存上运行 GLM 5.2 744B 模型"
+// (reader.mx) §11 (sigmoid + bias picks, plain sigmoid weighs, strict
+// greater-than scan so equal scores go to the lower id; the batch expert
+// union that reads each expert once); Edge0 write-up §七 (renormalised
+// weights with the 1e-20 term); "初始化与权重加载" (colibrì analysis) §1.2
+// (a single expert group: n_group == 1).
+#include "moe_internal.h"
+
+namespace moe {
+
+__device__ __forceinline__ float wsum(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+__device__ __forceinline__ uint32_t ordf(float c)
+{
+    uint32_t u = __float_as_uint(c);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Per-token sum, RMSNorm factor and sums of 64-column groups; one
+// wavefront per token.  H must be a multiple of 256.
+__global__ void __launch_bounds__(256) k_tokstats(Fwd f)
+{
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= f.T) return;
+    const int H = f.H;
+    const float* xt = f.x + (size_t)t * H;
+    float sum = 0.f, ss = 0.f;
+    for (int i0 = 0; i0 < H; i0 += 256) {
+        const float4 v = *(const float4*)(xt + i0 + lane * 4);
+        float gs = (v.x + v.y) + (v.z + v.w);
+        sum += gs;
+        ss = fmaf(v.x, v.x, ss);
+        ss = fmaf(v.y, v.y, ss);
+        ss = fmaf(v.z, v.z, ss);
+        ss = fmaf(v.w, v.w, ss);
+        gs += __shfl_xor(gs, 1);
+        gs += __shfl_xor(gs, 2);
+        gs += __shfl_xor(gs, 4);
+        gs += __shfl_xor(gs, 8);
+        if ((lane & 15) == 0) f.xgs[(size_t)t * (H / 64) + (i0 >> 6) + (lane >> 4)] = gs;
+    }
+    sum = wsum(sum);
+    ss = wsum(ss);
+    if (lane == 0) {
+        f.tok[t].xsum = sum;
+        f.tok[t].rscale = f.residual ? 1.0f / sqrtf(ss / (float)H + f.eps) : 1.0f;
+    }
+}
+
+// logits[t][e] = sum_h x[t][h] * W[e][h] (fp32, unnormalised x).  Tile: 32
+// tokens x 64 experts per 256-thread workgroup, 2 x 4 outputs per thread,
+// 32-column K steps staged through LDS.  B comes from the interleaved router
+// layout [Epad/64][H/4][64] float4.
+__global__ void __launch_bounds__(256) k_router_gemm(Fwd f)
+{
+    constexpr int TT = 32, KT = 32;
+    __shared__ float As[KT][TT + 1];
+    __shared__ float Bs[KT][64 + 4];
+    const int tid = threadIdx.x;
+    const int t0 = blockIdx.x * TT, b = blockIdx.y;
+    const int H = f.H, T = f.T, CH = H / 4;
+    const int ty = tid >> 4, tx = tid & 15;
+    const float4* wr = (const float4*)f.wr + (size_t)b * CH * 64;
+    float acc[2][4] = {};
+    for (int k0 = 0; k0 < H; k0 += KT) {
+        {   // A: 32 tokens x 32 columns, one float4 per thread
+            const int tt = tid >> 3, cc = (tid & 7) * 4;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (t0 + tt < T) v = *(const float4*)(f.x + (size_t)(t0 + tt) * H + k0 + cc);
+            As[cc + 0][tt] = v.x;
+            As[cc + 1][tt] = v.y;
+            As[cc + 2][tt] = v.z;
+            As[cc + 3][tt] = v.w;
+        }
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {  // B: 8 chunks x 64 experts
+            const int idx = tid + r * 256;
+            const int ch = idx >> 6, e = idx & 63;
+            const float4 v = wr[(size_t)(k0 / 4 + ch) * 64 + e];
+            Bs[ch * 4 + 0][e] = v.x;
+            Bs[ch * 4 + 1][e] = v.y;
+            Bs[ch * 4 + 2][e] = v.z;
+            Bs[ch * 4 + 3][e] = v.w;
+        }
+        __syncthreads();
+#pragma unroll 8
+        for (int k = 0; k < KT; ++k) {
+            const float a0 = As[k][ty * 2], a1 = As[k][ty * 2 + 1];
+            const float4 bv = *(const float4*)&Bs[k][tx * 4];
+            acc[0][0] = fmaf(a0, bv.x, acc[0][0]);
+            acc[0][1] = fmaf(a0, bv.y, acc[0][1]);
+            acc[0][2] = fmaf(a0, bv.z, acc[0][2]);
+            acc[0][3] = fmaf(a0, bv.w, acc[0][3]);
+            acc[1][0] = fmaf(a1, bv.x, acc[1][0]);
+            acc[1][1] = fmaf(a1, bv.y, acc[1][1]);
+            acc[1][2] = fmaf(a1, bv.z, acc[1][2]);
+            acc[1][3] = fmaf(a1, bv.w, acc[1][3]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int t = t0 + ty * 2 + i;
+        if (t < T)
+            *(float4*)(f.logits + (size_t)t * f.Epad + b * 64 + tx * 4) =
+                make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+    }
+}
+
+// Top-K per token, one wavefront per token (4 per workgroup): sigmoid of the
+// normalised logit, score = sigmoid + bias, K rounds of a wavefront argmax
+// over (score, lower id) keys, renormalised weights.
+__global__ void __launch_bounds__(256) k_topk(Fwd f)
+{
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= f.T) return;
+    const int E = f.E, K = f.K, Epad = f.Epad;
+    const float rs = f.tok[t].rscale;
+    float c[4], sg[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int e = lane + 64 * m;
+        c[m] = -INFINITY;
+        sg[m] = 0.f;
+        if (e < E) {
+            const float l = f.logits[(size_t)t * Epad + e] * rs;
+            sg[m] = 1.0f / (1.0f + expf(-l));
+            c[m] = sg[m] + f.bias[e];
+        }
+    }
+    uint32_t taken = 0;
+    float ssum = 0.f, mysig = 0.f;
+    int myid = 0;
+    for (int kk = 0; kk < K; ++kk) {
+        unsigned long long best = 0ull;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int e = lane + 64 * m;
+            if (e < Epad && !(taken & (1u << m))) {
+                const unsigned long long key =
+                    ((unsigned long long)ordf(c[m]) << 32) | (uint32_t)(0xFFFFu - e);
+                best = key > best ? key : best;
+            }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const unsigned long long other = __shfl_xor(best, o);
+            best = other > best ? other : best;
+        }
+        const int e = 0xFFFF - (int)(best & 0xFFFFu);
+        const int owner = e & 63, m = e >> 6;
+        float s_e = 0.f;
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm)
+            if (mm == m) s_e = sg[mm];
+        s_e = __shfl(s_e, owner);
+        if (lane == owner) taken |= 1u << m;
+        ssum += s_e;
+        if (lane == kk) {
+            myid = e;
+            mysig = s_e;
+        }
+    }
+    if (lane < K) {
+        const float wv = f.norm_topk ? f.routed_scale * (mysig / (ssum + 1e-20f))
+                                     : f.routed_scale * mysig;
+        f.ids[(size_t)t * K + lane] = myid;
+        f.wts[(size_t)t * K + lane] = wv;
+    }
+}
+
+// Stable counting sort of the T*K assignments by expert (one workgroup of
+// 1024 threads).  Within a 1024-assignment chunk, each wavefront finds the
+// lanes holding the same expert id with 8 ballots over the id's bits; a
+// per-expert running prefix over wavefronts and chunks keeps the order of
+// assignment indices.  If `groups` is set, also builds the forward's expert
+// groups (shared experts first, then active experts ascending) and flags
+// selected experts without a slot.
+__global__ void __launch_bounds__(1024) k_bucket(const int32_t* __restrict__ ids, int n, int E,
+                                                 int32_t* cnt, int32_t* off, int32_t* perm,
+                                                 int32_t* active, int32_t* n_active, Fwd f,
+                                                 int build_groups)
+{
+    __shared__ int s_cnt[256];
+    __shared__ int s_off[257];
+    __shared__ int s_act[256];
+    __shared__ int s_run[256];
+    __shared__ int s_nact;
+    __shared__ int wcnt[16][256];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    if (tid < 256) {
+        s_cnt[tid] = 0;
+        s_run[tid] = 0;
+    }
+    __syncthreads();
+    for (int a = tid; a < n; a += 1024) {
+        const int e = ids[a];
+        if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
+    }
+    __syncthreads();
+    if (w == 0) {
+        int c4[4], a4[4], sc = 0, sa = 0;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            c4[m] = s_cnt[lane * 4 + m];
+            a4[m] = c4[m] > 0;
+            sc += c4[m];
+            sa += a4[m];
+        }
+        int ic = sc, ia = sa;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int pc = __shfl_up(ic, o), pa = __shfl_up(ia, o);
+            if (lane >= o) {
+                ic += pc;
+                ia += pa;
+            }
+        }
+        int rc = ic - sc, ra = ia - sa;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            s_off[lane * 4 + m] = rc;
+            s_act[lane * 4 + m] = a4[m] ? ra : -1;
+            rc += c4[m];
+            ra += a4[m];
+        }
+        if (lane == 63) {
+            s_off[256] = rc;
+            s_nact = ra;
+        }
+    }
+    __syncthreads();
+    for (int base = 0; base < n; base += 1024) {
+        for (int i = tid; i < 16 * 256; i += 1024) (&wcnt[0][0])[i] = 0;
+        __syncthreads();
+        const int a = base + tid;
+        int e = a < n ? ids[a] : -1;
+        const bool valid = e >= 0 && e < E;
+        if (!valid) e = 0;
+        unsigned long long same = __ballot(valid);
+#pragma unroll
+        for (int bit = 0; bit < 8; ++bit) {
+            const bool on = (e >> bit) & 1;
+            const unsigned long long bb = __ballot(on);
+            same &= on ? bb : ~bb;
+        }
+        const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        const int rank = __popcll(same & below);
+        if (valid && rank == 0) wcnt[w][e] = __popcll(same);
+        __syncthreads();
+        if (tid < 256) {
+            int run = s_run[tid];
+            for (int v = 0; v < 16; ++v) {
+                const int c = wcnt[v][tid];
+                wcnt[v][tid] = run;
+                run += c;
+            }
+            s_run[tid] = run;
+        }
+        __syncthreads();
+        if (valid) perm[s_off[e] + wcnt[w][e] + rank] = a;
+        __syncthreads();
+    }
+    if (tid < E) {
+        cnt[tid] = s_cnt[tid];
+        off[tid] = s_off[tid];
+        if (s_act[tid] >= 0) active[s_act[tid]] = tid;
+    }
+    if (tid == 0) {
+        off[E] = s_off[E];
+        n_active[0] = s_nact;
+    }
+    if (!build_groups) return;
+    if (tid < E && s_act[tid] >= 0) {
+        const int slot = f.tbl[tid];
+        Group g;
+        g.base = slot >= 0 ? f.pool + (size_t)slot * f.slot_bytes : nullptr;
+        g.cnt = s_cnt[tid];
+        g.off = s_off[tid];
+        g.kind = 0;
+        g.expert = tid;
+        f.groups[f.n_shared + s_act[tid]] = g;
+        if (slot < 0) {
+            atomicOr(&f.status[0], (uint32_t)STATUS_NOT_RESIDENT);
+            const int code = f.layer * E + tid;
+            atomicOr(&f.status[1 + code / 32], 1u << (code % 32));
+        }
+    }
+    if (tid < f.n_shared) {
+        Group g;
+        g.base = f.shared + (size_t)tid * f.slot_bytes;
+        g.cnt = f.T;
+        g.off = tid;
+        g.kind = 1;
+        g.expert = -1;
+        f.groups[tid] = g;
+    }
+    if (tid == 0) f.n_groups[0] = f.n_shared + s_nact;
+}
+
+hipError_t launch_router_large(const Fwd& f, hipStream_t st, int stage)
+{
+    switch (stage) {
+    case 0:
+        hipLaunchKernelGGL(k_tokstats, dim3((f.T + 3) / 4), dim3(256), 0, st, f);
+        break;
+    case 1:
+        hipLaunchKernelGGL(k_router_gemm, dim3((f.T + 31) / 32, f.Epad / 64), dim3(256), 0, st, f);
+        break;
+    case 2:
+        hipLaunchKernelGGL(k_topk, dim3((f.T + 3) / 4), dim3(256), 0, st, f);
+        break;
+    default:
+        hipLaunchKernelGGL(k_bucket, dim3(1), dim3(1024), 0, st, (const int32_t*)f.ids, f.T * f.K,
+                           f.E, f.cnt, f.off, f.perm, f.active, f.n_active, f, 1);
+        break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_bucket(const int32_t* ids, int T, int K, int E, int32_t* cnt, int32_t* off,
+                         int32_t* perm, int32_t* active, int32_t* n_active, hipStream_t st)
+{
+    Fwd f{};
+    hipLaunchKernelGGL(k_bucket, dim3(1), dim3(1024), 0, st, ids, T * K, E, cnt, off, perm, active,
+                       n_active, f, 0);
+    return hipGetLastError();
+}
+
+}  // namespace moe

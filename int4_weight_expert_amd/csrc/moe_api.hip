@@ -1,0 +1,514 @@
+// moe_api.hip -- the C ABI of include/moe.h: context, HBM slot pool, slot
+// table, argument checks and kernel dispatch.
+//
+// The slot pool follows the expert-slot idea of "初始化与权重加载" (colibrì
+// analysis) §2.2 (ESlot: one expert's gate/up/down held together, looked up
+// by expert id) and of the Edge0 write-up §十四 (routing indices mapped
+// through a slot table that never leaves the GPU): experts live in HBM
+// slots, and a per-layer table expert id -> slot (-1 = not resident) is
+// read by the kernels, so a forward touches whichever experts are resident.
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "moe_internal.h"
+
+using namespace moe;
+
+struct moe_ctx {
+    moe_config cfg;
+    hipStream_t stream = nullptr;
+    int device = 0;
+    size_t slot_bytes = 0;
+    int Epad = 0;
+    uint8_t* pool = nullptr;
+    float* wr = nullptr;
+    float* bias = nullptr;
+    int* tbl = nullptr;
+    std::vector<int> tbl_host;
+    uint8_t* shared = nullptr;
+    uint8_t* staging = nullptr;
+    // workspace
+    float* part = nullptr;
+    float* logits = nullptr;
+    int32_t* ids = nullptr;
+    float* wts = nullptr;
+    TokStat* tok = nullptr;
+    float* xgs = nullptr;
+    int32_t* cnt = nullptr;
+    int32_t* off = nullptr;
+    int32_t* perm = nullptr;
+    int32_t* active = nullptr;
+    int32_t* n_active = nullptr;
+    Group* groups = nullptr;
+    int32_t* n_groups = nullptr;
+    float* h = nullptr;
+    float* hgs = nullptr;
+    float* ystage = nullptr;
+    uint32_t* counters = nullptr;
+    uint32_t* status = nullptr;
+    size_t status_words = 0;
+    int gemm_min_tokens = 64;
+    // timing
+    bool timing = false;
+    std::vector<hipEvent_t> events;
+    std::vector<const char*> names;
+    int n_marks = 0;
+    std::vector<void*> allocs;
+};
+
+namespace {
+
+constexpr int kDefaultGemmMin = 64;
+
+int hip_ok(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_E_HIP; }
+
+template <typename P>
+int dalloc(moe_ctx* c, P** p, size_t bytes)
+{
+    void* q = nullptr;
+    if (bytes == 0) bytes = 256;
+    if (hipMalloc(&q, bytes) != hipSuccess) return MOE_E_NOMEM;
+    c->allocs.push_back(q);
+    *p = (P*)q;
+    return MOE_OK;
+}
+
+size_t expert_bytes_for(int fmt, size_t H, size_t I)
+{
+    const size_t packed = 3 * H * I / 2;
+    if (fmt == MOE_W_INT4_ROW) return packed + 4 * (2 * I + H);
+    if (fmt == MOE_W_INT4_AFFINE_G64) return packed + 12 * H * I / 64;
+    return 0;
+}
+
+int router_slices(int H)
+{
+    // K-slices of the small-T router: a multiple of 4 dividing H/4, with at
+    // least 16 float4 chunks per slice, at most 64 slices
+    const int CH = H / 4;
+    int best = 4;
+    for (int s = 4; s <= 64; s += 4)
+        if (CH % s == 0 && CH / s >= 16) best = s;
+    return best;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb)
+{
+    const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+    return pa < pb + nb && pb < pa + na;
+}
+
+void mark(moe_ctx* c, const char* name)
+{
+    if (!c->timing) return;
+    if (c->n_marks >= (int)c->events.size()) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) return;
+        c->events.push_back(e);
+        c->names.push_back(nullptr);
+    }
+    c->names[c->n_marks] = name;
+    hipEventRecord(c->events[c->n_marks], c->stream);
+    c->n_marks++;
+}
+
+Fwd make_fwd(moe_ctx* c, const float* x, float* out, int T, int layer, int residual)
+{
+    const moe_config& g = c->cfg;
+    Fwd f{};
+    f.x = x;
+    f.out = out;
+    f.T = T;
+    f.H = g.hidden;
+    f.I = g.inter;
+    f.E = g.n_experts;
+    f.K = g.top_k;
+    f.n_shared = g.n_shared;
+    f.fmt = g.wfmt;
+    f.Epad = c->Epad;
+    f.residual = residual;
+    f.routed_scale = g.routed_scale;
+    f.eps = g.rms_eps;
+    f.norm_topk = g.norm_topk;
+    f.layer = layer;
+    f.wr = c->wr + (size_t)layer * c->Epad * g.hidden;
+    f.bias = c->bias + (size_t)layer * g.n_experts;
+    f.tbl = c->tbl + (size_t)layer * g.n_experts;
+    f.pool = c->pool;
+    f.slot_bytes = c->slot_bytes;
+    f.shared = c->shared + (size_t)layer * g.n_shared * c->slot_bytes;
+    f.part = c->part;
+    f.S = router_slices(g.hidden);
+    f.logits = c->logits;
+    f.ids = c->ids;
+    f.wts = c->wts;
+    f.tok = c->tok;
+    f.xgs = c->xgs;
+    f.cnt = c->cnt;
+    f.off = c->off;
+    f.perm = c->perm;
+    f.active = c->active;
+    f.n_active = c->n_active;
+    f.groups = c->groups;
+    f.n_groups = c->n_groups;
+    f.h = c->h;
+    f.hgs = c->hgs;
+    f.ystage = c->ystage;
+    f.counters = c->counters;
+    f.status = c->status;
+    f.n_layers = g.n_layers;
+    return f;
+}
+
+// router + bucketing; leaves ids/wts/groups in the workspace
+int run_router(moe_ctx* c, const Fwd& f)
+{
+    hipError_t e;
+    if (f.T <= ROUTER_SMALL_MAX_T) {
+        mark(c, "router_topk_bucket");
+        e = launch_router_small(f, c->stream);
+        if (e != hipSuccess) return MOE_E_HIP;
+        return MOE_OK;
+    }
+    static const char* names[4] = {"token_stats", "router_gemm", "topk", "bucket"};
+    for (int s = 0; s < 4; ++s) {
+        mark(c, names[s]);
+        e = launch_router_large(f, c->stream, s);
+        if (e != hipSuccess) return MOE_E_HIP;
+    }
+    return MOE_OK;
+}
+
+int run_forward(moe_ctx* c, const float* x, int T, int layer, float* out, int residual)
+{
+    if (!c || !x || !out) return MOE_E_ARG;
+    const moe_config& g = c->cfg;
+    if (T < 1 || T > g.max_tokens || layer < 0 || layer >= g.n_layers) return MOE_E_ARG;
+    const size_t nb = (size_t)T * g.hidden * sizeof(float);
+    if (!residual && overlaps(x, nb, out, nb)) return MOE_E_ARG;
+    c->n_marks = 0;
+    Fwd f = make_fwd(c, x, out, T, layer, residual);
+    int rc = run_router(c, f);
+    if (rc) return rc;
+    const int max_groups = g.n_shared + std::min(g.n_experts, T * g.top_k);
+    mark(c, "gateup_gemv");
+    if (launch_gateup_gemv(f, max_groups, c->stream) != hipSuccess) return MOE_E_HIP;
+    mark(c, "down_gemv_combine");
+    if (launch_down_gemv(f, max_groups, c->stream) != hipSuccess) return MOE_E_HIP;
+    mark(c, "end");
+    return MOE_OK;
+}
+
+int copy_in_blob(moe_ctx* c, uint8_t* dst_slot, const void* blob, size_t nbytes)
+{
+    if (!blob) return MOE_E_ARG;
+    if (nbytes != c->slot_bytes) return MOE_E_SIZE;
+    if (hipMemcpyAsync(c->staging, blob, nbytes, hipMemcpyDefault, c->stream) != hipSuccess)
+        return MOE_E_HIP;
+    if (launch_blob_to_slot(c->staging, dst_slot, c->cfg.wfmt, c->cfg.hidden, c->cfg.inter,
+                            c->stream) != hipSuccess)
+        return MOE_E_HIP;
+    return hip_ok(hipStreamSynchronize(c->stream));
+}
+
+int pack_into(moe_ctx* c, uint8_t* dst_slot, const float* Wg, const float* Wu, const float* Wd)
+{
+    if (!Wg || !Wu || !Wd) return MOE_E_ARG;
+    const int64_t H = c->cfg.hidden, I = c->cfg.inter;
+    const int64_t gq = I * (H / 2), dq = H * (I / 2);
+    uint8_t* b = c->staging;
+    uint8_t* sc = b + 2 * gq + dq;
+    hipError_t e;
+    if (c->cfg.wfmt == MOE_W_INT4_ROW) {
+        e = launch_pack_int4_rows(Wg, I, H, b, (float*)sc, c->stream);
+        if (e == hipSuccess) e = launch_pack_int4_rows(Wu, I, H, b + gq, (float*)sc + I, c->stream);
+        if (e == hipSuccess)
+            e = launch_pack_int4_rows(Wd, H, I, b + 2 * gq, (float*)sc + 2 * I, c->stream);
+    } else {
+        const int64_t ga = I * (H / 64) * 2;
+        e = launch_pack_affine_g64(Wg, I, H, b, (uint16_t*)sc, c->stream);
+        if (e == hipSuccess)
+            e = launch_pack_affine_g64(Wu, I, H, b + gq, (uint16_t*)sc + ga, c->stream);
+        if (e == hipSuccess)
+            e = launch_pack_affine_g64(Wd, H, I, b + 2 * gq, (uint16_t*)sc + 2 * ga, c->stream);
+    }
+    if (e != hipSuccess) return MOE_E_HIP;
+    return hip_ok(launch_blob_to_slot(b, dst_slot, c->cfg.wfmt, (int)H, (int)I, c->stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
+{
+    if (!cfg || !out) return MOE_E_ARG;
+    *out = nullptr;
+    const moe_config& g = *cfg;
+    if (g.hidden <= 0 || g.inter <= 0 || g.n_experts <= 0 || g.top_k <= 0 || g.n_layers <= 0 ||
+        g.n_slots < 0 || g.max_tokens <= 0 || g.n_shared < 0)
+        return MOE_E_ARG;
+    if (g.wfmt != MOE_W_INT4_ROW && g.wfmt != MOE_W_INT4_AFFINE_G64) return MOE_E_ARG;
+    if (g.n_group != 1 || g.topk_group != 1) return MOE_E_UNSUPPORTED;
+    if (g.n_experts > 256 || g.top_k > 8 || g.top_k > g.n_experts || g.n_shared > 1)
+        return MOE_E_UNSUPPORTED;
+    if (g.hidden % 256 || g.inter % 256) return MOE_E_UNSUPPORTED;
+    if ((size_t)g.max_tokens * g.top_k > 65536) return MOE_E_UNSUPPORTED;
+
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_E_HIP;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_E_HIP;
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MOE_E_HIP;
+
+    moe_ctx* c = new moe_ctx();
+    c->cfg = g;
+    c->stream = (hipStream_t)stream;
+    c->device = dev;
+    c->slot_bytes = expert_bytes_for(g.wfmt, g.hidden, g.inter);
+    c->Epad = (g.n_experts + 63) / 64 * 64;
+    const size_t H = g.hidden, I = g.inter, E = g.n_experts, L = g.n_layers, Tm = g.max_tokens;
+    const size_t K = g.top_k, rows = Tm * K + Tm * g.n_shared;
+    int rc = MOE_OK;
+    rc = rc ? rc : dalloc(c, &c->pool, (size_t)g.n_slots * c->slot_bytes);
+    rc = rc ? rc : dalloc(c, &c->wr, L * c->Epad * H * 4);
+    rc = rc ? rc : dalloc(c, &c->bias, L * E * 4);
+    rc = rc ? rc : dalloc(c, &c->tbl, L * E * 4);
+    rc = rc ? rc : dalloc(c, &c->shared, L * g.n_shared * c->slot_bytes);
+    rc = rc ? rc : dalloc(c, &c->staging, c->slot_bytes);
+    rc = rc ? rc : dalloc(c, &c->part, (size_t)64 * ROUTER_SMALL_MAX_T * c->Epad * 4);
+    rc = rc ? rc : dalloc(c, &c->logits, Tm * c->Epad * 4);
+    rc = rc ? rc : dalloc(c, &c->ids, Tm * K * 4);
+    rc = rc ? rc : dalloc(c, &c->wts, Tm * K * 4);
+    rc = rc ? rc : dalloc(c, &c->tok, Tm * sizeof(TokStat));
+    rc = rc ? rc : dalloc(c, &c->xgs, Tm * (H / 64) * 4);
+    rc = rc ? rc : dalloc(c, &c->cnt, E * 4);
+    rc = rc ? rc : dalloc(c, &c->off, (E + 1) * 4);
+    rc = rc ? rc : dalloc(c, &c->perm, Tm * K * 4);
+    rc = rc ? rc : dalloc(c, &c->active, E * 4);
+    rc = rc ? rc : dalloc(c, &c->n_active, 4);
+    rc = rc ? rc : dalloc(c, &c->groups, (E + g.n_shared) * sizeof(Group));
+    rc = rc ? rc : dalloc(c, &c->n_groups, 4);
+    rc = rc ? rc : dalloc(c, &c->h, rows * I * 4);
+    rc = rc ? rc : dalloc(c, &c->hgs, rows * (I / 64) * 4);
+    rc = rc ? rc : dalloc(c, &c->ystage, rows * H * 4);
+    rc = rc ? rc : dalloc(c, &c->counters, (1 + H / 64) * 4);
+    c->status_words = 1 + (L * E + 31) / 32;
+    rc = rc ? rc : dalloc(c, &c->status, c->status_words * 4);
+    if (rc == MOE_OK) {
+        c->tbl_host.assign(L * E, -1);
+        hipError_t e = hipMemcpy(c->tbl, c->tbl_host.data(), L * E * 4, hipMemcpyHostToDevice);
+        if (e == hipSuccess) e = hipMemset(c->counters, 0, (1 + H / 64) * 4);
+        if (e == hipSuccess) e = hipMemset(c->status, 0, c->status_words * 4);
+        if (e == hipSuccess) e = hipMemset(c->bias, 0, L * E * 4);
+        if (e == hipSuccess) e = hipMemset(c->wr, 0, L * c->Epad * H * 4);
+        if (e == hipSuccess && g.n_shared) e = hipMemset(c->shared, 0, L * g.n_shared * c->slot_bytes);
+        if (e == hipSuccess) e = hipDeviceSynchronize();
+        if (e != hipSuccess) rc = MOE_E_HIP;
+    }
+    if (rc != MOE_OK) {
+        moe_destroy(c);
+        return rc;
+    }
+    *out = c;
+    return MOE_OK;
+}
+
+void moe_destroy(moe_ctx* c)
+{
+    if (!c) return;
+    hipStreamSynchronize(c->stream);
+    for (hipEvent_t e : c->events) hipEventDestroy(e);
+    for (void* p : c->allocs) hipFree(p);
+    delete c;
+}
+
+int moe_set_stream(moe_ctx* c, void* stream)
+{
+    if (!c) return MOE_E_ARG;
+    c->stream = (hipStream_t)stream;
+    return MOE_OK;
+}
+
+size_t moe_expert_bytes(const moe_ctx* c) { return c ? c->slot_bytes : 0; }
+
+int moe_set_router(moe_ctx* c, int layer, const float* W, const float* bias)
+{
+    if (!c || !W || !bias || layer < 0 || layer >= c->cfg.n_layers) return MOE_E_ARG;
+    const size_t H = c->cfg.hidden, E = c->cfg.n_experts;
+    float* tmp = nullptr;
+    if (hipMalloc(&tmp, E * H * 4) != hipSuccess) return MOE_E_NOMEM;
+    hipError_t e = hipMemcpyAsync(tmp, W, E * H * 4, hipMemcpyDefault, c->stream);
+    if (e == hipSuccess)
+        e = launch_router_to_internal(tmp, c->wr + (size_t)layer * c->Epad * H, (int)E, c->Epad,
+                                      (int)H, c->stream);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(c->bias + (size_t)layer * E, bias, E * 4, hipMemcpyDefault, c->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+    hipFree(tmp);
+    return hip_ok(e);
+}
+
+int moe_load_expert(moe_ctx* c, int slot, const void* blob, size_t nbytes)
+{
+    if (!c) return MOE_E_ARG;
+    if (slot < 0 || slot >= c->cfg.n_slots) return MOE_E_SLOT;
+    return copy_in_blob(c, c->pool + (size_t)slot * c->slot_bytes, blob, nbytes);
+}
+
+int moe_pack_expert(moe_ctx* c, int slot, const float* Wg, const float* Wu, const float* Wd)
+{
+    if (!c) return MOE_E_ARG;
+    if (slot < 0 || slot >= c->cfg.n_slots) return MOE_E_SLOT;
+    return pack_into(c, c->pool + (size_t)slot * c->slot_bytes, Wg, Wu, Wd);
+}
+
+int moe_set_shared(moe_ctx* c, int layer, int s, const void* blob, size_t nbytes)
+{
+    if (!c || layer < 0 || layer >= c->cfg.n_layers || s < 0 || s >= c->cfg.n_shared)
+        return MOE_E_ARG;
+    return copy_in_blob(c, c->shared + ((size_t)layer * c->cfg.n_shared + s) * c->slot_bytes,
+                        blob, nbytes);
+}
+
+int moe_pack_shared(moe_ctx* c, int layer, int s, const float* Wg, const float* Wu,
+                    const float* Wd)
+{
+    if (!c || layer < 0 || layer >= c->cfg.n_layers || s < 0 || s >= c->cfg.n_shared)
+        return MOE_E_ARG;
+    return pack_into(c, c->shared + ((size_t)layer * c->cfg.n_shared + s) * c->slot_bytes, Wg,
+                     Wu, Wd);
+}
+
+int moe_map_expert(moe_ctx* c, int layer, int expert_id, int slot)
+{
+    if (!c || layer < 0 || layer >= c->cfg.n_layers || expert_id < 0 ||
+        expert_id >= c->cfg.n_experts)
+        return MOE_E_ARG;
+    if (slot < -1 || slot >= c->cfg.n_slots) return MOE_E_SLOT;
+    const size_t i = (size_t)layer * c->cfg.n_experts + expert_id;
+    c->tbl_host[i] = slot;
+    hipError_t e = hipMemcpyAsync(c->tbl + i, &c->tbl_host[i], 4, hipMemcpyHostToDevice, c->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+    return hip_ok(e);
+}
+
+int moe_read_slot(moe_ctx* c, int slot, void* dst, size_t nbytes)
+{
+    if (!c || !dst) return MOE_E_ARG;
+    if (slot < 0 || slot >= c->cfg.n_slots) return MOE_E_SLOT;
+    if (nbytes != c->slot_bytes) return MOE_E_SIZE;
+    hipError_t e = launch_slot_to_blob(c->pool + (size_t)slot * c->slot_bytes, c->staging,
+                                       c->cfg.wfmt, c->cfg.hidden, c->cfg.inter, c->stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(dst, c->staging, nbytes, hipMemcpyDefault, c->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+    return hip_ok(e);
+}
+
+int moe_forward(moe_ctx* c, const float* x, int T, int layer, float* out)
+{
+    return run_forward(c, x, T, layer, out, 0);
+}
+
+int moe_forward_residual(moe_ctx* c, float* x, int T, int layer)
+{
+    return run_forward(c, x, T, layer, x, 1);
+}
+
+int moe_route(moe_ctx* c, const float* x, int T, int layer, int32_t* ids, float* w)
+{
+    if (!c || !x || !ids || !w) return MOE_E_ARG;
+    const moe_config& g = c->cfg;
+    if (T < 1 || T > g.max_tokens || layer < 0 || layer >= g.n_layers) return MOE_E_ARG;
+    c->n_marks = 0;
+    Fwd f = make_fwd(c, x, nullptr, T, layer, 0);
+    int rc = run_router(c, f);
+    if (rc) return rc;
+    mark(c, "end");
+    const size_t n = (size_t)T * g.top_k;
+    hipError_t e = hipMemcpyAsync(ids, c->ids, n * 4, hipMemcpyDeviceToDevice, c->stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(w, c->wts, n * 4, hipMemcpyDeviceToDevice, c->stream);
+    return hip_ok(e);
+}
+
+int moe_status(moe_ctx* c, int32_t* missing, int cap, int* n_missing)
+{
+    if (!c) return MOE_E_ARG;
+    std::vector<uint32_t> st(c->status_words, 0);
+    hipError_t e = hipStreamSynchronize(c->stream);
+    if (e == hipSuccess)
+        e = hipMemcpy(st.data(), c->status, c->status_words * 4, hipMemcpyDeviceToHost);
+    if (e == hipSuccess) e = hipMemset(c->status, 0, c->status_words * 4);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) return MOE_E_HIP;
+    int n = 0;
+    for (size_t wd = 1; wd < c->status_words; ++wd)
+        for (int bit = 0; bit < 32; ++bit)
+            if (st[wd] & (1u << bit)) {
+                if (missing && n < cap) missing[n] = (int32_t)((wd - 1) * 32 + bit);
+                ++n;
+            }
+    if (n_missing) *n_missing = n;
+    if (st[0] & STATUS_NOT_RESIDENT) return MOE_E_NOT_RESIDENT;
+    if (st[0] & STATUS_RANGE) return MOE_E_RANGE;
+    return MOE_OK;
+}
+
+int moe_set_gemm_min_tokens(moe_ctx* c, int min_tokens)
+{
+    if (!c || min_tokens < 0) return MOE_E_ARG;
+    c->gemm_min_tokens = min_tokens ? min_tokens : kDefaultGemmMin;
+    return MOE_OK;
+}
+
+int moe_set_timing(moe_ctx* c, int on)
+{
+    if (!c) return MOE_E_ARG;
+    c->timing = on != 0;
+    return MOE_OK;
+}
+
+int moe_last_timings(moe_ctx* c, float* ms, const char** names, int cap, int* n)
+{
+    if (!c || !n) return MOE_E_ARG;
+    if (!c->timing || c->n_marks < 2) {
+        *n = 0;
+        return MOE_OK;
+    }
+    if (hipEventSynchronize(c->events[c->n_marks - 1]) != hipSuccess) return MOE_E_HIP;
+    const int k = c->n_marks - 1;
+    for (int i = 0; i < k && i < cap; ++i) {
+        float v = 0.f;
+        if (hipEventElapsedTime(&v, c->events[i], c->events[i + 1]) != hipSuccess) return MOE_E_HIP;
+        if (ms) ms[i] = v;
+        if (names) names[i] = c->names[i];
+    }
+    *n = k;
+    return MOE_OK;
+}
+
+int moe_pack_int4_rows(const float* w, int64_t O, int64_t I, uint8_t* q, float* s, void* stream)
+{
+    if (!w || !q || !s || O <= 0 || I <= 0 || (I & 1)) return MOE_E_ARG;
+    return hip_ok(launch_pack_int4_rows(w, O, I, q, s, (hipStream_t)stream));
+}
+
+int moe_pack_affine_g64(const float* w, int64_t O, int64_t I, uint8_t* q, uint16_t* scmn,
+                        void* stream)
+{
+    if (!w || !q || !scmn || O <= 0 || I <= 0 || (I % 64)) return MOE_E_ARG;
+    return hip_ok(launch_pack_affine_g64(w, O, I, q, scmn, (hipStream_t)stream));
+}
+
+int moe_bucket(const int32_t* ids, int T, int K, int E, int32_t* cnt, int32_t* off,
+               int32_t* perm, int32_t* active, int32_t* n_active, void* stream)
+{
+    if (!ids || !cnt || !off || !perm || !active || !n_active) return MOE_E_ARG;
+    if (T < 1 || K < 1 || E < 1 || E > 256 || (int64_t)T * K > 65536) return MOE_E_ARG;
+    return hip_ok(launch_bucket(ids, T, K, E, cnt, off, perm, active, n_active,
+                                (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+// moe_internal.h -- shared declarations of the MI355X int4 MoE library
+// (context, device work descriptors, kernel launchers).  Internal to the
+// library; the public ABI is include/moe.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Slot layout (the library's own order of an expert's bytes in HBM).
+//
+// Every int4 matrix [O][In] is stored as 64-row blocks: block b, 16-byte
+// chunk c (32 consecutive inputs) of its 64 rows are 1 KiB contiguous,
+//   byte offset ((b * (In/32) + c) * 64 + lane) * 16  holds row 64b+lane,
+//   inputs 32c .. 32c+31.
+// A wavefront reading chunk c of block b therefore issues one fully
+// coalesced 1 KiB load (16 B per lane, lane = output row), and every lane
+// needs the same 32 activations, which arrive as scalar (SGPR) operands.
+// Row format codes are stored offset-binary (code + 8, i.e. blob byte ^ 0x88)
+// so that unsigned byte conversion gives code + 8 directly.
+// Scales follow the three matrices: row format keeps fp32 sg[I] su[I] sd[H]
+// unchanged; affine format stores the (scale, min) bf16 pair of row 64b+lane,
+// group g at ((b * (In/64) + g) * 64 + lane) * 4.
+// Sizes equal the blob sizes, so a slot is moe_expert_bytes() long.
+// ---------------------------------------------------------------------------
+
+struct Group {
+    const uint8_t* base;  // slot bytes; nullptr = expert not resident
+    int cnt;              // tokens in this group
+    int off;              // routed: first index into perm; shared: shared index s
+    int kind;             // 0 routed, 1 shared
+    int expert;           // expert id (routed) or -1
+};
+
+struct TokStat {
+    float xsum;    // sum of x over the row (offset correction of int4 codes)
+    float rscale;  // RMSNorm factor (1 when the forward does not normalise)
+};
+
+// Launch-time description of one forward (all device pointers).
+struct Fwd {
+    const float* x;       // [T][H]
+    float* out;           // [T][H]
+    int T, H, I, E, K, n_shared, fmt, Epad;
+    int residual;         // 1: out = x + moe(rmsnorm(x)), x may equal out
+    float routed_scale, eps;
+    int norm_topk;
+    int layer;
+    const float* wr;      // router, interleaved [Epad/64][H/4][64] float4
+    const float* bias;    // [E]
+    const int* tbl;       // [E] slot table row of this layer
+    const uint8_t* pool;  // slot pool base
+    size_t slot_bytes;
+    const uint8_t* shared;  // n_shared shared experts of this layer (slot layout)
+    // workspace
+    float* part;          // small-T router partial logits [S][T][Epad]
+    int S;                // router K-slices
+    float* logits;        // [T][Epad] (large-T router)
+    int32_t* ids;         // [T][K]
+    float* wts;           // [T][K]
+    TokStat* tok;         // [T]
+    float* xgs;           // [T][H/64] group sums of x
+    int32_t* cnt;         // [E]
+    int32_t* off;         // [E+1]
+    int32_t* perm;        // [T*K]
+    int32_t* active;      // [E]
+    int32_t* n_active;    // [1]
+    Group* groups;        // [n_shared + E]
+    int32_t* n_groups;    // [1]
+    float* h;             // [T*K + T*n_shared][I]
+    float* hgs;           // [rows][I/64]
+    float* ystage;        // [rows][H]
+    uint32_t* counters;   // [1 + H/64]: router arrivals, then per row block
+    uint32_t* status;     // [0] flags, [1..] missing bitmap over layer*E+id
+    int n_layers;
+};
+
+enum { STATUS_NOT_RESIDENT = 1u, STATUS_RANGE = 2u };
+
+// launchers (return hipError_t)
+hipError_t launch_pack_int4_rows(const float* w, int64_t O, int64_t I, uint8_t* q, float* s,
+                                 hipStream_t st);
+hipError_t launch_pack_affine_g64(const float* w, int64_t O, int64_t I, uint8_t* q,
+                                  uint16_t* scmn, hipStream_t st);
+hipError_t launch_blob_to_slot(const uint8_t* blob, uint8_t* slot, int fmt, int H, int I,
+                               hipStream_t st);
+hipError_t launch_slot_to_blob(const uint8_t* slot, uint8_t* blob, int fmt, int H, int I,
+                               hipStream_t st);
+hipError_t launch_router_to_internal(const float* W, float* wr, int E, int Epad, int H,
+                                     hipStream_t st);
+hipError_t launch_bucket(const int32_t* ids, int T, int K, int E, int32_t* cnt, int32_t* off,
+                         int32_t* perm, int32_t* active, int32_t* n_active, hipStream_t st);
+
+// forward pieces; `names` receives static kernel names for timing
+hipError_t launch_router_small(const Fwd& f, hipStream_t st);
+hipError_t launch_router_large(const Fwd& f, hipStream_t st, int stage);
+hipError_t launch_gateup_gemv(const Fwd& f, int max_groups, hipStream_t st);
+hipError_t launch_down_gemv(const Fwd& f, int max_groups, hipStream_t st);
+
+constexpr int ROUTER_SMALL_MAX_T = 16;
+
+}  // namespace moe

@@ -1,0 +1,106 @@
+"""MoeLayer: a context of libmoe_int4.so with torch-tensor arguments.
+
+PyTorch provides device memory and the stream; every step of the layer runs
+in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import moe as M
+
+
+class MoeLayer:
+    def __init__(self, H: int, I: int, E: int, K: int, n_shared: int, n_layers: int, fmt: int,
+                 n_slots: int, max_tokens: int, routed_scale: float = 2.5, norm_topk: int = 1,
+                 rms_eps: float = 1e-6, stream: torch.cuda.Stream | None = None):
+        self.H, self.I, self.E, self.K = H, I, E, K
+        self.n_shared, self.n_layers, self.fmt = n_shared, n_layers, fmt
+        self.n_slots, self.max_tokens = n_slots, max_tokens
+        self.stream = stream if stream is not None else torch.cuda.current_stream()
+        cfg = M.make_config(H, I, E, K, n_shared, n_layers, fmt, n_slots, max_tokens,
+                            routed_scale=routed_scale, norm_topk=norm_topk, rms_eps=rms_eps)
+        self.ctx = M.moe_layer_create(cfg, self.stream.cuda_stream)
+        self.expert_bytes = M.moe_expert_bytes(self.ctx)
+
+    def close(self) -> None:
+        if self.ctx:
+            M.moe_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ---- weights -----------------------------------------------------------
+    def set_router(self, layer: int, W, bias) -> None:
+        W = _contig_f32(W)
+        bias = _contig_f32(bias)
+        M.moe_set_router(self.ctx, layer, W, bias)
+
+    def load_expert(self, slot: int, blob) -> None:
+        blob = _contig_u8(blob)
+        M._check("moe_load_expert", M.moe_load_expert(self.ctx, slot, blob, _nbytes(blob)))
+
+    def pack_expert(self, slot: int, Wg, Wu, Wd) -> None:
+        M._check("moe_pack_expert", M.moe_pack_expert(self.ctx, slot, Wg, Wu, Wd))
+
+    def set_shared(self, layer: int, s: int, blob) -> None:
+        blob = _contig_u8(blob)
+        M._check("moe_set_shared", M.moe_set_shared(self.ctx, layer, s, blob, _nbytes(blob)))
+
+    def pack_shared(self, layer: int, s: int, Wg, Wu, Wd) -> None:
+        M._check("moe_pack_shared", M.moe_pack_shared(self.ctx, layer, s, Wg, Wu, Wd))
+
+    def map(self, layer: int, expert_id: int, slot: int) -> None:
+        M._check("moe_map_expert", M.moe_map_expert(self.ctx, layer, expert_id, slot))
+
+    def read_slot(self, slot: int) -> np.ndarray:
+        out = np.empty(self.expert_bytes, dtype=np.uint8)
+        M._check("moe_read_slot", M.moe_read_slot(self.ctx, slot, out, self.expert_bytes))
+        return out
+
+    # ---- compute -----------------------------------------------------------
+    def forward(self, x: torch.Tensor, layer: int, out: torch.Tensor | None = None) -> torch.Tensor:
+        assert x.is_cuda and x.dtype == torch.float32 and x.is_contiguous()
+        T = x.shape[0]
+        if out is None:
+            out = torch.empty_like(x)
+        M._check("moe_forward", M.moe_forward(self.ctx, x, T, layer, out))
+        return out
+
+    def forward_residual(self, x: torch.Tensor, layer: int) -> torch.Tensor:
+        assert x.is_cuda and x.dtype == torch.float32 and x.is_contiguous()
+        M._check("moe_forward_residual", M.moe_forward_residual(self.ctx, x, x.shape[0], layer))
+        return x
+
+    def route(self, x: torch.Tensor, layer: int):
+        T = x.shape[0]
+        ids = torch.empty((T, self.K), dtype=torch.int32, device=x.device)
+        w = torch.empty((T, self.K), dtype=torch.float32, device=x.device)
+        M._check("moe_route", M.moe_route(self.ctx, x, T, layer, ids, w))
+        return ids, w
+
+    def status(self):
+        return M.moe_status(self.ctx)
+
+
+def _contig_f32(a):
+    if isinstance(a, np.ndarray):
+        return np.ascontiguousarray(a, dtype=np.float32)
+    return a.contiguous().float()
+
+
+def _contig_u8(a):
+    if isinstance(a, np.ndarray):
+        return np.ascontiguousarray(a, dtype=np.uint8)
+    return a.contiguous()
+
+
+def _nbytes(a) -> int:
+    if isinstance(a, np.ndarray):
+        return a.nbytes
+    return a.numel() * a.element_size()
