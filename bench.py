@@ -1,0 +1,327 @@
+#!/usr/bin/env python3
+"""Benchmark of the int4 MoE FFN step on one MI355X.
+
+Step = one moe_forward of a GLM-5.2-shape MoE layer (H=6144, 256 experts,
+top-8, I=2048, one shared expert, int4 per-row scales) on one decode token,
+rotating through 8 resident layers (38.7 GB of experts in the slot pool, so
+the 256 MB Infinity Cache cannot serve repeats).  Inputs are resident in HBM
+before the timed region.  Prints one JSON line.
+
+Also measured (under "extra"): the 8-token speculative-verify batch through
+8 chained layers, the Edge0-shape 40-layer decode step (affine int4 g64,
+top-4 and top-8), and the 2048-token prefill layer; and the CPU oracle on a
+bounded sample of the decode workload (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, datasheet
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA, datasheet
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def glm_bytes(cfg, n_experts_read: int, T: int) -> int:
+    """Algorithmic HBM bytes of one layer forward: router weights and bias,
+    every expert read once (codes + scales), tokens in and out."""
+    from int4_weight_expert_amd.moe import MOE_W_INT4_ROW  # noqa: F401
+    expert = 3 * cfg.H * cfg.I // 2 + 4 * (2 * cfg.I + cfg.H)
+    if cfg.fmt != 1:
+        expert = 3 * cfg.H * cfg.I // 2 + 12 * cfg.H * cfg.I // 64
+    return cfg.E * cfg.H * 4 + cfg.E * 4 + n_experts_read * expert + 2 * T * cfg.H * 4
+
+
+def gateup_unit_bytes(cfg) -> int:
+    """Algorithmic bytes of one expert's gate and up matrices (codes + scales)."""
+    if cfg.fmt == 1:
+        return 2 * (cfg.I * cfg.H // 2) + 2 * 4 * cfg.I
+    return 2 * (cfg.I * cfg.H // 2) + 2 * 4 * cfg.I * (cfg.H // 64)
+
+
+def time_graph(torch, ml, step_fns, steps: int, warmup: int):
+    """Captures the step functions (one per layer) into a HIP graph, checks a
+    replay against eager results, then times `steps` steps by replays."""
+    from int4_weight_expert_amd import moe as M
+    L = len(step_fns)
+    for i in range(warmup):
+        step_fns[i % L]()
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    M.moe_set_stream(ml.ctx, cap.cuda_stream)
+    try:
+        with torch.cuda.graph(g, stream=cap):
+            for fn in step_fns:
+                fn()
+    finally:
+        M.moe_set_stream(ml.ctx, torch.cuda.current_stream().cuda_stream)
+    reps = max(1, steps // L)
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    return g, dt / (reps * L), reps * L
+
+
+def time_eager(torch, step_fns, steps: int):
+    L = len(step_fns)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step_fns[i % L]()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def kernel_times(torch, ml, step_fns, steps: int):
+    """Average per-kernel durations (HIP events on the context's stream) over
+    `steps` eager steps; a short GPU sleep first lets the host queue run
+    ahead so that the events bracket kernels, not host gaps."""
+    from int4_weight_expert_amd import moe as M
+    L = len(step_fns)
+    torch.cuda.synchronize()
+    M.moe_set_timing(ml.ctx, True)
+    torch.cuda._sleep(50_000_000)
+    for i in range(steps):
+        step_fns[i % L]()
+    summary, nf = M.moe_timing_summary(ml.ctx)
+    M.moe_set_timing(ml.ctx, False)
+    torch.cuda.synchronize()
+    return dict(summary), nf
+
+
+def bench_decode(torch, args, result):
+    import synth
+    from int4_weight_expert_amd import workload
+    cfg = synth.CONFIGS["glm_decode"]
+    log(f"[bench] building {cfg.name}: {cfg.n_layers} layers x {cfg.E} experts")
+    ml = workload.build_layer(cfg, max_tokens=8)
+    L = cfg.n_layers
+    xs = [workload.tokens_device(cfg, T=1, stream=l) for l in range(L)]
+    outs = [torch.empty_like(x) for x in xs]
+    fns = [(lambda l=l: ml.forward(xs[l], l, outs[l])) for l in range(L)]
+    eager_ref = []
+    for l in range(L):
+        fns[l]()
+        eager_ref.append(outs[l].clone())
+    g, t_graph, n_timed = time_graph(torch, ml, fns, args.steps, args.warmup)
+    graph_ok = all(torch.equal(outs[l], eager_ref[l]) for l in range(L))
+    g.replay()
+    torch.cuda.synchronize()
+    graph_ok = graph_ok and all(torch.equal(outs[l], eager_ref[l]) for l in range(L))
+    t_eager = time_eager(torch, fns, args.steps)
+    kt, nf = kernel_times(torch, ml, fns, args.steps)
+    rc, missing = ml.status()
+    if rc != 0:
+        raise RuntimeError(f"status {rc} {missing}")
+    t_step = t_graph if graph_ok else t_eager
+    n_gateup = cfg.K + cfg.n_shared
+    alg_gateup = n_gateup * gateup_unit_bytes(cfg)
+    t_gu = kt["gateup_gemv"] * 1e-3
+    layer_bytes = glm_bytes(cfg, cfg.K + cfg.n_shared, 1)
+    result.update({
+        "metric": "MoE-FFN tokens/s (GLM-shape layer, T=1 decode)",
+        "value": 1.0 / t_step,
+        "unit": "tokens/s",
+        "ms_per_step": t_step * 1e3,
+        "steps": n_timed,
+        "roofline": {
+            "bound": "hbm", "achieved": alg_gateup / t_gu / 1e9, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": alg_gateup / t_gu / 1e9 / HBM_PEAK_GBS, "traffic": None,
+            "kernel": "k_gateup (fused int4 gate/up GEMV + SiLU*up)",
+            "algorithmic_bytes_per_launch": alg_gateup,
+            "avg_launch_ms": kt["gateup_gemv"],
+        },
+    })
+    result["extra"]["glm_decode"] = {
+        "us_per_layer_graph": t_graph * 1e6, "us_per_layer_eager": t_eager * 1e6,
+        "graph_replay_matches_eager": graph_ok,
+        "layer_algorithmic_bytes": layer_bytes,
+        "layer_gbps": layer_bytes / t_step / 1e9,
+        "layer_frac_hbm_peak": layer_bytes / t_step / 1e9 / HBM_PEAK_GBS,
+        "kernel_avg_ms": kt, "kernel_timing_forwards": nf,
+    }
+    log(f"[bench] glm_decode: {t_step * 1e6:.1f} us/layer (graph {t_graph * 1e6:.1f}, eager "
+        f"{t_eager * 1e6:.1f}); kernels {kt}")
+    ml.close()
+    del ml, xs, outs
+    torch.cuda.empty_cache()
+
+
+def bench_chain(torch, name, steps, result):
+    """Chained residual layers (x <- x + moe(rmsnorm(x))): per-layer time."""
+    import numpy as np
+    import synth
+    from int4_weight_expert_amd import workload
+    cfg = synth.CONFIGS[name]
+    log(f"[bench] building {name}: {cfg.n_layers} layers x {cfg.E} experts, T={cfg.T}")
+    ml = workload.build_layer(cfg)
+    L = cfg.n_layers
+    x0 = workload.tokens_device(cfg, T=cfg.T)
+    x = x0.clone()
+    distinct = []
+    for l in range(L):      # routing of the chain, for the byte count
+        ids, _ = ml.route(x, l)
+        distinct.append(len(np.unique(ids.cpu().numpy())))
+        ml.forward_residual(x, l)
+    fns = [(lambda l=l: ml.forward_residual(x, l)) for l in range(L)]
+    reps = max(1, steps // L)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        x.copy_(x0)
+        for fn in fns:
+            fn()
+    torch.cuda.synchronize()
+    t_eager = (time.perf_counter() - t0) / (reps * L)
+    x.copy_(x0)
+    g, t_graph, _ = time_graph(torch, ml, fns, reps * L, 0)
+    t = t_graph
+    bytes_layer = float(np.mean([glm_bytes(cfg, u + cfg.n_shared, cfg.T) for u in distinct]))
+    result["extra"][name] = {
+        "T": cfg.T, "layers": L, "us_per_layer": t * 1e6, "us_per_layer_eager": t_eager * 1e6,
+        "us_per_step_all_layers": t * L * 1e6, "tokens_per_s_per_layer": cfg.T / t,
+        "distinct_experts_per_layer": distinct,
+        "layer_algorithmic_bytes_mean": bytes_layer,
+        "layer_gbps": bytes_layer / t / 1e9, "layer_frac_hbm_peak": bytes_layer / t / 1e9 / HBM_PEAK_GBS,
+    }
+    log(f"[bench] {name}: {t * 1e6:.1f} us/layer (eager {t_eager * 1e6:.1f}), "
+        f"{bytes_layer / t / 1e9:.0f} GB/s")
+    ml.close()
+    del ml
+    torch.cuda.empty_cache()
+
+
+def bench_prefill(torch, steps, result):
+    import numpy as np
+    import synth
+    from int4_weight_expert_amd import workload
+    cfg = synth.CONFIGS["glm_prefill"]
+    log(f"[bench] building glm_prefill: T={cfg.T}")
+    ml = workload.build_layer(cfg)
+    x = workload.tokens_device(cfg)
+    out = torch.empty_like(x)
+    ids, _ = ml.route(x, 0)
+    distinct = len(np.unique(ids.cpu().numpy()))
+    ml.forward(x, 0, out)
+    torch.cuda.synchronize()
+    n = max(2, steps)
+    t0 = time.perf_counter()
+    for _ in range(n):
+        ml.forward(x, 0, out)
+    torch.cuda.synchronize()
+    t = (time.perf_counter() - t0) / n
+    kt, _ = kernel_times(torch, ml, [lambda: ml.forward(x, 0, out)], 3)
+    flops = 2.0 * (cfg.T * cfg.K + cfg.T * cfg.n_shared) * 3 * cfg.H * cfg.I
+    result["extra"]["glm_prefill"] = {
+        "T": cfg.T, "ms_per_layer": t * 1e3, "tokens_per_s": cfg.T / t,
+        "expert_flops": flops, "tflops": flops / t / 1e12,
+        "frac_fp16_mfma_peak": flops / t / 1e12 / BF16_PEAK_TFLOPS,
+        "distinct_experts": distinct, "kernel_avg_ms": kt,
+    }
+    log(f"[bench] glm_prefill: {t * 1e3:.2f} ms/layer, {flops / t / 1e12:.1f} TFLOP/s; {kt}")
+    ml.close()
+    del ml
+    torch.cuda.empty_cache()
+
+
+def cpu_baseline(n_tok: int):
+    """The oracle, as it stands, on a bounded sample of the decode workload:
+    n_tok token-layers (T=1) of the 8-layer GLM decode, single-threaded, with
+    the experts they select packed beforehand (not timed)."""
+    import numpy as np
+    import oracle
+    import synth
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from parity import OracleLayer
+    cfg = synth.CONFIGS["glm_decode"]
+    per = max(1, n_tok // cfg.n_layers)
+    jobs = []
+    for l in range(cfg.n_layers):
+        ref = OracleLayer(cfg, l)
+        x = synth.tokens(cfg, T=per, stream=1000 + l)
+        ids, *_ = ref.route(x)
+        ref.need(ids)
+        jobs.append((ref, x))
+    t0 = time.perf_counter()
+    n = 0
+    for ref, x in jobs:
+        blobs = [ref.cache.get(e) for e in range(cfg.E)]
+        for t in range(x.shape[0]):
+            oracle.moe_layer(x[t:t + 1], ref.W, ref.b, cfg.K, cfg.fmt, cfg.I, blobs, ref.shared)
+            n += 1
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} token-layers (T=1) of the 8-layer GLM decode workload "
+                      f"({per} tokens per layer), single-threaded C oracle, fp64 accumulate; "
+                      f"expert packing excluded; {dt:.1f} s",
+            "host_cpu": _cpu_model(), "host_nproc": os.cpu_count()}
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--no-extra", action="store_true", help="only the decode workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-tokens", type=int, default=16)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this build "
+              f"has no multi-GPU path; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    result = {
+        "metric": None, "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "glm_decode: GLM-5.2-shape MoE layer, H=6144, E=256, top-8, "
+                               "I=2048, 1 shared expert, int4 per-row scale, T=1, 8 resident "
+                               "layers rotated", "global_batch": 1, "seq_len": 1,
+                   "parallelism": "none (1 GPU)", "weights": "int4 (fp32 row scales)",
+                   "activations": "fp32"},
+        "extra": {},
+    }
+    bench_decode(torch, args, result)
+    if not args.no_extra:
+        bench_chain(torch, "glm_verify", 64, result)
+        bench_chain(torch, "edge0_decode", 200, result)
+        bench_chain(torch, "edge0_decode_k8", 200, result)
+        bench_prefill(torch, 3, result)
+    if not args.no_cpu:
+        log("[bench] cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

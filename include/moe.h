@@ -165,19 +165,28 @@ int moe_route(moe_ctx *ctx, const float *x, int T, int layer, int32_t *ids, floa
  * MOE_OK.  Clears the device status.  missing_ids/n_missing may be null. */
 int moe_status(moe_ctx *ctx, int32_t *missing_ids, int cap, int *n_missing);
 
+/* Description of the last HIP error a call of this context hit (the cause
+ * of its MOE_E_HIP), or "" if none; a static string. */
+const char *moe_last_error(moe_ctx *ctx);
+
 /* Which path moe_forward takes: tokens at or above this count use the MFMA
  * grouped GEMM (row format only), below it the int4 GEMV kernels.
  * Default 64.  0 restores the default. */
 int moe_set_gemm_min_tokens(moe_ctx *ctx, int min_tokens);
 
-/* Duration in milliseconds of the kernels of the last moe_forward (or
- * moe_forward_residual, moe_route), measured with HIP events on the
- * context's stream when timing is on.  Synchronises.  ms[i] receives
- * kernel i's duration in launch order; *n receives the kernel count and
- * names[i] (optional) a static string naming it.  Timing adds events
- * between kernels; leave it off for production.  Errors: MOE_E_ARG. */
+/* Per-kernel timing with HIP events on the context's stream.  While timing
+ * is on, every moe_forward / moe_forward_residual / moe_route records an
+ * event before each of its kernels and one after the last.
+ * moe_timing_summary synchronises on the last event and returns, for each
+ * kernel name in launch order, the average duration in milliseconds over
+ * the forwards recorded since timing was switched on (or since the last
+ * summary), then clears the record.  ms[i] and names[i] (static strings)
+ * receive up to cap entries, *n their count, *n_forwards (optional) the
+ * number of forwards averaged.  Timing adds event packets between kernels;
+ * leave it off in production.  Errors: MOE_E_ARG, MOE_E_HIP. */
 int moe_set_timing(moe_ctx *ctx, int on);
-int moe_last_timings(moe_ctx *ctx, float *ms, const char **names, int cap, int *n);
+int moe_timing_summary(moe_ctx *ctx, float *ms, const char **names, int cap, int *n,
+                       int *n_forwards);
 
 /* --- stand-alone steps, for callers that quantise or bucket themselves --- */
 

@@ -306,7 +306,11 @@ __global__ void __launch_bounds__(1024) k_bucket(const int32_t* __restrict__ ids
         g.expert = -1;
         f.groups[tid] = g;
     }
-    if (tid == 0) f.n_groups[0] = f.n_shared + s_nact;
+    if (tid == 0) {
+        f.n_groups[0] = f.n_shared + s_nact;
+        __hip_atomic_store(&f.queues[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&f.queues[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 hipError_t launch_router_large(const Fwd& f, hipStream_t st, int stage)

@@ -31,6 +31,7 @@ struct moe_ctx {
     uint8_t* staging = nullptr;
     // workspace
     float* part = nullptr;
+    float* tpart = nullptr;
     float* logits = nullptr;
     int32_t* ids = nullptr;
     float* wts = nullptr;
@@ -45,15 +46,23 @@ struct moe_ctx {
     int32_t* n_groups = nullptr;
     float* h = nullptr;
     float* hgs = nullptr;
-    float* ystage = nullptr;
+    float* gu_part = nullptr;
+    size_t gu_part_bytes = 0;
+    float* dn_part = nullptr;
+    size_t dn_part_bytes = 0;
+    uint32_t* gu_ctr = nullptr;
+    uint32_t* dn_ctr = nullptr;
+    uint32_t* queues = nullptr;
     uint32_t* counters = nullptr;
     uint32_t* status = nullptr;
     size_t status_words = 0;
     int gemm_min_tokens = 64;
+    int lds_max = 65536;
+    hipError_t last_err = hipSuccess;
     // timing
     bool timing = false;
-    std::vector<hipEvent_t> events;
-    std::vector<const char*> names;
+    std::vector<hipEvent_t> events;  // pool, reused after each summary
+    std::vector<const char*> names;  // per mark; nullptr = end of a forward
     int n_marks = 0;
     std::vector<void*> allocs;
 };
@@ -63,6 +72,13 @@ namespace {
 constexpr int kDefaultGemmMin = 64;
 
 int hip_ok(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_E_HIP; }
+
+// records a failing HIP call for moe_last_error
+int hip_rc(moe_ctx* c, hipError_t e)
+{
+    if (e != hipSuccess) c->last_err = e;
+    return hip_ok(e);
+}
 
 template <typename P>
 int dalloc(moe_ctx* c, P** p, size_t bytes)
@@ -83,15 +99,53 @@ size_t expert_bytes_for(int fmt, size_t H, size_t I)
     return 0;
 }
 
+// Partial rows of the small-T router: one per workgroup row of RW slices of
+// 64 input columns (RW = 8 wavefronts, or 4 when H/64 is not a multiple of 8)
 int router_slices(int H)
 {
-    // K-slices of the small-T router: a multiple of 4 dividing H/4, with at
-    // least 16 float4 chunks per slice, at most 64 slices
-    const int CH = H / 4;
-    int best = 4;
-    for (int s = 4; s <= 64; s += 4)
-        if (CH % s == 0 && CH / s >= 16) best = s;
-    return best;
+    const int slices = H / 64;
+    return slices / (slices % 8 == 0 ? 8 : 4);
+}
+
+// Largest chunks-per-slice from the preferred list that divides the row's
+// chunk count (all even, as the affine format needs whole 64-input groups).
+int pick_cpu(int chunks, const int* prefs, int n)
+{
+    for (int i = 0; i < n; ++i)
+        if (chunks % prefs[i] == 0) return prefs[i];
+    return chunks;
+}
+
+// Work plan of the persistent GEMVs for T tokens: k-slices per row block,
+// limited by the partial buffers.
+void plan_gemv(moe_ctx* c, Fwd& f)
+{
+    const moe_config& g = c->cfg;
+    const size_t rows = (size_t)f.T * g.top_k + (size_t)f.T * g.n_shared;
+    static const int gu_prefs[] = {16, 8, 12, 6, 4, 2};
+    static const int dn_prefs[] = {16, 8, 4, 2};
+    const int gc = g.hidden / 32, dc = g.inter / 32;
+    f.gu_cpu = pick_cpu(gc, gu_prefs, 6);
+    f.gu_ks = gc / f.gu_cpu;
+    if (rows * g.inter * 2 * 4 * f.gu_ks > c->gu_part_bytes) {
+        f.gu_ks = 1;
+        f.gu_cpu = gc;
+    }
+    f.dn_cpu = pick_cpu(dc, dn_prefs, 4);
+    f.dn_ks = dc / f.dn_cpu;
+    while (f.dn_ks > 1 && rows * g.hidden * 4 * f.dn_ks > c->dn_part_bytes) {
+        // fewer, longer slices: double the chunks per slice while it divides
+        if ((dc / f.dn_ks) * 2 <= dc && f.dn_ks % 2 == 0) {
+            f.dn_ks /= 2;
+            f.dn_cpu *= 2;
+        } else {
+            f.dn_ks = 1;
+            f.dn_cpu = dc;
+        }
+    }
+    const int max_groups = g.n_shared + std::min(g.n_experts, f.T * g.top_k);
+    f.gu_grid = (max_groups * (g.inter / 64) * f.gu_ks + 3) / 4;
+    f.dn_grid = (max_groups * (g.hidden / 64) * f.dn_ks + 3) / 4;
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb)
@@ -110,8 +164,7 @@ void mark(moe_ctx* c, const char* name)
         c->names.push_back(nullptr);
     }
     c->names[c->n_marks] = name;
-    hipEventRecord(c->events[c->n_marks], c->stream);
-    c->n_marks++;
+    if (hipEventRecord(c->events[c->n_marks], c->stream) == hipSuccess) c->n_marks++;
 }
 
 Fwd make_fwd(moe_ctx* c, const float* x, float* out, int T, int layer, int residual)
@@ -140,6 +193,7 @@ Fwd make_fwd(moe_ctx* c, const float* x, float* out, int T, int layer, int resid
     f.slot_bytes = c->slot_bytes;
     f.shared = c->shared + (size_t)layer * g.n_shared * c->slot_bytes;
     f.part = c->part;
+    f.tpart = c->tpart;
     f.S = router_slices(g.hidden);
     f.logits = c->logits;
     f.ids = c->ids;
@@ -155,10 +209,15 @@ Fwd make_fwd(moe_ctx* c, const float* x, float* out, int T, int layer, int resid
     f.n_groups = c->n_groups;
     f.h = c->h;
     f.hgs = c->hgs;
-    f.ystage = c->ystage;
+    f.gu_part = c->gu_part;
+    f.dn_part = c->dn_part;
+    f.gu_ctr = c->gu_ctr;
+    f.dn_ctr = c->dn_ctr;
+    f.queues = c->queues;
     f.counters = c->counters;
     f.status = c->status;
     f.n_layers = g.n_layers;
+    f.lds_max = c->lds_max;
     return f;
 }
 
@@ -168,15 +227,13 @@ int run_router(moe_ctx* c, const Fwd& f)
     hipError_t e;
     if (f.T <= ROUTER_SMALL_MAX_T) {
         mark(c, "router_topk_bucket");
-        e = launch_router_small(f, c->stream);
-        if (e != hipSuccess) return MOE_E_HIP;
-        return MOE_OK;
+        return hip_rc(c, launch_router_small(f, c->stream));
     }
     static const char* names[4] = {"token_stats", "router_gemm", "topk", "bucket"};
     for (int s = 0; s < 4; ++s) {
         mark(c, names[s]);
         e = launch_router_large(f, c->stream, s);
-        if (e != hipSuccess) return MOE_E_HIP;
+        if (e != hipSuccess) return hip_rc(c, e);
     }
     return MOE_OK;
 }
@@ -188,16 +245,17 @@ int run_forward(moe_ctx* c, const float* x, int T, int layer, float* out, int re
     if (T < 1 || T > g.max_tokens || layer < 0 || layer >= g.n_layers) return MOE_E_ARG;
     const size_t nb = (size_t)T * g.hidden * sizeof(float);
     if (!residual && overlaps(x, nb, out, nb)) return MOE_E_ARG;
-    c->n_marks = 0;
     Fwd f = make_fwd(c, x, out, T, layer, residual);
+    plan_gemv(c, f);
     int rc = run_router(c, f);
     if (rc) return rc;
-    const int max_groups = g.n_shared + std::min(g.n_experts, T * g.top_k);
     mark(c, "gateup_gemv");
-    if (launch_gateup_gemv(f, max_groups, c->stream) != hipSuccess) return MOE_E_HIP;
+    rc = hip_rc(c, launch_gateup_gemv(f, c->stream));
+    if (rc) return rc;
     mark(c, "down_gemv_combine");
-    if (launch_down_gemv(f, max_groups, c->stream) != hipSuccess) return MOE_E_HIP;
-    mark(c, "end");
+    rc = hip_rc(c, launch_down_gemv(f, c->stream));
+    if (rc) return rc;
+    mark(c, nullptr);
     return MOE_OK;
 }
 
@@ -254,7 +312,8 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
     if (g.n_group != 1 || g.topk_group != 1) return MOE_E_UNSUPPORTED;
     if (g.n_experts > 256 || g.top_k > 8 || g.top_k > g.n_experts || g.n_shared > 1)
         return MOE_E_UNSUPPORTED;
-    if (g.hidden % 256 || g.inter % 256) return MOE_E_UNSUPPORTED;
+    if (g.hidden % 256 || g.inter % 256 || g.hidden > 16384) return MOE_E_UNSUPPORTED;
+    if (g.wfmt == MOE_W_INT4_AFFINE_G64 && g.hidden % 512) return MOE_E_UNSUPPORTED;
     if ((size_t)g.max_tokens * g.top_k > 65536) return MOE_E_UNSUPPORTED;
 
     int dev = 0;
@@ -262,11 +321,16 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_E_HIP;
     if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MOE_E_HIP;
+    int lds_max = 65536;
+    if (hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+        hipSuccess)
+        lds_max = 65536;
 
     moe_ctx* c = new moe_ctx();
     c->cfg = g;
     c->stream = (hipStream_t)stream;
     c->device = dev;
+    c->lds_max = lds_max;
     c->slot_bytes = expert_bytes_for(g.wfmt, g.hidden, g.inter);
     c->Epad = (g.n_experts + 63) / 64 * 64;
     const size_t H = g.hidden, I = g.inter, E = g.n_experts, L = g.n_layers, Tm = g.max_tokens;
@@ -278,7 +342,8 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
     rc = rc ? rc : dalloc(c, &c->tbl, L * E * 4);
     rc = rc ? rc : dalloc(c, &c->shared, L * g.n_shared * c->slot_bytes);
     rc = rc ? rc : dalloc(c, &c->staging, c->slot_bytes);
-    rc = rc ? rc : dalloc(c, &c->part, (size_t)64 * ROUTER_SMALL_MAX_T * c->Epad * 4);
+    rc = rc ? rc : dalloc(c, &c->part, (H / 64) * ROUTER_SMALL_MAX_T * c->Epad * 4);
+    rc = rc ? rc : dalloc(c, &c->tpart, (H / 64) * ROUTER_SMALL_MAX_T * 2 * 4);
     rc = rc ? rc : dalloc(c, &c->logits, Tm * c->Epad * 4);
     rc = rc ? rc : dalloc(c, &c->ids, Tm * K * 4);
     rc = rc ? rc : dalloc(c, &c->wts, Tm * K * 4);
@@ -293,7 +358,17 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
     rc = rc ? rc : dalloc(c, &c->n_groups, 4);
     rc = rc ? rc : dalloc(c, &c->h, rows * I * 4);
     rc = rc ? rc : dalloc(c, &c->hgs, rows * (I / 64) * 4);
-    rc = rc ? rc : dalloc(c, &c->ystage, rows * H * 4);
+    {
+        // partial buffers of the persistent GEMVs: k-split for up to 64 tokens
+        const size_t r64 = std::min<size_t>(Tm, 64) * (K + g.n_shared);
+        c->gu_part_bytes = r64 * I * 2 * 4 * 16;
+        c->dn_part_bytes = std::max(rows * H * 4, r64 * H * 4 * 4);
+    }
+    rc = rc ? rc : dalloc(c, &c->gu_part, c->gu_part_bytes);
+    rc = rc ? rc : dalloc(c, &c->dn_part, c->dn_part_bytes);
+    rc = rc ? rc : dalloc(c, &c->gu_ctr, (E + g.n_shared) * (I / 64) * 4);
+    rc = rc ? rc : dalloc(c, &c->dn_ctr, (H / 64) * 4);
+    rc = rc ? rc : dalloc(c, &c->queues, 2 * 4);
     rc = rc ? rc : dalloc(c, &c->counters, (1 + H / 64) * 4);
     c->status_words = 1 + (L * E + 31) / 32;
     rc = rc ? rc : dalloc(c, &c->status, c->status_words * 4);
@@ -301,6 +376,9 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
         c->tbl_host.assign(L * E, -1);
         hipError_t e = hipMemcpy(c->tbl, c->tbl_host.data(), L * E * 4, hipMemcpyHostToDevice);
         if (e == hipSuccess) e = hipMemset(c->counters, 0, (1 + H / 64) * 4);
+        if (e == hipSuccess) e = hipMemset(c->gu_ctr, 0, (E + g.n_shared) * (I / 64) * 4);
+        if (e == hipSuccess) e = hipMemset(c->dn_ctr, 0, (H / 64) * 4);
+        if (e == hipSuccess) e = hipMemset(c->queues, 0, 2 * 4);
         if (e == hipSuccess) e = hipMemset(c->status, 0, c->status_words * 4);
         if (e == hipSuccess) e = hipMemset(c->bias, 0, L * E * 4);
         if (e == hipSuccess) e = hipMemset(c->wr, 0, L * c->Epad * H * 4);
@@ -422,11 +500,11 @@ int moe_route(moe_ctx* c, const float* x, int T, int layer, int32_t* ids, float*
     if (!c || !x || !ids || !w) return MOE_E_ARG;
     const moe_config& g = c->cfg;
     if (T < 1 || T > g.max_tokens || layer < 0 || layer >= g.n_layers) return MOE_E_ARG;
-    c->n_marks = 0;
     Fwd f = make_fwd(c, x, nullptr, T, layer, 0);
+    plan_gemv(c, f);
     int rc = run_router(c, f);
     if (rc) return rc;
-    mark(c, "end");
+    mark(c, nullptr);
     const size_t n = (size_t)T * g.top_k;
     hipError_t e = hipMemcpyAsync(ids, c->ids, n * 4, hipMemcpyDeviceToDevice, c->stream);
     if (e == hipSuccess) e = hipMemcpyAsync(w, c->wts, n * 4, hipMemcpyDeviceToDevice, c->stream);
@@ -456,6 +534,12 @@ int moe_status(moe_ctx* c, int32_t* missing, int cap, int* n_missing)
     return MOE_OK;
 }
 
+const char* moe_last_error(moe_ctx* c)
+{
+    if (!c) return "null context";
+    return c->last_err == hipSuccess ? "" : hipGetErrorString(c->last_err);
+}
+
 int moe_set_gemm_min_tokens(moe_ctx* c, int min_tokens)
 {
     if (!c || min_tokens < 0) return MOE_E_ARG;
@@ -467,25 +551,47 @@ int moe_set_timing(moe_ctx* c, int on)
 {
     if (!c) return MOE_E_ARG;
     c->timing = on != 0;
+    c->n_marks = 0;
     return MOE_OK;
 }
 
-int moe_last_timings(moe_ctx* c, float* ms, const char** names, int cap, int* n)
+int moe_timing_summary(moe_ctx* c, float* ms, const char** names, int cap, int* n,
+                       int* n_forwards)
 {
     if (!c || !n) return MOE_E_ARG;
-    if (!c->timing || c->n_marks < 2) {
-        *n = 0;
+    *n = 0;
+    if (n_forwards) *n_forwards = 0;
+    if (c->n_marks < 2) {
+        c->n_marks = 0;
         return MOE_OK;
     }
     if (hipEventSynchronize(c->events[c->n_marks - 1]) != hipSuccess) return MOE_E_HIP;
-    const int k = c->n_marks - 1;
-    for (int i = 0; i < k && i < cap; ++i) {
+    std::vector<const char*> order;
+    std::vector<double> sum;
+    std::vector<int> count;
+    int forwards = 0;
+    for (int i = 0; i + 1 < c->n_marks; ++i) {
+        if (c->names[i] == nullptr) continue;  // end mark of a forward
         float v = 0.f;
         if (hipEventElapsedTime(&v, c->events[i], c->events[i + 1]) != hipSuccess) return MOE_E_HIP;
-        if (ms) ms[i] = v;
-        if (names) names[i] = c->names[i];
+        size_t k = 0;
+        while (k < order.size() && strcmp(order[k], c->names[i]) != 0) ++k;
+        if (k == order.size()) {
+            order.push_back(c->names[i]);
+            sum.push_back(0.0);
+            count.push_back(0);
+        }
+        sum[k] += v;
+        count[k] += 1;
+        if (c->names[i + 1] == nullptr) ++forwards;
     }
-    *n = k;
+    for (size_t k = 0; k < order.size() && (int)k < cap; ++k) {
+        if (ms) ms[k] = (float)(sum[k] / count[k]);
+        if (names) names[k] = order[k];
+    }
+    *n = (int)std::min(order.size(), (size_t)cap);
+    if (n_forwards) *n_forwards = forwards;
+    c->n_marks = 0;
     return MOE_OK;
 }
 

@@ -59,7 +59,8 @@ struct Fwd {
     const uint8_t* shared;  // n_shared shared experts of this layer (slot layout)
     // workspace
     float* part;          // small-T router partial logits [S][T][Epad]
-    int S;                // router K-slices
+    float* tpart;         // small-T router partial token sums [S][T][2] (sum, sum of squares)
+    int S;                // router K-slices of 64 columns (S = H/64)
     float* logits;        // [T][Epad] (large-T router)
     int32_t* ids;         // [T][K]
     float* wts;           // [T][K]
@@ -73,11 +74,20 @@ struct Fwd {
     Group* groups;        // [n_shared + E]
     int32_t* n_groups;    // [1]
     float* h;             // [T*K + T*n_shared][I]
-    float* hgs;           // [rows][I/64]
-    float* ystage;        // [rows][H]
-    uint32_t* counters;   // [1 + H/64]: router arrivals, then per row block
+    float* hgs;           // [rows][I/64] (unused by the current kernels)
+    uint32_t* counters;   // [0]: router arrivals
     uint32_t* status;     // [0] flags, [1..] missing bitmap over layer*E+id
     int n_layers;
+    int lds_max;          // device LDS bytes per workgroup
+    // persistent GEMV work plan (see k_gemv.hip)
+    int gu_ks, gu_cpu;    // gate/up: k-slices per 64-row block, 16-byte chunks per slice
+    int dn_ks, dn_cpu;    // down: same
+    int gu_grid, dn_grid; // persistent workgroups launched
+    float* gu_part;       // [rows][I/64][gu_ks][2][64] when gu_ks > 1
+    float* dn_part;       // [rows][H/64][dn_ks][64]
+    uint32_t* gu_ctr;     // [(n_shared + E) * I/64] arrivals per (group, row block)
+    uint32_t* dn_ctr;     // [H/64] arrivals per row block
+    uint32_t* queues;     // [2] work counters of the two GEMV kernels, zeroed by the router
 };
 
 enum { STATUS_NOT_RESIDENT = 1u, STATUS_RANGE = 2u };
@@ -99,8 +109,9 @@ hipError_t launch_bucket(const int32_t* ids, int T, int K, int E, int32_t* cnt, 
 // forward pieces; `names` receives static kernel names for timing
 hipError_t launch_router_small(const Fwd& f, hipStream_t st);
 hipError_t launch_router_large(const Fwd& f, hipStream_t st, int stage);
-hipError_t launch_gateup_gemv(const Fwd& f, int max_groups, hipStream_t st);
-hipError_t launch_down_gemv(const Fwd& f, int max_groups, hipStream_t st);
+hipError_t launch_gateup_gemv(const Fwd& f, hipStream_t st);
+hipError_t launch_down_gemv(const Fwd& f, hipStream_t st);
+int gemv_grid(int which, int fmt, int T, int num_cu);
 
 constexpr int ROUTER_SMALL_MAX_T = 16;
 

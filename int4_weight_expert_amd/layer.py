@@ -69,19 +69,20 @@ class MoeLayer:
         T = x.shape[0]
         if out is None:
             out = torch.empty_like(x)
-        M._check("moe_forward", M.moe_forward(self.ctx, x, T, layer, out))
+        M._check("moe_forward", M.moe_forward(self.ctx, x, T, layer, out), self.ctx)
         return out
 
     def forward_residual(self, x: torch.Tensor, layer: int) -> torch.Tensor:
         assert x.is_cuda and x.dtype == torch.float32 and x.is_contiguous()
-        M._check("moe_forward_residual", M.moe_forward_residual(self.ctx, x, x.shape[0], layer))
+        M._check("moe_forward_residual", M.moe_forward_residual(self.ctx, x, x.shape[0], layer),
+                 self.ctx)
         return x
 
     def route(self, x: torch.Tensor, layer: int):
         T = x.shape[0]
         ids = torch.empty((T, self.K), dtype=torch.int32, device=x.device)
         w = torch.empty((T, self.K), dtype=torch.float32, device=x.device)
-        M._check("moe_route", M.moe_route(self.ctx, x, T, layer, ids, w))
+        M._check("moe_route", M.moe_route(self.ctx, x, T, layer, ids, w), self.ctx)
         return ids, w
 
     def status(self):

@@ -33,7 +33,7 @@ EXPORTS = ["moe_layer_create", "moe_destroy", "moe_set_stream", "moe_expert_byte
            "moe_set_router", "moe_load_expert", "moe_pack_expert", "moe_set_shared",
            "moe_pack_shared", "moe_map_expert", "moe_read_slot", "moe_forward",
            "moe_forward_residual", "moe_route", "moe_status", "moe_set_gemm_min_tokens",
-           "moe_set_timing", "moe_last_timings", "moe_pack_int4_rows", "moe_pack_affine_g64",
+           "moe_set_timing", "moe_timing_summary", "moe_last_error", "moe_pack_int4_rows", "moe_pack_affine_g64",
            "moe_bucket"]
 
 
@@ -81,7 +81,9 @@ def lib() -> ctypes.CDLL:
             "moe_status": ([vp, vp, i32, ctypes.POINTER(i32)], i32),
             "moe_set_gemm_min_tokens": ([vp, i32], i32),
             "moe_set_timing": ([vp, i32], i32),
-            "moe_last_timings": ([vp, vp, vp, i32, ctypes.POINTER(i32)], i32),
+            "moe_last_error": ([vp], ctypes.c_char_p),
+            "moe_timing_summary": ([vp, vp, vp, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)],
+                                   i32),
             "moe_pack_int4_rows": ([vp, i64, i64, vp, vp, vp], i32),
             "moe_pack_affine_g64": ([vp, i64, i64, vp, vp, vp], i32),
             "moe_bucket": ([vp, i32, i32, i32, vp, vp, vp, vp, vp, vp], i32),
@@ -106,10 +108,17 @@ def _ptr(t) -> int | None:
     raise TypeError(f"cannot pass {type(t)} as a pointer")
 
 
-def _check(fn: str, rc: int) -> int:
+def _check(fn: str, rc: int, ctx=None) -> int:
     if rc != MOE_OK:
-        raise MoeError(fn, rc)
+        err = MoeError(fn, rc)
+        if ctx and rc == MOE_E_HIP:
+            err.args = (f"{err.args[0]}: {moe_last_error(ctx)}",)
+        raise err
     return rc
+
+
+def moe_last_error(ctx) -> str:
+    return lib().moe_last_error(ctx).decode()
 
 
 def make_config(H, I, E, K, n_shared, n_layers, wfmt, n_slots, max_tokens, routed_scale=2.5,
@@ -197,12 +206,15 @@ def moe_set_timing(ctx, on: bool) -> int:
     return _check("moe_set_timing", lib().moe_set_timing(ctx, int(on)))
 
 
-def moe_last_timings(ctx, cap: int = 32) -> list[tuple[str, float]]:
+def moe_timing_summary(ctx, cap: int = 32) -> tuple[list[tuple[str, float]], int]:
+    """[(kernel name, average ms)], number of forwards averaged."""
     ms = (ctypes.c_float * cap)()
     names = (ctypes.c_char_p * cap)()
     n = ctypes.c_int(0)
-    _check("moe_last_timings", lib().moe_last_timings(ctx, ms, names, cap, ctypes.byref(n)))
-    return [(names[i].decode(), ms[i]) for i in range(min(n.value, cap))]
+    nf = ctypes.c_int(0)
+    _check("moe_timing_summary",
+           lib().moe_timing_summary(ctx, ms, names, cap, ctypes.byref(n), ctypes.byref(nf)))
+    return [(names[i].decode(), ms[i]) for i in range(min(n.value, cap))], nf.value
 
 
 def moe_pack_int4_rows(w, O, I, q, s, stream=0) -> int:

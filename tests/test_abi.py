@@ -12,7 +12,7 @@ HEADER = os.path.join(ROOT, "include", "moe.h")
 def declared_functions():
     src = open(HEADER, encoding="utf-8").read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    names = re.findall(r"^\s*(?:int|void|size_t)\s+\*?\s*(moe_\w+)\s*\(", src, flags=re.M)
+    names = re.findall(r"^\s*(?:int|void|size_t|const char)\s*\*?\s*(moe_\w+)\s*\(", src, flags=re.M)
     return sorted(set(names))
 
 

@@ -116,3 +116,30 @@ def test_load_expert_blob_path(layer, ref):
         assert torch.equal(a, b2)
     finally:
         ml.close()
+
+
+def test_graph_replay_matches_eager(layer):
+    """Forwards captured in a HIP graph: every replay, with eager work and
+    synchronisation between replays, equals the eager result."""
+    xs = [torch.from_numpy(synth.tokens(CFG, T=T, stream=30 + T)).cuda() for T in (1, 8)]
+    eager = [layer.forward(x, 0).clone() for x in xs]
+    outs = [torch.empty_like(x) for x in xs]
+    cap = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    M.moe_set_stream(layer.ctx, cap.cuda_stream)
+    try:
+        with torch.cuda.graph(g, stream=cap):
+            for x, o in zip(xs, outs):
+                M._check("moe_forward", M.moe_forward(layer.ctx, x, x.shape[0], 0, o))
+    finally:
+        M.moe_set_stream(layer.ctx, torch.cuda.current_stream().cuda_stream)
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o, e), rep
+        other = layer.forward(torch.from_numpy(synth.tokens(CFG, T=3, stream=99)).cuda(), 0)
+        torch.cuda.synchronize()
+        assert torch.isfinite(other).all()
