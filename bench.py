@@ -142,7 +142,7 @@ def bench_decode(torch, args, result):
         "roofline": {
             "bound": "hbm", "achieved": alg_gateup / t_gu / 1e9, "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": alg_gateup / t_gu / 1e9 / HBM_PEAK_GBS, "traffic": None,
-            "kernel": "k_gateup (fused int4 gate/up GEMV + SiLU*up)",
+            "kernel": "k_gu (int4 gate/up GEMV, one wavefront per (expert, 64-row block, k-slice))",
             "algorithmic_bytes_per_launch": alg_gateup,
             "avg_launch_ms": kt["gateup_gemv"],
         },

@@ -30,6 +30,13 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
 // Activations read by every lane at the same address, and read-only for the
 // whole kernel, go through the constant address space: scalar loads.
 typedef const __attribute__((address_space(4))) float cf32;
@@ -48,6 +55,11 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff
 {
     const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
     return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
 }
 
 // 8 codes of one dword against 8 activations read from LDS at a wave-uniform
@@ -74,6 +86,85 @@ __device__ __forceinline__ void dot32(const uint4& w, const float* xs, float& ae
     dot8(w.y, xs + 8, ae, ao);
     dot8(w.z, xs + 16, ae, ao);
     dot8(w.w, xs + 24, ae, ao);
+}
+
+// ---------------------------------------------------------------------------
+// fp16 dot path of the expert GEMVs.
+//
+// A dword of codes holds 8 nibbles n0..n7 (input i in bits 4i..4i+3).  Each
+// nibble is moved to bits 4..7 of an fp16 whose exponent field is that of
+// 1024 (0x6400): the half then reads exactly 1024 + 16 n.  One bit-field insert per
+// pair builds (n0,n4) (n1,n5) (n2,n6) (n3,n7), and v_dot2_f32_f16 multiplies
+// a pair with the matching pair of fp16 activations, accumulating in fp32.
+// Activations are staged once per forward in spans of 64 inputs: each span
+// is scaled by a power of two 2^k that puts its largest magnitude in
+// [2^13, 2^14) (exact, no overflow), rounded to fp16 and stored in pair
+// order, eight inputs per 16 bytes: x0 x4 x1 x5 x2 x6 x3 x7; beside it the
+// span keeps (2^-k, sum of its fp16 values).  Over a span,
+// sum (1024 + 16 n) x / 16 = sum n x + 64 sum x, and the kernels remove the
+// 64 sum x term (plus the code offset) with the span's stored sum, then
+// rescale by 2^-k.
+// ---------------------------------------------------------------------------
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+
+constexpr uint32_t NIB_MASK = 0x00F000F0u;
+
+// The magic exponent lives in a VGPR (gfx9 VOP3 takes no literal, and the
+// constant bus takes one SGPR: the mask).
+__device__ __forceinline__ uint32_t magic_vgpr()
+{
+    uint32_t r;
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(r));
+    return r;
+}
+
+__device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t a, uint32_t c)
+{
+    uint32_t r;
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "s"(mask), "v"(a), "v"(c));
+    return r;
+}
+
+// four fp16 pairs 1024 + 16 n of one dword of codes (v_bfi_b32 issues
+// faster than v_and_or_b32 on gfx950)
+__device__ __forceinline__ void nib_pairs(uint32_t w, uint32_t mv, uint32_t& p0, uint32_t& p1,
+                                          uint32_t& p2, uint32_t& p3)
+{
+    p0 = bfi(NIB_MASK, w << 4, mv);
+    p1 = bfi(NIB_MASK, w, mv);
+    p2 = bfi(NIB_MASK, w >> 4, mv);
+    p3 = bfi(NIB_MASK, w >> 8, mv);
+}
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, a), __builtin_bit_cast(h2_t, b), c,
+                                  false);
+}
+
+__device__ __forceinline__ uint32_t pack_h2(_Float16 lo, _Float16 hi)
+{
+    h2_t v;
+    v.x = lo;
+    v.y = hi;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Stages one span of 64 activations held one per lane (lane i = input i):
+// q16 receives the 64 fp16 values in pair order, *sc = (2^-k, sum).
+__device__ __forceinline__ void stage_span64(float v, int lane, uint16_t* __restrict__ q16,
+                                             float2* __restrict__ sc)
+{
+    const float m = wave_max(fabsf(v));
+    int e;
+    frexpf(m, &e);  // m = f 2^e, f in [0.5, 1)
+    e = max(e, -100);
+    const _Float16 h = (_Float16)(v * ldexpf(1.0f, 14 - e));
+    const float t = wave_sum((float)h);
+    const int g = lane >> 3, p = lane & 7;
+    q16[g * 8 + (p < 4 ? 2 * p : 2 * p - 7)] = __builtin_bit_cast(uint16_t, h);
+    if (lane == 0) *sc = make_float2(ldexpf(1.0f, e - 14), t);
 }
 
 // Data handed between workgroups of one kernel travels with agent-scope
@@ -124,14 +215,33 @@ __device__ __forceinline__ bool arrive_wave(uint32_t* counter, uint32_t expected
     return last;
 }
 
+// Wave-uniform copies (SGPRs) of values the compiler cannot prove uniform:
+// group descriptors and token indices read from memory by every lane.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ Group uni_group(const Group* __restrict__ GR, int gi)
+{
+    const Group g = GR[gi];
+    Group u;
+    const uint64_t p = (uint64_t)(uintptr_t)g.base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+    u.base = (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+    u.cnt = uni(g.cnt);
+    u.off = uni(g.off);
+    u.kind = uni(g.kind);
+    u.expert = uni(g.expert);
+    return u;
+}
+
 // Token j of an expert group: its token index t and its row r in h and in
-// the down partials (routed assignment a = t*K + k uses row a; shared
-// expert s uses T*K + s*T + t).
+// the expert outputs (routed assignment a = t*K + k uses row a; shared
+// expert s uses T*K + s*T + t).  Wave-uniform.
 __device__ __forceinline__ void tok_rows(const Fwd& f, const int32_t* __restrict__ perm,
                                          const Group& g, int j, int& t, int& r)
 {
     if (g.kind == 0) {
-        const int a = perm[g.off + j];
+        const int a = uni(perm[g.off + j]);
         t = a / f.K;
         r = a;
     } else {

@@ -1,5 +1,4 @@
-// k_gemv.hip -- the int4 expert GEMVs of the decode-size forward, as
-// persistent kernels over a work queue.
+// k_gemv.hip -- the int4 expert GEMVs of the decode-size forward.
 //
 // What is computed, cited by page title and section:
 //   "惊呆了！25GB 内存上运行 GLM 5.2 744B 模型" (reader.mx) §11: each chosen
@@ -11,28 +10,31 @@
 //     shared.
 //   Edge0 write-up (magicnetworld.com) §三: affine int4 with group size 64.
 //
-// Work decomposition.  A unit is (expert group g, 64-row block b, k-slice q):
-// one wavefront -- a workgroup of its own -- streams the slice's 16-byte
-// chunks of those 64 rows (lane = row, 1 KiB coalesced buffer loads, see the
-// slot layout) for every token of the group, two batches of loads in flight.
-// Thousands of small workgroups let the hardware dispatcher keep every SIMD
-// equally busy whatever the routing.  Partial sums go to a buffer indexed by
-// the unit and the last unit of a (group, row block) -- or of a row block,
-// for the down projection -- reduces them in a fixed order: results are
-// bitwise reproducible.
+// Work decomposition.  A unit is (expert group g, 64-row block b, k-slice q)
+// and is one wavefront, a workgroup of its own, so the hardware dispatcher
+// spreads the weight stream evenly over every SIMD whatever the routing.
+// The unit streams its slice's 16-byte chunks of the 64 rows (lane = row,
+// 1 KiB coalesced buffer loads, see the slot layout) with a rolling
+// prefetch: each chunk register is refilled with the chunk one step ahead
+// as soon as it is consumed.  The slice's activations (fp16 spans staged by
+// the router or by the gate/up finalize) are copied into the wavefront's
+// LDS once per pass and read with wave-uniform (broadcast) ds_read_b128.
+// Partial sums of the k-slices go to a small buffer; a finalize kernel
+// (gate/up: h = silu(g) * u, staged as fp16 spans for the down projection)
+// or the combine kernel (down: weighted sum over experts, residual) reduces
+// them in a fixed order, so results are bitwise reproducible.  With a single
+// k-slice the unit writes its result directly.
 //
-// Arithmetic per weight: one AND per 4 codes, one v_cvt_f32_ubyteN per code,
-// one v_fmac_f32 per code and token.  Row-format codes are stored code + 8;
-// the unit subtracts 8 * (sum of its activations) once.  Activations of the
-// slice are staged in the wavefront's own LDS area and read with
-// wave-uniform (broadcast) ds_read_b128.
+// Arithmetic per 8 codes and token: 3 shifts, 4 bit-field inserts (codes ->
+// fp16 1024 + 16 n, shared by the tokens of a pass) and 4 v_dot2_f32_f16;
+// per span of 64 inputs the fp32 sum is corrected with the span's stored
+// activation sum and rescaled (see k_common.h).
 #include "k_common.h"
 
 namespace moe {
 
-constexpr int SUB = 16;  // chunks staged in LDS at a time
-constexpr int UG = 4;    // chunks per batch of gate/up loads (x2 matrices)
-constexpr int UD = 8;    // chunks per batch of down loads
+constexpr int UG = 2;  // chunks per rolling step, gate/up (x2 matrices)
+constexpr int UD = 4;  // chunks per rolling step, down
 
 __device__ __forceinline__ void lds_wave_sync()
 {
@@ -40,81 +42,142 @@ __device__ __forceinline__ void lds_wave_sync()
     __builtin_amdgcn_wave_barrier();
 }
 
-// Unit index -> (group, row block, k-slice).  Units of one k-slice and row
-// block are adjacent across groups so that a (group, row block)'s slices are
-// spread over the launch.
-__device__ __forceinline__ void unit_coords(int u, int n_groups_max, int NB, int& gi, int& b,
-                                            int& q)
+__device__ __forceinline__ uint32_t dw(const uint4& v, int d)
 {
-    gi = u % n_groups_max;
-    const int rest = u / n_groups_max;
-    b = rest % NB;
-    q = rest / NB;
+    return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
 }
 
-// One batch of U chunks in flight per wavefront (the other resident
-// wavefronts of the SIMD hide the latency); the first batch is issued before
-// the activations are staged.  (Written out with macros: the buffers must
-// stay in registers.)
-#define GU_LOAD(BG, BU, I_)                                                        \
-    _Pragma("unroll") for (int k_ = 0; k_ < UG; ++k_)                               \
-    {                                                                              \
-        BG[k_] = bload16(rg, voff + k_ * 1024, (sc0 + (I_) * UG) * 1024);           \
-        BU[k_] = bload16(ru, voff + k_ * 1024, (sc0 + (I_) * UG) * 1024);           \
+// One dword of codes (8 inputs) against activation pair quad xv.
+__device__ __forceinline__ float dot_dword(uint32_t p0, uint32_t p1, uint32_t p2, uint32_t p3,
+                                           const uint4& xv, float acc)
+{
+    acc = dot2(p0, xv.x, acc);
+    acc = dot2(p1, xv.y, acc);
+    acc = dot2(p2, xv.z, acc);
+    acc = dot2(p3, xv.w, acc);
+    return acc;
+}
+
+// Chunk ck of the slice (4 dwords, 32 codes) of one matrix against the
+// tokens of the pass; xq = LDS activations [NT][CPU*4] uint4.
+template <int NT>
+__device__ __forceinline__ void chunk1(const uint4& w, const uint4* xq, int cpu4, int ck, int nj,
+                                       uint32_t mv, float (&acc)[NT])
+{
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        uint32_t p0, p1, p2, p3;
+        nib_pairs(dw(w, d), mv, p0, p1, p2, p3);
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+            if (j < nj) acc[j] = dot_dword(p0, p1, p2, p3, xq[j * cpu4 + ck * 4 + d], acc[j]);
     }
-#define GU_USE(BG, BU, I_)                                                         \
-    _Pragma("unroll") for (int j_ = 0; j_ < NT; ++j_) if (j_ < nj)                 \
-    {                                                                              \
-        _Pragma("unroll") for (int k_ = 0; k_ < UG; ++k_)                           \
-        {                                                                          \
-            const float* xp_ = xl + j_ * SUB * 32 + ((I_) * UG + k_) * 32;          \
-            dot32(BG[k_], xp_, ge[j_], go[j_]);                                    \
-            dot32(BU[k_], xp_, ue[j_], uo[j_]);                                    \
-        }                                                                          \
+}
+
+// Same for two matrices sharing the activations (gate and up).
+template <int NT>
+__device__ __forceinline__ void chunk2(const uint4& wa, const uint4& wb, const uint4* xq,
+                                       int cpu4, int ck, int nj, uint32_t mv, float (&aa)[NT],
+                                       float (&ab)[NT])
+{
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        uint32_t a0, a1, a2, a3, b0, b1, b2, b3;
+        nib_pairs(dw(wa, d), mv, a0, a1, a2, a3);
+        nib_pairs(dw(wb, d), mv, b0, b1, b2, b3);
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+            if (j < nj) {
+                const uint4 xv = xq[j * cpu4 + ck * 4 + d];
+                aa[j] = dot_dword(a0, a1, a2, a3, xv, aa[j]);
+                ab[j] = dot_dword(b0, b1, b2, b3, xv, ab[j]);
+            }
     }
-#define DN_LOAD(BD, I_)                                                            \
-    _Pragma("unroll") for (int k_ = 0; k_ < UD; ++k_)                               \
-        BD[k_] = bload16(rd, voff + k_ * 1024, (sc0 + (I_) * UD) * 1024);
-#define DN_USE(BD, I_)                                                             \
-    _Pragma("unroll") for (int j_ = 0; j_ < NT; ++j_) if (j_ < nj)                 \
-    {                                                                              \
-        _Pragma("unroll") for (int k_ = 0; k_ < UD; ++k_)                           \
-        {                                                                          \
-            dot32(BD[k_], hl + j_ * SUB * 32 + ((I_) * UD + k_) * 32, ye[j_], yo[j_]); \
-        }                                                                          \
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t p) { return __uint_as_float(p & 0xFFFF0000u); }
+
+// End of a span of 64 inputs: fold the span accumulator `a` into `tot`.
+// Row format (codes stored c + 8): sum c x = a/16 - 72 S.  Affine (w = sc q
+// + mn): sum w x = sc a/16 + (mn - 64 sc) S.  Then rescale by the span's 2^-k.
+template <int FMT>
+__device__ __forceinline__ float fold(float tot, float a, float2 span, uint32_t affine_pair)
+{
+    float v;
+    if (FMT == MOE_W_INT4_ROW) {
+        v = fmaf(a, 0.0625f, -72.f * span.y);
+    } else {
+        const float sc = bf16_lo(affine_pair), mn = bf16_hi(affine_pair);
+        v = fmaf(sc * 0.0625f, a, (mn - 64.f * sc) * span.y);
     }
+    return fmaf(v, span.x, tot);
+}
+
+// Copies the slice's staged activations of the pass's tokens into LDS:
+// xq [NT][CPU*4] uint4 then xs [NT][CPU/2] float2.
+template <int NT>
+__device__ __forceinline__ void copy_slice(const uint4* __restrict__ gq,
+                                           const float2* __restrict__ gs, const int (&src)[NT],
+                                           int nj, int row_q, int row_s, int c0, int CPU,
+                                           int lane, uint4* xq, float2* xs)
+{
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+        if (j < nj) {
+            const uint4* sq = gq + (size_t)src[j] * row_q + (size_t)c0 * 4;
+            const float2* ss = gs + (size_t)src[j] * row_s + c0 / 2;
+            for (int i = lane; i < CPU * 4; i += 64) xq[j * CPU * 4 + i] = sq[i];
+            for (int i = lane; i < CPU / 2; i += 64) xs[j * (CPU / 2) + i] = ss[i];
+        }
+    lds_wave_sync();
+}
+
+__device__ __forceinline__ void unit_coords(int u, int KS, int NB, int& q, int& b, int& gi)
+{
+    q = u % KS;
+    b = (u / KS) % NB;
+    gi = u / (KS * NB);
+}
 
 // ---------------------------------------------------------------------------
-// gate/up: h[r][row] = silu(sg[row] * (Wg x)_row * rs) * (su[row] * (Wu x)_row * rs)
+// gate/up unit: partial (sg (Wg x)_row, su (Wu x)_row) of one k-slice for the
+// group's tokens -> gpart[r][b][q][2][64]; with one k-slice, h directly.
 // ---------------------------------------------------------------------------
 
 template <int FMT, int NT>
-__global__ void __launch_bounds__(64, 4)
-    k_gu(Fwd f, const float* __restrict__ X, const Group* __restrict__ GR,
-         const int32_t* __restrict__ P, const TokStat* __restrict__ TS,
-         const int32_t* __restrict__ NG, float* __restrict__ Hout, int n_groups_max)
+__global__ void __launch_bounds__(64) k_gu(Fwd f)
 {
-    __shared__ float xl[NT * SUB * 32];
+    extern __shared__ uint4 lds4[];
     const int lane = threadIdx.x;
-    const int H = f.H, I = f.I, C = H / 32, G = H / 64, NB = I / 64;
-    const int KS = f.gu_ks, CPU = f.gu_cpu;
-    int gi, b, q;
-    unit_coords(blockIdx.x, n_groups_max, NB, gi, b, q);
-    if (gi >= NG[0]) return;
-    const Group grp = GR[gi];
-    const int row = b * 64 + lane, c0 = q * CPU;
+    const int KS = f.gu_ks, H = f.H, I = f.I, NB = I / 64, C = H / 32, G = H / 64;
+    int q, b, gi;
+    unit_coords(blockIdx.x, KS, NB, q, b, gi);
+    if (gi >= uni(f.n_groups[0])) return;
+    const Group grp = uni_group(f.groups, gi);
+    const int CPU = C / KS, c0 = q * CPU, row = b * 64 + lane;
+    uint4* xq = lds4;
+    float2* xs = (float2*)(lds4 + NT * CPU * 4);
     const uint8_t* base = grp.base;
-    const uint32_t voff = (uint32_t)lane * 16;
+    const uint32_t voff = (uint32_t)lane * 16, toff = (uint32_t)lane * 4;
+    const uint32_t mv = magic_vgpr();
     const __amdgpu_buffer_rsrc_t rg =
         make_rsrc(base + ((size_t)b * C + c0) * 1024, (uint32_t)CPU * 1024);
     const __amdgpu_buffer_rsrc_t ru =
         make_rsrc(base + (size_t)I * H / 2 + ((size_t)b * C + c0) * 1024, (uint32_t)CPU * 1024);
+    // row format: fp32 row scales after the codes; affine: (scale, min) bf16
+    // pair per row and 64-input group, [row block][group][64] per matrix
+    const uint8_t* tab = base + (size_t)3 * H * I / 2;
+    const __amdgpu_buffer_rsrc_t rtg = make_rsrc(tab + (size_t)b * G * 256, (uint32_t)G * 256);
+    const __amdgpu_buffer_rsrc_t rtu =
+        make_rsrc(tab + ((size_t)I * G + (size_t)b * G * 64) * 4, (uint32_t)G * 256);
     float sgr = 1.f, sur = 1.f;
     if (FMT == MOE_W_INT4_ROW && base != nullptr) {
-        const float* sc = (const float*)(base + (size_t)3 * H * I / 2);
-        sgr = sc[row];
-        sur = sc[I + row];
+        sgr = ((const float*)tab)[row];
+        sur = ((const float*)tab)[I + row];
     }
+    const int nst = CPU / UG;
+#pragma unroll 1
     for (int p0 = 0; p0 < grp.cnt; p0 += NT) {
         const int nj = min(NT, grp.cnt - p0);
         int tt[NT], rr[NT];
@@ -122,175 +185,134 @@ __global__ void __launch_bounds__(64, 4)
         for (int j = 0; j < NT; ++j) {
             tt[j] = 0;
             rr[j] = 0;
-            if (j < nj) tok_rows(f, P, grp, p0 + j, tt[j], rr[j]);
+            if (j < nj) tok_rows(f, f.perm, grp, p0 + j, tt[j], rr[j]);
         }
-        float ge[NT], go[NT], ue[NT], uo[NT], xs[NT];
+        float Gt[NT], Ut[NT], ag[NT], au[NT];
 #pragma unroll
-        for (int j = 0; j < NT; ++j) ge[j] = go[j] = ue[j] = uo[j] = xs[j] = 0.f;
+        for (int j = 0; j < NT; ++j) Gt[j] = Ut[j] = ag[j] = au[j] = 0.f;
         if (base != nullptr) {
-            for (int sc0 = 0; sc0 < CPU; sc0 += SUB) {
-                const int ns = min(SUB, CPU - sc0);
-                auto stage = [&]() {
+            uint4 A[UG], B[UG];
+            uint32_t PA = 0, PB = 0;
 #pragma unroll
-                    for (int j = 0; j < NT; ++j)
-                        if (j < nj) {
-                            const float4* src =
-                                (const float4*)(X + (size_t)tt[j] * H + (size_t)(c0 + sc0) * 32);
-                            for (int i = lane; i < ns * 8; i += 64) {
-                                const float4 v = src[i];
-                                ((float4*)(xl + j * SUB * 32))[i] = v;
-                                xs[j] += (v.x + v.y) + (v.z + v.w);
-                            }
-                        }
-                    lds_wave_sync();
-                };
-                if (FMT == MOE_W_INT4_ROW) {
-                    const int nbt = ns / UG;
-                    uint4 ag[UG], au[UG];
-                    if (nbt > 0) {
-                        GU_LOAD(ag, au, 0)
-                    }
-                    stage();  // overlaps the first batch's loads
-                    for (int i = 0; i < nbt; ++i) {
-                        if (i > 0) {
-                            GU_LOAD(ag, au, i)
-                        }
-                        GU_USE(ag, au, i)
-                    }
-                    for (int c = nbt * UG; c < ns; ++c) {
-                        const uint4 vg = bload16(rg, voff, (sc0 + c) * 1024);
-                        const uint4 vu = bload16(ru, voff, (sc0 + c) * 1024);
-#pragma unroll
-                        for (int j = 0; j < NT; ++j)
-                            if (j < nj) {
-                                const float* xp = xl + j * SUB * 32 + c * 32;
-                                dot32(vg, xp, ge[j], go[j]);
-                                dot32(vu, xp, ue[j], uo[j]);
-                            }
-                    }
-                } else {
-                    // affine: groups of 64 inputs (2 chunks), (scale, min) per row and group
-                    stage();
-                    const uint32_t* ag = (const uint32_t*)(base + (size_t)3 * H * I / 2) +
-                                         (size_t)b * G * 64 + lane;
-                    const uint32_t* au = ag + (size_t)I * G;
-                    for (int c = 0; c < ns; c += 2) {
-                        const int gq = (c0 + sc0 + c) / 2;
-                        const uint4 g0 = bload16(rg, voff, (sc0 + c) * 1024);
-                        const uint4 g1 = bload16(rg, voff + 1024, (sc0 + c) * 1024);
-                        const uint4 u0 = bload16(ru, voff, (sc0 + c) * 1024);
-                        const uint4 u1 = bload16(ru, voff + 1024, (sc0 + c) * 1024);
-                        const uint32_t pg = ag[(size_t)gq * 64], pu = au[(size_t)gq * 64];
-                        const float scg = __uint_as_float(pg << 16);
-                        const float mng = __uint_as_float(pg & 0xFFFF0000u);
-                        const float scu = __uint_as_float(pu << 16);
-                        const float mnu = __uint_as_float(pu & 0xFFFF0000u);
-#pragma unroll
-                        for (int j = 0; j < NT; ++j)
-                            if (j < nj) {
-                                const float* xp = xl + j * SUB * 32 + c * 32;
-                                const float sx = wave_sum(xp[lane]);
-                                float ae = 0.f, ao = 0.f, be = 0.f, bo = 0.f;
-                                dot32(g0, xp, ae, ao);
-                                dot32(g1, xp + 32, ae, ao);
-                                dot32(u0, xp, be, bo);
-                                dot32(u1, xp + 32, be, bo);
-                                ge[j] = fmaf(scg, fmaf(ao, 0.0625f, ae), fmaf(mng, sx, ge[j]));
-                                ue[j] = fmaf(scu, fmaf(bo, 0.0625f, be), fmaf(mnu, sx, ue[j]));
-                            }
-                    }
-                }
-                lds_wave_sync();
+            for (int k = 0; k < UG; ++k) {
+                A[k] = bload16(rg, voff + k * 1024, 0);
+                B[k] = bload16(ru, voff + k * 1024, 0);
             }
+            if (FMT != MOE_W_INT4_ROW) {
+                PA = bload4(rtg, toff, (uint32_t)(c0 / 2) * 256);
+                PB = bload4(rtu, toff, (uint32_t)(c0 / 2) * 256);
+            }
+            copy_slice<NT>(f.xq, f.xsc, tt, nj, H / 8, H / 64, c0, CPU, lane, xq, xs);
+            // one rolling step = one span (2 chunks); the last step loads nothing
+#define GU_STEP(I_, LOAD_)                                                               \
+    {                                                                                    \
+        const uint32_t pa = PA, pb = PB;                                                 \
+        _Pragma("unroll") for (int k = 0; k < UG; ++k)                                    \
+        {                                                                                \
+            const uint4 wa = A[k], wb = B[k];                                            \
+            if (LOAD_) {                                                                 \
+                A[k] = bload16(rg, voff + k * 1024, ((I_) + 1) * UG * 1024);             \
+                B[k] = bload16(ru, voff + k * 1024, ((I_) + 1) * UG * 1024);             \
+            }                                                                            \
+            chunk2<NT>(wa, wb, xq, CPU * 4, (I_) * UG + k, nj, mv, ag, au);               \
+        }                                                                                \
+        if (FMT != MOE_W_INT4_ROW && (LOAD_)) {                                          \
+            PA = bload4(rtg, toff, (uint32_t)(c0 / 2 + (I_) + 1) * 256);                 \
+            PB = bload4(rtu, toff, (uint32_t)(c0 / 2 + (I_) + 1) * 256);                 \
+        }                                                                                \
+        _Pragma("unroll") for (int j = 0; j < NT; ++j) if (j < nj)                       \
+        {                                                                                \
+            const float2 sp = xs[j * (CPU / 2) + (I_)];                                  \
+            Gt[j] = fold<FMT>(Gt[j], ag[j], sp, pa);                                     \
+            Ut[j] = fold<FMT>(Ut[j], au[j], sp, pb);                                     \
+            ag[j] = au[j] = 0.f;                                                         \
+        }                                                                                \
+    }
+#pragma unroll 1
+            for (int i = 0; i < nst - 1; ++i) GU_STEP(i, true)
+            GU_STEP(nst - 1, false)
+#undef GU_STEP
         }
 #pragma unroll
         for (int j = 0; j < NT; ++j)
             if (j < nj) {
-                float gp = ge[j], up = ue[j];
-                if (FMT == MOE_W_INT4_ROW) {
-                    const float x8 = 8.0f * wave_sum(xs[j]);
-                    gp = (fmaf(go[j], 0.0625f, ge[j]) - x8) * sgr;
-                    up = (fmaf(uo[j], 0.0625f, ue[j]) - x8) * sur;
-                }
+                const float g = Gt[j] * sgr, u = Ut[j] * sur;
                 if (KS == 1) {
-                    const float rs = TS[tt[j]].rscale;
-                    const float gg = gp * rs, uu = up * rs;
-                    Hout[(size_t)rr[j] * I + row] = gg / (1.0f + expf(-gg)) * uu;
+                    const float rs = f.tok[tt[j]].rscale;
+                    const float gg = g * rs, uu = u * rs;
+                    stage_span64(gg / (1.0f + expf(-gg)) * uu, lane,
+                                 (uint16_t*)(f.hq + (size_t)rr[j] * (I / 8) + b * 8),
+                                 f.hsc + (size_t)rr[j] * (I / 64) + b);
                 } else {
-                    float* pp = f.gu_part + (((size_t)rr[j] * NB + b) * KS + q) * 128;
-                    st_agent(pp + lane, gp);
-                    st_agent(pp + 64 + lane, up);
+                    float* o = f.gpart + (((size_t)rr[j] * NB + b) * KS + q) * 128;
+                    o[lane] = g;
+                    o[64 + lane] = u;
                 }
             }
-    }
-    if (KS > 1 && arrive_wave(&f.gu_ctr[gi * NB + b], KS)) {
-        for (int j = 0; j < grp.cnt; ++j) {
-            int t, r;
-            tok_rows(f, P, grp, j, t, r);
-            const float* pp = f.gu_part + ((size_t)r * NB + b) * KS * 128;
-            float gg = 0.f, uu = 0.f;
-            for (int q0 = 0; q0 < KS; q0 += 8) {
-                float a[8], c[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    a[i] = q0 + i < KS ? ld_agent(pp + (q0 + i) * 128 + lane) : 0.f;
-                    c[i] = q0 + i < KS ? ld_agent(pp + (q0 + i) * 128 + 64 + lane) : 0.f;
-                }
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    gg += a[i];
-                    uu += c[i];
-                }
-            }
-            const float rs = TS[t].rscale;
-            gg *= rs;
-            uu *= rs;
-            Hout[(size_t)r * I + row] = gg / (1.0f + expf(-gg)) * uu;
-        }
+        lds_wave_sync();
     }
 }
 
-// ---------------------------------------------------------------------------
-// down: partial y[r][row] over k-slices; the last unit of a row block sums
-// them and combines: out[t] = (x[t] +) sum_s y_shared_s + sum_k w_tk y_tk.
-// ---------------------------------------------------------------------------
-
-__device__ __forceinline__ float sum_slices(const float* pp, int KS, int lane)
+// gate/up finalize: one wavefront per (row r, block b): fixed-order sum of
+// the k-slices, h = silu(g rs) * (u rs), staged as an fp16 span.
+__global__ void __launch_bounds__(256) k_gu_fin(Fwd f, int n_rows)
 {
-    float s = 0.f;
-    for (int q0 = 0; q0 < KS; q0 += 8) {
-        float a[8];
+    const int lane = threadIdx.x & 63;
+    const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int NB = f.I / 64, KS = f.gu_ks;
+    if (w >= n_rows * NB) return;
+    const int r = w / NB, b = w - r * NB;
+    const float* p = f.gpart + ((size_t)r * NB + b) * KS * 128;
+    float gv[16], uv[16];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) a[i] = q0 + i < KS ? ld_agent(pp + (q0 + i) * 64 + lane) : 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) s += a[i];
+    for (int v = 0; v < 16; ++v) {
+        gv[v] = v < KS ? p[v * 128 + lane] : 0.f;
+        uv[v] = v < KS ? p[v * 128 + 64 + lane] : 0.f;
     }
-    return s;
+    float g = 0.f, u = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        g += gv[v];
+        u += uv[v];
+    }
+    const int TK = f.T * f.K;
+    const int t = r < TK ? r / f.K : (r - TK) % f.T;
+    const float rs = f.tok[t].rscale;
+    g *= rs;
+    u *= rs;
+    stage_span64(g / (1.0f + expf(-g)) * u, lane, (uint16_t*)(f.hq + (size_t)r * (f.I / 8) + b * 8),
+                 f.hsc + (size_t)r * (f.I / 64) + b);
 }
+
+// ---------------------------------------------------------------------------
+// down unit: partial sd (Wd h_r)_row of one k-slice -> ypart[r][b][q][64].
+// ---------------------------------------------------------------------------
 
 template <int FMT, int NT>
-__global__ void __launch_bounds__(64, 4)
-    k_dn(Fwd f, const Group* __restrict__ GR, const int32_t* __restrict__ P,
-         const float* __restrict__ Hin, const int32_t* __restrict__ NG, int n_groups_max,
-         int fused_combine)
+__global__ void __launch_bounds__(64) k_dn(Fwd f)
 {
-    __shared__ float hl[NT * SUB * 32];
+    extern __shared__ uint4 lds4[];
     const int lane = threadIdx.x;
-    const int H = f.H, I = f.I, C = I / 32, GI = I / 64, NB = H / 64;
-    const int KS = f.dn_ks, CPU = f.dn_cpu;
-    int gi, b, q;
-    unit_coords(blockIdx.x, n_groups_max, NB, gi, b, q);
-    const int n_groups = NG[0];
-    if (gi >= n_groups) return;
-    const Group grp = GR[gi];
-    const int row = b * 64 + lane, c0 = q * CPU;
+    const int KS = f.dn_ks, H = f.H, I = f.I, NB = H / 64, C = I / 32, GI = I / 64;
+    int q, b, gi;
+    unit_coords(blockIdx.x, KS, NB, q, b, gi);
+    if (gi >= uni(f.n_groups[0])) return;
+    const Group grp = uni_group(f.groups, gi);
+    const int CPU = C / KS, c0 = q * CPU, row = b * 64 + lane;
+    uint4* xq = lds4;
+    float2* xs = (float2*)(lds4 + NT * CPU * 4);
     const uint8_t* base = grp.base;
-    const uint32_t voff = (uint32_t)lane * 16;
+    const uint32_t voff = (uint32_t)lane * 16, toff = (uint32_t)lane * 4;
+    const uint32_t mv = magic_vgpr();
     const __amdgpu_buffer_rsrc_t rd =
         make_rsrc(base + (size_t)I * H + ((size_t)b * C + c0) * 1024, (uint32_t)CPU * 1024);
+    const uint8_t* tab = base + (size_t)3 * H * I / 2;
+    const __amdgpu_buffer_rsrc_t rtd = make_rsrc(
+        tab + ((size_t)2 * I * (H / 64) + (size_t)b * GI * 64) * 4, (uint32_t)GI * 256);
     float sdr = 1.f;
-    if (FMT == MOE_W_INT4_ROW && base != nullptr)
-        sdr = ((const float*)(base + (size_t)3 * H * I / 2))[2 * I + row];
+    if (FMT == MOE_W_INT4_ROW && base != nullptr) sdr = ((const float*)tab)[2 * I + row];
+    const int nst = CPU / UD;
+#pragma unroll 1
     for (int p0 = 0; p0 < grp.cnt; p0 += NT) {
         const int nj = min(NT, grp.cnt - p0);
         int rr[NT];
@@ -298,160 +320,142 @@ __global__ void __launch_bounds__(64, 4)
         for (int j = 0; j < NT; ++j) {
             int t = 0;
             rr[j] = 0;
-            if (j < nj) tok_rows(f, P, grp, p0 + j, t, rr[j]);
+            if (j < nj) tok_rows(f, f.perm, grp, p0 + j, t, rr[j]);
         }
-        float ye[NT], yo[NT], hs[NT];
+        float Yt[NT], a0[NT], a1[NT];
 #pragma unroll
-        for (int j = 0; j < NT; ++j) ye[j] = yo[j] = hs[j] = 0.f;
+        for (int j = 0; j < NT; ++j) Yt[j] = a0[j] = a1[j] = 0.f;
         if (base != nullptr) {
-            for (int sc0 = 0; sc0 < CPU; sc0 += SUB) {
-                const int ns = min(SUB, CPU - sc0);
-                auto stage = [&]() {
+            uint4 D[UD];
+            uint32_t P0 = 0, P1 = 0;
 #pragma unroll
-                    for (int j = 0; j < NT; ++j)
-                        if (j < nj) {
-                            const float4* src =
-                                (const float4*)(Hin + (size_t)rr[j] * I + (size_t)(c0 + sc0) * 32);
-                            for (int i = lane; i < ns * 8; i += 64) {
-                                const float4 v = src[i];
-                                ((float4*)(hl + j * SUB * 32))[i] = v;
-                                hs[j] += (v.x + v.y) + (v.z + v.w);
-                            }
-                        }
-                    lds_wave_sync();
-                };
-                if (FMT == MOE_W_INT4_ROW) {
-                    const int nbt = ns / UD;
-                    uint4 ad4[UD];
-                    if (nbt > 0) {
-                        DN_LOAD(ad4, 0)
-                    }
-                    stage();  // overlaps the first batch's loads
-                    for (int i = 0; i < nbt; ++i) {
-                        if (i > 0) {
-                            DN_LOAD(ad4, i)
-                        }
-                        DN_USE(ad4, i)
-                    }
-                    for (int c = nbt * UD; c < ns; ++c) {
-                        const uint4 vd = bload16(rd, voff, (sc0 + c) * 1024);
-#pragma unroll
-                        for (int j = 0; j < NT; ++j)
-                            if (j < nj) dot32(vd, hl + j * SUB * 32 + c * 32, ye[j], yo[j]);
-                    }
-                } else {
-                    stage();
-                    const uint32_t* ad = (const uint32_t*)(base + (size_t)3 * H * I / 2) +
-                                         (size_t)2 * I * (H / 64) + (size_t)b * GI * 64 + lane;
-                    for (int c = 0; c < ns; c += 2) {
-                        const int gq = (c0 + sc0 + c) / 2;
-                        const uint4 d0 = bload16(rd, voff, (sc0 + c) * 1024);
-                        const uint4 d1 = bload16(rd, voff + 1024, (sc0 + c) * 1024);
-                        const uint32_t pd = ad[(size_t)gq * 64];
-                        const float sc = __uint_as_float(pd << 16);
-                        const float mn = __uint_as_float(pd & 0xFFFF0000u);
-#pragma unroll
-                        for (int j = 0; j < NT; ++j)
-                            if (j < nj) {
-                                const float* hp = hl + j * SUB * 32 + c * 32;
-                                const float sh = wave_sum(hp[lane]);
-                                float ae = 0.f, ao = 0.f;
-                                dot32(d0, hp, ae, ao);
-                                dot32(d1, hp + 32, ae, ao);
-                                ye[j] = fmaf(sc, fmaf(ao, 0.0625f, ae), fmaf(mn, sh, ye[j]));
-                            }
-                    }
-                }
-                lds_wave_sync();
+            for (int k = 0; k < UD; ++k) D[k] = bload16(rd, voff + k * 1024, 0);
+            if (FMT != MOE_W_INT4_ROW) {
+                P0 = bload4(rtd, toff, (uint32_t)(c0 / 2) * 256);
+                P1 = bload4(rtd, toff, (uint32_t)(c0 / 2 + 1) * 256);
             }
+            copy_slice<NT>(f.hq, f.hsc, rr, nj, I / 8, I / 64, c0, CPU, lane, xq, xs);
+            // one rolling step = two spans (4 chunks); the last step loads nothing
+#define DN_STEP(I_, LOAD_)                                                               \
+    {                                                                                    \
+        const uint32_t p0v = P0, p1v = P1;                                               \
+        _Pragma("unroll") for (int k = 0; k < UD; ++k)                                    \
+        {                                                                                \
+            const uint4 wd = D[k];                                                       \
+            if (LOAD_) D[k] = bload16(rd, voff + k * 1024, ((I_) + 1) * UD * 1024);      \
+            if (k < 2) chunk1<NT>(wd, xq, CPU * 4, (I_) * UD + k, nj, mv, a0);            \
+            else chunk1<NT>(wd, xq, CPU * 4, (I_) * UD + k, nj, mv, a1);                  \
+        }                                                                                \
+        if (FMT != MOE_W_INT4_ROW && (LOAD_)) {                                          \
+            P0 = bload4(rtd, toff, (uint32_t)(c0 / 2 + 2 * (I_) + 2) * 256);             \
+            P1 = bload4(rtd, toff, (uint32_t)(c0 / 2 + 2 * (I_) + 3) * 256);             \
+        }                                                                                \
+        _Pragma("unroll") for (int j = 0; j < NT; ++j) if (j < nj)                       \
+        {                                                                                \
+            Yt[j] = fold<FMT>(Yt[j], a0[j], xs[j * (CPU / 2) + 2 * (I_)], p0v);          \
+            Yt[j] = fold<FMT>(Yt[j], a1[j], xs[j * (CPU / 2) + 2 * (I_) + 1], p1v);      \
+            a0[j] = a1[j] = 0.f;                                                         \
+        }                                                                                \
+    }
+#pragma unroll 1
+            for (int i = 0; i < nst - 1; ++i) DN_STEP(i, true)
+            DN_STEP(nst - 1, false)
+#undef DN_STEP
         }
 #pragma unroll
         for (int j = 0; j < NT; ++j)
-            if (j < nj) {
-                float yp = ye[j];
-                if (FMT == MOE_W_INT4_ROW)
-                    yp = (fmaf(yo[j], 0.0625f, ye[j]) - 8.0f * wave_sum(hs[j])) * sdr;
-                st_agent(f.dn_part + (((size_t)rr[j] * NB + b) * KS + q) * 64 + lane, yp);
-            }
-    }
-    if (fused_combine && arrive_wave(&f.dn_ctr[b], (uint32_t)(n_groups * KS))) {
-        const int T = f.T, K = f.K;
-        for (int t = 0; t < T; ++t) {
-            float m = 0.f;
-            for (int s = 0; s < f.n_shared; ++s) {
-                const int r = T * K + s * T + t;
-                m += sum_slices(f.dn_part + ((size_t)r * NB + b) * KS * 64, KS, lane);
-            }
-            for (int k = 0; k < K; ++k) {
-                const int r = t * K + k;
-                m = fmaf(f.wts[r], sum_slices(f.dn_part + ((size_t)r * NB + b) * KS * 64, KS, lane),
-                         m);
-            }
-            if (f.residual) m = f.x[(size_t)t * H + row] + m;
-            f.out[(size_t)t * H + row] = m;
-        }
+            if (j < nj) f.ypart[(((size_t)rr[j] * NB + b) * KS + q) * 64 + lane] = Yt[j] * sdr;
+        lds_wave_sync();
     }
 }
 
-// Stand-alone combine for token counts where the fused one would be a long
-// serial tail: one thread per output element, same fixed order.
+// Combine, one thread per output element, fixed order: shared experts, then
+// routed experts in rank order, each the sum of its k-slices in order;
+// out = (x +) that sum.
 __global__ void __launch_bounds__(256) k_combine(Fwd f)
 {
-    const int H = f.H, NB = H / 64, KS = f.dn_ks, T = f.T, K = f.K;
+    const int H = f.H, T = f.T, K = f.K, KS = f.dn_ks, NB = H / 64;
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (int64_t)T * H) return;
     const int t = (int)(idx / H), d = (int)(idx - (int64_t)t * H);
     const int b = d >> 6, lane = d & 63;
-    float m = 0.f;
-    for (int s = 0; s < f.n_shared; ++s) {
-        const float* pp = f.dn_part + ((size_t)(T * K + s * T + t) * NB + b) * KS * 64 + lane;
-        float y = 0.f;
-        for (int q = 0; q < KS; ++q) y += pp[q * 64];
-        m += y;
+    // up to 9 expert rows x 4 k-slices in flight
+    float v[9][4];
+#pragma unroll
+    for (int e = 0; e < 9; ++e) {
+        int r = -1;
+        if (e < f.n_shared) r = T * K + e * T + t;
+        else if (e - f.n_shared < K) r = t * K + (e - f.n_shared);
+        const float* p = f.ypart + ((size_t)(r < 0 ? 0 : r) * NB + b) * KS * 64 + lane;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) v[e][s] = (r >= 0 && s < KS) ? p[s * 64] : 0.f;
     }
-    for (int k = 0; k < K; ++k) {
-        const float* pp = f.dn_part + ((size_t)(t * K + k) * NB + b) * KS * 64 + lane;
-        float y = 0.f;
-        for (int q = 0; q < KS; ++q) y += pp[q * 64];
-        m = fmaf(f.wts[t * K + k], y, m);
+    float m = 0.f;
+#pragma unroll
+    for (int e = 0; e < 9; ++e) {
+        const float y = (v[e][0] + v[e][1]) + (v[e][2] + v[e][3]);
+        if (e < f.n_shared) m += y;
+        else if (e - f.n_shared < K) m = fmaf(f.wts[t * K + (e - f.n_shared)], y, m);
     }
     if (f.residual) m = f.x[idx] + m;
     f.out[idx] = m;
 }
 
 // ---------------------------------------------------------------------------
-// launch: one wavefront-sized workgroup per unit
+// launch
 // ---------------------------------------------------------------------------
 
+// Tokens per pass over the weights.
 static int tokens_per_pass(int T) { return T <= 1 ? 1 : T <= 2 ? 2 : 4; }
 
 static int max_groups(const Fwd& f) { return f.n_shared + std::min(f.E, f.T * f.K); }
 
+size_t gemv_lds_bytes(int chunks_per_slice, int T)
+{
+    const int nt = tokens_per_pass(T);
+    return (size_t)nt * (chunks_per_slice * 4 * 16 + (chunks_per_slice / 2) * 8);
+}
+
+int gemv_step_chunks(int which) { return which == 0 ? UG : UD; }
+
+int gemv_max_dn_ks() { return 4; }
+
+// Dynamic LDS above the default 64 KiB needs the kernel's attribute raised
+// (once per kernel, before its first launch that needs it).
+template <typename Kern>
+static hipError_t allow_lds(Kern kern, size_t lds, bool& done)
+{
+    if (lds <= 65536 || done) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    done = e == hipSuccess;
+    return e;
+}
+
 template <int FMT, int NT>
 static hipError_t gu_launch(const Fwd& f, hipStream_t st)
 {
-    const int mg = max_groups(f);
-    const unsigned grid = (unsigned)(mg * (f.I / 64) * f.gu_ks);
-    hipLaunchKernelGGL((k_gu<FMT, NT>), dim3(grid), dim3(64), 0, st, f, f.x, f.groups, f.perm,
-                       f.tok, f.n_groups, f.h, mg);
+    const int KS = f.gu_ks, CPU = f.H / 32 / KS;
+    const unsigned units = (unsigned)(max_groups(f) * (f.I / 64) * KS);
+    const size_t lds = gemv_lds_bytes(CPU, f.T);
+    static bool big = false;
+    hipError_t e0 = allow_lds(k_gu<FMT, NT>, lds, big);
+    if (e0 != hipSuccess) return e0;
+    hipLaunchKernelGGL((k_gu<FMT, NT>), dim3(units), dim3(64), lds, st, f);
     return hipGetLastError();
 }
 
 template <int FMT, int NT>
 static hipError_t dn_launch(const Fwd& f, hipStream_t st)
 {
-    const int mg = max_groups(f);
-    const unsigned grid = (unsigned)(mg * (f.H / 64) * f.dn_ks);
-    const int fused = f.T * (f.K + f.n_shared) * f.dn_ks <= 64;
-    hipLaunchKernelGGL((k_dn<FMT, NT>), dim3(grid), dim3(64), 0, st, f, f.groups, f.perm, f.h,
-                       f.n_groups, mg, fused);
-    hipError_t e = hipGetLastError();
-    if (e == hipSuccess && !fused) {
-        const int64_t n = (int64_t)f.T * f.H;
-        hipLaunchKernelGGL(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, f);
-        e = hipGetLastError();
-    }
-    return e;
+    const int KS = f.dn_ks, CPU = f.I / 32 / KS;
+    const unsigned units = (unsigned)(max_groups(f) * (f.H / 64) * KS);
+    const size_t lds = gemv_lds_bytes(CPU, f.T);
+    static bool big = false;
+    hipError_t e0 = allow_lds(k_dn<FMT, NT>, lds, big);
+    if (e0 != hipSuccess) return e0;
+    hipLaunchKernelGGL((k_dn<FMT, NT>), dim3(units), dim3(64), lds, st, f);
+    return hipGetLastError();
 }
 
 template <int FMT>
@@ -484,6 +488,23 @@ hipError_t launch_down_gemv(const Fwd& f, hipStream_t st)
 {
     if (f.fmt == MOE_W_INT4_ROW) return dn_dispatch<MOE_W_INT4_ROW>(f, st);
     return dn_dispatch<MOE_W_INT4_AFFINE_G64>(f, st);
+}
+
+bool gateup_needs_finalize(const Fwd& f) { return f.gu_ks > 1; }
+
+hipError_t launch_gateup_finalize(const Fwd& f, hipStream_t st)
+{
+    const int n_rows = f.T * (f.K + f.n_shared);
+    const int waves = n_rows * (f.I / 64);
+    hipLaunchKernelGGL(k_gu_fin, dim3((waves + 3) / 4), dim3(256), 0, st, f, n_rows);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const Fwd& f, hipStream_t st)
+{
+    const int64_t n = (int64_t)f.T * f.H;
+    hipLaunchKernelGGL(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, f);
+    return hipGetLastError();
 }
 
 }  // namespace moe

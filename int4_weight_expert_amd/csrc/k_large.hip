@@ -8,7 +8,7 @@
 // union that reads each expert once); Edge0 write-up §七 (renormalised
 // weights with the 1e-20 term); "初始化与权重加载" (colibrì analysis) §1.2
 // (a single expert group: n_group == 1).
-#include "moe_internal.h"
+#include "k_common.h"
 
 namespace moe {
 
@@ -35,19 +35,12 @@ __global__ void __launch_bounds__(256) k_tokstats(Fwd f)
     const int H = f.H;
     const float* xt = f.x + (size_t)t * H;
     float sum = 0.f, ss = 0.f;
-    for (int i0 = 0; i0 < H; i0 += 256) {
-        const float4 v = *(const float4*)(xt + i0 + lane * 4);
-        float gs = (v.x + v.y) + (v.z + v.w);
-        sum += gs;
-        ss = fmaf(v.x, v.x, ss);
-        ss = fmaf(v.y, v.y, ss);
-        ss = fmaf(v.z, v.z, ss);
-        ss = fmaf(v.w, v.w, ss);
-        gs += __shfl_xor(gs, 1);
-        gs += __shfl_xor(gs, 2);
-        gs += __shfl_xor(gs, 4);
-        gs += __shfl_xor(gs, 8);
-        if ((lane & 15) == 0) f.xgs[(size_t)t * (H / 64) + (i0 >> 6) + (lane >> 4)] = gs;
+    for (int s = 0; s < H / 64; ++s) {
+        const float v = xt[s * 64 + lane];
+        sum += v;
+        ss = fmaf(v, v, ss);
+        stage_span64(v, lane, (uint16_t*)(f.xq + (size_t)t * (H / 8) + s * 8),
+                     f.xsc + (size_t)t * (H / 64) + s);
     }
     sum = wsum(sum);
     ss = wsum(ss);
@@ -308,8 +301,6 @@ __global__ void __launch_bounds__(1024) k_bucket(const int32_t* __restrict__ ids
     }
     if (tid == 0) {
         f.n_groups[0] = f.n_shared + s_nact;
-        __hip_atomic_store(&f.queues[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&f.queues[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

@@ -30,15 +30,20 @@ __device__ __forceinline__ uint32_t ord_float(float c)
 }
 
 // ---------------------------------------------------------------------------
-// Router tail (one 256-thread workgroup): token statistics, sigmoid, bias,
-// top-K per token, weights, bucketing into expert groups, slot resolution.
-// Used by the small-T router (after the last partial arrives) for T <= 16.
+// Router tail (one workgroup, one thread per expert): token statistics,
+// sigmoid, bias, top-K per token, weights, bucketing into expert groups,
+// slot resolution.  Runs after the last router partial arrives (T <= 16).
+// Selection: the score key of expert e is (score, then lower id) packed in
+// 64 bits; its rank is the number of keys above it, computed by every
+// expert in parallel from LDS broadcasts, and experts of rank < K are the
+// choice in rank order -- the same set and order as K strict greater-than
+// scans.
 // ---------------------------------------------------------------------------
 
 template <int NT>
 __device__ void router_tail(const Fwd& f)
 {
-    __shared__ float s_c[NT][256];
+    __shared__ unsigned long long s_key[NT][256];
     __shared__ float s_sig[NT][256];
     __shared__ float s_rs[NT];
     __shared__ int s_ids[NT * 8];
@@ -48,90 +53,83 @@ __device__ void router_tail(const Fwd& f)
     __shared__ int s_nact;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int nthr = blockDim.x;
     const int T = f.T, H = f.H, E = f.E, K = f.K, Epad = f.Epad;
+    // independent loads first: bias and slot of this thread's expert
+    float bias_e = 0.f;
+    int slot_e = -1;
+    if (tid < E) {
+        bias_e = f.bias[tid];
+        slot_e = f.tbl[tid];
+    }
     // 1. token statistics: fixed-order sums of the per-slice partials
     if (tid < T) {
+        float a[32], c[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            a[i] = i < f.S ? ld_agent(&f.tpart[((size_t)i * T + tid) * 2 + 0]) : 0.f;
+            c[i] = i < f.S ? ld_agent(&f.tpart[((size_t)i * T + tid) * 2 + 1]) : 0.f;
+        }
         float sum = 0.f, ss = 0.f;
-        for (int s0 = 0; s0 < f.S; s0 += 8) {
-            float a[8], c[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                a[i] = s0 + i < f.S ? ld_agent(&f.tpart[((size_t)(s0 + i) * T + tid) * 2 + 0]) : 0.f;
-                c[i] = s0 + i < f.S ? ld_agent(&f.tpart[((size_t)(s0 + i) * T + tid) * 2 + 1]) : 0.f;
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                sum += a[i];
-                ss += c[i];
-            }
+        for (int i = 0; i < 32; ++i) {
+            sum += a[i];
+            ss += c[i];
         }
         const float rs = f.residual ? 1.0f / sqrtf(ss / (float)H + f.eps) : 1.0f;
         f.tok[tid].xsum = sum;
         f.tok[tid].rscale = rs;
         s_rs[tid] = rs;
     }
+    for (int e = tid; e < 256; e += nthr) s_cnt[e] = 0;
     __syncthreads();
 
-    // 2. logits (fixed-order sum of the K-slice partials), sigmoid, score
-    if (tid < Epad) {
+    // 2. logits (fixed-order sum of the K-slice partials), sigmoid, score key
+    if (tid < 256) {
         for (int t = 0; t < T; ++t) {
-            float l = 0.f;
-            for (int s0 = 0; s0 < f.S; s0 += 8) {
-                float a[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    a[i] = s0 + i < f.S ? ld_agent(&f.part[((size_t)(s0 + i) * T + t) * Epad + tid]) : 0.f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) l += a[i];
-            }
-            l *= s_rs[t];
-            float sig = 0.f, c = -INFINITY;
+            unsigned long long key = 0ull;  // padding experts: below every real key
+            float sig = 0.f;
             if (tid < E) {
+                float a[32];
+#pragma unroll
+                for (int i = 0; i < 32; ++i)
+                    a[i] = i < f.S ? ld_agent(&f.part[((size_t)i * T + t) * Epad + tid]) : 0.f;
+                float l = 0.f;
+#pragma unroll
+                for (int i = 0; i < 32; ++i) l += a[i];
+                l *= s_rs[t];
                 sig = 1.0f / (1.0f + expf(-l));
-                c = sig + f.bias[tid];
+                const float c = sig + bias_e;
+                key = ((unsigned long long)ord_float(c) << 32) | (uint32_t)(0xFFFFu - tid);
             }
-            s_c[t][tid] = c;
+            s_key[t][tid] = key;
             s_sig[t][tid] = sig;
         }
     }
-    for (int e = tid; e < 256; e += 256) s_cnt[e] = 0;
     __syncthreads();
 
-    // 3. top-K per token: K rounds of a wavefront argmax over 64-bit keys
-    //    (score order, then lower id), one wavefront per token
-    for (int t = w; t < T; t += 4) {
-        uint32_t taken = 0;
-        float ssum = 0.f;
-        for (int kk = 0; kk < K; ++kk) {
-            unsigned long long best = 0ull;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int e = lane + 64 * m;
-                if (e < Epad && !(taken & (1u << m))) {
-                    const unsigned long long key =
-                        ((unsigned long long)ord_float(s_c[t][e]) << 32) | (uint32_t)(0xFFFFu - e);
-                    best = key > best ? key : best;
-                }
+    // 3. ranks: experts with rank < K are chosen, in rank order
+    if (tid < E) {
+        for (int t = 0; t < T; ++t) {
+            const unsigned long long mine = s_key[t][tid];
+            int rank = 0;
+            for (int e = 0; e < Epad; e += 2) {
+                const ulonglong2 kk = *(const ulonglong2*)&s_key[t][e];
+                rank += (kk.x > mine) + (kk.y > mine);
             }
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) {
-                const unsigned long long other = __shfl_xor(best, o);
-                best = other > best ? other : best;
-            }
-            const int e = 0xFFFF - (int)(best & 0xFFFFu);
-            if ((e & 63) == lane) taken |= 1u << (e >> 6);
-            if (lane == 0) s_ids[t * K + kk] = e;
-            ssum += s_sig[t][e];
-        }
-        if (lane < K) {
-            const int e = s_ids[t * K + lane];
-            const float sg = s_sig[t][e];
-            const float wv = f.norm_topk ? f.routed_scale * (sg / (ssum + 1e-20f)) : f.routed_scale * sg;
-            f.ids[t * K + lane] = e;
-            f.wts[t * K + lane] = wv;
+            if (rank < K) s_ids[t * K + rank] = tid;
         }
     }
     __syncthreads();
+    // weights: renormalised over the chosen experts, summed in rank order
+    if (tid < T * K) {
+        const int t = tid / K;
+        float ssum = 0.f;
+        for (int k = 0; k < K; ++k) ssum += s_sig[t][s_ids[t * K + k]];
+        const float sg = s_sig[t][s_ids[tid]];
+        f.ids[tid] = s_ids[tid];
+        f.wts[tid] = f.norm_topk ? f.routed_scale * (sg / (ssum + 1e-20f)) : f.routed_scale * sg;
+    }
 
     // 4. bucketing: counts, exclusive scan, stable scatter, active groups
     const int n = T * K;
@@ -182,15 +180,14 @@ __device__ void router_tail(const Fwd& f)
         const int idx = s_act[tid];
         if (idx >= 0) {
             f.active[idx] = tid;
-            const int slot = f.tbl[tid];
             Group g;
-            g.base = slot >= 0 ? f.pool + (size_t)slot * f.slot_bytes : nullptr;
+            g.base = slot_e >= 0 ? f.pool + (size_t)slot_e * f.slot_bytes : nullptr;
             g.cnt = s_cnt[tid];
             g.off = s_off[tid];
             g.kind = 0;
             g.expert = tid;
             f.groups[f.n_shared + idx] = g;
-            if (slot < 0) {
+            if (slot_e < 0) {
                 atomicOr(&f.status[0], (uint32_t)STATUS_NOT_RESIDENT);
                 const int code = f.layer * E + tid;
                 atomicOr(&f.status[1 + code / 32], 1u << (code % 32));
@@ -209,8 +206,6 @@ __device__ void router_tail(const Fwd& f)
     if (tid == 0) {
         f.n_active[0] = s_nact;
         f.n_groups[0] = f.n_shared + s_nact;
-        __hip_atomic_store(&f.queues[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&f.queues[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -244,13 +239,16 @@ __global__ void __launch_bounds__(512) k_router_small(Fwd f, const float* __rest
                            __uint_as_float(q.w));
     }
     if (b == 0) {
+        // token sums and sums of squares of this 64-column span; the span
+        // staged as fp16 for the expert GEMVs
 #pragma unroll
         for (int j = 0; j < NT; ++j)
             if (j < T) {
                 const float xv = X[(size_t)j * H + s * 64 + lane];
                 const float gs = wave_sum(xv), ss = wave_sum(xv * xv);
+                stage_span64(xv, lane, (uint16_t*)(f.xq + (size_t)j * (H / 8) + s * 8),
+                             f.xsc + (size_t)j * (H / 64) + s);
                 if (lane == 0) {
-                    f.xgs[(size_t)j * (H / 64) + s] = gs;
                     sred[w][j][0] = gs;
                     sred[w][j][1] = ss;
                 }

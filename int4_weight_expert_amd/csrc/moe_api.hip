@@ -36,7 +36,8 @@ struct moe_ctx {
     int32_t* ids = nullptr;
     float* wts = nullptr;
     TokStat* tok = nullptr;
-    float* xgs = nullptr;
+    uint4* xq = nullptr;
+    float2* xsc = nullptr;
     int32_t* cnt = nullptr;
     int32_t* off = nullptr;
     int32_t* perm = nullptr;
@@ -44,15 +45,12 @@ struct moe_ctx {
     int32_t* n_active = nullptr;
     Group* groups = nullptr;
     int32_t* n_groups = nullptr;
-    float* h = nullptr;
-    float* hgs = nullptr;
-    float* gu_part = nullptr;
-    size_t gu_part_bytes = 0;
-    float* dn_part = nullptr;
-    size_t dn_part_bytes = 0;
-    uint32_t* gu_ctr = nullptr;
-    uint32_t* dn_ctr = nullptr;
-    uint32_t* queues = nullptr;
+    uint4* hq = nullptr;
+    float2* hsc = nullptr;
+    float* gpart = nullptr;
+    size_t gpart_bytes = 0;
+    float* ypart = nullptr;
+    size_t ypart_bytes = 0;
     uint32_t* counters = nullptr;
     uint32_t* status = nullptr;
     size_t status_words = 0;
@@ -107,45 +105,36 @@ int router_slices(int H)
     return slices / (slices % 8 == 0 ? 8 : 4);
 }
 
-// Largest chunks-per-slice from the preferred list that divides the row's
-// chunk count (all even, as the affine format needs whole 64-input groups).
-int pick_cpu(int chunks, const int* prefs, int n)
+// k-slices per (group, 64-row block) for a row of `chunks` 16-byte chunks:
+// the fewest that give about 3072 single-wavefront units (12 per CU), each
+// slice a whole number of rolling steps, within the partial buffer and the
+// LDS a unit may use.
+int pick_ks(int chunks, int blocks, int step, int max_ks, size_t part_need_per_ks,
+            size_t part_bytes, int T, int lds_max)
 {
-    for (int i = 0; i < n; ++i)
-        if (chunks % prefs[i] == 0) return prefs[i];
-    return chunks;
+    static const int cand[] = {1, 2, 3, 4, 6, 8, 12, 16};
+    int best = 1;
+    for (int ks : cand) {
+        if (ks > max_ks) break;
+        if (chunks % ks != 0 || (chunks / ks) % step != 0) continue;
+        if (ks > 1 && part_need_per_ks * ks > part_bytes) break;
+        if (gemv_lds_bytes(chunks / ks, T) > (size_t)lds_max) continue;
+        best = ks;
+        if ((int64_t)blocks * ks >= 3072) break;
+    }
+    return best;
 }
 
-// Work plan of the persistent GEMVs for T tokens: k-slices per row block,
-// limited by the partial buffers.
+// Work plan of the GEMVs for T tokens.
 void plan_gemv(moe_ctx* c, Fwd& f)
 {
     const moe_config& g = c->cfg;
-    const size_t rows = (size_t)f.T * g.top_k + (size_t)f.T * g.n_shared;
-    static const int gu_prefs[] = {16, 8, 12, 6, 4, 2};
-    static const int dn_prefs[] = {16, 8, 4, 2};
-    const int gc = g.hidden / 32, dc = g.inter / 32;
-    f.gu_cpu = pick_cpu(gc, gu_prefs, 6);
-    f.gu_ks = gc / f.gu_cpu;
-    if (rows * g.inter * 2 * 4 * f.gu_ks > c->gu_part_bytes) {
-        f.gu_ks = 1;
-        f.gu_cpu = gc;
-    }
-    f.dn_cpu = pick_cpu(dc, dn_prefs, 4);
-    f.dn_ks = dc / f.dn_cpu;
-    while (f.dn_ks > 1 && rows * g.hidden * 4 * f.dn_ks > c->dn_part_bytes) {
-        // fewer, longer slices: double the chunks per slice while it divides
-        if ((dc / f.dn_ks) * 2 <= dc && f.dn_ks % 2 == 0) {
-            f.dn_ks /= 2;
-            f.dn_cpu *= 2;
-        } else {
-            f.dn_ks = 1;
-            f.dn_cpu = dc;
-        }
-    }
     const int max_groups = g.n_shared + std::min(g.n_experts, f.T * g.top_k);
-    f.gu_grid = (max_groups * (g.inter / 64) * f.gu_ks + 3) / 4;
-    f.dn_grid = (max_groups * (g.hidden / 64) * f.dn_ks + 3) / 4;
+    const size_t rows = (size_t)f.T * (g.top_k + g.n_shared);
+    f.gu_ks = pick_ks(g.hidden / 32, max_groups * (g.inter / 64), gemv_step_chunks(0), 16,
+                      rows * g.inter * 2 * 4, c->gpart_bytes, f.T, c->lds_max);
+    f.dn_ks = pick_ks(g.inter / 32, max_groups * (g.hidden / 64), gemv_step_chunks(1),
+                      gemv_max_dn_ks(), rows * g.hidden * 4, c->ypart_bytes, f.T, c->lds_max);
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb)
@@ -199,7 +188,8 @@ Fwd make_fwd(moe_ctx* c, const float* x, float* out, int T, int layer, int resid
     f.ids = c->ids;
     f.wts = c->wts;
     f.tok = c->tok;
-    f.xgs = c->xgs;
+    f.xq = c->xq;
+    f.xsc = c->xsc;
     f.cnt = c->cnt;
     f.off = c->off;
     f.perm = c->perm;
@@ -207,13 +197,10 @@ Fwd make_fwd(moe_ctx* c, const float* x, float* out, int T, int layer, int resid
     f.n_active = c->n_active;
     f.groups = c->groups;
     f.n_groups = c->n_groups;
-    f.h = c->h;
-    f.hgs = c->hgs;
-    f.gu_part = c->gu_part;
-    f.dn_part = c->dn_part;
-    f.gu_ctr = c->gu_ctr;
-    f.dn_ctr = c->dn_ctr;
-    f.queues = c->queues;
+    f.hq = c->hq;
+    f.hsc = c->hsc;
+    f.gpart = c->gpart;
+    f.ypart = c->ypart;
     f.counters = c->counters;
     f.status = c->status;
     f.n_layers = g.n_layers;
@@ -252,8 +239,16 @@ int run_forward(moe_ctx* c, const float* x, int T, int layer, float* out, int re
     mark(c, "gateup_gemv");
     rc = hip_rc(c, launch_gateup_gemv(f, c->stream));
     if (rc) return rc;
-    mark(c, "down_gemv_combine");
+    if (gateup_needs_finalize(f)) {
+        mark(c, "gateup_finalize");
+        rc = hip_rc(c, launch_gateup_finalize(f, c->stream));
+        if (rc) return rc;
+    }
+    mark(c, "down_gemv");
     rc = hip_rc(c, launch_down_gemv(f, c->stream));
+    if (rc) return rc;
+    mark(c, "combine");
+    rc = hip_rc(c, launch_combine(f, c->stream));
     if (rc) return rc;
     mark(c, nullptr);
     return MOE_OK;
@@ -348,7 +343,8 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
     rc = rc ? rc : dalloc(c, &c->ids, Tm * K * 4);
     rc = rc ? rc : dalloc(c, &c->wts, Tm * K * 4);
     rc = rc ? rc : dalloc(c, &c->tok, Tm * sizeof(TokStat));
-    rc = rc ? rc : dalloc(c, &c->xgs, Tm * (H / 64) * 4);
+    rc = rc ? rc : dalloc(c, &c->xq, Tm * (H / 8) * 16);
+    rc = rc ? rc : dalloc(c, &c->xsc, Tm * (H / 64) * 8);
     rc = rc ? rc : dalloc(c, &c->cnt, E * 4);
     rc = rc ? rc : dalloc(c, &c->off, (E + 1) * 4);
     rc = rc ? rc : dalloc(c, &c->perm, Tm * K * 4);
@@ -356,19 +352,19 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
     rc = rc ? rc : dalloc(c, &c->n_active, 4);
     rc = rc ? rc : dalloc(c, &c->groups, (E + g.n_shared) * sizeof(Group));
     rc = rc ? rc : dalloc(c, &c->n_groups, 4);
-    rc = rc ? rc : dalloc(c, &c->h, rows * I * 4);
-    rc = rc ? rc : dalloc(c, &c->hgs, rows * (I / 64) * 4);
+    rc = rc ? rc : dalloc(c, &c->hq, rows * (I / 8) * 16);
+    rc = rc ? rc : dalloc(c, &c->hsc, rows * (I / 64) * 8);
     {
-        // partial buffers of the persistent GEMVs: k-split for up to 64 tokens
+        // k-split partials for up to 16 tokens (gate/up, 16 slices) and 64
+        // tokens (down, 4 slices); beyond that the plan falls back to fewer
+        // slices, down to one (gate/up then needs no partials at all).
+        const size_t r16 = std::min<size_t>(Tm, 16) * (K + g.n_shared);
         const size_t r64 = std::min<size_t>(Tm, 64) * (K + g.n_shared);
-        c->gu_part_bytes = r64 * I * 2 * 4 * 16;
-        c->dn_part_bytes = std::max(rows * H * 4, r64 * H * 4 * 4);
+        c->gpart_bytes = r16 * I * 2 * 4 * 16;
+        c->ypart_bytes = std::max(rows * H * 4, r64 * H * 4 * 4);
     }
-    rc = rc ? rc : dalloc(c, &c->gu_part, c->gu_part_bytes);
-    rc = rc ? rc : dalloc(c, &c->dn_part, c->dn_part_bytes);
-    rc = rc ? rc : dalloc(c, &c->gu_ctr, (E + g.n_shared) * (I / 64) * 4);
-    rc = rc ? rc : dalloc(c, &c->dn_ctr, (H / 64) * 4);
-    rc = rc ? rc : dalloc(c, &c->queues, 2 * 4);
+    rc = rc ? rc : dalloc(c, &c->gpart, c->gpart_bytes);
+    rc = rc ? rc : dalloc(c, &c->ypart, c->ypart_bytes);
     rc = rc ? rc : dalloc(c, &c->counters, (1 + H / 64) * 4);
     c->status_words = 1 + (L * E + 31) / 32;
     rc = rc ? rc : dalloc(c, &c->status, c->status_words * 4);
@@ -376,9 +372,6 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
         c->tbl_host.assign(L * E, -1);
         hipError_t e = hipMemcpy(c->tbl, c->tbl_host.data(), L * E * 4, hipMemcpyHostToDevice);
         if (e == hipSuccess) e = hipMemset(c->counters, 0, (1 + H / 64) * 4);
-        if (e == hipSuccess) e = hipMemset(c->gu_ctr, 0, (E + g.n_shared) * (I / 64) * 4);
-        if (e == hipSuccess) e = hipMemset(c->dn_ctr, 0, (H / 64) * 4);
-        if (e == hipSuccess) e = hipMemset(c->queues, 0, 2 * 4);
         if (e == hipSuccess) e = hipMemset(c->status, 0, c->status_words * 4);
         if (e == hipSuccess) e = hipMemset(c->bias, 0, L * E * 4);
         if (e == hipSuccess) e = hipMemset(c->wr, 0, L * c->Epad * H * 4);

@@ -65,7 +65,8 @@ struct Fwd {
     int32_t* ids;         // [T][K]
     float* wts;           // [T][K]
     TokStat* tok;         // [T]
-    float* xgs;           // [T][H/64] group sums of x
+    uint4* xq;            // [T][H/8] x staged as fp16 spans (pair order, see k_common.h)
+    float2* xsc;          // [T][H/64] per span (2^-k, sum of its fp16 values)
     int32_t* cnt;         // [E]
     int32_t* off;         // [E+1]
     int32_t* perm;        // [T*K]
@@ -73,21 +74,17 @@ struct Fwd {
     int32_t* n_active;    // [1]
     Group* groups;        // [n_shared + E]
     int32_t* n_groups;    // [1]
-    float* h;             // [T*K + T*n_shared][I]
-    float* hgs;           // [rows][I/64] (unused by the current kernels)
+    uint4* hq;            // [rows][I/8] h = silu(g) * u staged as fp16 spans
+    float2* hsc;          // [rows][I/64]
     uint32_t* counters;   // [0]: router arrivals
     uint32_t* status;     // [0] flags, [1..] missing bitmap over layer*E+id
     int n_layers;
     int lds_max;          // device LDS bytes per workgroup
-    // persistent GEMV work plan (see k_gemv.hip)
-    int gu_ks, gu_cpu;    // gate/up: k-slices per 64-row block, 16-byte chunks per slice
-    int dn_ks, dn_cpu;    // down: same
-    int gu_grid, dn_grid; // persistent workgroups launched
-    float* gu_part;       // [rows][I/64][gu_ks][2][64] when gu_ks > 1
-    float* dn_part;       // [rows][H/64][dn_ks][64]
-    uint32_t* gu_ctr;     // [(n_shared + E) * I/64] arrivals per (group, row block)
-    uint32_t* dn_ctr;     // [H/64] arrivals per row block
-    uint32_t* queues;     // [2] work counters of the two GEMV kernels, zeroed by the router
+    // GEMV work plan (see k_gemv.hip); rows = T*K + T*n_shared token rows
+    int gu_ks;            // gate/up: k-slices (units) per (group, 64-row block)
+    int dn_ks;            // down: same, at most gemv_max_dn_ks()
+    float* gpart;         // [rows][I/64][gu_ks][2][64] gate/up partials (gu_ks > 1)
+    float* ypart;         // [rows][H/64][dn_ks][64] down partials
 };
 
 enum { STATUS_NOT_RESIDENT = 1u, STATUS_RANGE = 2u };
@@ -111,7 +108,12 @@ hipError_t launch_router_small(const Fwd& f, hipStream_t st);
 hipError_t launch_router_large(const Fwd& f, hipStream_t st, int stage);
 hipError_t launch_gateup_gemv(const Fwd& f, hipStream_t st);
 hipError_t launch_down_gemv(const Fwd& f, hipStream_t st);
-int gemv_grid(int which, int fmt, int T, int num_cu);
+bool gateup_needs_finalize(const Fwd& f);
+hipError_t launch_gateup_finalize(const Fwd& f, hipStream_t st);
+hipError_t launch_combine(const Fwd& f, hipStream_t st);
+size_t gemv_lds_bytes(int chunks_per_slice, int T);
+int gemv_step_chunks(int which);
+int gemv_max_dn_ks();
 
 constexpr int ROUTER_SMALL_MAX_T = 16;
 
