@@ -30,20 +30,58 @@ __device__ __forceinline__ uint32_t ord_float(float c)
 }
 
 // ---------------------------------------------------------------------------
-// Router tail (one workgroup, one thread per expert): token statistics,
-// sigmoid, bias, top-K per token, weights, bucketing into expert groups,
-// slot resolution.  Runs after the last router partial arrives (T <= 16).
+// Router tail (one workgroup of 256 threads, one per expert): token
+// statistics, sigmoid, bias, top-K per token, weights, bucketing into expert
+// groups, slot resolution.  Runs in the last router workgroup to arrive
+// (T <= 8).
 // Selection: the score key of expert e is (score, then lower id) packed in
-// 64 bits; its rank is the number of keys above it, computed by every
-// expert in parallel from LDS broadcasts, and experts of rank < K are the
-// choice in rank order -- the same set and order as K strict greater-than
-// scans.
+// 64 bits, so keys are distinct and "greater key" is the pages' strict
+// greater-than scan order.  Each wavefront ranks the keys of one block of 64
+// experts among themselves; the block's keys of rank < K are candidates, and
+// the candidates' ranks among all candidates are the global ranks: the
+// experts of rank < K are the choice, in rank order.
 // ---------------------------------------------------------------------------
+
+constexpr int RT_THREADS = 256;
+
+// Partial layouts (written by the router workgroups with agent-scope stores):
+// logits of expert e, token t, slice row i at part[e * Sp + t * S + i] and
+// statistics (sum, sum of squares) at tpart[t * S2p + 2 i + {0, 1}], with
+// Sp, S2p rounded up to whole 16-byte vectors, so that each reader's values
+// are contiguous.
+__device__ __forceinline__ int router_sp(int T, int S) { return (T * S + 3) & ~3; }
+__device__ __forceinline__ int router_s2p(int S) { return (2 * S + 3) & ~3; }
+
+// 16-byte agent-coherent (sc1) buffer load
+__device__ __forceinline__ float4 bload16_agent(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                uint32_t soff)
+{
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 16);
+    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                       __uint_as_float(v.w));
+}
+
+// Fixed-order sum of n (<= 64) consecutive partials starting at float index
+// `at` of resource r (lane-private offset voff); all loads issued first.
+__device__ __forceinline__ void load64(__amdgpu_buffer_rsrc_t r, uint32_t voff, int at, int n,
+                                       float (&a)[64])
+{
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const float4 v = 4 * q < n ? bload16_agent(r, voff, (uint32_t)(at + 4 * q) * 4)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+        a[4 * q + 0] = 4 * q + 0 < n ? v.x : 0.f;  // padding floats are never written
+        a[4 * q + 1] = 4 * q + 1 < n ? v.y : 0.f;
+        a[4 * q + 2] = 4 * q + 2 < n ? v.z : 0.f;
+        a[4 * q + 3] = 4 * q + 3 < n ? v.w : 0.f;
+    }
+}
 
 template <int NT>
 __device__ void router_tail(const Fwd& f)
 {
     __shared__ unsigned long long s_key[NT][256];
+    __shared__ unsigned long long s_cand[NT][32];
     __shared__ float s_sig[NT][256];
     __shared__ float s_rs[NT];
     __shared__ int s_ids[NT * 8];
@@ -53,72 +91,129 @@ __device__ void router_tail(const Fwd& f)
     __shared__ int s_nact;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int nthr = blockDim.x;
-    const int T = f.T, H = f.H, E = f.E, K = f.K, Epad = f.Epad;
-    // independent loads first: bias and slot of this thread's expert
+    const int T = f.T, H = f.H, E = f.E, K = f.K, Epad = f.Epad, S = f.S;
+    const int Sp = router_sp(T, S), S2p = router_s2p(S);
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(f.part, (uint32_t)(Epad * Sp * 4));
+    const __amdgpu_buffer_rsrc_t rt = make_rsrc(f.tpart, (uint32_t)(T * S2p * 4));
     float bias_e = 0.f;
     int slot_e = -1;
     if (tid < E) {
         bias_e = f.bias[tid];
         slot_e = f.tbl[tid];
     }
-    // 1. token statistics: fixed-order sums of the per-slice partials
-    if (tid < T) {
-        float a[32], c[32];
+    // 1. token statistics and logits.  T = 1: every thread sums the token's
+    //    statistics itself (no barrier); otherwise thread t < T does, via LDS.
+    float lsum[NT];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            a[i] = i < f.S ? ld_agent(&f.tpart[((size_t)i * T + tid) * 2 + 0]) : 0.f;
-            c[i] = i < f.S ? ld_agent(&f.tpart[((size_t)i * T + tid) * 2 + 1]) : 0.f;
-        }
+    for (int t = 0; t < NT; ++t) lsum[t] = 0.f;
+    float rs0 = 1.f;
+    if (NT == 1) {
+        float a[64];
+        load64(rp, (uint32_t)tid * Sp * 4, 0, S, a);  // S <= 64
         float sum = 0.f, ss = 0.f;
+        for (int c0 = 0; c0 < 2 * S; c0 += 64) {
+            float st[64];
+            load64(rt, 0, c0, 2 * S - c0, st);
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            sum += a[i];
-            ss += c[i];
+            for (int i = 0; i < 32; ++i) {
+                sum += st[2 * i];
+                ss += st[2 * i + 1];
+            }
         }
-        const float rs = f.residual ? 1.0f / sqrtf(ss / (float)H + f.eps) : 1.0f;
-        f.tok[tid].xsum = sum;
-        f.tok[tid].rscale = rs;
-        s_rs[tid] = rs;
+#pragma unroll
+        for (int i = 0; i < 64; ++i) lsum[0] += a[i];
+        rs0 = f.residual ? 1.0f / sqrtf(ss / (float)H + f.eps) : 1.0f;
+        if (tid == 0) {
+            f.tok[0].xsum = sum;
+            f.tok[0].rscale = rs0;
+        }
+    } else {
+        if (tid < T) {
+            float sum = 0.f, ss = 0.f;
+            for (int c0 = 0; c0 < 2 * S; c0 += 64) {
+                float st[64];
+                load64(rt, 0, tid * S2p + c0, 2 * S - c0, st);
+#pragma unroll
+                for (int i = 0; i < 32; ++i) {
+                    sum += st[2 * i];
+                    ss += st[2 * i + 1];
+                }
+            }
+            const float rs = f.residual ? 1.0f / sqrtf(ss / (float)H + f.eps) : 1.0f;
+            f.tok[tid].xsum = sum;
+            f.tok[tid].rscale = rs;
+            s_rs[tid] = rs;
+        }
+        // expert tid's partials: token t, slice i at t * S + i
+        for (int k0 = 0; k0 < T * S; k0 += 64) {
+            float a[64];
+            load64(rp, (uint32_t)tid * Sp * 4, k0, T * S - k0, a);
+            int t = k0 / S, i = k0 - t * S;
+            float acc = 0.f;
+#pragma unroll
+            for (int k = 0; k < 64; ++k) {
+                acc += a[k];
+                if (++i == S) {
+#pragma unroll
+                    for (int j = 0; j < NT; ++j)
+                        if (j == t) lsum[j] += acc;
+                    acc = 0.f;
+                    i = 0;
+                    ++t;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+                if (j == t) lsum[j] += acc;
+        }
     }
-    for (int e = tid; e < 256; e += nthr) s_cnt[e] = 0;
-    __syncthreads();
+    for (int e = tid; e < 256; e += RT_THREADS) s_cnt[e] = 0;
+    for (int i = tid; i < T * 32; i += RT_THREADS) s_cand[i >> 5][i & 31] = 0ull;
+    if (NT > 1) __syncthreads();
 
-    // 2. logits (fixed-order sum of the K-slice partials), sigmoid, score key
-    if (tid < 256) {
-        for (int t = 0; t < T; ++t) {
-            unsigned long long key = 0ull;  // padding experts: below every real key
+    // 2. sigmoid, bias, score key (keys of all 256 slots are written: padding
+    //    experts get 0, below every real key)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+        if (t < T) {
+            unsigned long long key = 0ull;
             float sig = 0.f;
             if (tid < E) {
-                float a[32];
-#pragma unroll
-                for (int i = 0; i < 32; ++i)
-                    a[i] = i < f.S ? ld_agent(&f.part[((size_t)i * T + t) * Epad + tid]) : 0.f;
-                float l = 0.f;
-#pragma unroll
-                for (int i = 0; i < 32; ++i) l += a[i];
-                l *= s_rs[t];
-                sig = 1.0f / (1.0f + expf(-l));
+                const float rs = NT == 1 ? rs0 : s_rs[t];
+                sig = 1.0f / (1.0f + expf(-(lsum[t] * rs)));
                 const float c = sig + bias_e;
                 key = ((unsigned long long)ord_float(c) << 32) | (uint32_t)(0xFFFFu - tid);
             }
             s_key[t][tid] = key;
             s_sig[t][tid] = sig;
         }
-    }
     __syncthreads();
 
-    // 3. ranks: experts with rank < K are chosen, in rank order
-    if (tid < E) {
-        for (int t = 0; t < T; ++t) {
-            const unsigned long long mine = s_key[t][tid];
-            int rank = 0;
-            for (int e = 0; e < Epad; e += 2) {
-                const ulonglong2 kk = *(const ulonglong2*)&s_key[t][e];
-                rank += (kk.x > mine) + (kk.y > mine);
-            }
-            if (rank < K) s_ids[t * K + rank] = tid;
+    // 3a. ranks within each block of 64 experts; rank < K -> candidate
+    for (int pq = w; pq < T * 4; pq += RT_THREADS / 64) {
+        const int t = pq >> 2, blk = pq & 3;
+        const unsigned long long* kb = &s_key[t][blk * 64];
+        const unsigned long long mine = kb[lane];
+        int rank = 0;
+#pragma unroll
+        for (int e = 0; e < 64; e += 2) {
+            const ulonglong2 kk = *(const ulonglong2*)&kb[e];
+            rank += (kk.x > mine) + (kk.y > mine);
         }
+        if (rank < K) s_cand[t][blk * K + rank] = mine;
+    }
+    __syncthreads();
+    // 3b. ranks among the 4K candidates: global ranks of the top K
+    for (int tc = tid; tc < T * 32; tc += RT_THREADS) {
+        const int t = tc >> 5, c = tc & 31;
+        const unsigned long long mine = s_cand[t][c];
+        int rank = 0;
+#pragma unroll
+        for (int j = 0; j < 32; j += 2) {
+            const ulonglong2 kk = *(const ulonglong2*)&s_cand[t][j];
+            rank += (kk.x > mine) + (kk.y > mine);
+        }
+        if (c < 4 * K && rank < K) s_ids[t * K + rank] = (int)(0xFFFFu - (uint32_t)(mine & 0xFFFFu));
     }
     __syncthreads();
     // weights: renormalised over the chosen experts, summed in rank order
@@ -130,70 +225,6 @@ __device__ void router_tail(const Fwd& f)
         f.ids[tid] = s_ids[tid];
         f.wts[tid] = f.norm_topk ? f.routed_scale * (sg / (ssum + 1e-20f)) : f.routed_scale * sg;
     }
-
-    // 4. bucketing: counts, exclusive scan, stable scatter, active groups
-    const int n = T * K;
-    if (tid < n) atomicAdd(&s_cnt[s_ids[tid]], 1);
-    __syncthreads();
-    if (w == 0) {
-        int c4[4], a4[4], sc = 0, sa = 0;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            c4[m] = s_cnt[lane * 4 + m];
-            a4[m] = c4[m] > 0;
-            sc += c4[m];
-            sa += a4[m];
-        }
-        int ic = sc, ia = sa;  // inclusive wavefront scans
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int pc = __shfl_up(ic, o), pa = __shfl_up(ia, o);
-            if (lane >= o) {
-                ic += pc;
-                ia += pa;
-            }
-        }
-        int rc = ic - sc, ra = ia - sa;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            s_off[lane * 4 + m] = rc;
-            s_act[lane * 4 + m] = a4[m] ? ra : -1;
-            rc += c4[m];
-            ra += a4[m];
-        }
-        if (lane == 63) {
-            s_off[256] = rc;
-            s_nact = ra;
-        }
-    }
-    __syncthreads();
-    if (tid < n) {
-        const int e = s_ids[tid];
-        int rank = 0;
-        for (int a = 0; a < tid; ++a) rank += s_ids[a] == e;
-        f.perm[s_off[e] + rank] = tid;
-    }
-    if (tid < E) {
-        f.cnt[tid] = s_cnt[tid];
-        f.off[tid] = s_off[tid];
-        if (tid == 0) f.off[E] = s_off[E];
-        const int idx = s_act[tid];
-        if (idx >= 0) {
-            f.active[idx] = tid;
-            Group g;
-            g.base = slot_e >= 0 ? f.pool + (size_t)slot_e * f.slot_bytes : nullptr;
-            g.cnt = s_cnt[tid];
-            g.off = s_off[tid];
-            g.kind = 0;
-            g.expert = tid;
-            f.groups[f.n_shared + idx] = g;
-            if (slot_e < 0) {
-                atomicOr(&f.status[0], (uint32_t)STATUS_NOT_RESIDENT);
-                const int code = f.layer * E + tid;
-                atomicOr(&f.status[1 + code / 32], 1u << (code % 32));
-            }
-        }
-    }
     if (tid < f.n_shared) {
         Group g;
         g.base = f.shared + (size_t)tid * f.slot_bytes;
@@ -203,30 +234,125 @@ __device__ void router_tail(const Fwd& f)
         g.expert = -1;
         f.groups[tid] = g;
     }
-    if (tid == 0) {
-        f.n_active[0] = s_nact;
-        f.n_groups[0] = f.n_shared + s_nact;
+
+    // 4. bucketing into active expert groups (ascending expert id), each
+    //    group's assignments in assignment order
+    int cnt_e = 0, off_e = 0, idx_e = -1;
+    if (NT == 1) {
+        // one token: the K chosen experts are distinct, one assignment each
+        if (tid < E) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (k < K) {
+                    const int e = s_ids[k];
+                    off_e += e < tid;
+                    if (e == tid) {
+                        cnt_e = 1;
+                        idx_e = k;  // assignment index
+                    }
+                }
+            if (cnt_e) {
+                f.perm[off_e] = idx_e;
+                idx_e = off_e;  // group index = rank of the id among the chosen
+            }
+        }
+        if (tid == 0) {
+            f.n_active[0] = K;
+            f.n_groups[0] = f.n_shared + K;
+            f.off[E] = K;
+        }
+    } else {
+        const int n = T * K;
+        if (tid < n) atomicAdd(&s_cnt[s_ids[tid]], 1);
+        __syncthreads();
+        if (w == 0) {
+            int c4[4], a4[4], sc = 0, sa = 0;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                c4[m] = s_cnt[lane * 4 + m];
+                a4[m] = c4[m] > 0;
+                sc += c4[m];
+                sa += a4[m];
+            }
+            int ic = sc, ia = sa;  // inclusive wavefront scans
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int pc = __shfl_up(ic, o), pa = __shfl_up(ia, o);
+                if (lane >= o) {
+                    ic += pc;
+                    ia += pa;
+                }
+            }
+            int rc = ic - sc, ra = ia - sa;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                s_off[lane * 4 + m] = rc;
+                s_act[lane * 4 + m] = a4[m] ? ra : -1;
+                rc += c4[m];
+                ra += a4[m];
+            }
+            if (lane == 63) {
+                s_off[256] = rc;
+                s_nact = ra;
+            }
+        }
+        __syncthreads();
+        for (int a = tid; a < n; a += RT_THREADS) {
+            const int e = s_ids[a];
+            int rank = 0;
+            for (int b2 = 0; b2 < a; ++b2) rank += s_ids[b2] == e;
+            f.perm[s_off[e] + rank] = a;
+        }
+        if (tid < E) {
+            cnt_e = s_cnt[tid];
+            off_e = s_off[tid];
+            idx_e = s_act[tid];
+        }
+        if (tid == 0) {
+            f.n_active[0] = s_nact;
+            f.n_groups[0] = f.n_shared + s_nact;
+            f.off[E] = s_off[E];
+        }
+    }
+    if (tid < E) {
+        f.cnt[tid] = cnt_e;
+        f.off[tid] = off_e;
+        if (cnt_e > 0) {
+            f.active[idx_e] = tid;
+            Group g;
+            g.base = slot_e >= 0 ? f.pool + (size_t)slot_e * f.slot_bytes : nullptr;
+            g.cnt = cnt_e;
+            g.off = off_e;
+            g.kind = 0;
+            g.expert = tid;
+            f.groups[f.n_shared + idx_e] = g;
+            if (slot_e < 0) {
+                atomicOr(&f.status[0], (uint32_t)STATUS_NOT_RESIDENT);
+                const int code = f.layer * E + tid;
+                atomicOr(&f.status[1 + code / 32], 1u << (code % 32));
+            }
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
 // Small-T router: split-K GEMV over the interleaved router weights.
-// Workgroup (b, q) = expert block b (64 experts, one per lane) and RW
-// consecutive K-slices of 64 input columns (one per wavefront, 16 float4
-// chunks, all loads in flight at once), reduced in LDS in a fixed order.
-// Wavefronts of expert block 0 also form the token sums of their 64
-// columns (a group of the affine format) and the sums of squares.
-// Partials go to f.part / f.tpart (one per workgroup row q); the last
-// workgroup to arrive runs router_tail.
+// Workgroup (expert block b of 64, slice row q) has 4 wavefronts, each one of
+// 4 consecutive K-slices of 64 input columns (16 float4 chunks, all loads in
+// flight at once), reduced in LDS in a fixed order.  Wavefronts of expert
+// block 0 also form the token sums and sums of squares of their 64 columns
+// and stage them as an fp16 span for the expert GEMVs.  Partials go to
+// f.part / f.tpart (one row per workgroup row q); the last workgroup to
+// arrive runs router_tail.
 // ---------------------------------------------------------------------------
 
 template <int NT>
-__global__ void __launch_bounds__(512) k_router_small(Fwd f, const float* __restrict__ X)
+__global__ void __launch_bounds__(RT_THREADS) k_router_small(Fwd f, const float* __restrict__ X)
 {
-    __shared__ float red[8][NT][64];
-    __shared__ float sred[8][NT][2];
+    constexpr int RW = RT_THREADS / 64;
+    __shared__ float red[RW][NT][64];
+    __shared__ float sred[RW][NT][2];
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int RW = blockDim.x >> 6;
     const int b = blockIdx.x, s = blockIdx.y * RW + w;
     const int H = f.H, T = f.T, CH = H / 4;
     const __amdgpu_buffer_rsrc_t rw =
@@ -270,19 +396,22 @@ __global__ void __launch_bounds__(512) k_router_small(Fwd f, const float* __rest
         red[w][j][lane] = acc;
     }
     __syncthreads();
+    const int S = f.S, Sp = router_sp(T, S), S2p = router_s2p(S);
     for (int j = w; j < T; j += RW) {
         float acc = 0.f;
+#pragma unroll
         for (int v2 = 0; v2 < RW; ++v2) acc += red[v2][j][lane];
-        st_agent(&f.part[((size_t)blockIdx.y * T + j) * f.Epad + b * 64 + lane], acc);
+        st_agent(&f.part[(size_t)(b * 64 + lane) * Sp + j * S + blockIdx.y], acc);
     }
     if (b == 0 && w == 0 && lane < T) {
         float gs = 0.f, ss = 0.f;
+#pragma unroll
         for (int v2 = 0; v2 < RW; ++v2) {
             gs += sred[v2][lane][0];
             ss += sred[v2][lane][1];
         }
-        st_agent(&f.tpart[((size_t)blockIdx.y * T + lane) * 2 + 0], gs);
-        st_agent(&f.tpart[((size_t)blockIdx.y * T + lane) * 2 + 1], ss);
+        st_agent(&f.tpart[(size_t)lane * S2p + 2 * blockIdx.y + 0], gs);
+        st_agent(&f.tpart[(size_t)lane * S2p + 2 * blockIdx.y + 1], ss);
     }
 
     if (!arrive_block(&f.counters[0], gridDim.x * gridDim.y)) return;
@@ -293,15 +422,15 @@ __global__ void __launch_bounds__(512) k_router_small(Fwd f, const float* __rest
 // launchers
 // ---------------------------------------------------------------------------
 
+int router_small_slices(int H) { return (H / 64) / (RT_THREADS / 64); }
+
 hipError_t launch_router_small(const Fwd& f, hipStream_t st)
 {
-    const int slices = f.H / 64, rw = slices % 8 == 0 ? 8 : 4;
-    const dim3 grid(f.Epad / 64, slices / rw), block(rw * 64);
+    const dim3 grid(f.Epad / 64, router_small_slices(f.H)), block(RT_THREADS);
     if (f.T <= 1) hipLaunchKernelGGL(k_router_small<1>, grid, block, 0, st, f, f.x);
     else if (f.T <= 2) hipLaunchKernelGGL(k_router_small<2>, grid, block, 0, st, f, f.x);
     else if (f.T <= 4) hipLaunchKernelGGL(k_router_small<4>, grid, block, 0, st, f, f.x);
-    else if (f.T <= 8) hipLaunchKernelGGL(k_router_small<8>, grid, block, 0, st, f, f.x);
-    else hipLaunchKernelGGL(k_router_small<16>, grid, block, 0, st, f, f.x);
+    else hipLaunchKernelGGL(k_router_small<8>, grid, block, 0, st, f, f.x);
     return hipGetLastError();
 }
 

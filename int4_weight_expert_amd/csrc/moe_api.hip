@@ -97,14 +97,6 @@ size_t expert_bytes_for(int fmt, size_t H, size_t I)
     return 0;
 }
 
-// Partial rows of the small-T router: one per workgroup row of RW slices of
-// 64 input columns (RW = 8 wavefronts, or 4 when H/64 is not a multiple of 8)
-int router_slices(int H)
-{
-    const int slices = H / 64;
-    return slices / (slices % 8 == 0 ? 8 : 4);
-}
-
 // k-slices per (group, 64-row block) for a row of `chunks` 16-byte chunks:
 // the fewest that give about 3072 single-wavefront units (12 per CU), each
 // slice a whole number of rolling steps, within the partial buffer and the
@@ -183,7 +175,7 @@ Fwd make_fwd(moe_ctx* c, const float* x, float* out, int T, int layer, int resid
     f.shared = c->shared + (size_t)layer * g.n_shared * c->slot_bytes;
     f.part = c->part;
     f.tpart = c->tpart;
-    f.S = router_slices(g.hidden);
+    f.S = router_small_slices(g.hidden);
     f.logits = c->logits;
     f.ids = c->ids;
     f.wts = c->wts;

@@ -105,6 +105,7 @@ hipError_t launch_bucket(const int32_t* ids, int T, int K, int E, int32_t* cnt, 
 
 // forward pieces; `names` receives static kernel names for timing
 hipError_t launch_router_small(const Fwd& f, hipStream_t st);
+int router_small_slices(int H);  // partial rows of the small-T router
 hipError_t launch_router_large(const Fwd& f, hipStream_t st, int stage);
 hipError_t launch_gateup_gemv(const Fwd& f, hipStream_t st);
 hipError_t launch_down_gemv(const Fwd& f, hipStream_t st);
@@ -115,6 +116,6 @@ size_t gemv_lds_bytes(int chunks_per_slice, int T);
 int gemv_step_chunks(int which);
 int gemv_max_dn_ks();
 
-constexpr int ROUTER_SMALL_MAX_T = 16;
+constexpr int ROUTER_SMALL_MAX_T = 8;
 
 }  // namespace moe
