@@ -88,9 +88,9 @@ def time_eager(torch, step_fns, steps: int):
 
 
 def kernel_times(torch, ml, step_fns, steps: int):
-    """Average per-kernel durations (HIP events on the context's stream) over
-    `steps` eager steps; a short GPU sleep first lets the host queue run
-    ahead so that the events bracket kernels, not host gaps."""
+    """Average per-kernel durations from the library's marker events on its
+    stream over `steps` eager forwards; a short GPU sleep first lets the host
+    queue run ahead, so that the markers bracket kernels, not host gaps."""
     from int4_weight_expert_amd import moe as M
     L = len(step_fns)
     torch.cuda.synchronize()
@@ -141,7 +141,8 @@ def bench_decode(torch, args, result):
         "steps": n_timed,
         "roofline": {
             "bound": "hbm", "achieved": alg_gateup / t_gu / 1e9, "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": alg_gateup / t_gu / 1e9 / HBM_PEAK_GBS, "traffic": None,
+            "unit": "GB/s", "frac": alg_gateup / t_gu / 1e9 / HBM_PEAK_GBS,
+            "traffic": measured_traffic(),
             "kernel": "k_gu (int4 gate/up GEMV, one wavefront per (expert, 64-row block, k-slice))",
             "algorithmic_bytes_per_launch": alg_gateup,
             "avg_launch_ms": kt["gateup_gemv"],
@@ -239,6 +240,37 @@ def bench_prefill(torch, steps, result):
     torch.cuda.empty_cache()
 
 
+def copy_probe(torch, result):
+    """A plain device-to-device copy of known size (256 MiB read, 256 MiB
+    written, five times): the calibration kernel for the HBM byte counters."""
+    n = 64 << 20
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    result["extra"]["copy_probe"] = {"bytes_read_per_copy": n * 4, "bytes_written_per_copy": n * 4,
+                                     "copies": 5}
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the gate/up kernel from the committed counter
+    runs, if they were taken on the current kernel source (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    src = os.path.join(ROOT, "int4_weight_expert_amd", "csrc", "k_gemv.hip")
+    try:
+        rec = json.load(open(path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("k_gemv_sha256") != sha:
+        return None
+    return rec.get("k_gu_bytes_per_launch")
+
+
 def cpu_baseline(n_tok: int):
     """The oracle, as it stands, on a bounded sample of the decode workload:
     n_tok token-layers (T=1) of the 8-layer GLM decode, single-threaded, with
@@ -290,6 +322,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="only the decode workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=16)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this build "
@@ -312,6 +346,8 @@ def main():
         "extra": {},
     }
     bench_decode(torch, args, result)
+    if args.copy_probe:
+        copy_probe(torch, result)
     if not args.no_extra:
         bench_chain(torch, "glm_verify", 64, result)
         bench_chain(torch, "edge0_decode", 200, result)

@@ -175,15 +175,17 @@ const char *moe_last_error(moe_ctx *ctx);
 int moe_set_gemm_min_tokens(moe_ctx *ctx, int min_tokens);
 
 /* Per-kernel timing with HIP events on the context's stream.  While timing
- * is on, every moe_forward / moe_forward_residual / moe_route records an
- * event before each of its kernels and one after the last.
- * moe_timing_summary synchronises on the last event and returns, for each
+ * is on, every moe_forward / moe_forward_residual / moe_route records a
+ * marker event (created without a system-scope fence, so recording it writes
+ * back no caches) before each of its kernels and one after the last; a
+ * kernel's duration is the time between its marker and the next.
+ * moe_timing_summary synchronises on the last marker and returns, for each
  * kernel name in launch order, the average duration in milliseconds over
  * the forwards recorded since timing was switched on (or since the last
  * summary), then clears the record.  ms[i] and names[i] (static strings)
  * receive up to cap entries, *n their count, *n_forwards (optional) the
- * number of forwards averaged.  Timing adds event packets between kernels;
- * leave it off in production.  Errors: MOE_E_ARG, MOE_E_HIP. */
+ * number of forwards averaged.  Markers are not meant for graph capture.
+ * Errors: MOE_E_ARG, MOE_E_HIP (moe_last_error names the HIP error). */
 int moe_set_timing(moe_ctx *ctx, int on);
 int moe_timing_summary(moe_ctx *ctx, float *ms, const char **names, int cap, int *n,
                        int *n_forwards);

@@ -441,8 +441,7 @@ static hipError_t gu_launch(const Fwd& f, hipStream_t st)
     static bool big = false;
     hipError_t e0 = allow_lds(k_gu<FMT, NT>, lds, big);
     if (e0 != hipSuccess) return e0;
-    hipLaunchKernelGGL((k_gu<FMT, NT>), dim3(units), dim3(64), lds, st, f);
-    return hipGetLastError();
+    return launch_k(k_gu<FMT, NT>, dim3(units), dim3(64), lds, st, f);
 }
 
 template <int FMT, int NT>
@@ -454,8 +453,7 @@ static hipError_t dn_launch(const Fwd& f, hipStream_t st)
     static bool big = false;
     hipError_t e0 = allow_lds(k_dn<FMT, NT>, lds, big);
     if (e0 != hipSuccess) return e0;
-    hipLaunchKernelGGL((k_dn<FMT, NT>), dim3(units), dim3(64), lds, st, f);
-    return hipGetLastError();
+    return launch_k(k_dn<FMT, NT>, dim3(units), dim3(64), lds, st, f);
 }
 
 template <int FMT>
@@ -496,15 +494,13 @@ hipError_t launch_gateup_finalize(const Fwd& f, hipStream_t st)
 {
     const int n_rows = f.T * (f.K + f.n_shared);
     const int waves = n_rows * (f.I / 64);
-    hipLaunchKernelGGL(k_gu_fin, dim3((waves + 3) / 4), dim3(256), 0, st, f, n_rows);
-    return hipGetLastError();
+    return launch_k(k_gu_fin, dim3((waves + 3) / 4), dim3(256), 0, st, f, n_rows);
 }
 
 hipError_t launch_combine(const Fwd& f, hipStream_t st)
 {
     const int64_t n = (int64_t)f.T * f.H;
-    hipLaunchKernelGGL(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, f);
-    return hipGetLastError();
+    return launch_k(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, f);
 }
 
 }  // namespace moe

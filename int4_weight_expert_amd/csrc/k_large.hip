@@ -307,21 +307,14 @@ __global__ void __launch_bounds__(1024) k_bucket(const int32_t* __restrict__ ids
 hipError_t launch_router_large(const Fwd& f, hipStream_t st, int stage)
 {
     switch (stage) {
-    case 0:
-        hipLaunchKernelGGL(k_tokstats, dim3((f.T + 3) / 4), dim3(256), 0, st, f);
-        break;
+    case 0: return launch_k(k_tokstats, dim3((f.T + 3) / 4), dim3(256), 0, st, f);
     case 1:
-        hipLaunchKernelGGL(k_router_gemm, dim3((f.T + 31) / 32, f.Epad / 64), dim3(256), 0, st, f);
-        break;
-    case 2:
-        hipLaunchKernelGGL(k_topk, dim3((f.T + 3) / 4), dim3(256), 0, st, f);
-        break;
+        return launch_k(k_router_gemm, dim3((f.T + 31) / 32, f.Epad / 64), dim3(256), 0, st, f);
+    case 2: return launch_k(k_topk, dim3((f.T + 3) / 4), dim3(256), 0, st, f);
     default:
-        hipLaunchKernelGGL(k_bucket, dim3(1), dim3(1024), 0, st, (const int32_t*)f.ids, f.T * f.K,
-                           f.E, f.cnt, f.off, f.perm, f.active, f.n_active, f, 1);
-        break;
+        return launch_k(k_bucket, dim3(1), dim3(1024), 0, st, (const int32_t*)f.ids, f.T * f.K,
+                        f.E, f.cnt, f.off, f.perm, f.active, f.n_active, f, 1);
     }
-    return hipGetLastError();
 }
 
 hipError_t launch_bucket(const int32_t* ids, int T, int K, int E, int32_t* cnt, int32_t* off,

@@ -427,11 +427,10 @@ int router_small_slices(int H) { return (H / 64) / (RT_THREADS / 64); }
 hipError_t launch_router_small(const Fwd& f, hipStream_t st)
 {
     const dim3 grid(f.Epad / 64, router_small_slices(f.H)), block(RT_THREADS);
-    if (f.T <= 1) hipLaunchKernelGGL(k_router_small<1>, grid, block, 0, st, f, f.x);
-    else if (f.T <= 2) hipLaunchKernelGGL(k_router_small<2>, grid, block, 0, st, f, f.x);
-    else if (f.T <= 4) hipLaunchKernelGGL(k_router_small<4>, grid, block, 0, st, f, f.x);
-    else hipLaunchKernelGGL(k_router_small<8>, grid, block, 0, st, f, f.x);
-    return hipGetLastError();
+    if (f.T <= 1) return launch_k(k_router_small<1>, grid, block, 0, st, f, f.x);
+    if (f.T <= 2) return launch_k(k_router_small<2>, grid, block, 0, st, f, f.x);
+    if (f.T <= 4) return launch_k(k_router_small<4>, grid, block, 0, st, f, f.x);
+    return launch_k(k_router_small<8>, grid, block, 0, st, f, f.x);
 }
 
 }  // namespace moe

@@ -59,8 +59,8 @@ struct moe_ctx {
     hipError_t last_err = hipSuccess;
     // timing
     bool timing = false;
-    std::vector<hipEvent_t> events;  // pool, reused after each summary
-    std::vector<const char*> names;  // per mark; nullptr = end of a forward
+    std::vector<hipEvent_t> events;  // marker pool, reused after each summary
+    std::vector<const char*> names;  // per marker: kernel that follows; nullptr = end of a forward
     int n_marks = 0;
     std::vector<void*> allocs;
 };
@@ -135,12 +135,16 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb)
     return pa < pb + nb && pb < pa + na;
 }
 
+// Timing: a marker event before each kernel (named for it) and one after
+// the last kernel of a forward (name == nullptr).
 void mark(moe_ctx* c, const char* name)
 {
     if (!c->timing) return;
     if (c->n_marks >= (int)c->events.size()) {
+        // no system-scope fence on record: a marker then costs no cache
+        // write-back and brackets the kernels closely
         hipEvent_t e;
-        if (hipEventCreate(&e) != hipSuccess) return;
+        if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return;
         c->events.push_back(e);
         c->names.push_back(nullptr);
     }
@@ -550,15 +554,16 @@ int moe_timing_summary(moe_ctx* c, float* ms, const char** names, int cap, int* 
         c->n_marks = 0;
         return MOE_OK;
     }
-    if (hipEventSynchronize(c->events[c->n_marks - 1]) != hipSuccess) return MOE_E_HIP;
+    if (hipEventSynchronize(c->events[c->n_marks - 1]) != hipSuccess) return hip_rc(c, hipErrorUnknown);
     std::vector<const char*> order;
     std::vector<double> sum;
     std::vector<int> count;
     int forwards = 0;
     for (int i = 0; i + 1 < c->n_marks; ++i) {
-        if (c->names[i] == nullptr) continue;  // end mark of a forward
+        if (c->names[i] == nullptr) continue;  // end marker of a forward
         float v = 0.f;
-        if (hipEventElapsedTime(&v, c->events[i], c->events[i + 1]) != hipSuccess) return MOE_E_HIP;
+        const hipError_t e = hipEventElapsedTime(&v, c->events[i], c->events[i + 1]);
+        if (e != hipSuccess) return hip_rc(c, e);
         size_t k = 0;
         while (k < order.size() && strcmp(order[k], c->names[i]) != 0) ++k;
         if (k == order.size()) {

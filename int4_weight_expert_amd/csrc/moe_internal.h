@@ -103,7 +103,17 @@ hipError_t launch_router_to_internal(const float* W, float* wr, int E, int Epad,
 hipError_t launch_bucket(const int32_t* ids, int T, int K, int E, int32_t* cnt, int32_t* off,
                          int32_t* perm, int32_t* active, int32_t* n_active, hipStream_t st);
 
-// forward pieces; `names` receives static kernel names for timing
+// Typed kernel launch (arguments converted to the kernel's parameter types).
+template <typename... KArgs, typename... Args>
+hipError_t launch_k(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds,
+                    hipStream_t st, Args... args)
+{
+    static_assert(sizeof...(KArgs) == sizeof...(Args), "kernel argument count");
+    hipLaunchKernelGGL(kernel, grid, block, lds, st, static_cast<KArgs>(args)...);
+    return hipGetLastError();
+}
+
+// forward pieces
 hipError_t launch_router_small(const Fwd& f, hipStream_t st);
 int router_small_slices(int H);  // partial rows of the small-T router
 hipError_t launch_router_large(const Fwd& f, hipStream_t st, int stage);

@@ -203,7 +203,7 @@ def moe_set_gemm_min_tokens(ctx, n) -> int:
 
 
 def moe_set_timing(ctx, on: bool) -> int:
-    return _check("moe_set_timing", lib().moe_set_timing(ctx, int(on)))
+    return _check("moe_set_timing", lib().moe_set_timing(ctx, int(on)), ctx)
 
 
 def moe_timing_summary(ctx, cap: int = 32) -> tuple[list[tuple[str, float]], int]:
@@ -213,7 +213,7 @@ def moe_timing_summary(ctx, cap: int = 32) -> tuple[list[tuple[str, float]], int
     n = ctypes.c_int(0)
     nf = ctypes.c_int(0)
     _check("moe_timing_summary",
-           lib().moe_timing_summary(ctx, ms, names, cap, ctypes.byref(n), ctypes.byref(nf)))
+           lib().moe_timing_summary(ctx, ms, names, cap, ctypes.byref(n), ctypes.byref(nf)), ctx)
     return [(names[i].decode(), ms[i]) for i in range(min(n.value, cap))], nf.value
 
 
