@@ -1,0 +1,370 @@
+// k_gemm.hip -- the expert FFN for many tokens as MFMA grouped GEMMs.
+//
+// What is computed, cited by page title and section:
+//   "惊呆了！25GB 内存上运行 GLM 5.2 744B 模型" (reader.mx) §11: each chosen
+//     expert is SwiGLU on the rows routed to it (gate/up -> silu(g)*u ->
+//     down), each expert's weights read once for all of its rows; §04
+//     siluf(x) = x/(1+exp(-x)).
+//   GLM-5.2 dataflow page (devpress.csdn.net) §三 Step 6b-6d: 6144 -> 2048 ->
+//     6144 experts plus the always-active shared expert.
+// With hundreds of rows per expert the step is a dense contraction, so it
+// runs on the matrix cores: per expert group, [rows x H] . [H x I] twice
+// (gate and up, SiLU(gate)*up fused into the epilogue), then
+// [rows x I] . [I x H] (down).
+//
+// Operands.  Activations (x, then h) are staged per row as fp16 after an
+// exact power-of-two scale 2^k (largest magnitude in [2^13, 2^14)), in the
+// pair order of k_common.h (x0 x4 x1 x5 x2 x6 x3 x7 per 8 inputs), with the
+// row's (2^-k, sum of its fp16 values).  Codes become fp16 1024 + 16 n in
+// registers (3 shifts and 4 bit-field inserts per 8 codes), already in the
+// same pair order, so each v_mfma_f32_32x32x16_f16 multiplies matching
+// inputs; the epilogue recovers sum c x = acc/16 - 72 S (row format codes
+// are stored c + 8) and applies 2^-k and the fp32 row scale.  Accumulation
+// is fp32 in the matrix cores.
+//
+// Tiling.  A work item is (expert group, 128 rows of it, N tile) on a
+// workgroup of 4 wavefronts.  Gate/up: the N tile is 128 output rows; each
+// wavefront owns 32 of them in both matrices (two 32-column MFMA blocks).
+// Down: the N tile is 256 output rows, 64 per wavefront (two blocks).  Each
+// wavefront covers the 128 rows as four 32-row blocks: 8 accumulator tiles.
+// Per K step of 32 inputs (one 16-byte chunk of codes per output row): the
+// activation tile (128 x 32 fp16) is double-buffered in LDS, piece-major so
+// the A-operand reads are conflict-free; every wavefront loads its own codes
+// straight into registers (16 bytes per lane: the MFMA B operand needs 8
+// codes of one row per lane, lanes l and l+32 taking the two halves of a
+// chunk), GDEP steps ahead.
+#include "k_common.h"
+
+namespace moe {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float float16 __attribute__((ext_vector_type(16)));
+
+constexpr int GM = 128;    // rows per tile
+constexpr int GDEP = 4;    // K steps of codes in flight per wavefront
+
+enum { GEMM_GU = 0, GEMM_DN = 1 };
+
+// Row j of an expert group: token t and row r (as tok_rows, per lane).
+__device__ __forceinline__ void tok_rows_lane(const Fwd& f, const Group& g, int j, int& t, int& r)
+{
+    if (g.kind == 0) {
+        const int a = f.perm[g.off + j];
+        t = a / f.K;
+        r = a;
+    } else {
+        t = j;
+        r = f.T * f.K + g.off * f.T + j;
+    }
+}
+
+__device__ __forceinline__ half8 as_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
+{
+    return __builtin_bit_cast(half8, make_uint4(a, b, c, d));
+}
+
+// B operand of one 16-input half of a chunk: dword `d` of a row's 16 bytes
+__device__ __forceinline__ half8 b_operand(uint32_t dword, uint32_t mv)
+{
+    uint32_t p0, p1, p2, p3;
+    nib_pairs(dword, mv, p0, p1, p2, p3);
+    return as_half8(p0, p1, p2, p3);
+}
+
+template <int MODE>
+__global__ void __launch_bounds__(256, 2) k_gemm(Fwd f)
+{
+    __shared__ uint4 As[2][4][GM];  // [buffer][16-byte piece][row]
+    __shared__ int s_src[GM], s_out[GM];
+    __shared__ float s_inv[GM], s_sum[GM], s_rs[GM];
+
+    const int tile = blockIdx.x;
+    if (tile >= uni(f.n_tiles[0])) return;
+    const int2 td = f.tiles[tile];
+    const Group grp = uni_group(f.groups, uni(td.x));
+    const int m0 = uni(td.y);
+    const int rows = min(GM, grp.cnt - m0);
+    const int tid = threadIdx.x, lane = tid & 63, w = uni(tid >> 6);
+    const int n = lane & 31, half = lane >> 5;
+    const int H = f.H, I = f.I;
+    const int K = MODE == GEMM_GU ? H : I;  // reduction length
+    const int NC = K / 32;                  // K steps (chunks)
+
+    // per-row data of the tile
+    if (tid < GM) {
+        int src = -1, out = -1;
+        float inv = 0.f, S = 0.f, rs = 1.f;
+        if (tid < rows) {
+            int t, r;
+            tok_rows_lane(f, grp, m0 + tid, t, r);
+            out = r;
+            if (MODE == GEMM_GU) {
+                src = t;
+                const float2 xs = f.xrow[t];
+                inv = xs.x;
+                S = xs.y;
+                rs = f.tok[t].rscale;
+            } else {
+                src = r;
+                const float2 hs = f.hrow[r];
+                inv = hs.x;
+                S = hs.y;
+            }
+        }
+        s_src[tid] = src;
+        s_out[tid] = out;
+        s_inv[tid] = inv;
+        s_sum[tid] = S;
+        s_rs[tid] = rs;
+    }
+    __syncthreads();
+
+    // output rows of this wavefront's two B blocks, and their weight streams
+    const uint8_t* base = grp.base;
+    int o0, o1;
+    size_t mat0, mat1;
+    if (MODE == GEMM_GU) {
+        o0 = blockIdx.y * 128 + 32 * w + n;  // gate and up of the same row
+        o1 = o0;
+        mat0 = 0;
+        mat1 = (size_t)I * H / 2;
+    } else {
+        o0 = blockIdx.y * 256 + 64 * w + n;  // rows n and n + 32 of one block
+        o1 = o0 + 32;
+        mat0 = mat1 = (size_t)I * H;
+    }
+    const uint8_t* tab = base + (size_t)3 * H * I / 2;  // fp32 row scales
+
+    if (base == nullptr) {
+        // expert not resident: no contribution (the router flagged it)
+        for (int i = 0; i < rows; ++i) {
+            if (MODE == GEMM_GU) {
+                if (lane < 32) f.hbuf[(size_t)s_out[i] * I + o0] = 0.f;
+            } else {
+                if (lane < 32) {
+                    f.ypart[(size_t)s_out[i] * H + o0] = 0.f;
+                    f.ypart[(size_t)s_out[i] * H + o1] = 0.f;
+                }
+            }
+        }
+        return;
+    }
+
+    const uint32_t mv = magic_vgpr();
+    const int C = NC;  // chunks per weight row
+    const __amdgpu_buffer_rsrc_t rw0 =
+        make_rsrc(base + mat0 + (size_t)(o0 / 64) * C * 1024, (uint32_t)C * 1024);
+    const __amdgpu_buffer_rsrc_t rw1 =
+        make_rsrc(base + mat1 + (size_t)(o1 / 64) * C * 1024, (uint32_t)C * 1024);
+    const uint32_t v0 = (uint32_t)(o0 & 63) * 16, v1 = (uint32_t)(o1 & 63) * 16;
+
+    // activation loader: thread -> row tid/2, pieces 2*(tid&1) + {0, 1}
+    const int arow = tid >> 1, apc = (tid & 1) * 2;
+    const int asrc = s_src[arow];
+    const uint4* Ag = nullptr;
+    if (asrc >= 0)
+        Ag = (MODE == GEMM_GU ? f.xq + (size_t)asrc * (H / 8) : f.hq + (size_t)asrc * (I / 8)) +
+             apc;
+    const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+
+    float16 acc[4][2];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+        acc[mb][0] = (float16){};
+        acc[mb][1] = (float16){};
+    }
+
+    // prologue: chunk 0 into LDS buffer 0, chunk 1 in registers, GDEP
+    // chunks of codes in flight
+    uint4 na0 = z4, na1 = z4;
+    if (Ag) {
+        na0 = Ag[0];
+        na1 = Ag[1];
+    }
+    As[0][apc][arow] = na0;
+    As[0][apc + 1][arow] = na1;
+    na0 = na1 = z4;
+    if (Ag && NC > 1) {
+        na0 = Ag[4];
+        na1 = Ag[5];
+    }
+    uint4 B0[GDEP], B1[GDEP];
+#pragma unroll
+    for (int k = 0; k < GDEP; ++k) {
+        B0[k] = bload16(rw0, v0 + k * 1024, 0);
+        B1[k] = bload16(rw1, v1 + k * 1024, 0);
+    }
+    __syncthreads();
+
+#pragma unroll 1
+    for (int c0 = 0; c0 < NC; c0 += GDEP) {
+#pragma unroll
+        for (int k = 0; k < GDEP; ++k) {
+            const int c = c0 + k;
+            // next activation chunk into the other buffer (its readers of
+            // step c - 1 passed the barrier); then fetch the one after
+            if (c + 1 < NC) {
+                As[(c + 1) & 1][apc][arow] = na0;
+                As[(c + 1) & 1][apc + 1][arow] = na1;
+            }
+            if (c + 2 < NC && Ag) {
+                na0 = Ag[(c + 2) * 4];
+                na1 = Ag[(c + 2) * 4 + 1];
+            }
+            // codes of step c; refill the slot with step c + GDEP (a load
+            // past the row's last chunk returns zeros)
+            const uint4 w0 = B0[k], w1 = B1[k];
+            B0[k] = bload16(rw0, v0 + (c + GDEP) * 1024, 0);
+            B1[k] = bload16(rw1, v1 + (c + GDEP) * 1024, 0);
+            // lane half h takes dwords h (inputs 8h..8h+7) and 2 + h (16 + 8h..)
+            const half8 b00 = b_operand(half ? w0.y : w0.x, mv);
+            const half8 b01 = b_operand(half ? w0.w : w0.z, mv);
+            const half8 b10 = b_operand(half ? w1.y : w1.x, mv);
+            const half8 b11 = b_operand(half ? w1.w : w1.z, mv);
+            const uint4(*Ab)[GM] = As[c & 1];
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                const half8 a0 = __builtin_bit_cast(half8, Ab[half][32 * mb + n]);
+                const half8 a1 = __builtin_bit_cast(half8, Ab[2 + half][32 * mb + n]);
+                acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b00, acc[mb][0], 0, 0, 0);
+                acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b10, acc[mb][1], 0, 0, 0);
+                acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b01, acc[mb][0], 0, 0, 0);
+                acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b11, acc[mb][1], 0, 0, 0);
+            }
+            __syncthreads();
+        }
+    }
+
+    // epilogue: lane holds column o of each block, rows (j/4)*8 + half*4 + j%4
+    if (MODE == GEMM_GU) {
+        const float sg = ((const float*)tab)[o0], su = ((const float*)tab)[I + o0];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int i = 32 * mb + (j >> 2) * 8 + half * 4 + (j & 3);
+                if (i < rows) {
+                    const float sc = s_inv[i] * s_rs[i];
+                    const float g = fmaf(acc[mb][0][j], 0.0625f, -72.f * s_sum[i]) * sc * sg;
+                    const float u = fmaf(acc[mb][1][j], 0.0625f, -72.f * s_sum[i]) * sc * su;
+                    f.hbuf[(size_t)s_out[i] * I + o0] = g / (1.0f + expf(-g)) * u;
+                }
+            }
+    } else {
+        const float sd0 = ((const float*)tab)[2 * I + o0], sd1 = ((const float*)tab)[2 * I + o1];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int i = 32 * mb + (j >> 2) * 8 + half * 4 + (j & 3);
+                if (i < rows) {
+                    const float sc = s_inv[i];
+                    float* y = f.ypart + (size_t)s_out[i] * H;
+                    y[o0] = fmaf(acc[mb][0][j], 0.0625f, -72.f * s_sum[i]) * sc * sd0;
+                    y[o1] = fmaf(acc[mb][1][j], 0.0625f, -72.f * s_sum[i]) * sc * sd1;
+                }
+            }
+    }
+}
+
+// Per-row fp16 staging (one wavefront per row of `len` fp32 values):
+// q [rows][len/8] in pair order, s[row] = (2^-k, sum of the fp16 values).
+__global__ void __launch_bounds__(256) k_rowstage(const float* __restrict__ src, int n_rows,
+                                                  int len, uint4* __restrict__ q,
+                                                  float2* __restrict__ s)
+{
+    const int lane = threadIdx.x & 63;
+    const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= n_rows) return;
+    const float4* row = (const float4*)(src + (size_t)r * len);
+    const int n4 = len / 4;
+    float m = 0.f;
+    for (int i = lane; i < n4; i += 64) {
+        const float4 v = row[i];
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
+    m = wave_max(m);
+    int e;
+    frexpf(m, &e);
+    e = max(e, -100);
+    const float sc = ldexpf(1.0f, 14 - e);
+    float t = 0.f;
+    uint4* qr = q + (size_t)r * (len / 8);
+    for (int g = lane; g < len / 8; g += 64) {
+        const float4 a = row[2 * g], b = row[2 * g + 1];
+        const _Float16 h0 = (_Float16)(a.x * sc), h1 = (_Float16)(a.y * sc);
+        const _Float16 h2 = (_Float16)(a.z * sc), h3 = (_Float16)(a.w * sc);
+        const _Float16 h4 = (_Float16)(b.x * sc), h5 = (_Float16)(b.y * sc);
+        const _Float16 h6 = (_Float16)(b.z * sc), h7 = (_Float16)(b.w * sc);
+        qr[g] = make_uint4(pack_h2(h0, h4), pack_h2(h1, h5), pack_h2(h2, h6), pack_h2(h3, h7));
+        t += (((float)h0 + (float)h1) + ((float)h2 + (float)h3)) +
+             (((float)h4 + (float)h5) + ((float)h6 + (float)h7));
+    }
+    t = wave_sum(t);
+    if (lane == 0) s[r] = make_float2(ldexpf(1.0f, e - 14), t);
+}
+
+// Tile list: each active group's rows in tiles of GM, groups in order.
+__global__ void __launch_bounds__(512) k_tiles(Fwd f)
+{
+    __shared__ int s_n[512];
+    __shared__ int s_tot;
+    const int tid = threadIdx.x;
+    const int ng = f.n_groups[0];
+    int nt = 0;
+    if (tid < ng) nt = (f.groups[tid].cnt + GM - 1) / GM;
+    s_n[tid] = nt;
+    __syncthreads();
+    // inclusive scan (Hillis-Steele over 512 entries)
+    for (int o = 1; o < 512; o <<= 1) {
+        const int v = tid >= o ? s_n[tid - o] : 0;
+        __syncthreads();
+        s_n[tid] += v;
+        __syncthreads();
+    }
+    const int start = s_n[tid] - nt;
+    for (int i = 0; i < nt; ++i) f.tiles[start + i] = make_int2(tid, i * GM);
+    if (tid == 511) s_tot = s_n[511];
+    __syncthreads();
+    if (tid == 0) f.n_tiles[0] = s_tot;
+}
+
+// ---------------------------------------------------------------------------
+// launch
+// ---------------------------------------------------------------------------
+
+int gemm_max_tiles(int T, int K, int E, int n_shared)
+{
+    const int64_t routed = (int64_t)T * K;
+    return (int)((routed + GM - 1) / GM + std::min<int64_t>(E, routed) +
+                 (int64_t)n_shared * ((T + GM - 1) / GM));
+}
+
+hipError_t launch_gemm_prep(const Fwd& f, hipStream_t st)
+{
+    hipError_t e = launch_k(k_rowstage, dim3((f.T + 3) / 4), dim3(256), 0, st, f.x, f.T, f.H,
+                            f.xq, f.xrow);
+    if (e != hipSuccess) return e;
+    return launch_k(k_tiles, dim3(1), dim3(512), 0, st, f);
+}
+
+hipError_t launch_gemm_gateup(const Fwd& f, hipStream_t st)
+{
+    const int mt = gemm_max_tiles(f.T, f.K, f.E, f.n_shared);
+    return launch_k(k_gemm<GEMM_GU>, dim3(mt, f.I / 128), dim3(256), 0, st, f);
+}
+
+hipError_t launch_gemm_hstage(const Fwd& f, hipStream_t st)
+{
+    const int rows = f.T * (f.K + f.n_shared);
+    return launch_k(k_rowstage, dim3((rows + 3) / 4), dim3(256), 0, st, (const float*)f.hbuf,
+                    rows, f.I, f.hq, f.hrow);
+}
+
+hipError_t launch_gemm_down(const Fwd& f, hipStream_t st)
+{
+    const int mt = gemm_max_tiles(f.T, f.K, f.E, f.n_shared);
+    return launch_k(k_gemm<GEMM_DN>, dim3(mt, f.H / 256), dim3(256), 0, st, f);
+}
+
+}  // namespace moe

@@ -51,6 +51,11 @@ struct moe_ctx {
     size_t gpart_bytes = 0;
     float* ypart = nullptr;
     size_t ypart_bytes = 0;
+    float2* xrow = nullptr;
+    float2* hrow = nullptr;
+    float* hbuf = nullptr;
+    int2* tiles = nullptr;
+    int32_t* n_tiles = nullptr;
     uint32_t* counters = nullptr;
     uint32_t* status = nullptr;
     size_t status_words = 0;
@@ -197,6 +202,11 @@ Fwd make_fwd(moe_ctx* c, const float* x, float* out, int T, int layer, int resid
     f.hsc = c->hsc;
     f.gpart = c->gpart;
     f.ypart = c->ypart;
+    f.xrow = c->xrow;
+    f.hrow = c->hrow;
+    f.hbuf = c->hbuf;
+    f.tiles = c->tiles;
+    f.n_tiles = c->n_tiles;
     f.counters = c->counters;
     f.status = c->status;
     f.n_layers = g.n_layers;
@@ -221,6 +231,37 @@ int run_router(moe_ctx* c, const Fwd& f)
     return MOE_OK;
 }
 
+// Many tokens (row format): the expert FFN as MFMA grouped GEMMs.
+bool uses_gemm(const moe_ctx* c, int T)
+{
+    return c->hbuf != nullptr && T > ROUTER_SMALL_MAX_T && T >= c->gemm_min_tokens;
+}
+
+int run_forward_gemm(moe_ctx* c, Fwd& f)
+{
+    f.gu_ks = 1;
+    f.dn_ks = 1;  // combine reads ypart as [rows][H]
+    int rc = run_router(c, f);
+    if (rc) return rc;
+    mark(c, "gemm_prep");
+    rc = hip_rc(c, launch_gemm_prep(f, c->stream));
+    if (rc) return rc;
+    mark(c, "gemm_gateup");
+    rc = hip_rc(c, launch_gemm_gateup(f, c->stream));
+    if (rc) return rc;
+    mark(c, "gemm_hstage");
+    rc = hip_rc(c, launch_gemm_hstage(f, c->stream));
+    if (rc) return rc;
+    mark(c, "gemm_down");
+    rc = hip_rc(c, launch_gemm_down(f, c->stream));
+    if (rc) return rc;
+    mark(c, "combine");
+    rc = hip_rc(c, launch_combine(f, c->stream));
+    if (rc) return rc;
+    mark(c, nullptr);
+    return MOE_OK;
+}
+
 int run_forward(moe_ctx* c, const float* x, int T, int layer, float* out, int residual)
 {
     if (!c || !x || !out) return MOE_E_ARG;
@@ -229,6 +270,7 @@ int run_forward(moe_ctx* c, const float* x, int T, int layer, float* out, int re
     const size_t nb = (size_t)T * g.hidden * sizeof(float);
     if (!residual && overlaps(x, nb, out, nb)) return MOE_E_ARG;
     Fwd f = make_fwd(c, x, out, T, layer, residual);
+    if (uses_gemm(c, T)) return run_forward_gemm(c, f);
     plan_gemv(c, f);
     int rc = run_router(c, f);
     if (rc) return rc;
@@ -361,6 +403,14 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
     }
     rc = rc ? rc : dalloc(c, &c->gpart, c->gpart_bytes);
     rc = rc ? rc : dalloc(c, &c->ypart, c->ypart_bytes);
+    if (g.wfmt == MOE_W_INT4_ROW && Tm > ROUTER_SMALL_MAX_T) {
+        // grouped-GEMM path workspace
+        rc = rc ? rc : dalloc(c, &c->xrow, Tm * 8);
+        rc = rc ? rc : dalloc(c, &c->hrow, rows * 8);
+        rc = rc ? rc : dalloc(c, &c->hbuf, rows * I * 4);
+        rc = rc ? rc : dalloc(c, &c->tiles, (size_t)gemm_max_tiles((int)Tm, (int)K, E, g.n_shared) * 8);
+        rc = rc ? rc : dalloc(c, &c->n_tiles, 4);
+    }
     rc = rc ? rc : dalloc(c, &c->counters, (1 + H / 64) * 4);
     c->status_words = 1 + (L * E + 31) / 32;
     rc = rc ? rc : dalloc(c, &c->status, c->status_words * 4);

@@ -84,7 +84,13 @@ struct Fwd {
     int gu_ks;            // gate/up: k-slices (units) per (group, 64-row block)
     int dn_ks;            // down: same, at most gemv_max_dn_ks()
     float* gpart;         // [rows][I/64][gu_ks][2][64] gate/up partials (gu_ks > 1)
-    float* ypart;         // [rows][H/64][dn_ks][64] down partials
+    float* ypart;         // [rows][H/64][dn_ks][64] down partials ([rows][H] when dn_ks = 1)
+    // grouped-GEMM path (many tokens): x and h staged per row in xq / hq
+    float2* xrow;         // [T] per token (2^-k, sum of its fp16 values)
+    float2* hrow;         // [rows]
+    float* hbuf;          // [rows][I] h in fp32 (gate/up GEMM output)
+    int2* tiles;          // [max tiles] (group index, first row) of each 128-row tile
+    int32_t* n_tiles;     // [1]
 };
 
 enum { STATUS_NOT_RESIDENT = 1u, STATUS_RANGE = 2u };
@@ -120,6 +126,11 @@ hipError_t launch_router_large(const Fwd& f, hipStream_t st, int stage);
 hipError_t launch_gateup_gemv(const Fwd& f, hipStream_t st);
 hipError_t launch_down_gemv(const Fwd& f, hipStream_t st);
 bool gateup_needs_finalize(const Fwd& f);
+int gemm_max_tiles(int T, int K, int E, int n_shared);
+hipError_t launch_gemm_prep(const Fwd& f, hipStream_t st);
+hipError_t launch_gemm_gateup(const Fwd& f, hipStream_t st);
+hipError_t launch_gemm_hstage(const Fwd& f, hipStream_t st);
+hipError_t launch_gemm_down(const Fwd& f, hipStream_t st);
 hipError_t launch_gateup_finalize(const Fwd& f, hipStream_t st);
 hipError_t launch_combine(const Fwd& f, hipStream_t st);
 size_t gemv_lds_bytes(int chunks_per_slice, int T);
