@@ -217,7 +217,11 @@ def bench_prefill(torch, steps, result):
     x = workload.tokens_device(cfg)
     out = torch.empty_like(x)
     ids, _ = ml.route(x, 0)
-    distinct = len(np.unique(ids.cpu().numpy()))
+    ids_np = ids.cpu().numpy()
+    distinct = len(np.unique(ids_np))
+    counts = np.bincount(ids_np.ravel(), minlength=cfg.E)
+    tiles = int(np.sum((counts + 127) // 128) + cfg.n_shared * ((cfg.T + 127) // 128))
+    rows = int(counts.sum() + cfg.n_shared * cfg.T)
     ml.forward(x, 0, out)
     torch.cuda.synchronize()
     n = max(2, steps)
@@ -233,6 +237,8 @@ def bench_prefill(torch, steps, result):
         "expert_flops": flops, "tflops": flops / t / 1e12,
         "frac_fp16_mfma_peak": flops / t / 1e12 / BF16_PEAK_TFLOPS,
         "distinct_experts": distinct, "kernel_avg_ms": kt,
+        "tokens_per_expert_max": int(counts.max()), "gemm_tiles_128": tiles,
+        "gemm_row_occupancy": rows / (tiles * 128.0),
     }
     log(f"[bench] glm_prefill: {t * 1e3:.2f} ms/layer, {flops / t / 1e12:.1f} TFLOP/s; {kt}")
     ml.close()
@@ -322,6 +328,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="only the decode workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=16)
+    ap.add_argument("--only", choices=["decode", "verify", "edge0", "edge0_k8", "prefill"],
+                    help="run one workload only (for profiling); the JSON line then "
+                         "carries that workload in extra")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -345,10 +354,17 @@ def main():
                    "activations": "fp32"},
         "extra": {},
     }
+    if args.only and args.only != "decode":
+        {"verify": lambda: bench_chain(torch, "glm_verify", 64, result),
+         "edge0": lambda: bench_chain(torch, "edge0_decode", 200, result),
+         "edge0_k8": lambda: bench_chain(torch, "edge0_decode_k8", 200, result),
+         "prefill": lambda: bench_prefill(torch, 3, result)}[args.only]()
+        print(json.dumps(result), flush=True)
+        return
     bench_decode(torch, args, result)
     if args.copy_probe:
         copy_probe(torch, result)
-    if not args.no_extra:
+    if not args.no_extra and not args.only:
         bench_chain(torch, "glm_verify", 64, result)
         bench_chain(torch, "edge0_decode", 200, result)
         bench_chain(torch, "edge0_decode_k8", 200, result)

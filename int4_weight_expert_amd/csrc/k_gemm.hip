@@ -23,16 +23,18 @@
 // is fp32 in the matrix cores.
 //
 // Tiling.  A work item is (expert group, 128 rows of it, N tile) on a
-// workgroup of 4 wavefronts.  Gate/up: the N tile is 128 output rows; each
+// workgroup of 8 wavefronts.  Gate/up: the N tile is 256 output rows; each
 // wavefront owns 32 of them in both matrices (two 32-column MFMA blocks).
-// Down: the N tile is 256 output rows, 64 per wavefront (two blocks).  Each
+// Down: the N tile is 512 output rows, 64 per wavefront (two blocks).  Wide
+// N tiles let one staged activation tile feed many output columns: the
+// activations (2 bytes per input) are the larger share of operand traffic.  Each
 // wavefront covers the 128 rows as four 32-row blocks: 8 accumulator tiles.
 // Per K step of 32 inputs (one 16-byte chunk of codes per output row): the
 // activation tile (128 x 32 fp16) is double-buffered in LDS, piece-major so
 // the A-operand reads are conflict-free; every wavefront loads its own codes
 // straight into registers (16 bytes per lane: the MFMA B operand needs 8
 // codes of one row per lane, lanes l and l+32 taking the two halves of a
-// chunk), GDEP steps ahead.
+// chunk).  Activations and codes are fetched GDEP steps ahead.
 #include "k_common.h"
 
 namespace moe {
@@ -41,7 +43,8 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float16 __attribute__((ext_vector_type(16)));
 
 constexpr int GM = 128;    // rows per tile
-constexpr int GDEP = 4;    // K steps of codes in flight per wavefront
+constexpr int GDEP = 8;    // K steps of activations and codes in flight
+constexpr int GW = 8;      // wavefronts per workgroup
 
 enum { GEMM_GU = 0, GEMM_DN = 1 };
 
@@ -72,14 +75,25 @@ __device__ __forceinline__ half8 b_operand(uint32_t dword, uint32_t mv)
 }
 
 template <int MODE>
-__global__ void __launch_bounds__(256, 2) k_gemm(Fwd f)
+__global__ void __launch_bounds__(64 * GW, 1) k_gemm(Fwd f)
 {
     __shared__ uint4 As[2][4][GM];  // [buffer][16-byte piece][row]
     __shared__ int s_src[GM], s_out[GM];
     __shared__ float s_inv[GM], s_sum[GM], s_rs[GM];
 
-    const int tile = blockIdx.x;
-    if (tile >= uni(f.n_tiles[0])) return;
+    // Workgroup -> (tile, N tile), XCD-aware: workgroup p runs on XCD p % 8,
+    // so XCD x takes a contiguous range of the actual tiles with the N tiles
+    // innermost.  The workgroups sharing a tile's activations (all its N
+    // tiles), and neighbouring tiles of the same expert sharing weights, then
+    // run together behind one L2.
+    const int n_tiles = uni(f.n_tiles[0]);
+    const int NT = gridDim.y;  // N tiles
+    const int p = blockIdx.y * gridDim.x + blockIdx.x;
+    const int xcd = p & 7, q = p >> 3;
+    const int per = (n_tiles + 7) >> 3;  // tiles per XCD
+    const int tile = xcd * per + q / NT;
+    const int ntile = q % NT;
+    if (q / NT >= per || tile >= n_tiles) return;
     const int2 td = f.tiles[tile];
     const Group grp = uni_group(f.groups, uni(td.x));
     const int m0 = uni(td.y);
@@ -124,12 +138,12 @@ __global__ void __launch_bounds__(256, 2) k_gemm(Fwd f)
     int o0, o1;
     size_t mat0, mat1;
     if (MODE == GEMM_GU) {
-        o0 = blockIdx.y * 128 + 32 * w + n;  // gate and up of the same row
+        o0 = ntile * 256 + 32 * w + n;  // gate and up of the same row
         o1 = o0;
         mat0 = 0;
         mat1 = (size_t)I * H / 2;
     } else {
-        o0 = blockIdx.y * 256 + 64 * w + n;  // rows n and n + 32 of one block
+        o0 = ntile * 512 + 64 * w + n;  // rows n and n + 32 of one block
         o1 = o0 + 32;
         mat0 = mat1 = (size_t)I * H;
     }
@@ -151,15 +165,19 @@ __global__ void __launch_bounds__(256, 2) k_gemm(Fwd f)
     }
 
     const uint32_t mv = magic_vgpr();
+    // weight streams: the wavefront's rows lie in one 64-row block (a
+    // wave-uniform resource); the lane's row within it is the offset
     const int C = NC;  // chunks per weight row
+    const int blk = MODE == GEMM_GU ? ntile * 4 + (w >> 1) : ntile * 8 + w;
     const __amdgpu_buffer_rsrc_t rw0 =
-        make_rsrc(base + mat0 + (size_t)(o0 / 64) * C * 1024, (uint32_t)C * 1024);
+        make_rsrc(base + mat0 + (size_t)blk * C * 1024, (uint32_t)C * 1024);
     const __amdgpu_buffer_rsrc_t rw1 =
-        make_rsrc(base + mat1 + (size_t)(o1 / 64) * C * 1024, (uint32_t)C * 1024);
+        make_rsrc(base + mat1 + (size_t)blk * C * 1024, (uint32_t)C * 1024);
     const uint32_t v0 = (uint32_t)(o0 & 63) * 16, v1 = (uint32_t)(o1 & 63) * 16;
 
-    // activation loader: thread -> row tid/2, pieces 2*(tid&1) + {0, 1}
-    const int arow = tid >> 1, apc = (tid & 1) * 2;
+    // activation loader: thread -> row tid & 127, piece tid >> 7 (a
+    // wavefront writes 64 consecutive rows of one piece: no bank conflict)
+    const int arow = tid & (GM - 1), apc = tid >> 7;
     const int asrc = s_src[arow];
     const uint4* Ag = nullptr;
     if (asrc >= 0)
@@ -174,19 +192,18 @@ __global__ void __launch_bounds__(256, 2) k_gemm(Fwd f)
         acc[mb][1] = (float16){};
     }
 
-    // prologue: chunk 0 into LDS buffer 0, chunk 1 in registers, GDEP
-    // chunks of codes in flight
-    uint4 na0 = z4, na1 = z4;
-    if (Ag) {
-        na0 = Ag[0];
-        na1 = Ag[1];
-    }
-    As[0][apc][arow] = na0;
-    As[0][apc + 1][arow] = na1;
-    na0 = na1 = z4;
-    if (Ag && NC > 1) {
-        na0 = Ag[4];
-        na1 = Ag[5];
+    // prologue: chunk 0 into LDS buffer 0; activation chunks 1..GDEP-1 and
+    // code chunks 0..GDEP-1 in flight.  Activations and codes both run GDEP
+    // steps ahead, so that waiting for one (vmcnt counts in issue order)
+    // never drains the other early.
+    uint4 A0[GDEP];  // activation chunk j in slot j % GDEP
+    A0[0] = z4;
+    if (Ag) A0[0] = Ag[0];
+    As[0][apc][arow] = A0[0];
+#pragma unroll
+    for (int k = 1; k < GDEP; ++k) {
+        A0[k] = z4;
+        if (Ag) A0[k] = Ag[k * 4];
     }
     uint4 B0[GDEP], B1[GDEP];
 #pragma unroll
@@ -201,16 +218,12 @@ __global__ void __launch_bounds__(256, 2) k_gemm(Fwd f)
 #pragma unroll
         for (int k = 0; k < GDEP; ++k) {
             const int c = c0 + k;
-            // next activation chunk into the other buffer (its readers of
-            // step c - 1 passed the barrier); then fetch the one after
-            if (c + 1 < NC) {
-                As[(c + 1) & 1][apc][arow] = na0;
-                As[(c + 1) & 1][apc + 1][arow] = na1;
-            }
-            if (c + 2 < NC && Ag) {
-                na0 = Ag[(c + 2) * 4];
-                na1 = Ag[(c + 2) * 4 + 1];
-            }
+            // chunk c + 1 (slot (c + 1) % GDEP) into the other LDS buffer (its
+            // readers of step c - 1 passed the barrier); slot c % GDEP (chunk
+            // c, already in LDS) fetches chunk c + GDEP
+            const int s1 = (k + 1) % GDEP;
+            if (c + 1 < NC) As[(c + 1) & 1][apc][arow] = A0[s1];
+            if (Ag && c + GDEP < NC) A0[k] = Ag[(c + GDEP) * 4];
             // codes of step c; refill the slot with step c + GDEP (a load
             // past the row's last chunk returns zeros)
             const uint4 w0 = B0[k], w1 = B1[k];
@@ -222,14 +235,23 @@ __global__ void __launch_bounds__(256, 2) k_gemm(Fwd f)
             const half8 b10 = b_operand(half ? w1.y : w1.x, mv);
             const half8 b11 = b_operand(half ? w1.w : w1.z, mv);
             const uint4(*Ab)[GM] = As[c & 1];
+            half8 a0[4], a1[4];
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb) {
-                const half8 a0 = __builtin_bit_cast(half8, Ab[half][32 * mb + n]);
-                const half8 a1 = __builtin_bit_cast(half8, Ab[2 + half][32 * mb + n]);
-                acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b00, acc[mb][0], 0, 0, 0);
-                acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b10, acc[mb][1], 0, 0, 0);
-                acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b01, acc[mb][0], 0, 0, 0);
-                acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b11, acc[mb][1], 0, 0, 0);
+                a0[mb] = __builtin_bit_cast(half8, Ab[half][32 * mb + n]);
+                a1[mb] = __builtin_bit_cast(half8, Ab[2 + half][32 * mb + n]);
+            }
+            // first 16 inputs for all 8 accumulators, then the next 16: a
+            // dependent MFMA follows 7 independent ones
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0[mb], b00, acc[mb][0], 0, 0, 0);
+                acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0[mb], b10, acc[mb][1], 0, 0, 0);
+            }
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1[mb], b01, acc[mb][0], 0, 0, 0);
+                acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1[mb], b11, acc[mb][1], 0, 0, 0);
             }
             __syncthreads();
         }
@@ -348,10 +370,17 @@ hipError_t launch_gemm_prep(const Fwd& f, hipStream_t st)
     return launch_k(k_tiles, dim3(1), dim3(512), 0, st, f);
 }
 
+// grid: (max tiles rounded up to the 8 XCDs) x (N tiles); the kernel maps
+// workgroups onto the actual tiles
+static dim3 gemm_grid(const Fwd& f, int n_tiles_n)
+{
+    const int mt = (gemm_max_tiles(f.T, f.K, f.E, f.n_shared) + 7) / 8 * 8;
+    return dim3(mt, n_tiles_n);
+}
+
 hipError_t launch_gemm_gateup(const Fwd& f, hipStream_t st)
 {
-    const int mt = gemm_max_tiles(f.T, f.K, f.E, f.n_shared);
-    return launch_k(k_gemm<GEMM_GU>, dim3(mt, f.I / 128), dim3(256), 0, st, f);
+    return launch_k(k_gemm<GEMM_GU>, gemm_grid(f, f.I / 256), dim3(64 * GW), 0, st, f);
 }
 
 hipError_t launch_gemm_hstage(const Fwd& f, hipStream_t st)
@@ -363,8 +392,11 @@ hipError_t launch_gemm_hstage(const Fwd& f, hipStream_t st)
 
 hipError_t launch_gemm_down(const Fwd& f, hipStream_t st)
 {
-    const int mt = gemm_max_tiles(f.T, f.K, f.E, f.n_shared);
-    return launch_k(k_gemm<GEMM_DN>, dim3(mt, f.H / 256), dim3(256), 0, st, f);
+    return launch_k(k_gemm<GEMM_DN>, gemm_grid(f, f.H / 512), dim3(64 * GW), 0, st, f);
 }
+
+// Shapes the grouped GEMM tiles exactly: N tiles of 256 (gate/up) and 512
+// (down) output rows.
+bool gemm_shape_ok(int H, int I) { return H % 512 == 0 && I % 256 == 0; }
 
 }  // namespace moe

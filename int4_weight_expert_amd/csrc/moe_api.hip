@@ -234,7 +234,8 @@ int run_router(moe_ctx* c, const Fwd& f)
 // Many tokens (row format): the expert FFN as MFMA grouped GEMMs.
 bool uses_gemm(const moe_ctx* c, int T)
 {
-    return c->hbuf != nullptr && T > ROUTER_SMALL_MAX_T && T >= c->gemm_min_tokens;
+    return c->hbuf != nullptr && T > ROUTER_SMALL_MAX_T && T >= c->gemm_min_tokens &&
+           gemm_shape_ok(c->cfg.hidden, c->cfg.inter);
 }
 
 int run_forward_gemm(moe_ctx* c, Fwd& f)

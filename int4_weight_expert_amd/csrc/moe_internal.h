@@ -127,6 +127,7 @@ hipError_t launch_gateup_gemv(const Fwd& f, hipStream_t st);
 hipError_t launch_down_gemv(const Fwd& f, hipStream_t st);
 bool gateup_needs_finalize(const Fwd& f);
 int gemm_max_tiles(int T, int K, int E, int n_shared);
+bool gemm_shape_ok(int H, int I);
 hipError_t launch_gemm_prep(const Fwd& f, hipStream_t st);
 hipError_t launch_gemm_gateup(const Fwd& f, hipStream_t st);
 hipError_t launch_gemm_hstage(const Fwd& f, hipStream_t st);
