@@ -362,11 +362,9 @@ int gemm_max_tiles(int T, int K, int E, int n_shared)
                  (int64_t)n_shared * ((T + GM - 1) / GM));
 }
 
+// the row staging of x happens in the router's token statistics
 hipError_t launch_gemm_prep(const Fwd& f, hipStream_t st)
 {
-    hipError_t e = launch_k(k_rowstage, dim3((f.T + 3) / 4), dim3(256), 0, st, f.x, f.T, f.H,
-                            f.xq, f.xrow);
-    if (e != hipSuccess) return e;
     return launch_k(k_tiles, dim3(1), dim3(512), 0, st, f);
 }
 

@@ -34,85 +34,106 @@ __global__ void __launch_bounds__(256) k_tokstats(Fwd f)
     if (t >= f.T) return;
     const int H = f.H;
     const float* xt = f.x + (size_t)t * H;
-    float sum = 0.f, ss = 0.f;
+    float sum = 0.f, ss = 0.f, mx = 0.f;
     for (int s = 0; s < H / 64; ++s) {
         const float v = xt[s * 64 + lane];
         sum += v;
         ss = fmaf(v, v, ss);
-        stage_span64(v, lane, (uint16_t*)(f.xq + (size_t)t * (H / 8) + s * 8),
-                     f.xsc + (size_t)t * (H / 64) + s);
+        mx = fmaxf(mx, fabsf(v));
+        if (f.row_staging == 0)  // expert GEMVs: fp16 spans of 64
+            stage_span64(v, lane, (uint16_t*)(f.xq + (size_t)t * (H / 8) + s * 8),
+                         f.xsc + (size_t)t * (H / 64) + s);
     }
     sum = wsum(sum);
     ss = wsum(ss);
+    if (f.row_staging) {
+        // grouped GEMM: the whole row as fp16 with one power-of-two scale
+        // (largest magnitude in [2^13, 2^14)), in pair order, and its sum
+        mx = wave_max(mx);
+        int e;
+        frexpf(mx, &e);
+        e = max(e, -100);
+        const float sc = ldexpf(1.0f, 14 - e);
+        float ts = 0.f;
+        const float4* row = (const float4*)xt;
+        uint4* q = f.xq + (size_t)t * (H / 8);
+        for (int g = lane; g < H / 8; g += 64) {
+            const float4 a = row[2 * g], b = row[2 * g + 1];
+            const _Float16 h0 = (_Float16)(a.x * sc), h1 = (_Float16)(a.y * sc);
+            const _Float16 h2 = (_Float16)(a.z * sc), h3 = (_Float16)(a.w * sc);
+            const _Float16 h4 = (_Float16)(b.x * sc), h5 = (_Float16)(b.y * sc);
+            const _Float16 h6 = (_Float16)(b.z * sc), h7 = (_Float16)(b.w * sc);
+            q[g] = make_uint4(pack_h2(h0, h4), pack_h2(h1, h5), pack_h2(h2, h6), pack_h2(h3, h7));
+            ts += (((float)h0 + (float)h1) + ((float)h2 + (float)h3)) +
+                  (((float)h4 + (float)h5) + ((float)h6 + (float)h7));
+        }
+        ts = wsum(ts);
+        if (lane == 0) f.xrow[t] = make_float2(ldexpf(1.0f, e - 14), ts);
+    }
     if (lane == 0) {
         f.tok[t].xsum = sum;
         f.tok[t].rscale = f.residual ? 1.0f / sqrtf(ss / (float)H + f.eps) : 1.0f;
     }
 }
 
-// logits[t][e] = sum_h x[t][h] * W[e][h] (fp32, unnormalised x).  Tile: 32
-// tokens x 64 experts per 256-thread workgroup, 2 x 4 outputs per thread,
-// 32-column K steps staged through LDS.  B comes from the interleaved router
-// layout [Epad/64][H/4][64] float4.
-__global__ void __launch_bounds__(256) k_router_gemm(Fwd f)
+// Router logits for many tokens on the fp32 matrix cores
+// (v_mfma_f32_32x32x2_f32: fp32 products, fp32 accumulation).  Workgroup =
+// 32 tokens x 64 experts; its 8 wavefronts each take one eighth of the H
+// inputs, with two accumulator pairs (even and odd steps) per 32-expert
+// block, and the slices are summed in LDS in a fixed order.  Per step of 8
+// inputs a lane loads one float4 of x (4 consecutive inputs of its token)
+// and one float4 of the interleaved router weights per 32-expert block; the
+// lanes of the lower half take inputs k..k+3, the upper half k+4..k+7, so
+// MFMA step j pairs inputs k+j and k+4+j in both operands.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__global__ void __launch_bounds__(512) k_router_mfma(Fwd f)
 {
-    constexpr int TT = 32, KT = 32;
-    __shared__ float As[KT][TT + 1];
-    __shared__ float Bs[KT][64 + 4];
-    const int tid = threadIdx.x;
-    const int t0 = blockIdx.x * TT, b = blockIdx.y;
-    const int H = f.H, T = f.T, CH = H / 4;
-    const int ty = tid >> 4, tx = tid & 15;
-    const float4* wr = (const float4*)f.wr + (size_t)b * CH * 64;
-    float acc[2][4] = {};
-    for (int k0 = 0; k0 < H; k0 += KT) {
-        {   // A: 32 tokens x 32 columns, one float4 per thread
-            const int tt = tid >> 3, cc = (tid & 7) * 4;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (t0 + tt < T) v = *(const float4*)(f.x + (size_t)(t0 + tt) * H + k0 + cc);
-            As[cc + 0][tt] = v.x;
-            As[cc + 1][tt] = v.y;
-            As[cc + 2][tt] = v.z;
-            As[cc + 3][tt] = v.w;
-        }
+    __shared__ float red[8][2 * 16 * 64];  // [wave][block][reg][lane]
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int H = f.H, T = f.T;
+    const int t0 = blockIdx.x * 32, eb = blockIdx.y;
+    const int h = lane >> 5, m = lane & 31;
+    const int row = t0 + m;
+    const float4* xr = row < T ? (const float4*)(f.x + (size_t)row * H) : nullptr;
+    const float4* wb = (const float4*)f.wr + (size_t)eb * (H / 4) * 64;
+    const int KW = H / 8;  // inputs per wavefront (H is a multiple of 256)
+    f32x16 acc[2][2];
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {  // B: 8 chunks x 64 experts
-            const int idx = tid + r * 256;
-            const int ch = idx >> 6, e = idx & 63;
-            const float4 v = wr[(size_t)(k0 / 4 + ch) * 64 + e];
-            Bs[ch * 4 + 0][e] = v.x;
-            Bs[ch * 4 + 1][e] = v.y;
-            Bs[ch * 4 + 2][e] = v.z;
-            Bs[ch * 4 + 3][e] = v.w;
-        }
-        __syncthreads();
-#pragma unroll 8
-        for (int k = 0; k < KT; ++k) {
-            const float a0 = As[k][ty * 2], a1 = As[k][ty * 2 + 1];
-            const float4 bv = *(const float4*)&Bs[k][tx * 4];
-            acc[0][0] = fmaf(a0, bv.x, acc[0][0]);
-            acc[0][1] = fmaf(a0, bv.y, acc[0][1]);
-            acc[0][2] = fmaf(a0, bv.z, acc[0][2]);
-            acc[0][3] = fmaf(a0, bv.w, acc[0][3]);
-            acc[1][0] = fmaf(a1, bv.x, acc[1][0]);
-            acc[1][1] = fmaf(a1, bv.y, acc[1][1]);
-            acc[1][2] = fmaf(a1, bv.z, acc[1][2]);
-            acc[1][3] = fmaf(a1, bv.w, acc[1][3]);
-        }
-        __syncthreads();
+    for (int b = 0; b < 2; ++b) acc[b][0] = acc[b][1] = (f32x16){};
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 2
+    for (int k = w * KW; k < (w + 1) * KW; k += 8) {
+        const int q = (k >> 2) + h;  // float4 index of this lane's 4 inputs
+        const float4 a = xr ? xr[q] : z;
+        const float4 b0 = wb[(size_t)q * 64 + m];
+        const float4 b1 = wb[(size_t)q * 64 + 32 + m];
+        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, b0.x, acc[0][0], 0, 0, 0);
+        acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, b1.x, acc[1][0], 0, 0, 0);
+        acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, b0.y, acc[0][1], 0, 0, 0);
+        acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, b1.y, acc[1][1], 0, 0, 0);
+        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, b0.z, acc[0][0], 0, 0, 0);
+        acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, b1.z, acc[1][0], 0, 0, 0);
+        acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, b0.w, acc[0][1], 0, 0, 0);
+        acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, b1.w, acc[1][1], 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int t = t0 + ty * 2 + i;
-        if (t < T)
-            *(float4*)(f.logits + (size_t)t * f.Epad + b * 64 + tx * 4) =
-                make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) red[w][(b * 16 + j) * 64 + lane] = acc[b][0][j] + acc[b][1][j];
+    __syncthreads();
+    // output (token, expert) of entry (block b, reg j, lane l):
+    // token (j/4)*8 + (l/32)*4 + j%4, expert b*32 + l%32
+    for (int i = threadIdx.x; i < 2 * 16 * 64; i += 512) {
+        float v = 0.f;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) v += red[s][i];
+        const int b = i >> 10, j = (i >> 6) & 15, l = i & 63;
+        const int t = t0 + (j >> 2) * 8 + (l >> 5) * 4 + (j & 3);
+        if (t < T) f.logits[(size_t)t * f.Epad + eb * 64 + b * 32 + (l & 31)] = v;
     }
 }
 
-// Top-K per token, one wavefront per token (4 per workgroup): sigmoid of the
-// normalised logit, score = sigmoid + bias, K rounds of a wavefront argmax
-// over (score, lower id) keys, renormalised weights.
 __global__ void __launch_bounds__(256) k_topk(Fwd f)
 {
     const int lane = threadIdx.x & 63;
@@ -309,7 +330,7 @@ hipError_t launch_router_large(const Fwd& f, hipStream_t st, int stage)
     switch (stage) {
     case 0: return launch_k(k_tokstats, dim3((f.T + 3) / 4), dim3(256), 0, st, f);
     case 1:
-        return launch_k(k_router_gemm, dim3((f.T + 31) / 32, f.Epad / 64), dim3(256), 0, st, f);
+        return launch_k(k_router_mfma, dim3((f.T + 31) / 32, f.Epad / 64), dim3(512), 0, st, f);
     case 2: return launch_k(k_topk, dim3((f.T + 3) / 4), dim3(256), 0, st, f);
     default:
         return launch_k(k_bucket, dim3(1), dim3(1024), 0, st, (const int32_t*)f.ids, f.T * f.K,

@@ -242,9 +242,10 @@ int run_forward_gemm(moe_ctx* c, Fwd& f)
 {
     f.gu_ks = 1;
     f.dn_ks = 1;  // combine reads ypart as [rows][H]
+    f.row_staging = 1;
     int rc = run_router(c, f);
     if (rc) return rc;
-    mark(c, "gemm_prep");
+    mark(c, "gemm_tiles");
     rc = hip_rc(c, launch_gemm_prep(f, c->stream));
     if (rc) return rc;
     mark(c, "gemm_gateup");

@@ -86,6 +86,7 @@ struct Fwd {
     float* gpart;         // [rows][I/64][gu_ks][2][64] gate/up partials (gu_ks > 1)
     float* ypart;         // [rows][H/64][dn_ks][64] down partials ([rows][H] when dn_ks = 1)
     // grouped-GEMM path (many tokens): x and h staged per row in xq / hq
+    int row_staging;      // 1: stage x per row (grouped GEMM), 0: in spans of 64 (GEMVs)
     float2* xrow;         // [T] per token (2^-k, sum of its fp16 values)
     float2* hrow;         // [rows]
     float* hbuf;          // [rows][I] h in fp32 (gate/up GEMM output)
