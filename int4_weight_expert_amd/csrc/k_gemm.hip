@@ -32,9 +32,9 @@
 // Per K step of 32 inputs (one 16-byte chunk of codes per output row): the
 // activation tile (128 x 32 fp16) is double-buffered in LDS, piece-major so
 // the A-operand reads are conflict-free; every wavefront loads its own codes
-// straight into registers (16 bytes per lane: the MFMA B operand needs 8
-// codes of one row per lane, lanes l and l+32 taking the two halves of a
-// chunk).  Activations and codes are fetched GDEP steps ahead.
+// straight into registers (8 bytes per lane: lanes l and l+32 read the two
+// halves of a row's chunk, each half feeding one MFMA per step).
+// Activations and codes are fetched GDEP steps ahead.
 #include "k_common.h"
 
 namespace moe {
@@ -74,6 +74,171 @@ __device__ __forceinline__ half8 b_operand(uint32_t dword, uint32_t mv)
     return as_half8(p0, p1, p2, p3);
 }
 
+// Output rows o0, o1 of wavefront w's two B blocks in N tile `ntile`, and
+// the byte offsets of their matrices in the expert's slot.
+template <int MODE>
+__device__ __forceinline__ void gemm_out_rows(int ntile, int w, int n, int H, int I, int& o0,
+                                              int& o1, size_t& mat0, size_t& mat1)
+{
+    if (MODE == GEMM_GU) {
+        o0 = ntile * 256 + 32 * w + n;  // gate and up of the same row
+        o1 = o0;
+        mat0 = 0;
+        mat1 = (size_t)I * H / 2;
+    } else {
+        o0 = ntile * 512 + 64 * w + n;  // rows n and n + 32 of one block
+        o1 = o0 + 32;
+        mat0 = mat1 = (size_t)I * H;
+    }
+}
+
+// The tile's prologue, K loop and epilogue, specialised on the number MB of
+// 32-row blocks that hold rows of the group: a partial tile issues only its
+// blocks' LDS reads and MFMAs.  Each specialisation is self-contained, so no
+// register array lives across the dispatch.
+template <int MODE, int MB>
+__device__ __forceinline__ void gemm_tile(const Fwd& f, uint4 (*As)[4][GM], const int* s_src,
+                                          const int* s_out, const float* s_inv,
+                                          const float* s_sum, const float* s_rs,
+                                          const uint8_t* base, int ntile, int rows)
+{
+    const int tid = threadIdx.x, lane = tid & 63, w = uni(tid >> 6);
+    const int n = lane & 31, half = lane >> 5;
+    const int H = f.H, I = f.I;
+    const int K = MODE == GEMM_GU ? H : I;  // reduction length
+    const int NC = K / 32;                  // K steps (chunks)
+    int o0, o1;
+    size_t mat0, mat1;
+    gemm_out_rows<MODE>(ntile, w, n, H, I, o0, o1, mat0, mat1);
+    const uint8_t* tab = base + (size_t)3 * H * I / 2;  // fp32 row scales
+
+    const uint32_t mv = magic_vgpr();
+    // weight streams: the wavefront's rows lie in one 64-row block (a
+    // wave-uniform resource); the lane's row within it is the offset
+    const int C = NC;  // chunks per weight row
+    const int blk = MODE == GEMM_GU ? ntile * 4 + (w >> 1) : ntile * 8 + w;
+    const __amdgpu_buffer_rsrc_t rw0 =
+        make_rsrc(base + mat0 + (size_t)blk * C * 1024, (uint32_t)C * 1024);
+    const __amdgpu_buffer_rsrc_t rw1 =
+        make_rsrc(base + mat1 + (size_t)blk * C * 1024, (uint32_t)C * 1024);
+    // lane half h reads bytes 8h..8h+7 of the row's 16-byte chunk
+    const uint32_t v0 = (uint32_t)(o0 & 63) * 16 + half * 8;
+    const uint32_t v1 = (uint32_t)(o1 & 63) * 16 + half * 8;
+
+    // activation loader: thread -> row tid & 127, piece tid >> 7 (a
+    // wavefront writes 64 consecutive rows of one piece: no bank conflict)
+    const int arow = tid & (GM - 1), apc = tid >> 7;
+    const int asrc = s_src[arow];
+    const uint4* Ag = nullptr;
+    if (asrc >= 0)
+        Ag = (MODE == GEMM_GU ? f.xq + (size_t)asrc * (H / 8) : f.hq + (size_t)asrc * (I / 8)) +
+             apc;
+    const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+
+    float16 acc[4][2];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        acc[mb][0] = (float16){};
+        acc[mb][1] = (float16){};
+    }
+
+    // prologue: chunk 0 into LDS buffer 0; activation chunks 1..GDEP-1 and
+    // code chunks 0..GDEP-1 in flight.  Activations and codes both run GDEP
+    // steps ahead, so that waiting for one (vmcnt counts in issue order)
+    // never drains the other early.
+    uint4 A0[GDEP];  // activation chunk j in slot j % GDEP
+    A0[0] = z4;
+    if (Ag) A0[0] = Ag[0];
+    As[0][apc][arow] = A0[0];
+#pragma unroll
+    for (int k = 1; k < GDEP; ++k) {
+        A0[k] = z4;
+        if (Ag) A0[k] = Ag[k * 4];
+    }
+    uint2 B0[GDEP], B1[GDEP];
+#pragma unroll
+    for (int k = 0; k < GDEP; ++k) {
+        B0[k] = bload8(rw0, v0 + k * 1024, 0);
+        B1[k] = bload8(rw1, v1 + k * 1024, 0);
+    }
+    __syncthreads();
+
+#pragma unroll 1
+    for (int c0 = 0; c0 < NC; c0 += GDEP) {
+#pragma unroll
+        for (int k = 0; k < GDEP; ++k) {
+            const int c = c0 + k;
+            // chunk c + 1 (slot (c + 1) % GDEP) into the other LDS buffer (its
+            // readers of step c - 1 passed the barrier); slot c % GDEP (chunk
+            // c, already in LDS) fetches chunk c + GDEP
+            const int s1 = (k + 1) % GDEP;
+            if (c + 1 < NC) As[(c + 1) & 1][apc][arow] = A0[s1];
+            if (Ag && c + GDEP < NC) A0[k] = Ag[(c + GDEP) * 4];
+            // codes of step c; refill the slot with step c + GDEP (a load
+            // past the row's last chunk returns zeros)
+            const uint2 w0 = B0[k], w1 = B1[k];
+            B0[k] = bload8(rw0, v0 + (c + GDEP) * 1024, 0);
+            B1[k] = bload8(rw1, v1 + (c + GDEP) * 1024, 0);
+            // the K order inside a chunk is free as long as A and B agree:
+            // lane half h takes inputs 16h..16h+7 in the first MFMA and
+            // 16h+8..16h+15 in the second (dwords 2h, 2h+1; LDS pieces 2h, 2h+1)
+            const half8 b00 = b_operand(w0.x, mv), b01 = b_operand(w0.y, mv);
+            const half8 b10 = b_operand(w1.x, mv), b11 = b_operand(w1.y, mv);
+            const uint4(*Ab)[GM] = As[c & 1];
+            half8 a0[4], a1[4];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                a0[mb] = __builtin_bit_cast(half8, Ab[2 * half][32 * mb + n]);
+                a1[mb] = __builtin_bit_cast(half8, Ab[2 * half + 1][32 * mb + n]);
+            }
+            // first 16 inputs for all 8 accumulators, then the next 16: a
+            // dependent MFMA follows 7 independent ones
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0[mb], b00, acc[mb][0], 0, 0, 0);
+                acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0[mb], b10, acc[mb][1], 0, 0, 0);
+            }
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1[mb], b01, acc[mb][0], 0, 0, 0);
+                acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1[mb], b11, acc[mb][1], 0, 0, 0);
+            }
+            __syncthreads();
+        }
+    }
+
+    // epilogue: lane holds column o of each block, rows (j/4)*8 + half*4 + j%4
+    if (MODE == GEMM_GU) {
+        const float sg = ((const float*)tab)[o0], su = ((const float*)tab)[I + o0];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int i = 32 * mb + (j >> 2) * 8 + half * 4 + (j & 3);
+                if (i < rows) {
+                    const float sc = s_inv[i] * s_rs[i];
+                    const float g = fmaf(acc[mb][0][j], 0.0625f, -72.f * s_sum[i]) * sc * sg;
+                    const float u = fmaf(acc[mb][1][j], 0.0625f, -72.f * s_sum[i]) * sc * su;
+                    f.hbuf[(size_t)s_out[i] * I + o0] = g / (1.0f + expf(-g)) * u;
+                }
+            }
+    } else {
+        const float sd0 = ((const float*)tab)[2 * I + o0], sd1 = ((const float*)tab)[2 * I + o1];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int i = 32 * mb + (j >> 2) * 8 + half * 4 + (j & 3);
+                if (i < rows) {
+                    const float sc = s_inv[i];
+                    float* y = f.ypart + (size_t)s_out[i] * H;
+                    y[o0] = fmaf(acc[mb][0][j], 0.0625f, -72.f * s_sum[i]) * sc * sd0;
+                    y[o1] = fmaf(acc[mb][1][j], 0.0625f, -72.f * s_sum[i]) * sc * sd1;
+                }
+            }
+    }
+}
+
 template <int MODE>
 __global__ void __launch_bounds__(64 * GW, 1) k_gemm(Fwd f)
 {
@@ -99,10 +264,8 @@ __global__ void __launch_bounds__(64 * GW, 1) k_gemm(Fwd f)
     const int m0 = uni(td.y);
     const int rows = min(GM, grp.cnt - m0);
     const int tid = threadIdx.x, lane = tid & 63, w = uni(tid >> 6);
-    const int n = lane & 31, half = lane >> 5;
+    const int n = lane & 31;
     const int H = f.H, I = f.I;
-    const int K = MODE == GEMM_GU ? H : I;  // reduction length
-    const int NC = K / 32;                  // K steps (chunks)
 
     // per-row data of the tile
     if (tid < GM) {
@@ -133,24 +296,13 @@ __global__ void __launch_bounds__(64 * GW, 1) k_gemm(Fwd f)
     }
     __syncthreads();
 
-    // output rows of this wavefront's two B blocks, and their weight streams
+    // output rows of this wavefront's two B blocks
     const uint8_t* base = grp.base;
-    int o0, o1;
-    size_t mat0, mat1;
-    if (MODE == GEMM_GU) {
-        o0 = ntile * 256 + 32 * w + n;  // gate and up of the same row
-        o1 = o0;
-        mat0 = 0;
-        mat1 = (size_t)I * H / 2;
-    } else {
-        o0 = ntile * 512 + 64 * w + n;  // rows n and n + 32 of one block
-        o1 = o0 + 32;
-        mat0 = mat1 = (size_t)I * H;
-    }
-    const uint8_t* tab = base + (size_t)3 * H * I / 2;  // fp32 row scales
-
     if (base == nullptr) {
         // expert not resident: no contribution (the router flagged it)
+        int o0, o1;
+        size_t mat0, mat1;
+        gemm_out_rows<MODE>(ntile, w, n, H, I, o0, o1, mat0, mat1);
         for (int i = 0; i < rows; ++i) {
             if (MODE == GEMM_GU) {
                 if (lane < 32) f.hbuf[(size_t)s_out[i] * I + o0] = 0.f;
@@ -163,129 +315,11 @@ __global__ void __launch_bounds__(64 * GW, 1) k_gemm(Fwd f)
         }
         return;
     }
-
-    const uint32_t mv = magic_vgpr();
-    // weight streams: the wavefront's rows lie in one 64-row block (a
-    // wave-uniform resource); the lane's row within it is the offset
-    const int C = NC;  // chunks per weight row
-    const int blk = MODE == GEMM_GU ? ntile * 4 + (w >> 1) : ntile * 8 + w;
-    const __amdgpu_buffer_rsrc_t rw0 =
-        make_rsrc(base + mat0 + (size_t)blk * C * 1024, (uint32_t)C * 1024);
-    const __amdgpu_buffer_rsrc_t rw1 =
-        make_rsrc(base + mat1 + (size_t)blk * C * 1024, (uint32_t)C * 1024);
-    const uint32_t v0 = (uint32_t)(o0 & 63) * 16, v1 = (uint32_t)(o1 & 63) * 16;
-
-    // activation loader: thread -> row tid & 127, piece tid >> 7 (a
-    // wavefront writes 64 consecutive rows of one piece: no bank conflict)
-    const int arow = tid & (GM - 1), apc = tid >> 7;
-    const int asrc = s_src[arow];
-    const uint4* Ag = nullptr;
-    if (asrc >= 0)
-        Ag = (MODE == GEMM_GU ? f.xq + (size_t)asrc * (H / 8) : f.hq + (size_t)asrc * (I / 8)) +
-             apc;
-    const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
-
-    float16 acc[4][2];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-        acc[mb][0] = (float16){};
-        acc[mb][1] = (float16){};
-    }
-
-    // prologue: chunk 0 into LDS buffer 0; activation chunks 1..GDEP-1 and
-    // code chunks 0..GDEP-1 in flight.  Activations and codes both run GDEP
-    // steps ahead, so that waiting for one (vmcnt counts in issue order)
-    // never drains the other early.
-    uint4 A0[GDEP];  // activation chunk j in slot j % GDEP
-    A0[0] = z4;
-    if (Ag) A0[0] = Ag[0];
-    As[0][apc][arow] = A0[0];
-#pragma unroll
-    for (int k = 1; k < GDEP; ++k) {
-        A0[k] = z4;
-        if (Ag) A0[k] = Ag[k * 4];
-    }
-    uint4 B0[GDEP], B1[GDEP];
-#pragma unroll
-    for (int k = 0; k < GDEP; ++k) {
-        B0[k] = bload16(rw0, v0 + k * 1024, 0);
-        B1[k] = bload16(rw1, v1 + k * 1024, 0);
-    }
-    __syncthreads();
-
-#pragma unroll 1
-    for (int c0 = 0; c0 < NC; c0 += GDEP) {
-#pragma unroll
-        for (int k = 0; k < GDEP; ++k) {
-            const int c = c0 + k;
-            // chunk c + 1 (slot (c + 1) % GDEP) into the other LDS buffer (its
-            // readers of step c - 1 passed the barrier); slot c % GDEP (chunk
-            // c, already in LDS) fetches chunk c + GDEP
-            const int s1 = (k + 1) % GDEP;
-            if (c + 1 < NC) As[(c + 1) & 1][apc][arow] = A0[s1];
-            if (Ag && c + GDEP < NC) A0[k] = Ag[(c + GDEP) * 4];
-            // codes of step c; refill the slot with step c + GDEP (a load
-            // past the row's last chunk returns zeros)
-            const uint4 w0 = B0[k], w1 = B1[k];
-            B0[k] = bload16(rw0, v0 + (c + GDEP) * 1024, 0);
-            B1[k] = bload16(rw1, v1 + (c + GDEP) * 1024, 0);
-            // lane half h takes dwords h (inputs 8h..8h+7) and 2 + h (16 + 8h..)
-            const half8 b00 = b_operand(half ? w0.y : w0.x, mv);
-            const half8 b01 = b_operand(half ? w0.w : w0.z, mv);
-            const half8 b10 = b_operand(half ? w1.y : w1.x, mv);
-            const half8 b11 = b_operand(half ? w1.w : w1.z, mv);
-            const uint4(*Ab)[GM] = As[c & 1];
-            half8 a0[4], a1[4];
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-                a0[mb] = __builtin_bit_cast(half8, Ab[half][32 * mb + n]);
-                a1[mb] = __builtin_bit_cast(half8, Ab[2 + half][32 * mb + n]);
-            }
-            // first 16 inputs for all 8 accumulators, then the next 16: a
-            // dependent MFMA follows 7 independent ones
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-                acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0[mb], b00, acc[mb][0], 0, 0, 0);
-                acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0[mb], b10, acc[mb][1], 0, 0, 0);
-            }
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-                acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1[mb], b01, acc[mb][0], 0, 0, 0);
-                acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1[mb], b11, acc[mb][1], 0, 0, 0);
-            }
-            __syncthreads();
-        }
-    }
-
-    // epilogue: lane holds column o of each block, rows (j/4)*8 + half*4 + j%4
-    if (MODE == GEMM_GU) {
-        const float sg = ((const float*)tab)[o0], su = ((const float*)tab)[I + o0];
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int i = 32 * mb + (j >> 2) * 8 + half * 4 + (j & 3);
-                if (i < rows) {
-                    const float sc = s_inv[i] * s_rs[i];
-                    const float g = fmaf(acc[mb][0][j], 0.0625f, -72.f * s_sum[i]) * sc * sg;
-                    const float u = fmaf(acc[mb][1][j], 0.0625f, -72.f * s_sum[i]) * sc * su;
-                    f.hbuf[(size_t)s_out[i] * I + o0] = g / (1.0f + expf(-g)) * u;
-                }
-            }
-    } else {
-        const float sd0 = ((const float*)tab)[2 * I + o0], sd1 = ((const float*)tab)[2 * I + o1];
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int i = 32 * mb + (j >> 2) * 8 + half * 4 + (j & 3);
-                if (i < rows) {
-                    const float sc = s_inv[i];
-                    float* y = f.ypart + (size_t)s_out[i] * H;
-                    y[o0] = fmaf(acc[mb][0][j], 0.0625f, -72.f * s_sum[i]) * sc * sd0;
-                    y[o1] = fmaf(acc[mb][1][j], 0.0625f, -72.f * s_sum[i]) * sc * sd1;
-                }
-            }
+    switch ((rows + 31) >> 5) {
+    case 1: gemm_tile<MODE, 1>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
+    case 2: gemm_tile<MODE, 2>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
+    case 3: gemm_tile<MODE, 3>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
+    default: gemm_tile<MODE, 4>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
     }
 }
 
