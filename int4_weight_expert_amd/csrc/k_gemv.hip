@@ -402,6 +402,205 @@ __global__ void __launch_bounds__(256) k_combine(Fwd f)
 }
 
 // ---------------------------------------------------------------------------
+// One token: the down projection and the combine in one kernel.  The output
+// rows go to 256 workgroups (one per CU), RG groups of 8 rows each, so that
+// every CU streams the same share; a workgroup covers its rows for every
+// expert slot (the shared experts, then the routed ones in rank order), so
+// the whole reduction of those rows stays inside it: no partial sums leave
+// the workgroup and no combine kernel follows.  Wavefront w takes chunk
+// group w (8 chunks of 32 inputs) of every (slot, row group): lane = (row r
+// of 8, chunk c of 8), one 16-byte code load covering 8 rows x 8 chunks,
+// DC_D loads in flight.  The slots' h (fp16 spans, staged by the gate/up
+// finalize) is copied to LDS once.  Sums are reduced in LDS in a fixed order
+// (chunk, then wavefront), scaled, weighted and added in slot order (+ x).
+// ---------------------------------------------------------------------------
+
+constexpr int DC_NE = 9;   // expert slots at most (shared + routed)
+constexpr int DC_D = 12;   // code loads in flight per wavefront
+constexpr int DC_HL = 5;   // h staging loads per thread at most
+
+// LDS: h [NE][I/8] uint4 + spans [NE][I/64] float2, later reused for the
+// partial sums [NCG][NE][RG][64] and the chunk-reduced [NCG][NE][RG][8].
+size_t dn2_lds_bytes(int I, int RG)
+{
+    const int ncg = I / 256;
+    const size_t h = (size_t)DC_NE * I * 2 + (size_t)DC_NE * (I / 64) * 8;
+    const size_t r = (size_t)ncg * DC_NE * RG * 64 * 4 + (size_t)ncg * DC_NE * RG * 8 * 4;
+    return std::max(h, r);
+}
+
+template <int FMT, int RG>
+__global__ void __launch_bounds__(512) k_dn2(Fwd f)
+{
+    extern __shared__ uint4 lds4[];
+    __shared__ uint64_t s_base[DC_NE];
+    __shared__ int s_row[DC_NE];
+    __shared__ float s_wt[DC_NE];
+    const int tid = threadIdx.x, lane = tid & 63, w = uni(tid >> 6);
+    const int NCG = (int)(blockDim.x >> 6);  // chunk groups = wavefronts
+    const int H = f.H, I = f.I, NP = I / 64, C = I / 32;
+    const int ne = f.n_shared + f.K;
+
+    // slot table: shared experts first, routed experts in rank order
+    if (tid < DC_NE) {
+        s_base[tid] = 0ull;
+        s_row[tid] = 0;
+        s_wt[tid] = 0.f;
+    }
+    __syncthreads();
+    if (tid < uni(f.n_groups[0])) {
+        const Group g = f.groups[tid];
+        int e, r;
+        float wt = 1.f;
+        if (g.kind == 1) {
+            e = g.off;
+            r = f.K + g.off;  // T = 1
+        } else {
+            r = f.perm[g.off];  // assignment = rank
+            e = f.n_shared + r;
+            wt = f.wts[r];
+        }
+        s_base[e] = (uint64_t)(uintptr_t)g.base;
+        s_row[e] = r;
+        s_wt[e] = wt;
+    }
+    __syncthreads();
+
+    uint4* hq = lds4;                                // [DC_NE][I/8]
+    float2* hs = (float2*)(lds4 + DC_NE * (I / 8));  // [DC_NE][NP]
+    // h staging loads first (they return before the code stream)
+    const int nh = ne * (I / 8), nsc = ne * NP, nthr = 64 * NCG;
+    uint4 hv[DC_HL];
+#pragma unroll
+    for (int k = 0; k < DC_HL; ++k) {
+        const int i = tid + k * nthr;
+        const int e = min(i / (I / 8), DC_NE - 1), c = i - e * (I / 8);
+        hv[k] = i < nh ? f.hq[(size_t)s_row[e] * (I / 8) + c] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    float2 sv = make_float2(0.f, 0.f);
+    if (tid < nsc) sv = f.hsc[(size_t)s_row[tid / NP] * NP + tid % NP];
+
+    // slot bases (wave-uniform); a slot without an expert (beyond ne, or not
+    // resident) gets an empty resource, whose loads return zeros; its sums
+    // are never combined
+    uint64_t bases[DC_NE];
+#pragma unroll
+    for (int e = 0; e < DC_NE; ++e) {
+        const uint64_t b = e < ne ? s_base[e] : 0ull;
+        bases[e] = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b)) |
+                   ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32)) << 32);
+    }
+    const uint8_t* anchor = (const uint8_t*)f.x;  // any valid address
+    const int r8 = lane & 7, c8 = lane >> 3;
+    const int chunk = 8 * w + c8;  // this lane's chunk (32 inputs)
+    // per slot: one resource over the whole down matrix (codes) and its
+    // table; the row group's block and row go into the lane offset
+    auto code_rsrc = [&](int e) {
+        const uint8_t* b = (const uint8_t*)(uintptr_t)bases[e];
+        return make_rsrc(b ? b + (size_t)I * H : anchor, b ? (uint32_t)((size_t)I * H / 2) : 0u);
+    };
+    auto tab_rsrc = [&](int e) {
+        const uint8_t* b = (const uint8_t*)(uintptr_t)bases[e];
+        return make_rsrc(b ? b + (size_t)3 * H * I / 2 + (size_t)2 * I * (H / 64) * 4 : anchor,
+                         (b && FMT != MOE_W_INT4_ROW) ? (uint32_t)(H / 64) * NP * 256 : 0u);
+    };
+    uint32_t coff[RG], toff[RG];
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+        const int rg = blockIdx.x * RG + g, blk = rg >> 3, row64 = (rg & 7) * 8 + r8;
+        coff[g] = (uint32_t)blk * C * 1024 + (uint32_t)chunk * 1024 + (uint32_t)row64 * 16;
+        toff[g] = (uint32_t)blk * NP * 256 + (uint32_t)(chunk >> 1) * 256 + (uint32_t)row64 * 4;
+    }
+    const uint32_t mv = magic_vgpr();
+    constexpr int NS = DC_NE * RG;  // steps (slot e, row group g), e outer
+    uint4 R[DC_D];
+    uint32_t P[DC_D];
+#pragma unroll
+    for (int st = 0; st < DC_D; ++st)
+        if (st < NS) {
+            const int e = st / RG, g = st % RG;
+            R[st] = bload16(code_rsrc(e), coff[g], 0);
+            P[st] = FMT != MOE_W_INT4_ROW ? bload4(tab_rsrc(e), toff[g], 0) : 0u;
+        }
+#pragma unroll
+    for (int k = 0; k < DC_HL; ++k) {
+        const int i = tid + k * nthr;
+        if (i < nh) hq[i] = hv[k];
+    }
+    if (tid < nsc) hs[tid] = sv;
+    __syncthreads();
+
+    float Y[NS];
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+        const int e = st / RG;
+        const uint4 wv = R[st % DC_D];
+        const uint32_t pv = P[st % DC_D];
+        const int sn = st + DC_D;
+        if (sn < NS) {
+            const int en = sn / RG, gn = sn % RG;
+            R[st % DC_D] = bload16(code_rsrc(en), coff[gn], 0);
+            if (FMT != MOE_W_INT4_ROW) P[st % DC_D] = bload4(tab_rsrc(en), toff[gn], 0);
+        }
+        // 32 codes of row r8 (of row group g), chunk `chunk`, against the slot's h
+        const uint4* xv = hq + e * (I / 8) + chunk * 4;
+        float a = 0.f;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            uint32_t p0, p1, p2, p3;
+            nib_pairs(dw(wv, d), mv, p0, p1, p2, p3);
+            a = dot_dword(p0, p1, p2, p3, xv[d], a);
+        }
+        // the span's correction term once (its even chunk), then 2^-k
+        const float2 sp = hs[e * NP + (chunk >> 1)];
+        const bool odd = chunk & 1;
+        float v;
+        if (FMT == MOE_W_INT4_ROW) {
+            v = fmaf(a, 0.0625f, odd ? 0.f : -72.f * sp.y);
+        } else {
+            const float sc = bf16_lo(pv), mn = bf16_hi(pv);
+            v = fmaf(sc * 0.0625f, a, odd ? 0.f : (mn - 64.f * sc) * sp.y);
+        }
+        Y[st] = v * sp.x;
+    }
+    __syncthreads();  // h is no longer read: its LDS takes the partial sums
+    float* red = (float*)lds4;                          // [NCG][NS][64]
+    float* red8 = red + (size_t)NCG * NS * 64;          // [NCG][NS][8]
+#pragma unroll
+    for (int st = 0; st < NS; ++st) red[(w * NS + st) * 64 + lane] = Y[st];
+    __syncthreads();
+    // sum over the 8 chunks of each wavefront, in chunk order
+    for (int i = tid; i < NCG * NS * 8; i += nthr) {
+        const int ws = i >> 3, r = i & 7;
+        float y = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) y += red[ws * 64 + c * 8 + r];
+        red8[i] = y;
+    }
+    __syncthreads();
+    // row (g, r): sum over the wavefronts in order, scale, weight, combine
+    if (tid < 8 * RG) {
+        const int g = tid >> 3, r = tid & 7;
+        const int o = (blockIdx.x * RG + g) * 8 + r;
+        float m = 0.f;
+#pragma unroll
+        for (int e = 0; e < DC_NE; ++e)
+            if (e < ne) {
+                float y = 0.f;
+                for (int v2 = 0; v2 < NCG; ++v2) y += red8[(v2 * NS + e * RG + g) * 8 + r];
+                const uint8_t* base = (const uint8_t*)(uintptr_t)s_base[e];
+                if (base == nullptr) y = 0.f;  // not resident: no contribution
+                else if (FMT == MOE_W_INT4_ROW)
+                    y *= ((const float*)(base + (size_t)3 * H * I / 2))[2 * I + o];
+                if (e < f.n_shared) m += y;
+                else m = fmaf(s_wt[e], y, m);
+            }
+        if (f.residual) m = f.x[o] + m;
+        f.out[o] = m;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // launch
 // ---------------------------------------------------------------------------
 
@@ -495,6 +694,42 @@ hipError_t launch_gateup_finalize(const Fwd& f, hipStream_t st)
     const int n_rows = f.T * (f.K + f.n_shared);
     const int waves = n_rows * (f.I / 64);
     return launch_k(k_gu_fin, dim3((waves + 3) / 4), dim3(256), 0, st, f, n_rows);
+}
+
+// One-token down + combine: shapes it covers (otherwise the down GEMV and
+// the combine kernel run): 256 workgroups of H/256 rows in groups of 8, one
+// wavefront per 256 inputs.
+static int dn2_rg(const Fwd& f) { return f.H % 2048 == 0 ? f.H / 2048 : 0; }
+
+// Used for small down projections (at most 16 MiB of codes per token),
+// where the separate combine launch dominates; the many-unit down GEMV
+// streams large ones faster.
+bool down_combine1_ok(const Fwd& f)
+{
+    const int rg = dn2_rg(f), ncg = f.I / 256, ne = f.n_shared + f.K;
+    return f.T == 1 && ne <= DC_NE && (size_t)ne * f.H * f.I / 2 <= ((size_t)16 << 20) && rg >= 1 && rg <= 4 && f.I % 256 == 0 && ncg >= 1 &&
+           ncg <= 8 && ne * (f.I / 8) <= DC_HL * 64 * ncg && ne * (f.I / 64) <= 64 * ncg &&
+           dn2_lds_bytes(f.I, rg) <= 65536;
+}
+
+template <int FMT>
+static hipError_t dn2_launch(const Fwd& f, hipStream_t st)
+{
+    const int rg = dn2_rg(f);
+    const dim3 grid(f.H / (8 * rg)), block(64 * (f.I / 256));
+    const size_t lds = dn2_lds_bytes(f.I, rg);
+    switch (rg) {
+    case 1: return launch_k(k_dn2<FMT, 1>, grid, block, lds, st, f);
+    case 2: return launch_k(k_dn2<FMT, 2>, grid, block, lds, st, f);
+    case 3: return launch_k(k_dn2<FMT, 3>, grid, block, lds, st, f);
+    default: return launch_k(k_dn2<FMT, 4>, grid, block, lds, st, f);
+    }
+}
+
+hipError_t launch_down_combine1(const Fwd& f, hipStream_t st)
+{
+    if (f.fmt == MOE_W_INT4_ROW) return dn2_launch<MOE_W_INT4_ROW>(f, st);
+    return dn2_launch<MOE_W_INT4_AFFINE_G64>(f, st);
 }
 
 hipError_t launch_combine(const Fwd& f, hipStream_t st)

@@ -284,6 +284,13 @@ int run_forward(moe_ctx* c, const float* x, int T, int layer, float* out, int re
         rc = hip_rc(c, launch_gateup_finalize(f, c->stream));
         if (rc) return rc;
     }
+    if (down_combine1_ok(f)) {
+        mark(c, "down_combine");
+        rc = hip_rc(c, launch_down_combine1(f, c->stream));
+        if (rc) return rc;
+        mark(c, nullptr);
+        return MOE_OK;
+    }
     mark(c, "down_gemv");
     rc = hip_rc(c, launch_down_gemv(f, c->stream));
     if (rc) return rc;

@@ -135,6 +135,8 @@ hipError_t launch_gemm_hstage(const Fwd& f, hipStream_t st);
 hipError_t launch_gemm_down(const Fwd& f, hipStream_t st);
 hipError_t launch_gateup_finalize(const Fwd& f, hipStream_t st);
 hipError_t launch_combine(const Fwd& f, hipStream_t st);
+bool down_combine1_ok(const Fwd& f);
+hipError_t launch_down_combine1(const Fwd& f, hipStream_t st);
 size_t gemv_lds_bytes(int chunks_per_slice, int T);
 int gemv_step_chunks(int which);
 int gemv_max_dn_ks();

@@ -54,6 +54,12 @@ CONFIGS = {
     # Edge0 shape, affine int4 g64, 40 chained layers, one token, top-4
     "edge0_decode": LayerConfig("edge0_decode", H=2048, I=512, E=256, K=4, n_shared=0,
                                 fmt=W_INT4_AFFINE_G64, T=1, n_layers=40, seed=200, chained=True),
+    # small one-token layers with a shared expert (row and affine formats):
+    # shapes whose down projection and combine run as one kernel
+    "mid_row": LayerConfig("mid_row", H=2048, I=256, E=32, K=4, n_shared=1, fmt=W_INT4_ROW, T=1,
+                           n_layers=1, seed=400),
+    "mid_affine": LayerConfig("mid_affine", H=2048, I=512, E=32, K=8, n_shared=1,
+                              fmt=W_INT4_AFFINE_G64, T=1, n_layers=1, seed=401),
     # GLM-5.2 shape prefill, 2048 tokens, one layer
     "glm_prefill": LayerConfig("glm_prefill", H=6144, I=2048, E=256, K=8, n_shared=1,
                                fmt=W_INT4_ROW, T=2048, n_layers=1, seed=300, zipf_c=0.2),
