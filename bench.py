@@ -358,7 +358,7 @@ def main():
         {"verify": lambda: bench_chain(torch, "glm_verify", 64, result),
          "edge0": lambda: bench_chain(torch, "edge0_decode", 200, result),
          "edge0_k8": lambda: bench_chain(torch, "edge0_decode_k8", 200, result),
-         "prefill": lambda: bench_prefill(torch, 3, result)}[args.only]()
+         "prefill": lambda: bench_prefill(torch, 20, result)}[args.only]()
         print(json.dumps(result), flush=True)
         return
     bench_decode(torch, args, result)
@@ -368,7 +368,7 @@ def main():
         bench_chain(torch, "glm_verify", 64, result)
         bench_chain(torch, "edge0_decode", 200, result)
         bench_chain(torch, "edge0_decode_k8", 200, result)
-        bench_prefill(torch, 3, result)
+        bench_prefill(torch, 20, result)
     if not args.no_cpu:
         log("[bench] cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
