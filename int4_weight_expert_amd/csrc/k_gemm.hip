@@ -246,19 +246,18 @@ __global__ void __launch_bounds__(64 * GW, 1) k_gemm(Fwd f)
     __shared__ int s_src[GM], s_out[GM];
     __shared__ float s_inv[GM], s_sum[GM], s_rs[GM];
 
-    // Workgroup -> (tile, N tile), XCD-aware: workgroup p runs on XCD p % 8,
-    // so XCD x takes a contiguous range of the actual tiles with the N tiles
-    // innermost.  The workgroups sharing a tile's activations (all its N
-    // tiles), and neighbouring tiles of the same expert sharing weights, then
-    // run together behind one L2.
+    // Workgroup -> (tile, N tile), XCD-aware: workgroup p runs on XCD p % 8;
+    // tile i (the list is longest first) goes to XCD i % 8 with its N tiles
+    // innermost, so the workgroups sharing a tile's activations run together
+    // behind one L2 and every XCD gets an even share of the work, longest
+    // tiles first (little imbalance at the end of the launch).
     const int n_tiles = uni(f.n_tiles[0]);
     const int NT = gridDim.y;  // N tiles
     const int p = blockIdx.y * gridDim.x + blockIdx.x;
     const int xcd = p & 7, q = p >> 3;
-    const int per = (n_tiles + 7) >> 3;  // tiles per XCD
-    const int tile = xcd * per + q / NT;
+    const int tile = (q / NT) * 8 + xcd;  // tile i on XCD i mod 8
     const int ntile = q % NT;
-    if (q / NT >= per || tile >= n_tiles) return;
+    if (tile >= n_tiles) return;
     const int2 td = f.tiles[tile];
     const Group grp = uni_group(f.groups, uni(td.x));
     const int m0 = uni(td.y);
@@ -360,29 +359,53 @@ __global__ void __launch_bounds__(256) k_rowstage(const float* __restrict__ src,
     if (lane == 0) s[r] = make_float2(ldexpf(1.0f, e - 14), t);
 }
 
-// Tile list: each active group's rows in tiles of GM, groups in order.
+// Inclusive sum over the 512 threads of a workgroup (wavefront scans, then
+// the 8 wavefront totals); *total receives the sum of all.
+__device__ __forceinline__ int block_scan512(int v, int* s_w, int* total)
+{
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(v, o);
+        if (lane >= o) v += u;
+    }
+    if (lane == 63) s_w[w] = v;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        before += i < w ? s_w[i] : 0;
+        all += s_w[i];
+    }
+    __syncthreads();  // s_w may be rewritten by the next scan
+    *total = all;
+    return before + v;
+}
+
+// Tile list, longest first: every group's full 128-row tiles (groups in
+// order), then the partial tiles by descending number of occupied 32-row
+// blocks (groups in order within a class).  k_gemm runs tile i on XCD i mod 8,
+// so every XCD gets an even share of each class, longest first.
 __global__ void __launch_bounds__(512) k_tiles(Fwd f)
 {
-    __shared__ int s_n[512];
-    __shared__ int s_tot;
+    __shared__ int s_w[8];
     const int tid = threadIdx.x;
     const int ng = f.n_groups[0];
-    int nt = 0;
-    if (tid < ng) nt = (f.groups[tid].cnt + GM - 1) / GM;
-    s_n[tid] = nt;
-    __syncthreads();
-    // inclusive scan (Hillis-Steele over 512 entries)
-    for (int o = 1; o < 512; o <<= 1) {
-        const int v = tid >= o ? s_n[tid - o] : 0;
-        __syncthreads();
-        s_n[tid] += v;
-        __syncthreads();
+    int cnt = 0;
+    if (tid < ng) cnt = f.groups[tid].cnt;
+    const int nfull = cnt / GM, rem = cnt - nfull * GM;
+    const int cls = rem ? (rem + 31) >> 5 : 0;  // occupied blocks of the partial tile
+    int base = 0;
+    // pass 0: full tiles; passes 1..4: partial tiles with 4, 3, 2, 1 blocks
+    for (int pass = 0; pass < 5; ++pass) {
+        const int v = pass == 0 ? nfull : (cls == 5 - pass ? 1 : 0);
+        int total;
+        const int excl = block_scan512(v, s_w, &total) - v;
+        for (int i = 0; i < v; ++i)
+            f.tiles[base + excl + i] = make_int2(tid, pass == 0 ? i * GM : nfull * GM);
+        base += total;
     }
-    const int start = s_n[tid] - nt;
-    for (int i = 0; i < nt; ++i) f.tiles[start + i] = make_int2(tid, i * GM);
-    if (tid == 511) s_tot = s_n[511];
-    __syncthreads();
-    if (tid == 0) f.n_tiles[0] = s_tot;
+    if (tid == 0) f.n_tiles[0] = base;
 }
 
 // ---------------------------------------------------------------------------
