@@ -174,6 +174,65 @@ __device__ __forceinline__ void stage_span64(float v, int lane, uint16_t* __rest
     if (lane == 0) *sc = make_float2(ldexpf(1.0f, e - 14), t);
 }
 
+// One row of `len` fp32 values (len a multiple of 8), held by one
+// wavefront, staged as fp16 with one power-of-two scale that puts its largest
+// magnitude in [2^13, 2^14): q[len/8] in pair order and *s = (2^-k, sum of
+// the fp16 values).  Lane l holds 8-value groups l, l + 64, ... (NG of them,
+// NG >= len / 512), all loaded before anything else.  Also returns the
+// row's fp32 sum and sum of squares (wavefront totals).
+template <int NG>
+__device__ __forceinline__ void stage_row(const float* __restrict__ row, int len, int lane,
+                                          uint4* __restrict__ q, float2* __restrict__ s,
+                                          float& sum, float& ss)
+{
+    const float4* r4 = (const float4*)row;
+    const int ng = len / 8;
+    float4 a[NG], b[NG];
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+        const int g = lane + 64 * i;
+        a[i] = b[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (g < ng) {
+            a[i] = r4[2 * g];
+            b[i] = r4[2 * g + 1];
+        }
+    }
+    float m = 0.f, su = 0.f, sq = 0.f;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+        const float v[8] = {a[i].x, a[i].y, a[i].z, a[i].w, b[i].x, b[i].y, b[i].z, b[i].w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            m = fmaxf(m, fabsf(v[k]));
+            su += v[k];
+            sq = fmaf(v[k], v[k], sq);
+        }
+    }
+    m = wave_max(m);
+    sum = wave_sum(su);
+    ss = wave_sum(sq);
+    int e;
+    frexpf(m, &e);
+    e = max(e, -100);
+    const float sc = ldexpf(1.0f, 14 - e);
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+        const int g = lane + 64 * i;
+        if (g < ng) {
+            const _Float16 h0 = (_Float16)(a[i].x * sc), h1 = (_Float16)(a[i].y * sc);
+            const _Float16 h2 = (_Float16)(a[i].z * sc), h3 = (_Float16)(a[i].w * sc);
+            const _Float16 h4 = (_Float16)(b[i].x * sc), h5 = (_Float16)(b[i].y * sc);
+            const _Float16 h6 = (_Float16)(b[i].z * sc), h7 = (_Float16)(b[i].w * sc);
+            q[g] = make_uint4(pack_h2(h0, h4), pack_h2(h1, h5), pack_h2(h2, h6), pack_h2(h3, h7));
+            t += (((float)h0 + (float)h1) + ((float)h2 + (float)h3)) +
+                 (((float)h4 + (float)h5) + ((float)h6 + (float)h7));
+        }
+    }
+    t = wave_sum(t);
+    if (lane == 0) *s = make_float2(ldexpf(1.0f, e - 14), t);
+}
+
 // Data handed between workgroups of one kernel travels with agent-scope
 // relaxed atomic accesses (sc1 loads/stores, coherent across the XCDs' L2s
 // without writing back or invalidating whole caches).  An arrival first

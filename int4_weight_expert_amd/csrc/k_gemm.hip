@@ -324,6 +324,7 @@ __global__ void __launch_bounds__(64 * GW, 1) k_gemm(Fwd f)
 
 // Per-row fp16 staging (one wavefront per row of `len` fp32 values):
 // q [rows][len/8] in pair order, s[row] = (2^-k, sum of the fp16 values).
+template <int NG>
 __global__ void __launch_bounds__(256) k_rowstage(const float* __restrict__ src, int n_rows,
                                                   int len, uint4* __restrict__ q,
                                                   float2* __restrict__ s)
@@ -331,32 +332,8 @@ __global__ void __launch_bounds__(256) k_rowstage(const float* __restrict__ src,
     const int lane = threadIdx.x & 63;
     const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (r >= n_rows) return;
-    const float4* row = (const float4*)(src + (size_t)r * len);
-    const int n4 = len / 4;
-    float m = 0.f;
-    for (int i = lane; i < n4; i += 64) {
-        const float4 v = row[i];
-        m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-    }
-    m = wave_max(m);
-    int e;
-    frexpf(m, &e);
-    e = max(e, -100);
-    const float sc = ldexpf(1.0f, 14 - e);
-    float t = 0.f;
-    uint4* qr = q + (size_t)r * (len / 8);
-    for (int g = lane; g < len / 8; g += 64) {
-        const float4 a = row[2 * g], b = row[2 * g + 1];
-        const _Float16 h0 = (_Float16)(a.x * sc), h1 = (_Float16)(a.y * sc);
-        const _Float16 h2 = (_Float16)(a.z * sc), h3 = (_Float16)(a.w * sc);
-        const _Float16 h4 = (_Float16)(b.x * sc), h5 = (_Float16)(b.y * sc);
-        const _Float16 h6 = (_Float16)(b.z * sc), h7 = (_Float16)(b.w * sc);
-        qr[g] = make_uint4(pack_h2(h0, h4), pack_h2(h1, h5), pack_h2(h2, h6), pack_h2(h3, h7));
-        t += (((float)h0 + (float)h1) + ((float)h2 + (float)h3)) +
-             (((float)h4 + (float)h5) + ((float)h6 + (float)h7));
-    }
-    t = wave_sum(t);
-    if (lane == 0) s[r] = make_float2(ldexpf(1.0f, e - 14), t);
+    float sum, ss;
+    stage_row<NG>(src + (size_t)r * len, len, lane, q + (size_t)r * (len / 8), s + r, sum, ss);
 }
 
 // Inclusive sum over the 512 threads of a workgroup (wavefront scans, then
@@ -441,8 +418,17 @@ hipError_t launch_gemm_gateup(const Fwd& f, hipStream_t st)
 hipError_t launch_gemm_hstage(const Fwd& f, hipStream_t st)
 {
     const int rows = f.T * (f.K + f.n_shared);
-    return launch_k(k_rowstage, dim3((rows + 3) / 4), dim3(256), 0, st, (const float*)f.hbuf,
-                    rows, f.I, f.hq, f.hrow);
+    const dim3 grid((rows + 3) / 4), block(256);
+    const int ng = (f.I + 511) / 512;  // 8-value groups per lane
+    auto go = [&](auto kern) {
+        return launch_k(kern, grid, block, 0, st, (const float*)f.hbuf, rows, f.I, f.hq, f.hrow);
+    };
+    if (ng <= 1) return go(k_rowstage<1>);
+    if (ng <= 2) return go(k_rowstage<2>);
+    if (ng <= 4) return go(k_rowstage<4>);
+    if (ng <= 8) return go(k_rowstage<8>);
+    if (ng <= 12) return go(k_rowstage<12>);
+    return go(k_rowstage<16>);
 }
 
 hipError_t launch_gemm_down(const Fwd& f, hipStream_t st)
@@ -451,7 +437,8 @@ hipError_t launch_gemm_down(const Fwd& f, hipStream_t st)
 }
 
 // Shapes the grouped GEMM tiles exactly: N tiles of 256 (gate/up) and 512
-// (down) output rows.
-bool gemm_shape_ok(int H, int I) { return H % 512 == 0 && I % 256 == 0; }
+// (down) output rows; rows of at most 8192 values for the one-pass row
+// staging (16 groups of 8 per lane).
+bool gemm_shape_ok(int H, int I) { return H % 512 == 0 && I % 256 == 0 && H <= 8192 && I <= 8192; }
 
 }  // namespace moe

@@ -600,6 +600,47 @@ __global__ void __launch_bounds__(512) k_dn2(Fwd f)
     }
 }
 
+// Combine of single-slice partials ([rows][H], the grouped GEMM's layout),
+// one thread per 4 consecutive outputs of a token: the same fixed order and
+// arithmetic per element as combine_one.
+__global__ void __launch_bounds__(256) k_combine_rows(Fwd f)
+{
+    const int H4 = f.H / 4, T = f.T, K = f.K;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (int64_t)T * H4) return;
+    const int t = (int)(idx / H4), d4 = (int)(idx - (int64_t)t * H4);
+    float4 v[9];
+#pragma unroll
+    for (int e = 0; e < 9; ++e) {
+        int r = -1;
+        if (e < f.n_shared) r = T * K + e * T + t;
+        else if (e - f.n_shared < K) r = t * K + (e - f.n_shared);
+        v[e] = r >= 0 ? ((const float4*)(f.ypart + (size_t)r * f.H))[d4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float4 m = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int e = 0; e < 9; ++e) {
+        if (e < f.n_shared) {
+            m.x += v[e].x;
+            m.y += v[e].y;
+            m.z += v[e].z;
+            m.w += v[e].w;
+        } else if (e - f.n_shared < K) {
+            const float w = f.wts[t * K + (e - f.n_shared)];
+            m.x = fmaf(w, v[e].x, m.x);
+            m.y = fmaf(w, v[e].y, m.y);
+            m.z = fmaf(w, v[e].z, m.z);
+            m.w = fmaf(w, v[e].w, m.w);
+        }
+    }
+    float4* o = (float4*)(f.out + (size_t)t * f.H) + d4;
+    if (f.residual) {
+        const float4 x = ((const float4*)(f.x + (size_t)t * f.H))[d4];
+        m = make_float4(x.x + m.x, x.y + m.y, x.z + m.z, x.w + m.w);
+    }
+    *o = m;
+}
+
 // ---------------------------------------------------------------------------
 // launch
 // ---------------------------------------------------------------------------
@@ -734,6 +775,10 @@ hipError_t launch_down_combine1(const Fwd& f, hipStream_t st)
 
 hipError_t launch_combine(const Fwd& f, hipStream_t st)
 {
+    if (f.dn_ks == 1 && f.n_shared + f.K <= 9) {
+        const int64_t n = (int64_t)f.T * (f.H / 4);
+        return launch_k(k_combine_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, f);
+    }
     const int64_t n = (int64_t)f.T * f.H;
     return launch_k(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, f);
 }

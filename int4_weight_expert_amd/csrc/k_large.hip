@@ -27,6 +27,7 @@ __device__ __forceinline__ uint32_t ordf(float c)
 
 // Per-token sum, RMSNorm factor and sums of 64-column groups; one
 // wavefront per token.  H must be a multiple of 256.
+template <int NG>
 __global__ void __launch_bounds__(256) k_tokstats(Fwd f)
 {
     const int lane = threadIdx.x & 63;
@@ -34,41 +35,22 @@ __global__ void __launch_bounds__(256) k_tokstats(Fwd f)
     if (t >= f.T) return;
     const int H = f.H;
     const float* xt = f.x + (size_t)t * H;
-    float sum = 0.f, ss = 0.f, mx = 0.f;
-    for (int s = 0; s < H / 64; ++s) {
-        const float v = xt[s * 64 + lane];
-        sum += v;
-        ss = fmaf(v, v, ss);
-        mx = fmaxf(mx, fabsf(v));
-        if (f.row_staging == 0)  // expert GEMVs: fp16 spans of 64
-            stage_span64(v, lane, (uint16_t*)(f.xq + (size_t)t * (H / 8) + s * 8),
-                         f.xsc + (size_t)t * (H / 64) + s);
-    }
-    sum = wsum(sum);
-    ss = wsum(ss);
-    if (f.row_staging) {
+    float sum = 0.f, ss = 0.f;
+    if constexpr (NG > 0) {
         // grouped GEMM: the whole row as fp16 with one power-of-two scale
         // (largest magnitude in [2^13, 2^14)), in pair order, and its sum
-        mx = wave_max(mx);
-        int e;
-        frexpf(mx, &e);
-        e = max(e, -100);
-        const float sc = ldexpf(1.0f, 14 - e);
-        float ts = 0.f;
-        const float4* row = (const float4*)xt;
-        uint4* q = f.xq + (size_t)t * (H / 8);
-        for (int g = lane; g < H / 8; g += 64) {
-            const float4 a = row[2 * g], b = row[2 * g + 1];
-            const _Float16 h0 = (_Float16)(a.x * sc), h1 = (_Float16)(a.y * sc);
-            const _Float16 h2 = (_Float16)(a.z * sc), h3 = (_Float16)(a.w * sc);
-            const _Float16 h4 = (_Float16)(b.x * sc), h5 = (_Float16)(b.y * sc);
-            const _Float16 h6 = (_Float16)(b.z * sc), h7 = (_Float16)(b.w * sc);
-            q[g] = make_uint4(pack_h2(h0, h4), pack_h2(h1, h5), pack_h2(h2, h6), pack_h2(h3, h7));
-            ts += (((float)h0 + (float)h1) + ((float)h2 + (float)h3)) +
-                  (((float)h4 + (float)h5) + ((float)h6 + (float)h7));
+        stage_row<NG>(xt, H, lane, f.xq + (size_t)t * (H / 8), f.xrow + t, sum, ss);
+    } else {
+        // expert GEMVs: fp16 spans of 64
+        for (int s = 0; s < H / 64; ++s) {
+            const float v = xt[s * 64 + lane];
+            sum += v;
+            ss = fmaf(v, v, ss);
+            stage_span64(v, lane, (uint16_t*)(f.xq + (size_t)t * (H / 8) + s * 8),
+                         f.xsc + (size_t)t * (H / 64) + s);
         }
-        ts = wsum(ts);
-        if (lane == 0) f.xrow[t] = make_float2(ldexpf(1.0f, e - 14), ts);
+        sum = wsum(sum);
+        ss = wsum(ss);
     }
     if (lane == 0) {
         f.tok[t].xsum = sum;
@@ -328,7 +310,17 @@ __global__ void __launch_bounds__(1024) k_bucket(const int32_t* __restrict__ ids
 hipError_t launch_router_large(const Fwd& f, hipStream_t st, int stage)
 {
     switch (stage) {
-    case 0: return launch_k(k_tokstats, dim3((f.T + 3) / 4), dim3(256), 0, st, f);
+    case 0: {
+        const dim3 grid((f.T + 3) / 4), block(256);
+        if (!f.row_staging) return launch_k(k_tokstats<0>, grid, block, 0, st, f);
+        const int ng = (f.H + 511) / 512;  // 8-value groups per lane (H <= 8192 here)
+        if (ng <= 1) return launch_k(k_tokstats<1>, grid, block, 0, st, f);
+        if (ng <= 2) return launch_k(k_tokstats<2>, grid, block, 0, st, f);
+        if (ng <= 4) return launch_k(k_tokstats<4>, grid, block, 0, st, f);
+        if (ng <= 8) return launch_k(k_tokstats<8>, grid, block, 0, st, f);
+        if (ng <= 12) return launch_k(k_tokstats<12>, grid, block, 0, st, f);
+        return launch_k(k_tokstats<16>, grid, block, 0, st, f);
+    }
     case 1:
         return launch_k(k_router_mfma, dim3((f.T + 31) / 32, f.Epad / 64), dim3(512), 0, st, f);
     case 2: return launch_k(k_topk, dim3((f.T + 3) / 4), dim3(256), 0, st, f);
