@@ -60,60 +60,87 @@ __global__ void __launch_bounds__(256) k_tokstats(Fwd f)
 
 // Router logits for many tokens on the fp32 matrix cores
 // (v_mfma_f32_32x32x2_f32: fp32 products, fp32 accumulation).  Workgroup =
-// 32 tokens x 64 experts; its 8 wavefronts each take one eighth of the H
-// inputs, with two accumulator pairs (even and odd steps) per 32-expert
-// block, and the slices are summed in LDS in a fixed order.  Per step of 8
-// inputs a lane loads one float4 of x (4 consecutive inputs of its token)
-// and one float4 of the interleaved router weights per 32-expert block; the
-// lanes of the lower half take inputs k..k+3, the upper half k+4..k+7, so
-// MFMA step j pairs inputs k+j and k+4+j in both operands.
+// 64 tokens x every expert x one of ROUTER_SLICES slices of the H inputs, so
+// x is read once and each router weight once per 64 tokens.  x goes through
+// LDS in chunks of 32 inputs (double-buffered, input-major so that the
+// operand reads are conflict-free); wavefront w takes experts 32w..32w+31
+// for both 32-token blocks, its router weights straight from memory.  Per
+// step of 8 inputs the lanes of the lower half take inputs k..k+3, the upper
+// half k+4..k+7, so MFMA step j pairs inputs k+j and k+4+j in both operands;
+// two accumulator pairs (even and odd steps) per token block.  Each slice's
+// partial logits go to a plane of their own; k_topk sums the planes in slice
+// order.
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 __global__ void __launch_bounds__(512) k_router_mfma(Fwd f)
 {
-    __shared__ float red[8][2 * 16 * 64];  // [wave][block][reg][lane]
-    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int H = f.H, T = f.T;
-    const int t0 = blockIdx.x * 32, eb = blockIdx.y;
+    __shared__ float4 xs[2][8][64];  // [buffer][float4 of the chunk][token]
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nthr = blockDim.x;
+    const int H = f.H, T = f.T, Epad = f.Epad;
+    const int t0 = blockIdx.x * 64, slice = blockIdx.y;
     const int h = lane >> 5, m = lane & 31;
-    const int row = t0 + m;
-    const float4* xr = row < T ? (const float4*)(f.x + (size_t)row * H) : nullptr;
-    const float4* wb = (const float4*)f.wr + (size_t)eb * (H / 4) * 64;
-    const int KW = H / 8;  // inputs per wavefront (H is a multiple of 256)
+    // expert e = 32w + m: interleaved block e / 64, lane e % 64
+    const float4* wb = (const float4*)f.wr + (size_t)(w >> 1) * (H / 4) * 64 + (w & 1) * 32 + m;
+    const int KC = H / ROUTER_SLICES;  // inputs per slice (H is a multiple of 256)
+    const int kb = slice * KC, NCH = KC / 32;
+    // x loader: threads cover (token, float4) pairs of a chunk, 512 in all
+    auto load_x = [&](int ch, float4 (&v)[4]) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = tid + r * nthr;  // pair index
+            const int tok = i >> 3, j = i & 7;
+            v[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (i < 512 && t0 + tok < T)
+                v[r] = ((const float4*)(f.x + (size_t)(t0 + tok) * H + kb + ch * 32))[j];
+        }
+    };
+    auto store_x = [&](int buf, const float4 (&v)[4]) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = tid + r * nthr;
+            if (i < 512) xs[buf][i & 7][i >> 3] = v[r];
+        }
+    };
     f32x16 acc[2][2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[b][0] = acc[b][1] = (f32x16){};
-    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 2
-    for (int k = w * KW; k < (w + 1) * KW; k += 8) {
-        const int q = (k >> 2) + h;  // float4 index of this lane's 4 inputs
-        const float4 a = xr ? xr[q] : z;
-        const float4 b0 = wb[(size_t)q * 64 + m];
-        const float4 b1 = wb[(size_t)q * 64 + 32 + m];
-        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, b0.x, acc[0][0], 0, 0, 0);
-        acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.x, b1.x, acc[1][0], 0, 0, 0);
-        acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, b0.y, acc[0][1], 0, 0, 0);
-        acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.y, b1.y, acc[1][1], 0, 0, 0);
-        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, b0.z, acc[0][0], 0, 0, 0);
-        acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.z, b1.z, acc[1][0], 0, 0, 0);
-        acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, b0.w, acc[0][1], 0, 0, 0);
-        acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a.w, b1.w, acc[1][1], 0, 0, 0);
-    }
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) red[w][(b * 16 + j) * 64 + lane] = acc[b][0][j] + acc[b][1][j];
+    float4 xv[4];
+    load_x(0, xv);
+    store_x(0, xv);
     __syncthreads();
-    // output (token, expert) of entry (block b, reg j, lane l):
-    // token (j/4)*8 + (l/32)*4 + j%4, expert b*32 + l%32
-    for (int i = threadIdx.x; i < 2 * 16 * 64; i += 512) {
-        float v = 0.f;
+    for (int ch = 0; ch < NCH; ++ch) {
+        const int buf = ch & 1;
+        if (ch + 1 < NCH) load_x(ch + 1, xv);
+        float4 bw[4];
 #pragma unroll
-        for (int s = 0; s < 8; ++s) v += red[s][i];
-        const int b = i >> 10, j = (i >> 6) & 15, l = i & 63;
-        const int t = t0 + (j >> 2) * 8 + (l >> 5) * 4 + (j & 3);
-        if (t < T) f.logits[(size_t)t * f.Epad + eb * 64 + b * 32 + (l & 31)] = v;
+        for (int st = 0; st < 4; ++st) bw[st] = wb[(size_t)((kb + ch * 32 + st * 8) / 4 + h) * 64];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const float4 a0 = xs[buf][2 * st + h][m], a1 = xs[buf][2 * st + h][32 + m];
+            const float4 b = bw[st];
+            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.x, b.x, acc[0][0], 0, 0, 0);
+            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.x, b.x, acc[1][0], 0, 0, 0);
+            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.y, b.y, acc[0][1], 0, 0, 0);
+            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.y, b.y, acc[1][1], 0, 0, 0);
+            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.z, b.z, acc[0][0], 0, 0, 0);
+            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.z, b.z, acc[1][0], 0, 0, 0);
+            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.w, b.w, acc[0][1], 0, 0, 0);
+            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.w, b.w, acc[1][1], 0, 0, 0);
+        }
+        if (ch + 1 < NCH) store_x(buf ^ 1, xv);
+        __syncthreads();
     }
+    // entry (reg j, lane l) of a 32 x 32 tile: token (j/4)*8 + (l/32)*4 + j%4,
+    // expert l%32
+    float* plane = f.logits + (size_t)slice * T * Epad;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int t = t0 + 32 * tb + (j >> 2) * 8 + h * 4 + (j & 3);
+            if (t < T) plane[(size_t)t * Epad + 32 * w + m] = acc[tb][0][j] + acc[tb][1][j];
+        }
 }
 
 __global__ void __launch_bounds__(256) k_topk(Fwd f)
@@ -130,7 +157,12 @@ __global__ void __launch_bounds__(256) k_topk(Fwd f)
         c[m] = -INFINITY;
         sg[m] = 0.f;
         if (e < E) {
-            const float l = f.logits[(size_t)t * Epad + e] * rs;
+            // the router's slice partials, summed in slice order
+            float l = 0.f;
+#pragma unroll
+            for (int sl = 0; sl < ROUTER_SLICES; ++sl)
+                l += f.logits[((size_t)sl * f.T + t) * Epad + e];
+            l *= rs;
             sg[m] = 1.0f / (1.0f + expf(-l));
             c[m] = sg[m] + f.bias[e];
         }
@@ -322,7 +354,8 @@ hipError_t launch_router_large(const Fwd& f, hipStream_t st, int stage)
         return launch_k(k_tokstats<16>, grid, block, 0, st, f);
     }
     case 1:
-        return launch_k(k_router_mfma, dim3((f.T + 31) / 32, f.Epad / 64), dim3(512), 0, st, f);
+        return launch_k(k_router_mfma, dim3((f.T + 63) / 64, ROUTER_SLICES), dim3(64 * (f.Epad / 32)), 0,
+                        st, f);
     case 2: return launch_k(k_topk, dim3((f.T + 3) / 4), dim3(256), 0, st, f);
     default:
         return launch_k(k_bucket, dim3(1), dim3(1024), 0, st, (const int32_t*)f.ids, f.T * f.K,

@@ -386,7 +386,7 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
     rc = rc ? rc : dalloc(c, &c->staging, c->slot_bytes);
     rc = rc ? rc : dalloc(c, &c->part, (H / 64) * ROUTER_SMALL_MAX_T * c->Epad * 4);
     rc = rc ? rc : dalloc(c, &c->tpart, (H / 64) * ROUTER_SMALL_MAX_T * 2 * 4);
-    rc = rc ? rc : dalloc(c, &c->logits, Tm * c->Epad * 4);
+    rc = rc ? rc : dalloc(c, &c->logits, (size_t)ROUTER_SLICES * Tm * c->Epad * 4);
     rc = rc ? rc : dalloc(c, &c->ids, Tm * K * 4);
     rc = rc ? rc : dalloc(c, &c->wts, Tm * K * 4);
     rc = rc ? rc : dalloc(c, &c->tok, Tm * sizeof(TokStat));

@@ -61,7 +61,7 @@ struct Fwd {
     float* part;          // small-T router partial logits [S][T][Epad]
     float* tpart;         // small-T router partial token sums [S][T][2] (sum, sum of squares)
     int S;                // router K-slices of 64 columns (S = H/64)
-    float* logits;        // [T][Epad] (large-T router)
+    float* logits;        // [ROUTER_SLICES][T][Epad] partial logits (large-T router)
     int32_t* ids;         // [T][K]
     float* wts;           // [T][K]
     TokStat* tok;         // [T]
@@ -142,5 +142,6 @@ int gemv_step_chunks(int which);
 int gemv_max_dn_ks();
 
 constexpr int ROUTER_SMALL_MAX_T = 8;
+constexpr int ROUTER_SLICES = 8;  // H slices of the large-T router (partial logit planes)
 
 }  // namespace moe
