@@ -77,6 +77,24 @@ def time_graph(torch, ml, step_fns, steps: int, warmup: int):
     return g, dt / (reps * L), reps * L
 
 
+def replay_percentiles(torch, g, n_layers: int, reps: int = 50):
+    """Median, p10 and p90 of the per-layer time over `reps` single graph
+    replays (each replay runs every resident layer once), from events
+    recorded around each replay on the replay stream."""
+    import numpy as np
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 / n_layers for a, b in evs])
+    return {"median_us_per_layer": float(np.median(us)), "p10_us_per_layer": float(np.quantile(us, 0.1)),
+            "p90_us_per_layer": float(np.quantile(us, 0.9)), "replays": reps}
+
+
 def time_eager(torch, step_fns, steps: int):
     L = len(step_fns)
     torch.cuda.synchronize()
@@ -120,6 +138,7 @@ def bench_decode(torch, args, result):
         eager_ref.append(outs[l].clone())
     g, t_graph, n_timed = time_graph(torch, ml, fns, args.steps, args.warmup)
     graph_ok = all(torch.equal(outs[l], eager_ref[l]) for l in range(L))
+    pct = replay_percentiles(torch, g, L)
     g.replay()
     torch.cuda.synchronize()
     graph_ok = graph_ok and all(torch.equal(outs[l], eager_ref[l]) for l in range(L))
@@ -150,6 +169,7 @@ def bench_decode(torch, args, result):
     })
     result["extra"]["glm_decode"] = {
         "us_per_layer_graph": t_graph * 1e6, "us_per_layer_eager": t_eager * 1e6,
+        "graph_replay_percentiles": pct,
         "graph_replay_matches_eager": graph_ok,
         "layer_algorithmic_bytes": layer_bytes,
         "layer_gbps": layer_bytes / t_step / 1e9,
@@ -192,9 +212,12 @@ def bench_chain(torch, name, steps, result):
     x.copy_(x0)
     g, t_graph, _ = time_graph(torch, ml, fns, reps * L, 0)
     t = t_graph
+    x.copy_(x0)
+    pct = replay_percentiles(torch, g, L, reps=20)
     bytes_layer = float(np.mean([glm_bytes(cfg, u + cfg.n_shared, cfg.T) for u in distinct]))
     result["extra"][name] = {
         "T": cfg.T, "layers": L, "us_per_layer": t * 1e6, "us_per_layer_eager": t_eager * 1e6,
+        "graph_replay_percentiles": pct,
         "us_per_step_all_layers": t * L * 1e6, "tokens_per_s_per_layer": cfg.T / t,
         "distinct_experts_per_layer": distinct,
         "layer_algorithmic_bytes_mean": bytes_layer,
@@ -222,23 +245,36 @@ def bench_prefill(torch, steps, result):
     counts = np.bincount(ids_np.ravel(), minlength=cfg.E)
     tiles = int(np.sum((counts + 127) // 128) + cfg.n_shared * ((cfg.T + 127) // 128))
     rows = int(counts.sum() + cfg.n_shared * cfg.T)
+    sizes = np.concatenate([counts[counts > 0], np.full(cfg.n_shared, cfg.T)])
+    issued = int(np.sum((sizes // 128) * 128 + ((sizes % 128 + 31) // 32) * 32))  # 32-row blocks
     ml.forward(x, 0, out)
     torch.cuda.synchronize()
+    eager_out = out.clone()
     n = max(2, steps)
     t0 = time.perf_counter()
     for _ in range(n):
         ml.forward(x, 0, out)
     torch.cuda.synchronize()
-    t = (time.perf_counter() - t0) / n
+    t_eager = (time.perf_counter() - t0) / n
+    # one forward captured in a HIP graph and replayed (as the decode bench)
+    g, t, _ = time_graph(torch, ml, [lambda: ml.forward(x, 0, out)], n, 2)
+    graph_ok = bool(torch.equal(out, eager_out))
+    pct = replay_percentiles(torch, g, 1, reps=n)
+    pct = {"median_ms": pct["median_us_per_layer"] * 1e-3, "p10_ms": pct["p10_us_per_layer"] * 1e-3,
+           "p90_ms": pct["p90_us_per_layer"] * 1e-3, "replays": n}
+    if not graph_ok:
+        t = t_eager
     kt, _ = kernel_times(torch, ml, [lambda: ml.forward(x, 0, out)], 3)
     flops = 2.0 * (cfg.T * cfg.K + cfg.T * cfg.n_shared) * 3 * cfg.H * cfg.I
     result["extra"]["glm_prefill"] = {
-        "T": cfg.T, "ms_per_layer": t * 1e3, "tokens_per_s": cfg.T / t,
+        "T": cfg.T, "ms_per_layer": t * 1e3, "ms_per_layer_eager": t_eager * 1e3,
+        "graph_replay_matches_eager": graph_ok, "graph_replay_percentiles": pct, "tokens_per_s": cfg.T / t,
         "expert_flops": flops, "tflops": flops / t / 1e12,
         "frac_fp16_mfma_peak": flops / t / 1e12 / BF16_PEAK_TFLOPS,
         "distinct_experts": distinct, "kernel_avg_ms": kt,
         "tokens_per_expert_max": int(counts.max()), "gemm_tiles_128": tiles,
-        "gemm_row_occupancy": rows / (tiles * 128.0),
+        "gemm_row_occupancy": rows / (tiles * 128.0), "gemm_rows_issued_32": issued,
+        "gemm_issued_row_occupancy": rows / float(issued),
     }
     log(f"[bench] glm_prefill: {t * 1e3:.2f} ms/layer, {flops / t / 1e12:.1f} TFLOP/s; {kt}")
     ml.close()
