@@ -54,6 +54,9 @@ def lib() -> ctypes.CDLL:
         L.orc_expert.restype = i32
         L.orc_route.argtypes = [vp, i32, i64, vp, vp, i32, i32, f32, i32, vp, vp, vp, vp, vp, vp]
         L.orc_route.restype = i32
+        L.orc_route_groups.argtypes = [vp, i32, i64, vp, vp, i32, i32, i32, i32, f32, i32, vp, vp,
+                                       vp, vp, vp, vp, vp]
+        L.orc_route_groups.restype = i32
         L.orc_bucket.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp]
         L.orc_bucket.restype = i32
         L.orc_combine.argtypes = [i32, i32, i64, i32, vp, vp, vp, vp]
@@ -61,6 +64,9 @@ def lib() -> ctypes.CDLL:
         L.orc_moe_layer.argtypes = [vp, i32, i64, i64, i32, i32, i32, vp, vp, f32, i32, vp, i32,
                                     vp, vp, vp, vp]
         L.orc_moe_layer.restype = i32
+        L.orc_moe_layer_groups.argtypes = [vp, i32, i64, i64, i32, i32, i32, vp, vp, i32, i32, f32,
+                                           i32, vp, i32, vp, vp, vp, vp]
+        L.orc_moe_layer_groups.restype = i32
         L.orc_rmsnorm.argtypes = [vp, i32, i64, f32, vp]
         L.orc_rmsnorm.restype = None
         L.orc_residual_layer.argtypes = [vp, i32, i64, i64, i32, i32, i32, vp, vp, f32, i32, vp,
@@ -165,8 +171,19 @@ def expert(fmt: int, H: int, I: int, blob: np.ndarray, x: np.ndarray):
     return y, h
 
 
-def route(x, Wr, bias, K: int, routed_scale: float = 2.5, norm_topk: int = 1):
-    """Returns ids [T,K], wts [T,K], logits [T,E], sig [T,E], gap_k [T], gap_in [T]."""
+def route(x, Wr, bias, K: int, routed_scale: float = 2.5, norm_topk: int = 1, n_group: int = 1,
+          topk_group: int = 1):
+    """Returns ids [T,K], wts [T,K], logits [T,E], sig [T,E], gap_k [T], gap_in [T].
+    With groups, gap_k is the smaller of the K-th/(K+1)-th score gap and the
+    kept/excluded group-score gap (either closes on a near tie)."""
+    ids, wts, logits, sig, gk, gi, gg = route_groups(x, Wr, bias, K, n_group, topk_group,
+                                                      routed_scale, norm_topk)
+    return ids, wts, logits, sig, np.minimum(gk, gg), gi
+
+
+def route_groups(x, Wr, bias, K: int, n_group: int, topk_group: int, routed_scale: float = 2.5,
+                 norm_topk: int = 1):
+    """As route, plus gap_g [T]: the kept/excluded group-score gap."""
     x, Wr, bias = _f32(x), _f32(Wr), _f32(bias)
     T, H = x.shape
     E = Wr.shape[0]
@@ -176,11 +193,13 @@ def route(x, Wr, bias, K: int, routed_scale: float = 2.5, norm_topk: int = 1):
     sig = np.empty((T, E), dtype=np.float32)
     gk = np.empty(T, dtype=np.float64)
     gi = np.empty(T, dtype=np.float64)
-    rc = lib().orc_route(_p(x), T, H, _p(Wr), _p(bias), E, K, routed_scale, norm_topk, _p(ids),
-                         _p(wts), _p(logits), _p(sig), _p(gk), _p(gi))
+    gg = np.empty(T, dtype=np.float64)
+    rc = lib().orc_route_groups(_p(x), T, H, _p(Wr), _p(bias), E, K, n_group, topk_group,
+                                routed_scale, norm_topk, _p(ids), _p(wts), _p(logits), _p(sig),
+                                _p(gk), _p(gi), _p(gg))
     if rc:
-        raise ValueError(f"orc_route failed ({rc})")
-    return ids, wts, logits, sig, gk, gi
+        raise ValueError(f"orc_route_groups failed ({rc})")
+    return ids, wts, logits, sig, gk, gi, gg
 
 
 def bucket(ids: np.ndarray, E: int):
@@ -214,7 +233,8 @@ def _blob_array(blobs):
     return arr
 
 
-def moe_layer(x, Wr, bias, K, fmt, I, blobs, shared_blobs, routed_scale=2.5, norm_topk=1):
+def moe_layer(x, Wr, bias, K, fmt, I, blobs, shared_blobs, routed_scale=2.5, norm_topk=1,
+              n_group=1, topk_group=1):
     """Whole layer; blobs is a list of E blobs (None = not resident)."""
     x, Wr, bias = _f32(x), _f32(Wr), _f32(bias)
     T, H = x.shape
@@ -224,10 +244,11 @@ def moe_layer(x, Wr, bias, K, fmt, I, blobs, shared_blobs, routed_scale=2.5, nor
     wts = np.empty((T, K), dtype=np.float32)
     ba = _blob_array(blobs)
     sa = _blob_array(shared_blobs) if shared_blobs else None
-    rc = lib().orc_moe_layer(_p(x), T, H, I, E, K, fmt, _p(Wr), _p(bias), routed_scale, norm_topk,
-                             ctypes.cast(ba, ctypes.c_void_p), len(shared_blobs or []),
-                             ctypes.cast(sa, ctypes.c_void_p) if sa is not None else None,
-                             _p(out), _p(ids), _p(wts))
+    rc = lib().orc_moe_layer_groups(_p(x), T, H, I, E, K, fmt, _p(Wr), _p(bias), n_group,
+                                    topk_group, routed_scale, norm_topk,
+                                    ctypes.cast(ba, ctypes.c_void_p), len(shared_blobs or []),
+                                    ctypes.cast(sa, ctypes.c_void_p) if sa is not None else None,
+                                    _p(out), _p(ids), _p(wts))
     if rc:
         raise ValueError(f"orc_moe_layer failed ({rc})")
     return out, ids, wts

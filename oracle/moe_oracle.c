@@ -344,20 +344,42 @@ int orc_expert(int fmt, int64_t H, int64_t I, const uint8_t *blob, const float *
  * ranks (or +inf when K == 1).  Selection: K passes, each taking the
  * not-yet-taken expert with the strictly largest c, scanning ids upward from
  * a start value of -1e30 (so equal scores go to the lower id). */
-int orc_route(const float *x, int T, int64_t H, const float *Wr, const float *bias, int E, int K,
-              float routed_scale, int norm_topk, int32_t *ids, float *wts, float *logits_out,
-              float *sig_out, double *gap_k, double *gap_in)
+/* O4b: group-limited selection ([EDGE0] §七, the sigmoid-group family, rule
+ * ②: rank the groups by the sum of their two best scores, keep G groups, mask
+ * the rest, then take the top K among the kept groups; rule ① makes the
+ * scores the biased c = σ + b).  The E experts form n_group groups of
+ * E/n_group consecutive ids.  A group's score is the fp32 sum of its two
+ * largest c.  topk_group passes each keep the not-yet-kept group with the
+ * strictly largest score (scanning groups upward from -1e30, so equal scores
+ * keep the lower group); the experts of the other groups are excluded, and
+ * the K experts are taken from the rest exactly as in O4.  n_group = 1 is O4.
+ * gap_g [T] (optional) = score of the last kept group - the largest score of
+ * an excluded group (+inf when every group is kept).  gap_k is then taken
+ * among the kept experts (+inf when they are exactly K). */
+int orc_route_groups(const float *x, int T, int64_t H, const float *Wr, const float *bias, int E,
+                     int K, int n_group, int topk_group, float routed_scale, int norm_topk,
+                     int32_t *ids, float *wts, float *logits_out, float *sig_out, double *gap_k,
+                     double *gap_in, double *gap_g)
 {
     if (K < 1 || K > E) return -1;
+    if (n_group < 1 || E % n_group != 0 || topk_group < 1 || topk_group > n_group) return -1;
+    const int gsz = E / n_group;
+    if (n_group > 1 && gsz < 2) return -1;
+    const int n_kept = topk_group * gsz;  /* experts left after the group step */
+    if (K > n_kept) return -1;
     float *sig = (float *)malloc(sizeof(float) * (size_t)E);
     float *c = (float *)malloc(sizeof(float) * (size_t)E);
     char *taken = (char *)malloc((size_t)E);
     int32_t *rank = (int32_t *)malloc(sizeof(int32_t) * (size_t)(K + 1));
-    if (!sig || !c || !taken || !rank) {
+    float *gs = (float *)malloc(sizeof(float) * (size_t)n_group);
+    char *gkept = (char *)malloc((size_t)n_group);
+    if (!sig || !c || !taken || !rank || !gs || !gkept) {
         free(sig);
         free(c);
         free(taken);
         free(rank);
+        free(gs);
+        free(gkept);
         return -2;
     }
     for (int t = 0; t < T; ++t) {
@@ -373,7 +395,53 @@ int orc_route(const float *x, int T, int64_t H, const float *Wr, const float *bi
             if (sig_out) sig_out[(int64_t)t * E + e] = sig[e];
         }
         memset(taken, 0, (size_t)E);
-        int npass = K < E ? K + 1 : K;
+        if (n_group > 1) {
+            /* group scores: the sum of each group's two largest c */
+            for (int g = 0; g < n_group; ++g) {
+                float a = -INFINITY, b2 = -INFINITY;
+                for (int e = g * gsz; e < (g + 1) * gsz; ++e) {
+                    if (c[e] > a) {
+                        b2 = a;
+                        a = c[e];
+                    } else if (c[e] > b2) {
+                        b2 = c[e];
+                    }
+                }
+                gs[g] = a + b2;
+            }
+            memset(gkept, 0, (size_t)n_group);
+            float last = 0.f;
+            for (int kg = 0; kg < topk_group; ++kg) {
+                int best = -1;
+                float bv = -1e30f;
+                for (int g = 0; g < n_group; ++g)
+                    if (!gkept[g] && gs[g] > bv) {
+                        bv = gs[g];
+                        best = g;
+                    }
+                if (best < 0) { /* non-finite scores: not a valid input */
+                    free(sig);
+                    free(c);
+                    free(taken);
+                    free(rank);
+                    free(gs);
+                    free(gkept);
+                    return -3;
+                }
+                gkept[best] = 1;
+                last = bv;
+            }
+            double next = -INFINITY;
+            for (int g = 0; g < n_group; ++g)
+                if (!gkept[g] && (double)gs[g] > next) next = (double)gs[g];
+            if (gap_g) gap_g[t] = topk_group < n_group ? (double)last - next : INFINITY;
+            /* the excluded groups' experts are never selectable */
+            for (int e = 0; e < E; ++e)
+                if (!gkept[e / gsz]) taken[e] = 1;
+        } else if (gap_g) {
+            gap_g[t] = INFINITY;
+        }
+        int npass = K < n_kept ? K + 1 : K;
         for (int kk = 0; kk < npass; ++kk) {
             int best = -1;
             float bv = -1e30f;
@@ -387,6 +455,8 @@ int orc_route(const float *x, int T, int64_t H, const float *Wr, const float *bi
                 free(c);
                 free(taken);
                 free(rank);
+                free(gs);
+                free(gkept);
                 return -3;
             }
             rank[kk] = best;
@@ -400,7 +470,7 @@ int orc_route(const float *x, int T, int64_t H, const float *Wr, const float *bi
             ids[(int64_t)t * K + kk] = rank[kk];
             wts[(int64_t)t * K + kk] = (float)(w * (double)routed_scale);
         }
-        if (gap_k) gap_k[t] = K < E ? (double)c[rank[K - 1]] - (double)c[rank[K]] : INFINITY;
+        if (gap_k) gap_k[t] = K < n_kept ? (double)c[rank[K - 1]] - (double)c[rank[K]] : INFINITY;
         if (gap_in) {
             double m = INFINITY;
             for (int kk = 0; kk + 1 < K; ++kk) {
@@ -414,7 +484,18 @@ int orc_route(const float *x, int T, int64_t H, const float *Wr, const float *bi
     free(c);
     free(taken);
     free(rank);
+    free(gs);
+    free(gkept);
     return 0;
+}
+
+/* O4 (one group: every expert selectable). */
+int orc_route(const float *x, int T, int64_t H, const float *Wr, const float *bias, int E, int K,
+              float routed_scale, int norm_topk, int32_t *ids, float *wts, float *logits_out,
+              float *sig_out, double *gap_k, double *gap_in)
+{
+    return orc_route_groups(x, T, H, Wr, bias, E, K, 1, 1, routed_scale, norm_topk, ids, wts,
+                            logits_out, sig_out, gap_k, gap_in, NULL);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -475,13 +556,14 @@ void orc_combine(int T, int K, int64_t H, int n_shared, const float *y_routed, c
 /* Returns 0, or -5 if a selected expert is not resident.                    */
 /* ------------------------------------------------------------------------ */
 
-int orc_moe_layer(const float *x, int T, int64_t H, int64_t I, int E, int K, int fmt,
-                  const float *Wr, const float *bias, float routed_scale, int norm_topk,
-                  const uint8_t *const *blobs, int n_shared, const uint8_t *const *shared_blobs,
-                  float *out, int32_t *ids, float *wts)
+int orc_moe_layer_groups(const float *x, int T, int64_t H, int64_t I, int E, int K, int fmt,
+                         const float *Wr, const float *bias, int n_group, int topk_group,
+                         float routed_scale, int norm_topk, const uint8_t *const *blobs,
+                         int n_shared, const uint8_t *const *shared_blobs, float *out,
+                         int32_t *ids, float *wts)
 {
-    int rc = orc_route(x, T, H, Wr, bias, E, K, routed_scale, norm_topk, ids, wts, NULL, NULL,
-                       NULL, NULL);
+    int rc = orc_route_groups(x, T, H, Wr, bias, E, K, n_group, topk_group, routed_scale,
+                              norm_topk, ids, wts, NULL, NULL, NULL, NULL, NULL);
     if (rc) return rc;
     float *yr = (float *)malloc(sizeof(float) * (size_t)((int64_t)T * K * H));
     float *ys = (float *)malloc(sizeof(float) * (size_t)((int64_t)(n_shared > 0 ? n_shared : 1) * T * H));
@@ -504,6 +586,15 @@ int orc_moe_layer(const float *x, int T, int64_t H, int64_t I, int E, int K, int
     free(yr);
     free(ys);
     return rc;
+}
+
+int orc_moe_layer(const float *x, int T, int64_t H, int64_t I, int E, int K, int fmt,
+                  const float *Wr, const float *bias, float routed_scale, int norm_topk,
+                  const uint8_t *const *blobs, int n_shared, const uint8_t *const *shared_blobs,
+                  float *out, int32_t *ids, float *wts)
+{
+    return orc_moe_layer_groups(x, T, H, I, E, K, fmt, Wr, bias, 1, 1, routed_scale, norm_topk,
+                                blobs, n_shared, shared_blobs, out, ids, wts);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -276,6 +276,108 @@ def test_gap_flags():
 
 
 # ---------------------------------------------------------------------------
+# O4b: group-limited selection ([EDGE0] §七 sigmoid-group, rules ① and ②)
+# ---------------------------------------------------------------------------
+
+def _route_groups_by_bias(bias, K, n_group, topk_group):
+    E = len(bias)
+    x = np.zeros((1, 8), dtype=np.float32)
+    W = np.zeros((E, 8), dtype=np.float32)
+    return oracle.route_groups(x, W, np.asarray(bias, dtype=np.float32), K, n_group, topk_group)
+
+
+def _groups_brute_force(c, K, n_group, topk_group):
+    """The definition by sorting: group score = fp32 sum of the group's two
+    largest scores; keep the topk_group best groups (ties: lower group);
+    top-K of the kept experts (ties: lower id)."""
+    E = len(c)
+    gsz = E // n_group
+    score = []
+    for g in range(n_group):
+        top = sorted((np.float32(v) for v in c[g * gsz:(g + 1) * gsz]), reverse=True)
+        score.append(np.float32(top[0]) + np.float32(top[1]) if gsz >= 2 else np.float32(top[0]))
+    kept = sorted(range(n_group), key=lambda g: (-float(score[g]), g))[:topk_group]
+    alive = [e for e in range(E) if e // gsz in kept]
+    return sorted(alive, key=lambda e: (-float(c[e]), e))[:K], score, kept
+
+
+def test_groups_equal_brute_force_sort_with_ties():
+    rng = np.random.default_rng(21)
+    for trial in range(400):
+        n_group = int(rng.integers(1, 7))
+        gsz = int(rng.integers(2, 5))
+        E = n_group * gsz
+        topk_group = int(rng.integers(1, n_group + 1))
+        K = int(rng.integers(1, topk_group * gsz + 1))
+        bias = rng.integers(-3, 4, size=E).astype(np.float32) / 4   # many ties
+        ids, wts, logits, sig, gk, gi, gg = _route_groups_by_bias(bias, K, n_group, topk_group)
+        c = (np.float32(0.5) + bias).astype(np.float32)
+        want, _, _ = _groups_brute_force(c, K, n_group, topk_group)
+        assert list(ids[0]) == want, (n_group, gsz, topk_group, K, bias)
+        assert np.allclose(wts[0], 2.5 / K, rtol=0, atol=1e-6)
+
+
+def test_groups_exclude_the_best_single_expert():
+    # expert 0 has the best score, but its group's second is the worst: group
+    # 0 scores 0.9 + (-0.9) and loses to groups 1 and 2
+    bias = np.array([0.9, -0.9, 0.5, 0.4, 0.3, 0.3, 0.0, 0.0], dtype=np.float32) - 0.5
+    ids, *_ = _route_groups_by_bias(bias, 2, 4, 2)
+    assert list(ids[0]) == [2, 3]
+    ids1, *_ = _route_by_bias(bias, 2)      # without groups expert 0 wins
+    assert list(ids1[0]) == [0, 2]
+
+
+def test_group_ties_keep_the_lower_group():
+    # all four groups score 1.0: groups 0 and 1 are kept
+    bias = np.array([0.1, -0.1, 0.2, -0.2, 0.0, 0.0, 0.3, -0.3], dtype=np.float32)
+    ids, wts, lg, sg, gk, gi, gg = _route_groups_by_bias(bias, 4, 4, 2)
+    assert sorted(ids[0].tolist()) == [0, 1, 2, 3]
+    assert list(ids[0]) == [2, 0, 1, 3]
+    assert gg[0] == 0.0
+
+
+def test_all_groups_kept_is_plain_topk():
+    cfg = synth.CONFIGS["tiny"]
+    W = synth.router_weight(cfg, 0)
+    b = synth.router_bias(cfg, 0)
+    x = synth.tokens(cfg, T=12)
+    ids, wts, lg, sg, gk, gi = oracle.route(x, W, b, 4)
+    for ng in (2, 4, 8):
+        ids2, wts2, lg2, sg2, gk2, gi2, gg2 = oracle.route_groups(x, W, b, 4, ng, ng)
+        assert np.array_equal(ids2, ids) and np.array_equal(wts2, wts)
+        assert np.all(np.isinf(gg2))
+
+
+def test_groups_on_router_scores():
+    """Real router scores: the selection is the sorting definition applied to
+    c = sigma + bias, the weights renormalise the chosen sigmas, and gap_g is
+    the kept/excluded group-score gap."""
+    cfg = synth.CONFIGS["tiny"]
+    W = synth.router_weight(cfg, 0)
+    b = synth.router_bias(cfg, 0)
+    x = synth.tokens(cfg, T=16, stream=3)
+    ng, kg, K = 8, 3, 6
+    ids, wts, lg, sg, gk, gi, gg = oracle.route_groups(x, W, b, K, ng, kg)
+    for t in range(16):
+        c = (sg[t] + b).astype(np.float32)
+        want, score, kept = _groups_brute_force(c, K, ng, kg)
+        assert list(ids[t]) == want
+        s = sg[t, ids[t]].astype(np.float64)
+        assert np.allclose(wts[t], 2.5 * s / s.sum(), rtol=1e-7)
+        out = [g for g in range(ng) if g not in kept]
+        assert gg[t] == pytest.approx(float(score[kept[-1]]) - max(float(score[g]) for g in out))
+
+
+def test_groups_reject_bad_shapes():
+    x = np.zeros((1, 8), dtype=np.float32)
+    W = np.zeros((8, 8), dtype=np.float32)
+    b = np.zeros(8, dtype=np.float32)
+    for ng, kg, K in ((3, 1, 1), (8, 1, 1), (4, 5, 1), (4, 1, 3)):
+        with pytest.raises(ValueError):
+            oracle.route_groups(x, W, b, K, ng, kg)
+
+
+# ---------------------------------------------------------------------------
 # O5: bucketing
 # ---------------------------------------------------------------------------
 
