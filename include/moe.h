@@ -18,11 +18,13 @@
  *           6144->256 top-8, 6b SwiGLU experts 6144->2048->6144, 6c the
  *           always-active shared expert, 6d output = routed sum + shared);
  *   [COLI]  "初始化与权重加载" (colibrì analysis) §1.1-1.2 (n_group,
- *           topk_group, norm_topk, routed_scale; n_group must be 1), §2.2
- *           (ESlot: an expert slot addressed by expert id);
+ *           topk_group, norm_topk, routed_scale; GLM-5.2 has n_group = 1),
+ *           §2.2 (ESlot: an expert slot addressed by expert id);
  *   [EDGE0] Edge0 write-up (magicnetworld.com) §三 (affine int4, group size
- *           64), §七 (sigmoid-group weights with the 1e-20 term), §十四
- *           (routing indices mapped through a slot table on the device).
+ *           64), §七 (sigmoid-group routing: biased selection scores, group
+ *           ranking by the sum of the two best scores, G groups kept, weights
+ *           with the 1e-20 term), §十四 (routing indices mapped through a
+ *           slot table on the device).
  *
  * Conventions for every entry point:
  *   - return MOE_OK (0) or a negative MOE_E_* code; nothing calls exit();
@@ -72,8 +74,13 @@ typedef struct moe_config {
     int n_shared;       /* 0 or 1 always-active shared experts (weight 1) */
     int n_layers;       /* layers whose router/shared/slot table are held */
     int wfmt;           /* MOE_W_INT4_ROW or MOE_W_INT4_AFFINE_G64 */
-    int n_group;        /* expert groups of the router: must be 1 ([COLI] §1.2) */
-    int topk_group;     /* groups kept: must be 1 */
+    int n_group;        /* expert groups of the router, 1..64 dividing E, >= 2
+                           experts each; 1 = plain top-K (GLM-5.2, [COLI] §1.2).
+                           More: a group's score is the fp32 sum of its two
+                           largest sigma + bias, the topk_group best groups are
+                           kept (ties: lower group), top-K among their experts
+                           ([EDGE0] §七) */
+    int topk_group;     /* groups kept, 1..n_group, with K <= topk_group * E / n_group */
     float routed_scale; /* routed scaling factor (GLM-5.2: 2.5) */
     int norm_topk;      /* 1: renormalise chosen sigmas before scaling ([EDGE0] §七) */
     int n_slots;        /* expert slots in the HBM pool */
@@ -85,8 +92,9 @@ typedef struct moe_config {
  * (n_slots * moe_expert_bytes), per-layer router weights, bias, shared
  * experts and slot table (all entries -1 = not resident), and a workspace
  * sized for max_tokens.  stream: a hipStream_t (NULL = default stream).
- * Errors: MOE_E_ARG (null/invalid field), MOE_E_UNSUPPORTED (n_group or
- * topk_group != 1, E > 256, K > 8, H or I not a multiple of 64),
+ * Errors: MOE_E_ARG (null/invalid field, topk_group outside 1..n_group),
+ * MOE_E_UNSUPPORTED (n_group > 64 or not dividing E into groups of >= 2,
+ * K > topk_group * E / n_group, E > 256, K > 8, H or I not a multiple of 256),
  * MOE_E_NOMEM, MOE_E_HIP (no device or not gfx950). */
 int moe_layer_create(const moe_config *cfg, void *stream, moe_ctx **out);
 

@@ -167,6 +167,46 @@ __global__ void __launch_bounds__(256) k_topk(Fwd f)
             c[m] = sg[m] + f.bias[e];
         }
     }
+    // group-limited selection: a group's score is the fp32 sum of its two
+    // largest c; the topk_group best groups are kept (strictly greater, equal
+    // scores keep the lower group); the other groups' experts are excluded
+    if (f.n_group > 1) {
+        __shared__ float s_c[4][256];
+        const int wv = threadIdx.x >> 6, NG = f.n_group, GS = E / NG;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) s_c[wv][lane + 64 * m] = c[m];
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wavefront's writes are visible to it
+        __builtin_amdgcn_wave_barrier();
+        unsigned long long gkey = 0ull;  // (score, lower group first), 0 for lanes >= NG
+        if (lane < NG) {
+            float a = -INFINITY, b2 = -INFINITY;
+            for (int e = lane * GS; e < (lane + 1) * GS; ++e) {
+                const float v = s_c[wv][e];
+                if (v > a) {
+                    b2 = a;
+                    a = v;
+                } else if (v > b2) {
+                    b2 = v;
+                }
+            }
+            gkey = ((unsigned long long)ordf(a + b2) << 32) | (uint32_t)(0xFFFFu - lane);
+        }
+        unsigned long long kept = 0ull;
+        for (int kg = 0; kg < f.topk_group; ++kg) {
+            unsigned long long best = (kept >> lane) & 1ull ? 0ull : gkey;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                const unsigned long long other = __shfl_xor(best, o);
+                best = other > best ? other : best;
+            }
+            kept |= 1ull << (0xFFFF - (int)(best & 0xFFFFu));
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int e = lane + 64 * m;
+            if (e < E && !((kept >> (e / GS)) & 1ull)) c[m] = -INFINITY;
+        }
+    }
     uint32_t taken = 0;
     float ssum = 0.f, mysig = 0.f;
     int myid = 0;

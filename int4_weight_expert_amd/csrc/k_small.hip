@@ -29,6 +29,13 @@ __device__ __forceinline__ uint32_t ord_float(float c)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The score c of a selection key (ord_float(c) << 32 | id bits), exactly.
+__device__ __forceinline__ float key_score(unsigned long long key)
+{
+    const uint32_t o = (uint32_t)(key >> 32);
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
 // ---------------------------------------------------------------------------
 // Router tail (one workgroup of 256 threads, one per expert): token
 // statistics, sigmoid, bias, top-K per token, weights, bucketing into expert
@@ -188,6 +195,51 @@ __device__ void router_tail(const Fwd& f)
             s_sig[t][tid] = sig;
         }
     __syncthreads();
+
+    // 2b. group-limited selection: a group's score is the fp32 sum of its two
+    //     largest c; the topk_group best groups are kept (strictly greater,
+    //     equal scores keep the lower group); the other groups' keys drop to
+    //     0, below every real key
+    if (f.n_group > 1) {
+        __shared__ float s_gs[NT][64];
+        __shared__ unsigned long long s_kept[NT];
+        const int NG = f.n_group, GS = E / NG;
+        for (int i = tid; i < T * NG; i += RT_THREADS) {
+            const int t = i / NG, g = i - t * NG;
+            float a = -INFINITY, b2 = -INFINITY;
+            for (int e = g * GS; e < (g + 1) * GS; ++e) {
+                const float c = key_score(s_key[t][e]);
+                if (c > a) {
+                    b2 = a;
+                    a = c;
+                } else if (c > b2) {
+                    b2 = c;
+                }
+            }
+            s_gs[t][g] = a + b2;
+        }
+        __syncthreads();
+        if (tid < T) {
+            unsigned long long kept = 0ull;
+            for (int kg = 0; kg < f.topk_group; ++kg) {
+                int best = 0;
+                float bv = -1e30f;
+                for (int g = 0; g < NG; ++g)
+                    if (!((kept >> g) & 1ull) && s_gs[tid][g] > bv) {
+                        bv = s_gs[tid][g];
+                        best = g;
+                    }
+                kept |= 1ull << best;
+            }
+            s_kept[tid] = kept;
+        }
+        __syncthreads();
+        if (tid < E)
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                if (t < T && !((s_kept[t] >> (tid / GS)) & 1ull)) s_key[t][tid] = 0ull;
+        __syncthreads();
+    }
 
     // 3a. ranks within each block of 64 experts; rank < K -> candidate
     for (int pq = w; pq < T * 4; pq += RT_THREADS / 64) {

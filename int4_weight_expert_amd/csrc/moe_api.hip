@@ -208,6 +208,8 @@ Fwd make_fwd(moe_ctx* c, const float* x, float* out, int T, int layer, int resid
     f.tiles = c->tiles;
     f.n_tiles = c->n_tiles;
     f.counters = c->counters;
+    f.n_group = g.n_group;
+    f.topk_group = g.topk_group;
     f.status = c->status;
     f.n_layers = g.n_layers;
     f.lds_max = c->lds_max;
@@ -351,7 +353,11 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
         g.n_slots < 0 || g.max_tokens <= 0 || g.n_shared < 0)
         return MOE_E_ARG;
     if (g.wfmt != MOE_W_INT4_ROW && g.wfmt != MOE_W_INT4_AFFINE_G64) return MOE_E_ARG;
-    if (g.n_group != 1 || g.topk_group != 1) return MOE_E_UNSUPPORTED;
+    if (g.n_group < 1 || g.topk_group < 1 || g.topk_group > g.n_group) return MOE_E_ARG;
+    if (g.n_group > 1 &&
+        (g.n_group > 64 || g.n_experts % g.n_group || g.n_experts / g.n_group < 2 ||
+         g.top_k > g.topk_group * (g.n_experts / g.n_group)))
+        return MOE_E_UNSUPPORTED;
     if (g.n_experts > 256 || g.top_k > 8 || g.top_k > g.n_experts || g.n_shared > 1)
         return MOE_E_UNSUPPORTED;
     if (g.hidden % 256 || g.inter % 256 || g.hidden > 16384) return MOE_E_UNSUPPORTED;

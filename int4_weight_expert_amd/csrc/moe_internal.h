@@ -50,6 +50,7 @@ struct Fwd {
     int residual;         // 1: out = x + moe(rmsnorm(x)), x may equal out
     float routed_scale, eps;
     int norm_topk;
+    int n_group, topk_group;  // group-limited selection (n_group = 1: none)
     int layer;
     const float* wr;      // router, interleaved [Epad/64][H/4][64] float4
     const float* bias;    // [E]

@@ -34,6 +34,8 @@ class LayerConfig:
     sigma_x: float = 1.0
     routed_scale: float = 2.5
     norm_topk: int = 1
+    n_group: int = 1          # expert groups of the router (group-limited selection)
+    topk_group: int = 1       # groups kept per token
     eps: float = 1e-6
 
     def with_(self, **kw) -> "LayerConfig":
@@ -60,6 +62,13 @@ CONFIGS = {
                            n_layers=1, seed=400),
     "mid_affine": LayerConfig("mid_affine", H=2048, I=512, E=32, K=8, n_shared=1,
                               fmt=W_INT4_AFFINE_G64, T=1, n_layers=1, seed=401),
+    # group-limited routing (8 groups of 32 experts, 4 kept, the Edge0
+    # write-up's 8B setting) on small layers, row and affine formats
+    "grouped_row": LayerConfig("grouped_row", H=2048, I=256, E=256, K=8, n_shared=1,
+                               fmt=W_INT4_ROW, T=1, n_layers=1, seed=500, n_group=8, topk_group=4),
+    "grouped_affine": LayerConfig("grouped_affine", H=2048, I=512, E=256, K=8, n_shared=0,
+                                  fmt=W_INT4_AFFINE_G64, T=1, n_layers=1, seed=501, n_group=8,
+                                  topk_group=4),
     # GLM-5.2 shape prefill, 2048 tokens, one layer
     "glm_prefill": LayerConfig("glm_prefill", H=6144, I=2048, E=256, K=8, n_shared=1,
                                fmt=W_INT4_ROW, T=2048, n_layers=1, seed=300, zipf_c=0.2),

@@ -46,8 +46,11 @@ def test_null_arguments_are_rejected_without_device_work():
 
 def test_create_rejects_unsupported_config_before_touching_a_device():
     from int4_weight_expert_amd import moe as M
-    bad = [dict(n_group=8, topk_group=4), dict(E=300), dict(K=9), dict(H=6000),
-           dict(wfmt=3), dict(max_tokens=0)]
+    # invalid router groupings: groups not dividing E, one-expert groups,
+    # more groups kept than exist, K above the kept experts
+    bad = [dict(n_group=3, topk_group=1), dict(n_group=32, topk_group=4),
+           dict(n_group=8, topk_group=9), dict(n_group=16, topk_group=1),
+           dict(E=300), dict(K=9), dict(H=6000), dict(wfmt=3), dict(max_tokens=0)]
     for kw in bad:
         base = dict(H=512, I=256, E=32, K=4, n_shared=1, n_layers=1, wfmt=1, n_slots=32,
                     max_tokens=4)

@@ -158,6 +158,7 @@ def test_argument_errors():
         assert rc == 0
     finally:
         ml.close()
-    cfg = M.make_config(512, 256, 32, 4, 1, 1, 1, 4, 4, n_group=8, topk_group=4)
+    # K = 4 above the 2 experts of the one kept group
+    cfg = M.make_config(512, 256, 32, 4, 1, 1, 1, 4, 4, n_group=16, topk_group=1)
     rc, h = M.moe_layer_create_rc(cfg)
     assert rc == M.MOE_E_UNSUPPORTED and not h
