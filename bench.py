@@ -183,6 +183,35 @@ def bench_decode(torch, args, result):
     torch.cuda.empty_cache()
 
 
+def bench_rotated(torch, name, steps, result):
+    """One-token forwards rotated over the resident layers (as the decode
+    bench), graph-replayed: per-layer time and percentiles."""
+    import synth
+    from int4_weight_expert_amd import workload
+    cfg = synth.CONFIGS[name]
+    log(f"[bench] building {name}: {cfg.n_layers} layers x {cfg.E} experts")
+    ml = workload.build_layer(cfg, max_tokens=8)
+    L = cfg.n_layers
+    xs = [workload.tokens_device(cfg, T=1, stream=l) for l in range(L)]
+    outs = [torch.empty_like(x) for x in xs]
+    fns = [(lambda l=l: ml.forward(xs[l], l, outs[l])) for l in range(L)]
+    for fn in fns:
+        fn()
+    g, t, _ = time_graph(torch, ml, fns, steps, 20)
+    pct = replay_percentiles(torch, g, L)
+    layer_bytes = glm_bytes(cfg, cfg.K + cfg.n_shared, 1)
+    result["extra"][name] = {
+        "T": 1, "layers": L, "n_group": cfg.n_group, "topk_group": cfg.topk_group,
+        "us_per_layer": t * 1e6, "graph_replay_percentiles": pct,
+        "layer_algorithmic_bytes": layer_bytes, "layer_gbps": layer_bytes / t / 1e9,
+        "layer_frac_hbm_peak": layer_bytes / t / 1e9 / HBM_PEAK_GBS,
+    }
+    log(f"[bench] {name}: {t * 1e6:.1f} us/layer, {layer_bytes / t / 1e9:.0f} GB/s")
+    ml.close()
+    del ml, xs, outs
+    torch.cuda.empty_cache()
+
+
 def bench_chain(torch, name, steps, result):
     """Chained residual layers (x <- x + moe(rmsnorm(x))): per-layer time."""
     import numpy as np
@@ -364,7 +393,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="only the decode workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=16)
-    ap.add_argument("--only", choices=["decode", "verify", "edge0", "edge0_k8", "prefill"],
+    ap.add_argument("--only", choices=["decode", "verify", "edge0", "edge0_k8", "prefill", "grouped"],
                     help="run one workload only (for profiling); the JSON line then "
                          "carries that workload in extra")
     ap.add_argument("--copy-probe", action="store_true",
@@ -394,7 +423,8 @@ def main():
         {"verify": lambda: bench_chain(torch, "glm_verify", 64, result),
          "edge0": lambda: bench_chain(torch, "edge0_decode", 200, result),
          "edge0_k8": lambda: bench_chain(torch, "edge0_decode_k8", 200, result),
-         "prefill": lambda: bench_prefill(torch, 20, result)}[args.only]()
+         "prefill": lambda: bench_prefill(torch, 20, result),
+         "grouped": lambda: bench_rotated(torch, "glm_decode_grouped", 200, result)}[args.only]()
         print(json.dumps(result), flush=True)
         return
     bench_decode(torch, args, result)
@@ -404,6 +434,7 @@ def main():
         bench_chain(torch, "glm_verify", 64, result)
         bench_chain(torch, "edge0_decode", 200, result)
         bench_chain(torch, "edge0_decode_k8", 200, result)
+        bench_rotated(torch, "glm_decode_grouped", 200, result)
         bench_prefill(torch, 20, result)
     if not args.no_cpu:
         log("[bench] cpu baseline (oracle)")

@@ -168,39 +168,40 @@ __global__ void __launch_bounds__(256) k_topk(Fwd f)
         }
     }
     // group-limited selection: a group's score is the fp32 sum of its two
-    // largest c; the topk_group best groups are kept (strictly greater, equal
-    // scores keep the lower group); the other groups' experts are excluded
+    // largest c; a group is kept when fewer than topk_group groups rank above
+    // it (greater score, or equal score and lower index: the strictly-greater
+    // scan's order); the other groups' experts are excluded
     if (f.n_group > 1) {
         __shared__ float s_c[4][256];
+        __shared__ float s_gs[4][64];
         const int wv = threadIdx.x >> 6, NG = f.n_group, GS = E / NG;
 #pragma unroll
         for (int m = 0; m < 4; ++m) s_c[wv][lane + 64 * m] = c[m];
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wavefront's writes are visible to it
         __builtin_amdgcn_wave_barrier();
-        unsigned long long gkey = 0ull;  // (score, lower group first), 0 for lanes >= NG
         if (lane < NG) {
             float a = -INFINITY, b2 = -INFINITY;
+#pragma unroll 8
             for (int e = lane * GS; e < (lane + 1) * GS; ++e) {
                 const float v = s_c[wv][e];
-                if (v > a) {
-                    b2 = a;
-                    a = v;
-                } else if (v > b2) {
-                    b2 = v;
-                }
+                b2 = fmaxf(b2, fminf(a, v));
+                a = fmaxf(a, v);
             }
-            gkey = ((unsigned long long)ordf(a + b2) << 32) | (uint32_t)(0xFFFFu - lane);
+            s_gs[wv][lane] = a + b2;
         }
-        unsigned long long kept = 0ull;
-        for (int kg = 0; kg < f.topk_group; ++kg) {
-            unsigned long long best = (kept >> lane) & 1ull ? 0ull : gkey;
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) {
-                const unsigned long long other = __shfl_xor(best, o);
-                best = other > best ? other : best;
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_wave_barrier();
+        uint64_t kept = 0ull;
+        if (lane < NG) {
+            const float mine = s_gs[wv][lane];
+            int rank = 0;
+            for (int h = 0; h < NG; ++h) {
+                const float o = s_gs[wv][h];
+                rank += (o > mine) || (o == mine && h < lane);
             }
-            kept |= 1ull << (0xFFFF - (int)(best & 0xFFFFu));
+            kept = rank < f.topk_group;
         }
+        kept = __ballot(kept != 0ull);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int e = lane + 64 * m;

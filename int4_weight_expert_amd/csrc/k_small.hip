@@ -197,47 +197,40 @@ __device__ void router_tail(const Fwd& f)
     __syncthreads();
 
     // 2b. group-limited selection: a group's score is the fp32 sum of its two
-    //     largest c; the topk_group best groups are kept (strictly greater,
-    //     equal scores keep the lower group); the other groups' keys drop to
-    //     0, below every real key
+    //     largest c; a group is kept when fewer than topk_group groups rank
+    //     above it (greater score, or equal score and lower index: the
+    //     strictly-greater scan's order); the other groups' keys drop to 0,
+    //     below every real key
     if (f.n_group > 1) {
         __shared__ float s_gs[NT][64];
-        __shared__ unsigned long long s_kept[NT];
         const int NG = f.n_group, GS = E / NG;
         for (int i = tid; i < T * NG; i += RT_THREADS) {
             const int t = i / NG, g = i - t * NG;
+            const unsigned long long* kb = &s_key[t][g * GS];
             float a = -INFINITY, b2 = -INFINITY;
-            for (int e = g * GS; e < (g + 1) * GS; ++e) {
-                const float c = key_score(s_key[t][e]);
-                if (c > a) {
-                    b2 = a;
-                    a = c;
-                } else if (c > b2) {
-                    b2 = c;
-                }
+#pragma unroll 8
+            for (int e = 0; e < GS; ++e) {
+                const float c = key_score(kb[e]);
+                b2 = fmaxf(b2, fminf(a, c));
+                a = fmaxf(a, c);
             }
             s_gs[t][g] = a + b2;
         }
         __syncthreads();
-        if (tid < T) {
-            unsigned long long kept = 0ull;
-            for (int kg = 0; kg < f.topk_group; ++kg) {
-                int best = 0;
-                float bv = -1e30f;
-                for (int g = 0; g < NG; ++g)
-                    if (!((kept >> g) & 1ull) && s_gs[tid][g] > bv) {
-                        bv = s_gs[tid][g];
-                        best = g;
-                    }
-                kept |= 1ull << best;
-            }
-            s_kept[tid] = kept;
-        }
-        __syncthreads();
-        if (tid < E)
+        if (tid < E) {
+            const int g = tid / GS;
 #pragma unroll
             for (int t = 0; t < NT; ++t)
-                if (t < T && !((s_kept[t] >> (tid / GS)) & 1ull)) s_key[t][tid] = 0ull;
+                if (t < T) {
+                    const float mine = s_gs[t][g];
+                    int rank = 0;
+                    for (int h = 0; h < NG; ++h) {
+                        const float o = s_gs[t][h];
+                        rank += (o > mine) || (o == mine && h < g);
+                    }
+                    if (rank >= f.topk_group) s_key[t][tid] = 0ull;
+                }
+        }
         __syncthreads();
     }
 

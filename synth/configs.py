@@ -74,3 +74,6 @@ CONFIGS = {
                                fmt=W_INT4_ROW, T=2048, n_layers=1, seed=300, zipf_c=0.2),
 }
 CONFIGS["edge0_decode_k8"] = CONFIGS["edge0_decode"].with_(name="edge0_decode_k8", K=8)
+# GLM-5.2 shape decode with group-limited routing (8 groups, 4 kept), 4 layers
+CONFIGS["glm_decode_grouped"] = CONFIGS["glm_decode"].with_(name="glm_decode_grouped", n_group=8,
+                                                             topk_group=4, n_layers=4, seed=600)
