@@ -54,9 +54,9 @@ def lib() -> ctypes.CDLL:
         L.orc_expert.restype = i32
         L.orc_route.argtypes = [vp, i32, i64, vp, vp, i32, i32, f32, i32, vp, vp, vp, vp, vp, vp]
         L.orc_route.restype = i32
-        L.orc_route_groups.argtypes = [vp, i32, i64, vp, vp, i32, i32, i32, i32, f32, i32, vp, vp,
-                                       vp, vp, vp, vp, vp]
-        L.orc_route_groups.restype = i32
+        L.orc_route_full.argtypes = [vp, i32, i64, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp,
+                                     vp, vp, vp, vp, vp, vp]
+        L.orc_route_full.restype = i32
         L.orc_bucket.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, vp]
         L.orc_bucket.restype = i32
         L.orc_combine.argtypes = [i32, i32, i64, i32, vp, vp, vp, vp]
@@ -64,9 +64,9 @@ def lib() -> ctypes.CDLL:
         L.orc_moe_layer.argtypes = [vp, i32, i64, i64, i32, i32, i32, vp, vp, f32, i32, vp, i32,
                                     vp, vp, vp, vp]
         L.orc_moe_layer.restype = i32
-        L.orc_moe_layer_groups.argtypes = [vp, i32, i64, i64, i32, i32, i32, vp, vp, i32, i32, f32,
-                                           i32, vp, i32, vp, vp, vp, vp]
-        L.orc_moe_layer_groups.restype = i32
+        L.orc_moe_layer_full.argtypes = [vp, i32, i64, i64, i32, i32, i32, vp, vp, i32, i32, i32,
+                                         f32, i32, vp, i32, vp, vp, vp, vp]
+        L.orc_moe_layer_full.restype = i32
         L.orc_rmsnorm.argtypes = [vp, i32, i64, f32, vp]
         L.orc_rmsnorm.restype = None
         L.orc_residual_layer.argtypes = [vp, i32, i64, i64, i32, i32, i32, vp, vp, f32, i32, vp,
@@ -171,18 +171,23 @@ def expert(fmt: int, H: int, I: int, blob: np.ndarray, x: np.ndarray):
     return y, h
 
 
+SCORE_SIGMOID, SCORE_SOFTMAX = 0, 1
+
+
 def route(x, Wr, bias, K: int, routed_scale: float = 2.5, norm_topk: int = 1, n_group: int = 1,
-          topk_group: int = 1):
-    """Returns ids [T,K], wts [T,K], logits [T,E], sig [T,E], gap_k [T], gap_in [T].
-    With groups, gap_k is the smaller of the K-th/(K+1)-th score gap and the
-    kept/excluded group-score gap (either closes on a near tie)."""
+          topk_group: int = 1, scoring: int = SCORE_SIGMOID):
+    """Returns ids [T,K], wts [T,K], logits [T,E], scores [T,E] (sigmoid, or
+    softmax probabilities), gap_k [T], gap_in [T].  With groups, gap_k is the
+    smaller of the K-th/(K+1)-th score gap and the kept/excluded group-score
+    gap (either closes on a near tie); with softmax scoring the gaps are
+    logit differences."""
     ids, wts, logits, sig, gk, gi, gg = route_groups(x, Wr, bias, K, n_group, topk_group,
-                                                      routed_scale, norm_topk)
+                                                      routed_scale, norm_topk, scoring)
     return ids, wts, logits, sig, np.minimum(gk, gg), gi
 
 
 def route_groups(x, Wr, bias, K: int, n_group: int, topk_group: int, routed_scale: float = 2.5,
-                 norm_topk: int = 1):
+                 norm_topk: int = 1, scoring: int = SCORE_SIGMOID):
     """As route, plus gap_g [T]: the kept/excluded group-score gap."""
     x, Wr, bias = _f32(x), _f32(Wr), _f32(bias)
     T, H = x.shape
@@ -194,11 +199,11 @@ def route_groups(x, Wr, bias, K: int, n_group: int, topk_group: int, routed_scal
     gk = np.empty(T, dtype=np.float64)
     gi = np.empty(T, dtype=np.float64)
     gg = np.empty(T, dtype=np.float64)
-    rc = lib().orc_route_groups(_p(x), T, H, _p(Wr), _p(bias), E, K, n_group, topk_group,
-                                routed_scale, norm_topk, _p(ids), _p(wts), _p(logits), _p(sig),
-                                _p(gk), _p(gi), _p(gg))
+    rc = lib().orc_route_full(_p(x), T, H, _p(Wr), _p(bias), E, K, scoring, n_group, topk_group,
+                              routed_scale, norm_topk, _p(ids), _p(wts), _p(logits), _p(sig),
+                              _p(gk), _p(gi), _p(gg))
     if rc:
-        raise ValueError(f"orc_route_groups failed ({rc})")
+        raise ValueError(f"orc_route_full failed ({rc})")
     return ids, wts, logits, sig, gk, gi, gg
 
 
@@ -234,7 +239,7 @@ def _blob_array(blobs):
 
 
 def moe_layer(x, Wr, bias, K, fmt, I, blobs, shared_blobs, routed_scale=2.5, norm_topk=1,
-              n_group=1, topk_group=1):
+              n_group=1, topk_group=1, scoring=SCORE_SIGMOID):
     """Whole layer; blobs is a list of E blobs (None = not resident)."""
     x, Wr, bias = _f32(x), _f32(Wr), _f32(bias)
     T, H = x.shape
@@ -244,8 +249,8 @@ def moe_layer(x, Wr, bias, K, fmt, I, blobs, shared_blobs, routed_scale=2.5, nor
     wts = np.empty((T, K), dtype=np.float32)
     ba = _blob_array(blobs)
     sa = _blob_array(shared_blobs) if shared_blobs else None
-    rc = lib().orc_moe_layer_groups(_p(x), T, H, I, E, K, fmt, _p(Wr), _p(bias), n_group,
-                                    topk_group, routed_scale, norm_topk,
+    rc = lib().orc_moe_layer_full(_p(x), T, H, I, E, K, fmt, _p(Wr), _p(bias), scoring, n_group,
+                                  topk_group, routed_scale, norm_topk,
                                     ctypes.cast(ba, ctypes.c_void_p), len(shared_blobs or []),
                                     ctypes.cast(sa, ctypes.c_void_p) if sa is not None else None,
                                     _p(out), _p(ids), _p(wts))

@@ -356,12 +356,21 @@ int orc_expert(int fmt, int64_t H, int64_t I, const uint8_t *blob, const float *
  * gap_g [T] (optional) = score of the last kept group - the largest score of
  * an excluded group (+inf when every group is kept).  gap_k is then taken
  * among the kept experts (+inf when they are exactly K). */
-int orc_route_groups(const float *x, int T, int64_t H, const float *Wr, const float *bias, int E,
-                     int K, int n_group, int topk_group, float routed_scale, int norm_topk,
-                     int32_t *ids, float *wts, float *logits_out, float *sig_out, double *gap_k,
-                     double *gap_in, double *gap_g)
+/* O4c: softmax scoring ([EDGE0] §七 softmax-top-k family; [GLM-C] §05 the
+ * olmoe prototype's moe step): g = softmax(l) over all E logits, shifted by
+ * the largest logit, in fp64 and rounded to fp32; the selection scans g (no
+ * bias) as O4 scans c; the weights are g (norm_topk = 0, the prototype's
+ * w = val) or g / (sum of the chosen g) (norm_topk = 1, renormalised to one),
+ * times routed_scale.  Groups apply to sigmoid scoring only.  For softmax,
+ * gap_k and gap_in are logit differences (the order of g is that of l). */
+int orc_route_full(const float *x, int T, int64_t H, const float *Wr, const float *bias, int E,
+                   int K, int scoring, int n_group, int topk_group, float routed_scale,
+                   int norm_topk, int32_t *ids, float *wts, float *logits_out, float *sig_out,
+                   double *gap_k, double *gap_in, double *gap_g)
 {
     if (K < 1 || K > E) return -1;
+    if (scoring != 0 && scoring != 1) return -1;
+    if (scoring == 1 && n_group != 1) return -1;
     if (n_group < 1 || E % n_group != 0 || topk_group < 1 || topk_group > n_group) return -1;
     const int gsz = E / n_group;
     if (n_group > 1 && gsz < 2) return -1;
@@ -373,13 +382,15 @@ int orc_route_groups(const float *x, int T, int64_t H, const float *Wr, const fl
     int32_t *rank = (int32_t *)malloc(sizeof(int32_t) * (size_t)(K + 1));
     float *gs = (float *)malloc(sizeof(float) * (size_t)n_group);
     char *gkept = (char *)malloc((size_t)n_group);
-    if (!sig || !c || !taken || !rank || !gs || !gkept) {
+    float *lg = (float *)malloc(sizeof(float) * (size_t)E);
+    if (!sig || !c || !taken || !rank || !gs || !gkept || !lg) {
         free(sig);
         free(c);
         free(taken);
         free(rank);
         free(gs);
         free(gkept);
+        free(lg);
         return -2;
     }
     for (int t = 0; t < T; ++t) {
@@ -389,11 +400,25 @@ int orc_route_groups(const float *x, int T, int64_t H, const float *Wr, const fl
             const float *wr = Wr + (int64_t)e * H;
             for (int64_t i = 0; i < H; ++i) acc += (double)wr[i] * (double)xt[i];
             float l = (float)acc;
-            sig[e] = (float)(1.0 / (1.0 + exp(-(double)l)));
-            c[e] = sig[e] + bias[e];
+            lg[e] = l;
+            if (scoring == 0) {
+                sig[e] = (float)(1.0 / (1.0 + exp(-(double)l)));
+                c[e] = sig[e] + bias[e];
+            }
             if (logits_out) logits_out[(int64_t)t * E + e] = l;
-            if (sig_out) sig_out[(int64_t)t * E + e] = sig[e];
         }
+        if (scoring == 1) {
+            double m = -INFINITY, z = 0.0;
+            for (int e = 0; e < E; ++e)
+                if ((double)lg[e] > m) m = (double)lg[e];
+            for (int e = 0; e < E; ++e) z += exp((double)lg[e] - m);
+            for (int e = 0; e < E; ++e) {
+                sig[e] = (float)(exp((double)lg[e] - m) / z);
+                c[e] = sig[e];
+            }
+        }
+        if (sig_out)
+            for (int e = 0; e < E; ++e) sig_out[(int64_t)t * E + e] = sig[e];
         memset(taken, 0, (size_t)E);
         if (n_group > 1) {
             /* group scores: the sum of each group's two largest c */
@@ -426,6 +451,7 @@ int orc_route_groups(const float *x, int T, int64_t H, const float *Wr, const fl
                     free(rank);
                     free(gs);
                     free(gkept);
+                    free(lg);
                     return -3;
                 }
                 gkept[best] = 1;
@@ -457,6 +483,7 @@ int orc_route_groups(const float *x, int T, int64_t H, const float *Wr, const fl
                 free(rank);
                 free(gs);
                 free(gkept);
+                free(lg);
                 return -3;
             }
             rank[kk] = best;
@@ -470,11 +497,13 @@ int orc_route_groups(const float *x, int T, int64_t H, const float *Wr, const fl
             ids[(int64_t)t * K + kk] = rank[kk];
             wts[(int64_t)t * K + kk] = (float)(w * (double)routed_scale);
         }
-        if (gap_k) gap_k[t] = K < n_kept ? (double)c[rank[K - 1]] - (double)c[rank[K]] : INFINITY;
+        /* gaps in selection-score units (sigmoid) or logit units (softmax) */
+        const float *gv = scoring == 1 ? lg : c;
+        if (gap_k) gap_k[t] = K < n_kept ? (double)gv[rank[K - 1]] - (double)gv[rank[K]] : INFINITY;
         if (gap_in) {
             double m = INFINITY;
             for (int kk = 0; kk + 1 < K; ++kk) {
-                double gdiff = (double)c[rank[kk]] - (double)c[rank[kk + 1]];
+                double gdiff = (double)gv[rank[kk]] - (double)gv[rank[kk + 1]];
                 if (gdiff < m) m = gdiff;
             }
             gap_in[t] = m;
@@ -486,7 +515,18 @@ int orc_route_groups(const float *x, int T, int64_t H, const float *Wr, const fl
     free(rank);
     free(gs);
     free(gkept);
+    free(lg);
     return 0;
+}
+
+/* O4b with sigmoid scoring. */
+int orc_route_groups(const float *x, int T, int64_t H, const float *Wr, const float *bias, int E,
+                     int K, int n_group, int topk_group, float routed_scale, int norm_topk,
+                     int32_t *ids, float *wts, float *logits_out, float *sig_out, double *gap_k,
+                     double *gap_in, double *gap_g)
+{
+    return orc_route_full(x, T, H, Wr, bias, E, K, 0, n_group, topk_group, routed_scale, norm_topk,
+                          ids, wts, logits_out, sig_out, gap_k, gap_in, gap_g);
 }
 
 /* O4 (one group: every expert selectable). */
@@ -556,14 +596,14 @@ void orc_combine(int T, int K, int64_t H, int n_shared, const float *y_routed, c
 /* Returns 0, or -5 if a selected expert is not resident.                    */
 /* ------------------------------------------------------------------------ */
 
-int orc_moe_layer_groups(const float *x, int T, int64_t H, int64_t I, int E, int K, int fmt,
-                         const float *Wr, const float *bias, int n_group, int topk_group,
-                         float routed_scale, int norm_topk, const uint8_t *const *blobs,
-                         int n_shared, const uint8_t *const *shared_blobs, float *out,
-                         int32_t *ids, float *wts)
+int orc_moe_layer_full(const float *x, int T, int64_t H, int64_t I, int E, int K, int fmt,
+                       const float *Wr, const float *bias, int scoring, int n_group,
+                       int topk_group, float routed_scale, int norm_topk,
+                       const uint8_t *const *blobs, int n_shared,
+                       const uint8_t *const *shared_blobs, float *out, int32_t *ids, float *wts)
 {
-    int rc = orc_route_groups(x, T, H, Wr, bias, E, K, n_group, topk_group, routed_scale,
-                              norm_topk, ids, wts, NULL, NULL, NULL, NULL, NULL);
+    int rc = orc_route_full(x, T, H, Wr, bias, E, K, scoring, n_group, topk_group, routed_scale,
+                            norm_topk, ids, wts, NULL, NULL, NULL, NULL, NULL);
     if (rc) return rc;
     float *yr = (float *)malloc(sizeof(float) * (size_t)((int64_t)T * K * H));
     float *ys = (float *)malloc(sizeof(float) * (size_t)((int64_t)(n_shared > 0 ? n_shared : 1) * T * H));
@@ -593,8 +633,8 @@ int orc_moe_layer(const float *x, int T, int64_t H, int64_t I, int E, int K, int
                   const uint8_t *const *blobs, int n_shared, const uint8_t *const *shared_blobs,
                   float *out, int32_t *ids, float *wts)
 {
-    return orc_moe_layer_groups(x, T, H, I, E, K, fmt, Wr, bias, 1, 1, routed_scale, norm_topk,
-                                blobs, n_shared, shared_blobs, out, ids, wts);
+    return orc_moe_layer_full(x, T, H, I, E, K, fmt, Wr, bias, 0, 1, 1, routed_scale, norm_topk,
+                              blobs, n_shared, shared_blobs, out, ids, wts);
 }
 
 /* ------------------------------------------------------------------------ */

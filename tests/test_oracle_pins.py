@@ -378,6 +378,74 @@ def test_groups_reject_bad_shapes():
 
 
 # ---------------------------------------------------------------------------
+# O4c: softmax scoring ([EDGE0] §七 softmax-top-k; [GLM-C] §05 olmoe step)
+# ---------------------------------------------------------------------------
+
+SM = oracle.SCORE_SOFTMAX
+
+
+def test_softmax_equal_logits_uniform_and_lowest_ids():
+    E, K = 16, 4
+    x = np.zeros((1, 8), dtype=np.float32)
+    W = np.zeros((E, 8), dtype=np.float32)
+    b = np.linspace(-1, 1, E).astype(np.float32)          # ignored by softmax scoring
+    ids, wts, lg, p, gk, gi = oracle.route(x, W, b, K, 1.0, 1, scoring=SM)
+    assert np.all(p == np.float32(1.0 / E))
+    assert list(ids[0]) == [0, 1, 2, 3]
+    assert np.allclose(wts[0], 1.0 / K, rtol=0, atol=1e-7)       # renormalised to one
+    ids, wts, *_ = oracle.route(x, W, b, K, 1.0, 0, scoring=SM)
+    assert np.allclose(wts[0], 1.0 / E, rtol=0, atol=1e-8)       # raw probabilities
+    assert gk[0] == 0.0
+
+
+def test_softmax_matches_numpy_and_sorting_definition():
+    cfg = synth.CONFIGS["tiny"]
+    W = synth.router_weight(cfg, 0)
+    b = synth.router_bias(cfg, 0)
+    x = synth.tokens(cfg, T=16, stream=9)
+    K = 4
+    ids, wts, lg, p, gk, gi = oracle.route(x, W, b, K, 1.0, 1, scoring=SM)
+    ref = np.exp(lg.astype(np.float64) - lg.max(axis=1, keepdims=True))
+    ref /= ref.sum(axis=1, keepdims=True)
+    assert np.allclose(p, ref, rtol=2e-7, atol=0)
+    assert np.allclose(p.sum(axis=1), 1.0, atol=1e-6)
+    for t in range(16):
+        want = sorted(range(cfg.E), key=lambda e: (-float(p[t, e]), e))[:K]
+        assert list(ids[t]) == want
+        s = p[t, ids[t]].astype(np.float64)
+        assert np.allclose(wts[t], s / s.sum(), rtol=1e-7)
+        lgs = sorted(lg[t].tolist(), reverse=True)
+        assert gk[t] == pytest.approx(lgs[K - 1] - lgs[K])          # logit units
+    ids0, wts0, *_ = oracle.route(x, W, b, K, 2.0, 0, scoring=SM)
+    assert np.array_equal(ids0, ids)
+    for t in range(16):
+        assert np.allclose(wts0[t], 2.0 * p[t, ids[t]], rtol=1e-7)
+
+
+def test_softmax_shift_invariance_and_bias_ignored():
+    cfg = synth.CONFIGS["tiny"]
+    W = synth.router_weight(cfg, 0)
+    x = synth.tokens(cfg, T=8, stream=4)
+    # a constant input column with equal weights shifts every logit equally
+    x1 = np.concatenate([x, np.ones((8, 1), np.float32)], axis=1)
+    W1 = np.concatenate([W, np.full((cfg.E, 1), 3.0, np.float32)], axis=1)
+    W0 = np.concatenate([W, np.zeros((cfg.E, 1), np.float32)], axis=1)
+    z = np.zeros(cfg.E, np.float32)
+    ids_a, wts_a, _, p_a, *_ = oracle.route(x1, W0, z, 4, 1.0, 1, scoring=SM)
+    ids_b, wts_b, _, p_b, *_ = oracle.route(x1, W1, z + 5.0, 4, 1.0, 1, scoring=SM)
+    assert np.array_equal(ids_a, ids_b)
+    assert np.allclose(p_a, p_b, rtol=2e-6, atol=0)
+    assert np.allclose(wts_a, wts_b, rtol=2e-6)
+
+
+def test_softmax_with_groups_is_rejected():
+    x = np.zeros((1, 8), dtype=np.float32)
+    W = np.zeros((8, 8), dtype=np.float32)
+    with pytest.raises(ValueError):
+        oracle.route_groups(x, W, np.zeros(8, np.float32), 2, 2, 1, scoring=SM)
+
+
+# ---------------------------------------------------------------------------
 # O5: bucketing
 # ---------------------------------------------------------------------------
 
