@@ -202,6 +202,7 @@ def bench_rotated(torch, name, steps, result):
     layer_bytes = glm_bytes(cfg, cfg.K + cfg.n_shared, 1)
     result["extra"][name] = {
         "T": 1, "layers": L, "n_group": cfg.n_group, "topk_group": cfg.topk_group,
+        "scoring": "softmax" if cfg.scoring else "sigmoid",
         "us_per_layer": t * 1e6, "graph_replay_percentiles": pct,
         "layer_algorithmic_bytes": layer_bytes, "layer_gbps": layer_bytes / t / 1e9,
         "layer_frac_hbm_peak": layer_bytes / t / 1e9 / HBM_PEAK_GBS,
@@ -393,7 +394,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="only the decode workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=16)
-    ap.add_argument("--only", choices=["decode", "verify", "edge0", "edge0_k8", "prefill", "grouped"],
+    ap.add_argument("--only", choices=["decode", "verify", "edge0", "edge0_k8", "prefill", "grouped",
+                                       "softmax"],
                     help="run one workload only (for profiling); the JSON line then "
                          "carries that workload in extra")
     ap.add_argument("--copy-probe", action="store_true",
@@ -424,7 +426,8 @@ def main():
          "edge0": lambda: bench_chain(torch, "edge0_decode", 200, result),
          "edge0_k8": lambda: bench_chain(torch, "edge0_decode_k8", 200, result),
          "prefill": lambda: bench_prefill(torch, 20, result),
-         "grouped": lambda: bench_rotated(torch, "glm_decode_grouped", 200, result)}[args.only]()
+         "grouped": lambda: bench_rotated(torch, "glm_decode_grouped", 200, result),
+         "softmax": lambda: bench_rotated(torch, "glm_decode_softmax", 200, result)}[args.only]()
         print(json.dumps(result), flush=True)
         return
     bench_decode(torch, args, result)
@@ -435,6 +438,7 @@ def main():
         bench_chain(torch, "edge0_decode", 200, result)
         bench_chain(torch, "edge0_decode_k8", 200, result)
         bench_rotated(torch, "glm_decode_grouped", 200, result)
+        bench_rotated(torch, "glm_decode_softmax", 200, result)
         bench_prefill(torch, 20, result)
     if not args.no_cpu:
         log("[bench] cpu baseline (oracle)")

@@ -66,6 +66,12 @@ typedef struct moe_ctx moe_ctx;
 #define MOE_W_INT4_ROW 1        /* symmetric int4, one fp32 scale per output row */
 #define MOE_W_INT4_AFFINE_G64 2 /* affine int4, bf16 scale and min per 64 inputs */
 
+/* router scoring (moe_config.scoring) */
+#define MOE_SCORE_SIGMOID 0 /* sigma(l) + bias selects, sigma weighs ([GLM-C] §11, [EDGE0] §七) */
+#define MOE_SCORE_SOFTMAX 1 /* softmax(l) over all experts selects (no bias) and weighs: raw
+                               (norm_topk = 0, the [GLM-C] §05 olmoe step) or renormalised
+                               to one (norm_topk = 1, [EDGE0] §七 softmax-top-k); one group */
+
 typedef struct moe_config {
     int hidden;         /* H, multiple of 64 */
     int inter;          /* I, multiple of 64 */
@@ -86,6 +92,7 @@ typedef struct moe_config {
     int n_slots;        /* expert slots in the HBM pool */
     int max_tokens;     /* largest T passed to moe_forward / moe_route */
     float rms_eps;      /* eps of the RMSNorm used by moe_forward_residual */
+    int scoring;        /* MOE_SCORE_SIGMOID or MOE_SCORE_SOFTMAX */
 } moe_config;
 
 /* Creates a context on the current HIP device: allocates the slot pool

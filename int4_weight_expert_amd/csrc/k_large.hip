@@ -163,9 +163,35 @@ __global__ void __launch_bounds__(256) k_topk(Fwd f)
             for (int sl = 0; sl < ROUTER_SLICES; ++sl)
                 l += f.logits[((size_t)sl * f.T + t) * Epad + e];
             l *= rs;
-            sg[m] = 1.0f / (1.0f + expf(-l));
-            c[m] = sg[m] + f.bias[e];
+            if (f.scoring == MOE_SCORE_SOFTMAX) {
+                sg[m] = l;  // the probability follows below
+            } else {
+                sg[m] = 1.0f / (1.0f + expf(-l));
+                c[m] = sg[m] + f.bias[e];
+            }
         }
+    }
+    // softmax scoring: probabilities over all experts (shifted by the largest
+    // logit); they weigh and select, no bias
+    if (f.scoring == MOE_SCORE_SOFTMAX) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            if (lane + 64 * m < E) mx = fmaxf(mx, sg[m]);
+        mx = wave_max(mx);
+        float z = 0.f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            sg[m] = lane + 64 * m < E ? expf(sg[m] - mx) : 0.f;
+            z += sg[m];
+        }
+        z = wsum(z);
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            if (lane + 64 * m < E) {
+                sg[m] = sg[m] / z;
+                c[m] = sg[m];
+            }
     }
     // group-limited selection: a group's score is the fp32 sum of its two
     // largest c; a group is kept when fewer than topk_group groups rank above

@@ -178,17 +178,61 @@ __device__ void router_tail(const Fwd& f)
     for (int i = tid; i < T * 32; i += RT_THREADS) s_cand[i >> 5][i & 31] = 0ull;
     if (NT > 1) __syncthreads();
 
-    // 2. sigmoid, bias, score key (keys of all 256 slots are written: padding
-    //    experts get 0, below every real key)
+    // 2. scores and keys (keys of all 256 slots are written: padding experts
+    //    get 0, below every real key).  Sigmoid: sigma weighs, sigma + bias
+    //    selects.  Softmax: the probability over all experts (shifted by the
+    //    token's largest logit) weighs and selects.
+    float prob[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) prob[t] = 0.f;
+    if (f.scoring == MOE_SCORE_SOFTMAX) {
+        __shared__ float s_red[NT][RT_THREADS / 64];
+        float l[NT], m[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            l[t] = -INFINITY;
+            if (t < T && tid < E) l[t] = lsum[t] * (NT == 1 ? rs0 : s_rs[t]);
+            const float v = wave_max(l[t]);
+            if (lane == 0) s_red[t][w] = v;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            m[t] = s_red[t][0];
+#pragma unroll
+            for (int i = 1; i < RT_THREADS / 64; ++i) m[t] = fmaxf(m[t], s_red[t][i]);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            prob[t] = (t < T && tid < E) ? expf(l[t] - m[t]) : 0.f;
+            const float v = wave_sum(prob[t]);
+            if (lane == 0) s_red[t][w] = v;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            float z = 0.f;
+#pragma unroll
+            for (int i = 0; i < RT_THREADS / 64; ++i) z += s_red[t][i];
+            prob[t] = prob[t] / z;
+        }
+    }
 #pragma unroll
     for (int t = 0; t < NT; ++t)
         if (t < T) {
             unsigned long long key = 0ull;
             float sig = 0.f;
             if (tid < E) {
-                const float rs = NT == 1 ? rs0 : s_rs[t];
-                sig = 1.0f / (1.0f + expf(-(lsum[t] * rs)));
-                const float c = sig + bias_e;
+                float c;
+                if (f.scoring == MOE_SCORE_SOFTMAX) {
+                    sig = prob[t];
+                    c = sig;
+                } else {
+                    const float rs = NT == 1 ? rs0 : s_rs[t];
+                    sig = 1.0f / (1.0f + expf(-(lsum[t] * rs)));
+                    c = sig + bias_e;
+                }
                 key = ((unsigned long long)ord_float(c) << 32) | (uint32_t)(0xFFFFu - tid);
             }
             s_key[t][tid] = key;

@@ -209,6 +209,7 @@ Fwd make_fwd(moe_ctx* c, const float* x, float* out, int T, int layer, int resid
     f.n_tiles = c->n_tiles;
     f.counters = c->counters;
     f.n_group = g.n_group;
+    f.scoring = g.scoring;
     f.topk_group = g.topk_group;
     f.status = c->status;
     f.n_layers = g.n_layers;
@@ -354,6 +355,8 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
         return MOE_E_ARG;
     if (g.wfmt != MOE_W_INT4_ROW && g.wfmt != MOE_W_INT4_AFFINE_G64) return MOE_E_ARG;
     if (g.n_group < 1 || g.topk_group < 1 || g.topk_group > g.n_group) return MOE_E_ARG;
+    if (g.scoring != MOE_SCORE_SIGMOID && g.scoring != MOE_SCORE_SOFTMAX) return MOE_E_ARG;
+    if (g.scoring == MOE_SCORE_SOFTMAX && g.n_group != 1) return MOE_E_UNSUPPORTED;
     if (g.n_group > 1 &&
         (g.n_group > 64 || g.n_experts % g.n_group || g.n_experts / g.n_group < 2 ||
          g.top_k > g.topk_group * (g.n_experts / g.n_group)))

@@ -51,6 +51,7 @@ struct Fwd {
     float routed_scale, eps;
     int norm_topk;
     int n_group, topk_group;  // group-limited selection (n_group = 1: none)
+    int scoring;          // MOE_SCORE_SIGMOID or MOE_SCORE_SOFTMAX
     int layer;
     const float* wr;      // router, interleaved [Epad/64][H/4][64] float4
     const float* bias;    // [E]

@@ -15,14 +15,14 @@ class MoeLayer:
     def __init__(self, H: int, I: int, E: int, K: int, n_shared: int, n_layers: int, fmt: int,
                  n_slots: int, max_tokens: int, routed_scale: float = 2.5, norm_topk: int = 1,
                  rms_eps: float = 1e-6, stream: torch.cuda.Stream | None = None,
-                 n_group: int = 1, topk_group: int = 1):
+                 n_group: int = 1, topk_group: int = 1, scoring: int = 0):
         self.H, self.I, self.E, self.K = H, I, E, K
         self.n_shared, self.n_layers, self.fmt = n_shared, n_layers, fmt
         self.n_slots, self.max_tokens = n_slots, max_tokens
         self.stream = stream if stream is not None else torch.cuda.current_stream()
         cfg = M.make_config(H, I, E, K, n_shared, n_layers, fmt, n_slots, max_tokens,
                             routed_scale=routed_scale, norm_topk=norm_topk, rms_eps=rms_eps,
-                            n_group=n_group, topk_group=topk_group)
+                            n_group=n_group, topk_group=topk_group, scoring=scoring)
         self.ctx = M.moe_layer_create(cfg, self.stream.cuda_stream)
         self.expert_bytes = M.moe_expert_bytes(self.ctx)
 

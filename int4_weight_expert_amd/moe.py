@@ -23,6 +23,7 @@ MOE_E_HIP = -6
 MOE_E_UNSUPPORTED = -7
 MOE_E_RANGE = -8
 MOE_W_INT4_ROW = 1
+MOE_SCORE_SIGMOID, MOE_SCORE_SOFTMAX = 0, 1
 MOE_W_INT4_AFFINE_G64 = 2
 
 ERROR_NAMES = {0: "MOE_OK", -1: "MOE_E_ARG", -2: "MOE_E_NOMEM", -3: "MOE_E_SIZE",
@@ -43,7 +44,7 @@ class moe_config(ctypes.Structure):
                 ("wfmt", ctypes.c_int), ("n_group", ctypes.c_int), ("topk_group", ctypes.c_int),
                 ("routed_scale", ctypes.c_float), ("norm_topk", ctypes.c_int),
                 ("n_slots", ctypes.c_int), ("max_tokens", ctypes.c_int),
-                ("rms_eps", ctypes.c_float)]
+                ("rms_eps", ctypes.c_float), ("scoring", ctypes.c_int)]
 
 
 class MoeError(RuntimeError):
@@ -122,9 +123,9 @@ def moe_last_error(ctx) -> str:
 
 
 def make_config(H, I, E, K, n_shared, n_layers, wfmt, n_slots, max_tokens, routed_scale=2.5,
-                norm_topk=1, rms_eps=1e-6, n_group=1, topk_group=1) -> moe_config:
+                norm_topk=1, rms_eps=1e-6, n_group=1, topk_group=1, scoring=0) -> moe_config:
     return moe_config(H, I, E, K, n_shared, n_layers, wfmt, n_group, topk_group, routed_scale,
-                      norm_topk, n_slots, max_tokens, rms_eps)
+                      norm_topk, n_slots, max_tokens, rms_eps, scoring)
 
 
 def moe_layer_create(cfg: moe_config, stream: int = 0) -> int:

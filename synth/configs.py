@@ -36,6 +36,7 @@ class LayerConfig:
     norm_topk: int = 1
     n_group: int = 1          # expert groups of the router (group-limited selection)
     topk_group: int = 1       # groups kept per token
+    scoring: int = 0          # 0 sigmoid (+ bias selects), 1 softmax over all experts
     eps: float = 1e-6
 
     def with_(self, **kw) -> "LayerConfig":
@@ -69,6 +70,14 @@ CONFIGS = {
     "grouped_affine": LayerConfig("grouped_affine", H=2048, I=512, E=256, K=8, n_shared=0,
                                   fmt=W_INT4_AFFINE_G64, T=1, n_layers=1, seed=501, n_group=8,
                                   topk_group=4),
+    # softmax scoring over all experts: renormalised weights (row format,
+    # shared expert) and raw probabilities (affine, the olmoe-style step)
+    "softmax_renorm": LayerConfig("softmax_renorm", H=2048, I=256, E=64, K=8, n_shared=1,
+                                  fmt=W_INT4_ROW, T=1, n_layers=1, seed=700, scoring=1,
+                                  routed_scale=1.0, norm_topk=1),
+    "softmax_raw": LayerConfig("softmax_raw", H=2048, I=512, E=32, K=4, n_shared=0,
+                               fmt=W_INT4_AFFINE_G64, T=1, n_layers=1, seed=701, scoring=1,
+                               routed_scale=1.0, norm_topk=0),
     # GLM-5.2 shape prefill, 2048 tokens, one layer
     "glm_prefill": LayerConfig("glm_prefill", H=6144, I=2048, E=256, K=8, n_shared=1,
                                fmt=W_INT4_ROW, T=2048, n_layers=1, seed=300, zipf_c=0.2),
@@ -77,3 +86,6 @@ CONFIGS["edge0_decode_k8"] = CONFIGS["edge0_decode"].with_(name="edge0_decode_k8
 # GLM-5.2 shape decode with group-limited routing (8 groups, 4 kept), 4 layers
 CONFIGS["glm_decode_grouped"] = CONFIGS["glm_decode"].with_(name="glm_decode_grouped", n_group=8,
                                                              topk_group=4, n_layers=4, seed=600)
+# the same decode layer scored by a softmax over all experts (renormalised top-8)
+CONFIGS["glm_decode_softmax"] = CONFIGS["glm_decode"].with_(name="glm_decode_softmax", scoring=1,
+                                                            n_layers=4, seed=601)

@@ -54,7 +54,7 @@ class OracleLayer:
     def route(self, x):
         cfg = self.cfg
         return oracle.route(x, self.W, self.b, cfg.K, cfg.routed_scale, cfg.norm_topk, cfg.n_group,
-                            cfg.topk_group)
+                            cfg.topk_group, cfg.scoring)
 
     def need(self, experts):
         missing = [e for e in set(int(v) for v in np.ravel(experts)) if e not in self.cache]
@@ -74,7 +74,7 @@ class OracleLayer:
         def one(t):
             o, _, _ = oracle.moe_layer(xin[t:t + 1], self.W, self.b, cfg.K, cfg.fmt, cfg.I, blobs,
                                        self.shared, cfg.routed_scale, cfg.norm_topk, cfg.n_group,
-                                       cfg.topk_group)
+                                       cfg.topk_group, cfg.scoring)
             return o[0]
 
         with ThreadPoolExecutor(max_workers=workers) as ex:
