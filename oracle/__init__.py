@@ -72,6 +72,13 @@ def lib() -> ctypes.CDLL:
         L.orc_residual_layer.argtypes = [vp, i32, i64, i64, i32, i32, i32, vp, vp, f32, i32, vp,
                                          i32, vp, f32, vp, vp]
         L.orc_residual_layer.restype = i32
+        L.orc_fp8_e4m3_to_f32.argtypes = [ctypes.c_uint8]
+        L.orc_fp8_e4m3_to_f32.restype = f32
+        L.orc_dequant_fp8_block.argtypes = [vp, vp, i64, i64, i64, vp]
+        L.orc_bf16_to_f32.argtypes = [vp, i64, vp]
+        L.orc_convert_int4_container.argtypes = [vp, i64, i64, vp, vp]
+        for name in ("orc_dequant_fp8_block", "orc_bf16_to_f32", "orc_convert_int4_container"):
+            getattr(L, name).restype = None
         for name in ("orc_pack_int4_row", "orc_unpack_int4_row", "orc_dequant_int4_row",
                      "orc_pack_affine_g64", "orc_dequant_affine_g64"):
             getattr(L, name).restype = None
@@ -102,6 +109,64 @@ def pack_int4_row(w: np.ndarray):
     q = np.empty((O, (I + 1) // 2), dtype=np.uint8)
     s = np.empty(O, dtype=np.float32)
     lib().orc_pack_int4_row(_p(w), O, I, _p(q), _p(s))
+    return q, s
+
+
+SRC_F32, SRC_BF16, SRC_FP8_E4M3 = 0, 1, 2
+FP8_BLOCK = 128
+
+
+def fp8_e4m3_to_f32(codes) -> np.ndarray:
+    """FP8 E4M3 (fn) codes -> fp32, code by code ([GLM-C] §06)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    out = np.array([lib().orc_fp8_e4m3_to_f32(int(v)) for v in c.reshape(-1)], dtype=np.float32)
+    return out.reshape(c.shape)
+
+
+def dequant_fp8_block(q: np.ndarray, sinv: np.ndarray, block: int = FP8_BLOCK) -> np.ndarray:
+    """fp8 [O][I] times its [ceil(O/B)][ceil(I/B)] inverse block scales ([GLM-C] §06)."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    O, I = q.shape
+    sinv = _f32(sinv)
+    assert sinv.shape == ((O + block - 1) // block, (I + block - 1) // block)
+    w = np.empty((O, I), dtype=np.float32)
+    lib().orc_dequant_fp8_block(_p(q), _p(sinv), O, I, block, _p(w))
+    return w
+
+
+def bf16_to_f32(b: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    w = np.empty(b.shape, dtype=np.float32)
+    lib().orc_bf16_to_f32(_p(b), b.size, _p(w))
+    return w
+
+
+def decode_source(w, src: int, sinv=None) -> np.ndarray:
+    """Checkpoint tensor -> fp32: fp32 as is, bf16 bits widened, FP8 E4M3
+    codes times their block inverse scales ([GLM-C] §06)."""
+    if src == SRC_F32:
+        return _f32(w)
+    if src == SRC_BF16:
+        return bf16_to_f32(w)
+    if src == SRC_FP8_E4M3:
+        return dequant_fp8_block(w, sinv)
+    raise ValueError(src)
+
+
+def requant_int4_rows(w, src: int, sinv=None):
+    """Checkpoint tensor -> per-row int4 (O1 after the decode)."""
+    return pack_int4_row(decode_source(w, src, sinv))
+
+
+def convert_int4_container(w: np.ndarray):
+    """The converter's container: offset-binary codes [O][I/2] and fp32 row
+    scales ([GLM-C] §06 quant_int4 with bits = 4)."""
+    w = _f32(w)
+    O, I = w.shape
+    assert I % 2 == 0
+    q = np.empty((O, I // 2), dtype=np.uint8)
+    s = np.empty(O, dtype=np.float32)
+    lib().orc_convert_int4_container(_p(w), O, I, _p(q), _p(s))
     return q, s
 
 

@@ -17,8 +17,8 @@
  * Sources (web pages; cited by title and section):
  *   [GLM-C]  "惊呆了！25GB 内存上运行 GLM 5.2 744B 模型" (reader.mx): section 04
  *            (basic math: rmsnorm, siluf), 05 (400-line streaming engine:
- *            quantize_rows, moe()), 06 (FP8 to int4: quant_int4, pack_int4,
- *            decoded container), 07 (np.rint == lrintf), 11 (MoE routing and
+ *            quantize_rows, moe()), 06 (FP8 to int4: FP8 block-scale decode,
+ *            quant_int4, pack_int4, decoded container), 07 (np.rint == lrintf), 11 (MoE routing and
  *            expert execution), 13 (contiguous expert slab, VRAM hot tier).
  *   [FLOW]   GLM-5.2 inference dataflow page (devpress.csdn.net), section
  *            2.3 (MoE FFN: 256 routed + 1 shared) and section 三, Step 6
@@ -150,6 +150,72 @@ void orc_dequant_int4_row(const uint8_t *q, const float *s, int64_t O, int64_t I
     for (int64_t o = 0; o < O; ++o)
         for (int64_t i = 0; i < I; ++i)
             w[o * I + i] = (double)nib_signed(q + o * rb, i) * (double)s[o];
+}
+
+/* ------------------------------------------------------------------------ */
+/* O0: the step before the path, the checkpoint converter ([GLM-C] §06):      */
+/* FP8 E4M3 weights with one fp32 inverse scale per 128 x 128 block, or bf16, */
+/* decoded to fp32, then packed as O1; and the converter's container, which   */
+/* stores code + 8.                                                           */
+/* ------------------------------------------------------------------------ */
+
+/* FP8 E4M3 of the "fn" kind the checkpoint's dtype names (float8_e4m3fn):
+ * sign bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0 is
+ * subnormal (m/8 * 2^-6); no infinities; S.1111.111 is NaN.  Exact. */
+float orc_fp8_e4m3_to_f32(uint8_t b)
+{
+    int neg = b >> 7, e = (b >> 3) & 0xF, m = b & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) v = ldexp((double)m / 8.0, -6);
+    else v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return (float)(neg ? -v : v);
+}
+
+/* Block-scale decode: w[o][i] = fp8(q[o][i]) * sinv[o/B][i/B], one fp32
+ * multiply, sinv [ceil(O/B)][ceil(I/B)] row-major; the page repeats the
+ * scale tensor over each B x B block and crops it to [O, I] (B = 128). */
+void orc_dequant_fp8_block(const uint8_t *q, const float *sinv, int64_t O, int64_t I, int64_t B,
+                           float *w)
+{
+    int64_t nbi = (I + B - 1) / B;
+    for (int64_t o = 0; o < O; ++o)
+        for (int64_t i = 0; i < I; ++i) {
+            float a = orc_fp8_e4m3_to_f32(q[o * I + i]);
+            float sc = sinv[(o / B) * nbi + i / B];
+            w[o * I + i] = a * sc;
+        }
+}
+
+/* bf16 -> fp32, exact (the page's .to(float32) of non-FP8 tensors). */
+void orc_bf16_to_f32(const uint16_t *b, int64_t n, float *w)
+{
+    for (int64_t i = 0; i < n; ++i) w[i] = bf16_to_f32(b[i]);
+}
+
+/* The converter's own packer, bits = 4: s = amax/7 floored at 1e-8, code =
+ * rint(w/s) clamped to [-8, 7], stored offset binary (code + 8), column 2j
+ * in the low nibble of byte j.  I even.  q [O][I/2], s [O]. */
+void orc_convert_int4_container(const float *w, int64_t O, int64_t I, uint8_t *q, float *s)
+{
+    for (int64_t o = 0; o < O; ++o) {
+        const float *wr = w + o * I;
+        float amax = 0.0f;
+        for (int64_t i = 0; i < I; ++i)
+            if (fabsf(wr[i]) > amax) amax = fabsf(wr[i]);
+        float sc = amax / 7.0f;
+        if (sc < 1e-8f) sc = 1e-8f;
+        s[o] = sc;
+        for (int64_t j = 0; j < I / 2; ++j) {
+            int v[2];
+            for (int h = 0; h < 2; ++h) {
+                v[h] = (int)rintf(wr[2 * j + h] / sc);
+                if (v[h] > 7) v[h] = 7;
+                if (v[h] < -8) v[h] = -8;
+            }
+            q[o * (I / 2) + j] = (uint8_t)((v[0] + 8) | ((v[1] + 8) << 4));
+        }
+    }
 }
 
 /* ------------------------------------------------------------------------ */

@@ -625,3 +625,123 @@ def test_rmsnorm_closed_form_and_scale_invariance():
     b = oracle.rmsnorm(8 * y, eps=0.0)
     assert np.array_equal(a, b)
     assert np.allclose((a.astype(np.float64) ** 2).mean(axis=1), 1.0, rtol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# O0: the converter step before the path ([GLM-C] §06): FP8 E4M3 with block
+# inverse scales, bf16, and the offset-binary container
+# ---------------------------------------------------------------------------
+
+def _f8(values):
+    """fp32 values exactly representable in E4M3 -> their codes (torch's encoder)."""
+    torch = pytest.importorskip("torch")
+    return torch.tensor(np.asarray(values, dtype=np.float32)).to(torch.float8_e4m3fn) \
+        .view(torch.uint8).numpy()
+
+
+def test_fp8_decode_matches_torch_on_every_code():
+    torch = pytest.importorskip("torch")
+    c = np.arange(256, dtype=np.uint8)
+    got = oracle.fp8_e4m3_to_f32(c)
+    ref = torch.from_numpy(c).view(torch.float8_e4m3fn).float().numpy()
+    nan = np.isnan(ref)
+    assert list(np.where(nan)[0]) == [0x7F, 0xFF]
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_fp8_decode_closed_forms():
+    d = lambda b: float(oracle.fp8_e4m3_to_f32([b])[0])  # noqa: E731
+    assert d(0x38) == 1.0 and d(0x40) == 2.0 and d(0xB8) == -1.0
+    assert d(0x7E) == 448.0 and d(0xFE) == -448.0          # largest finite
+    assert d(0x08) == 2.0 ** -6                             # smallest normal
+    assert d(0x01) == 2.0 ** -9 and d(0x07) == 7 * 2.0 ** -9  # subnormals
+    assert d(0x00) == 0.0 and math.copysign(1.0, d(0x80)) == -1.0
+    assert d(0x3C) == 1.5 and d(0x44) == 3.0
+
+
+def test_fp8_block_dequant_matches_page_expression():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(11)
+    O, I = 300, 200                                   # ragged in both block dims
+    q = rng.integers(0, 256, size=(O, I), dtype=np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x33                      # no NaN codes
+    sinv = rng.uniform(1e-5, 1e-2, size=(3, 2)).astype(np.float32)
+    got = oracle.dequant_fp8_block(q, sinv)
+    w = torch.from_numpy(q).view(torch.float8_e4m3fn).to(torch.float32)
+    sc = torch.from_numpy(sinv).repeat_interleave(128, 0).repeat_interleave(128, 1)[:O, :I]
+    assert np.array_equal(got.view(np.uint32), (w * sc).numpy().view(np.uint32))
+
+
+def test_fp8_block_boundaries():
+    O, I = 260, 390
+    q = np.full((O, I), 0x38, dtype=np.uint8)        # every code 1.0
+    sinv = np.array([[2.0 ** (4 * a + b) for b in range(4)] for a in range(3)], dtype=np.float32)
+    w = oracle.dequant_fp8_block(q, sinv)
+    oo, ii = np.meshgrid(np.arange(O), np.arange(I), indexing="ij")
+    assert np.array_equal(w, sinv[oo // 128, ii // 128])
+
+
+def test_bf16_decode():
+    torch = pytest.importorskip("torch")
+    b = np.array([0x3F80, 0xC000, 0x0000, 0x8000, 0x7F80, 0x3E4C], dtype=np.uint16)
+    w = oracle.bf16_to_f32(b)
+    assert list(w[:5]) == [1.0, -2.0, 0.0, -0.0, np.inf] and math.copysign(1, w[3]) == -1
+    r = np.random.default_rng(3).integers(0, 0x7F80, size=1000).astype(np.uint16)
+    ref = torch.from_numpy(r.view(np.int16)).view(torch.bfloat16).float().numpy()
+    assert np.array_equal(oracle.bf16_to_f32(r).view(np.uint32), ref.view(np.uint32))
+
+
+def test_requant_fp8_on_the_grid_gives_the_integers():
+    rng = np.random.default_rng(5)
+    O, I = 130, 256
+    ints = rng.integers(-7, 8, size=(O, I))
+    ints[:, 7] = 7                                    # row max 7: s = sinv exactly
+    q = _f8(ints)
+    # one power of two per row block, the same for both column blocks
+    sinv = np.repeat(2.0 ** rng.integers(-12, -4, size=(2, 1)), 2, axis=1).astype(np.float32)
+    codes, s = oracle.requant_int4_rows(q, oracle.SRC_FP8_E4M3, sinv)
+    assert np.array_equal(s, sinv[np.arange(O) // 128, 0])
+    assert np.array_equal(oracle.unpack_int4_row(codes, I).astype(int), ints)
+
+
+def test_requant_ties_go_to_even():
+    # row max 7 with sinv 1: s = 1, so w / s is w itself; halves round to even
+    vals = [7.0, 2.5, 3.5, -2.5, 1.5, -0.5, 0.5, -1.5, 5.5, -6.5, 4.5, 0.0]
+    want = [7, 2, 4, -2, 2, 0, 0, -2, 6, -6, 4, 0]
+    q = _f8([vals])
+    codes, s = oracle.requant_int4_rows(q, oracle.SRC_FP8_E4M3, np.ones((1, 1), np.float32))
+    assert s[0] == 1.0
+    assert list(oracle.unpack_int4_row(codes, len(vals))[0]) == want
+
+
+def test_requant_bf16_equals_pack_of_widened_values():
+    rng = np.random.default_rng(8)
+    w = (rng.standard_normal((64, 128)) * 0.02).astype(np.float32)
+    b = (w.view(np.uint32) >> 16).astype(np.uint16)   # truncated to bf16 bits
+    widened = (b.astype(np.uint32) << 16).view(np.float32)
+    codes, s = oracle.requant_int4_rows(b, oracle.SRC_BF16)
+    c2, s2 = oracle.pack_int4_row(widened)
+    assert np.array_equal(codes, c2) and np.array_equal(s, s2)
+
+
+def test_container_converter_is_the_blob_with_flipped_nibbles():
+    rng = np.random.default_rng(9)
+    w = (rng.standard_normal((96, 512)) * 0.02).astype(np.float32)
+    w[3] = 0.0                                        # floor row
+    qc, sc = oracle.convert_int4_container(w)
+    qb, sb = oracle.pack_int4_row(w)
+    assert np.array_equal(sc, sb)
+    assert np.array_equal(qc, qb ^ 0x88)
+
+
+def test_container_converter_reproduces_page_bytes():
+    g = _golden("int4_container_example.txt")
+    raw = [int(b, 16) for b in g["bytes_offset_binary"].split()]
+    codes = []
+    for b in raw:
+        codes += [(b & 0xF) - 8, (b >> 4) - 8]
+    row = np.array(codes + [7, 0], dtype=np.float32) * 0.25   # a 7 fixes s = 0.25
+    q, s = oracle.convert_int4_container(row[None, :])
+    assert s[0] == 0.25
+    assert list(q[0, :8]) == raw
