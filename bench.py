@@ -213,6 +213,58 @@ def bench_rotated(torch, name, steps, result):
     torch.cuda.empty_cache()
 
 
+def bench_requant(torch, result, n_experts: int = 32, steps: int = 256):
+    """The converter step on the device: FP8 E4M3 GLM-5.2-shape experts
+    (gate/up [2048, 6144], down [6144, 2048], one fp32 inverse scale per
+    128 x 128 block) requantised to int4 straight into slots, one launch per
+    expert, graph-replayed over n_experts distinct sources (1.2 GB, beyond the
+    Infinity Cache)."""
+    import numpy as np
+    import synth
+    from int4_weight_expert_amd import moe as M
+    from int4_weight_expert_amd.layer import MoeLayer
+    H, I = 6144, 2048
+    log(f"[bench] requant: {n_experts} FP8 experts H={H} I={I}")
+    ml = MoeLayer(H, I, 256, 8, 0, 1, M.MOE_W_INT4_ROW, n_slots=n_experts, max_tokens=1)
+    tmp = torch.empty(H * I, dtype=torch.float32, device="cuda")
+    srcs = []
+    for e in range(n_experts):
+        mats = []
+        for t, (O, In) in enumerate([(I, H), (I, H), (H, I)]):
+            k = synth.key(800, 0, t, e)
+            synth.gpu_fill_gauss(tmp.data_ptr(), O * In, k, 112.0, 0,
+                                 torch.cuda.current_stream().cuda_stream)
+            q = tmp.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).clone()
+            nb = ((O + 127) // 128) * ((In + 127) // 128)
+            si = (0.02 * 4 / 448 * np.exp(synth.gauss(k, nb, 0.3, idx0=O * In)
+                                          .astype(np.float64))).astype(np.float32)
+            mats.append((q, torch.from_numpy(si).cuda()))
+        srcs.append(mats)
+    del tmp
+    fns = [(lambda e=e: ml.requant_expert(e, M.MOE_SRC_FP8_E4M3, srcs[e][0][0], srcs[e][1][0],
+                                          srcs[e][2][0], srcs[e][0][1], srcs[e][1][1],
+                                          srcs[e][2][1])) for e in range(n_experts)]
+    for fn in fns:
+        fn()
+    torch.cuda.synchronize()
+    first = ml.read_slot(0)
+    g, t, _ = time_graph(torch, ml, fns, steps, n_experts)
+    assert np.array_equal(ml.read_slot(0), first), "graph replay changed a slot"
+    read_b = 3 * H * I + 4 * (2 * (I // 128) * (H // 128) + (H // 128) * (I // 128))
+    write_b = 3 * H * I // 2 + 4 * (2 * I + H)
+    result["extra"]["requant_fp8_glm_expert"] = {
+        "experts": n_experts, "us_per_expert": t * 1e6, "algorithmic_bytes": read_b + write_b,
+        "read_bytes": read_b, "write_bytes": write_b,
+        "gbps": (read_b + write_b) / t / 1e9,
+        "frac_hbm_peak": (read_b + write_b) / t / 1e9 / HBM_PEAK_GBS,
+        "experts_per_s": 1.0 / t,
+    }
+    log(f"[bench] requant: {t * 1e6:.1f} us/expert, {(read_b + write_b) / t / 1e9:.0f} GB/s")
+    ml.close()
+    del ml, srcs, g
+    torch.cuda.empty_cache()
+
+
 def bench_chain(torch, name, steps, result):
     """Chained residual layers (x <- x + moe(rmsnorm(x))): per-layer time."""
     import numpy as np
@@ -395,7 +447,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=16)
     ap.add_argument("--only", choices=["decode", "verify", "edge0", "edge0_k8", "prefill", "grouped",
-                                       "softmax"],
+                                       "softmax", "requant"],
                     help="run one workload only (for profiling); the JSON line then "
                          "carries that workload in extra")
     ap.add_argument("--copy-probe", action="store_true",
@@ -427,7 +479,8 @@ def main():
          "edge0_k8": lambda: bench_chain(torch, "edge0_decode_k8", 200, result),
          "prefill": lambda: bench_prefill(torch, 20, result),
          "grouped": lambda: bench_rotated(torch, "glm_decode_grouped", 200, result),
-         "softmax": lambda: bench_rotated(torch, "glm_decode_softmax", 200, result)}[args.only]()
+         "softmax": lambda: bench_rotated(torch, "glm_decode_softmax", 200, result),
+         "requant": lambda: bench_requant(torch, result)}[args.only]()
         print(json.dumps(result), flush=True)
         return
     bench_decode(torch, args, result)
@@ -439,6 +492,7 @@ def main():
         bench_chain(torch, "edge0_decode_k8", 200, result)
         bench_rotated(torch, "glm_decode_grouped", 200, result)
         bench_rotated(torch, "glm_decode_softmax", 200, result)
+        bench_requant(torch, result)
         bench_prefill(torch, 20, result)
     if not args.no_cpu:
         log("[bench] cpu baseline (oracle)")

@@ -142,11 +142,45 @@ int moe_load_expert(moe_ctx *ctx, int slot, const void *blob, size_t nbytes);
  * quantiser as moe_pack_int4_rows / moe_pack_affine_g64.  Asynchronous. */
 int moe_pack_expert(moe_ctx *ctx, int slot, const float *Wg, const float *Wu, const float *Wd);
 
+/* Checkpoint source kinds of the requantiser ([GLM-C] §06 FP8 to int4). */
+#define MOE_SRC_F32 0      /* fp32 */
+#define MOE_SRC_BF16 1     /* bf16 bit patterns (uint16) */
+#define MOE_SRC_FP8_E4M3 2 /* FP8 E4M3 (fn: bias 7, no inf) codes with fp32 inverse scales,
+                            * one per 128 x 128 block, [ceil(O/128)][ceil(In/128)] row-major;
+                            * weight = fp8 value * its block's inverse scale (fp32 product) */
+
+/* The converter step on the device ([GLM-C] §06): decodes a checkpoint
+ * expert (Wg, Wu [I][H], Wd [H][I] row-major device pointers of kind src;
+ * sinv_* the FP8 inverse scales, ignored otherwise) to fp32 and quantises
+ * it into a slot in the layer's format, as moe_pack_expert does from fp32.
+ * NaN codes give unspecified codes.  Asynchronous on the context's stream.
+ * Errors: MOE_E_SLOT, MOE_E_ARG (null, unknown src, FP8 without scales),
+ * MOE_E_HIP. */
+int moe_requant_expert(moe_ctx *ctx, int slot, int src, const void *Wg, const void *Wu,
+                       const void *Wd, const float *sinv_g, const float *sinv_u,
+                       const float *sinv_d);
+
+/* Imports one expert of the converter's int4 container ([GLM-C] §06: per
+ * tensor, U8 codes [O][In/2] stored as code + 8, first column in the low
+ * nibble, and fp32 row scales; weight = code * scale) into a slot: qg, qu
+ * [I][H/2], qd [H][I/2], sg, su [I], sd [H]; host or device pointers.
+ * Codes -8..7 are all accepted.  Row format only.  Synchronous.
+ * Errors: MOE_E_SLOT, MOE_E_ARG, MOE_E_UNSUPPORTED (affine layer), MOE_E_HIP. */
+int moe_import_expert(moe_ctx *ctx, int slot, const uint8_t *qg, const uint8_t *qu,
+                      const uint8_t *qd, const float *sg, const float *su, const float *sd);
+
 /* Shared expert s of a layer, from a blob (host or device; synchronous) or
  * from device fp32 weights (asynchronous).  Errors: MOE_E_ARG, MOE_E_SIZE. */
 int moe_set_shared(moe_ctx *ctx, int layer, int s, const void *blob, size_t nbytes);
 int moe_pack_shared(moe_ctx *ctx, int layer, int s, const float *Wg, const float *Wu,
                     const float *Wd);
+/* The shared expert s of a layer from a checkpoint source or the container,
+ * as moe_requant_expert / moe_import_expert.  Errors: MOE_E_ARG and theirs. */
+int moe_requant_shared(moe_ctx *ctx, int layer, int s, int src, const void *Wg, const void *Wu,
+                       const void *Wd, const float *sinv_g, const float *sinv_u,
+                       const float *sinv_d);
+int moe_import_shared(moe_ctx *ctx, int layer, int s, const uint8_t *qg, const uint8_t *qu,
+                      const uint8_t *qd, const float *sg, const float *su, const float *sd);
 
 /* Points (layer, expert_id) at a slot, or unmaps it with slot = -1
  * ([COLI] §2.2 ESlot, [EDGE0] §十四 slot table).  Several layers or ids may
@@ -220,6 +254,15 @@ int moe_pack_int4_rows(const float *w, int64_t O, int64_t I, uint8_t *q, float *
  * bf16 (scale, min).  Device pointers; I a multiple of 64. */
 int moe_pack_affine_g64(const float *w, int64_t O, int64_t I, uint8_t *q, uint16_t *scmn,
                         void *stream);
+
+/* The same two quantisers from a checkpoint source (src, sinv as for
+ * moe_requant_expert; w a device pointer of that kind).  Rows a multiple
+ * of 32 wide up to 8192 run one wavefront per row with each element read
+ * once.  Errors: MOE_E_ARG, MOE_E_HIP. */
+int moe_requant_int4_rows(const void *w, int src, const float *sinv, int64_t O, int64_t I,
+                          uint8_t *q, float *s, void *stream);
+int moe_requant_affine_g64(const void *w, int src, const float *sinv, int64_t O, int64_t I,
+                           uint8_t *q, uint16_t *scmn, void *stream);
 
 /* Token -> expert bucketing of ids [T][K] (device) ([GLM-C] §11 batch
  * expert union): cnt [E], off [E+1] (exclusive scan), perm [T*K] =

@@ -9,6 +9,12 @@
 //   affine int4 with group size 64: Edge0 write-up (magicnetworld.com) §三.
 // Both decisions (code from a float) are taken in fp32 with IEEE
 // round-to-nearest division and rint, the precision the pages use.
+//
+// Sources: fp32, bf16, or FP8 E4M3 (fn) codes with one fp32 inverse scale
+// per 128 x 128 block, the checkpoint's form ("惊呆了！…" §06, FP8 block
+// decode: fp8 value times its block's inverse scale, one fp32 multiply).
+// The FP8 decode is gfx950's v_cvt_pk_f32_fp8, which decodes the fn
+// variant exactly (checked against every code by the parity tests).
 #include "moe_internal.h"
 
 namespace moe {
@@ -41,17 +47,37 @@ __device__ __forceinline__ int code_row(float w, float s)
     return v > 7 ? 7 : (v < -7 ? -7 : v);
 }
 
-// One 256-thread workgroup per output row (grid-stride over rows).
-__global__ void __launch_bounds__(256) k_pack_int4_rows(const float* __restrict__ w, int64_t O,
+// Element (o, i) of a source matrix [O][I], decoded to fp32.  nbi = number
+// of 128-wide block columns of the FP8 inverse scales.
+template <int SRC>
+__device__ __forceinline__ float src_elem(const void* __restrict__ w,
+                                          const float* __restrict__ sinv, int64_t o, int64_t i,
+                                          int64_t I, int64_t nbi)
+{
+    if constexpr (SRC == MOE_SRC_F32) {
+        return ((const float*)w)[o * I + i];
+    } else if constexpr (SRC == MOE_SRC_BF16) {
+        return __uint_as_float((uint32_t)((const uint16_t*)w)[o * I + i] << 16);
+    } else {
+        const int b = ((const uint8_t*)w)[o * I + i];
+        return __builtin_amdgcn_cvt_f32_fp8(b, 0) * sinv[(o >> 7) * nbi + (i >> 7)];
+    }
+}
+
+// Any even I: one 256-thread workgroup per output row (grid-stride over rows).
+template <int SRC>
+__global__ void __launch_bounds__(256) k_pack_int4_rows(const void* __restrict__ w,
+                                                        const float* __restrict__ sinv, int64_t O,
                                                         int64_t I, uint8_t* __restrict__ q,
                                                         float* __restrict__ s)
 {
     __shared__ float red[4];
     const int tid = threadIdx.x;
+    const int64_t nbi = (I + 127) >> 7;
     for (int64_t o = blockIdx.x; o < O; o += gridDim.x) {
-        const float* wr = w + o * I;
         float amax = 0.0f;
-        for (int64_t i = tid; i < I; i += 256) amax = fmaxf(amax, fabsf(wr[i]));
+        for (int64_t i = tid; i < I; i += 256)
+            amax = fmaxf(amax, fabsf(src_elem<SRC>(w, sinv, o, i, I, nbi)));
         amax = wave_max(amax);
         if ((tid & 63) == 0) red[tid >> 6] = amax;
         __syncthreads();
@@ -62,24 +88,241 @@ __global__ void __launch_bounds__(256) k_pack_int4_rows(const float* __restrict_
         if (tid == 0) s[o] = sc;
         uint8_t* qr = q + o * (I / 2);
         for (int64_t j = tid; j < I / 2; j += 256) {
-            int v0 = code_row(wr[2 * j], sc), v1 = code_row(wr[2 * j + 1], sc);
+            int v0 = code_row(src_elem<SRC>(w, sinv, o, 2 * j, I, nbi), sc);
+            int v1 = code_row(src_elem<SRC>(w, sinv, o, 2 * j + 1, I, nbi), sc);
             qr[j] = (uint8_t)((v0 & 0xF) | ((v1 & 0xF) << 4));
         }
     }
 }
 
+// ---------------------------------------------------------------------------
+// Tiled requantiser for I a multiple of 32 up to 8192 (the expert shapes).
+// A workgroup of 4 wavefronts takes 8 consecutive rows of one matrix, 2 per
+// wavefront.  Lane l holds the 16-input units l, l + 64, ... of its row
+// (each unit one coalesced 16-byte FP8 load, 32 bytes of bf16, 64 of fp32)
+// in registers, so each element is read once; the row maximum is a
+// wavefront max.  Codes go out as 8 bytes per unit: in the blob layout
+// directly (consecutive lanes, consecutive bytes); in the slot interleave
+// through LDS, so that each store writes the 8 rows' 16-byte pieces of one
+// 32-input chunk, 128 contiguous bytes.  8-row tiles keep every tile of an
+// expert resident at once (no partial second round of workgroups).
+//
+// Code = rint(fl(w / s)) with w = fl(v * bs) for FP8 (bs its block's
+// inverse scale).  With y = fl(1/s) (correctly rounded, once per row), the
+// quotient is q0 = w*y refined once, q = fma(fma(-s, q0, w), y, q0).  Only
+// codes matter, and they can differ from the IEEE quotient's only where
+// w/s lies within a few ulps of a half-integer; for every divisor
+// significand and every dividend within 24 ulps of k*s (k = 0.5 .. 7.5) this
+// sequence gives the IEEE quotient's code (exhaustive host check, with a
+// test of its own), and the device parity tests compare every code with
+// the oracle's IEEE division.  Adding 1.5 * 2^23 (+ 8 for the slot's offset
+// binary) rounds to the nearest integer, ties to even, and leaves the code
+// in the low byte, since s = fl(amax/7) bounds |w/s| by 7 plus an ulp.
+// ---------------------------------------------------------------------------
+struct RqMat {
+    const void* src;     // [O][In] source elements
+    const float* sinv;   // FP8 inverse scales [ceil(O/128)][ceil(In/128)]
+    uint8_t* q;          // codes (blob rows or the slot's matrix)
+    float* s;            // [O] row scales
+    int O, In;
+};
+
+struct RqArgs {
+    RqMat m[3];
+    int tiles[3];        // 8-row tiles per matrix
+};
+
+constexpr int RQ_ROWS = 8;                        // rows per workgroup
+constexpr int RQ_TSTRIDE = RQ_ROWS * 16 + 16;     // LDS bytes per 32-input chunk (padded)
+
+template <int SRC> struct RqUnit;  // 16-byte loads per 16-input unit
+template <> struct RqUnit<MOE_SRC_FP8_E4M3> { static constexpr int N = 1; };
+template <> struct RqUnit<MOE_SRC_BF16> { static constexpr int N = 2; };
+template <> struct RqUnit<MOE_SRC_F32> { static constexpr int N = 4; };
+
+// Largest |value| of one unit, before the block scale.  FP8 and bf16 are
+// sign-magnitude, so with the sign cleared their order is the integers'
+// order (and rounding the product by a positive scale keeps it: max fl(|v|
+// * bs) = fl(max|v| * bs)).
+template <int SRC>
+__device__ __forceinline__ float rq_unit_amax(const uint4 (&r)[RqUnit<SRC>::N])
+{
+    if constexpr (SRC == MOE_SRC_FP8_E4M3) {
+        const uint32_t w[4] = {r[0].x & 0x7F7F7F7Fu, r[0].y & 0x7F7F7F7Fu, r[0].z & 0x7F7F7F7Fu,
+                               r[0].w & 0x7F7F7F7Fu};
+        uint32_t m = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            m = max(m, max(w[k] & 0xFFu, (w[k] >> 8) & 0xFFu));
+            m = max(m, max((w[k] >> 16) & 0xFFu, w[k] >> 24));
+        }
+        return __builtin_amdgcn_cvt_f32_fp8((int)m, 0);
+    } else if constexpr (SRC == MOE_SRC_BF16) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t w[4] = {r[j].x, r[j].y, r[j].z, r[j].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) m = max(m, max(w[k] & 0x7FFFu, (w[k] >> 16) & 0x7FFFu));
+        }
+        return __uint_as_float(m << 16);
+    } else {
+        float m = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            m = fmaxf(m, fmaxf(fmaxf(fabsf(__uint_as_float(r[j].x)), fabsf(__uint_as_float(r[j].y))),
+                               fmaxf(fabsf(__uint_as_float(r[j].z)), fabsf(__uint_as_float(r[j].w)))));
+        return m;
+    }
+}
+
+// Inputs 8h .. 8h+7 of a unit, decoded to fp32 (before the block scale).
+template <int SRC>
+__device__ __forceinline__ void rq_decode8(const uint4 (&r)[RqUnit<SRC>::N], int h, float (&v)[8])
+{
+    if constexpr (SRC == MOE_SRC_FP8_E4M3) {
+        const uint32_t w[2] = {h ? r[0].z : r[0].x, h ? r[0].w : r[0].y};
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);
+            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);
+            v[4 * k + 0] = lo[0];
+            v[4 * k + 1] = lo[1];
+            v[4 * k + 2] = hi[0];
+            v[4 * k + 3] = hi[1];
+        }
+    } else if constexpr (SRC == MOE_SRC_BF16) {
+        const uint4 u = r[h];
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[2 * k] = __uint_as_float(w[k] << 16);
+            v[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint4 u = r[2 * h + j];
+            v[4 * j + 0] = __uint_as_float(u.x);
+            v[4 * j + 1] = __uint_as_float(u.y);
+            v[4 * j + 2] = __uint_as_float(u.z);
+            v[4 * j + 3] = __uint_as_float(u.w);
+        }
+    }
+}
+
+// 8 codes (+ off) as nibbles, input 0 in the low nibble.  y = q + 1.5*2^23
+// + off holds rint(q) + off in its low byte (two's complement).
+__device__ __forceinline__ uint32_t rq_pack8(const float (&q)[8], float magic)
+{
+    uint32_t y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = __float_as_uint(q[e] + magic);
+    const uint32_t ev = __builtin_amdgcn_perm(y[2], y[0], 0x0C0C0400u) |
+                        __builtin_amdgcn_perm(y[6], y[4], 0x04000C0Cu);
+    const uint32_t od = __builtin_amdgcn_perm(y[3], y[1], 0x0C0C0400u) |
+                        __builtin_amdgcn_perm(y[7], y[5], 0x04000C0Cu);
+    return (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
+}
+
+template <int SRC, bool SLOT>
+__global__ void __launch_bounds__(RQ_ROWS * 32) k_requant_rows(RqArgs a)
+{
+    constexpr int NU = RqUnit<SRC>::N;
+    constexpr int ESZ = SRC == MOE_SRC_FP8_E4M3 ? 1 : (SRC == MOE_SRC_BF16 ? 2 : 4);
+    extern __shared__ __align__(16) uint8_t rq_tile[];
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int t = blockIdx.x, mi = 0;
+    if (t >= a.tiles[0]) {
+        t -= a.tiles[0];
+        mi = 1;
+        if (t >= a.tiles[1]) {
+            t -= a.tiles[1];
+            mi = 2;
+        }
+    }
+    const RqMat m = a.m[mi];
+    const int o0 = t * RQ_ROWS;
+    const int U = m.In >> 4, C = m.In >> 5, nbi = (m.In + 127) >> 7;
+    const float magic = SLOT ? 12582920.0f : 12582912.0f;  // 1.5 * 2^23 (+ 8)
+#pragma unroll 1
+    for (int rr = 0; rr < 2; ++rr) {
+        const int ro = 2 * wv + rr, o = o0 + ro;
+        if (o >= m.O) break;
+        const uint8_t* row = (const uint8_t*)m.src + (size_t)o * m.In * ESZ;
+        uint4 raw[8][NU];
+        float bs[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int u = min(lane + 64 * k, U - 1);  // past the row end: reread its last unit
+#pragma unroll
+            for (int j = 0; j < NU; ++j) raw[k][j] = ((const uint4*)(row + (size_t)u * 16 * ESZ))[j];
+            bs[k] = SRC == MOE_SRC_FP8_E4M3 ? m.sinv[(size_t)(o >> 7) * nbi + (u >> 3)] : 1.0f;
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (lane + 64 * k < U) {
+                const float um = rq_unit_amax<SRC>(raw[k]);
+                amax = fmaxf(amax, SRC == MOE_SRC_FP8_E4M3 ? um * bs[k] : um);
+            }
+        amax = wave_max(amax);
+        float sc = __fdiv_rn(amax, 7.0f);
+        if (sc < 1e-8f) sc = 1e-8f;
+        const float rinv = __fdiv_rn(1.0f, sc);
+        if (lane == 0) m.s[o] = sc;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int u = lane + 64 * k;
+            if (u < U) {
+                uint32_t nib[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    float v[8], q[8];
+                    rq_decode8<SRC>(raw[k], h, v);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float w = SRC == MOE_SRC_FP8_E4M3 ? v[e] * bs[k] : v[e];
+                        const float q0 = w * rinv;
+                        q[e] = fmaf(fmaf(-sc, q0, w), rinv, q0);
+                    }
+                    nib[h] = rq_pack8(q, magic);
+                }
+                if (SLOT)
+                    *(uint2*)(rq_tile + (u >> 1) * RQ_TSTRIDE + ro * 16 + (u & 1) * 8) =
+                        make_uint2(nib[0], nib[1]);
+                else
+                    *(uint2*)(m.q + (size_t)o * (m.In / 2) + (size_t)u * 8) = make_uint2(nib[0], nib[1]);
+            }
+        }
+    }
+    if (SLOT) {  // every matrix's O is a multiple of 64, so the tile is full
+        __syncthreads();
+        const int b = o0 >> 6, rb = o0 & 63;
+        for (int i = threadIdx.x; i < C * RQ_ROWS; i += RQ_ROWS * 32) {
+            const int c = i / RQ_ROWS, r = i % RQ_ROWS;
+            *(uint4*)(m.q + (((size_t)b * C + c) * 64 + rb + r) * 16) =
+                *(const uint4*)(rq_tile + c * RQ_TSTRIDE + r * 16);
+        }
+    }
+}
+
 // One wavefront per (row, group of 64 inputs); 4 groups per workgroup.
-__global__ void __launch_bounds__(256) k_pack_affine_g64(const float* __restrict__ w, int64_t O,
+template <int SRC>
+__global__ void __launch_bounds__(256) k_pack_affine_g64(const void* __restrict__ w,
+                                                         const float* __restrict__ sinv, int64_t O,
                                                          int64_t I, uint8_t* __restrict__ q,
                                                          uint16_t* __restrict__ scmn)
 {
     const int lane = threadIdx.x & 63;
     const int64_t G = I / 64;
     const int64_t total = O * G;
+    const int64_t nbi = (I + 127) >> 7;
     for (int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); item < total;
          item += (int64_t)gridDim.x * 4) {
         const int64_t o = item / G, g = item % G;
-        const float v = w[o * I + g * 64 + lane];
+        const float v = src_elem<SRC>(w, sinv, o, g * 64 + lane, I, nbi);
         const float lo = wave_min(v), hi = wave_max(v);
         const uint16_t sc16 = bf16_rne(__fdiv_rn(hi - lo, 15.0f));
         const uint16_t mn16 = bf16_rne(lo);
@@ -161,26 +404,119 @@ static unsigned grid_for(int64_t items, int64_t per_block)
     return (unsigned)g;
 }
 
-hipError_t launch_pack_int4_rows(const float* w, int64_t O, int64_t I, uint8_t* q, float* s,
-                                 hipStream_t st)
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// The tiled kernel covers In a multiple of 32 up to 8192 with 16-byte
+// aligned rows.
+static bool rq_fast_ok(const void* src, const void* q, int64_t O, int64_t In)
 {
-    hipLaunchKernelGGL(k_pack_int4_rows, dim3(grid_for(O, 1)), dim3(256), 0, st, w, O, I, q, s);
+    return In > 0 && In % 32 == 0 && In <= 8192 && O < (1 << 30) && aligned16(src) &&
+           aligned16(q);
+}
+
+template <bool SLOT>
+static hipError_t launch_rq(int src, const RqArgs& a, hipStream_t st)
+{
+    int maxC = 0;
+    for (int i = 0; i < 3; ++i)
+        if (a.tiles[i] > 0 && a.m[i].In / 32 > maxC) maxC = a.m[i].In / 32;
+    const dim3 grid(a.tiles[0] + a.tiles[1] + a.tiles[2]), block(RQ_ROWS * 32);
+    const size_t lds = SLOT ? (size_t)maxC * RQ_TSTRIDE : 0;
+    switch (src) {
+    case MOE_SRC_F32:
+        hipLaunchKernelGGL((k_requant_rows<MOE_SRC_F32, SLOT>), grid, block, lds, st, a);
+        break;
+    case MOE_SRC_BF16:
+        hipLaunchKernelGGL((k_requant_rows<MOE_SRC_BF16, SLOT>), grid, block, lds, st, a);
+        break;
+    case MOE_SRC_FP8_E4M3:
+        hipLaunchKernelGGL((k_requant_rows<MOE_SRC_FP8_E4M3, SLOT>), grid, block, lds, st, a);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
-hipError_t launch_pack_affine_g64(const float* w, int64_t O, int64_t I, uint8_t* q,
-                                  uint16_t* scmn, hipStream_t st)
+hipError_t launch_requant_rows(const void* w, int src, const float* sinv, int64_t O, int64_t I,
+                               uint8_t* q, float* s, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_pack_affine_g64, dim3(grid_for(O * (I / 64), 4)), dim3(256), 0, st, w,
-                       O, I, q, scmn);
+    if (rq_fast_ok(w, q, O, I)) {
+        RqArgs a{};
+        a.m[0] = RqMat{w, sinv, q, s, (int)O, (int)I};
+        a.tiles[0] = (int)((O + RQ_ROWS - 1) / RQ_ROWS);
+        return launch_rq<false>(src, a, st);
+    }
+    const dim3 grid(grid_for(O, 1)), block(256);
+    switch (src) {
+    case MOE_SRC_F32:
+        hipLaunchKernelGGL(k_pack_int4_rows<MOE_SRC_F32>, grid, block, 0, st, w, sinv, O, I, q, s);
+        break;
+    case MOE_SRC_BF16:
+        hipLaunchKernelGGL(k_pack_int4_rows<MOE_SRC_BF16>, grid, block, 0, st, w, sinv, O, I, q, s);
+        break;
+    case MOE_SRC_FP8_E4M3:
+        hipLaunchKernelGGL(k_pack_int4_rows<MOE_SRC_FP8_E4M3>, grid, block, 0, st, w, sinv, O, I, q,
+                           s);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
+}
+
+hipError_t launch_requant_affine(const void* w, int src, const float* sinv, int64_t O, int64_t I,
+                                 uint8_t* q, uint16_t* scmn, hipStream_t st)
+{
+    const dim3 grid(grid_for(O * (I / 64), 4)), block(256);
+    switch (src) {
+    case MOE_SRC_F32:
+        hipLaunchKernelGGL(k_pack_affine_g64<MOE_SRC_F32>, grid, block, 0, st, w, sinv, O, I, q,
+                           scmn);
+        break;
+    case MOE_SRC_BF16:
+        hipLaunchKernelGGL(k_pack_affine_g64<MOE_SRC_BF16>, grid, block, 0, st, w, sinv, O, I, q,
+                           scmn);
+        break;
+    case MOE_SRC_FP8_E4M3:
+        hipLaunchKernelGGL(k_pack_affine_g64<MOE_SRC_FP8_E4M3>, grid, block, 0, st, w, sinv, O, I,
+                           q, scmn);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+bool requant_slot_ok(const void* wg, const void* wu, const void* wd, const uint8_t* slot, int H,
+                     int I)
+{
+    const int64_t gq = (int64_t)I * (H / 2);
+    return rq_fast_ok(wg, slot, I, H) && rq_fast_ok(wu, slot + gq, I, H) &&
+           rq_fast_ok(wd, slot + 2 * gq, H, I);
+}
+
+// Row format: the three matrices of one expert in one launch, codes and
+// scales written straight into the slot.
+hipError_t launch_requant_slot(int src, const void* wg, const void* wu, const void* wd,
+                               const float* sg, const float* su, const float* sd, int H, int I,
+                               uint8_t* slot, hipStream_t st)
+{
+    const int64_t gq = (int64_t)I * (H / 2), dq = (int64_t)H * (I / 2);
+    float* sc = (float*)(slot + 2 * gq + dq);
+    RqArgs a{};
+    a.m[0] = RqMat{wg, sg, slot, sc, I, H};
+    a.m[1] = RqMat{wu, su, slot + gq, sc + I, I, H};
+    a.m[2] = RqMat{wd, sd, slot + 2 * gq, sc + 2 * I, H, I};
+    a.tiles[0] = a.tiles[1] = I / RQ_ROWS;
+    a.tiles[2] = H / RQ_ROWS;
+    return launch_rq<true>(src, a, st);
 }
 
 static hipError_t convert(const uint8_t* src, uint8_t* dst, int fmt, int H, int I, int to_slot,
-                          hipStream_t st)
+                          uint32_t flip, hipStream_t st)
 {
     const int64_t gq = (int64_t)I * (H / 2), dq = (int64_t)H * (I / 2);
-    const uint32_t flip = fmt == MOE_W_INT4_ROW ? 0x88888888u : 0u;
     const int64_t mats[3][3] = {{0, I, H}, {gq, I, H}, {2 * gq, H, I}};  // offset, O, In
     for (auto& m : mats) {
         hipLaunchKernelGGL(k_interleave, dim3(grid_for(m[1] * (m[2] / 32), 256)), dim3(256), 0,
@@ -202,16 +538,26 @@ static hipError_t convert(const uint8_t* src, uint8_t* dst, int fmt, int H, int 
     return hipGetLastError();
 }
 
+static uint32_t blob_flip(int fmt) { return fmt == MOE_W_INT4_ROW ? 0x88888888u : 0u; }
+
 hipError_t launch_blob_to_slot(const uint8_t* blob, uint8_t* slot, int fmt, int H, int I,
                                hipStream_t st)
 {
-    return convert(blob, slot, fmt, H, I, 1, st);
+    return convert(blob, slot, fmt, H, I, 1, blob_flip(fmt), st);
 }
 
 hipError_t launch_slot_to_blob(const uint8_t* slot, uint8_t* blob, int fmt, int H, int I,
                                hipStream_t st)
 {
-    return convert(slot, blob, fmt, H, I, 0, st);
+    return convert(slot, blob, fmt, H, I, 0, blob_flip(fmt), st);
+}
+
+// The converter's container (row format, codes already offset binary, the
+// slot's own coding): interleave only.
+hipError_t launch_container_to_slot(const uint8_t* staged, uint8_t* slot, int H, int I,
+                                    hipStream_t st)
+{
+    return convert(staged, slot, MOE_W_INT4_ROW, H, I, 1, 0u, st);
 }
 
 hipError_t launch_router_to_internal(const float* W, float* wr, int E, int Epad, int H,

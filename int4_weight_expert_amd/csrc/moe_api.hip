@@ -316,29 +316,56 @@ int copy_in_blob(moe_ctx* c, uint8_t* dst_slot, const void* blob, size_t nbytes)
     return hip_ok(hipStreamSynchronize(c->stream));
 }
 
-int pack_into(moe_ctx* c, uint8_t* dst_slot, const float* Wg, const float* Wu, const float* Wd)
+int requant_into(moe_ctx* c, uint8_t* dst_slot, int src, const void* Wg, const void* Wu,
+                 const void* Wd, const float* sg, const float* su, const float* sd)
 {
     if (!Wg || !Wu || !Wd) return MOE_E_ARG;
+    if (src != MOE_SRC_F32 && src != MOE_SRC_BF16 && src != MOE_SRC_FP8_E4M3) return MOE_E_ARG;
+    if (src == MOE_SRC_FP8_E4M3 && (!sg || !su || !sd)) return MOE_E_ARG;
     const int64_t H = c->cfg.hidden, I = c->cfg.inter;
+    if (c->cfg.wfmt == MOE_W_INT4_ROW && requant_slot_ok(Wg, Wu, Wd, dst_slot, (int)H, (int)I))
+        return hip_ok(launch_requant_slot(src, Wg, Wu, Wd, sg, su, sd, (int)H, (int)I, dst_slot,
+                                          c->stream));
     const int64_t gq = I * (H / 2), dq = H * (I / 2);
     uint8_t* b = c->staging;
     uint8_t* sc = b + 2 * gq + dq;
     hipError_t e;
     if (c->cfg.wfmt == MOE_W_INT4_ROW) {
-        e = launch_pack_int4_rows(Wg, I, H, b, (float*)sc, c->stream);
-        if (e == hipSuccess) e = launch_pack_int4_rows(Wu, I, H, b + gq, (float*)sc + I, c->stream);
+        e = launch_requant_rows(Wg, src, sg, I, H, b, (float*)sc, c->stream);
         if (e == hipSuccess)
-            e = launch_pack_int4_rows(Wd, H, I, b + 2 * gq, (float*)sc + 2 * I, c->stream);
+            e = launch_requant_rows(Wu, src, su, I, H, b + gq, (float*)sc + I, c->stream);
+        if (e == hipSuccess)
+            e = launch_requant_rows(Wd, src, sd, H, I, b + 2 * gq, (float*)sc + 2 * I, c->stream);
     } else {
         const int64_t ga = I * (H / 64) * 2;
-        e = launch_pack_affine_g64(Wg, I, H, b, (uint16_t*)sc, c->stream);
+        e = launch_requant_affine(Wg, src, sg, I, H, b, (uint16_t*)sc, c->stream);
         if (e == hipSuccess)
-            e = launch_pack_affine_g64(Wu, I, H, b + gq, (uint16_t*)sc + ga, c->stream);
+            e = launch_requant_affine(Wu, src, su, I, H, b + gq, (uint16_t*)sc + ga, c->stream);
         if (e == hipSuccess)
-            e = launch_pack_affine_g64(Wd, H, I, b + 2 * gq, (uint16_t*)sc + 2 * ga, c->stream);
+            e = launch_requant_affine(Wd, src, sd, H, I, b + 2 * gq, (uint16_t*)sc + 2 * ga,
+                                      c->stream);
     }
     if (e != hipSuccess) return MOE_E_HIP;
     return hip_ok(launch_blob_to_slot(b, dst_slot, c->cfg.wfmt, (int)H, (int)I, c->stream));
+}
+
+int import_into(moe_ctx* c, uint8_t* dst_slot, const uint8_t* qg, const uint8_t* qu,
+                const uint8_t* qd, const float* sg, const float* su, const float* sd)
+{
+    if (c->cfg.wfmt != MOE_W_INT4_ROW) return MOE_E_UNSUPPORTED;
+    if (!qg || !qu || !qd || !sg || !su || !sd) return MOE_E_ARG;
+    const size_t H = c->cfg.hidden, I = c->cfg.inter;
+    const size_t gq = I * (H / 2), dq = H * (I / 2), sb = 2 * gq + dq;
+    uint8_t* b = c->staging;
+    const struct { void* dst; const void* src; size_t n; } parts[6] = {
+        {b, qg, gq}, {b + gq, qu, gq}, {b + 2 * gq, qd, dq},
+        {b + sb, sg, 4 * I}, {b + sb + 4 * I, su, 4 * I}, {b + sb + 8 * I, sd, 4 * H}};
+    for (const auto& p : parts)
+        if (hipMemcpyAsync(p.dst, p.src, p.n, hipMemcpyDefault, c->stream) != hipSuccess)
+            return MOE_E_HIP;
+    if (launch_container_to_slot(b, dst_slot, (int)H, (int)I, c->stream) != hipSuccess)
+        return MOE_E_HIP;
+    return hip_ok(hipStreamSynchronize(c->stream));
 }
 
 }  // namespace
@@ -497,7 +524,26 @@ int moe_pack_expert(moe_ctx* c, int slot, const float* Wg, const float* Wu, cons
 {
     if (!c) return MOE_E_ARG;
     if (slot < 0 || slot >= c->cfg.n_slots) return MOE_E_SLOT;
-    return pack_into(c, c->pool + (size_t)slot * c->slot_bytes, Wg, Wu, Wd);
+    return requant_into(c, c->pool + (size_t)slot * c->slot_bytes, MOE_SRC_F32, Wg, Wu, Wd,
+                        nullptr, nullptr, nullptr);
+}
+
+int moe_requant_expert(moe_ctx* c, int slot, int src, const void* Wg, const void* Wu,
+                       const void* Wd, const float* sinv_g, const float* sinv_u,
+                       const float* sinv_d)
+{
+    if (!c) return MOE_E_ARG;
+    if (slot < 0 || slot >= c->cfg.n_slots) return MOE_E_SLOT;
+    return requant_into(c, c->pool + (size_t)slot * c->slot_bytes, src, Wg, Wu, Wd, sinv_g,
+                        sinv_u, sinv_d);
+}
+
+int moe_import_expert(moe_ctx* c, int slot, const uint8_t* qg, const uint8_t* qu,
+                      const uint8_t* qd, const float* sg, const float* su, const float* sd)
+{
+    if (!c) return MOE_E_ARG;
+    if (slot < 0 || slot >= c->cfg.n_slots) return MOE_E_SLOT;
+    return import_into(c, c->pool + (size_t)slot * c->slot_bytes, qg, qu, qd, sg, su, sd);
 }
 
 int moe_set_shared(moe_ctx* c, int layer, int s, const void* blob, size_t nbytes)
@@ -513,8 +559,27 @@ int moe_pack_shared(moe_ctx* c, int layer, int s, const float* Wg, const float* 
 {
     if (!c || layer < 0 || layer >= c->cfg.n_layers || s < 0 || s >= c->cfg.n_shared)
         return MOE_E_ARG;
-    return pack_into(c, c->shared + ((size_t)layer * c->cfg.n_shared + s) * c->slot_bytes, Wg,
-                     Wu, Wd);
+    return requant_into(c, c->shared + ((size_t)layer * c->cfg.n_shared + s) * c->slot_bytes,
+                        MOE_SRC_F32, Wg, Wu, Wd, nullptr, nullptr, nullptr);
+}
+
+int moe_requant_shared(moe_ctx* c, int layer, int s, int src, const void* Wg, const void* Wu,
+                       const void* Wd, const float* sinv_g, const float* sinv_u,
+                       const float* sinv_d)
+{
+    if (!c || layer < 0 || layer >= c->cfg.n_layers || s < 0 || s >= c->cfg.n_shared)
+        return MOE_E_ARG;
+    return requant_into(c, c->shared + ((size_t)layer * c->cfg.n_shared + s) * c->slot_bytes,
+                        src, Wg, Wu, Wd, sinv_g, sinv_u, sinv_d);
+}
+
+int moe_import_shared(moe_ctx* c, int layer, int s, const uint8_t* qg, const uint8_t* qu,
+                      const uint8_t* qd, const float* sg, const float* su, const float* sd)
+{
+    if (!c || layer < 0 || layer >= c->cfg.n_layers || s < 0 || s >= c->cfg.n_shared)
+        return MOE_E_ARG;
+    return import_into(c, c->shared + ((size_t)layer * c->cfg.n_shared + s) * c->slot_bytes, qg,
+                       qu, qd, sg, su, sd);
 }
 
 int moe_map_expert(moe_ctx* c, int layer, int expert_id, int slot)
@@ -655,15 +720,34 @@ int moe_timing_summary(moe_ctx* c, float* ms, const char** names, int cap, int* 
 
 int moe_pack_int4_rows(const float* w, int64_t O, int64_t I, uint8_t* q, float* s, void* stream)
 {
-    if (!w || !q || !s || O <= 0 || I <= 0 || (I & 1)) return MOE_E_ARG;
-    return hip_ok(launch_pack_int4_rows(w, O, I, q, s, (hipStream_t)stream));
+    return moe_requant_int4_rows(w, MOE_SRC_F32, nullptr, O, I, q, s, stream);
 }
 
 int moe_pack_affine_g64(const float* w, int64_t O, int64_t I, uint8_t* q, uint16_t* scmn,
                         void* stream)
 {
-    if (!w || !q || !scmn || O <= 0 || I <= 0 || (I % 64)) return MOE_E_ARG;
-    return hip_ok(launch_pack_affine_g64(w, O, I, q, scmn, (hipStream_t)stream));
+    return moe_requant_affine_g64(w, MOE_SRC_F32, nullptr, O, I, q, scmn, stream);
+}
+
+static bool src_ok(int src, const float* sinv)
+{
+    if (src == MOE_SRC_F32 || src == MOE_SRC_BF16) return true;
+    return src == MOE_SRC_FP8_E4M3 && sinv != nullptr;
+}
+
+int moe_requant_int4_rows(const void* w, int src, const float* sinv, int64_t O, int64_t I,
+                          uint8_t* q, float* s, void* stream)
+{
+    if (!w || !q || !s || O <= 0 || I <= 0 || (I & 1) || !src_ok(src, sinv)) return MOE_E_ARG;
+    return hip_ok(launch_requant_rows(w, src, sinv, O, I, q, s, (hipStream_t)stream));
+}
+
+int moe_requant_affine_g64(const void* w, int src, const float* sinv, int64_t O, int64_t I,
+                           uint8_t* q, uint16_t* scmn, void* stream)
+{
+    if (!w || !q || !scmn || O <= 0 || I <= 0 || (I % 64) || !src_ok(src, sinv))
+        return MOE_E_ARG;
+    return hip_ok(launch_requant_affine(w, src, sinv, O, I, q, scmn, (hipStream_t)stream));
 }
 
 int moe_bucket(const int32_t* ids, int T, int K, int E, int32_t* cnt, int32_t* off,

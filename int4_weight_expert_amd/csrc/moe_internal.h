@@ -99,10 +99,17 @@ struct Fwd {
 enum { STATUS_NOT_RESIDENT = 1u, STATUS_RANGE = 2u };
 
 // launchers (return hipError_t)
-hipError_t launch_pack_int4_rows(const float* w, int64_t O, int64_t I, uint8_t* q, float* s,
-                                 hipStream_t st);
-hipError_t launch_pack_affine_g64(const float* w, int64_t O, int64_t I, uint8_t* q,
-                                  uint16_t* scmn, hipStream_t st);
+hipError_t launch_requant_rows(const void* w, int src, const float* sinv, int64_t O, int64_t I,
+                               uint8_t* q, float* s, hipStream_t st);
+hipError_t launch_requant_affine(const void* w, int src, const float* sinv, int64_t O, int64_t I,
+                                 uint8_t* q, uint16_t* scmn, hipStream_t st);
+bool requant_slot_ok(const void* wg, const void* wu, const void* wd, const uint8_t* slot, int H,
+                     int I);
+hipError_t launch_requant_slot(int src, const void* wg, const void* wu, const void* wd,
+                               const float* sg, const float* su, const float* sd, int H, int I,
+                               uint8_t* slot, hipStream_t st);
+hipError_t launch_container_to_slot(const uint8_t* staged, uint8_t* slot, int H, int I,
+                                    hipStream_t st);
 hipError_t launch_blob_to_slot(const uint8_t* blob, uint8_t* slot, int fmt, int H, int I,
                                hipStream_t st);
 hipError_t launch_slot_to_blob(const uint8_t* slot, uint8_t* blob, int fmt, int H, int I,

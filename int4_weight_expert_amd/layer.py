@@ -57,6 +57,30 @@ class MoeLayer:
     def pack_shared(self, layer: int, s: int, Wg, Wu, Wd) -> None:
         M._check("moe_pack_shared", M.moe_pack_shared(self.ctx, layer, s, Wg, Wu, Wd))
 
+    def requant_expert(self, slot: int, src: int, Wg, Wu, Wd, sg=None, su=None, sd=None) -> None:
+        """Checkpoint tensors on the device (fp32, bf16 as int16/uint16 bits, or FP8 as
+        uint8 codes with fp32 block inverse scales) -> int4 in a slot."""
+        M._check("moe_requant_expert",
+                 M.moe_requant_expert(self.ctx, slot, src, Wg, Wu, Wd, sg, su, sd), self.ctx)
+
+    def requant_shared(self, layer: int, s: int, src: int, Wg, Wu, Wd, sg=None, su=None,
+                       sd=None) -> None:
+        M._check("moe_requant_shared",
+                 M.moe_requant_shared(self.ctx, layer, s, src, Wg, Wu, Wd, sg, su, sd), self.ctx)
+
+    def import_expert(self, slot: int, qg, qu, qd, sg, su, sd) -> None:
+        """The converter's container (offset-binary codes, fp32 row scales) -> a slot."""
+        qg, qu, qd = (_contig_u8(a) for a in (qg, qu, qd))
+        sg, su, sd = (_contig_f32(a) for a in (sg, su, sd))
+        M._check("moe_import_expert", M.moe_import_expert(self.ctx, slot, qg, qu, qd, sg, su, sd),
+                 self.ctx)
+
+    def import_shared(self, layer: int, s: int, qg, qu, qd, sg, su, sd) -> None:
+        qg, qu, qd = (_contig_u8(a) for a in (qg, qu, qd))
+        sg, su, sd = (_contig_f32(a) for a in (sg, su, sd))
+        M._check("moe_import_shared",
+                 M.moe_import_shared(self.ctx, layer, s, qg, qu, qd, sg, su, sd), self.ctx)
+
     def map(self, layer: int, expert_id: int, slot: int) -> None:
         M._check("moe_map_expert", M.moe_map_expert(self.ctx, layer, expert_id, slot))
 

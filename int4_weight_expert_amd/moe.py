@@ -25,6 +25,7 @@ MOE_E_RANGE = -8
 MOE_W_INT4_ROW = 1
 MOE_SCORE_SIGMOID, MOE_SCORE_SOFTMAX = 0, 1
 MOE_W_INT4_AFFINE_G64 = 2
+MOE_SRC_F32, MOE_SRC_BF16, MOE_SRC_FP8_E4M3 = 0, 1, 2
 
 ERROR_NAMES = {0: "MOE_OK", -1: "MOE_E_ARG", -2: "MOE_E_NOMEM", -3: "MOE_E_SIZE",
                -4: "MOE_E_SLOT", -5: "MOE_E_NOT_RESIDENT", -6: "MOE_E_HIP",
@@ -35,7 +36,8 @@ EXPORTS = ["moe_layer_create", "moe_destroy", "moe_set_stream", "moe_expert_byte
            "moe_pack_shared", "moe_map_expert", "moe_read_slot", "moe_forward",
            "moe_forward_residual", "moe_route", "moe_status", "moe_set_gemm_min_tokens",
            "moe_set_timing", "moe_timing_summary", "moe_last_error", "moe_pack_int4_rows", "moe_pack_affine_g64",
-           "moe_bucket"]
+           "moe_bucket", "moe_requant_expert", "moe_import_expert", "moe_requant_shared",
+           "moe_import_shared", "moe_requant_int4_rows", "moe_requant_affine_g64"]
 
 
 class moe_config(ctypes.Structure):
@@ -88,6 +90,12 @@ def lib() -> ctypes.CDLL:
             "moe_pack_int4_rows": ([vp, i64, i64, vp, vp, vp], i32),
             "moe_pack_affine_g64": ([vp, i64, i64, vp, vp, vp], i32),
             "moe_bucket": ([vp, i32, i32, i32, vp, vp, vp, vp, vp, vp], i32),
+            "moe_requant_expert": ([vp, i32, i32, vp, vp, vp, vp, vp, vp], i32),
+            "moe_import_expert": ([vp, i32, vp, vp, vp, vp, vp, vp], i32),
+            "moe_requant_shared": ([vp, i32, i32, i32, vp, vp, vp, vp, vp, vp], i32),
+            "moe_import_shared": ([vp, i32, i32, vp, vp, vp, vp, vp, vp], i32),
+            "moe_requant_int4_rows": ([vp, i32, vp, i64, i64, vp, vp, vp], i32),
+            "moe_requant_affine_g64": ([vp, i32, vp, i64, i64, vp, vp, vp], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -224,6 +232,35 @@ def moe_pack_int4_rows(w, O, I, q, s, stream=0) -> int:
 
 def moe_pack_affine_g64(w, O, I, q, scmn, stream=0) -> int:
     return lib().moe_pack_affine_g64(_ptr(w), O, I, _ptr(q), _ptr(scmn), stream)
+
+
+def moe_requant_expert(ctx, slot, src, Wg, Wu, Wd, sg=None, su=None, sd=None) -> int:
+    return lib().moe_requant_expert(ctx, slot, src, _ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(sg),
+                                    _ptr(su), _ptr(sd))
+
+
+def moe_import_expert(ctx, slot, qg, qu, qd, sg, su, sd) -> int:
+    return lib().moe_import_expert(ctx, slot, _ptr(qg), _ptr(qu), _ptr(qd), _ptr(sg), _ptr(su),
+                                   _ptr(sd))
+
+
+def moe_requant_shared(ctx, layer, s, src, Wg, Wu, Wd, sg=None, su=None, sd=None) -> int:
+    return lib().moe_requant_shared(ctx, layer, s, src, _ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(sg),
+                                    _ptr(su), _ptr(sd))
+
+
+def moe_import_shared(ctx, layer, s, qg, qu, qd, sg, su, sd) -> int:
+    return lib().moe_import_shared(ctx, layer, s, _ptr(qg), _ptr(qu), _ptr(qd), _ptr(sg),
+                                   _ptr(su), _ptr(sd))
+
+
+def moe_requant_int4_rows(w, src, sinv, O, I, q, s, stream=0) -> int:
+    return lib().moe_requant_int4_rows(_ptr(w), src, _ptr(sinv), O, I, _ptr(q), _ptr(s), stream)
+
+
+def moe_requant_affine_g64(w, src, sinv, O, I, q, scmn, stream=0) -> int:
+    return lib().moe_requant_affine_g64(_ptr(w), src, _ptr(sinv), O, I, _ptr(q), _ptr(scmn),
+                                        stream)
 
 
 def moe_bucket(ids, T, K, E, cnt, off, perm, active, n_active, stream=0) -> int:

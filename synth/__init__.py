@@ -140,3 +140,31 @@ def tokens(cfg: LayerConfig, T: int | None = None, stream: int = 0) -> np.ndarra
     T = cfg.T if T is None else T
     k = key(cfg.seed, 0, T_X, stream)
     return gauss(k, T * cfg.H, cfg.sigma_x).reshape(T, cfg.H)
+
+
+# --------------------------------------------------------------------------
+# Checkpoint-form tensors (inputs of the requantiser): synthetic stand-ins of
+# an FP8 E4M3 checkpoint tensor with one fp32 inverse scale per 128 x 128
+# block, and of a bf16 one.  Encoding uses torch's casts; nothing here
+# decodes or quantises to int4.
+# --------------------------------------------------------------------------
+
+def fp8_checkpoint(k: int, O: int, I: int, sigma: float, block: int = 128):
+    """codes [O][I] uint8 (E4M3 fn) of N(0, 112) clipped to the format's
+    +-448, and inverse scales [ceil(O/B)][ceil(I/B)] fp32 spread
+    log-normally (sd 0.3) around sigma * 4 / 448, so that code * scale has
+    roughly the spread of N(0, sigma) weights."""
+    import torch
+    v = np.clip(gauss(k, O * I, 112.0), -448.0, 448.0).reshape(O, I)
+    codes = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    nb = ((O + block - 1) // block, (I + block - 1) // block)
+    ls = gauss(k, nb[0] * nb[1], 0.3, idx0=O * I).reshape(nb).astype(np.float64)
+    sinv = (sigma * 4.0 / 448.0 * np.exp(ls)).astype(np.float32)
+    return codes, sinv
+
+
+def bf16_checkpoint(k: int, O: int, I: int, sigma: float) -> np.ndarray:
+    """bf16 bit patterns [O][I] (uint16) of N(0, sigma), rounded by torch."""
+    import torch
+    w = gauss(k, O * I, sigma).reshape(O, I)
+    return torch.from_numpy(w).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
