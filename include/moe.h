@@ -61,6 +61,7 @@ typedef struct moe_ctx moe_ctx;
 #define MOE_E_HIP (-6)          /* a HIP runtime call failed */
 #define MOE_E_UNSUPPORTED (-7)  /* configuration outside what the kernels do */
 #define MOE_E_RANGE (-8)        /* fp16 activation overflow on the GEMM path (moe_status) */
+#define MOE_E_BUSY (-9)         /* slot still named by the slot table (asynchronous loads) */
 
 /* expert weight formats (layout of an expert blob, see moe_load_expert) */
 #define MOE_W_INT4_ROW 1        /* symmetric int4, one fp32 scale per output row */
@@ -186,6 +187,83 @@ int moe_import_shared(moe_ctx *ctx, int layer, int s, const uint8_t *qg, const u
  * ([COLI] §2.2 ESlot, [EDGE0] §十四 slot table).  Several layers or ids may
  * share a slot.  Errors: MOE_E_ARG, MOE_E_SLOT. */
 int moe_map_expert(moe_ctx *ctx, int layer, int expert_id, int slot);
+
+/* --- residency: asynchronous loads, staged (sticky) slots, whole layers ---
+ *
+ * Edge0 write-up §十四: the staged executor keeps fixed slots reached
+ * through a slot table and per step rewrites only the experts that changed;
+ * the whole-layer path loads a layer's experts at once, overlapped with the
+ * previous layer's GPU work.  "惊呆了！…" §13: an expert's three matrices
+ * stored contiguously are read with one read into its slab.
+ *
+ * Asynchronous loads copy a slot image (an expert's bytes already in the
+ * slot's own order, see moe_blob_to_image) from host memory (pinned for
+ * the copy to overlap compute; device memory also works) on a copy stream
+ * of the library's own.  Ordering is kept per slot: the compute stream
+ * waits for a slot's load before the table names the slot or before the
+ * library touches the slot on it; a load waits until forwards enqueued
+ * before the slot's last table entry went (or before a synchronous write
+ * into it) are done.  A slot still named by the table takes no
+ * asynchronous load (MOE_E_BUSY).  The caller keeps an image valid until
+ * the load is done (moe_sync_copies, or a synchronised forward that
+ * follows the map). */
+
+/* Table updates, in stream order on the context's stream, without a sync:
+ * (layer, expert_ids[i]) -> slots[i] (-1 unmaps).  Later entries for the
+ * same id win.  Errors: MOE_E_ARG, MOE_E_SLOT, MOE_E_HIP. */
+int moe_map_experts_async(moe_ctx *ctx, int layer, int n, const int *expert_ids,
+                          const int *slots);
+
+/* Loads one slot image (nbytes == moe_expert_bytes) into a slot that the
+ * table does not name.  Returns once the copy is enqueued.
+ * Errors: MOE_E_SLOT, MOE_E_SIZE, MOE_E_BUSY, MOE_E_ARG, MOE_E_HIP. */
+int moe_load_image_async(moe_ctx *ctx, int slot, const void *image, size_t nbytes);
+
+/* Whole-layer load: n slot images stored back to back (experts 0..n-1 of
+ * the layer, nbytes == n * moe_expert_bytes) in one copy into slots
+ * first_slot .. first_slot+n-1, then (layer, e) -> first_slot + e.
+ * Errors: as moe_load_image_async. */
+int moe_load_layer_async(moe_ctx *ctx, int layer, int first_slot, int n, const void *images,
+                         size_t nbytes);
+
+/* Waits for every load enqueued so far.  Errors: MOE_E_ARG, MOE_E_HIP. */
+int moe_sync_copies(moe_ctx *ctx);
+
+/* Staged slots: layer l owns slots first_slot + l*per_layer .. +per_layer-1
+ * (none of them named by the table when staging starts).  Resets what the
+ * staged slots are known to hold.  Errors: MOE_E_ARG, MOE_E_SLOT. */
+int moe_set_staging(moe_ctx *ctx, int first_slot, int per_layer);
+
+/* One step of the staged executor for a layer: the n distinct experts
+ * expert_ids (n <= per_layer) become resident in the layer's staged slots.
+ * Experts already held stay where they are (sticky); the others are loaded
+ * from images[i] (slot images; only those loaded are read) into empty
+ * slots first, then into the slots least recently wanted, whose old
+ * experts leave the table.  Experts held but not wanted stay mapped.
+ * *n_loaded (optional) = number of images loaded.  Asynchronous.
+ * Errors: MOE_E_ARG (staging not set, n too large, bad or repeated id,
+ * missing image), MOE_E_BUSY, MOE_E_HIP. */
+int moe_stage_experts(moe_ctx *ctx, int layer, int n, const int *expert_ids,
+                      const void *const *images, int *n_loaded);
+
+/* The staged executor's slot choice, on the host (no context, no GPU):
+ * held[n_slots] = expert held by each slot (-1 empty), last_used[n_slots]
+ * = step it was last wanted; want[n_want] distinct ids.  slot_of[i] = slot
+ * for want[i], load[i] = 1 if it must be loaded.  Wanted experts already
+ * held keep their slot; the rest take empty slots (ascending), then the
+ * slots with the smallest last_used (ties: lower slot).  Returns the
+ * number of loads, or -1 for bad arguments (n_want > n_slots, a repeated
+ * or negative id). */
+int moe_sticky_plan(const int *held, const int64_t *last_used, int n_slots, const int *want,
+                    int n_want, int *slot_of, int *load);
+
+/* The slot image of an expert blob, on the host (no context, no GPU): the
+ * blob's bytes in the slot's own order (64-row interleave, row-format codes
+ * offset binary, affine pairs interleaved).  hidden and inter multiples of
+ * 64.  Returns MOE_OK, MOE_E_ARG or MOE_E_SIZE. */
+size_t moe_image_bytes(int wfmt, int hidden, int inter);
+int moe_blob_to_image(int wfmt, int hidden, int inter, const void *blob, size_t nbytes,
+                      void *image);
 
 /* Copies a slot back out in blob layout to dst (host or device pointer).
  * Synchronous.  Errors: MOE_E_SLOT, MOE_E_SIZE, MOE_E_ARG. */

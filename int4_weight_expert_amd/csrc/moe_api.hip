@@ -12,76 +12,26 @@
 #include <algorithm>
 #include <vector>
 
-#include "moe_internal.h"
+#include "moe_ctx.h"
 
 using namespace moe;
 
-struct moe_ctx {
-    moe_config cfg;
-    hipStream_t stream = nullptr;
-    int device = 0;
-    size_t slot_bytes = 0;
-    int Epad = 0;
-    uint8_t* pool = nullptr;
-    float* wr = nullptr;
-    float* bias = nullptr;
-    int* tbl = nullptr;
-    std::vector<int> tbl_host;
-    uint8_t* shared = nullptr;
-    uint8_t* staging = nullptr;
-    // workspace
-    float* part = nullptr;
-    float* tpart = nullptr;
-    float* logits = nullptr;
-    int32_t* ids = nullptr;
-    float* wts = nullptr;
-    TokStat* tok = nullptr;
-    uint4* xq = nullptr;
-    float2* xsc = nullptr;
-    int32_t* cnt = nullptr;
-    int32_t* off = nullptr;
-    int32_t* perm = nullptr;
-    int32_t* active = nullptr;
-    int32_t* n_active = nullptr;
-    Group* groups = nullptr;
-    int32_t* n_groups = nullptr;
-    uint4* hq = nullptr;
-    float2* hsc = nullptr;
-    float* gpart = nullptr;
-    size_t gpart_bytes = 0;
-    float* ypart = nullptr;
-    size_t ypart_bytes = 0;
-    float2* xrow = nullptr;
-    float2* hrow = nullptr;
-    float* hbuf = nullptr;
-    int2* tiles = nullptr;
-    int32_t* n_tiles = nullptr;
-    uint32_t* counters = nullptr;
-    uint32_t* status = nullptr;
-    size_t status_words = 0;
-    int gemm_min_tokens = 64;
-    int lds_max = 65536;
-    hipError_t last_err = hipSuccess;
-    // timing
-    bool timing = false;
-    std::vector<hipEvent_t> events;  // marker pool, reused after each summary
-    std::vector<const char*> names;  // per marker: kernel that follows; nullptr = end of a forward
-    int n_marks = 0;
-    std::vector<void*> allocs;
-};
 
-namespace {
-
-constexpr int kDefaultGemmMin = 64;
+namespace moe {
 
 int hip_ok(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_E_HIP; }
 
-// records a failing HIP call for moe_last_error
 int hip_rc(moe_ctx* c, hipError_t e)
 {
     if (e != hipSuccess) c->last_err = e;
     return hip_ok(e);
 }
+
+}  // namespace moe
+
+namespace {
+
+constexpr int kDefaultGemmMin = 64;
 
 template <typename P>
 int dalloc(moe_ctx* c, P** p, size_t bytes)
@@ -304,7 +254,7 @@ int run_forward(moe_ctx* c, const float* x, int T, int layer, float* out, int re
     return MOE_OK;
 }
 
-int copy_in_blob(moe_ctx* c, uint8_t* dst_slot, const void* blob, size_t nbytes)
+int copy_in_blob_impl(moe_ctx* c, uint8_t* dst_slot, const void* blob, size_t nbytes)
 {
     if (!blob) return MOE_E_ARG;
     if (nbytes != c->slot_bytes) return MOE_E_SIZE;
@@ -316,7 +266,7 @@ int copy_in_blob(moe_ctx* c, uint8_t* dst_slot, const void* blob, size_t nbytes)
     return hip_ok(hipStreamSynchronize(c->stream));
 }
 
-int requant_into(moe_ctx* c, uint8_t* dst_slot, int src, const void* Wg, const void* Wu,
+int requant_into_impl(moe_ctx* c, uint8_t* dst_slot, int src, const void* Wg, const void* Wu,
                  const void* Wd, const float* sg, const float* su, const float* sd)
 {
     if (!Wg || !Wu || !Wd) return MOE_E_ARG;
@@ -349,7 +299,7 @@ int requant_into(moe_ctx* c, uint8_t* dst_slot, int src, const void* Wg, const v
     return hip_ok(launch_blob_to_slot(b, dst_slot, c->cfg.wfmt, (int)H, (int)I, c->stream));
 }
 
-int import_into(moe_ctx* c, uint8_t* dst_slot, const uint8_t* qg, const uint8_t* qu,
+int import_into_impl(moe_ctx* c, uint8_t* dst_slot, const uint8_t* qg, const uint8_t* qu,
                 const uint8_t* qd, const float* sg, const float* su, const float* sd)
 {
     if (c->cfg.wfmt != MOE_W_INT4_ROW) return MOE_E_UNSUPPORTED;
@@ -366,6 +316,30 @@ int import_into(moe_ctx* c, uint8_t* dst_slot, const uint8_t* qg, const uint8_t*
     if (launch_container_to_slot(b, dst_slot, (int)H, (int)I, c->stream) != hipSuccess)
         return MOE_E_HIP;
     return hip_ok(hipStreamSynchronize(c->stream));
+}
+
+// The three slot writers, ordered against asynchronous loads into the same slot.
+int copy_in_blob(moe_ctx* c, uint8_t* dst, const void* blob, size_t nbytes)
+{
+    int rc = slot_compute_ready(c, dst);
+    rc = rc ? rc : copy_in_blob_impl(c, dst, blob, nbytes);
+    return rc ? rc : slot_compute_written(c, dst);
+}
+
+int requant_into(moe_ctx* c, uint8_t* dst, int src, const void* Wg, const void* Wu,
+                 const void* Wd, const float* sg, const float* su, const float* sd)
+{
+    int rc = slot_compute_ready(c, dst);
+    rc = rc ? rc : requant_into_impl(c, dst, src, Wg, Wu, Wd, sg, su, sd);
+    return rc ? rc : slot_compute_written(c, dst);
+}
+
+int import_into(moe_ctx* c, uint8_t* dst, const uint8_t* qg, const uint8_t* qu,
+                const uint8_t* qd, const float* sg, const float* su, const float* sd)
+{
+    int rc = slot_compute_ready(c, dst);
+    rc = rc ? rc : import_into_impl(c, dst, qg, qu, qd, sg, su, sd);
+    return rc ? rc : slot_compute_written(c, dst);
 }
 
 }  // namespace
@@ -470,6 +444,7 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
         if (e == hipSuccess) e = hipDeviceSynchronize();
         if (e != hipSuccess) rc = MOE_E_HIP;
     }
+    rc = rc ? rc : residency_init(c);
     if (rc != MOE_OK) {
         moe_destroy(c);
         return rc;
@@ -482,6 +457,7 @@ void moe_destroy(moe_ctx* c)
 {
     if (!c) return;
     hipStreamSynchronize(c->stream);
+    residency_destroy(c);
     for (hipEvent_t e : c->events) hipEventDestroy(e);
     for (void* p : c->allocs) hipFree(p);
     delete c;
@@ -582,24 +558,13 @@ int moe_import_shared(moe_ctx* c, int layer, int s, const uint8_t* qg, const uin
                        qu, qd, sg, su, sd);
 }
 
-int moe_map_expert(moe_ctx* c, int layer, int expert_id, int slot)
-{
-    if (!c || layer < 0 || layer >= c->cfg.n_layers || expert_id < 0 ||
-        expert_id >= c->cfg.n_experts)
-        return MOE_E_ARG;
-    if (slot < -1 || slot >= c->cfg.n_slots) return MOE_E_SLOT;
-    const size_t i = (size_t)layer * c->cfg.n_experts + expert_id;
-    c->tbl_host[i] = slot;
-    hipError_t e = hipMemcpyAsync(c->tbl + i, &c->tbl_host[i], 4, hipMemcpyHostToDevice, c->stream);
-    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
-    return hip_ok(e);
-}
-
 int moe_read_slot(moe_ctx* c, int slot, void* dst, size_t nbytes)
 {
     if (!c || !dst) return MOE_E_ARG;
     if (slot < 0 || slot >= c->cfg.n_slots) return MOE_E_SLOT;
     if (nbytes != c->slot_bytes) return MOE_E_SIZE;
+    const int rc = slot_compute_ready(c, c->pool + (size_t)slot * c->slot_bytes);
+    if (rc) return rc;
     hipError_t e = launch_slot_to_blob(c->pool + (size_t)slot * c->slot_bytes, c->staging,
                                        c->cfg.wfmt, c->cfg.hidden, c->cfg.inter, c->stream);
     if (e == hipSuccess) e = hipMemcpyAsync(dst, c->staging, nbytes, hipMemcpyDefault, c->stream);

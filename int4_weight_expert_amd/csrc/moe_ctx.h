@@ -1,0 +1,89 @@
+// moe_ctx.h -- the library context (internal; the public ABI is include/moe.h).
+#pragma once
+
+#include <vector>
+
+#include "moe_internal.h"
+
+struct moe_ctx {
+    moe_config cfg;
+    hipStream_t stream = nullptr;
+    int device = 0;
+    size_t slot_bytes = 0;
+    int Epad = 0;
+    uint8_t* pool = nullptr;
+    float* wr = nullptr;
+    float* bias = nullptr;
+    int* tbl = nullptr;
+    std::vector<int> tbl_host;
+    uint8_t* shared = nullptr;
+    uint8_t* staging = nullptr;
+    // workspace
+    float* part = nullptr;
+    float* tpart = nullptr;
+    float* logits = nullptr;
+    int32_t* ids = nullptr;
+    float* wts = nullptr;
+    moe::TokStat* tok = nullptr;
+    uint4* xq = nullptr;
+    float2* xsc = nullptr;
+    int32_t* cnt = nullptr;
+    int32_t* off = nullptr;
+    int32_t* perm = nullptr;
+    int32_t* active = nullptr;
+    int32_t* n_active = nullptr;
+    moe::Group* groups = nullptr;
+    int32_t* n_groups = nullptr;
+    uint4* hq = nullptr;
+    float2* hsc = nullptr;
+    float* gpart = nullptr;
+    size_t gpart_bytes = 0;
+    float* ypart = nullptr;
+    size_t ypart_bytes = 0;
+    float2* xrow = nullptr;
+    float2* hrow = nullptr;
+    float* hbuf = nullptr;
+    int2* tiles = nullptr;
+    int32_t* n_tiles = nullptr;
+    uint32_t* counters = nullptr;
+    uint32_t* status = nullptr;
+    size_t status_words = 0;
+    int gemm_min_tokens = 64;
+    int lds_max = 65536;
+    hipError_t last_err = hipSuccess;
+    // timing
+    bool timing = false;
+    std::vector<hipEvent_t> events;  // marker pool, reused after each summary
+    std::vector<const char*> names;  // per marker: kernel that follows; nullptr = end of a forward
+    int n_marks = 0;
+    std::vector<void*> allocs;
+    // residency (moe_stage.hip): asynchronous loads on a copy stream of the
+    // library's own, ordered against the compute stream per slot
+    hipStream_t copy_stream = nullptr;
+    std::vector<int> slot_refs;            // slot-table entries naming each slot
+    std::vector<hipEvent_t> copy_done;     // per slot: its last asynchronous load
+    std::vector<hipEvent_t> slot_free;     // per slot: compute-stream point after its last use
+    std::vector<uint8_t> copy_pending;     // copy_done recorded, not yet waited by the compute stream
+    std::vector<uint8_t> free_pending;     // slot_free recorded, not yet waited by the copy stream
+    int stage_first = -1, stage_per_layer = 0;
+    std::vector<int> stage_ids;            // [layer][per_layer] expert held by each staging slot
+    std::vector<int64_t> stage_used;       // step at which that expert was last wanted
+    int64_t stage_step = 0;
+};
+
+namespace moe {
+
+int hip_ok(hipError_t e);
+int hip_rc(moe_ctx* c, hipError_t e);  // records a failing HIP call for moe_last_error
+
+// Residency bookkeeping shared by the synchronous and asynchronous paths.
+int residency_init(moe_ctx* c);
+void residency_destroy(moe_ctx* c);
+// Before the compute stream writes or reads a slot's bytes itself: wait for
+// an asynchronous load into it that the compute stream has not waited for.
+int slot_compute_ready(moe_ctx* c, uint8_t* dst);
+// After the compute stream has enqueued a write into a slot: later
+// asynchronous loads into that slot wait for it.
+int slot_compute_written(moe_ctx* c, uint8_t* dst);
+
+}  // namespace moe

@@ -81,6 +81,36 @@ class MoeLayer:
         M._check("moe_import_shared",
                  M.moe_import_shared(self.ctx, layer, s, qg, qu, qd, sg, su, sd), self.ctx)
 
+    # ---- residency: asynchronous loads, staged slots, whole layers ----------
+    def image(self, blob) -> np.ndarray:
+        """Slot image of a host blob (the bytes an asynchronous load copies)."""
+        return M.moe_blob_to_image(self.fmt, self.H, self.I, blob)
+
+    def load_image_async(self, slot: int, image) -> None:
+        M._check("moe_load_image_async",
+                 M.moe_load_image_async(self.ctx, slot, image, _nbytes(image)), self.ctx)
+
+    def map_async(self, layer: int, expert_ids, slots) -> None:
+        M._check("moe_map_experts_async",
+                 M.moe_map_experts_async(self.ctx, layer, expert_ids, slots), self.ctx)
+
+    def load_layer_async(self, layer: int, first_slot: int, n: int, images) -> None:
+        M._check("moe_load_layer_async",
+                 M.moe_load_layer_async(self.ctx, layer, first_slot, n, images, _nbytes(images)),
+                 self.ctx)
+
+    def sync_copies(self) -> None:
+        M._check("moe_sync_copies", M.moe_sync_copies(self.ctx), self.ctx)
+
+    def set_staging(self, first_slot: int, per_layer: int) -> None:
+        M._check("moe_set_staging", M.moe_set_staging(self.ctx, first_slot, per_layer), self.ctx)
+
+    def stage(self, layer: int, expert_ids, images) -> int:
+        """Staged executor step: returns how many images were loaded."""
+        rc, n = M.moe_stage_experts(self.ctx, layer, expert_ids, images)
+        M._check("moe_stage_experts", rc, self.ctx)
+        return n
+
     def map(self, layer: int, expert_id: int, slot: int) -> None:
         M._check("moe_map_expert", M.moe_map_expert(self.ctx, layer, expert_id, slot))
 

@@ -22,6 +22,7 @@ MOE_E_NOT_RESIDENT = -5
 MOE_E_HIP = -6
 MOE_E_UNSUPPORTED = -7
 MOE_E_RANGE = -8
+MOE_E_BUSY = -9
 MOE_W_INT4_ROW = 1
 MOE_SCORE_SIGMOID, MOE_SCORE_SOFTMAX = 0, 1
 MOE_W_INT4_AFFINE_G64 = 2
@@ -29,7 +30,7 @@ MOE_SRC_F32, MOE_SRC_BF16, MOE_SRC_FP8_E4M3 = 0, 1, 2
 
 ERROR_NAMES = {0: "MOE_OK", -1: "MOE_E_ARG", -2: "MOE_E_NOMEM", -3: "MOE_E_SIZE",
                -4: "MOE_E_SLOT", -5: "MOE_E_NOT_RESIDENT", -6: "MOE_E_HIP",
-               -7: "MOE_E_UNSUPPORTED", -8: "MOE_E_RANGE"}
+               -7: "MOE_E_UNSUPPORTED", -8: "MOE_E_RANGE", -9: "MOE_E_BUSY"}
 
 EXPORTS = ["moe_layer_create", "moe_destroy", "moe_set_stream", "moe_expert_bytes",
            "moe_set_router", "moe_load_expert", "moe_pack_expert", "moe_set_shared",
@@ -37,7 +38,10 @@ EXPORTS = ["moe_layer_create", "moe_destroy", "moe_set_stream", "moe_expert_byte
            "moe_forward_residual", "moe_route", "moe_status", "moe_set_gemm_min_tokens",
            "moe_set_timing", "moe_timing_summary", "moe_last_error", "moe_pack_int4_rows", "moe_pack_affine_g64",
            "moe_bucket", "moe_requant_expert", "moe_import_expert", "moe_requant_shared",
-           "moe_import_shared", "moe_requant_int4_rows", "moe_requant_affine_g64"]
+           "moe_import_shared", "moe_requant_int4_rows", "moe_requant_affine_g64",
+           "moe_map_experts_async", "moe_load_image_async", "moe_load_layer_async",
+           "moe_sync_copies", "moe_set_staging", "moe_stage_experts", "moe_sticky_plan",
+           "moe_image_bytes", "moe_blob_to_image"]
 
 
 class moe_config(ctypes.Structure):
@@ -96,6 +100,15 @@ def lib() -> ctypes.CDLL:
             "moe_import_shared": ([vp, i32, i32, vp, vp, vp, vp, vp, vp], i32),
             "moe_requant_int4_rows": ([vp, i32, vp, i64, i64, vp, vp, vp], i32),
             "moe_requant_affine_g64": ([vp, i32, vp, i64, i64, vp, vp, vp], i32),
+            "moe_map_experts_async": ([vp, i32, i32, vp, vp], i32),
+            "moe_load_image_async": ([vp, i32, vp, sz], i32),
+            "moe_load_layer_async": ([vp, i32, i32, i32, vp, sz], i32),
+            "moe_sync_copies": ([vp], i32),
+            "moe_set_staging": ([vp, i32, i32], i32),
+            "moe_stage_experts": ([vp, i32, i32, vp, vp, ctypes.POINTER(i32)], i32),
+            "moe_sticky_plan": ([vp, vp, i32, vp, i32, vp, vp], i32),
+            "moe_image_bytes": ([i32, i32, i32], sz),
+            "moe_blob_to_image": ([i32, i32, i32, vp, sz, vp], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -261,6 +274,61 @@ def moe_requant_int4_rows(w, src, sinv, O, I, q, s, stream=0) -> int:
 def moe_requant_affine_g64(w, src, sinv, O, I, q, scmn, stream=0) -> int:
     return lib().moe_requant_affine_g64(_ptr(w), src, _ptr(sinv), O, I, _ptr(q), _ptr(scmn),
                                         stream)
+
+
+def moe_map_experts_async(ctx, layer, expert_ids, slots) -> int:
+    ids = (ctypes.c_int * len(expert_ids))(*[int(v) for v in expert_ids])
+    sl = (ctypes.c_int * len(slots))(*[int(v) for v in slots])
+    return lib().moe_map_experts_async(ctx, layer, len(expert_ids), ids, sl)
+
+
+def moe_load_image_async(ctx, slot, image, nbytes) -> int:
+    return lib().moe_load_image_async(ctx, slot, _ptr(image), nbytes)
+
+
+def moe_load_layer_async(ctx, layer, first_slot, n, images, nbytes) -> int:
+    return lib().moe_load_layer_async(ctx, layer, first_slot, n, _ptr(images), nbytes)
+
+
+def moe_sync_copies(ctx) -> int:
+    return lib().moe_sync_copies(ctx)
+
+
+def moe_set_staging(ctx, first_slot, per_layer) -> int:
+    return lib().moe_set_staging(ctx, first_slot, per_layer)
+
+
+def moe_stage_experts(ctx, layer, expert_ids, images) -> tuple[int, int]:
+    """images: one pointer-like per id (None allowed where no load is needed)."""
+    n = len(expert_ids)
+    ids = (ctypes.c_int * n)(*[int(v) for v in expert_ids])
+    ptrs = (ctypes.c_void_p * n)(*[_ptr(im) for im in images])
+    nl = ctypes.c_int(0)
+    rc = lib().moe_stage_experts(ctx, layer, n, ids, ptrs, ctypes.byref(nl))
+    return rc, nl.value
+
+
+def moe_sticky_plan(held, last_used, want):
+    """(n_loads, slot_of, load) for the staged executor's slot choice."""
+    import numpy as np
+    held = np.ascontiguousarray(held, dtype=np.int32)
+    last_used = np.ascontiguousarray(last_used, dtype=np.int64)
+    want = np.ascontiguousarray(want, dtype=np.int32)
+    slot_of = np.empty(len(want), dtype=np.int32)
+    load = np.empty(len(want), dtype=np.int32)
+    n = lib().moe_sticky_plan(held.ctypes.data, last_used.ctypes.data, len(held),
+                              want.ctypes.data, len(want), slot_of.ctypes.data, load.ctypes.data)
+    return n, slot_of, load
+
+
+def moe_blob_to_image(wfmt, hidden, inter, blob):
+    """Slot image (numpy uint8) of a host blob."""
+    import numpy as np
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    image = np.empty_like(blob)
+    _check("moe_blob_to_image", lib().moe_blob_to_image(wfmt, hidden, inter, blob.ctypes.data,
+                                                        blob.nbytes, image.ctypes.data))
+    return image
 
 
 def moe_bucket(ids, T, K, E, cnt, off, perm, active, n_active, stream=0) -> int:
