@@ -265,6 +265,119 @@ def bench_requant(torch, result, n_experts: int = 32, steps: int = 256):
     torch.cuda.empty_cache()
 
 
+def bench_staged(torch, result, n_layers: int = 8, per_layer: int = 16, n_tokens: int = 64):
+    """The staged executor on the Edge0 shape (H=2048, I=512, 256 affine
+    experts, top-4): every layer-step stages the experts its token routes to
+    (sticky slots, loads of slot images from pinned host memory on the copy
+    stream) and runs the layer.  Reported beside it: the same loads alone
+    and the same forwards with every expert resident, so the overlap of
+    copies and compute shows."""
+    import numpy as np
+    import synth
+    from int4_weight_expert_amd import moe as M
+    from int4_weight_expert_amd.layer import MoeLayer
+    cfg = synth.CONFIGS["edge0_decode"]
+    H, I, E, K, L = cfg.H, cfg.I, cfg.E, cfg.K, n_layers
+    log(f"[bench] staged: building {L} x {E} Edge0 slot images in pinned memory")
+    src = MoeLayer(H, I, E, K, 0, 1, cfg.fmt, n_slots=1, max_tokens=1)
+    nb = src.expert_bytes
+    images = torch.empty((L, E, nb), dtype=torch.uint8, pin_memory=True)
+    n = I * H
+    w = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(3)]
+    st = torch.cuda.current_stream().cuda_stream
+    for l in range(L):
+        for e in range(E):
+            for t, k in enumerate(synth.expert_keys(cfg, l, e)):
+                synth.gpu_fill_gauss(w[t].data_ptr(), n, k, cfg.sigma_w, 0, st)
+            src.pack_expert(0, *w)
+            images[l, e].numpy()[:] = src.image(src.read_slot(0))
+    src.close()
+    del w
+    # routing of every (token, layer) from the routers alone
+    ml = MoeLayer(H, I, E, K, 0, L, cfg.fmt, n_slots=L * per_layer, max_tokens=n_tokens)
+    full = MoeLayer(H, I, E, K, 0, L, cfg.fmt, n_slots=L * E, max_tokens=n_tokens)
+    xs = []
+    ids = np.empty((L, n_tokens, K), dtype=np.int32)
+    for l in range(L):
+        Wr, br = synth.router_weight(cfg, l), synth.router_bias(cfg, l)
+        ml.set_router(l, Wr, br)
+        full.set_router(l, Wr, br)
+        x = torch.from_numpy(synth.tokens(cfg, T=n_tokens, stream=500 + l)).cuda()
+        xs.append(x)
+        ids[l] = ml.route(x, l)[0].cpu().numpy()
+        full.load_layer_async(l, l * E, E, images[l])
+    full.sync_copies()
+    ptrs = [[images[l, e].data_ptr() for e in range(E)] for l in range(L)]
+    outs = [torch.empty((1, H), dtype=torch.float32, device="cuda") for _ in range(L)]
+
+    def staged(run_forward=True, run_stage=True, ctx=ml):
+        loads = 0
+        for t in range(n_tokens):
+            for l in range(L):
+                want = sorted(set(ids[l, t].tolist()))
+                if run_stage:
+                    loads += ctx.stage(l, want, [ptrs[l][e] for e in want])
+                if run_forward:
+                    ctx.forward(xs[l][t:t + 1], l, outs[l])
+        return loads
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        r = fn()
+        t_host = time.perf_counter() - t0
+        ml.sync_copies()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, t_host, r
+
+    def reset():
+        ml.set_staging(0, per_layer)
+        for l in range(L):     # the staged slots leave the table: the next run starts cold
+            ml.map_async(l, list(range(E)), [-1] * E)
+        torch.cuda.synchronize()
+
+    steps = n_tokens * L
+    ml.set_staging(0, per_layer)
+    timed(lambda: staged())                       # warm-up (events, first touches)
+    reset()
+    t_both, t_host, loads = timed(lambda: staged())
+    t_comp, t_host_c, _ = timed(lambda: staged(run_stage=False, ctx=full))
+    # the same number of slot-image copies as raw pinned copies on two streams
+    dst = torch.empty((2, nb), dtype=torch.uint8, device="cuda")
+    ss = [torch.cuda.Stream(), torch.cuda.Stream()]
+    flat = images.view(L * E, nb)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(loads):
+        with torch.cuda.stream(ss[i % 2]):
+            dst[i % 2].copy_(flat[(i * 97) % (L * E)], non_blocking=True)
+    torch.cuda.synchronize()
+    t_plain = time.perf_counter() - t0
+    del dst
+    bytes_loaded = loads * nb
+    out = {
+        "layers": L, "tokens": n_tokens, "per_layer_slots": per_layer, "expert_bytes": nb,
+        "loads_per_layer_step": loads / steps, "sticky_hit_rate": 1 - loads / (steps * K),
+        "us_per_layer_staged": t_both / steps * 1e6,
+        "us_per_layer_resident": t_comp / steps * 1e6,
+        "us_per_layer_plain_copies": t_plain / steps * 1e6,
+        "host_enqueue_us_per_layer_staged": t_host / steps * 1e6,
+        "host_enqueue_us_per_layer_resident": t_host_c / steps * 1e6,
+        "h2d_gbps_staged": bytes_loaded / t_both / 1e9,
+        "h2d_gbps_plain_copies": bytes_loaded / t_plain / 1e9,
+        "copy_hidden_frac": max(0.0, min(1.0, (t_plain + t_comp - t_both) / min(t_plain, t_comp))),
+    }
+    result["extra"]["staged_edge0"] = out
+    log(f"[bench] staged: {out['us_per_layer_staged']:.1f} us/layer-step (host enqueue "
+        f"{out['host_enqueue_us_per_layer_staged']:.1f}; plain copies "
+        f"{out['us_per_layer_plain_copies']:.1f}, resident {out['us_per_layer_resident']:.1f}), "
+        f"{out['loads_per_layer_step']:.2f} loads/step, {out['h2d_gbps_staged']:.1f} GB/s H2D")
+    ml.close()
+    full.close()
+    del images, ml, full
+    torch.cuda.empty_cache()
+
+
 def bench_chain(torch, name, steps, result):
     """Chained residual layers (x <- x + moe(rmsnorm(x))): per-layer time."""
     import numpy as np
@@ -447,7 +560,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=16)
     ap.add_argument("--only", choices=["decode", "verify", "edge0", "edge0_k8", "prefill", "grouped",
-                                       "softmax", "requant"],
+                                       "softmax", "requant", "staged"],
                     help="run one workload only (for profiling); the JSON line then "
                          "carries that workload in extra")
     ap.add_argument("--copy-probe", action="store_true",
@@ -480,7 +593,8 @@ def main():
          "prefill": lambda: bench_prefill(torch, 20, result),
          "grouped": lambda: bench_rotated(torch, "glm_decode_grouped", 200, result),
          "softmax": lambda: bench_rotated(torch, "glm_decode_softmax", 200, result),
-         "requant": lambda: bench_requant(torch, result)}[args.only]()
+         "requant": lambda: bench_requant(torch, result),
+         "staged": lambda: bench_staged(torch, result)}[args.only]()
         print(json.dumps(result), flush=True)
         return
     bench_decode(torch, args, result)
@@ -493,6 +607,7 @@ def main():
         bench_rotated(torch, "glm_decode_grouped", 200, result)
         bench_rotated(torch, "glm_decode_softmax", 200, result)
         bench_requant(torch, result)
+        bench_staged(torch, result)
         bench_prefill(torch, 20, result)
     if not args.no_cpu:
         log("[bench] cpu baseline (oracle)")

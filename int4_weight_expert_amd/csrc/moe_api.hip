@@ -574,12 +574,14 @@ int moe_read_slot(moe_ctx* c, int slot, void* dst, size_t nbytes)
 
 int moe_forward(moe_ctx* c, const float* x, int T, int layer, float* out)
 {
-    return run_forward(c, x, T, layer, out, 0);
+    const int rc = run_forward(c, x, T, layer, out, 0);
+    return rc ? rc : forward_done(c, layer);
 }
 
 int moe_forward_residual(moe_ctx* c, float* x, int T, int layer)
 {
-    return run_forward(c, x, T, layer, x, 1);
+    const int rc = run_forward(c, x, T, layer, x, 1);
+    return rc ? rc : forward_done(c, layer);
 }
 
 int moe_route(moe_ctx* c, const float* x, int T, int layer, int32_t* ids, float* w)

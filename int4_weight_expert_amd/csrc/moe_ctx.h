@@ -57,14 +57,24 @@ struct moe_ctx {
     std::vector<const char*> names;  // per marker: kernel that follows; nullptr = end of a forward
     int n_marks = 0;
     std::vector<void*> allocs;
-    // residency (moe_stage.hip): asynchronous loads on a copy stream of the
+    // residency (moe_stage.hip): asynchronous loads on copy streams of the
     // library's own, ordered against the compute stream per slot
-    hipStream_t copy_stream = nullptr;
+    static constexpr int kCopyStreams = 2;
+    hipStream_t copy_streams[kCopyStreams] = {nullptr, nullptr};
+    int next_copy = 0;
     std::vector<int> slot_refs;            // slot-table entries naming each slot
     std::vector<hipEvent_t> copy_done;     // per slot: its last asynchronous load
-    std::vector<hipEvent_t> slot_free;     // per slot: compute-stream point after its last use
+    std::vector<hipEvent_t> slot_free;     // per slot: compute-stream point after a write by it
     std::vector<uint8_t> copy_pending;     // copy_done recorded, not yet waited by the compute stream
-    std::vector<uint8_t> free_pending;     // slot_free recorded, not yet waited by the copy stream
+    std::vector<uint8_t> free_pending;     // slot_free recorded, not yet waited by a load
+    std::vector<std::vector<int>> slot_layers;  // layers whose table named the slot since its load
+    std::vector<uint64_t> copy_seq;        // per slot: order of its last load
+    std::vector<uint8_t> copy_sid;         // per slot: copy stream of its last load
+    uint64_t copy_counter = 0;
+    std::vector<std::pair<int, int>> pending_ups;  // table updates not yet launched
+    bool track_fwd = false;                // record layer_fwd after each forward
+    std::vector<hipEvent_t> layer_fwd;     // per layer: after its latest forward
+    std::vector<uint8_t> layer_fwd_rec;    // layer_fwd recorded at least once
     int stage_first = -1, stage_per_layer = 0;
     std::vector<int> stage_ids;            // [layer][per_layer] expert held by each staging slot
     std::vector<int64_t> stage_used;       // step at which that expert was last wanted
@@ -85,5 +95,7 @@ int slot_compute_ready(moe_ctx* c, uint8_t* dst);
 // After the compute stream has enqueued a write into a slot: later
 // asynchronous loads into that slot wait for it.
 int slot_compute_written(moe_ctx* c, uint8_t* dst);
+// After a forward of a layer is enqueued (reads the slots its table names).
+int forward_done(moe_ctx* c, int layer);
 
 }  // namespace moe

@@ -1,6 +1,6 @@
 // moe_stage.hip -- expert residency around the slot pool: the slot table
 // (synchronous and asynchronous updates), asynchronous loads of slot images
-// from host memory on a copy stream of the library's own, the staged
+// from host memory on copy streams of the library's own, the staged
 // executor's sticky slots, whole-layer loads, and the slot image on the host.
 //
 // Sources, cited by page title and section:
@@ -13,15 +13,20 @@
 //   "惊呆了！25GB 内存上运行 GLM 5.2 744B 模型" §13: an expert's three
 //     matrices stored contiguously are read with one read into its slab.
 //
-// Ordering.  Loads run on the copy stream; the forward runs on the compute
-// stream.  Per slot, the library keeps
+// Ordering.  Loads run on two copy streams used in turn; the forward runs on
+// the compute stream.  Per slot, the library keeps
 //   - copy_done: recorded on the copy stream after a load into the slot;
 //     the compute stream waits for it before the table names the slot or
 //     before it touches the slot's bytes itself;
-//   - slot_free: recorded on the compute stream when the slot's last table
-//     entry goes, or after the compute stream wrote the slot; a later load
-//     into the slot waits for it, so a forward enqueued earlier that may
-//     still read the old expert finishes first.
+//   - the layers whose table named the slot since its last load: a load
+//     into the slot waits for the latest forward of each of them (an event
+//     recorded after every forward once asynchronous loads are in use), so
+//     a forward that may still read the old expert finishes first, and a
+//     load never waits for compute enqueued after the slot left the table;
+//     where a layer had no recorded forward, the load waits for everything
+//     enqueued on the compute stream so far;
+//   - slot_free: recorded on the compute stream after the compute stream
+//     wrote the slot itself (synchronous loads); a later load waits for it.
 // A slot still named by the table cannot take an asynchronous load.
 #include <string.h>
 
@@ -65,30 +70,48 @@ int slot_index(const moe_ctx* c, const uint8_t* p)
     return (int)(off / c->slot_bytes);
 }
 
-// Table updates (entry layer*E + id -> slot, -1 = unmap), applied on the
-// compute stream in stream order; later entries for the same index win.
-int apply_updates(moe_ctx* c, const std::vector<std::pair<int, int>>& ups_in)
+// Table updates (entry layer*E + id -> slot, -1 = unmap).  record_update
+// keeps the host's view (table mirror, reference counts, the layers that
+// named a slot) at once; flush_updates makes the compute stream wait for
+// the loads into newly named slots (once per copy stream: its latest such
+// load, since a stream's copies finish in order; none if already done) and
+// writes the device table, in stream order, later entries winning.
+void record_update(moe_ctx* c, int idx, int slot)
 {
+    const int old = c->tbl_host[idx];
+    if (old == slot) return;
+    if (old >= 0) --c->slot_refs[old];
+    if (slot >= 0) {
+        c->slot_refs[slot]++;
+        const int layer = idx / c->cfg.n_experts;
+        auto& v = c->slot_layers[slot];
+        if (std::find(v.begin(), v.end(), layer) == v.end()) v.push_back(layer);
+    }
+    c->tbl_host[idx] = slot;
+    c->pending_ups.push_back({idx, slot});
+}
+
+int flush_updates(moe_ctx* c)
+{
+    if (c->pending_ups.empty()) return MOE_OK;
     std::map<int, int> last;
-    for (const auto& u : ups_in) last[u.first] = u.second;
-    std::vector<std::pair<int, int>> ups;
-    std::vector<int> freed;
+    for (const auto& u : c->pending_ups) last[u.first] = u.second;
+    c->pending_ups.clear();
+    int wait_slot[moe_ctx::kCopyStreams];
+    for (int& w : wait_slot) w = -1;
     for (const auto& u : last) {
-        const int old = c->tbl_host[u.first];
-        if (old == u.second) continue;
-        ups.push_back(u);
-        if (old >= 0 && --c->slot_refs[old] == 0) freed.push_back(old);
-        if (u.second >= 0) c->slot_refs[u.second]++;
-        c->tbl_host[u.first] = u.second;
-    }
-    for (const auto& u : ups) {
         const int s = u.second;
-        if (s >= 0 && c->copy_pending[s]) {
-            const hipError_t e = hipStreamWaitEvent(c->stream, c->copy_done[s], 0);
-            if (e != hipSuccess) return hip_rc(c, e);
-            c->copy_pending[s] = 0;
-        }
+        if (s < 0 || !c->copy_pending[s]) continue;
+        int& w = wait_slot[c->copy_sid[s]];
+        if (w < 0 || c->copy_seq[s] > c->copy_seq[w]) w = s;
+        c->copy_pending[s] = 0;
     }
+    for (int w : wait_slot) {
+        if (w < 0 || hipEventQuery(c->copy_done[w]) == hipSuccess) continue;
+        const hipError_t e = hipStreamWaitEvent(c->stream, c->copy_done[w], 0);
+        if (e != hipSuccess) return hip_rc(c, e);
+    }
+    std::vector<std::pair<int, int>> ups(last.begin(), last.end());
     for (size_t i = 0; i < ups.size(); i += kTblBatch) {
         TblUpd t{};
         t.n = (int)std::min(ups.size() - i, (size_t)kTblBatch);
@@ -100,14 +123,63 @@ int apply_updates(moe_ctx* c, const std::vector<std::pair<int, int>>& ups_in)
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return hip_rc(c, e);
     }
-    for (int s : freed) {
-        if (c->slot_refs[s] != 0) continue;
-        hipEvent_t ev = slot_event(c->slot_free, s);
-        if (!ev) return MOE_E_HIP;
-        const hipError_t e = hipEventRecord(ev, c->stream);
+    return MOE_OK;
+}
+
+int apply_updates(moe_ctx* c, const std::vector<std::pair<int, int>>& ups)
+{
+    for (const auto& u : ups) record_update(c, u.first, u.second);
+    return flush_updates(c);
+}
+
+// The copy stream waits until no forward that may read the slot's old
+// expert is left to run.
+int wait_slot_readers(moe_ctx* c, int slot, hipStream_t cs)
+{
+    hipError_t e = hipSuccess;
+    bool tail = false;
+    for (int layer : c->slot_layers[slot]) {
+        if (!c->layer_fwd_rec[layer]) {
+            tail = true;
+            continue;
+        }
+        if (hipEventQuery(c->layer_fwd[layer]) == hipSuccess) continue;  // already done
+        e = hipStreamWaitEvent(cs, c->layer_fwd[layer], 0);
         if (e != hipSuccess) return hip_rc(c, e);
-        c->free_pending[s] = 1;
     }
+    if (tail) {
+        hipEvent_t ev = slot_event(c->slot_free, slot);
+        if (!ev) return MOE_E_HIP;
+        e = hipEventRecord(ev, c->stream);
+        if (e != hipSuccess) return hip_rc(c, e);
+        c->free_pending[slot] = 1;
+    }
+    if (c->free_pending[slot]) {
+        e = hipStreamWaitEvent(cs, c->slot_free[slot], 0);
+        if (e != hipSuccess) return hip_rc(c, e);
+        c->free_pending[slot] = 0;
+    }
+    c->slot_layers[slot].clear();
+    return MOE_OK;
+}
+
+int next_copy_stream(moe_ctx* c)
+{
+    c->track_fwd = true;
+    const int s = c->next_copy;
+    c->next_copy = (c->next_copy + 1) % moe_ctx::kCopyStreams;
+    return s;
+}
+
+int note_copy(moe_ctx* c, int slot, int sid)
+{
+    hipEvent_t ev = slot_event(c->copy_done, slot);
+    if (!ev) return MOE_E_HIP;
+    const hipError_t e = hipEventRecord(ev, c->copy_streams[sid]);
+    if (e != hipSuccess) return hip_rc(c, e);
+    c->copy_pending[slot] = 1;
+    c->copy_sid[slot] = (uint8_t)sid;
+    c->copy_seq[slot] = ++c->copy_counter;
     return MOE_OK;
 }
 
@@ -115,21 +187,14 @@ int apply_updates(moe_ctx* c, const std::vector<std::pair<int, int>>& ups_in)
 int load_async(moe_ctx* c, int slot, const void* image)
 {
     if (c->slot_refs[slot] > 0) return MOE_E_BUSY;
-    hipError_t e = hipSuccess;
-    if (c->free_pending[slot]) {
-        e = hipStreamWaitEvent(c->copy_stream, c->slot_free[slot], 0);
-        if (e != hipSuccess) return hip_rc(c, e);
-        c->free_pending[slot] = 0;
-    }
-    e = hipMemcpyAsync(c->pool + (size_t)slot * c->slot_bytes, image, c->slot_bytes,
-                       hipMemcpyDefault, c->copy_stream);
+    const int sid = next_copy_stream(c);
+    hipStream_t cs = c->copy_streams[sid];
+    const int rc = wait_slot_readers(c, slot, cs);
+    if (rc) return rc;
+    const hipError_t e = hipMemcpyAsync(c->pool + (size_t)slot * c->slot_bytes, image,
+                                        c->slot_bytes, hipMemcpyDefault, cs);
     if (e != hipSuccess) return hip_rc(c, e);
-    hipEvent_t ev = slot_event(c->copy_done, slot);
-    if (!ev) return MOE_E_HIP;
-    e = hipEventRecord(ev, c->copy_stream);
-    if (e != hipSuccess) return hip_rc(c, e);
-    c->copy_pending[slot] = 1;
-    return MOE_OK;
+    return note_copy(c, slot, sid);
 }
 
 size_t image_bytes(int fmt, int64_t H, int64_t I)
@@ -152,28 +217,52 @@ int residency_init(moe_ctx* c)
     c->slot_free.assign(n, nullptr);
     c->copy_pending.assign(n, 0);
     c->free_pending.assign(n, 0);
-    return hip_ok(hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking));
+    c->slot_layers.assign(n, {});
+    c->copy_seq.assign(n, 0);
+    c->copy_sid.assign(n, 0);
+    c->layer_fwd.assign(c->cfg.n_layers, nullptr);
+    c->layer_fwd_rec.assign(c->cfg.n_layers, 0);
+    for (auto& s : c->copy_streams) {
+        const hipError_t e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+        if (e != hipSuccess) return hip_ok(e);
+    }
+    return MOE_OK;
 }
 
 void residency_destroy(moe_ctx* c)
 {
-    if (c->copy_stream) hipStreamSynchronize(c->copy_stream);
+    for (auto& s : c->copy_streams)
+        if (s) hipStreamSynchronize(s);
     for (hipEvent_t e : c->copy_done)
         if (e) hipEventDestroy(e);
     for (hipEvent_t e : c->slot_free)
         if (e) hipEventDestroy(e);
-    if (c->copy_stream) hipStreamDestroy(c->copy_stream);
-    c->copy_stream = nullptr;
+    for (hipEvent_t e : c->layer_fwd)
+        if (e) hipEventDestroy(e);
+    for (auto& s : c->copy_streams) {
+        if (s) hipStreamDestroy(s);
+        s = nullptr;
+    }
+}
+
+int forward_done(moe_ctx* c, int layer)
+{
+    if (!c->track_fwd) return MOE_OK;
+    hipEvent_t ev = slot_event(c->layer_fwd, layer);
+    if (!ev) return MOE_E_HIP;
+    const hipError_t e = hipEventRecord(ev, c->stream);
+    if (e != hipSuccess) return hip_rc(c, e);
+    c->layer_fwd_rec[layer] = 1;
+    return MOE_OK;
 }
 
 int slot_compute_ready(moe_ctx* c, uint8_t* dst)
 {
     const int s = slot_index(c, dst);
     if (s < 0 || !c->copy_pending[s]) return MOE_OK;
-    const hipError_t e = hipStreamWaitEvent(c->stream, c->copy_done[s], 0);
-    if (e != hipSuccess) return hip_rc(c, e);
     c->copy_pending[s] = 0;
-    return MOE_OK;
+    if (hipEventQuery(c->copy_done[s]) == hipSuccess) return MOE_OK;
+    return hip_rc(c, hipStreamWaitEvent(c->stream, c->copy_done[s], 0));
 }
 
 int slot_compute_written(moe_ctx* c, uint8_t* dst)
@@ -234,22 +323,18 @@ int moe_load_layer_async(moe_ctx* c, int layer, int first_slot, int n, const voi
     if (nbytes != (size_t)n * c->slot_bytes) return MOE_E_SIZE;
     for (int s = first_slot; s < first_slot + n; ++s)
         if (c->slot_refs[s] > 0) return MOE_E_BUSY;
-    hipError_t e = hipSuccess;
+    const int sid = next_copy_stream(c);
+    hipStream_t cs = c->copy_streams[sid];
     for (int s = first_slot; s < first_slot + n; ++s) {
-        if (!c->free_pending[s]) continue;
-        e = hipStreamWaitEvent(c->copy_stream, c->slot_free[s], 0);
-        if (e != hipSuccess) return hip_rc(c, e);
-        c->free_pending[s] = 0;
+        const int rc = wait_slot_readers(c, s, cs);
+        if (rc) return rc;
     }
-    e = hipMemcpyAsync(c->pool + (size_t)first_slot * c->slot_bytes, images, nbytes,
-                       hipMemcpyDefault, c->copy_stream);
+    const hipError_t e = hipMemcpyAsync(c->pool + (size_t)first_slot * c->slot_bytes, images,
+                                        nbytes, hipMemcpyDefault, cs);
     if (e != hipSuccess) return hip_rc(c, e);
     for (int s = first_slot; s < first_slot + n; ++s) {
-        hipEvent_t ev = slot_event(c->copy_done, s);
-        if (!ev) return MOE_E_HIP;
-        e = hipEventRecord(ev, c->copy_stream);
-        if (e != hipSuccess) return hip_rc(c, e);
-        c->copy_pending[s] = 1;
+        const int rc = note_copy(c, s, sid);
+        if (rc) return rc;
     }
     std::vector<std::pair<int, int>> ups;
     for (int i = 0; i < n; ++i) ups.push_back({layer * c->cfg.n_experts + i, first_slot + i});
@@ -259,7 +344,11 @@ int moe_load_layer_async(moe_ctx* c, int layer, int first_slot, int n, const voi
 int moe_sync_copies(moe_ctx* c)
 {
     if (!c) return MOE_E_ARG;
-    return hip_rc(c, hipStreamSynchronize(c->copy_stream));
+    for (auto& s : c->copy_streams) {
+        const hipError_t e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return hip_rc(c, e);
+    }
+    return MOE_OK;
 }
 
 int moe_set_staging(moe_ctx* c, int first_slot, int per_layer)
@@ -333,30 +422,30 @@ int moe_stage_experts(moe_ctx* c, int layer, int n, const int* expert_ids,
     if (nl < 0) return MOE_E_ARG;
     for (int i = 0; i < n; ++i)
         if (load[i] && !images[i]) return MOE_E_ARG;
-    // evict: the replaced experts leave the table first
-    std::vector<std::pair<int, int>> ups;
+    // evict: the replaced experts leave the table (the device table is
+    // written once, after the loads are enqueued: no forward can come in
+    // between, and the loads wait for the forwards that may read the slots)
     for (int i = 0; i < n; ++i) {
         if (!load[i]) continue;
         const int j = slot_of[i], old = held[j];
-        if (old >= 0 && c->tbl_host[layer * E + old] == base + j) ups.push_back({layer * E + old, -1});
+        if (old >= 0 && c->tbl_host[layer * E + old] == base + j) record_update(c, layer * E + old, -1);
+        held[j] = -1;
     }
-    int rc = apply_updates(c, ups);
-    if (rc) return rc;
-    for (int i = 0; i < n; ++i) {
-        if (!load[i]) continue;
-        rc = load_async(c, base + slot_of[i], images[i]);
-        if (rc) return rc;
-        held[slot_of[i]] = -1;
+    int rc = MOE_OK;
+    for (int i = 0; i < n && rc == MOE_OK; ++i)
+        if (load[i]) rc = load_async(c, base + slot_of[i], images[i]);
+    if (rc) {
+        flush_updates(c);
+        return rc;
     }
-    ups.clear();
     for (int i = 0; i < n; ++i) {
         const int j = slot_of[i];
         held[j] = expert_ids[i];
         used[j] = c->stage_step;
-        ups.push_back({layer * E + expert_ids[i], base + j});
+        record_update(c, layer * E + expert_ids[i], base + j);
     }
     ++c->stage_step;
-    rc = apply_updates(c, ups);
+    rc = flush_updates(c);
     if (rc) return rc;
     if (n_loaded) *n_loaded = nl;
     return MOE_OK;
