@@ -85,7 +85,7 @@ __device__ __forceinline__ void load64(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
 }
 
 template <int NT>
-__device__ void router_tail(const Fwd& f)
+__device__ void router_tail(const Fwd& f, float bias_e, int slot_e)
 {
     __shared__ unsigned long long s_key[NT][256];
     __shared__ unsigned long long s_cand[NT][32];
@@ -102,12 +102,6 @@ __device__ void router_tail(const Fwd& f)
     const int Sp = router_sp(T, S), S2p = router_s2p(S);
     const __amdgpu_buffer_rsrc_t rp = make_rsrc(f.part, (uint32_t)(Epad * Sp * 4));
     const __amdgpu_buffer_rsrc_t rt = make_rsrc(f.tpart, (uint32_t)(T * S2p * 4));
-    float bias_e = 0.f;
-    int slot_e = -1;
-    if (tid < E) {
-        bias_e = f.bias[tid];
-        slot_e = f.tbl[tid];
-    }
     // 1. token statistics and logits.  T = 1: every thread sums the token's
     //    statistics itself (no barrier); otherwise thread t < T does, via LDS.
     float lsum[NT];
@@ -444,6 +438,14 @@ __global__ void __launch_bounds__(RT_THREADS) k_router_small(Fwd f, const float*
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int b = blockIdx.x, s = blockIdx.y * RW + w;
     const int H = f.H, T = f.T, CH = H / 4;
+    // expert tid's bias and slot, for whichever workgroup runs the tail:
+    // loaded first, so that they have arrived long before the last arrival
+    float bias_e = 0.f;
+    int slot_e = -1;
+    if ((int)threadIdx.x < f.E) {
+        bias_e = f.bias[threadIdx.x];
+        slot_e = f.tbl[threadIdx.x];
+    }
     const __amdgpu_buffer_rsrc_t rw =
         make_rsrc((const float4*)f.wr + ((size_t)b * CH + (size_t)s * 16) * 64, 16 * 1024);
     float4 v[16];
@@ -504,7 +506,7 @@ __global__ void __launch_bounds__(RT_THREADS) k_router_small(Fwd f, const float*
     }
 
     if (!arrive_block(&f.counters[0], gridDim.x * gridDim.y)) return;
-    router_tail<NT>(f);
+    router_tail<NT>(f, bias_e, slot_e);
 }
 
 // ---------------------------------------------------------------------------
