@@ -17,6 +17,7 @@ SO = os.path.join(_HERE, "libmoe_oracle.so")
 
 W_INT4_ROW = 1
 W_INT4_AFFINE_G64 = 2
+W_INT8_ROW = 3
 
 
 def build() -> None:
@@ -64,7 +65,7 @@ def lib() -> ctypes.CDLL:
         L.orc_moe_layer.argtypes = [vp, i32, i64, i64, i32, i32, i32, vp, vp, f32, i32, vp, i32,
                                     vp, vp, vp, vp]
         L.orc_moe_layer.restype = i32
-        L.orc_moe_layer_full.argtypes = [vp, i32, i64, i64, i32, i32, i32, vp, vp, i32, i32, i32,
+        L.orc_moe_layer_full.argtypes = [vp, i32, i64, i64, i32, i32, i32, i32, vp, vp, i32, i32, i32,
                                          f32, i32, vp, i32, vp, vp, vp, vp]
         L.orc_moe_layer_full.restype = i32
         L.orc_rmsnorm.argtypes = [vp, i32, i64, f32, vp]
@@ -77,6 +78,8 @@ def lib() -> ctypes.CDLL:
         L.orc_dequant_fp8_block.argtypes = [vp, vp, i64, i64, i64, vp]
         L.orc_bf16_to_f32.argtypes = [vp, i64, vp]
         L.orc_convert_int4_container.argtypes = [vp, i64, i64, vp, vp]
+        L.orc_pack_int8_row.argtypes = [vp, i64, i64, vp, vp]
+        L.orc_pack_int8_row.restype = None
         for name in ("orc_dequant_fp8_block", "orc_bf16_to_f32", "orc_convert_int4_container"):
             getattr(L, name).restype = None
         for name in ("orc_pack_int4_row", "orc_unpack_int4_row", "orc_dequant_int4_row",
@@ -167,6 +170,16 @@ def convert_int4_container(w: np.ndarray):
     q = np.empty((O, I // 2), dtype=np.uint8)
     s = np.empty(O, dtype=np.float32)
     lib().orc_convert_int4_container(_p(w), O, I, _p(q), _p(s))
+    return q, s
+
+
+def pack_int8_row(w: np.ndarray):
+    """Per-row int8 ([GLM-C] §05 quantize_rows, bits = 8): (q int8 [O][I], s [O])."""
+    w = _f32(w)
+    O, I = w.shape
+    q = np.empty((O, I), dtype=np.int8)
+    s = np.empty(O, dtype=np.float32)
+    lib().orc_pack_int8_row(_p(w), O, I, _p(q), _p(s))
     return q, s
 
 
@@ -304,7 +317,7 @@ def _blob_array(blobs):
 
 
 def moe_layer(x, Wr, bias, K, fmt, I, blobs, shared_blobs, routed_scale=2.5, norm_topk=1,
-              n_group=1, topk_group=1, scoring=SCORE_SIGMOID):
+              n_group=1, topk_group=1, scoring=SCORE_SIGMOID, shared_fmt=0):
     """Whole layer; blobs is a list of E blobs (None = not resident)."""
     x, Wr, bias = _f32(x), _f32(Wr), _f32(bias)
     T, H = x.shape
@@ -314,7 +327,8 @@ def moe_layer(x, Wr, bias, K, fmt, I, blobs, shared_blobs, routed_scale=2.5, nor
     wts = np.empty((T, K), dtype=np.float32)
     ba = _blob_array(blobs)
     sa = _blob_array(shared_blobs) if shared_blobs else None
-    rc = lib().orc_moe_layer_full(_p(x), T, H, I, E, K, fmt, _p(Wr), _p(bias), scoring, n_group,
+    rc = lib().orc_moe_layer_full(_p(x), T, H, I, E, K, fmt, shared_fmt, _p(Wr), _p(bias), scoring,
+                                  n_group,
                                   topk_group, routed_scale, norm_topk,
                                     ctypes.cast(ba, ctypes.c_void_p), len(shared_blobs or []),
                                     ctypes.cast(sa, ctypes.c_void_p) if sa is not None else None,

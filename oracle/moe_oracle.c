@@ -52,7 +52,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORC_W_INT4_ROW = 1, ORC_W_INT4_AFFINE_G64 = 2 };
+enum { ORC_W_INT4_ROW = 1, ORC_W_INT4_AFFINE_G64 = 2, ORC_W_INT8_ROW = 3 };
 
 /* ------------------------------------------------------------------------ */
 /* Sizes ([GLM-C] §13 one contiguous g|u|d slab per expert; [EDGE0] §三).    */
@@ -60,6 +60,7 @@ enum { ORC_W_INT4_ROW = 1, ORC_W_INT4_AFFINE_G64 = 2 };
 
 int64_t orc_blob_bytes(int fmt, int64_t H, int64_t I)
 {
+    if (fmt == ORC_W_INT8_ROW) return 3 * H * I + 4 * (I + I + H);
     int64_t packed = I * (H / 2) * 2 + H * (I / 2);
     if (fmt == ORC_W_INT4_ROW) return packed + 4 * (I + I + H);
     if (fmt == ORC_W_INT4_AFFINE_G64) return packed + 4 * (I * (H / 64) * 2 + H * (I / 64));
@@ -150,6 +151,33 @@ void orc_dequant_int4_row(const uint8_t *q, const float *s, int64_t O, int64_t I
     for (int64_t o = 0; o < O; ++o)
         for (int64_t i = 0; i < I; ++i)
             w[o * I + i] = (double)nib_signed(q + o * rb, i) * (double)s[o];
+}
+
+/* ------------------------------------------------------------------------ */
+/* O1b: per-row symmetric int8 ([GLM-C] §05 quantize_rows with bits = 8: the  */
+/* streaming engine's expert format, and the dense precision of the           */
+/* converted model, §06-07)                                                   */
+/* ------------------------------------------------------------------------ */
+
+/* w [O][I] -> q [O][I] int8, s [O]: s = max|w| / 127 floored at 1e-8,
+ * q = rint(w / s) clamped to [-128, 127]. */
+void orc_pack_int8_row(const float *w, int64_t O, int64_t I, int8_t *q, float *s)
+{
+    for (int64_t o = 0; o < O; ++o) {
+        const float *wr = w + o * I;
+        float amax = 0.0f;
+        for (int64_t i = 0; i < I; ++i)
+            if (fabsf(wr[i]) > amax) amax = fabsf(wr[i]);
+        float sc = amax / 127.0f;
+        if (sc < 1e-8f) sc = 1e-8f;
+        s[o] = sc;
+        for (int64_t i = 0; i < I; ++i) {
+            int v = (int)rintf(wr[i] / sc);
+            if (v > 127) v = 127;
+            if (v < -128) v = -128;
+            q[o * I + i] = (int8_t)v;
+        }
+    }
 }
 
 /* ------------------------------------------------------------------------ */
@@ -280,6 +308,14 @@ void orc_dequant_affine_g64(const uint8_t *q, const uint16_t *scmn, int64_t O, i
 int orc_pack_expert(int fmt, int64_t H, int64_t I, const float *Wg, const float *Wu,
                     const float *Wd, uint8_t *blob)
 {
+    if (fmt == ORC_W_INT8_ROW) {
+        int8_t *q = (int8_t *)blob;
+        float *sc = (float *)(blob + 3 * H * I);
+        orc_pack_int8_row(Wg, I, H, q, sc);
+        orc_pack_int8_row(Wu, I, H, q + I * H, sc + I);
+        orc_pack_int8_row(Wd, H, I, q + 2 * I * H, sc + 2 * I);
+        return 0;
+    }
     int64_t gq = I * (H / 2), dq = H * (I / 2);
     uint8_t *qg = blob, *qu = blob + gq, *qd = blob + 2 * gq, *sc = blob + 2 * gq + dq;
     if (fmt == ORC_W_INT4_ROW) {
@@ -303,6 +339,14 @@ int orc_pack_expert(int fmt, int64_t H, int64_t I, const float *Wg, const float 
 int orc_dequant_expert(int fmt, int64_t H, int64_t I, const uint8_t *blob, double *wg,
                        double *wu, double *wd)
 {
+    if (fmt == ORC_W_INT8_ROW) {
+        const int8_t *q = (const int8_t *)blob;
+        const float *s = (const float *)(blob + 3 * H * I);
+        for (int64_t i = 0; i < I * H; ++i) wg[i] = (double)q[i] * (double)s[i / H];
+        for (int64_t i = 0; i < I * H; ++i) wu[i] = (double)q[I * H + i] * (double)s[I + i / H];
+        for (int64_t i = 0; i < H * I; ++i) wd[i] = (double)q[2 * I * H + i] * (double)s[2 * I + i / I];
+        return 0;
+    }
     int64_t gq = I * (H / 2), dq = H * (I / 2);
     const uint8_t *qg = blob, *qu = blob + gq, *qd = blob + 2 * gq, *sc = blob + 2 * gq + dq;
     if (fmt == ORC_W_INT4_ROW) {
@@ -339,6 +383,10 @@ static void dequant_row(int fmt, const uint8_t *q, const uint8_t *sc, int64_t ro
         const uint8_t *r = q + row * (in / 2);
         double s = (double)((const float *)sc)[row];
         for (int64_t i = 0; i < in; ++i) out[i] = (double)nib_signed(r, i) * s;
+    } else if (fmt == ORC_W_INT8_ROW) {
+        const int8_t *r = (const int8_t *)q + row * in;
+        double s = (double)((const float *)sc)[row];
+        for (int64_t i = 0; i < in; ++i) out[i] = (double)r[i] * s;
     } else {
         const uint8_t *r = q + row * (in / 2);
         const uint16_t *a = (const uint16_t *)sc + row * (in / 64) * 2;
@@ -354,11 +402,15 @@ static void dequant_row(int fmt, const uint8_t *q, const uint8_t *sc, int64_t ro
 int orc_expert(int fmt, int64_t H, int64_t I, const uint8_t *blob, const float *x, float *y,
                float *h_out)
 {
-    if (fmt != ORC_W_INT4_ROW && fmt != ORC_W_INT4_AFFINE_G64) return -1;
+    if (fmt != ORC_W_INT4_ROW && fmt != ORC_W_INT4_AFFINE_G64 && fmt != ORC_W_INT8_ROW) return -1;
     int64_t gq = I * (H / 2), dq = H * (I / 2);
+    if (fmt == ORC_W_INT8_ROW) {
+        gq = I * H;
+        dq = H * I;
+    }
     const uint8_t *qg = blob, *qu = blob + gq, *qd = blob + 2 * gq, *sc = blob + 2 * gq + dq;
     const uint8_t *scg, *scu, *scd;
-    if (fmt == ORC_W_INT4_ROW) {
+    if (fmt == ORC_W_INT4_ROW || fmt == ORC_W_INT8_ROW) {
         scg = sc;
         scu = sc + 4 * I;
         scd = sc + 8 * I;
@@ -663,11 +715,12 @@ void orc_combine(int T, int K, int64_t H, int n_shared, const float *y_routed, c
 /* ------------------------------------------------------------------------ */
 
 int orc_moe_layer_full(const float *x, int T, int64_t H, int64_t I, int E, int K, int fmt,
-                       const float *Wr, const float *bias, int scoring, int n_group,
-                       int topk_group, float routed_scale, int norm_topk,
+                       int shared_fmt, const float *Wr, const float *bias, int scoring,
+                       int n_group, int topk_group, float routed_scale, int norm_topk,
                        const uint8_t *const *blobs, int n_shared,
                        const uint8_t *const *shared_blobs, float *out, int32_t *ids, float *wts)
 {
+    if (shared_fmt == 0) shared_fmt = fmt;
     int rc = orc_route_full(x, T, H, Wr, bias, E, K, scoring, n_group, topk_group, routed_scale,
                             norm_topk, ids, wts, NULL, NULL, NULL, NULL, NULL);
     if (rc) return rc;
@@ -686,7 +739,8 @@ int orc_moe_layer_full(const float *x, int T, int64_t H, int64_t I, int E, int K
             else rc = orc_expert(fmt, H, I, b, xt, yr + ((int64_t)t * K + k) * H, NULL);
         }
         for (int s = 0; s < n_shared && rc == 0; ++s)
-            rc = orc_expert(fmt, H, I, shared_blobs[s], xt, ys + ((int64_t)s * T + t) * H, NULL);
+            rc = orc_expert(shared_fmt, H, I, shared_blobs[s], xt, ys + ((int64_t)s * T + t) * H,
+                            NULL);
     }
     if (rc == 0) orc_combine(T, K, H, n_shared, yr, wts, ys, out);
     free(yr);
@@ -699,7 +753,7 @@ int orc_moe_layer(const float *x, int T, int64_t H, int64_t I, int E, int K, int
                   const uint8_t *const *blobs, int n_shared, const uint8_t *const *shared_blobs,
                   float *out, int32_t *ids, float *wts)
 {
-    return orc_moe_layer_full(x, T, H, I, E, K, fmt, Wr, bias, 0, 1, 1, routed_scale, norm_topk,
+    return orc_moe_layer_full(x, T, H, I, E, K, fmt, 0, Wr, bias, 0, 1, 1, routed_scale, norm_topk,
                               blobs, n_shared, shared_blobs, out, ids, wts);
 }
 

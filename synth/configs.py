@@ -37,6 +37,7 @@ class LayerConfig:
     n_group: int = 1          # expert groups of the router (group-limited selection)
     topk_group: int = 1       # groups kept per token
     scoring: int = 0          # 0 sigmoid (+ bias selects), 1 softmax over all experts
+    shared_fmt: int = 0       # shared experts' format: 0 = fmt, 3 = per-row int8
     eps: float = 1e-6
 
     def with_(self, **kw) -> "LayerConfig":

@@ -31,7 +31,9 @@ def log(msg: str) -> None:
 
 
 def oracle_blob(cfg, layer: int, e: int) -> np.ndarray:
-    return oracle.pack_expert(cfg.fmt, *synth.expert_weights(cfg, layer, e))
+    """Expert e's blob; e >= E is shared expert e - E, in the shared format."""
+    fmt = cfg.shared_fmt if (e >= cfg.E and cfg.shared_fmt) else cfg.fmt
+    return oracle.pack_expert(fmt, *synth.expert_weights(cfg, layer, e))
 
 
 def oracle_blobs(cfg, layer: int, experts, workers: int = 8) -> dict:
@@ -74,7 +76,7 @@ class OracleLayer:
         def one(t):
             o, _, _ = oracle.moe_layer(xin[t:t + 1], self.W, self.b, cfg.K, cfg.fmt, cfg.I, blobs,
                                        self.shared, cfg.routed_scale, cfg.norm_topk, cfg.n_group,
-                                       cfg.topk_group, cfg.scoring)
+                                       cfg.topk_group, cfg.scoring, cfg.shared_fmt)
             return o[0]
 
         with ThreadPoolExecutor(max_workers=workers) as ex:

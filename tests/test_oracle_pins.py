@@ -745,3 +745,71 @@ def test_container_converter_reproduces_page_bytes():
     q, s = oracle.convert_int4_container(row[None, :])
     assert s[0] == 0.25
     assert list(q[0, :8]) == raw
+
+
+# ---------------------------------------------------------------------------
+# O1b: per-row int8 ([GLM-C] §05 quantize_rows, bits = 8), the shared
+# expert's format option
+# ---------------------------------------------------------------------------
+
+I8 = oracle.W_INT8_ROW
+
+
+def test_int8_blob_is_one_byte_per_weight():
+    # the page's int8 expert slot: one byte per parameter plus one fp32 scale per row
+    for H, I in [(6144, 2048), (512, 256)]:
+        assert oracle.blob_bytes(I8, H, I) == 3 * H * I + 4 * (2 * I + H)
+
+
+def test_int8_on_grid_values_come_back_exactly():
+    rng = np.random.default_rng(21)
+    k = rng.integers(-127, 128, size=(40, 96))
+    k[:, 3] = 127                                        # row max 127: s = step exactly
+    step = (2.0 ** rng.integers(-12, -4, size=(40, 1))).astype(np.float32)
+    q, s = oracle.pack_int8_row((k * step).astype(np.float32))
+    assert np.array_equal(s, step[:, 0])
+    assert np.array_equal(q.astype(int), k)
+
+
+def test_int8_ties_floor_and_bound():
+    w = np.array([[127.0, 2.5, 3.5, -2.5, -0.5, 0.5, 126.5, -126.5]], dtype=np.float32)
+    q, s = oracle.pack_int8_row(w)
+    assert s[0] == 1.0 and list(q[0]) == [127, 2, 4, -2, 0, 0, 126, -126]
+    q, s = oracle.pack_int8_row(np.zeros((2, 64), np.float32))
+    assert np.all(s == np.float32(1e-8)) and np.all(q == 0)
+    w = (np.random.default_rng(2).standard_normal((64, 256)) * 0.02).astype(np.float32)
+    q, s = oracle.pack_int8_row(w)
+    assert q.min() >= -127 and q.max() <= 127            # s = amax/127: -128 never occurs
+    err = np.abs(w.astype(np.float64) - q.astype(np.float64) * s[:, None].astype(np.float64))
+    assert np.all(err <= s[:, None] * 0.5 * (1 + 1e-6))
+
+
+def test_int8_expert_closed_form():
+    # constant weights c: codes are all 127, dequantised exactly to c
+    H, I, c = 128, 64, 0.015625
+    x = np.random.default_rng(3).standard_normal(H).astype(np.float32)
+    blob = oracle.pack_expert(I8, np.full((I, H), c, np.float32), np.full((I, H), c, np.float32),
+                              np.full((H, I), c, np.float32))
+    y, h = oracle.expert(I8, H, I, blob, x)
+    g = c * x.astype(np.float64).sum()
+    hv = np.float32(g / (1 + np.exp(-g)) * g)
+    assert np.allclose(h, hv, rtol=1e-6)
+    assert np.allclose(y, c * I * np.float64(hv), rtol=1e-6)
+
+
+def test_layer_with_int8_shared_is_routed_plus_shared():
+    rng = np.random.default_rng(4)
+    H, I, E, K = 128, 64, 8, 2
+    x = rng.standard_normal((3, H)).astype(np.float32)
+    Wr = (rng.standard_normal((E, H)) * 0.05).astype(np.float32)
+    b = (rng.standard_normal(E) * 0.1).astype(np.float32)
+    mk = lambda fmt: oracle.pack_expert(fmt, *(  # noqa: E731
+        (rng.standard_normal(sh) * 0.02).astype(np.float32) for sh in [(I, H), (I, H), (H, I)]))
+    blobs = [mk(ROW) for _ in range(E)]
+    sh = mk(I8)
+    out, ids, wts = oracle.moe_layer(x, Wr, b, K, ROW, I, blobs, [sh], shared_fmt=I8)
+    for t in range(3):
+        ref = oracle.expert(I8, H, I, sh, x[t])[0].astype(np.float64)
+        for k in range(K):
+            ref += wts[t, k] * oracle.expert(ROW, H, I, blobs[ids[t, k]], x[t])[0]
+        assert np.allclose(out[t], ref, rtol=1e-5, atol=1e-7)
