@@ -31,14 +31,23 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def glm_bytes(cfg, n_experts_read: int, T: int) -> int:
+def expert_bytes(cfg, fmt: int) -> int:
+    """One expert's codes and scales in format fmt (1 int4 row, 2 int4
+    affine g64, 3 int8 row)."""
+    if fmt == 1:
+        return 3 * cfg.H * cfg.I // 2 + 4 * (2 * cfg.I + cfg.H)
+    if fmt == 3:
+        return 3 * cfg.H * cfg.I + 4 * (2 * cfg.I + cfg.H)
+    return 3 * cfg.H * cfg.I // 2 + 12 * cfg.H * cfg.I // 64
+
+
+def glm_bytes(cfg, n_routed_read: int, T: int) -> int:
     """Algorithmic HBM bytes of one layer forward: router weights and bias,
-    every expert read once (codes + scales), tokens in and out."""
-    from int4_weight_expert_amd.moe import MOE_W_INT4_ROW  # noqa: F401
-    expert = 3 * cfg.H * cfg.I // 2 + 4 * (2 * cfg.I + cfg.H)
-    if cfg.fmt != 1:
-        expert = 3 * cfg.H * cfg.I // 2 + 12 * cfg.H * cfg.I // 64
-    return cfg.E * cfg.H * 4 + cfg.E * 4 + n_experts_read * expert + 2 * T * cfg.H * 4
+    every routed expert read once and the shared experts (codes + scales),
+    tokens in and out."""
+    shared = cfg.n_shared * expert_bytes(cfg, cfg.shared_fmt or cfg.fmt)
+    return (cfg.E * cfg.H * 4 + cfg.E * 4 + n_routed_read * expert_bytes(cfg, cfg.fmt) + shared
+            + 2 * T * cfg.H * 4)
 
 
 def gateup_unit_bytes(cfg) -> int:
@@ -151,7 +160,7 @@ def bench_decode(torch, args, result):
     n_gateup = cfg.K + cfg.n_shared
     alg_gateup = n_gateup * gateup_unit_bytes(cfg)
     t_gu = kt["gateup_gemv"] * 1e-3
-    layer_bytes = glm_bytes(cfg, cfg.K + cfg.n_shared, 1)
+    layer_bytes = glm_bytes(cfg, cfg.K, 1)
     result.update({
         "metric": "MoE-FFN tokens/s (GLM-shape layer, T=1 decode)",
         "value": 1.0 / t_step,
@@ -199,10 +208,11 @@ def bench_rotated(torch, name, steps, result):
         fn()
     g, t, _ = time_graph(torch, ml, fns, steps, 20)
     pct = replay_percentiles(torch, g, L)
-    layer_bytes = glm_bytes(cfg, cfg.K + cfg.n_shared, 1)
+    layer_bytes = glm_bytes(cfg, cfg.K, 1)
     result["extra"][name] = {
         "T": 1, "layers": L, "n_group": cfg.n_group, "topk_group": cfg.topk_group,
         "scoring": "softmax" if cfg.scoring else "sigmoid",
+        "shared_format": "int8 row" if cfg.shared_fmt == 3 else "as routed",
         "us_per_layer": t * 1e6, "graph_replay_percentiles": pct,
         "layer_algorithmic_bytes": layer_bytes, "layer_gbps": layer_bytes / t / 1e9,
         "layer_frac_hbm_peak": layer_bytes / t / 1e9 / HBM_PEAK_GBS,
@@ -409,7 +419,7 @@ def bench_chain(torch, name, steps, result):
     t = t_graph
     x.copy_(x0)
     pct = replay_percentiles(torch, g, L, reps=20)
-    bytes_layer = float(np.mean([glm_bytes(cfg, u + cfg.n_shared, cfg.T) for u in distinct]))
+    bytes_layer = float(np.mean([glm_bytes(cfg, u, cfg.T) for u in distinct]))
     result["extra"][name] = {
         "T": cfg.T, "layers": L, "us_per_layer": t * 1e6, "us_per_layer_eager": t_eager * 1e6,
         "graph_replay_percentiles": pct,
@@ -560,7 +570,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=16)
     ap.add_argument("--only", choices=["decode", "verify", "edge0", "edge0_k8", "prefill", "grouped",
-                                       "softmax", "requant", "staged"],
+                                       "softmax", "int8_shared", "requant", "staged"],
                     help="run one workload only (for profiling); the JSON line then "
                          "carries that workload in extra")
     ap.add_argument("--copy-probe", action="store_true",
@@ -593,6 +603,7 @@ def main():
          "prefill": lambda: bench_prefill(torch, 20, result),
          "grouped": lambda: bench_rotated(torch, "glm_decode_grouped", 200, result),
          "softmax": lambda: bench_rotated(torch, "glm_decode_softmax", 200, result),
+         "int8_shared": lambda: bench_rotated(torch, "glm_decode_int8_shared", 200, result),
          "requant": lambda: bench_requant(torch, result),
          "staged": lambda: bench_staged(torch, result)}[args.only]()
         print(json.dumps(result), flush=True)
@@ -606,6 +617,7 @@ def main():
         bench_chain(torch, "edge0_decode_k8", 200, result)
         bench_rotated(torch, "glm_decode_grouped", 200, result)
         bench_rotated(torch, "glm_decode_softmax", 200, result)
+        bench_rotated(torch, "glm_decode_int8_shared", 200, result)
         bench_requant(torch, result)
         bench_staged(torch, result)
         bench_prefill(torch, 20, result)

@@ -66,6 +66,7 @@ typedef struct moe_ctx moe_ctx;
 /* expert weight formats (layout of an expert blob, see moe_load_expert) */
 #define MOE_W_INT4_ROW 1        /* symmetric int4, one fp32 scale per output row */
 #define MOE_W_INT4_AFFINE_G64 2 /* affine int4, bf16 scale and min per 64 inputs */
+#define MOE_W_INT8_ROW 3        /* symmetric int8, one fp32 scale per output row (shared experts) */
 
 /* router scoring (moe_config.scoring) */
 #define MOE_SCORE_SIGMOID 0 /* sigma(l) + bias selects, sigma weighs ([GLM-C] §11, [EDGE0] §七) */
@@ -94,6 +95,12 @@ typedef struct moe_config {
     int max_tokens;     /* largest T passed to moe_forward / moe_route */
     float rms_eps;      /* eps of the RMSNorm used by moe_forward_residual */
     int scoring;        /* MOE_SCORE_SIGMOID or MOE_SCORE_SOFTMAX */
+    int shared_fmt;     /* shared experts' format: 0 (= wfmt) or MOE_W_INT8_ROW, the per-row
+                         * int8 of [GLM-C] §05 quantize_rows (bits = 8), the dense precision
+                         * of the converted model (§06-07).  Blob: Qg[I][H] Qu[I][H] Qd[H][I]
+                         * int8 (two's complement), then sg[I] su[I] sd[H] fp32; weight =
+                         * code * scale.  With int8 shared experts every forward runs the
+                         * expert GEMVs (the grouped GEMM is not used). */
 } moe_config;
 
 /* Creates a context on the current HIP device: allocates the slot pool
@@ -171,7 +178,9 @@ int moe_import_expert(moe_ctx *ctx, int slot, const uint8_t *qg, const uint8_t *
                       const uint8_t *qd, const float *sg, const float *su, const float *sd);
 
 /* Shared expert s of a layer, from a blob (host or device; synchronous) or
- * from device fp32 weights (asynchronous).  Errors: MOE_E_ARG, MOE_E_SIZE. */
+ * from device fp32 weights (asynchronous), in the shared experts' format
+ * (moe_config.shared_fmt; nbytes == moe_shared_bytes).  Errors: MOE_E_ARG,
+ * MOE_E_SIZE (moe_import_shared: MOE_E_UNSUPPORTED for int8). */
 int moe_set_shared(moe_ctx *ctx, int layer, int s, const void *blob, size_t nbytes);
 int moe_pack_shared(moe_ctx *ctx, int layer, int s, const float *Wg, const float *Wu,
                     const float *Wd);
@@ -265,6 +274,11 @@ size_t moe_image_bytes(int wfmt, int hidden, int inter);
 int moe_blob_to_image(int wfmt, int hidden, int inter, const void *blob, size_t nbytes,
                       void *image);
 
+/* Shared expert s of a layer back out in its blob layout (nbytes ==
+ * moe_shared_bytes).  Synchronous.  Errors: MOE_E_ARG, MOE_E_SIZE, MOE_E_HIP. */
+int moe_read_shared(moe_ctx *ctx, int layer, int s, void *dst, size_t nbytes);
+size_t moe_shared_bytes(const moe_ctx *ctx);
+
 /* Copies a slot back out in blob layout to dst (host or device pointer).
  * Synchronous.  Errors: MOE_E_SLOT, MOE_E_SIZE, MOE_E_ARG. */
 int moe_read_slot(moe_ctx *ctx, int slot, void *dst, size_t nbytes);
@@ -341,6 +355,12 @@ int moe_requant_int4_rows(const void *w, int src, const float *sinv, int64_t O, 
                           uint8_t *q, float *s, void *stream);
 int moe_requant_affine_g64(const void *w, int src, const float *sinv, int64_t O, int64_t I,
                            uint8_t *q, uint16_t *scmn, void *stream);
+/* Per-row int8 ([GLM-C] §05 quantize_rows, bits = 8): s = max|w|/127
+ * floored at 1e-8, code = rint(w / s) clamped to [-128, 127] (fp32 IEEE
+ * division, round half to even); q [O][I] int8.  Device pointers.
+ * Errors: MOE_E_ARG, MOE_E_HIP. */
+int moe_requant_int8_rows(const void *w, int src, const float *sinv, int64_t O, int64_t I,
+                          int8_t *q, float *s, void *stream);
 
 /* Token -> expert bucketing of ids [T][K] (device) ([GLM-C] §11 batch
  * expert union): cnt [E], off [E+1] (exclusive scan), perm [T*K] =

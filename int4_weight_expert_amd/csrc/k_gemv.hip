@@ -141,11 +141,190 @@ __device__ __forceinline__ void unit_coords(int u, int KS, int NB, int& q, int& 
 }
 
 // ---------------------------------------------------------------------------
+// Per-row int8 shared experts ("惊呆了！…" §05 quantize_rows with bits = 8,
+// the dense precision of the converted model, §06-07).  The slot holds each
+// matrix [O][In] as 64-row blocks of 16-input chunks, ((b * In/16 + c) * 64 +
+// lane) * 16, codes offset binary (q + 128).  A unit is the int4 kernels'
+// unit (group, 64-row block, k-slice, with the same k-slice count and the
+// same partial layout), taken as a branch of the int4 GEMV launch for groups
+// 0 .. n_shared - 1, so the finalize and the combine are shared.  A code
+// byte n becomes the fp16 1024 + n (v_perm_b32 then an OR), in the staged
+// activations' pair order; per span of 64 inputs sum q x = acc - 1152 S.
+// ---------------------------------------------------------------------------
+
+// Bytes i and 4 + i of an 8-byte group as the fp16 pair (1024 + b_i, 1024 + b_{4+i}).
+__device__ __forceinline__ uint32_t byte_pair(uint32_t lo, uint32_t hi, uint32_t sel)
+{
+    return __builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u;
+}
+
+// One 16-input chunk (4 dwords of codes) against activation quads 2c, 2c+1.
+__device__ __forceinline__ float dot_chunk8(const uint4& w, const uint4& x0, const uint4& x1,
+                                            float acc)
+{
+    acc = dot_dword(byte_pair(w.x, w.y, 0x0C040C00u), byte_pair(w.x, w.y, 0x0C050C01u),
+                    byte_pair(w.x, w.y, 0x0C060C02u), byte_pair(w.x, w.y, 0x0C070C03u), x0, acc);
+    acc = dot_dword(byte_pair(w.z, w.w, 0x0C040C00u), byte_pair(w.z, w.w, 0x0C050C01u),
+                    byte_pair(w.z, w.w, 0x0C060C02u), byte_pair(w.z, w.w, 0x0C070C03u), x1, acc);
+    return acc;
+}
+
+__device__ __forceinline__ float fold8(float tot, float a, float2 span)
+{
+    return fmaf(a - 1152.f * span.y, span.x, tot);
+}
+
+template <int NT>
+__device__ __forceinline__ void gu8_unit(const Fwd& f, int q, int b, int gi, uint4* lds4)
+{
+    const int lane = threadIdx.x;
+    const int KS = f.gu_ks, H = f.H, I = f.I, NB = I / 64;
+    const int CPU4 = H / 32 / KS;               // the int4 slice: its activations
+    const int C8 = H / 16, CPU8 = 2 * CPU4;     // 16-input chunks of the row and of the slice
+    const Group grp = uni_group(f.groups, gi);
+    const int c0 = q * CPU8, row = b * 64 + lane, nsp = CPU8 / 4;
+    uint4* xq = lds4;
+    float2* xs = (float2*)(lds4 + NT * CPU4 * 4);
+    const uint8_t* base = grp.base;
+    const uint32_t voff = (uint32_t)lane * 16;
+    const __amdgpu_buffer_rsrc_t rg =
+        make_rsrc(base + ((size_t)b * C8 + c0) * 1024, (uint32_t)CPU8 * 1024);
+    const __amdgpu_buffer_rsrc_t ru =
+        make_rsrc(base + (size_t)I * H + ((size_t)b * C8 + c0) * 1024, (uint32_t)CPU8 * 1024);
+    const float* tab = (const float*)(base + (size_t)3 * H * I);
+    const float sgr = tab[row], sur = tab[I + row];
+#pragma unroll 1
+    for (int p0 = 0; p0 < grp.cnt; p0 += NT) {
+        const int nj = min(NT, grp.cnt - p0);
+        int tt[NT], rr[NT];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            tt[j] = 0;
+            rr[j] = 0;
+            if (j < nj) tok_rows(f, f.perm, grp, p0 + j, tt[j], rr[j]);
+        }
+        float Gt[NT], Ut[NT];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) Gt[j] = Ut[j] = 0.f;
+        uint4 A[4], B[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            A[k] = bload16(rg, voff + k * 1024, 0);
+            B[k] = bload16(ru, voff + k * 1024, 0);
+        }
+        copy_slice<NT>(f.xq, f.xsc, tt, nj, H / 8, H / 64, q * CPU4, CPU4, lane, xq, xs);
+#pragma unroll 1
+        for (int sp = 0; sp < nsp; ++sp) {
+            float ag[NT], au[NT];
+#pragma unroll
+            for (int j = 0; j < NT; ++j) ag[j] = au[j] = 0.f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint4 wa = A[k], wb = B[k];
+                // the same chunk of the next span (a load past the slice returns zeros)
+                A[k] = bload16(rg, voff + k * 1024, (uint32_t)(sp + 1) * 4096);
+                B[k] = bload16(ru, voff + k * 1024, (uint32_t)(sp + 1) * 4096);
+#pragma unroll
+                for (int j = 0; j < NT; ++j)
+                    if (j < nj) {
+                        const uint4* xj = xq + j * CPU4 * 4 + sp * 8 + 2 * k;
+                        ag[j] = dot_chunk8(wa, xj[0], xj[1], ag[j]);
+                        au[j] = dot_chunk8(wb, xj[0], xj[1], au[j]);
+                    }
+            }
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+                if (j < nj) {
+                    const float2 span = xs[j * (CPU4 / 2) + sp];
+                    Gt[j] = fold8(Gt[j], ag[j], span);
+                    Ut[j] = fold8(Ut[j], au[j], span);
+                }
+        }
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+            if (j < nj) {
+                const float g = Gt[j] * sgr, u = Ut[j] * sur;
+                if (KS == 1) {
+                    const float rs = f.tok[tt[j]].rscale;
+                    const float gg = g * rs, uu = u * rs;
+                    stage_span64(gg / (1.0f + expf(-gg)) * uu, lane,
+                                 (uint16_t*)(f.hq + (size_t)rr[j] * (I / 8) + b * 8),
+                                 f.hsc + (size_t)rr[j] * (I / 64) + b);
+                } else {
+                    float* o = f.gpart + (((size_t)rr[j] * NB + b) * KS + q) * 128;
+                    o[lane] = g;
+                    o[64 + lane] = u;
+                }
+            }
+        lds_wave_sync();
+    }
+}
+
+template <int NT>
+__device__ __forceinline__ void dn8_unit(const Fwd& f, int q, int b, int gi, uint4* lds4)
+{
+    const int lane = threadIdx.x;
+    const int KS = f.dn_ks, H = f.H, I = f.I, NB = H / 64;
+    const int CPU4 = I / 32 / KS, C8 = I / 16, CPU8 = 2 * CPU4;
+    const Group grp = uni_group(f.groups, gi);
+    const int c0 = q * CPU8, row = b * 64 + lane, nsp = CPU8 / 4;
+    uint4* xq = lds4;
+    float2* xs = (float2*)(lds4 + NT * CPU4 * 4);
+    const uint8_t* base = grp.base;
+    const uint32_t voff = (uint32_t)lane * 16;
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(
+        base + (size_t)2 * I * H + ((size_t)b * C8 + c0) * 1024, (uint32_t)CPU8 * 1024);
+    const float sdr = ((const float*)(base + (size_t)3 * H * I))[2 * I + row];
+#pragma unroll 1
+    for (int p0 = 0; p0 < grp.cnt; p0 += NT) {
+        const int nj = min(NT, grp.cnt - p0);
+        int rr[NT];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            int t = 0;
+            rr[j] = 0;
+            if (j < nj) tok_rows(f, f.perm, grp, p0 + j, t, rr[j]);
+        }
+        float Yt[NT];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) Yt[j] = 0.f;
+        uint4 D[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) D[k] = bload16(rd, voff + k * 1024, 0);
+        copy_slice<NT>(f.hq, f.hsc, rr, nj, I / 8, I / 64, q * CPU4, CPU4, lane, xq, xs);
+#pragma unroll 1
+        for (int sp = 0; sp < nsp; ++sp) {
+            float a[NT];
+#pragma unroll
+            for (int j = 0; j < NT; ++j) a[j] = 0.f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint4 wd = D[k];
+                D[k] = bload16(rd, voff + k * 1024, (uint32_t)(sp + 1) * 4096);
+#pragma unroll
+                for (int j = 0; j < NT; ++j)
+                    if (j < nj) {
+                        const uint4* xj = xq + j * CPU4 * 4 + sp * 8 + 2 * k;
+                        a[j] = dot_chunk8(wd, xj[0], xj[1], a[j]);
+                    }
+            }
+#pragma unroll
+            for (int j = 0; j < NT; ++j)
+                if (j < nj) Yt[j] = fold8(Yt[j], a[j], xs[j * (CPU4 / 2) + sp]);
+        }
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+            if (j < nj) f.ypart[(((size_t)rr[j] * NB + b) * KS + q) * 64 + lane] = Yt[j] * sdr;
+        lds_wave_sync();
+    }
+}
+
+// ---------------------------------------------------------------------------
 // gate/up unit: partial (sg (Wg x)_row, su (Wu x)_row) of one k-slice for the
 // group's tokens -> gpart[r][b][q][2][64]; with one k-slice, h directly.
 // ---------------------------------------------------------------------------
 
-template <int FMT, int NT>
+template <int FMT, int NT, bool S8>
 __global__ void __launch_bounds__(64) k_gu(Fwd f)
 {
     extern __shared__ uint4 lds4[];
@@ -154,6 +333,10 @@ __global__ void __launch_bounds__(64) k_gu(Fwd f)
     int q, b, gi;
     unit_coords(blockIdx.x, KS, NB, q, b, gi);
     if (gi >= uni(f.n_groups[0])) return;
+    if (S8 && gi < f.n_shared) {  // int8 shared expert (groups 0 .. n_shared - 1)
+        gu8_unit<NT>(f, q, b, gi, lds4);
+        return;
+    }
     const Group grp = uni_group(f.groups, gi);
     const int CPU = C / KS, c0 = q * CPU, row = b * 64 + lane;
     uint4* xq = lds4;
@@ -288,7 +471,7 @@ __global__ void __launch_bounds__(256) k_gu_fin(Fwd f, int n_rows)
 // down unit: partial sd (Wd h_r)_row of one k-slice -> ypart[r][b][q][64].
 // ---------------------------------------------------------------------------
 
-template <int FMT, int NT>
+template <int FMT, int NT, bool S8>
 __global__ void __launch_bounds__(64) k_dn(Fwd f)
 {
     extern __shared__ uint4 lds4[];
@@ -297,6 +480,10 @@ __global__ void __launch_bounds__(64) k_dn(Fwd f)
     int q, b, gi;
     unit_coords(blockIdx.x, KS, NB, q, b, gi);
     if (gi >= uni(f.n_groups[0])) return;
+    if (S8 && gi < f.n_shared) {
+        dn8_unit<NT>(f, q, b, gi, lds4);
+        return;
+    }
     const Group grp = uni_group(f.groups, gi);
     const int CPU = C / KS, c0 = q * CPU, row = b * 64 + lane;
     uint4* xq = lds4;
@@ -672,60 +859,70 @@ static hipError_t allow_lds(Kern kern, size_t lds, bool& done)
     return e;
 }
 
-template <int FMT, int NT>
+template <int FMT, int NT, bool S8>
 static hipError_t gu_launch(const Fwd& f, hipStream_t st)
 {
     const int KS = f.gu_ks, CPU = f.H / 32 / KS;
     const unsigned units = (unsigned)(max_groups(f) * (f.I / 64) * KS);
     const size_t lds = gemv_lds_bytes(CPU, f.T);
     static bool big = false;
-    hipError_t e0 = allow_lds(k_gu<FMT, NT>, lds, big);
+    hipError_t e0 = allow_lds(k_gu<FMT, NT, S8>, lds, big);
     if (e0 != hipSuccess) return e0;
-    return launch_k(k_gu<FMT, NT>, dim3(units), dim3(64), lds, st, f);
+    return launch_k(k_gu<FMT, NT, S8>, dim3(units), dim3(64), lds, st, f);
 }
 
-template <int FMT, int NT>
+template <int FMT, int NT, bool S8>
 static hipError_t dn_launch(const Fwd& f, hipStream_t st)
 {
     const int KS = f.dn_ks, CPU = f.I / 32 / KS;
     const unsigned units = (unsigned)(max_groups(f) * (f.H / 64) * KS);
     const size_t lds = gemv_lds_bytes(CPU, f.T);
     static bool big = false;
-    hipError_t e0 = allow_lds(k_dn<FMT, NT>, lds, big);
+    hipError_t e0 = allow_lds(k_dn<FMT, NT, S8>, lds, big);
     if (e0 != hipSuccess) return e0;
-    return launch_k(k_dn<FMT, NT>, dim3(units), dim3(64), lds, st, f);
+    return launch_k(k_dn<FMT, NT, S8>, dim3(units), dim3(64), lds, st, f);
 }
 
-template <int FMT>
+template <int FMT, bool S8>
 static hipError_t gu_dispatch(const Fwd& f, hipStream_t st)
 {
     switch (tokens_per_pass(f.T)) {
-    case 1: return gu_launch<FMT, 1>(f, st);
-    case 2: return gu_launch<FMT, 2>(f, st);
-    default: return gu_launch<FMT, 4>(f, st);
+    case 1: return gu_launch<FMT, 1, S8>(f, st);
+    case 2: return gu_launch<FMT, 2, S8>(f, st);
+    default: return gu_launch<FMT, 4, S8>(f, st);
     }
 }
 
-template <int FMT>
+template <int FMT, bool S8>
 static hipError_t dn_dispatch(const Fwd& f, hipStream_t st)
 {
     switch (tokens_per_pass(f.T)) {
-    case 1: return dn_launch<FMT, 1>(f, st);
-    case 2: return dn_launch<FMT, 2>(f, st);
-    default: return dn_launch<FMT, 4>(f, st);
+    case 1: return dn_launch<FMT, 1, S8>(f, st);
+    case 2: return dn_launch<FMT, 2, S8>(f, st);
+    default: return dn_launch<FMT, 4, S8>(f, st);
     }
 }
 
+bool shared_int8(const Fwd& f) { return f.n_shared > 0 && f.shared_fmt == MOE_W_INT8_ROW; }
+
+// With int8 shared experts, their units take the int8 branch inside the same
+// launch as the routed experts' units.
 hipError_t launch_gateup_gemv(const Fwd& f, hipStream_t st)
 {
-    if (f.fmt == MOE_W_INT4_ROW) return gu_dispatch<MOE_W_INT4_ROW>(f, st);
-    return gu_dispatch<MOE_W_INT4_AFFINE_G64>(f, st);
+    const bool s8 = shared_int8(f);
+    if (f.fmt == MOE_W_INT4_ROW)
+        return s8 ? gu_dispatch<MOE_W_INT4_ROW, true>(f, st) : gu_dispatch<MOE_W_INT4_ROW, false>(f, st);
+    return s8 ? gu_dispatch<MOE_W_INT4_AFFINE_G64, true>(f, st)
+              : gu_dispatch<MOE_W_INT4_AFFINE_G64, false>(f, st);
 }
 
 hipError_t launch_down_gemv(const Fwd& f, hipStream_t st)
 {
-    if (f.fmt == MOE_W_INT4_ROW) return dn_dispatch<MOE_W_INT4_ROW>(f, st);
-    return dn_dispatch<MOE_W_INT4_AFFINE_G64>(f, st);
+    const bool s8 = shared_int8(f);
+    if (f.fmt == MOE_W_INT4_ROW)
+        return s8 ? dn_dispatch<MOE_W_INT4_ROW, true>(f, st) : dn_dispatch<MOE_W_INT4_ROW, false>(f, st);
+    return s8 ? dn_dispatch<MOE_W_INT4_AFFINE_G64, true>(f, st)
+              : dn_dispatch<MOE_W_INT4_AFFINE_G64, false>(f, st);
 }
 
 bool gateup_needs_finalize(const Fwd& f) { return f.gu_ks > 1; }
@@ -748,7 +945,7 @@ static int dn2_rg(const Fwd& f) { return f.H % 2048 == 0 ? f.H / 2048 : 0; }
 bool down_combine1_ok(const Fwd& f)
 {
     const int rg = dn2_rg(f), ncg = f.I / 256, ne = f.n_shared + f.K;
-    return f.T == 1 && ne <= DC_NE && (size_t)ne * f.H * f.I / 2 <= ((size_t)16 << 20) && rg >= 1 && rg <= 4 && f.I % 256 == 0 && ncg >= 1 &&
+    return f.T == 1 && !shared_int8(f) && ne <= DC_NE && (size_t)ne * f.H * f.I / 2 <= ((size_t)16 << 20) && rg >= 1 && rg <= 4 && f.I % 256 == 0 && ncg >= 1 &&
            ncg <= 8 && ne * (f.I / 8) <= DC_HL * 64 * ncg && ne * (f.I / 64) <= 64 * ncg &&
            dn2_lds_bytes(f.I, rg) <= 65536;
 }

@@ -394,7 +394,7 @@ __global__ void __launch_bounds__(1024) k_bucket(const int32_t* __restrict__ ids
     }
     if (tid < f.n_shared) {
         Group g;
-        g.base = f.shared + (size_t)tid * f.slot_bytes;
+        g.base = f.shared + (size_t)tid * f.shared_bytes;
         g.cnt = f.T;
         g.off = tid;
         g.kind = 1;

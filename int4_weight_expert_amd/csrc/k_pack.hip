@@ -308,6 +308,37 @@ __global__ void __launch_bounds__(RQ_ROWS * 32) k_requant_rows(RqArgs a)
     }
 }
 
+// Per-row int8 ("惊呆了！…" §05 quantize_rows with bits = 8): s = max|w|/127
+// floored at 1e-8, code = rint(w / s) clamped to [-128, 127], q [O][I] int8.
+// One 256-thread workgroup per row.
+template <int SRC>
+__global__ void __launch_bounds__(256) k_pack_int8_rows(const void* __restrict__ w,
+                                                        const float* __restrict__ sinv, int64_t O,
+                                                        int64_t I, int8_t* __restrict__ q,
+                                                        float* __restrict__ s)
+{
+    __shared__ float red[4];
+    const int tid = threadIdx.x;
+    const int64_t nbi = (I + 127) >> 7;
+    for (int64_t o = blockIdx.x; o < O; o += gridDim.x) {
+        float amax = 0.0f;
+        for (int64_t i = tid; i < I; i += 256)
+            amax = fmaxf(amax, fabsf(src_elem<SRC>(w, sinv, o, i, I, nbi)));
+        amax = wave_max(amax);
+        if ((tid & 63) == 0) red[tid >> 6] = amax;
+        __syncthreads();
+        amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        __syncthreads();
+        float sc = __fdiv_rn(amax, 127.0f);
+        if (sc < 1e-8f) sc = 1e-8f;
+        if (tid == 0) s[o] = sc;
+        for (int64_t i = tid; i < I; i += 256) {
+            int v = (int)rintf(__fdiv_rn(src_elem<SRC>(w, sinv, o, i, I, nbi), sc));
+            q[o * I + i] = (int8_t)(v > 127 ? 127 : (v < -128 ? -128 : v));
+        }
+    }
+}
+
 // One wavefront per (row, group of 64 inputs); 4 groups per workgroup.
 template <int SRC>
 __global__ void __launch_bounds__(256) k_pack_affine_g64(const void* __restrict__ w,
@@ -488,6 +519,27 @@ hipError_t launch_requant_affine(const void* w, int src, const float* sinv, int6
     return hipGetLastError();
 }
 
+hipError_t launch_requant_int8_rows(const void* w, int src, const float* sinv, int64_t O,
+                                    int64_t I, int8_t* q, float* s, hipStream_t st)
+{
+    const dim3 grid(grid_for(O, 1)), block(256);
+    switch (src) {
+    case MOE_SRC_F32:
+        hipLaunchKernelGGL(k_pack_int8_rows<MOE_SRC_F32>, grid, block, 0, st, w, sinv, O, I, q, s);
+        break;
+    case MOE_SRC_BF16:
+        hipLaunchKernelGGL(k_pack_int8_rows<MOE_SRC_BF16>, grid, block, 0, st, w, sinv, O, I, q, s);
+        break;
+    case MOE_SRC_FP8_E4M3:
+        hipLaunchKernelGGL(k_pack_int8_rows<MOE_SRC_FP8_E4M3>, grid, block, 0, st, w, sinv, O, I, q,
+                           s);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 bool requant_slot_ok(const void* wg, const void* wu, const void* wd, const uint8_t* slot, int H,
                      int I)
 {
@@ -516,6 +568,19 @@ hipError_t launch_requant_slot(int src, const void* wg, const void* wu, const vo
 static hipError_t convert(const uint8_t* src, uint8_t* dst, int fmt, int H, int I, int to_slot,
                           uint32_t flip, hipStream_t st)
 {
+    if (fmt == MOE_W_INT8_ROW) {
+        // int8 matrices [O][In]: 64-row blocks of 16-input chunks, codes offset
+        // binary (q + 128 = byte ^ 0x80); the interleave of an int4 matrix of
+        // twice the width has exactly that layout
+        const int64_t m8 = (int64_t)I * H;
+        const int64_t mats[3][3] = {{0, I, H}, {m8, I, H}, {2 * m8, H, I}};
+        for (auto& m : mats)
+            hipLaunchKernelGGL(k_interleave, dim3(grid_for(m[1] * (m[2] / 16), 256)), dim3(256), 0,
+                               st, src + m[0], dst + m[0], m[1], 2 * m[2], 0x80808080u, to_slot);
+        const hipError_t e = hipMemcpyAsync(dst + 3 * m8, src + 3 * m8, (size_t)(2 * I + H) * 4,
+                                            hipMemcpyDeviceToDevice, st);
+        return e != hipSuccess ? e : hipGetLastError();
+    }
     const int64_t gq = (int64_t)I * (H / 2), dq = (int64_t)H * (I / 2);
     const int64_t mats[3][3] = {{0, I, H}, {gq, I, H}, {2 * gq, H, I}};  // offset, O, In
     for (auto& m : mats) {
@@ -538,7 +603,10 @@ static hipError_t convert(const uint8_t* src, uint8_t* dst, int fmt, int H, int 
     return hipGetLastError();
 }
 
-static uint32_t blob_flip(int fmt) { return fmt == MOE_W_INT4_ROW ? 0x88888888u : 0u; }
+static uint32_t blob_flip(int fmt)
+{
+    return fmt == MOE_W_INT4_ROW ? 0x88888888u : (fmt == MOE_W_INT8_ROW ? 0x80808080u : 0u);
+}
 
 hipError_t launch_blob_to_slot(const uint8_t* blob, uint8_t* slot, int fmt, int H, int I,
                                hipStream_t st)

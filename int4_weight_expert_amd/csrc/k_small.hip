@@ -310,7 +310,7 @@ __device__ void router_tail(const Fwd& f, float bias_e, int slot_e)
     }
     if (tid < f.n_shared) {
         Group g;
-        g.base = f.shared + (size_t)tid * f.slot_bytes;
+        g.base = f.shared + (size_t)tid * f.shared_bytes;
         g.cnt = T;
         g.off = tid;
         g.kind = 1;

@@ -49,6 +49,7 @@ size_t expert_bytes_for(int fmt, size_t H, size_t I)
     const size_t packed = 3 * H * I / 2;
     if (fmt == MOE_W_INT4_ROW) return packed + 4 * (2 * I + H);
     if (fmt == MOE_W_INT4_AFFINE_G64) return packed + 12 * H * I / 64;
+    if (fmt == MOE_W_INT8_ROW) return 3 * H * I + 4 * (2 * I + H);
     return 0;
 }
 
@@ -131,7 +132,9 @@ Fwd make_fwd(moe_ctx* c, const float* x, float* out, int T, int layer, int resid
     f.tbl = c->tbl + (size_t)layer * g.n_experts;
     f.pool = c->pool;
     f.slot_bytes = c->slot_bytes;
-    f.shared = c->shared + (size_t)layer * g.n_shared * c->slot_bytes;
+    f.shared_fmt = c->shared_fmt;
+    f.shared_bytes = c->shared_bytes;
+    f.shared = c->shared + (size_t)layer * g.n_shared * c->shared_bytes;
     f.part = c->part;
     f.tpart = c->tpart;
     f.S = router_small_slices(g.hidden);
@@ -188,7 +191,8 @@ int run_router(moe_ctx* c, const Fwd& f)
 bool uses_gemm(const moe_ctx* c, int T)
 {
     return c->hbuf != nullptr && T > ROUTER_SMALL_MAX_T && T >= c->gemm_min_tokens &&
-           gemm_shape_ok(c->cfg.hidden, c->cfg.inter);
+           gemm_shape_ok(c->cfg.hidden, c->cfg.inter) &&
+           !(c->cfg.n_shared > 0 && c->shared_fmt == MOE_W_INT8_ROW);
 }
 
 int run_forward_gemm(moe_ctx* c, Fwd& f)
@@ -254,14 +258,30 @@ int run_forward(moe_ctx* c, const float* x, int T, int layer, float* out, int re
     return MOE_OK;
 }
 
+// Format and size of the expert slot at dst: the shared experts' slots may
+// use their own format.
+bool in_shared(const moe_ctx* c, const uint8_t* dst)
+{
+    return c->shared && dst >= c->shared &&
+           dst < c->shared + (size_t)c->cfg.n_layers * c->cfg.n_shared * c->shared_bytes;
+}
+int fmt_of(const moe_ctx* c, const uint8_t* dst)
+{
+    return in_shared(c, dst) ? c->shared_fmt : c->cfg.wfmt;
+}
+size_t bytes_of(const moe_ctx* c, const uint8_t* dst)
+{
+    return in_shared(c, dst) ? c->shared_bytes : c->slot_bytes;
+}
+
 int copy_in_blob_impl(moe_ctx* c, uint8_t* dst_slot, const void* blob, size_t nbytes)
 {
     if (!blob) return MOE_E_ARG;
-    if (nbytes != c->slot_bytes) return MOE_E_SIZE;
+    if (nbytes != bytes_of(c, dst_slot)) return MOE_E_SIZE;
     if (hipMemcpyAsync(c->staging, blob, nbytes, hipMemcpyDefault, c->stream) != hipSuccess)
         return MOE_E_HIP;
-    if (launch_blob_to_slot(c->staging, dst_slot, c->cfg.wfmt, c->cfg.hidden, c->cfg.inter,
-                            c->stream) != hipSuccess)
+    if (launch_blob_to_slot(c->staging, dst_slot, fmt_of(c, dst_slot), c->cfg.hidden,
+                            c->cfg.inter, c->stream) != hipSuccess)
         return MOE_E_HIP;
     return hip_ok(hipStreamSynchronize(c->stream));
 }
@@ -273,6 +293,17 @@ int requant_into_impl(moe_ctx* c, uint8_t* dst_slot, int src, const void* Wg, co
     if (src != MOE_SRC_F32 && src != MOE_SRC_BF16 && src != MOE_SRC_FP8_E4M3) return MOE_E_ARG;
     if (src == MOE_SRC_FP8_E4M3 && (!sg || !su || !sd)) return MOE_E_ARG;
     const int64_t H = c->cfg.hidden, I = c->cfg.inter;
+    if (fmt_of(c, dst_slot) == MOE_W_INT8_ROW) {
+        int8_t* q = (int8_t*)c->staging;
+        float* sc = (float*)(c->staging + 3 * H * I);
+        hipError_t e = launch_requant_int8_rows(Wg, src, sg, I, H, q, sc, c->stream);
+        if (e == hipSuccess) e = launch_requant_int8_rows(Wu, src, su, I, H, q + I * H, sc + I, c->stream);
+        if (e == hipSuccess)
+            e = launch_requant_int8_rows(Wd, src, sd, H, I, q + 2 * I * H, sc + 2 * I, c->stream);
+        if (e == hipSuccess)
+            e = launch_blob_to_slot(c->staging, dst_slot, MOE_W_INT8_ROW, (int)H, (int)I, c->stream);
+        return hip_ok(e);
+    }
     if (c->cfg.wfmt == MOE_W_INT4_ROW && requant_slot_ok(Wg, Wu, Wd, dst_slot, (int)H, (int)I))
         return hip_ok(launch_requant_slot(src, Wg, Wu, Wd, sg, su, sd, (int)H, (int)I, dst_slot,
                                           c->stream));
@@ -302,7 +333,7 @@ int requant_into_impl(moe_ctx* c, uint8_t* dst_slot, int src, const void* Wg, co
 int import_into_impl(moe_ctx* c, uint8_t* dst_slot, const uint8_t* qg, const uint8_t* qu,
                 const uint8_t* qd, const float* sg, const float* su, const float* sd)
 {
-    if (c->cfg.wfmt != MOE_W_INT4_ROW) return MOE_E_UNSUPPORTED;
+    if (fmt_of(c, dst_slot) != MOE_W_INT4_ROW) return MOE_E_UNSUPPORTED;
     if (!qg || !qu || !qd || !sg || !su || !sd) return MOE_E_ARG;
     const size_t H = c->cfg.hidden, I = c->cfg.inter;
     const size_t gq = I * (H / 2), dq = H * (I / 2), sb = 2 * gq + dq;
@@ -355,6 +386,8 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
         g.n_slots < 0 || g.max_tokens <= 0 || g.n_shared < 0)
         return MOE_E_ARG;
     if (g.wfmt != MOE_W_INT4_ROW && g.wfmt != MOE_W_INT4_AFFINE_G64) return MOE_E_ARG;
+    if (g.shared_fmt != 0 && g.shared_fmt != g.wfmt && g.shared_fmt != MOE_W_INT8_ROW)
+        return MOE_E_ARG;
     if (g.n_group < 1 || g.topk_group < 1 || g.topk_group > g.n_group) return MOE_E_ARG;
     if (g.scoring != MOE_SCORE_SIGMOID && g.scoring != MOE_SCORE_SOFTMAX) return MOE_E_ARG;
     if (g.scoring == MOE_SCORE_SOFTMAX && g.n_group != 1) return MOE_E_UNSUPPORTED;
@@ -384,6 +417,8 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
     c->device = dev;
     c->lds_max = lds_max;
     c->slot_bytes = expert_bytes_for(g.wfmt, g.hidden, g.inter);
+    c->shared_fmt = g.shared_fmt ? g.shared_fmt : g.wfmt;
+    c->shared_bytes = expert_bytes_for(c->shared_fmt, g.hidden, g.inter);
     c->Epad = (g.n_experts + 63) / 64 * 64;
     const size_t H = g.hidden, I = g.inter, E = g.n_experts, L = g.n_layers, Tm = g.max_tokens;
     const size_t K = g.top_k, rows = Tm * K + Tm * g.n_shared;
@@ -392,8 +427,8 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
     rc = rc ? rc : dalloc(c, &c->wr, L * c->Epad * H * 4);
     rc = rc ? rc : dalloc(c, &c->bias, L * E * 4);
     rc = rc ? rc : dalloc(c, &c->tbl, L * E * 4);
-    rc = rc ? rc : dalloc(c, &c->shared, L * g.n_shared * c->slot_bytes);
-    rc = rc ? rc : dalloc(c, &c->staging, c->slot_bytes);
+    rc = rc ? rc : dalloc(c, &c->shared, L * g.n_shared * c->shared_bytes);
+    rc = rc ? rc : dalloc(c, &c->staging, std::max(c->slot_bytes, c->shared_bytes));
     rc = rc ? rc : dalloc(c, &c->part, (H / 64) * ROUTER_SMALL_MAX_T * c->Epad * 4);
     rc = rc ? rc : dalloc(c, &c->tpart, (H / 64) * ROUTER_SMALL_MAX_T * 2 * 4);
     rc = rc ? rc : dalloc(c, &c->logits, (size_t)ROUTER_SLICES * Tm * c->Epad * 4);
@@ -440,7 +475,7 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
         if (e == hipSuccess) e = hipMemset(c->status, 0, c->status_words * 4);
         if (e == hipSuccess) e = hipMemset(c->bias, 0, L * E * 4);
         if (e == hipSuccess) e = hipMemset(c->wr, 0, L * c->Epad * H * 4);
-        if (e == hipSuccess && g.n_shared) e = hipMemset(c->shared, 0, L * g.n_shared * c->slot_bytes);
+        if (e == hipSuccess && g.n_shared) e = hipMemset(c->shared, 0, L * g.n_shared * c->shared_bytes);
         if (e == hipSuccess) e = hipDeviceSynchronize();
         if (e != hipSuccess) rc = MOE_E_HIP;
     }
@@ -684,6 +719,30 @@ int moe_timing_summary(moe_ctx* c, float* ms, const char** names, int cap, int* 
     c->n_marks = 0;
     return MOE_OK;
 }
+
+int moe_requant_int8_rows(const void* w, int src, const float* sinv, int64_t O, int64_t I,
+                          int8_t* q, float* s, void* stream)
+{
+    if (!w || !q || !s || O <= 0 || I <= 0) return MOE_E_ARG;
+    if (src != MOE_SRC_F32 && src != MOE_SRC_BF16 && !(src == MOE_SRC_FP8_E4M3 && sinv))
+        return MOE_E_ARG;
+    return hip_ok(launch_requant_int8_rows(w, src, sinv, O, I, q, s, (hipStream_t)stream));
+}
+
+int moe_read_shared(moe_ctx* c, int layer, int s, void* dst, size_t nbytes)
+{
+    if (!c || !dst || layer < 0 || layer >= c->cfg.n_layers || s < 0 || s >= c->cfg.n_shared)
+        return MOE_E_ARG;
+    if (nbytes != c->shared_bytes) return MOE_E_SIZE;
+    const uint8_t* src = c->shared + ((size_t)layer * c->cfg.n_shared + s) * c->shared_bytes;
+    hipError_t e = launch_slot_to_blob(src, c->staging, c->shared_fmt, c->cfg.hidden,
+                                       c->cfg.inter, c->stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(dst, c->staging, nbytes, hipMemcpyDefault, c->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+    return hip_rc(c, e);
+}
+
+size_t moe_shared_bytes(const moe_ctx* c) { return c ? c->shared_bytes : 0; }
 
 int moe_pack_int4_rows(const float* w, int64_t O, int64_t I, uint8_t* q, float* s, void* stream)
 {

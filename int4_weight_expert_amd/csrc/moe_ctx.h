@@ -10,6 +10,8 @@ struct moe_ctx {
     hipStream_t stream = nullptr;
     int device = 0;
     size_t slot_bytes = 0;
+    int shared_fmt = 0;        // resolved format of the shared experts
+    size_t shared_bytes = 0;   // bytes of one shared expert's slot
     int Epad = 0;
     uint8_t* pool = nullptr;
     float* wr = nullptr;

@@ -47,6 +47,8 @@ struct Fwd {
     const float* x;       // [T][H]
     float* out;           // [T][H]
     int T, H, I, E, K, n_shared, fmt, Epad;
+    int shared_fmt;       // the shared experts' format (fmt, or MOE_W_INT8_ROW)
+    size_t shared_bytes;  // bytes of one shared expert's slot
     int residual;         // 1: out = x + moe(rmsnorm(x)), x may equal out
     float routed_scale, eps;
     int norm_topk;
@@ -103,6 +105,9 @@ hipError_t launch_requant_rows(const void* w, int src, const float* sinv, int64_
                                uint8_t* q, float* s, hipStream_t st);
 hipError_t launch_requant_affine(const void* w, int src, const float* sinv, int64_t O, int64_t I,
                                  uint8_t* q, uint16_t* scmn, hipStream_t st);
+hipError_t launch_requant_int8_rows(const void* w, int src, const float* sinv, int64_t O,
+                                    int64_t I, int8_t* q, float* s, hipStream_t st);
+bool shared_int8(const Fwd& f);
 bool requant_slot_ok(const void* wg, const void* wu, const void* wd, const uint8_t* slot, int H,
                      int I);
 hipError_t launch_requant_slot(int src, const void* wg, const void* wu, const void* wd,

@@ -15,16 +15,18 @@ class MoeLayer:
     def __init__(self, H: int, I: int, E: int, K: int, n_shared: int, n_layers: int, fmt: int,
                  n_slots: int, max_tokens: int, routed_scale: float = 2.5, norm_topk: int = 1,
                  rms_eps: float = 1e-6, stream: torch.cuda.Stream | None = None,
-                 n_group: int = 1, topk_group: int = 1, scoring: int = 0):
+                 n_group: int = 1, topk_group: int = 1, scoring: int = 0, shared_fmt: int = 0):
         self.H, self.I, self.E, self.K = H, I, E, K
         self.n_shared, self.n_layers, self.fmt = n_shared, n_layers, fmt
         self.n_slots, self.max_tokens = n_slots, max_tokens
         self.stream = stream if stream is not None else torch.cuda.current_stream()
         cfg = M.make_config(H, I, E, K, n_shared, n_layers, fmt, n_slots, max_tokens,
                             routed_scale=routed_scale, norm_topk=norm_topk, rms_eps=rms_eps,
-                            n_group=n_group, topk_group=topk_group, scoring=scoring)
+                            n_group=n_group, topk_group=topk_group, scoring=scoring,
+                            shared_fmt=shared_fmt)
         self.ctx = M.moe_layer_create(cfg, self.stream.cuda_stream)
         self.expert_bytes = M.moe_expert_bytes(self.ctx)
+        self.shared_bytes = M.lib().moe_shared_bytes(self.ctx)
 
     def close(self) -> None:
         if self.ctx:
@@ -49,6 +51,11 @@ class MoeLayer:
 
     def pack_expert(self, slot: int, Wg, Wu, Wd) -> None:
         M._check("moe_pack_expert", M.moe_pack_expert(self.ctx, slot, Wg, Wu, Wd))
+
+    def read_shared(self, layer: int, s: int) -> np.ndarray:
+        out = np.empty(self.shared_bytes, dtype=np.uint8)
+        M._check("moe_read_shared", M.moe_read_shared(self.ctx, layer, s, out, self.shared_bytes))
+        return out
 
     def set_shared(self, layer: int, s: int, blob) -> None:
         blob = _contig_u8(blob)

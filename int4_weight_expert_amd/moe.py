@@ -26,6 +26,7 @@ MOE_E_BUSY = -9
 MOE_W_INT4_ROW = 1
 MOE_SCORE_SIGMOID, MOE_SCORE_SOFTMAX = 0, 1
 MOE_W_INT4_AFFINE_G64 = 2
+MOE_W_INT8_ROW = 3
 MOE_SRC_F32, MOE_SRC_BF16, MOE_SRC_FP8_E4M3 = 0, 1, 2
 
 ERROR_NAMES = {0: "MOE_OK", -1: "MOE_E_ARG", -2: "MOE_E_NOMEM", -3: "MOE_E_SIZE",
@@ -41,7 +42,8 @@ EXPORTS = ["moe_layer_create", "moe_destroy", "moe_set_stream", "moe_expert_byte
            "moe_import_shared", "moe_requant_int4_rows", "moe_requant_affine_g64",
            "moe_map_experts_async", "moe_load_image_async", "moe_load_layer_async",
            "moe_sync_copies", "moe_set_staging", "moe_stage_experts", "moe_sticky_plan",
-           "moe_image_bytes", "moe_blob_to_image"]
+           "moe_image_bytes", "moe_blob_to_image", "moe_requant_int8_rows", "moe_read_shared",
+           "moe_shared_bytes"]
 
 
 class moe_config(ctypes.Structure):
@@ -50,7 +52,7 @@ class moe_config(ctypes.Structure):
                 ("wfmt", ctypes.c_int), ("n_group", ctypes.c_int), ("topk_group", ctypes.c_int),
                 ("routed_scale", ctypes.c_float), ("norm_topk", ctypes.c_int),
                 ("n_slots", ctypes.c_int), ("max_tokens", ctypes.c_int),
-                ("rms_eps", ctypes.c_float), ("scoring", ctypes.c_int)]
+                ("rms_eps", ctypes.c_float), ("scoring", ctypes.c_int), ("shared_fmt", ctypes.c_int)]
 
 
 class MoeError(RuntimeError):
@@ -109,6 +111,9 @@ def lib() -> ctypes.CDLL:
             "moe_sticky_plan": ([vp, vp, i32, vp, i32, vp, vp], i32),
             "moe_image_bytes": ([i32, i32, i32], sz),
             "moe_blob_to_image": ([i32, i32, i32, vp, sz, vp], i32),
+            "moe_requant_int8_rows": ([vp, i32, vp, i64, i64, vp, vp, vp], i32),
+            "moe_read_shared": ([vp, i32, i32, vp, sz], i32),
+            "moe_shared_bytes": ([vp], sz),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -144,9 +149,10 @@ def moe_last_error(ctx) -> str:
 
 
 def make_config(H, I, E, K, n_shared, n_layers, wfmt, n_slots, max_tokens, routed_scale=2.5,
-                norm_topk=1, rms_eps=1e-6, n_group=1, topk_group=1, scoring=0) -> moe_config:
+                norm_topk=1, rms_eps=1e-6, n_group=1, topk_group=1, scoring=0,
+                shared_fmt=0) -> moe_config:
     return moe_config(H, I, E, K, n_shared, n_layers, wfmt, n_group, topk_group, routed_scale,
-                      norm_topk, n_slots, max_tokens, rms_eps, scoring)
+                      norm_topk, n_slots, max_tokens, rms_eps, scoring, shared_fmt)
 
 
 def moe_layer_create(cfg: moe_config, stream: int = 0) -> int:
@@ -329,6 +335,14 @@ def moe_blob_to_image(wfmt, hidden, inter, blob):
     _check("moe_blob_to_image", lib().moe_blob_to_image(wfmt, hidden, inter, blob.ctypes.data,
                                                         blob.nbytes, image.ctypes.data))
     return image
+
+
+def moe_requant_int8_rows(w, src, sinv, O, I, q, s, stream=0) -> int:
+    return lib().moe_requant_int8_rows(_ptr(w), src, _ptr(sinv), O, I, _ptr(q), _ptr(s), stream)
+
+
+def moe_read_shared(ctx, layer, s, dst, nbytes) -> int:
+    return lib().moe_read_shared(ctx, layer, s, _ptr(dst), nbytes)
 
 
 def moe_bucket(ids, T, K, E, cnt, off, perm, active, n_active, stream=0) -> int:

@@ -22,7 +22,7 @@ def build_layer(cfg: LayerConfig, n_layers: int | None = None, max_tokens: int |
     ml = MoeLayer(cfg.H, cfg.I, cfg.E, cfg.K, cfg.n_shared, L, cfg.fmt, n_slots=L * cfg.E,
                   max_tokens=Tm, routed_scale=cfg.routed_scale, norm_topk=cfg.norm_topk,
                   rms_eps=cfg.eps, stream=stream, n_group=cfg.n_group, topk_group=cfg.topk_group,
-                  scoring=cfg.scoring)
+                  scoring=cfg.scoring, shared_fmt=cfg.shared_fmt)
     dev = torch.device("cuda", torch.cuda.current_device())
     n = cfg.I * cfg.H
     wg = torch.empty(n, dtype=torch.float32, device=dev)

@@ -87,6 +87,12 @@ CONFIGS["edge0_decode_k8"] = CONFIGS["edge0_decode"].with_(name="edge0_decode_k8
 # GLM-5.2 shape decode with group-limited routing (8 groups, 4 kept), 4 layers
 CONFIGS["glm_decode_grouped"] = CONFIGS["glm_decode"].with_(name="glm_decode_grouped", n_group=8,
                                                              topk_group=4, n_layers=4, seed=600)
+# per-row int8 shared experts (the converted model's dense precision)
+CONFIGS["int8_shared"] = CONFIGS["tiny"].with_(name="int8_shared", shared_fmt=3, seed=710)
+CONFIGS["mid_int8_shared"] = CONFIGS["mid_row"].with_(name="mid_int8_shared", shared_fmt=3,
+                                                      seed=711)
+CONFIGS["glm_decode_int8_shared"] = CONFIGS["glm_decode"].with_(name="glm_decode_int8_shared",
+                                                                shared_fmt=3, n_layers=4, seed=602)
 # the same decode layer scored by a softmax over all experts (renormalised top-8)
 CONFIGS["glm_decode_softmax"] = CONFIGS["glm_decode"].with_(name="glm_decode_softmax", scoring=1,
                                                             n_layers=4, seed=601)

@@ -1,0 +1,164 @@
+"""Per-row int8 shared experts ([GLM-C] §05 quantize_rows, bits = 8): the
+device quantiser bit-exact against the oracle, the shared slot's bytes, and
+layer forwards (T = 1 .. 64, plain and residual) against the oracle with
+the routed experts in int4 and the shared expert in int8."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from parity import OracleLayer, check_ids, flags, log, oracle_blob, rel_err, REL_TOL
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from int4_weight_expert_amd import moe as M, workload  # noqa: E402
+from int4_weight_expert_amd.layer import MoeLayer  # noqa: E402
+
+KINDS = {"f32": oracle.SRC_F32, "bf16": oracle.SRC_BF16, "fp8": oracle.SRC_FP8_E4M3}
+
+
+@pytest.mark.parametrize("kind", list(KINDS))
+@pytest.mark.parametrize("O,I", [(130, 256), (64, 2048), (7, 6)])
+def test_int8_quantiser_bit_exact(kind, O, I):
+    k = synth.key(950, 0, O, I)
+    if kind == "fp8":
+        w, sinv = synth.fp8_checkpoint(k, O, I, 0.02)
+    elif kind == "bf16":
+        w, sinv = synth.bf16_checkpoint(k, O, I, 0.02), None
+    else:
+        w, sinv = synth.gauss(k, O * I, 0.02).reshape(O, I), None
+    w = w.copy()
+    if O > 2:
+        w[0] = 0
+    src = torch.from_numpy(w.view(np.int16) if w.dtype == np.uint16 else w).cuda()
+    si = None if sinv is None else torch.from_numpy(sinv).cuda()
+    q = torch.empty((O, I), dtype=torch.int8, device="cuda")
+    s = torch.empty(O, dtype=torch.float32, device="cuda")
+    M._check("moe_requant_int8_rows", M.moe_requant_int8_rows(src, KINDS[kind], si, O, I, q, s, 0))
+    torch.cuda.synchronize()
+    rq, rs = oracle.pack_int8_row(oracle.decode_source(w, KINDS[kind], sinv))
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), rq)
+
+
+@pytest.fixture(scope="module", params=["int8_shared", "mid_int8_shared"])
+def case(request):
+    cfg = synth.CONFIGS[request.param]
+    ml = workload.build_layer(cfg, max_tokens=64)
+    yield cfg, ml, OracleLayer(cfg, 0)
+    ml.close()
+
+
+def test_shared_slot_bytes(case):
+    cfg, ml, _ = case
+    assert ml.shared_bytes == oracle.blob_bytes(oracle.W_INT8_ROW, cfg.H, cfg.I)
+    assert np.array_equal(ml.read_shared(0, 0), oracle_blob(cfg, 0, cfg.E))
+
+
+@pytest.mark.parametrize("T", [1, 3, 8, 20, 64])
+@pytest.mark.parametrize("residual", [False, True])
+def test_forward_matches_oracle(case, T, residual):
+    cfg, ml, ref = case
+    x = synth.tokens(cfg, T=T, stream=T)
+    xd = torch.from_numpy(x).cuda()
+    if residual:
+        got = ml.forward_residual(xd.clone(), 0).cpu().numpy()
+    else:
+        got = ml.forward(xd, 0).cpu().numpy()
+        ids, w = ml.route(xd, 0)
+    assert ml.status()[0] == 0
+    r_out, r_ids, r_w, gk, gi = ref.forward(x, residual=residual)
+    if not residual:
+        check_ids(ids.cpu().numpy(), r_ids, w.cpu().numpy(), r_w, gk, gi, f"{cfg.name} T={T}")
+    excluded, _ = flags(gk, gi)
+    err = rel_err(got, r_out, ~excluded)
+    log(f"{cfg.name} T={T} residual={residual}: max|d|/max|ref| = {err:.2e}")
+    assert err <= REL_TOL
+
+
+def test_blob_path_and_errors():
+    cfg = synth.CONFIGS["int8_shared"]
+    ml = MoeLayer(cfg.H, cfg.I, cfg.E, cfg.K, 1, 1, cfg.fmt, n_slots=1, max_tokens=4,
+                  shared_fmt=oracle.W_INT8_ROW)
+    try:
+        blob = oracle_blob(cfg, 0, cfg.E)
+        ml.set_shared(0, 0, blob)
+        assert np.array_equal(ml.read_shared(0, 0), blob)
+        assert M.moe_set_shared(ml.ctx, 0, 0, blob, blob.nbytes - 1) == M.MOE_E_SIZE
+        q = np.zeros(cfg.I * cfg.H // 2, np.uint8)
+        s = np.zeros(cfg.H, np.float32)
+        assert M.moe_import_shared(ml.ctx, 0, 0, q, q, q, s, s, s) == M.MOE_E_UNSUPPORTED
+    finally:
+        ml.close()
+    bad = M.make_config(cfg.H, cfg.I, cfg.E, cfg.K, 1, 1, cfg.fmt, 1, 4, shared_fmt=2)
+    assert M.moe_layer_create_rc(bad)[0] == M.MOE_E_ARG
+
+
+def test_glm_decode_int8_shared():
+    cfg = synth.CONFIGS["glm_decode_int8_shared"]
+    ml = workload.build_layer(cfg, n_layers=1, max_tokens=2)
+    ref = OracleLayer(cfg, 0)
+    try:
+        for T in (1, 2):
+            x = synth.tokens(cfg, T=T, stream=T)
+            got = ml.forward(torch.from_numpy(x).cuda(), 0).cpu().numpy()
+            r_out, _, _, gk, gi = ref.forward(x)
+            excluded, _ = flags(gk, gi)
+            err = rel_err(got, r_out, ~excluded)
+            log(f"GLM decode, int8 shared, T={T}: max|d|/max|ref| = {err:.2e}")
+            assert err <= REL_TOL
+    finally:
+        ml.close()
+
+
+@pytest.mark.parametrize("kind", ["f32", "bf16", "fp8"])
+def test_requant_shared_int8(kind):
+    """Checkpoint tensors on the device -> the int8 shared slot, byte for
+    byte the oracle's blob of the decoded weights."""
+    H, I = 512, 768
+    ml = MoeLayer(H, I, 16, 2, 1, 1, oracle.W_INT4_ROW, n_slots=1, max_tokens=2,
+                  shared_fmt=oracle.W_INT8_ROW)
+    try:
+        srcs = []
+        for t, (O, In) in enumerate([(I, H), (I, H), (H, I)]):
+            k = synth.key(951, 0, t)
+            if kind == "fp8":
+                srcs.append(synth.fp8_checkpoint(k, O, In, 0.02))
+            elif kind == "bf16":
+                srcs.append((synth.bf16_checkpoint(k, O, In, 0.02), None))
+            else:
+                srcs.append((synth.gauss(k, O * In, 0.02).reshape(O, In), None))
+
+        def dev(a):
+            if a is None:
+                return None
+            a = np.ascontiguousarray(a)
+            return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+
+        ml.requant_shared(0, 0, KINDS[kind], *[dev(w) for w, _ in srcs], *[dev(s) for _, s in srcs])
+        want = oracle.pack_expert(oracle.W_INT8_ROW,
+                                  *[oracle.decode_source(w, KINDS[kind], s) for w, s in srcs])
+        assert np.array_equal(ml.read_shared(0, 0), want)
+    finally:
+        ml.close()
+
+
+def test_many_tokens_stay_on_gemv():
+    """T = 300 (past the k-slice partial buffers' 16 and 64 tokens, so the
+    plan drops to fewer slices): int8 shared experts keep every T on the
+    GEMV path."""
+    cfg = synth.CONFIGS["int8_shared"]
+    ml = workload.build_layer(cfg, max_tokens=300)
+    ref = OracleLayer(cfg, 0)
+    try:
+        x = synth.tokens(cfg, T=300, stream=9)
+        got = ml.forward(torch.from_numpy(x).cuda(), 0).cpu().numpy()
+        assert ml.status()[0] == 0
+        r_out, _, _, gk, gi = ref.forward(x)
+        excluded, _ = flags(gk, gi)
+        err = rel_err(got, r_out, ~excluded)
+        log(f"int8_shared T=300: max|d|/max|ref| = {err:.2e}, {int(excluded.sum())} flagged")
+        assert err <= REL_TOL
+    finally:
+        ml.close()
