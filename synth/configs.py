@@ -91,6 +91,8 @@ CONFIGS["glm_decode_grouped"] = CONFIGS["glm_decode"].with_(name="glm_decode_gro
 CONFIGS["int8_shared"] = CONFIGS["tiny"].with_(name="int8_shared", shared_fmt=3, seed=710)
 CONFIGS["mid_int8_shared"] = CONFIGS["mid_row"].with_(name="mid_int8_shared", shared_fmt=3,
                                                       seed=711)
+CONFIGS["affine_int8_shared"] = CONFIGS["mid_affine"].with_(name="affine_int8_shared", shared_fmt=3,
+                                                          seed=712)
 CONFIGS["glm_decode_int8_shared"] = CONFIGS["glm_decode"].with_(name="glm_decode_int8_shared",
                                                                 shared_fmt=3, n_layers=4, seed=602)
 # the same decode layer scored by a softmax over all experts (renormalised top-8)

@@ -42,7 +42,7 @@ def test_int8_quantiser_bit_exact(kind, O, I):
     assert np.array_equal(q.cpu().numpy(), rq)
 
 
-@pytest.fixture(scope="module", params=["int8_shared", "mid_int8_shared"])
+@pytest.fixture(scope="module", params=["int8_shared", "mid_int8_shared", "affine_int8_shared"])
 def case(request):
     cfg = synth.CONFIGS[request.param]
     ml = workload.build_layer(cfg, max_tokens=64)
