@@ -52,12 +52,17 @@ __device__ __forceinline__ float key_score(unsigned long long key)
 constexpr int RT_THREADS = 256;
 
 // Partial layouts (written by the router workgroups with agent-scope stores):
-// logits of expert e, token t, slice row i at part[e * Sp + t * S + i] and
-// statistics (sum, sum of squares) at tpart[t * S2p + 2 i + {0, 1}], with
-// Sp, S2p rounded up to whole 16-byte vectors, so that each reader's values
-// are contiguous.
+// one token: the logit partials of expert e, slice row i at part[e * Sp + i]
+// (the tail's thread e reads its row contiguously); several tokens:
+// part[(i * T + t) * Epad + e] (a block's last workgroup sums them, lanes =
+// experts, into the logits at part_logits(), [t][Epad]).  Statistics (sum,
+// sum of squares) of token t at tpart[t * S2p + 2 i + {0, 1}].  Sp, S2p are
+// rounded up to whole 16-byte vectors.
 __device__ __forceinline__ int router_sp(int T, int S) { return (T * S + 3) & ~3; }
 __device__ __forceinline__ int router_s2p(int S) { return (2 * S + 3) & ~3; }
+// past the largest partial region, S * 8 * Epad floats (the buffer holds
+// (H / 64) * 8 * Epad = 4 S * 8 * Epad)
+__device__ __forceinline__ float* part_logits(const Fwd& f) { return f.part + (size_t)f.S * 8 * f.Epad; }
 
 // 16-byte agent-coherent (sc1) buffer load
 __device__ __forceinline__ float4 bload16_agent(__amdgpu_buffer_rsrc_t r, uint32_t voff,
@@ -108,12 +113,18 @@ __device__ void router_tail(const Fwd& f, float bias_e, int slot_e)
 #pragma unroll
     for (int t = 0; t < NT; ++t) lsum[t] = 0.f;
     float rs0 = 1.f;
+    // (the loads of a step are issued together, before any of them is used)
     if (NT == 1) {
-        float a[64];
+        float a[64], st[64];
         load64(rp, (uint32_t)tid * Sp * 4, 0, S, a);  // S <= 64
+        load64(rt, 0, 0, min(2 * S, 64), st);
         float sum = 0.f, ss = 0.f;
-        for (int c0 = 0; c0 < 2 * S; c0 += 64) {
-            float st[64];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            sum += st[2 * i];
+            ss += st[2 * i + 1];
+        }
+        for (int c0 = 64; c0 < 2 * S; c0 += 64) {  // H > 8192
             load64(rt, 0, c0, 2 * S - c0, st);
 #pragma unroll
             for (int i = 0; i < 32; ++i) {
@@ -129,44 +140,37 @@ __device__ void router_tail(const Fwd& f, float bias_e, int slot_e)
             f.tok[0].rscale = rs0;
         }
     } else {
-        if (tid < T) {
-            float sum = 0.f, ss = 0.f;
-            for (int c0 = 0; c0 < 2 * S; c0 += 64) {
-                float st[64];
-                load64(rt, 0, tid * S2p + c0, 2 * S - c0, st);
+        // expert tid's logits (summed per expert block by its last
+        // workgroup) and, for thread t < T, token t's statistics; every
+        // thread loads (indices clamped), so that no branch separates them
+        const float* lg = part_logits(f);
+        const int ec = min(tid, Epad - 1), tc = min(tid, T - 1);
+        float lv[NT], st[64];
 #pragma unroll
-                for (int i = 0; i < 32; ++i) {
-                    sum += st[2 * i];
-                    ss += st[2 * i + 1];
-                }
+        for (int t = 0; t < NT; ++t) lv[t] = ld_agent(&lg[(size_t)min(t, T - 1) * Epad + ec]);
+        load64(rt, (uint32_t)tc * S2p * 4, 0, min(2 * S, 64), st);
+        float sum = 0.f, ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            sum += st[2 * i];
+            ss += st[2 * i + 1];
+        }
+        for (int c0 = 64; c0 < 2 * S; c0 += 64) {  // H > 8192
+            load64(rt, (uint32_t)tc * S2p * 4, c0, 2 * S - c0, st);
+#pragma unroll
+            for (int i = 0; i < 32; ++i) {
+                sum += st[2 * i];
+                ss += st[2 * i + 1];
             }
+        }
+        if (tid < T) {
             const float rs = f.residual ? 1.0f / sqrtf(ss / (float)H + f.eps) : 1.0f;
             f.tok[tid].xsum = sum;
             f.tok[tid].rscale = rs;
             s_rs[tid] = rs;
         }
-        // expert tid's partials: token t, slice i at t * S + i
-        for (int k0 = 0; k0 < T * S; k0 += 64) {
-            float a[64];
-            load64(rp, (uint32_t)tid * Sp * 4, k0, T * S - k0, a);
-            int t = k0 / S, i = k0 - t * S;
-            float acc = 0.f;
 #pragma unroll
-            for (int k = 0; k < 64; ++k) {
-                acc += a[k];
-                if (++i == S) {
-#pragma unroll
-                    for (int j = 0; j < NT; ++j)
-                        if (j == t) lsum[j] += acc;
-                    acc = 0.f;
-                    i = 0;
-                    ++t;
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < NT; ++j)
-                if (j == t) lsum[j] += acc;
-        }
+        for (int t = 0; t < NT; ++t) lsum[t] = (t < T && tid < E) ? lv[t] : 0.f;
     }
     for (int e = tid; e < 256; e += RT_THREADS) s_cnt[e] = 0;
     for (int i = tid; i < T * 32; i += RT_THREADS) s_cand[i >> 5][i & 31] = 0ull;
@@ -455,13 +459,26 @@ __global__ void __launch_bounds__(RT_THREADS) k_router_small(Fwd f, const float*
         v[u] = make_float4(__uint_as_float(q.x), __uint_as_float(q.y), __uint_as_float(q.z),
                            __uint_as_float(q.w));
     }
-    if (b == 0) {
+    const int nb = gridDim.x;
+    // this span of every token, one coalesced load each (several tokens: the
+    // dot products read it back from LDS; one token reads it through the
+    // scalar cache instead)
+    __shared__ float xl[NT > 1 ? RW : 1][NT][64];
+    float xa[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+        xa[j] = (j < T && (NT > 1 || j % nb == b)) ? X[(size_t)j * H + s * 64 + lane] : 0.f;
+    if (NT > 1) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) xl[NT > 1 ? w : 0][j][lane] = xa[j];
+    }
+    {
         // token sums and sums of squares of this 64-column span; the span
-        // staged as fp16 for the expert GEMVs
+        // staged as fp16 for the expert GEMVs (token j by expert block j mod nb)
 #pragma unroll
         for (int j = 0; j < NT; ++j)
-            if (j < T) {
-                const float xv = X[(size_t)j * H + s * 64 + lane];
+            if (j < T && j % nb == b) {
+                const float xv = xa[j];
                 const float gs = wave_sum(xv), ss = wave_sum(xv * xv);
                 stage_span64(xv, lane, (uint16_t*)(f.xq + (size_t)j * (H / 8) + s * 8),
                              f.xsc + (size_t)j * (H / 64) + s);
@@ -471,17 +488,30 @@ __global__ void __launch_bounds__(RT_THREADS) k_router_small(Fwd f, const float*
                 }
             }
     }
+    if (NT > 1) __syncthreads();
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
         float acc = 0.f;
         if (j < T) {
-            cf32* xs = as_const(X + (size_t)j * H + s * 64);
+            if (NT == 1) {
+                cf32* xs = as_const(X + (size_t)j * H + s * 64);
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                acc = fmaf(v[u].x, xs[4 * u + 0], acc);
-                acc = fmaf(v[u].y, xs[4 * u + 1], acc);
-                acc = fmaf(v[u].z, xs[4 * u + 2], acc);
-                acc = fmaf(v[u].w, xs[4 * u + 3], acc);
+                for (int u = 0; u < 16; ++u) {
+                    acc = fmaf(v[u].x, xs[4 * u + 0], acc);
+                    acc = fmaf(v[u].y, xs[4 * u + 1], acc);
+                    acc = fmaf(v[u].z, xs[4 * u + 2], acc);
+                    acc = fmaf(v[u].w, xs[4 * u + 3], acc);
+                }
+            } else {
+                const float4* x4 = (const float4*)xl[NT > 1 ? w : 0][j];
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    const float4 xq = x4[u];
+                    acc = fmaf(v[u].x, xq.x, acc);
+                    acc = fmaf(v[u].y, xq.y, acc);
+                    acc = fmaf(v[u].z, xq.z, acc);
+                    acc = fmaf(v[u].w, xq.w, acc);
+                }
             }
         }
         red[w][j][lane] = acc;
@@ -492,9 +522,11 @@ __global__ void __launch_bounds__(RT_THREADS) k_router_small(Fwd f, const float*
         float acc = 0.f;
 #pragma unroll
         for (int v2 = 0; v2 < RW; ++v2) acc += red[v2][j][lane];
-        st_agent(&f.part[(size_t)(b * 64 + lane) * Sp + j * S + blockIdx.y], acc);
+        const size_t at = NT == 1 ? (size_t)(b * 64 + lane) * Sp + blockIdx.y
+                                  : ((size_t)blockIdx.y * T + j) * f.Epad + b * 64 + lane;
+        st_agent(&f.part[at], acc);
     }
-    if (b == 0 && w == 0 && lane < T) {
+    if (w == 0 && lane < T && lane % nb == b) {
         float gs = 0.f, ss = 0.f;
 #pragma unroll
         for (int v2 = 0; v2 < RW; ++v2) {
@@ -505,7 +537,36 @@ __global__ void __launch_bounds__(RT_THREADS) k_router_small(Fwd f, const float*
         st_agent(&f.tpart[(size_t)lane * S2p + 2 * blockIdx.y + 1], ss);
     }
 
-    if (!arrive_block(&f.counters[0], gridDim.x * gridDim.y)) return;
+    if (NT == 1) {
+        if (!arrive_block(&f.counters[0], gridDim.x * gridDim.y)) return;
+    } else {
+        // the last of the block's workgroups sums its 64 experts' partials
+        // (slices in order) into the logits; the last block runs the tail
+        if (!arrive_block(&f.counters[1 + b], gridDim.y)) return;
+        // (all loads unconditional, indices clamped, so that they issue together)
+        const int tq = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        constexpr int NJ = (NT + RW - 1) / RW;  // tokens per wavefront
+        float pv[NJ][64];
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) {
+            const int j = tq + jj * RW;
+            const float* pj = f.part + (size_t)min(j, T - 1) * f.Epad + b * 64 + lane;
+#pragma unroll
+            for (int i = 0; i < 64; ++i) {
+                const float v = ld_agent(pj + (size_t)min(i, S - 1) * T * f.Epad);
+                pv[jj][i] = (j < T && i < S) ? v : 0.f;
+            }
+        }
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) {
+            const int j = tq + jj * RW;
+            float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < 64; ++i) acc += pv[jj][i];
+            if (j < T) st_agent(&part_logits(f)[(size_t)j * f.Epad + b * 64 + lane], acc);
+        }
+        if (!arrive_block(&f.counters[0], gridDim.x)) return;
+    }
     router_tail<NT>(f, bias_e, slot_e);
 }
 

@@ -54,9 +54,13 @@ size_t expert_bytes_for(int fmt, size_t H, size_t I)
 }
 
 // k-slices per (group, 64-row block) for a row of `chunks` 16-byte chunks:
-// the fewest that give about 3072 single-wavefront units (12 per CU), each
-// slice a whole number of rolling steps, within the partial buffer and the
-// LDS a unit may use.
+// the fewest that give about 3072 single-wavefront units (12 per CU) whose
+// activation slices are small enough in LDS for 32 units to stay resident
+// per CU (with several tokens per pass the slice grows with the tokens),
+// each slice a whole number of rolling steps, within the partial buffer and
+// the LDS a unit may use.
+constexpr size_t GEMV_LDS_RESIDENT = 160 * 1024 / 32;
+
 int pick_ks(int chunks, int blocks, int step, int max_ks, size_t part_need_per_ks,
             size_t part_bytes, int T, int lds_max)
 {
@@ -66,9 +70,10 @@ int pick_ks(int chunks, int blocks, int step, int max_ks, size_t part_need_per_k
         if (ks > max_ks) break;
         if (chunks % ks != 0 || (chunks / ks) % step != 0) continue;
         if (ks > 1 && part_need_per_ks * ks > part_bytes) break;
-        if (gemv_lds_bytes(chunks / ks, T) > (size_t)lds_max) continue;
+        const size_t lds = gemv_lds_bytes(chunks / ks, T);
+        if (lds > (size_t)lds_max) continue;
         best = ks;
-        if ((int64_t)blocks * ks >= 3072) break;
+        if ((int64_t)blocks * ks >= 3072 && lds <= GEMV_LDS_RESIDENT) break;
     }
     return best;
 }
