@@ -276,18 +276,29 @@ __device__ void router_tail(const Fwd& f, float bias_e, int slot_e)
         __syncthreads();
     }
 
-    // 3a. ranks within each block of 64 experts; rank < K -> candidate
-    for (int pq = w; pq < T * 4; pq += RT_THREADS / 64) {
+    // 3a. ranks within each block of 64 experts; rank < K -> candidate (two
+    //     (token, block) pairs per pass, so that their LDS reads overlap)
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    constexpr int PP = NT > 1 ? 2 : 1;  // one token: one pair per wavefront
+    for (int pq = wu; pq < T * 4; pq += PP * (RT_THREADS / 64)) {
+        const int pq2 = PP == 2 ? pq + RT_THREADS / 64 : pq;
         const int t = pq >> 2, blk = pq & 3;
+        const int t2 = min(pq2, T * 4 - 1) >> 2, blk2 = min(pq2, T * 4 - 1) & 3;
         const unsigned long long* kb = &s_key[t][blk * 64];
-        const unsigned long long mine = kb[lane];
-        int rank = 0;
+        const unsigned long long* kb2 = &s_key[t2][blk2 * 64];
+        const unsigned long long mine = kb[lane], mine2 = kb2[lane];
+        int rank = 0, rank2 = 0;
 #pragma unroll
         for (int e = 0; e < 64; e += 2) {
             const ulonglong2 kk = *(const ulonglong2*)&kb[e];
             rank += (kk.x > mine) + (kk.y > mine);
+            if (PP == 2) {
+                const ulonglong2 kk2 = *(const ulonglong2*)&kb2[e];
+                rank2 += (kk2.x > mine2) + (kk2.y > mine2);
+            }
         }
         if (rank < K) s_cand[t][blk * K + rank] = mine;
+        if (PP == 2 && pq2 < T * 4 && rank2 < K) s_cand[t2][blk2 * K + rank2] = mine2;
     }
     __syncthreads();
     // 3b. ranks among the 4K candidates: global ranks of the top K
