@@ -30,6 +30,10 @@ CASES = {
     "e256_top8": (cfg("e256_top8", 256, 256, 256, 8, seed=904), (1, 8, 33)),
     "every_expert": (cfg("every_expert", 512, 256, 8, 8, seed=905), (1, 3, 70)),
     "top1": (cfg("top1", 512, 256, 16, 1, seed=906), (1, 8, 100)),
+    # the small router's largest partial region at several tokens: 64 column
+    # slices x 8 tokens x 4 expert blocks, each block summed by its own last
+    # workgroup
+    "max_hidden_e256": (cfg("max_hidden_e256", 16384, 256, 256, 2, seed=909), (8, 3)),
 }
 
 
