@@ -436,6 +436,129 @@ __global__ void __launch_bounds__(64) k_gu(Fwd f)
     }
 }
 
+// One workgroup per (group, 64-row block), for layers with few of them (each
+// then gets a CU of its own): wavefront q streams k-slice q exactly as a
+// k_gu unit does, the slices' (sg Wg x, su Wu x) meet in LDS and are summed
+// in slice order (the finalize kernel's order, so h is bit-identical), and
+// token j's h is staged by wavefront j mod KS.  No partials leave the
+// workgroup and no finalize kernel follows.
+__host__ __device__ constexpr int gemv_wave_lds_u4(int CPU, int nt) { return (nt * CPU * 68 + 15) / 16; }
+
+template <int FMT, int NT>
+__global__ void __launch_bounds__(1024) k_gu_wg(Fwd f)
+{
+    extern __shared__ uint4 lds4[];
+    const int lane = threadIdx.x & 63, q = uni((int)(threadIdx.x >> 6));
+    const int KS = f.gu_ks, H = f.H, I = f.I, NB = I / 64, C = H / 32, G = H / 64;
+    const int b = blockIdx.x % NB, gi = blockIdx.x / NB;
+    if (gi >= uni(f.n_groups[0])) return;
+    const Group grp = uni_group(f.groups, gi);
+    const int CPU = C / KS, c0 = q * CPU, row = b * 64 + lane;
+    const int wl = gemv_wave_lds_u4(CPU, NT);
+    uint4* xq = lds4 + q * wl;
+    float2* xs = (float2*)(xq + NT * CPU * 4);
+    float* red = (float*)(lds4 + KS * wl);  // [KS][NT][2][64]
+    const uint8_t* base = grp.base;
+    const uint32_t voff = (uint32_t)lane * 16, toff = (uint32_t)lane * 4;
+    const uint32_t mv = magic_vgpr();
+    const __amdgpu_buffer_rsrc_t rg =
+        make_rsrc(base + ((size_t)b * C + c0) * 1024, (uint32_t)CPU * 1024);
+    const __amdgpu_buffer_rsrc_t ru =
+        make_rsrc(base + (size_t)I * H / 2 + ((size_t)b * C + c0) * 1024, (uint32_t)CPU * 1024);
+    // row format: fp32 row scales after the codes; affine: (scale, min) bf16
+    // pair per row and 64-input group, [row block][group][64] per matrix
+    const uint8_t* tab = base + (size_t)3 * H * I / 2;
+    const __amdgpu_buffer_rsrc_t rtg = make_rsrc(tab + (size_t)b * G * 256, (uint32_t)G * 256);
+    const __amdgpu_buffer_rsrc_t rtu =
+        make_rsrc(tab + ((size_t)I * G + (size_t)b * G * 64) * 4, (uint32_t)G * 256);
+    float sgr = 1.f, sur = 1.f;
+    if (FMT == MOE_W_INT4_ROW && base != nullptr) {
+        sgr = ((const float*)tab)[row];
+        sur = ((const float*)tab)[I + row];
+    }
+    const int nst = CPU / UG;
+#pragma unroll 1
+    for (int p0 = 0; p0 < grp.cnt; p0 += NT) {
+        const int nj = min(NT, grp.cnt - p0);
+        int tt[NT], rr[NT];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            tt[j] = 0;
+            rr[j] = 0;
+            if (j < nj) tok_rows(f, f.perm, grp, p0 + j, tt[j], rr[j]);
+        }
+        float Gt[NT], Ut[NT], ag[NT], au[NT];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) Gt[j] = Ut[j] = ag[j] = au[j] = 0.f;
+        if (base != nullptr) {
+            uint4 A[UG], B[UG];
+            uint32_t PA = 0, PB = 0;
+#pragma unroll
+            for (int k = 0; k < UG; ++k) {
+                A[k] = bload16(rg, voff + k * 1024, 0);
+                B[k] = bload16(ru, voff + k * 1024, 0);
+            }
+            if (FMT != MOE_W_INT4_ROW) {
+                PA = bload4(rtg, toff, (uint32_t)(c0 / 2) * 256);
+                PB = bload4(rtu, toff, (uint32_t)(c0 / 2) * 256);
+            }
+            copy_slice<NT>(f.xq, f.xsc, tt, nj, H / 8, H / 64, c0, CPU, lane, xq, xs);
+            // one rolling step = one span (2 chunks); the last step loads nothing
+#define GU_STEP(I_, LOAD_)                                                               \
+    {                                                                                    \
+        const uint32_t pa = PA, pb = PB;                                                 \
+        _Pragma("unroll") for (int k = 0; k < UG; ++k)                                    \
+        {                                                                                \
+            const uint4 wa = A[k], wb = B[k];                                            \
+            if (LOAD_) {                                                                 \
+                A[k] = bload16(rg, voff + k * 1024, ((I_) + 1) * UG * 1024);             \
+                B[k] = bload16(ru, voff + k * 1024, ((I_) + 1) * UG * 1024);             \
+            }                                                                            \
+            chunk2<NT>(wa, wb, xq, CPU * 4, (I_) * UG + k, nj, mv, ag, au);               \
+        }                                                                                \
+        if (FMT != MOE_W_INT4_ROW && (LOAD_)) {                                          \
+            PA = bload4(rtg, toff, (uint32_t)(c0 / 2 + (I_) + 1) * 256);                 \
+            PB = bload4(rtu, toff, (uint32_t)(c0 / 2 + (I_) + 1) * 256);                 \
+        }                                                                                \
+        _Pragma("unroll") for (int j = 0; j < NT; ++j) if (j < nj)                       \
+        {                                                                                \
+            const float2 sp = xs[j * (CPU / 2) + (I_)];                                  \
+            Gt[j] = fold<FMT>(Gt[j], ag[j], sp, pa);                                     \
+            Ut[j] = fold<FMT>(Ut[j], au[j], sp, pb);                                     \
+            ag[j] = au[j] = 0.f;                                                         \
+        }                                                                                \
+    }
+#pragma unroll 1
+            for (int i = 0; i < nst - 1; ++i) GU_STEP(i, true)
+            GU_STEP(nst - 1, false)
+#undef GU_STEP
+        }
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+            if (j < nj) {
+                red[(q * NT + j) * 128 + lane] = Gt[j] * sgr;
+                red[(q * NT + j) * 128 + 64 + lane] = Ut[j] * sur;
+            }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+            if (j < nj && j % KS == q) {
+                float g = 0.f, u = 0.f;
+                for (int s2 = 0; s2 < KS; ++s2) {
+                    g += red[(s2 * NT + j) * 128 + lane];
+                    u += red[(s2 * NT + j) * 128 + 64 + lane];
+                }
+                const float rs = f.tok[tt[j]].rscale;
+                g *= rs;
+                u *= rs;
+                stage_span64(g / (1.0f + expf(-g)) * u, lane,
+                             (uint16_t*)(f.hq + (size_t)rr[j] * (I / 8) + b * 8),
+                             f.hsc + (size_t)rr[j] * (I / 64) + b);
+            }
+        __syncthreads();
+    }
+}
+
 // gate/up finalize: one wavefront per (row r, block b): fixed-order sum of
 // the k-slices, h = silu(g rs) * (u rs), staged as an fp16 span.
 __global__ void __launch_bounds__(256) k_gu_fin(Fwd f, int n_rows)
@@ -905,10 +1028,41 @@ static hipError_t dn_dispatch(const Fwd& f, hipStream_t st)
 
 bool shared_int8(const Fwd& f) { return f.n_shared > 0 && f.shared_fmt == MOE_W_INT8_ROW; }
 
+size_t gemv_wg_lds_bytes(int chunks_per_slice, int T, int ks)
+{
+    const int nt = tokens_per_pass(T);
+    return (size_t)ks * gemv_wave_lds_u4(chunks_per_slice, nt) * 16 + (size_t)ks * nt * 128 * 4;
+}
+
+template <int FMT, int NT>
+static hipError_t gu_wg_launch(const Fwd& f, hipStream_t st)
+{
+    const int KS = f.gu_ks, CPU = f.H / 32 / KS;
+    const unsigned wgs = (unsigned)(max_groups(f) * (f.I / 64));
+    const size_t lds = gemv_wg_lds_bytes(CPU, f.T, KS);
+    static bool big = false;
+    hipError_t e0 = allow_lds(k_gu_wg<FMT, NT>, lds, big);
+    if (e0 != hipSuccess) return e0;
+    return launch_k(k_gu_wg<FMT, NT>, dim3(wgs), dim3(64 * KS), lds, st, f);
+}
+
+template <int FMT>
+static hipError_t gu_wg_dispatch(const Fwd& f, hipStream_t st)
+{
+    switch (tokens_per_pass(f.T)) {
+    case 1: return gu_wg_launch<FMT, 1>(f, st);
+    case 2: return gu_wg_launch<FMT, 2>(f, st);
+    default: return gu_wg_launch<FMT, 4>(f, st);
+    }
+}
+
 // With int8 shared experts, their units take the int8 branch inside the same
 // launch as the routed experts' units.
 hipError_t launch_gateup_gemv(const Fwd& f, hipStream_t st)
 {
+    if (f.gu_wg)
+        return f.fmt == MOE_W_INT4_ROW ? gu_wg_dispatch<MOE_W_INT4_ROW>(f, st)
+                                       : gu_wg_dispatch<MOE_W_INT4_AFFINE_G64>(f, st);
     const bool s8 = shared_int8(f);
     if (f.fmt == MOE_W_INT4_ROW)
         return s8 ? gu_dispatch<MOE_W_INT4_ROW, true>(f, st) : gu_dispatch<MOE_W_INT4_ROW, false>(f, st);
@@ -925,7 +1079,7 @@ hipError_t launch_down_gemv(const Fwd& f, hipStream_t st)
               : dn_dispatch<MOE_W_INT4_AFFINE_G64, false>(f, st);
 }
 
-bool gateup_needs_finalize(const Fwd& f) { return f.gu_ks > 1; }
+bool gateup_needs_finalize(const Fwd& f) { return f.gu_ks > 1 && !f.gu_wg; }
 
 hipError_t launch_gateup_finalize(const Fwd& f, hipStream_t st)
 {

@@ -88,6 +88,11 @@ void plan_gemv(moe_ctx* c, Fwd& f)
                       rows * g.inter * 2 * 4, c->gpart_bytes, f.T, c->lds_max);
     f.dn_ks = pick_ks(g.inter / 32, max_groups * (g.hidden / 64), gemv_step_chunks(1),
                       gemv_max_dn_ks(), rows * g.hidden * 4, c->ypart_bytes, f.T, c->lds_max);
+    // few (group, block) pairs: one workgroup each, its k-slices reduced in LDS
+    const int gu_blocks = max_groups * (g.inter / 64);
+    f.gu_wg = gu_blocks <= 128 && f.gu_ks > 1 && f.gu_ks <= 16 &&
+              gemv_wg_lds_bytes(g.hidden / 32 / f.gu_ks, f.T, f.gu_ks) <= (size_t)c->lds_max &&
+              !(g.n_shared > 0 && c->shared_fmt == MOE_W_INT8_ROW);
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb)

@@ -87,6 +87,7 @@ struct Fwd {
     // GEMV work plan (see k_gemv.hip); rows = T*K + T*n_shared token rows
     int gu_ks;            // gate/up: k-slices (units) per (group, 64-row block)
     int dn_ks;            // down: same, at most gemv_max_dn_ks()
+    int gu_wg;            // gate/up as one workgroup per (group, block), k-slices as its waves
     float* gpart;         // [rows][I/64][gu_ks][2][64] gate/up partials (gu_ks > 1)
     float* ypart;         // [rows][H/64][dn_ks][64] down partials ([rows][H] when dn_ks = 1)
     // grouped-GEMM path (many tokens): x and h staged per row in xq / hq
@@ -141,6 +142,7 @@ hipError_t launch_router_large(const Fwd& f, hipStream_t st, int stage);
 hipError_t launch_gateup_gemv(const Fwd& f, hipStream_t st);
 hipError_t launch_down_gemv(const Fwd& f, hipStream_t st);
 bool gateup_needs_finalize(const Fwd& f);
+size_t gemv_wg_lds_bytes(int chunks_per_slice, int T, int ks);
 int gemm_max_tiles(int T, int K, int E, int n_shared);
 bool gemm_shape_ok(int H, int I);
 hipError_t launch_gemm_prep(const Fwd& f, hipStream_t st);
