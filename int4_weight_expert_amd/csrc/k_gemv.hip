@@ -80,19 +80,42 @@ __device__ __forceinline__ void chunk2(const uint4& wa, const uint4& wb, const u
                                        int cpu4, int ck, int nj, uint32_t mv, float (&aa)[NT],
                                        float (&ab)[NT])
 {
+    if (NT == 1) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            uint32_t a0, a1, a2, a3, b0, b1, b2, b3;
+            nib_pairs(dw(wa, d), mv, a0, a1, a2, a3);
+            nib_pairs(dw(wb, d), mv, b0, b1, b2, b3);
+            const uint4 xv = xq[ck * 4 + d];
+            aa[0] = dot_dword(a0, a1, a2, a3, xv, aa[0]);
+            ab[0] = dot_dword(b0, b1, b2, b3, xv, ab[0]);
+        }
+        return;
+    }
+    // several tokens: the chunk's codes dequantised once, then per token its
+    // four activation vectors read together (one LDS wait per token and chunk;
+    // the down projection's single matrix does better with the per-dword order)
+    uint32_t pa[16], pb[16];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-        uint32_t a0, a1, a2, a3, b0, b1, b2, b3;
-        nib_pairs(dw(wa, d), mv, a0, a1, a2, a3);
-        nib_pairs(dw(wb, d), mv, b0, b1, b2, b3);
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-            if (j < nj) {
-                const uint4 xv = xq[j * cpu4 + ck * 4 + d];
-                aa[j] = dot_dword(a0, a1, a2, a3, xv, aa[j]);
-                ab[j] = dot_dword(b0, b1, b2, b3, xv, ab[j]);
-            }
+        nib_pairs(dw(wa, d), mv, pa[4 * d], pa[4 * d + 1], pa[4 * d + 2], pa[4 * d + 3]);
+        nib_pairs(dw(wb, d), mv, pb[4 * d], pb[4 * d + 1], pb[4 * d + 2], pb[4 * d + 3]);
     }
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+        if (j < nj) {
+            const uint4* xj = xq + j * cpu4 + ck * 4;
+            const uint4 x0 = xj[0], x1 = xj[1], x2 = xj[2], x3 = xj[3];
+            float a = aa[j], bb = ab[j];
+            a = dot_dword(pa[0], pa[1], pa[2], pa[3], x0, a);
+            bb = dot_dword(pb[0], pb[1], pb[2], pb[3], x0, bb);
+            a = dot_dword(pa[4], pa[5], pa[6], pa[7], x1, a);
+            bb = dot_dword(pb[4], pb[5], pb[6], pb[7], x1, bb);
+            a = dot_dword(pa[8], pa[9], pa[10], pa[11], x2, a);
+            bb = dot_dword(pb[8], pb[9], pb[10], pb[11], x2, bb);
+            aa[j] = dot_dword(pa[12], pa[13], pa[14], pa[15], x3, a);
+            ab[j] = dot_dword(pb[12], pb[13], pb[14], pb[15], x3, bb);
+        }
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t p) { return __uint_as_float(p << 16); }
