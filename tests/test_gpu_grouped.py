@@ -27,8 +27,6 @@ def case(request):
 @pytest.mark.parametrize("T", [1, 3, 8, 20, 64, TMAX])
 def test_forward_matches_oracle(case, T):
     cfg, layer, ref = case
-    if cfg.fmt == oracle.W_INT4_AFFINE_G64 and T > 20:
-        pytest.skip("affine layers run the GEMV path at every T; T <= 20 covers it")
     log(f"{cfg.name} forward T={T}")
     x = synth.tokens(cfg, T=T, stream=T)
     xd = torch.from_numpy(x).cuda()
