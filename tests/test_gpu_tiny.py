@@ -121,8 +121,10 @@ def test_load_expert_blob_path(layer, ref):
 def test_graph_replay_matches_eager(layer):
     """Forwards captured in a HIP graph: every replay, with eager work and
     synchronisation between replays, equals the eager result."""
-    # T = 1 and 8: the GEMV path; T = 64: the grouped-GEMM path
-    xs = [torch.from_numpy(synth.tokens(CFG, T=T, stream=30 + T)).cuda() for T in (1, 8, 64)]
+    # T = 1 and 8: the GEMV path (8: the router's per-block reductions);
+    # T = 4: gate/up as one workgroup per (group, block); T = 64: the
+    # grouped-GEMM path
+    xs = [torch.from_numpy(synth.tokens(CFG, T=T, stream=30 + T)).cuda() for T in (1, 4, 8, 64)]
     eager = [layer.forward(x, 0).clone() for x in xs]
     outs = [torch.empty_like(x) for x in xs]
     cap = torch.cuda.Stream()
