@@ -1,6 +1,6 @@
 // k_small.hip -- the decode-size router (few tokens): split-K router GEMV
 // with the token statistics, then (in the last workgroup to finish) sigmoid,
-// correction bias, wavefront top-k, renormalised weights and the
+// correction bias, top-k by ranks, renormalised weights and the
 // token->expert bucketing that feeds the expert GEMVs.
 //
 // What is computed, cited by page title and section:
@@ -438,10 +438,12 @@ __device__ void router_tail(const Fwd& f, float bias_e, int slot_e)
 // Workgroup (expert block b of 64, slice row q) has 4 wavefronts, each one of
 // 4 consecutive K-slices of 64 input columns (16 float4 chunks, all loads in
 // flight at once), reduced in LDS in a fixed order.  Wavefronts of expert
-// block 0 also form the token sums and sums of squares of their 64 columns
-// and stage them as an fp16 span for the expert GEMVs.  Partials go to
-// f.part / f.tpart (one row per workgroup row q); the last workgroup to
-// arrive runs router_tail.
+// block j mod nb also form token j's sums and sums of squares of their 64
+// columns and stage them as an fp16 span for the expert GEMVs.  Partials go
+// to f.part / f.tpart (one row per workgroup row q).  One token: the last
+// workgroup to arrive runs router_tail.  Several tokens: the last workgroup
+// of each expert block sums that block's partials into logits (slices in
+// order), and the last of those runs router_tail.
 // ---------------------------------------------------------------------------
 
 template <int NT>
