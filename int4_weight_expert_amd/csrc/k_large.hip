@@ -108,13 +108,19 @@ __global__ void __launch_bounds__(512) k_router_mfma(Fwd f)
     float4 xv[4];
     load_x(0, xv);
     store_x(0, xv);
+    // weights one chunk ahead in registers (the next chunk's index clamped,
+    // so the loads carry no branch)
+    float4 bw[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) bw[st] = wb[(size_t)((kb + st * 8) / 4 + h) * 64];
     __syncthreads();
     for (int ch = 0; ch < NCH; ++ch) {
         const int buf = ch & 1;
+        const int cn = min(ch + 1, NCH - 1);
         if (ch + 1 < NCH) load_x(ch + 1, xv);
-        float4 bw[4];
+        float4 bn[4];
 #pragma unroll
-        for (int st = 0; st < 4; ++st) bw[st] = wb[(size_t)((kb + ch * 32 + st * 8) / 4 + h) * 64];
+        for (int st = 0; st < 4; ++st) bn[st] = wb[(size_t)((kb + cn * 32 + st * 8) / 4 + h) * 64];
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
             const float4 a0 = xs[buf][2 * st + h][m], a1 = xs[buf][2 * st + h][32 + m];
@@ -130,6 +136,8 @@ __global__ void __launch_bounds__(512) k_router_mfma(Fwd f)
         }
         if (ch + 1 < NCH) store_x(buf ^ 1, xv);
         __syncthreads();
+#pragma unroll
+        for (int st = 0; st < 4; ++st) bw[st] = bn[st];
     }
     // entry (reg j, lane l) of a 32 x 32 tile: token (j/4)*8 + (l/32)*4 + j%4,
     // expert l%32
