@@ -145,6 +145,28 @@ __device__ __forceinline__ void copy_slice(const uint4* __restrict__ gq,
                                            int nj, int row_q, int row_s, int c0, int CPU,
                                            int lane, uint4* xq, float2* xs)
 {
+    if (CPU <= 16) {
+        // one vector and one span scale per lane and token: every token's
+        // loads issue together (indices clamped, absent tokens read token 0),
+        // then the stores
+        const int i = min(lane, CPU * 4 - 1), k = min(lane, CPU / 2 - 1);
+        uint4 vq[NT];
+        float2 vs[NT];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            const int sj = j < nj ? src[j] : src[0];
+            vq[j] = gq[(size_t)sj * row_q + (size_t)c0 * 4 + i];
+            vs[j] = gs[(size_t)sj * row_s + c0 / 2 + k];
+        }
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+            if (j < nj) {
+                if (lane < CPU * 4) xq[j * CPU * 4 + lane] = vq[j];
+                if (lane < CPU / 2) xs[j * (CPU / 2) + lane] = vs[j];
+            }
+        lds_wave_sync();
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < NT; ++j)
         if (j < nj) {
@@ -592,12 +614,18 @@ __global__ void __launch_bounds__(256) k_gu_fin(Fwd f, int n_rows)
     if (w >= n_rows * NB) return;
     const int r = w / NB, b = w - r * NB;
     const float* p = f.gpart + ((size_t)r * NB + b) * KS * 128;
+    // all loads unconditional (slice index clamped), so that they issue
+    // together; the slices past KS are then zeroed
     float gv[16], uv[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-        gv[v] = v < KS ? p[v * 128 + lane] : 0.f;
-        uv[v] = v < KS ? p[v * 128 + 64 + lane] : 0.f;
+        const int vc = min(v, KS - 1);
+        gv[v] = p[vc * 128 + lane];
+        uv[v] = p[vc * 128 + 64 + lane];
     }
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+        if (v >= KS) gv[v] = uv[v] = 0.f;
     float g = 0.f, u = 0.f;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -720,8 +748,12 @@ __global__ void __launch_bounds__(256) k_combine(Fwd f)
         if (e < f.n_shared) r = T * K + e * T + t;
         else if (e - f.n_shared < K) r = t * K + (e - f.n_shared);
         const float* p = f.ypart + ((size_t)(r < 0 ? 0 : r) * NB + b) * KS * 64 + lane;
+        // unconditional loads (indices clamped), then the absent ones zeroed
 #pragma unroll
-        for (int s = 0; s < 4; ++s) v[e][s] = (r >= 0 && s < KS) ? p[s * 64] : 0.f;
+        for (int s = 0; s < 4; ++s) v[e][s] = p[min(s, KS - 1) * 64];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            if (r < 0 || s >= KS) v[e][s] = 0.f;
     }
     float m = 0.f;
 #pragma unroll
