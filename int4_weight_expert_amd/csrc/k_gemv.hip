@@ -138,14 +138,17 @@ __device__ __forceinline__ float fold(float tot, float a, float2 span, uint32_t 
 }
 
 // Copies the slice's staged activations of the pass's tokens into LDS:
-// xq [NT][CPU*4] uint4 then xs [NT][CPU/2] float2.
-template <int NT>
+// xq [NT][CPU*4] uint4 then xs [NT][CPU/2] float2.  BATCH: for slices of
+// up to 16 chunks, every token's loads first, then the stores (the int8
+// units, which hold more codes in flight, keep the loop form: the batch
+// would push them past 128 VGPRs).
+template <int NT, bool BATCH = true>
 __device__ __forceinline__ void copy_slice(const uint4* __restrict__ gq,
                                            const float2* __restrict__ gs, const int (&src)[NT],
                                            int nj, int row_q, int row_s, int c0, int CPU,
                                            int lane, uint4* xq, float2* xs)
 {
-    if (CPU <= 16) {
+    if (BATCH && CPU <= 16) {
         // one vector and one span scale per lane and token: every token's
         // loads issue together (indices clamped, absent tokens read token 0),
         // then the stores
@@ -257,7 +260,7 @@ __device__ __forceinline__ void gu8_unit(const Fwd& f, int q, int b, int gi, uin
             A[k] = bload16(rg, voff + k * 1024, 0);
             B[k] = bload16(ru, voff + k * 1024, 0);
         }
-        copy_slice<NT>(f.xq, f.xsc, tt, nj, H / 8, H / 64, q * CPU4, CPU4, lane, xq, xs);
+        copy_slice<NT, false>(f.xq, f.xsc, tt, nj, H / 8, H / 64, q * CPU4, CPU4, lane, xq, xs);
 #pragma unroll 1
         for (int sp = 0; sp < nsp; ++sp) {
             float ag[NT], au[NT];
@@ -336,7 +339,7 @@ __device__ __forceinline__ void dn8_unit(const Fwd& f, int q, int b, int gi, uin
         uint4 D[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) D[k] = bload16(rd, voff + k * 1024, 0);
-        copy_slice<NT>(f.hq, f.hsc, rr, nj, I / 8, I / 64, q * CPU4, CPU4, lane, xq, xs);
+        copy_slice<NT, false>(f.hq, f.hsc, rr, nj, I / 8, I / 64, q * CPU4, CPU4, lane, xq, xs);
 #pragma unroll 1
         for (int sp = 0; sp < nsp; ++sp) {
             float a[NT];
