@@ -162,3 +162,35 @@ def test_many_tokens_stay_on_gemv():
         assert err <= REL_TOL
     finally:
         ml.close()
+
+
+def test_graph_replay_int8_shared():
+    """int8 shared experts under HIP-graph capture: every replay, with eager
+    work and synchronisation between replays, equals the eager result."""
+    cfg = synth.CONFIGS["int8_shared"]
+    ml = workload.build_layer(cfg, max_tokens=8)
+    try:
+        xs = [torch.from_numpy(synth.tokens(cfg, T=T, stream=40 + T)).cuda() for T in (1, 4, 8)]
+        eager = [ml.forward(x, 0).clone() for x in xs]
+        outs = [torch.empty_like(x) for x in xs]
+        cap = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        M.moe_set_stream(ml.ctx, cap.cuda_stream)
+        try:
+            with torch.cuda.graph(g, stream=cap):
+                for x, o in zip(xs, outs):
+                    M._check("moe_forward", M.moe_forward(ml.ctx, x, x.shape[0], 0, o))
+        finally:
+            M.moe_set_stream(ml.ctx, torch.cuda.current_stream().cuda_stream)
+        for rep in range(4):
+            for o in outs:
+                o.fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            for o, e in zip(outs, eager):
+                assert torch.equal(o, e), rep
+            other = ml.forward(torch.from_numpy(synth.tokens(cfg, T=3, stream=98)).cuda(), 0)
+            torch.cuda.synchronize()
+            assert torch.isfinite(other).all()
+    finally:
+        ml.close()
