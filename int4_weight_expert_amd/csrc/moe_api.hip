@@ -95,6 +95,14 @@ void plan_gemv(moe_ctx* c, Fwd& f)
               !(g.n_shared > 0 && c->shared_fmt == MOE_W_INT8_ROW);
 }
 
+// Shared expert s of a layer: the layer's n_shared shared slots are
+// consecutive, each shared_bytes long (the shared format may differ from the
+// routed experts', so the routed slot size is not the stride).
+uint8_t* shared_slot(const moe_ctx* c, int layer, int s)
+{
+    return c->shared + ((size_t)layer * c->cfg.n_shared + s) * c->shared_bytes;
+}
+
 bool overlaps(const void* a, size_t na, const void* b, size_t nb)
 {
     const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
@@ -144,7 +152,7 @@ Fwd make_fwd(moe_ctx* c, const float* x, float* out, int T, int layer, int resid
     f.slot_bytes = c->slot_bytes;
     f.shared_fmt = c->shared_fmt;
     f.shared_bytes = c->shared_bytes;
-    f.shared = c->shared + (size_t)layer * g.n_shared * c->shared_bytes;
+    f.shared = shared_slot(c, layer, 0);
     f.part = c->part;
     f.tpart = c->tpart;
     f.S = router_small_slices(g.hidden);
@@ -571,7 +579,7 @@ int moe_set_shared(moe_ctx* c, int layer, int s, const void* blob, size_t nbytes
 {
     if (!c || layer < 0 || layer >= c->cfg.n_layers || s < 0 || s >= c->cfg.n_shared)
         return MOE_E_ARG;
-    return copy_in_blob(c, c->shared + ((size_t)layer * c->cfg.n_shared + s) * c->slot_bytes,
+    return copy_in_blob(c, shared_slot(c, layer, s),
                         blob, nbytes);
 }
 
@@ -580,7 +588,7 @@ int moe_pack_shared(moe_ctx* c, int layer, int s, const float* Wg, const float* 
 {
     if (!c || layer < 0 || layer >= c->cfg.n_layers || s < 0 || s >= c->cfg.n_shared)
         return MOE_E_ARG;
-    return requant_into(c, c->shared + ((size_t)layer * c->cfg.n_shared + s) * c->slot_bytes,
+    return requant_into(c, shared_slot(c, layer, s),
                         MOE_SRC_F32, Wg, Wu, Wd, nullptr, nullptr, nullptr);
 }
 
@@ -590,7 +598,7 @@ int moe_requant_shared(moe_ctx* c, int layer, int s, int src, const void* Wg, co
 {
     if (!c || layer < 0 || layer >= c->cfg.n_layers || s < 0 || s >= c->cfg.n_shared)
         return MOE_E_ARG;
-    return requant_into(c, c->shared + ((size_t)layer * c->cfg.n_shared + s) * c->slot_bytes,
+    return requant_into(c, shared_slot(c, layer, s),
                         src, Wg, Wu, Wd, sinv_g, sinv_u, sinv_d);
 }
 
@@ -599,7 +607,7 @@ int moe_import_shared(moe_ctx* c, int layer, int s, const uint8_t* qg, const uin
 {
     if (!c || layer < 0 || layer >= c->cfg.n_layers || s < 0 || s >= c->cfg.n_shared)
         return MOE_E_ARG;
-    return import_into(c, c->shared + ((size_t)layer * c->cfg.n_shared + s) * c->slot_bytes, qg,
+    return import_into(c, shared_slot(c, layer, s), qg,
                        qu, qd, sg, su, sd);
 }
 
@@ -649,12 +657,13 @@ int moe_status(moe_ctx* c, int32_t* missing, int cap, int* n_missing)
 {
     if (!c) return MOE_E_ARG;
     std::vector<uint32_t> st(c->status_words, 0);
-    hipError_t e = hipStreamSynchronize(c->stream);
-    if (e == hipSuccess)
-        e = hipMemcpy(st.data(), c->status, c->status_words * 4, hipMemcpyDeviceToHost);
-    if (e == hipSuccess) e = hipMemset(c->status, 0, c->status_words * 4);
-    if (e == hipSuccess) e = hipDeviceSynchronize();
-    if (e != hipSuccess) return MOE_E_HIP;
+    // read and clear on the context's stream only (other streams of the
+    // device are not waited for)
+    hipError_t e = hipMemcpyAsync(st.data(), c->status, c->status_words * 4,
+                                  hipMemcpyDeviceToHost, c->stream);
+    if (e == hipSuccess) e = hipMemsetAsync(c->status, 0, c->status_words * 4, c->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+    if (e != hipSuccess) return hip_rc(c, e);
     int n = 0;
     for (size_t wd = 1; wd < c->status_words; ++wd)
         for (int bit = 0; bit < 32; ++bit)
@@ -744,7 +753,7 @@ int moe_read_shared(moe_ctx* c, int layer, int s, void* dst, size_t nbytes)
     if (!c || !dst || layer < 0 || layer >= c->cfg.n_layers || s < 0 || s >= c->cfg.n_shared)
         return MOE_E_ARG;
     if (nbytes != c->shared_bytes) return MOE_E_SIZE;
-    const uint8_t* src = c->shared + ((size_t)layer * c->cfg.n_shared + s) * c->shared_bytes;
+    const uint8_t* src = shared_slot(c, layer, s);
     hipError_t e = launch_slot_to_blob(src, c->staging, c->shared_fmt, c->cfg.hidden,
                                        c->cfg.inter, c->stream);
     if (e == hipSuccess) e = hipMemcpyAsync(dst, c->staging, nbytes, hipMemcpyDefault, c->stream);

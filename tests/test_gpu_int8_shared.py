@@ -7,7 +7,8 @@ import pytest
 
 import oracle
 import synth
-from parity import OracleLayer, check_ids, flags, log, oracle_blob, rel_err, REL_TOL
+from parity import (OracleLayer, check_ids, check_residual, flags, log, oracle_blob, rel_err,
+                    REL_TOL)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -72,9 +73,14 @@ def test_forward_matches_oracle(case, T, residual):
     if not residual:
         check_ids(ids.cpu().numpy(), r_ids, w.cpu().numpy(), r_w, gk, gi, f"{cfg.name} T={T}")
     excluded, _ = flags(gk, gi)
-    err = rel_err(got, r_out, ~excluded)
-    log(f"{cfg.name} T={T} residual={residual}: max|d|/max|ref| = {err:.2e}")
-    assert err <= REL_TOL
+    if residual:
+        err, term = check_residual(x, got, r_out, ~excluded, f"{cfg.name} T={T}")
+        log(f"{cfg.name} T={T} residual: max|d|/max|ref| = {err:.2e} (new x), {term:.2e} "
+            f"(moe term)")
+    else:
+        err = rel_err(got, r_out, ~excluded)
+        log(f"{cfg.name} T={T}: max|d|/max|ref| = {err:.2e}")
+        assert err <= REL_TOL
 
 
 def test_blob_path_and_errors():
@@ -108,6 +114,40 @@ def test_glm_decode_int8_shared():
             err = rel_err(got, r_out, ~excluded)
             log(f"GLM decode, int8 shared, T={T}: max|d|/max|ref| = {err:.2e}")
             assert err <= REL_TOL
+    finally:
+        ml.close()
+
+
+@pytest.mark.parametrize("name", ["int8_shared", "affine_int8_shared"])
+def test_int8_shared_several_layers(name):
+    """Three layers with int8 shared experts: each layer's shared slot (its
+    own stride, not the routed slot size) reads back as the oracle's blob
+    after the device pack, after a host blob (the last layer) and after a
+    requantised fp32 source (layer 1), and a forward on every layer matches
+    the oracle."""
+    cfg = synth.CONFIGS[name].with_(n_layers=3)
+    ml = workload.build_layer(cfg, max_tokens=8)
+    try:
+        L = cfg.n_layers
+        ml.set_shared(L - 1, 0, oracle_blob(cfg, L - 1, cfg.E))
+        wg, wu, wd = synth.expert_weights(cfg, 1, cfg.E)
+        M._check("moe_requant_shared", M.moe_requant_shared(
+            ml.ctx, 1, 0, M.MOE_SRC_F32, torch.from_numpy(wg).cuda(), torch.from_numpy(wu).cuda(),
+            torch.from_numpy(wd).cuda(), None, None, None))
+        torch.cuda.synchronize()
+        for layer in range(L):
+            assert np.array_equal(ml.read_shared(layer, 0), oracle_blob(cfg, layer, cfg.E)), layer
+        for layer in range(L):
+            ref = OracleLayer(cfg, layer)
+            for T in (1, 5):
+                x = synth.tokens(cfg, T=T, stream=20 + layer)
+                got = ml.forward(torch.from_numpy(x).cuda(), layer).cpu().numpy()
+                r_out, _, _, gk, gi = ref.forward(x)
+                excluded, _ = flags(gk, gi)
+                err = rel_err(got, r_out, ~excluded)
+                log(f"{name} layer {layer} T={T}: max|d|/max|ref| = {err:.2e}")
+                assert err <= REL_TOL
+        assert ml.status()[0] == 0
     finally:
         ml.close()
 
