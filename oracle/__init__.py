@@ -14,6 +14,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SO = os.path.join(_HERE, "libmoe_oracle.so")
+# a differently built copy of the same source (e.g. with sanitizers) may be
+# loaded instead; build() still writes the default library
+_LOAD = os.environ.get("MOE_ORACLE_SO", SO)
 
 W_INT4_ROW = 1
 W_INT4_AFFINE_G64 = 2
@@ -34,9 +37,9 @@ _lib = None
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(SO):
+        if _LOAD == SO and not os.path.exists(SO):
             build()
-        L = ctypes.CDLL(SO)
+        L = ctypes.CDLL(_LOAD)
         vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
         L.orc_blob_bytes.argtypes = [i32, i64, i64]
         L.orc_blob_bytes.restype = i64
@@ -70,8 +73,8 @@ def lib() -> ctypes.CDLL:
         L.orc_moe_layer_full.restype = i32
         L.orc_rmsnorm.argtypes = [vp, i32, i64, f32, vp]
         L.orc_rmsnorm.restype = None
-        L.orc_residual_layer.argtypes = [vp, i32, i64, i64, i32, i32, i32, vp, vp, f32, i32, vp,
-                                         i32, vp, f32, vp, vp]
+        L.orc_residual_layer.argtypes = [vp, i32, i64, i64, i32, i32, i32, i32, vp, vp, i32, i32,
+                                         i32, f32, i32, vp, i32, vp, f32, vp, vp]
         L.orc_residual_layer.restype = i32
         L.orc_fp8_e4m3_to_f32.argtypes = [ctypes.c_uint8]
         L.orc_fp8_e4m3_to_f32.restype = f32
@@ -347,7 +350,7 @@ def rmsnorm(x, eps: float = 1e-6):
 
 
 def residual_layer(x, Wr, bias, K, fmt, I, blobs, shared_blobs, eps=1e-6, routed_scale=2.5,
-                   norm_topk=1):
+                   norm_topk=1, n_group=1, topk_group=1, scoring=SCORE_SIGMOID, shared_fmt=0):
     """x <- x + moe(rmsnorm(x)); returns (new x, ids, wts)."""
     x = _f32(x).copy()
     T, H = x.shape
@@ -357,9 +360,9 @@ def residual_layer(x, Wr, bias, K, fmt, I, blobs, shared_blobs, eps=1e-6, routed
     wts = np.empty((T, K), dtype=np.float32)
     ba = _blob_array(blobs)
     sa = _blob_array(shared_blobs) if shared_blobs else None
-    rc = lib().orc_residual_layer(_p(x), T, H, I, E, K, fmt, _p(Wr), _p(bias), routed_scale,
-                                  norm_topk, ctypes.cast(ba, ctypes.c_void_p),
-                                  len(shared_blobs or []),
+    rc = lib().orc_residual_layer(_p(x), T, H, I, E, K, fmt, shared_fmt, _p(Wr), _p(bias),
+                                  scoring, n_group, topk_group, routed_scale, norm_topk,
+                                  ctypes.cast(ba, ctypes.c_void_p), len(shared_blobs or []),
                                   ctypes.cast(sa, ctypes.c_void_p) if sa is not None else None,
                                   eps, _p(ids), _p(wts))
     if rc:

@@ -773,9 +773,11 @@ void orc_rmsnorm(const float *x, int T, int64_t H, float eps, float *out)
     }
 }
 
-/* x [T][H] updated in place: x <- x + moe(rmsnorm(x)). */
+/* x [T][H] updated in place: x <- x + moe(rmsnorm(x)), the layer of
+ * orc_moe_layer_full (any scoring, grouping and shared format). */
 int orc_residual_layer(float *x, int T, int64_t H, int64_t I, int E, int K, int fmt,
-                       const float *Wr, const float *bias, float routed_scale, int norm_topk,
+                       int shared_fmt, const float *Wr, const float *bias, int scoring,
+                       int n_group, int topk_group, float routed_scale, int norm_topk,
                        const uint8_t *const *blobs, int n_shared,
                        const uint8_t *const *shared_blobs, float eps, int32_t *ids, float *wts)
 {
@@ -787,8 +789,9 @@ int orc_residual_layer(float *x, int T, int64_t H, int64_t I, int E, int K, int 
         return -2;
     }
     orc_rmsnorm(x, T, H, eps, xn);
-    int rc = orc_moe_layer(xn, T, H, I, E, K, fmt, Wr, bias, routed_scale, norm_topk, blobs,
-                           n_shared, shared_blobs, m, ids, wts);
+    int rc = orc_moe_layer_full(xn, T, H, I, E, K, fmt, shared_fmt, Wr, bias, scoring, n_group,
+                                topk_group, routed_scale, norm_topk, blobs, n_shared,
+                                shared_blobs, m, ids, wts);
     if (rc == 0)
         for (int64_t j = 0; j < (int64_t)T * H; ++j) x[j] = x[j] + m[j];
     free(xn);

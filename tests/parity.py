@@ -74,15 +74,20 @@ class OracleLayer:
         blobs = [self.cache.get(e) for e in range(cfg.E)]
 
         def one(t):
-            o, _, _ = oracle.moe_layer(xin[t:t + 1], self.W, self.b, cfg.K, cfg.fmt, cfg.I, blobs,
-                                       self.shared, cfg.routed_scale, cfg.norm_topk, cfg.n_group,
-                                       cfg.topk_group, cfg.scoring, cfg.shared_fmt)
+            if residual:
+                o, _, _ = oracle.residual_layer(x[t:t + 1], self.W, self.b, cfg.K, cfg.fmt, cfg.I,
+                                                blobs, self.shared, cfg.eps, cfg.routed_scale,
+                                                cfg.norm_topk, cfg.n_group, cfg.topk_group,
+                                                cfg.scoring, cfg.shared_fmt)
+            else:
+                o, _, _ = oracle.moe_layer(xin[t:t + 1], self.W, self.b, cfg.K, cfg.fmt, cfg.I,
+                                           blobs, self.shared, cfg.routed_scale, cfg.norm_topk,
+                                           cfg.n_group, cfg.topk_group, cfg.scoring,
+                                           cfg.shared_fmt)
             return o[0]
 
         with ThreadPoolExecutor(max_workers=workers) as ex:
             out = np.stack(list(ex.map(one, range(x.shape[0]))))
-        if residual:
-            out = (x + out).astype(np.float32)
         return out, ids, wts, gk, gi
 
 
@@ -127,3 +132,17 @@ def rel_err(out_gpu, out_ref, keep=None) -> float:
     if orf.size == 0:
         return 0.0
     return float(np.abs(og - orf).max() / max(np.abs(orf).max(), 1e-30))
+
+
+def check_residual(x, got_next, ref_next, keep=None, what=""):
+    """A residual step x <- x + moe(rmsnorm(x)) checked twice at REL_TOL:
+    the new x, and the MoE term alone (got_next - x against ref_next - x),
+    so that a large x cannot hide an error in the term.  Returns both
+    relative errors."""
+    x = np.asarray(x, dtype=np.float64)
+    e_next = rel_err(got_next, ref_next, keep)
+    e_term = rel_err(np.asarray(got_next, dtype=np.float64) - x,
+                     np.asarray(ref_next, dtype=np.float64) - x, keep)
+    assert e_next <= REL_TOL, f"{what}: new x max|d|/max|ref| = {e_next:.3e}"
+    assert e_term <= REL_TOL, f"{what}: moe term max|d|/max|ref| = {e_term:.3e}"
+    return e_next, e_term

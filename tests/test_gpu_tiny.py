@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 import synth
-from parity import OracleLayer, check_ids, flags, log, rel_err, REL_TOL
+from parity import OracleLayer, check_ids, flags, log, rel_err, REL_TOL, check_residual
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -54,9 +54,8 @@ def test_residual_matches_oracle(layer, ref, T):
     layer.forward_residual(xd, 0)
     r_out, r_ids, r_w, gk, gi = ref.forward(x, residual=True)
     excluded, _ = flags(gk, gi)
-    err = rel_err(xd.cpu().numpy(), r_out, ~excluded)
-    log(f"  max|d|/max|ref| = {err:.3e}")
-    assert err <= REL_TOL
+    e_next, e_term = check_residual(x, xd.cpu().numpy(), r_out, ~excluded, f"T={T}")
+    log(f"  max|d|/max|ref| = {e_next:.3e} (new x), {e_term:.3e} (moe term)")
 
 
 def test_deterministic(layer):

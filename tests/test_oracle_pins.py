@@ -51,16 +51,30 @@ def test_edge0_expert_bytes_match_byte_account():
 
 
 def test_mac_counts_match_dataflow_page():
+    """The oracle's own expert counts its multiply-adds: with every code +1,
+    every scale 1 and x = 1, a gate (or up) row sums exactly its H inputs, so
+    g = u = H and h = silu(H) * H = H^2 (exp(-6144) underflows to 0); a down
+    row sums its I values of h, so y = I * h.  Rows times inputs per row give
+    the MACs of one token through one expert."""
     g = _golden("expert_sizes.txt")
     H, I, E = 6144, 2048, 256
-    # the oracle's dequantised matrices of one GLM-shape expert hold exactly
-    # 3*H*I weights, one MAC each per token
-    wg, wu, wd = (np.zeros((I, 64)), np.zeros((I, 64)), np.zeros((64, I)))
-    assert wg.shape[0] == I and wd.shape[1] == I
-    macs = 3 * H * I
+    nb = oracle.blob_bytes(ROW, H, I)
+    blob = np.full(nb, 0x11, dtype=np.uint8)            # two +1 codes per byte
+    blob[3 * H * I // 2:] = np.ones(2 * I + H, dtype=np.float32).view(np.uint8)
+    y, h = oracle.expert(ROW, H, I, blob, np.ones(H, dtype=np.float32))
+    assert h.shape == (I,) and y.shape == (H,)
+    per_gate_row = np.sqrt(h.astype(np.float64))         # g = u = inputs per row
+    per_down_row = y.astype(np.float64) / float(h[0])   # inputs per down row
+    assert np.all(per_gate_row == H) and np.all(per_down_row == I)
+    macs = int(per_gate_row.sum() * 2 + per_down_row.sum())
+    assert macs == 3 * H * I
     assert round(macs / 1e6, 1) == float(g["glm_expert_mmacs"])
     assert round(8 * macs / 1e6) == float(g["glm_routed8_mmacs"])
-    assert round(H * E / 1e6, 1) == float(g["glm_router_mmacs"])
+    # the router: one logit per expert, each a dot product over H inputs
+    _, _, logits, _, _, _ = oracle.route(np.ones((1, H), np.float32),
+                                         np.ones((E, H), np.float32), np.zeros(E, np.float32), 8)
+    assert logits.shape == (1, E) and np.all(logits == H)
+    assert round(logits.size * float(logits[0, 0]) / 1e6, 1) == float(g["glm_router_mmacs"])
 
 
 # ---------------------------------------------------------------------------
@@ -614,6 +628,44 @@ def test_layer_missing_expert_is_an_error():
     holes[int(ids[0, 0])] = None
     with pytest.raises(ValueError):
         oracle.moe_layer(x, W, b, cfg.K, cfg.fmt, cfg.I, holes, shared)
+
+
+def _ones_blob(H, I, s_gu=1.0, s_d=1.0):
+    """Row-format blob with every code +1: gate/up row scales s_gu, down s_d."""
+    blob = np.full(oracle.blob_bytes(ROW, H, I), 0x11, dtype=np.uint8)
+    sc = np.concatenate([np.full(2 * I, s_gu), np.full(H, s_d)]).astype(np.float32)
+    blob[3 * H * I // 2:] = sc.view(np.uint8)
+    return blob
+
+
+def test_residual_layer_closed_form():
+    """x <- x + moe(rmsnorm(x)) with a routed expert and a shared expert whose
+    codes are all +1: for v = rmsnorm(x) and S = sum(v), an all-ones gate/up
+    row with scale s gives g = u = s*S, h = silu(s*S) * s*S, and the all-ones
+    down rows give y = I*h; the one chosen expert (K = 1, renormalised weight
+    = routed_scale) enters with 2.5, the shared expert with 1.  Written in
+    float64 from x directly: S = sum(x) / sqrt(mean(x^2) + eps)."""
+    H, I, E, eps = 64, 32, 4, 1e-6
+    x = (synth.gauss(synth.key(31, 0, synth.T_X, 0), 3 * H, 1.0) * 3.0).reshape(3, H)
+    W = np.zeros((E, H), np.float32)
+    b = np.array([0.0, 0.3, 0.0, 0.1], np.float32)       # sigma = 0.5 everywhere: expert 1 wins
+    zero = np.zeros(oracle.blob_bytes(ROW, H, I), np.uint8)
+    blobs = [zero, _ones_blob(H, I), zero, zero]
+    shared = [_ones_blob(H, I, s_gu=0.5)]
+    got, ids, wts = oracle.residual_layer(x, W, b, 1, ROW, I, blobs, shared, eps=eps)
+    assert np.all(ids == 1) and np.all(wts == np.float32(2.5))
+    xd = x.astype(np.float64)
+    S = xd.sum(axis=1) / np.sqrt((xd * xd).mean(axis=1) + eps)
+    silu = lambda z: z / (1 + np.exp(-z))
+    term = 2.5 * I * S * silu(S) + I * (0.5 * S) * silu(0.5 * S)
+    want = xd + term[:, None]
+    assert np.allclose(got, want, rtol=2e-6, atol=2e-6 * np.abs(term).max())
+    # the other readings differ: no norm (x + moe(x)) or the norm after the add
+    S_raw = xd.sum(axis=1)
+    assert not np.allclose(got[:, 0], xd[:, 0] + 2.5 * I * S_raw * silu(S_raw), rtol=1e-3)
+    # zero experts: x comes back bit for bit
+    same, _, _ = oracle.residual_layer(x, W, b, 1, ROW, I, [zero] * E, [zero], eps=eps)
+    assert np.array_equal(same, x)
 
 
 def test_rmsnorm_closed_form_and_scale_invariance():
