@@ -60,7 +60,7 @@ typedef struct moe_ctx moe_ctx;
 #define MOE_E_NOT_RESIDENT (-5) /* a selected expert had no slot (moe_status) */
 #define MOE_E_HIP (-6)          /* a HIP runtime call failed */
 #define MOE_E_UNSUPPORTED (-7)  /* configuration outside what the kernels do */
-#define MOE_E_RANGE (-8)        /* fp16 activation overflow on the GEMM path (moe_status) */
+#define MOE_E_RANGE (-8)        /* an input row was not finite (moe_status) */
 #define MOE_E_BUSY (-9)         /* slot still named by the slot table (asynchronous loads) */
 
 /* expert weight formats (layout of an expert blob, see moe_load_expert) */
@@ -75,8 +75,8 @@ typedef struct moe_ctx moe_ctx;
                                to one (norm_topk = 1, [EDGE0] §七 softmax-top-k); one group */
 
 typedef struct moe_config {
-    int hidden;         /* H, multiple of 64 */
-    int inter;          /* I, multiple of 64 */
+    int hidden;         /* H, multiple of 256, at most 16384 (affine: multiple of 512) */
+    int inter;          /* I, multiple of 256 */
     int n_experts;      /* E, 1..256 routed experts */
     int top_k;          /* K, 1..min(8, E) */
     int n_shared;       /* 0 or 1 always-active shared experts (weight 1) */
@@ -103,7 +103,10 @@ typedef struct moe_config {
                          * expert GEMVs (the grouped GEMM is not used). */
 } moe_config;
 
-/* Creates a context on the current HIP device: allocates the slot pool
+/* Creates a context on the current HIP device ([GLM-C] §11: the layer's
+ * shape and routing constants; [COLI] §1.1-1.2: n_group, topk_group,
+ * norm_topk and routed_scale read from the model's config, an unsupported
+ * combination stopping the load): allocates the slot pool
  * (n_slots * moe_expert_bytes), per-layer router weights, bias, shared
  * experts and slot table (all entries -1 = not resident), and a workspace
  * sized for max_tokens.  stream: a hipStream_t (NULL = default stream).
@@ -125,8 +128,10 @@ int moe_set_stream(moe_ctx *ctx, void *stream);
  * Returns 0 for a null context. */
 size_t moe_expert_bytes(const moe_ctx *ctx);
 
-/* Sets layer's router: W [E][H] fp32 row-major, bias [E] fp32; host or
- * device pointers.  Synchronous: returns after the data is copied in.
+/* Sets layer's router ([FLOW] §三 Step 6a: the 6144 -> 256 gate; [GLM-C]
+ * §11: its fp32 weight and the correction bias added to the sigmoid before
+ * the top-K): W [E][H] fp32 row-major, bias [E] fp32; host or device
+ * pointers.  Synchronous: returns after the data is copied in.
  * Errors: MOE_E_ARG (null, layer out of range). */
 int moe_set_router(moe_ctx *ctx, int layer, const float *W, const float *bias);
 
@@ -296,14 +301,22 @@ int moe_forward(moe_ctx *ctx, const float *x, int T, int layer, float *out);
  * x: device pointer [T][H].  Errors: MOE_E_ARG. */
 int moe_forward_residual(moe_ctx *ctx, float *x, int T, int layer);
 
-/* Router only: ids [T][K] int32 (descending score), w [T][K] fp32, device
+/* Router only ([GLM-C] §11 routing: sigmoid + bias picks the top K, the
+ * plain sigmoid of the picked experts weighs; [EDGE0] §七 renormalised
+ * weights): ids [T][K] int32 (descending score), w [T][K] fp32, device
  * pointers.  Errors: MOE_E_ARG. */
 int moe_route(moe_ctx *ctx, const float *x, int T, int layer, int32_t *ids, float *w);
 
-/* Synchronises the stream and reports errors found on the device since the
- * last call: MOE_E_NOT_RESIDENT (then up to cap missing (layer*E + id)
- * codes go to missing_ids, *n_missing = their count), MOE_E_RANGE, or
- * MOE_OK.  Clears the device status.  missing_ids/n_missing may be null. */
+/* The GPU path's success-or-failure report ([GLM-C] §12: the matmul
+ * dispatcher tries the GPU entry first and takes another route when it
+ * reports failure; here nothing falls back, the caller decides).  Synchronises
+ * the context's stream (not the whole device) and reports errors found on
+ * the device since the last call: MOE_E_NOT_RESIDENT (a selected expert had
+ * no slot; up to cap missing (layer*E + id) codes go to missing_ids,
+ * *n_missing = their count), MOE_E_RANGE (a row of x held a NaN or an
+ * infinity, or values whose squares overflow fp32; those rows' outputs are
+ * unspecified), or MOE_OK.  Clears the device status on the same stream.
+ * missing_ids/n_missing may be null.  Errors: MOE_E_ARG, MOE_E_HIP. */
 int moe_status(moe_ctx *ctx, int32_t *missing_ids, int cap, int *n_missing);
 
 /* Description of the last HIP error a call of this context hit (the cause

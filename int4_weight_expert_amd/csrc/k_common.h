@@ -239,6 +239,17 @@ __device__ __forceinline__ void stage_row(const float* __restrict__ row, int len
 // waits for the caller's stores to complete (s_waitcnt vmcnt(0)), then
 // bumps the counter; whoever sees the last count reads everything.  The
 // last arriver resets the counter for the next launch.
+// Why this orders the hand-off without release/acquire: (1) the compiler
+// may reorder relaxed atomics to different addresses, so a compiler-only
+// fence (__atomic_signal_fence, no instruction) sits on both sides of the
+// arrival and keeps the data stores before it and the reader's loads after
+// it in program order; (2) in hardware, vmcnt(0) returns only once every
+// earlier vector store has been acknowledged by the memory level that makes
+// it agent-coherent (sc1), and the counter update is issued after that;
+// (3) the reader's sc1 loads miss the non-coherent caches and are issued
+// only after its fetch_add has returned the last count (a value dependence
+// through the branch).  An agent-scope acq_rel would instead write back
+// and invalidate the whole L2, which costs more than the hand-off.
 __device__ __forceinline__ void st_agent(float* p, float v)
 {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -253,6 +264,7 @@ __device__ __forceinline__ float ld_agent(const float* p)
 __device__ __forceinline__ bool arrive_block(uint32_t* counter, uint32_t expected)
 {
     __shared__ int s_last;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -264,12 +276,14 @@ __device__ __forceinline__ bool arrive_block(uint32_t* counter, uint32_t expecte
     const bool last = s_last;
     if (last && threadIdx.x == 0)
         __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     return last;
 }
 
 // single-wavefront arrival
 __device__ __forceinline__ bool arrive_wave(uint32_t* counter, uint32_t expected)
 {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0);
     uint32_t prev = 0;
     if ((threadIdx.x & 63) == 0)
@@ -278,7 +292,16 @@ __device__ __forceinline__ bool arrive_wave(uint32_t* counter, uint32_t expected
     const bool last = prev == expected - 1;
     if (last && (threadIdx.x & 63) == 0)
         __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     return last;
+}
+
+// A token whose sum of squares is not finite (x holds a NaN or an infinity,
+// or magnitudes whose squares overflow fp32) sets the range status bit
+// (moe_status reports MOE_E_RANGE); its outputs are then unspecified.
+__device__ __forceinline__ void flag_range(const Fwd& f, float ss)
+{
+    if (!(ss <= 3.402823466e38f)) atomicOr(&f.status[0], (uint32_t)STATUS_RANGE);
 }
 
 // Wave-uniform copies (SGPRs) of values the compiler cannot prove uniform:

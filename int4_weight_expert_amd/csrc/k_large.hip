@@ -55,6 +55,7 @@ __global__ void __launch_bounds__(256) k_tokstats(Fwd f)
     if (lane == 0) {
         f.tok[t].xsum = sum;
         f.tok[t].rscale = f.residual ? 1.0f / sqrtf(ss / (float)H + f.eps) : 1.0f;
+        flag_range(f, ss);
     }
 }
 

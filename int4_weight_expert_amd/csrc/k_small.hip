@@ -138,6 +138,7 @@ __device__ void router_tail(const Fwd& f, float bias_e, int slot_e)
         if (tid == 0) {
             f.tok[0].xsum = sum;
             f.tok[0].rscale = rs0;
+            flag_range(f, ss);
         }
     } else {
         // expert tid's logits (summed per expert block by its last
@@ -168,6 +169,7 @@ __device__ void router_tail(const Fwd& f, float bias_e, int slot_e)
             f.tok[tid].xsum = sum;
             f.tok[tid].rscale = rs;
             s_rs[tid] = rs;
+            flag_range(f, ss);
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t) lsum[t] = (t < T && tid < E) ? lv[t] : 0.f;

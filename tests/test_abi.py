@@ -82,3 +82,21 @@ def test_package_does_not_import_the_oracle():
                 txt = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert "import oracle" not in txt and "from oracle" not in txt, f
                 assert "moe_oracle" not in txt, f
+
+
+def test_every_status_code_has_a_producing_path():
+    """Each MOE_E_* code the header defines is returned by some path of the
+    library source (the GPU tests produce each one at run time; MOE_E_HIP
+    is produced here, without a GPU, by create)."""
+    hdr = open(HEADER, encoding="utf-8").read()
+    codes = re.findall(r"#define\s+(MOE_E_\w+)\s", hdr)
+    assert len(codes) >= 9
+    csrc = os.path.join(ROOT, "int4_weight_expert_amd", "csrc")
+    src = "".join(open(os.path.join(csrc, f), encoding="utf-8").read()
+                  for f in os.listdir(csrc) if f.endswith((".hip", ".h")))
+    for code in codes:
+        produced = re.search(r"(return|\?|:)\s*" + code + r"\b", src)
+        assert produced, f"{code} is never returned"
+    # the device-side codes are raised by a status bit that a kernel sets
+    assert "atomicOr(&f.status[0], (uint32_t)STATUS_RANGE)" in src
+    assert "atomicOr(&f.status[0], (uint32_t)STATUS_NOT_RESIDENT)" in src
