@@ -38,7 +38,10 @@ int dalloc(moe_ctx* c, P** p, size_t bytes)
 {
     void* q = nullptr;
     if (bytes == 0) bytes = 256;
-    if (hipMalloc(&q, bytes) != hipSuccess) return MOE_E_NOMEM;
+    if (hipMalloc(&q, bytes) != hipSuccess) {
+        (void)hipGetLastError();  // a failed allocation must not surface in a later call
+        return MOE_E_NOMEM;
+    }
     c->allocs.push_back(q);
     *p = (P*)q;
     return MOE_OK;
@@ -530,7 +533,10 @@ int moe_set_router(moe_ctx* c, int layer, const float* W, const float* bias)
     if (!c || !W || !bias || layer < 0 || layer >= c->cfg.n_layers) return MOE_E_ARG;
     const size_t H = c->cfg.hidden, E = c->cfg.n_experts;
     float* tmp = nullptr;
-    if (hipMalloc(&tmp, E * H * 4) != hipSuccess) return MOE_E_NOMEM;
+    if (hipMalloc(&tmp, E * H * 4) != hipSuccess) {
+        (void)hipGetLastError();
+        return MOE_E_NOMEM;
+    }
     hipError_t e = hipMemcpyAsync(tmp, W, E * H * 4, hipMemcpyDefault, c->stream);
     if (e == hipSuccess)
         e = launch_router_to_internal(tmp, c->wr + (size_t)layer * c->Epad * H, (int)E, c->Epad,

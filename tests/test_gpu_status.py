@@ -74,7 +74,7 @@ def test_non_finite_input_is_reported(layer, T):
 
 def test_missing_expert_code(layer):
     x = synth.tokens(CFG, T=1, stream=401)
-    _, r_ids, _, _, _ = OracleLayer(CFG, 0).route(x)
+    r_ids = OracleLayer(CFG, 0).route(x)[0]
     victim = int(r_ids[0, 0])
     layer.map(0, victim, -1)
     try:
