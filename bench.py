@@ -7,10 +7,15 @@ rotating through 8 resident layers (38.7 GB of experts in the slot pool, so
 the 256 MB Infinity Cache cannot serve repeats).  Inputs are resident in HBM
 before the timed region.  Prints one JSON line.
 
-Also measured (under "extra"): the 8-token speculative-verify batch through
-8 chained layers, the Edge0-shape 40-layer decode step (affine int4 g64,
-top-4 and top-8), and the 2048-token prefill layer; and the CPU oracle on a
-bounded sample of the decode workload (cpu_baseline).
+The timed region is one replay of a HIP graph holding exactly --steps
+forwards (layers in turn), bracketed by a full synchronisation and events;
+the headline is the median over several such replays.  Also measured
+(under "extra"): a streaming-read probe (the HBM read rate this part
+reaches), the 8-token speculative-verify batch through 8 chained layers,
+the Edge0-shape 40-layer decode step (affine int4 g64, top-4 and top-8), the
+2048-token prefill layer and the variants of the decode layer; and the CPU
+oracle on bounded samples of each workload, one thread and all host cores
+(cpu_baseline, and extra.cpu_baseline_by_workload).
 """
 from __future__ import annotations
 
@@ -57,9 +62,14 @@ def gateup_unit_bytes(cfg) -> int:
     return 2 * (cfg.I * cfg.H // 2) + 2 * 4 * cfg.I * (cfg.H // 64)
 
 
-def time_graph(torch, ml, step_fns, steps: int, warmup: int):
-    """Captures the step functions (one per layer) into a HIP graph, checks a
-    replay against eager results, then times `steps` steps by replays."""
+def time_graph(torch, ml, step_fns, steps: int, warmup: int, replays: int = 5):
+    """Captures exactly `steps` step calls (step_fns[i % len], so the
+    resident layers rotate) into one HIP graph and times `replays` replays
+    of it, each bracketed by events on the replay stream after a full
+    synchronisation.  Returns (graph, median seconds per step, stats): the
+    headline is the median replay divided by `steps`; the stats also carry
+    p10/p90 and the host wall clock of each bracketed replay."""
+    import numpy as np
     from int4_weight_expert_amd import moe as M
     L = len(step_fns)
     for i in range(warmup):
@@ -70,38 +80,31 @@ def time_graph(torch, ml, step_fns, steps: int, warmup: int):
     M.moe_set_stream(ml.ctx, cap.cuda_stream)
     try:
         with torch.cuda.graph(g, stream=cap):
-            for fn in step_fns:
-                fn()
+            for i in range(steps):
+                step_fns[i % L]()
     finally:
         M.moe_set_stream(ml.ctx, torch.cuda.current_stream().cuda_stream)
-    reps = max(1, steps // L)
     for _ in range(2):
         g.replay()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        g.replay()
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    return g, dt / (reps * L), reps * L
-
-
-def replay_percentiles(torch, g, n_layers: int, reps: int = 50):
-    """Median, p10 and p90 of the per-layer time over `reps` single graph
-    replays (each replay runs every resident layer once), from events
-    recorded around each replay on the replay stream."""
-    import numpy as np
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
-    torch.cuda.synchronize()
-    for a, b in evs:
+    ev, wall = [], []
+    for _ in range(replays):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
         a.record()
         g.replay()
         b.record()
-    torch.cuda.synchronize()
-    us = np.array([a.elapsed_time(b) * 1e3 / n_layers for a, b in evs])
-    return {"median_us_per_layer": float(np.median(us)), "p10_us_per_layer": float(np.quantile(us, 0.1)),
-            "p90_us_per_layer": float(np.quantile(us, 0.9)), "replays": reps}
+        torch.cuda.synchronize()
+        wall.append(time.perf_counter() - t0)
+        ev.append(a.elapsed_time(b) * 1e-3)
+    per = np.array(ev) / steps
+    stats = {"steps_per_replay": steps, "replays": replays,
+             "median_us_per_step": float(np.median(per)) * 1e6,
+             "p10_us_per_step": float(np.quantile(per, 0.1)) * 1e6,
+             "p90_us_per_step": float(np.quantile(per, 0.9)) * 1e6,
+             "wall_us_per_step_mean": float(np.mean(wall)) / steps * 1e6}
+    return g, float(np.median(per)), stats
 
 
 def time_eager(torch, step_fns, steps: int):
@@ -145,12 +148,10 @@ def bench_decode(torch, args, result):
     for l in range(L):
         fns[l]()
         eager_ref.append(outs[l].clone())
-    g, t_graph, n_timed = time_graph(torch, ml, fns, args.steps, args.warmup)
+    g, t_graph, pct = time_graph(torch, ml, fns, args.steps, args.warmup,
+                                 replays=max(5, -(-400 // args.steps)))
+    n_timed = args.steps
     graph_ok = all(torch.equal(outs[l], eager_ref[l]) for l in range(L))
-    pct = replay_percentiles(torch, g, L)
-    g.replay()
-    torch.cuda.synchronize()
-    graph_ok = graph_ok and all(torch.equal(outs[l], eager_ref[l]) for l in range(L))
     t_eager = time_eager(torch, fns, args.steps)
     kt, nf = kernel_times(torch, ml, fns, args.steps)
     rc, missing = ml.status()
@@ -206,8 +207,7 @@ def bench_rotated(torch, name, steps, result):
     fns = [(lambda l=l: ml.forward(xs[l], l, outs[l])) for l in range(L)]
     for fn in fns:
         fn()
-    g, t, _ = time_graph(torch, ml, fns, steps, 20)
-    pct = replay_percentiles(torch, g, L)
+    g, t, pct = time_graph(torch, ml, fns, steps, 20)
     layer_bytes = glm_bytes(cfg, cfg.K, 1)
     result["extra"][name] = {
         "T": 1, "layers": L, "n_group": cfg.n_group, "topk_group": cfg.topk_group,
@@ -415,10 +415,9 @@ def bench_chain(torch, name, steps, result):
     torch.cuda.synchronize()
     t_eager = (time.perf_counter() - t0) / (reps * L)
     x.copy_(x0)
-    g, t_graph, _ = time_graph(torch, ml, fns, reps * L, 0)
+    g, t_graph, pct = time_graph(torch, ml, fns, reps * L, 0)
     t = t_graph
     x.copy_(x0)
-    pct = replay_percentiles(torch, g, L, reps=20)
     bytes_layer = float(np.mean([glm_bytes(cfg, u, cfg.T) for u in distinct]))
     result["extra"][name] = {
         "T": cfg.T, "layers": L, "us_per_layer": t * 1e6, "us_per_layer_eager": t_eager * 1e6,
@@ -462,11 +461,8 @@ def bench_prefill(torch, steps, result):
     torch.cuda.synchronize()
     t_eager = (time.perf_counter() - t0) / n
     # one forward captured in a HIP graph and replayed (as the decode bench)
-    g, t, _ = time_graph(torch, ml, [lambda: ml.forward(x, 0, out)], n, 2)
+    g, t, pct = time_graph(torch, ml, [lambda: ml.forward(x, 0, out)], n, 2)
     graph_ok = bool(torch.equal(out, eager_out))
-    pct = replay_percentiles(torch, g, 1, reps=n)
-    pct = {"median_ms": pct["median_us_per_layer"] * 1e-3, "p10_ms": pct["p10_us_per_layer"] * 1e-3,
-           "p90_ms": pct["p90_us_per_layer"] * 1e-3, "replays": n}
     if not graph_ok:
         t = t_eager
     kt, _ = kernel_times(torch, ml, [lambda: ml.forward(x, 0, out)], 3)
@@ -502,6 +498,62 @@ def copy_probe(torch, result):
     torch.cuda.empty_cache()
 
 
+def stream_ceiling(torch, result, unit_bytes: int):
+    """The HBM read rate a plain streaming kernel reaches here (the
+    achievable ceiling the byte-bound kernels are held against): reads of
+    `unit_bytes` (the decode gate/up launch's algorithmic bytes) rotated
+    over 16 disjoint windows of a 2 GiB buffer, so that the 256 MB Infinity
+    Cache cannot serve repeats, and reads of the whole 2 GiB; grid sizes and
+    plain or non-temporal loads swept, each launch timed with events on the
+    current stream (median of 48)."""
+    import ctypes
+    import numpy as np
+    lib = ctypes.CDLL(os.path.join(ROOT, "int4_weight_expert_amd", "libhbm_probe.so"))
+    lib.hbm_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]
+    lib.hbm_probe_read.restype = ctypes.c_int
+    total = 2 << 30
+    buf = torch.full((total,), 0x5A, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(16384, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream()
+    unit = unit_bytes // 4096 * 4096
+    win = total // 16
+
+    def run(nbytes, blocks, nt, n=48, rotate=True):
+        evs = []
+        for i in range(n):
+            off = (i % 16) * win if rotate else 0
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            rc = lib.hbm_probe_read(buf.data_ptr() + off, nbytes, blocks, nt, sink.data_ptr(),
+                                    0xDEADBEEF, st.cuda_stream)
+            b.record(st)
+            if rc != 0:
+                raise RuntimeError(f"hbm_probe_read: hip error {rc}")
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        ms = np.median([a.elapsed_time(b) for a, b in evs])
+        return nbytes / (ms * 1e-3) / 1e9, float(ms)
+
+    rows = []
+    for nt in (0, 1):
+        for blocks in (1024, 2048, 4096, 8192):
+            gbs, ms = run(unit, blocks, nt)
+            rows.append({"bytes": unit, "rotated_windows": 16, "blocks": blocks,
+                         "nontemporal": bool(nt), "gbps": gbs, "median_ms": ms})
+    best = max(rows, key=lambda r: r["gbps"])
+    gbs_all, ms_all = run(total, best["blocks"], int(best["nontemporal"]), n=8, rotate=False)
+    out = {"unit_reads": rows, "best_unit_gbps": best["gbps"],
+           "whole_2gib_gbps": gbs_all, "whole_2gib_ms": ms_all,
+           "ceiling_gbps": max(best["gbps"], gbs_all)}
+    result["extra"]["hbm_stream_probe"] = out
+    log(f"[bench] streaming-read ceiling: {best['gbps']:.0f} GB/s for {unit} B reads "
+        f"({best['blocks']} blocks, nt={best['nontemporal']}), {gbs_all:.0f} GB/s whole 2 GiB")
+    del buf, sink
+    torch.cuda.empty_cache()
+    return out["ceiling_gbps"]
+
+
 def measured_traffic():
     """HBM bytes per launch of the gate/up kernel from the committed counter
     runs, if they were taken on the current kernel source (else None)."""
@@ -518,37 +570,113 @@ def measured_traffic():
     return rec.get("k_gu_bytes_per_launch")
 
 
-def cpu_baseline(n_tok: int):
-    """The oracle, as it stands, on a bounded sample of the decode workload:
-    n_tok token-layers (T=1) of the 8-layer GLM decode, single-threaded, with
-    the experts they select packed beforehand (not timed)."""
-    import numpy as np
+def _oracle_rate(jobs, threads: int):
+    """Times the oracle over jobs [(OracleLayer, x [T,H], residual)], one
+    token per call, on `threads` host threads (each oracle call is
+    single-threaded C and releases the interpreter lock).  Returns
+    (token-layers, seconds)."""
+    from concurrent.futures import ThreadPoolExecutor
+    import oracle
+    calls = []
+    for ref, x, residual in jobs:
+        cfg = ref.cfg
+        blobs = [ref.cache.get(e) for e in range(cfg.E)]
+        for t in range(x.shape[0]):
+            calls.append((ref, cfg, blobs, x[t:t + 1], residual))
+
+    def one(c):
+        ref, cfg, blobs, xt, residual = c
+        if residual:
+            oracle.residual_layer(xt, ref.W, ref.b, cfg.K, cfg.fmt, cfg.I, blobs, ref.shared,
+                                  cfg.eps, cfg.routed_scale, cfg.norm_topk)
+        else:
+            oracle.moe_layer(xt, ref.W, ref.b, cfg.K, cfg.fmt, cfg.I, blobs, ref.shared)
+
+    t0 = time.perf_counter()
+    if threads == 1:
+        for c in calls:
+            one(c)
+    else:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(one, calls))
+    return len(calls), time.perf_counter() - t0
+
+
+def _oracle_jobs(cfg, layers, T, stream0, residual=False):
+    """Routes each sample on the oracle and packs the experts it selects
+    (not timed)."""
     import oracle
     import synth
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from parity import OracleLayer
+    jobs = []
+    for l in layers:
+        ref = OracleLayer(cfg, l)
+        x = synth.tokens(cfg, T=T, stream=stream0 + l)
+        xin = oracle.rmsnorm(x, cfg.eps) if residual else x
+        ids, *_ = ref.route(xin)
+        ref.need(ids)
+        jobs.append((ref, x, residual))
+    return jobs
+
+
+def cpu_baseline(n_tok: int):
+    """The oracle, as it stands, on bounded samples of each workload, timed
+    on this host (forward only: routing for the sample and expert packing
+    happen before the clock starts).  Returns (the headline entry for the
+    decode workload, per-workload entries)."""
+    import synth
+    nproc = min(16, os.cpu_count() or 1)
+    host = {"host_cpu": _cpu_model(), "host_nproc": os.cpu_count()}
+    out = {}
+    # GLM decode (T = 1): n_tok token-layers over the 8 layers, one thread
     cfg = synth.CONFIGS["glm_decode"]
     per = max(1, n_tok // cfg.n_layers)
-    jobs = []
-    for l in range(cfg.n_layers):
-        ref = OracleLayer(cfg, l)
-        x = synth.tokens(cfg, T=per, stream=1000 + l)
-        ids, *_ = ref.route(x)
-        ref.need(ids)
-        jobs.append((ref, x))
-    t0 = time.perf_counter()
-    n = 0
-    for ref, x in jobs:
-        blobs = [ref.cache.get(e) for e in range(cfg.E)]
-        for t in range(x.shape[0]):
-            oracle.moe_layer(x[t:t + 1], ref.W, ref.b, cfg.K, cfg.fmt, cfg.I, blobs, ref.shared)
-            n += 1
-    dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} token-layers (T=1) of the 8-layer GLM decode workload "
-                      f"({per} tokens per layer), single-threaded C oracle, fp64 accumulate; "
-                      f"expert packing excluded; {dt:.1f} s",
-            "host_cpu": _cpu_model(), "host_nproc": os.cpu_count()}
+    jobs = _oracle_jobs(cfg, range(cfg.n_layers), per, 1000)
+    n, dt = _oracle_rate(jobs, 1)
+    head = {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} token-layers (T=1) of the 8-layer GLM decode workload ({per} tokens "
+                      f"per layer), single-threaded C oracle, fp64 accumulate; expert packing "
+                      f"excluded; {dt:.1f} s", **host}
+    # the same workload on every host core: P threads over a larger sample
+    jobs_p = _oracle_jobs(cfg, [0], 6 * nproc, 2000)
+    n, dt = _oracle_rate(jobs_p, nproc)
+    out["glm_decode_all_cores"] = {"value": n / dt, "unit": "tokens/s", "cores": nproc,
+                                   "sample": f"{n} tokens (T=1 each) through layer 0 of the GLM "
+                                             f"decode workload, {nproc} threads, {dt:.1f} s"}
+    # GLM verify (T = 8 x 8 chained layers): 2 of the 8 layers, scaled to the stack
+    cfg = synth.CONFIGS["glm_verify"]
+    jobs = _oracle_jobs(cfg, range(2), cfg.T, 3000, residual=True)
+    n, dt = _oracle_rate(jobs, 1)
+    per_layer = dt / 2
+    out["glm_verify"] = {"value": cfg.T / (per_layer * cfg.n_layers),
+                         "unit": "tokens/s per 8-layer stack", "cores": 1,
+                         "s_per_layer": per_layer,
+                         "sample": f"T=8 through 2 of the 8 chained layers ({n} token-layers, "
+                                   f"{dt:.1f} s), scaled to 8 layers"}
+    # Edge0 (T = 1 x 40 chained layers), top-4 and top-8: the whole step
+    for name in ("edge0_decode", "edge0_decode_k8"):
+        cfg = synth.CONFIGS[name]
+        jobs = _oracle_jobs(cfg, range(cfg.n_layers), 1, 4000, residual=True)
+        n, dt = _oracle_rate(jobs, 1)
+        out[name] = {"value": 1.0 / dt, "unit": "40-layer steps/s (tokens/s)", "cores": 1,
+                     "s_per_layer": dt / cfg.n_layers,
+                     "sample": f"one token through all {cfg.n_layers} layers ({dt:.2f} s)"}
+    # GLM prefill (T = 2048): a 32-token slice, one thread and all cores
+    cfg = synth.CONFIGS["glm_prefill"]
+    jobs = _oracle_jobs(cfg, [0], 32, 5000)
+    n, dt = _oracle_rate(jobs, 1)
+    out["glm_prefill"] = {"value": n / dt, "unit": "tokens/s", "cores": 1,
+                          "ms_per_2048_layer": 2048 / (n / dt) * 1e3,
+                          "sample": f"{n} of the 2048 tokens ({dt:.1f} s), scaled"}
+    jobs = _oracle_jobs(cfg, [0], 6 * nproc, 6000)
+    n, dt = _oracle_rate(jobs, nproc)
+    out["glm_prefill_all_cores"] = {"value": n / dt, "unit": "tokens/s", "cores": nproc,
+                                    "ms_per_2048_layer": 2048 / (n / dt) * 1e3,
+                                    "sample": f"{n} tokens, {nproc} threads ({dt:.1f} s), scaled"}
+    for v in out.values():
+        v["kind"] = "oracle"
+    return head, out
 
 
 def _cpu_model() -> str:
@@ -569,6 +697,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="only the decode workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=16)
+    ap.add_argument("--no-probe", action="store_true", help="skip the streaming-read ceiling")
     ap.add_argument("--only", choices=["decode", "verify", "edge0", "edge0_k8", "prefill", "grouped",
                                        "softmax", "int8_shared", "requant", "staged"],
                     help="run one workload only (for profiling); the JSON line then "
@@ -588,12 +717,14 @@ def main():
     result = {
         "metric": None, "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "vs_baseline": None, "dtype": "int4 x fp16 -> fp32", "data": "synthetic",
         "config": {"workload": "glm_decode: GLM-5.2-shape MoE layer, H=6144, E=256, top-8, "
                                "I=2048, 1 shared expert, int4 per-row scale, T=1, 8 resident "
                                "layers rotated", "global_batch": 1, "seq_len": 1,
                    "parallelism": "none (1 GPU)", "weights": "int4 (fp32 row scales)",
-                   "activations": "fp32"},
+                   "activations": "fp32 in and out; inside the expert GEMVs each 64-input "
+                                  "span of x and of h is rounded once to fp16 after an exact "
+                                  "power-of-two scale; fp32 accumulate"},
         "extra": {},
     }
     if args.only and args.only != "decode":
@@ -609,6 +740,13 @@ def main():
         print(json.dumps(result), flush=True)
         return
     bench_decode(torch, args, result)
+    if not args.no_probe:
+        ceil = stream_ceiling(torch, result, result["roofline"]["algorithmic_bytes_per_launch"])
+        rf = result["roofline"]
+        rf["stream_ceiling_gbps"] = ceil
+        rf["frac_of_stream_ceiling"] = rf["achieved"] / ceil
+        lay = result["extra"]["glm_decode"]
+        lay["layer_frac_of_stream_ceiling"] = lay["layer_gbps"] / ceil
     if args.copy_probe:
         copy_probe(torch, result)
     if not args.no_extra and not args.only:
@@ -623,7 +761,8 @@ def main():
         bench_prefill(torch, 20, result)
     if not args.no_cpu:
         log("[bench] cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(args.cpu_tokens)
+        result["cpu_baseline"], result["extra"]["cpu_baseline_by_workload"] = \
+            cpu_baseline(args.cpu_tokens)
     print(json.dumps(result), flush=True)
 
 

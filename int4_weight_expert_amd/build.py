@@ -11,6 +11,11 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_int4.so")
 
+# the streaming-read probe the benchmark measures the HBM ceiling with: a
+# library of its own, not part of the MoE path
+PROBE_SRC = "hbm_probe.hip"
+PROBE_LIB = os.path.join(HERE, "libhbm_probe.so")
+
 SOURCES = ["moe_api.hip", "moe_stage.hip", "k_pack.hip", "k_small.hip", "k_large.hip", "k_gemv.hip", "k_gemm.hip"]
 
 # -packed-fp32-ops: keep hipcc from forming v_pk_{add,mul,fma}_f32 out of
@@ -35,11 +40,15 @@ def _compile(src: str) -> str:
 
 def build() -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + 1)) as ex:
+        objs = list(ex.map(_compile, SOURCES + [PROBE_SRC]))
     tmp = LIB + ".tmp"
-    subprocess.check_call(["hipcc", "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp])
+    subprocess.check_call(["hipcc", "-shared", "-fPIC", "--offload-arch=gfx950", *objs[:-1], "-o",
+                           tmp])
     os.replace(tmp, LIB)
+    subprocess.check_call(["hipcc", "-shared", "-fPIC", "--offload-arch=gfx950", objs[-1], "-o",
+                           PROBE_LIB + ".tmp"])
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
     return LIB
 
 
