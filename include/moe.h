@@ -135,6 +135,18 @@ size_t moe_expert_bytes(const moe_ctx *ctx);
  * Errors: MOE_E_ARG (null, layer out of range). */
 int moe_set_router(moe_ctx *ctx, int layer, const float *W, const float *bias);
 
+/* moe_set_router for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same result, staged through a fixed device array of the
+ * library (16 MiB per device, enough for every router a context accepts:
+ * E * H <= 256 * 16384) instead of a temporary; calls no allocating
+ * routine.  Synchronous on the context's stream.  The array is shared by
+ * every context on a device and keeps the last call's contents: calls that
+ * overlap on one device (other threads, other streams) race; calls from
+ * one thread never overlap.  Errors: MOE_E_ARG, MOE_E_SIZE (E * H beyond
+ * the array), MOE_E_HIP. */
+int moe_set_router_noalloc(moe_ctx *ctx, int layer, const float *W, const float *bias);
+
 /* Copies one expert blob (host or device pointer, nbytes ==
  * moe_expert_bytes) into a pool slot ([GLM-C] §13 contiguous slab).
  * Blob layout, little-endian, row-major, output rows:

@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "moe_ctx.h"
@@ -32,6 +33,37 @@ int hip_rc(moe_ctx* c, hipError_t e)
 namespace {
 
 constexpr int kDefaultGemmMin = 64;
+
+// Staging of moe_set_router_noalloc: the caller's router matrix is copied
+// here before the layout kernel reads it, in place of the temporary that
+// moe_set_router allocates.  One copy per device, held until the process
+// ends; its size covers the largest router a context accepts (256 experts x
+// 16384 inputs, 16 MiB).  Host code uses only the per-device address that
+// hipGetSymbolAddress returns (the array's name is not a device address on
+// the host).
+constexpr size_t kRouterScratchFloats = (size_t)256 * 16384;
+__device__ __align__(256) float scratch[kRouterScratchFloats];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// Looks up (once per device, with that device current) the address of this
+// device's scratch array.  Returns nullptr on failure.
+float* router_scratch(int dev)
+{
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = (float*)p;
+    }
+    return g_scratch_ptr[dev];
+}
 
 template <typename P>
 int dalloc(moe_ctx* c, P** p, size_t bytes)
@@ -501,6 +533,7 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
         if (e != hipSuccess) rc = MOE_E_HIP;
     }
     rc = rc ? rc : residency_init(c);
+    if (rc == MOE_OK && !router_scratch(dev)) rc = MOE_E_HIP;
     if (rc != MOE_OK) {
         moe_destroy(c);
         return rc;
@@ -546,6 +579,23 @@ int moe_set_router(moe_ctx* c, int layer, const float* W, const float* bias)
     if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
     hipFree(tmp);
     return hip_ok(e);
+}
+
+int moe_set_router_noalloc(moe_ctx* c, int layer, const float* W, const float* bias)
+{
+    if (!c || !W || !bias || layer < 0 || layer >= c->cfg.n_layers) return MOE_E_ARG;
+    const size_t H = c->cfg.hidden, E = c->cfg.n_experts;
+    if (E * H > kRouterScratchFloats) return MOE_E_SIZE;
+    float* tmp = router_scratch(c->device);  // set up by create on this device
+    if (!tmp) return MOE_E_HIP;
+    hipError_t e = hipMemcpyAsync(tmp, W, E * H * 4, hipMemcpyDefault, c->stream);
+    if (e == hipSuccess)
+        e = launch_router_to_internal(tmp, c->wr + (size_t)layer * c->Epad * H, (int)E, c->Epad,
+                                      (int)H, c->stream);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(c->bias + (size_t)layer * E, bias, E * 4, hipMemcpyDefault, c->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+    return hip_rc(c, e);
 }
 
 int moe_load_expert(moe_ctx* c, int slot, const void* blob, size_t nbytes)

@@ -43,7 +43,7 @@ EXPORTS = ["moe_layer_create", "moe_destroy", "moe_set_stream", "moe_expert_byte
            "moe_map_experts_async", "moe_load_image_async", "moe_load_layer_async",
            "moe_sync_copies", "moe_set_staging", "moe_stage_experts", "moe_sticky_plan",
            "moe_image_bytes", "moe_blob_to_image", "moe_requant_int8_rows", "moe_read_shared",
-           "moe_shared_bytes"]
+           "moe_shared_bytes", "moe_set_router_noalloc"]
 
 
 class moe_config(ctypes.Structure):
@@ -78,6 +78,7 @@ def lib() -> ctypes.CDLL:
             "moe_set_stream": ([vp, vp], i32),
             "moe_expert_bytes": ([vp], sz),
             "moe_set_router": ([vp, i32, vp, vp], i32),
+            "moe_set_router_noalloc": ([vp, i32, vp, vp], i32),
             "moe_load_expert": ([vp, i32, vp, sz], i32),
             "moe_pack_expert": ([vp, i32, vp, vp, vp], i32),
             "moe_set_shared": ([vp, i32, i32, vp, sz], i32),
@@ -181,6 +182,10 @@ def moe_expert_bytes(ctx: int) -> int:
 
 def moe_set_router(ctx, layer, W, bias) -> int:
     return _check("moe_set_router", lib().moe_set_router(ctx, layer, _ptr(W), _ptr(bias)))
+
+
+def moe_set_router_noalloc(ctx, layer, W, bias) -> int:
+    return lib().moe_set_router_noalloc(ctx, layer, _ptr(W), _ptr(bias))
 
 
 def moe_load_expert(ctx, slot, blob, nbytes) -> int:
