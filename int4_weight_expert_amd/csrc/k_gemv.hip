@@ -181,6 +181,45 @@ __device__ __forceinline__ void copy_slice(const uint4* __restrict__ gq,
     lds_wave_sync();
 }
 
+// The slice's h of one row from fp32 (the one-token gate/up kernel's
+// output) into LDS as fp16 spans, as the gate/up finalize stages it: per span
+// of 64 inputs a power of two that puts its largest magnitude in [2^13,
+// 2^14), pair order, (2^-k, sum of the fp16 values).  Lane g takes inputs
+// 8g..8g+7 of the slice; a span's 8 lanes agree on its scale.
+__device__ __forceinline__ void stage_slice_f32(const float* __restrict__ hrow, int c0, int CPU,
+                                                int lane, uint4* xq, float2* xs)
+{
+    const int n8 = CPU * 4;
+    const float4* h4 = (const float4*)(hrow + (size_t)c0 * 32);
+    for (int g0 = 0; g0 < n8; g0 += 64) {
+        const int g = g0 + lane, gc = min(g, n8 - 1);
+        const float4 a = h4[2 * gc], b = h4[2 * gc + 1];
+        float m = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
+                        fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+        m = fmaxf(m, __shfl_xor(m, 1));
+        m = fmaxf(m, __shfl_xor(m, 2));
+        m = fmaxf(m, __shfl_xor(m, 4));
+        int e;
+        frexpf(m, &e);
+        e = max(e, -100);
+        const float sc = ldexpf(1.0f, 14 - e);
+        const _Float16 h0 = (_Float16)(a.x * sc), h1 = (_Float16)(a.y * sc);
+        const _Float16 h2 = (_Float16)(a.z * sc), h3 = (_Float16)(a.w * sc);
+        const _Float16 h4v = (_Float16)(b.x * sc), h5 = (_Float16)(b.y * sc);
+        const _Float16 h6 = (_Float16)(b.z * sc), h7 = (_Float16)(b.w * sc);
+        float t = (((float)h0 + (float)h1) + ((float)h2 + (float)h3)) +
+                  (((float)h4v + (float)h5) + ((float)h6 + (float)h7));
+        t += __shfl_xor(t, 1);
+        t += __shfl_xor(t, 2);
+        t += __shfl_xor(t, 4);
+        if (g < n8) {
+            xq[g] = make_uint4(pack_h2(h0, h4v), pack_h2(h1, h5), pack_h2(h2, h6), pack_h2(h3, h7));
+            if ((g & 7) == 0) xs[g >> 3] = make_float2(ldexpf(1.0f, e - 14), t);
+        }
+    }
+    lds_wave_sync();
+}
+
 __device__ __forceinline__ void unit_coords(int u, int KS, int NB, int& q, int& b, int& gi)
 {
     q = u % KS;
@@ -648,7 +687,7 @@ __global__ void __launch_bounds__(256) k_gu_fin(Fwd f, int n_rows)
 // down unit: partial sd (Wd h_r)_row of one k-slice -> ypart[r][b][q][64].
 // ---------------------------------------------------------------------------
 
-template <int FMT, int NT, bool S8>
+template <int FMT, int NT, bool S8, bool HF = false>
 __global__ void __launch_bounds__(64) k_dn(Fwd f)
 {
     extern __shared__ uint4 lds4[];
@@ -698,7 +737,10 @@ __global__ void __launch_bounds__(64) k_dn(Fwd f)
                 P0 = bload4(rtd, toff, (uint32_t)(c0 / 2) * 256);
                 P1 = bload4(rtd, toff, (uint32_t)(c0 / 2 + 1) * 256);
             }
-            copy_slice<NT>(f.hq, f.hsc, rr, nj, I / 8, I / 64, c0, CPU, lane, xq, xs);
+            if (HF)  // one token, h in fp32 from the one-token gate/up kernel
+                stage_slice_f32(f.hf + (size_t)rr[0] * I, c0, CPU, lane, xq, xs);
+            else
+                copy_slice<NT>(f.hq, f.hsc, rr, nj, I / 8, I / 64, c0, CPU, lane, xq, xs);
             // one rolling step = two spans (4 chunks); the last step loads nothing
 #define DN_STEP(I_, LOAD_)                                                               \
     {                                                                                    \
@@ -1052,16 +1094,16 @@ static hipError_t gu_launch(const Fwd& f, hipStream_t st)
     return launch_k(k_gu<FMT, NT, S8>, dim3(units), dim3(64), lds, st, f);
 }
 
-template <int FMT, int NT, bool S8>
+template <int FMT, int NT, bool S8, bool HF = false>
 static hipError_t dn_launch(const Fwd& f, hipStream_t st)
 {
     const int KS = f.dn_ks, CPU = f.I / 32 / KS;
     const unsigned units = (unsigned)(max_groups(f) * (f.H / 64) * KS);
     const size_t lds = gemv_lds_bytes(CPU, f.T);
     static bool big = false;
-    hipError_t e0 = allow_lds(k_dn<FMT, NT, S8>, lds, big);
+    hipError_t e0 = allow_lds(k_dn<FMT, NT, S8, HF>, lds, big);
     if (e0 != hipSuccess) return e0;
-    return launch_k(k_dn<FMT, NT, S8>, dim3(units), dim3(64), lds, st, f);
+    return launch_k(k_dn<FMT, NT, S8, HF>, dim3(units), dim3(64), lds, st, f);
 }
 
 template <int FMT, bool S8>
@@ -1130,6 +1172,9 @@ hipError_t launch_gateup_gemv(const Fwd& f, hipStream_t st)
 
 hipError_t launch_down_gemv(const Fwd& f, hipStream_t st)
 {
+    if (f.h_f32)  // one token after the one-token gate/up kernel (int4 shared experts)
+        return f.fmt == MOE_W_INT4_ROW ? dn_launch<MOE_W_INT4_ROW, 1, false, true>(f, st)
+                                       : dn_launch<MOE_W_INT4_AFFINE_G64, 1, false, true>(f, st);
     const bool s8 = shared_int8(f);
     if (f.fmt == MOE_W_INT4_ROW)
         return s8 ? dn_dispatch<MOE_W_INT4_ROW, true>(f, st) : dn_dispatch<MOE_W_INT4_ROW, false>(f, st);

@@ -211,6 +211,7 @@ Fwd make_fwd(moe_ctx* c, const float* x, float* out, int T, int layer, int resid
     f.xrow = c->xrow;
     f.hrow = c->hrow;
     f.hbuf = c->hbuf;
+    f.hf = c->hf;
     f.tiles = c->tiles;
     f.n_tiles = c->n_tiles;
     f.counters = c->counters;
@@ -286,6 +287,31 @@ int run_forward(moe_ctx* c, const float* x, int T, int layer, float* out, int re
     plan_gemv(c, f);
     int rc = run_router(c, f);
     if (rc) return rc;
+    if (c->tok1 && tok1_ok(f)) {
+        // one token: gate/up straight to h (no k-slice partials, no
+        // finalize); small layers then run down with the combine in one
+        // kernel, large ones the down GEMV (its h slices staged from fp32)
+        // and the combine
+        mark(c, "gateup_gemv");
+        rc = hip_rc(c, launch_tok1_gateup(f, c->stream));
+        if (rc) return rc;
+        if (tok1_down_ok(f)) {
+            mark(c, "down_combine");
+            rc = hip_rc(c, launch_tok1_down(f, c->stream));
+            if (rc) return rc;
+            mark(c, nullptr);
+            return MOE_OK;
+        }
+        f.h_f32 = 1;
+        mark(c, "down_gemv");
+        rc = hip_rc(c, launch_down_gemv(f, c->stream));
+        if (rc) return rc;
+        mark(c, "combine");
+        rc = hip_rc(c, launch_combine(f, c->stream));
+        if (rc) return rc;
+        mark(c, nullptr);
+        return MOE_OK;
+    }
     mark(c, "gateup_gemv");
     rc = hip_rc(c, launch_gateup_gemv(f, c->stream));
     if (rc) return rc;
@@ -499,6 +525,7 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
     rc = rc ? rc : dalloc(c, &c->n_groups, 4);
     rc = rc ? rc : dalloc(c, &c->hq, rows * (I / 8) * 16);
     rc = rc ? rc : dalloc(c, &c->hsc, rows * (I / 64) * 8);
+    rc = rc ? rc : dalloc(c, &c->hf, (K + g.n_shared) * I * 4);
     {
         // k-split partials for up to 16 tokens (gate/up, 16 slices) and 64
         // tokens (down, 4 slices); beyond that the plan falls back to fewer

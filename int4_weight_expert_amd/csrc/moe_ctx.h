@@ -45,12 +45,14 @@ struct moe_ctx {
     float2* xrow = nullptr;
     float2* hrow = nullptr;
     float* hbuf = nullptr;
+    float* hf = nullptr;
     int2* tiles = nullptr;
     int32_t* n_tiles = nullptr;
     uint32_t* counters = nullptr;
     uint32_t* status = nullptr;
     size_t status_words = 0;
     int gemm_min_tokens = 64;
+    bool tok1 = true;          // one token: the k_tok1 kernels where the shape allows
     int lds_max = 65536;
     hipError_t last_err = hipSuccess;
     // timing

@@ -95,6 +95,8 @@ struct Fwd {
     float2* xrow;         // [T] per token (2^-k, sum of its fp16 values)
     float2* hrow;         // [rows]
     float* hbuf;          // [rows][I] h in fp32 (gate/up GEMM output)
+    float* hf;            // [K + n_shared][I] h in fp32 of the one-token kernels
+    int h_f32;            // 1: the down GEMV stages its h slices from hf (one token)
     int2* tiles;          // [max tiles] (group index, first row) of each 128-row tile
     int32_t* n_tiles;     // [1]
 };
@@ -151,6 +153,10 @@ hipError_t launch_gemm_hstage(const Fwd& f, hipStream_t st);
 hipError_t launch_gemm_down(const Fwd& f, hipStream_t st);
 hipError_t launch_gateup_finalize(const Fwd& f, hipStream_t st);
 hipError_t launch_combine(const Fwd& f, hipStream_t st);
+bool tok1_ok(const Fwd& f);
+bool tok1_down_ok(const Fwd& f);
+hipError_t launch_tok1_gateup(const Fwd& f, hipStream_t st);
+hipError_t launch_tok1_down(const Fwd& f, hipStream_t st);
 bool down_combine1_ok(const Fwd& f);
 hipError_t launch_down_combine1(const Fwd& f, hipStream_t st);
 size_t gemv_lds_bytes(int chunks_per_slice, int T);
