@@ -586,6 +586,119 @@ __global__ void __launch_bounds__(RT_THREADS) k_router_small(Fwd f, const float*
 }
 
 // ---------------------------------------------------------------------------
+// One-token router, logits only: workgroup e computes expert e's whole raw
+// logit x . Wr[e] from the row-major copy of the router weights (4
+// wavefronts, each a quarter of the H inputs, all loads in flight at once,
+// reduced in LDS in wavefront order) and stores it (part[4 e]); workgroup 0
+// also forms the token's sum and sum of squares (tpart, and the RMSNorm
+// factor), workgroup e stages x spans e, e + E, ... as fp16 for the expert
+// kernels.  The selection (sigmoid, bias, top-K, weights) runs in the
+// one-token gate/up kernel, after this launch, instead of in a last
+// workgroup behind a cross-workgroup arrival.
+// ---------------------------------------------------------------------------
+
+template <int Q>  // float4 loads per lane and wavefront (H = 1024 Q)
+__global__ void __launch_bounds__(RT_THREADS) k_router1(Fwd f, const float* __restrict__ X)
+{
+    constexpr int NW = RT_THREADS / 64;
+    __shared__ float s_red[NW][3];
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int e = blockIdx.x, H = f.H;
+    const float4* wr = (const float4*)(f.wr_rows + (size_t)e * H) + (size_t)w * (H / 16);
+    const float4* x4 = (const float4*)X + (size_t)w * (H / 16);
+    float4 a[Q], v[Q];
+#pragma unroll
+    for (int k = 0; k < Q; ++k) {
+        a[k] = wr[k * 64 + lane];
+        v[k] = x4[k * 64 + lane];
+    }
+    // x spans e, e + E, ... as fp16 for the expert kernels (wavefront 0)
+    if (w == 0)
+        for (int sp = e; sp < H / 64; sp += gridDim.x) {
+            const float xv = X[sp * 64 + lane];
+            stage_span64(xv, lane, (uint16_t*)(f.xq + (size_t)sp * 8), f.xsc + sp);
+        }
+    float acc = 0.f, sum = 0.f, ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < Q; ++k) {
+        acc = fmaf(a[k].x, v[k].x, acc);
+        acc = fmaf(a[k].y, v[k].y, acc);
+        acc = fmaf(a[k].z, v[k].z, acc);
+        acc = fmaf(a[k].w, v[k].w, acc);
+    }
+    acc = wave_sum(acc);
+    if (e == 0) {  // the token's statistics, once
+#pragma unroll
+        for (int k = 0; k < Q; ++k) {
+            sum += (v[k].x + v[k].y) + (v[k].z + v[k].w);
+            ss = fmaf(v[k].x, v[k].x, ss);
+            ss = fmaf(v[k].y, v[k].y, ss);
+            ss = fmaf(v[k].z, v[k].z, ss);
+            ss = fmaf(v[k].w, v[k].w, ss);
+        }
+        sum = wave_sum(sum);
+        ss = wave_sum(ss);
+    }
+    if (lane == 0) {
+        s_red[w][0] = acc;
+        s_red[w][1] = sum;
+        s_red[w][2] = ss;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float l = 0.f, gs = 0.f, sq = 0.f;
+#pragma unroll
+        for (int v2 = 0; v2 < NW; ++v2) {
+            l += s_red[v2][0];
+            gs += s_red[v2][1];
+            sq += s_red[v2][2];
+        }
+        st_agent(&f.part[(size_t)e * 4], l);  // one slice per expert (row stride 4)
+        if (e == 0) {                         // one slice of token statistics
+            st_agent(&f.tpart[0], gs);
+            st_agent(&f.tpart[1], sq);
+            f.tok[0].xsum = gs;
+            f.tok[0].rscale = f.residual ? 1.0f / sqrtf(sq / (float)H + f.eps) : 1.0f;
+        }
+    }
+    // the descriptors that do not depend on the selection (which the
+    // gate/up kernel makes)
+    if (e == 0 && (int)threadIdx.x < f.n_shared) {
+        Group g;
+        g.base = f.shared + (size_t)threadIdx.x * f.shared_bytes;
+        g.cnt = 1;
+        g.off = threadIdx.x;
+        g.kind = 1;
+        g.expert = -1;
+        f.groups[threadIdx.x] = g;
+    }
+    if (e == 0 && threadIdx.x == 0) {
+        f.n_groups[0] = f.n_shared + f.K;
+        *f.sel_flag = 0u;  // the gate/up kernel publishes its selection anew
+    }
+}
+
+bool router1_ok(const Fwd& f)
+{
+    return f.T == 1 && f.wr_rows != nullptr && f.H % 1024 == 0 && f.H / 1024 <= 8;
+}
+
+hipError_t launch_router1(const Fwd& f, hipStream_t st)
+{
+    const dim3 grid((unsigned)f.E), block(RT_THREADS);
+    switch (f.H / 1024) {
+    case 1: return launch_k(k_router1<1>, grid, block, 0, st, f, f.x);
+    case 2: return launch_k(k_router1<2>, grid, block, 0, st, f, f.x);
+    case 3: return launch_k(k_router1<3>, grid, block, 0, st, f, f.x);
+    case 4: return launch_k(k_router1<4>, grid, block, 0, st, f, f.x);
+    case 5: return launch_k(k_router1<5>, grid, block, 0, st, f, f.x);
+    case 6: return launch_k(k_router1<6>, grid, block, 0, st, f, f.x);
+    case 7: return launch_k(k_router1<7>, grid, block, 0, st, f, f.x);
+    default: return launch_k(k_router1<8>, grid, block, 0, st, f, f.x);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 

@@ -106,11 +106,88 @@ __device__ __forceinline__ uint32_t h2pack(_Float16 lo, _Float16 hi)
 }  // namespace
 
 // ---------------------------------------------------------------------------
+// One-token selection inside a 256-thread workgroup (sigmoid scoring, one
+// group): thread e scores expert e from its raw logit (the router's dot
+// product) times the token's RMSNorm factor: sigma, c = sigma + bias, key =
+// (c, then lower id) in 64 bits, so distinct keys order as the pages'
+// strict greater-than scan.  Wavefront w ranks block w of 64 experts; the
+// block's keys of rank < K are candidates, and ranks among the 4K
+// candidates give the top K in rank order.  Weights: sigma of the chosen
+// experts, renormalised (+1e-20) and scaled, summed in rank order.  The
+// same steps and arithmetic as the router tail.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t ordf1(float c)
+{
+    const uint32_t u = __float_as_uint(c);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+struct Sel1 {
+    unsigned long long key[256];
+    unsigned long long cand[32];
+    float sig[256];
+    int slot[256];
+    int ids[8];
+    float wts[8];
+};
+
+// Returns with s.ids / s.wts / s.slot valid for every thread of the block.
+__device__ void select1(const Fwd& f, Sel1& s)
+{
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, E = f.E, K = f.K;
+    const float l = tid < E ? f.part[(size_t)tid * 4] : 0.f;
+    const float bias = tid < E ? f.bias[tid] : 0.f;
+    const int slot = tid < E ? f.tbl[tid] : -1;
+    const float ss = f.tpart[1];
+    const float rs = f.residual ? 1.0f / sqrtf(ss / (float)f.H + f.eps) : 1.0f;
+    unsigned long long key = 0ull;
+    float sig = 0.f;
+    if (tid < E) {
+        sig = 1.0f / (1.0f + expf(-(l * rs)));
+        key = ((unsigned long long)ordf1(sig + bias) << 32) | (uint32_t)(0xFFFFu - tid);
+    }
+    s.key[tid] = key;
+    s.sig[tid] = sig;
+    s.slot[tid] = slot;
+    if (tid < 32) s.cand[tid] = 0ull;  // blocks with fewer than K real experts leave slots unset
+    __syncthreads();
+    {
+        const unsigned long long* kb = &s.key[w * 64];
+        const unsigned long long mine = kb[lane];
+        int rank = 0;
+#pragma unroll
+        for (int e = 0; e < 64; e += 2) {
+            const ulonglong2 kk = *(const ulonglong2*)&kb[e];
+            rank += (kk.x > mine) + (kk.y > mine);
+        }
+        if (rank < K) s.cand[w * K + rank] = mine;
+    }
+    __syncthreads();
+    if (tid < 4 * K) {
+        const unsigned long long mine = s.cand[tid];
+        int rank = 0;
+        for (int j = 0; j < 4 * K; ++j) rank += s.cand[j] > mine;
+        if (rank < K) s.ids[rank] = (int)(0xFFFFu - (uint32_t)(mine & 0xFFFFu));
+    }
+    __syncthreads();
+    if (tid < K) {
+        float sum = 0.f;
+        for (int k = 0; k < K; ++k) sum += s.sig[s.ids[k]];
+        const float sg = s.sig[s.ids[tid]];
+        s.wts[tid] = f.norm_topk ? f.routed_scale * (sg / (sum + 1e-20f)) : f.routed_scale * sg;
+    }
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
 // gate/up, one token: workgroup (group gi, 8-row block sb of I), W waves each
 // taking H / W inputs in NST steps of 16 chunks, every load issued at once
 // ---------------------------------------------------------------------------
 
-template <int FMT, int W, int NST>
+constexpr int SEL_POLLS = 4096;  // flag polls (with a short sleep each) before selecting locally
+
+template <int FMT, int W, int NST, bool SEL>
 __global__ void __launch_bounds__(64 * W) k_gu8(Fwd f)
 {
     extern __shared__ uint4 lds4[];
@@ -118,14 +195,104 @@ __global__ void __launch_bounds__(64 * W) k_gu8(Fwd f)
     const int lane = threadIdx.x & 63, w = uni((int)(threadIdx.x >> 6));
     const int H = f.H, I = f.I, C = H / 32, G = H / 64, NSB = I / 8;
     const int sb = blockIdx.x % NSB, gi = blockIdx.x / NSB;
-    if (gi >= uni(f.n_groups[0])) return;
-    const Group grp = uni_group(f.groups, gi);
-    int t, r;
-    tok_rows(f, f.perm, grp, 0, t, r);
+    int t = 0, r;
+    const uint8_t* base;
+    if (SEL) {
+        // the router left raw logits.  Group ns + k is the expert of rank k.
+        // Small layers: every routed workgroup selects for itself.  Large
+        // layers (sel_leader): the first routed workgroup (group ns, row
+        // block 0; dispatched before the others) selects and publishes each
+        // rank's slot with an agent-scope flag; the other routed workgroups
+        // poll the flag a bounded number of times and, if it has not come,
+        // select for themselves (same steps, same result), so no workgroup
+        // ever waits unboundedly.  The first routed workgroup also writes
+        // the selection out for the later kernels.
+        const int ns = f.n_shared;
+        if (gi < ns) {
+            base = f.shared + (size_t)gi * f.shared_bytes;
+            r = f.K + gi;
+        } else {
+            __shared__ Sel1 sel;
+            __shared__ int s_ok;
+            __shared__ uint64_t s_base;
+            const int k = gi - ns;
+            r = k;
+            if (!f.sel_leader || (k == 0 && sb == 0)) {
+                // the leader (or, on small layers, every routed workgroup)
+                select1(f, sel);
+                if (k == 0 && sb == 0 && (int)threadIdx.x < f.K) {
+                    const int kk = threadIdx.x, ek = sel.ids[kk], sk = sel.slot[ek];
+                    const uint8_t* bk = sk >= 0 ? f.pool + (size_t)sk * f.slot_bytes : nullptr;
+                    f.ids[kk] = ek;
+                    f.wts[kk] = sel.wts[kk];
+                    f.perm[kk] = kk;
+                    Group g;
+                    g.base = bk;
+                    g.cnt = 1;
+                    g.off = kk;
+                    g.kind = 0;
+                    g.expert = ek;
+                    f.groups[ns + kk] = g;
+                    __hip_atomic_store(&f.sel_base[kk], (uint64_t)(uintptr_t)bk, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                    if (sk < 0) {
+                        atomicOr(&f.status[0], (uint32_t)STATUS_NOT_RESIDENT);
+                        const int code = f.layer * f.E + ek;
+                        atomicOr(&f.status[1 + code / 32], 1u << (code % 32));
+                    }
+                }
+                if (f.sel_leader) {
+                    // the bases reach agent coherence before the flag does
+                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                    __builtin_amdgcn_s_waitcnt(0);
+                    __syncthreads();
+                    if (threadIdx.x == 0)
+                        __hip_atomic_store(f.sel_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                if (threadIdx.x == 0) {
+                    const int slot = sel.slot[sel.ids[k]];
+                    s_base = (uint64_t)(uintptr_t)(slot >= 0 ? f.pool + (size_t)slot * f.slot_bytes
+                                                             : nullptr);
+                }
+                __syncthreads();
+            } else {
+                if (threadIdx.x == 0) {
+                    int ok = 0;
+                    for (int i = 0; i < SEL_POLLS; ++i) {
+                        if (__hip_atomic_load(f.sel_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 1u) {
+                            ok = 1;
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(8);
+                    }
+                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                    if (ok)
+                        s_base = __hip_atomic_load(&f.sel_base[k], __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+                    s_ok = ok;
+                }
+                __syncthreads();
+                if (!s_ok) {  // not published in time: select here
+                    select1(f, sel);
+                    const int slot = sel.slot[sel.ids[k]];
+                    if (threadIdx.x == 0)
+                        s_base = (uint64_t)(uintptr_t)(slot >= 0 ? f.pool + (size_t)slot * f.slot_bytes : nullptr);
+                    __syncthreads();
+                }
+            }
+            base = (const uint8_t*)(uintptr_t)s_base;
+        }
+        base = (const uint8_t*)(uintptr_t)(((uint64_t)(uint32_t)uni((int)(uint32_t)(uintptr_t)base)) |
+                                           ((uint64_t)(uint32_t)uni((int)(uint32_t)((uintptr_t)base >> 32)) << 32));
+    } else {
+        if (gi >= uni(f.n_groups[0])) return;
+        const Group grp = uni_group(f.groups, gi);
+        tok_rows(f, f.perm, grp, 0, t, r);
+        base = grp.base;
+    }
     const int b = sb >> 3, s8 = sb & 7, rr = lane & 7, j = lane >> 3;
     constexpr int CW = 16 * NST, NSP = CW / 2;  // chunks and spans of the wave
     const int c0 = w * CW;
-    const uint8_t* base = grp.base;
     const uint8_t* anchor = (const uint8_t*)f.x;  // any valid address (empty resources)
     const uint32_t mbytes = base ? (uint32_t)C * 1024 : 0u;
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(base ? base + (size_t)b * C * 1024 : anchor, mbytes);
@@ -374,9 +541,14 @@ hipError_t gu8_go(const Fwd& f, hipStream_t st)
 {
     const unsigned wgs = (unsigned)((f.n_shared + f.K) * (f.I / 8));
     const size_t lds = gu8_lds(W, NST);
-    const hipError_t e = lds_attr(k_gu8<FMT, W, NST>, lds);
+    if (W == 4 && f.sel_in_gateup) {
+        const hipError_t e = lds_attr(k_gu8<FMT, 4, NST, true>, lds);
+        if (e != hipSuccess) return e;
+        return launch_k(k_gu8<FMT, 4, NST, true>, dim3(wgs), dim3(256), lds, st, f);
+    }
+    const hipError_t e = lds_attr(k_gu8<FMT, W, NST, false>, lds);
     if (e != hipSuccess) return e;
-    return launch_k(k_gu8<FMT, W, NST>, dim3(wgs), dim3(64 * W), lds, st, f);
+    return launch_k(k_gu8<FMT, W, NST, false>, dim3(wgs), dim3(64 * W), lds, st, f);
 }
 
 template <int FMT, int W>
@@ -444,6 +616,22 @@ bool tok1_down_ok(const Fwd& f)
     return tok1_ok(f) && f.I <= 2048 && ne <= D8_NE && (size_t)ne * f.H * f.I / 2 <= ((size_t)16 << 20) &&
            dn8_lds(f.I, ne) <= (size_t)f.lds_max;
 }
+
+// The selection can move into the gate/up kernel (256-thread workgroups,
+// one thread per expert) for the plain sigmoid top-K.
+bool tok1_sel_ok(const Fwd& f)
+{
+    int W = 0, nst = 0;
+    return tok1_ok(f) && gu8_shape(f.H, W, nst) && W == 4 && f.E <= 256 &&
+           f.scoring == MOE_SCORE_SIGMOID && f.n_group == 1;
+}
+
+// The selection runs in the gate/up kernel: by its first routed workgroup,
+// published to the others, on large layers (where selecting in all 2,048
+// routed workgroups of the GLM shape would hold their loads back); by every
+// routed workgroup on small ones (at most 512 gate/up workgroups), where
+// waiting for the publication costs more.
+bool tok1_sel_leader(const Fwd& f) { return (f.n_shared + f.K) * (f.I / 8) > 512; }
 
 hipError_t launch_tok1_gateup(const Fwd& f, hipStream_t st)
 {

@@ -181,6 +181,7 @@ Fwd make_fwd(moe_ctx* c, const float* x, float* out, int T, int layer, int resid
     f.norm_topk = g.norm_topk;
     f.layer = layer;
     f.wr = c->wr + (size_t)layer * c->Epad * g.hidden;
+    f.wr_rows = c->wr_rows ? c->wr_rows + (size_t)layer * g.n_experts * g.hidden : nullptr;
     f.bias = c->bias + (size_t)layer * g.n_experts;
     f.tbl = c->tbl + (size_t)layer * g.n_experts;
     f.pool = c->pool;
@@ -215,6 +216,8 @@ Fwd make_fwd(moe_ctx* c, const float* x, float* out, int T, int layer, int resid
     f.tiles = c->tiles;
     f.n_tiles = c->n_tiles;
     f.counters = c->counters;
+    f.sel_flag = c->sel_flag;
+    f.sel_base = c->sel_base;
     f.n_group = g.n_group;
     f.scoring = g.scoring;
     f.topk_group = g.topk_group;
@@ -228,6 +231,10 @@ Fwd make_fwd(moe_ctx* c, const float* x, float* out, int T, int layer, int resid
 int run_router(moe_ctx* c, const Fwd& f)
 {
     hipError_t e;
+    if (f.sel_in_gateup) {  // logits only: the one-token gate/up kernel selects
+        mark(c, "router_logits");
+        return hip_rc(c, launch_router1(f, c->stream));
+    }
     if (f.T <= ROUTER_SMALL_MAX_T) {
         mark(c, "router_topk_bucket");
         return hip_rc(c, launch_router_small(f, c->stream));
@@ -285,6 +292,10 @@ int run_forward(moe_ctx* c, const float* x, int T, int layer, float* out, int re
     Fwd f = make_fwd(c, x, out, T, layer, residual);
     if (uses_gemm(c, T)) return run_forward_gemm(c, f);
     plan_gemv(c, f);
+    if (c->tok1 && router1_ok(f) && tok1_sel_ok(f)) {
+        f.sel_in_gateup = 1;
+        f.sel_leader = tok1_sel_leader(f);
+    }
     int rc = run_router(c, f);
     if (rc) return rc;
     if (c->tok1 && tok1_ok(f)) {
@@ -504,6 +515,7 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
     int rc = MOE_OK;
     rc = rc ? rc : dalloc(c, &c->pool, (size_t)g.n_slots * c->slot_bytes);
     rc = rc ? rc : dalloc(c, &c->wr, L * c->Epad * H * 4);
+    rc = rc ? rc : dalloc(c, &c->wr_rows, L * E * H * 4);
     rc = rc ? rc : dalloc(c, &c->bias, L * E * 4);
     rc = rc ? rc : dalloc(c, &c->tbl, L * E * 4);
     rc = rc ? rc : dalloc(c, &c->shared, L * g.n_shared * c->shared_bytes);
@@ -546,6 +558,8 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
         rc = rc ? rc : dalloc(c, &c->n_tiles, 4);
     }
     rc = rc ? rc : dalloc(c, &c->counters, (1 + H / 64) * 4);
+    rc = rc ? rc : dalloc(c, &c->sel_flag, 4);
+    rc = rc ? rc : dalloc(c, &c->sel_base, 8 * 8);
     c->status_words = 1 + (L * E + 31) / 32;
     rc = rc ? rc : dalloc(c, &c->status, c->status_words * 4);
     if (rc == MOE_OK) {
@@ -555,6 +569,7 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
         if (e == hipSuccess) e = hipMemset(c->status, 0, c->status_words * 4);
         if (e == hipSuccess) e = hipMemset(c->bias, 0, L * E * 4);
         if (e == hipSuccess) e = hipMemset(c->wr, 0, L * c->Epad * H * 4);
+        if (e == hipSuccess) e = hipMemset(c->wr_rows, 0, L * E * H * 4);
         if (e == hipSuccess && g.n_shared) e = hipMemset(c->shared, 0, L * g.n_shared * c->shared_bytes);
         if (e == hipSuccess) e = hipDeviceSynchronize();
         if (e != hipSuccess) rc = MOE_E_HIP;
@@ -602,6 +617,9 @@ int moe_set_router(moe_ctx* c, int layer, const float* W, const float* bias)
         e = launch_router_to_internal(tmp, c->wr + (size_t)layer * c->Epad * H, (int)E, c->Epad,
                                       (int)H, c->stream);
     if (e == hipSuccess)
+        e = hipMemcpyAsync(c->wr_rows + (size_t)layer * E * H, tmp, E * H * 4,
+                           hipMemcpyDeviceToDevice, c->stream);
+    if (e == hipSuccess)
         e = hipMemcpyAsync(c->bias + (size_t)layer * E, bias, E * 4, hipMemcpyDefault, c->stream);
     if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
     hipFree(tmp);
@@ -619,6 +637,9 @@ int moe_set_router_noalloc(moe_ctx* c, int layer, const float* W, const float* b
     if (e == hipSuccess)
         e = launch_router_to_internal(tmp, c->wr + (size_t)layer * c->Epad * H, (int)E, c->Epad,
                                       (int)H, c->stream);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(c->wr_rows + (size_t)layer * E * H, tmp, E * H * 4,
+                           hipMemcpyDeviceToDevice, c->stream);
     if (e == hipSuccess)
         e = hipMemcpyAsync(c->bias + (size_t)layer * E, bias, E * 4, hipMemcpyDefault, c->stream);
     if (e == hipSuccess) e = hipStreamSynchronize(c->stream);

@@ -15,6 +15,7 @@ struct moe_ctx {
     int Epad = 0;
     uint8_t* pool = nullptr;
     float* wr = nullptr;
+    float* wr_rows = nullptr;  // the router weights again, row-major [L][E][H]
     float* bias = nullptr;
     int* tbl = nullptr;
     std::vector<int> tbl_host;
@@ -49,6 +50,8 @@ struct moe_ctx {
     int2* tiles = nullptr;
     int32_t* n_tiles = nullptr;
     uint32_t* counters = nullptr;
+    uint32_t* sel_flag = nullptr;
+    uint64_t* sel_base = nullptr;
     uint32_t* status = nullptr;
     size_t status_words = 0;
     int gemm_min_tokens = 64;

@@ -56,6 +56,7 @@ struct Fwd {
     int scoring;          // MOE_SCORE_SIGMOID or MOE_SCORE_SOFTMAX
     int layer;
     const float* wr;      // router, interleaved [Epad/64][H/4][64] float4
+    const float* wr_rows; // router, row-major [E][H] (the one-token router)
     const float* bias;    // [E]
     const int* tbl;       // [E] slot table row of this layer
     const uint8_t* pool;  // slot pool base
@@ -97,6 +98,10 @@ struct Fwd {
     float* hbuf;          // [rows][I] h in fp32 (gate/up GEMM output)
     float* hf;            // [K + n_shared][I] h in fp32 of the one-token kernels
     int h_f32;            // 1: the down GEMV stages its h slices from hf (one token)
+    int sel_in_gateup;    // 1: the one-token gate/up kernel selects the experts itself
+    int sel_leader;       // 1: one gate/up workgroup selects and publishes to the others
+    uint32_t* sel_flag;   // [1] the gate/up kernel's selection published (reset by the router)
+    uint64_t* sel_base;   // [8] slot base of each rank, published with sel_flag
     int2* tiles;          // [max tiles] (group index, first row) of each 128-row tile
     int32_t* n_tiles;     // [1]
 };
@@ -139,6 +144,8 @@ hipError_t launch_k(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds,
 
 // forward pieces
 hipError_t launch_router_small(const Fwd& f, hipStream_t st);
+bool router1_ok(const Fwd& f);
+hipError_t launch_router1(const Fwd& f, hipStream_t st);
 int router_small_slices(int H);  // partial rows of the small-T router
 hipError_t launch_router_large(const Fwd& f, hipStream_t st, int stage);
 hipError_t launch_gateup_gemv(const Fwd& f, hipStream_t st);
@@ -155,6 +162,8 @@ hipError_t launch_gateup_finalize(const Fwd& f, hipStream_t st);
 hipError_t launch_combine(const Fwd& f, hipStream_t st);
 bool tok1_ok(const Fwd& f);
 bool tok1_down_ok(const Fwd& f);
+bool tok1_sel_ok(const Fwd& f);
+bool tok1_sel_leader(const Fwd& f);
 hipError_t launch_tok1_gateup(const Fwd& f, hipStream_t st);
 hipError_t launch_tok1_down(const Fwd& f, hipStream_t st);
 bool down_combine1_ok(const Fwd& f);
