@@ -434,12 +434,12 @@ def bench_chain(torch, name, steps, result):
     torch.cuda.empty_cache()
 
 
-def bench_prefill(torch, steps, result):
+def bench_prefill(torch, steps, result, name="glm_prefill"):
     import numpy as np
     import synth
     from int4_weight_expert_amd import workload
-    cfg = synth.CONFIGS["glm_prefill"]
-    log(f"[bench] building glm_prefill: T={cfg.T}")
+    cfg = synth.CONFIGS[name]
+    log(f"[bench] building {name}: T={cfg.T}")
     ml = workload.build_layer(cfg)
     x = workload.tokens_device(cfg)
     out = torch.empty_like(x)
@@ -467,8 +467,9 @@ def bench_prefill(torch, steps, result):
         t = t_eager
     kt, _ = kernel_times(torch, ml, [lambda: ml.forward(x, 0, out)], 3)
     flops = 2.0 * (cfg.T * cfg.K + cfg.T * cfg.n_shared) * 3 * cfg.H * cfg.I
-    result["extra"]["glm_prefill"] = {
-        "T": cfg.T, "ms_per_layer": t * 1e3, "ms_per_layer_eager": t_eager * 1e3,
+    result["extra"][name] = {
+        "T": cfg.T, "shared_format": "int8 row" if cfg.shared_fmt == 3 else "as routed",
+        "ms_per_layer": t * 1e3, "ms_per_layer_eager": t_eager * 1e3,
         "graph_replay_matches_eager": graph_ok, "graph_replay_percentiles": pct, "tokens_per_s": cfg.T / t,
         "expert_flops": flops, "tflops": flops / t / 1e12,
         "frac_fp16_mfma_peak": flops / t / 1e12 / BF16_PEAK_TFLOPS,
@@ -477,7 +478,7 @@ def bench_prefill(torch, steps, result):
         "gemm_row_occupancy": rows / (tiles * 128.0), "gemm_rows_issued_32": issued,
         "gemm_issued_row_occupancy": rows / float(issued),
     }
-    log(f"[bench] glm_prefill: {t * 1e3:.2f} ms/layer, {flops / t / 1e12:.1f} TFLOP/s; {kt}")
+    log(f"[bench] {name}: {t * 1e3:.2f} ms/layer, {flops / t / 1e12:.1f} TFLOP/s; {kt}")
     ml.close()
     del ml
     torch.cuda.empty_cache()
@@ -699,7 +700,8 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=16)
     ap.add_argument("--no-probe", action="store_true", help="skip the streaming-read ceiling")
     ap.add_argument("--only", choices=["decode", "verify", "edge0", "edge0_k8", "prefill", "grouped",
-                                       "softmax", "int8_shared", "requant", "staged"],
+                                       "softmax", "int8_shared", "requant", "staged",
+                                       "prefill_int8_shared"],
                     help="run one workload only (for profiling); the JSON line then "
                          "carries that workload in extra")
     ap.add_argument("--copy-probe", action="store_true",
@@ -732,6 +734,7 @@ def main():
          "edge0": lambda: bench_chain(torch, "edge0_decode", 200, result),
          "edge0_k8": lambda: bench_chain(torch, "edge0_decode_k8", 200, result),
          "prefill": lambda: bench_prefill(torch, 20, result),
+         "prefill_int8_shared": lambda: bench_prefill(torch, 20, result, "glm_prefill_int8_shared"),
          "grouped": lambda: bench_rotated(torch, "glm_decode_grouped", 200, result),
          "softmax": lambda: bench_rotated(torch, "glm_decode_softmax", 200, result),
          "int8_shared": lambda: bench_rotated(torch, "glm_decode_int8_shared", 200, result),
@@ -759,6 +762,7 @@ def main():
         bench_requant(torch, result)
         bench_staged(torch, result)
         bench_prefill(torch, 20, result)
+        bench_prefill(torch, 10, result, "glm_prefill_int8_shared")
     if not args.no_cpu:
         log("[bench] cpu baseline (oracle)")
         result["cpu_baseline"], result["extra"]["cpu_baseline_by_workload"] = \

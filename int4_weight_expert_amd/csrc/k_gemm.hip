@@ -35,6 +35,8 @@
 // straight into registers (8 bytes per lane: lanes l and l+32 read the two
 // halves of a row's chunk, each half feeding one MFMA per step).
 // Activations and codes are fetched GDEP steps ahead.
+#include <type_traits>
+
 #include "k_common.h"
 
 namespace moe {
@@ -76,27 +78,41 @@ __device__ __forceinline__ half8 b_operand(uint32_t dword, uint32_t mv)
 
 // Output rows o0, o1 of wavefront w's two B blocks in N tile `ntile`, and
 // the byte offsets of their matrices in the expert's slot.
-template <int MODE>
+template <int MODE, bool S8 = false>
 __device__ __forceinline__ void gemm_out_rows(int ntile, int w, int n, int H, int I, int& o0,
                                               int& o1, size_t& mat0, size_t& mat1)
 {
+    // int8 matrices take a byte per weight, int4 half a byte
+    const size_t msz = S8 ? (size_t)I * H : (size_t)I * H / 2;
     if (MODE == GEMM_GU) {
         o0 = ntile * 256 + 32 * w + n;  // gate and up of the same row
         o1 = o0;
         mat0 = 0;
-        mat1 = (size_t)I * H / 2;
+        mat1 = msz;
     } else {
         o0 = ntile * 512 + 64 * w + n;  // rows n and n + 32 of one block
         o1 = o0 + 32;
-        mat0 = mat1 = (size_t)I * H;
+        mat0 = mat1 = 2 * msz;
     }
+}
+
+// B operand of 8 int8 codes (stored q + 128): bytes i and 4 + i of the
+// dword pair as the fp16 pair (1024 + b_i, 1024 + b_{4+i}), the activations'
+// pair order
+__device__ __forceinline__ half8 b_operand8(uint32_t lo, uint32_t hi)
+{
+    const uint32_t p0 = __builtin_amdgcn_perm(hi, lo, 0x0C040C00u) | 0x64006400u;
+    const uint32_t p1 = __builtin_amdgcn_perm(hi, lo, 0x0C050C01u) | 0x64006400u;
+    const uint32_t p2 = __builtin_amdgcn_perm(hi, lo, 0x0C060C02u) | 0x64006400u;
+    const uint32_t p3 = __builtin_amdgcn_perm(hi, lo, 0x0C070C03u) | 0x64006400u;
+    return as_half8(p0, p1, p2, p3);
 }
 
 // The tile's prologue, K loop and epilogue, specialised on the number MB of
 // 32-row blocks that hold rows of the group: a partial tile issues only its
 // blocks' LDS reads and MFMAs.  Each specialisation is self-contained, so no
 // register array lives across the dispatch.
-template <int MODE, int MB>
+template <int MODE, int MB, bool S8>
 __device__ __forceinline__ void gemm_tile(const Fwd& f, uint4 (*As)[4][GM], const int* s_src,
                                           const int* s_out, const float* s_inv,
                                           const float* s_sum, const float* s_rs,
@@ -109,21 +125,25 @@ __device__ __forceinline__ void gemm_tile(const Fwd& f, uint4 (*As)[4][GM], cons
     const int NC = K / 32;                  // K steps (chunks)
     int o0, o1;
     size_t mat0, mat1;
-    gemm_out_rows<MODE>(ntile, w, n, H, I, o0, o1, mat0, mat1);
-    const uint8_t* tab = base + (size_t)3 * H * I / 2;  // fp32 row scales
+    gemm_out_rows<MODE, S8>(ntile, w, n, H, I, o0, o1, mat0, mat1);
+    // fp32 row scales after the three matrices
+    const uint8_t* tab = base + (S8 ? (size_t)3 * H * I : (size_t)3 * H * I / 2);
 
     const uint32_t mv = magic_vgpr();
     // weight streams: the wavefront's rows lie in one 64-row block (a
-    // wave-uniform resource); the lane's row within it is the offset
-    const int C = NC;  // chunks per weight row
+    // wave-uniform resource); the lane's row within it is the offset.  A
+    // 16-byte chunk holds 32 int4 codes or 16 int8 codes: a K step of 32
+    // inputs is one int4 chunk (lane half h reads its bytes 8h..8h+7) or two
+    // int8 chunks (lane half h reads chunk 2 step + h whole).
+    const int C = S8 ? 2 * NC : NC;  // chunks per weight row
     const int blk = MODE == GEMM_GU ? ntile * 4 + (w >> 1) : ntile * 8 + w;
     const __amdgpu_buffer_rsrc_t rw0 =
         make_rsrc(base + mat0 + (size_t)blk * C * 1024, (uint32_t)C * 1024);
     const __amdgpu_buffer_rsrc_t rw1 =
         make_rsrc(base + mat1 + (size_t)blk * C * 1024, (uint32_t)C * 1024);
-    // lane half h reads bytes 8h..8h+7 of the row's 16-byte chunk
-    const uint32_t v0 = (uint32_t)(o0 & 63) * 16 + half * 8;
-    const uint32_t v1 = (uint32_t)(o1 & 63) * 16 + half * 8;
+    const uint32_t v0 = S8 ? (uint32_t)(o0 & 63) * 16 + half * 1024 : (uint32_t)(o0 & 63) * 16 + half * 8;
+    const uint32_t v1 = S8 ? (uint32_t)(o1 & 63) * 16 + half * 1024 : (uint32_t)(o1 & 63) * 16 + half * 8;
+    constexpr uint32_t STEP = S8 ? 2048 : 1024;  // code bytes per K step and 64-row block
 
     // activation loader: thread -> row tid & 127, piece tid >> 7 (a
     // wavefront writes 64 consecutive rows of one piece: no bank conflict)
@@ -155,11 +175,19 @@ __device__ __forceinline__ void gemm_tile(const Fwd& f, uint4 (*As)[4][GM], cons
         A0[k] = z4;
         if (Ag) A0[k] = Ag[k * 4];
     }
-    uint2 B0[GDEP], B1[GDEP];
+    // codes: int4 8 bytes per lane and step, int8 16 bytes (GDEP steps
+    // either way)
+    typedef typename std::conditional<S8, uint4, uint2>::type BT;
+    BT B0[GDEP], B1[GDEP];
 #pragma unroll
     for (int k = 0; k < GDEP; ++k) {
-        B0[k] = bload8(rw0, v0 + k * 1024, 0);
-        B1[k] = bload8(rw1, v1 + k * 1024, 0);
+        if constexpr (S8) {
+            B0[k] = bload16(rw0, v0 + k * STEP, 0);
+            B1[k] = bload16(rw1, v1 + k * STEP, 0);
+        } else {
+            B0[k] = bload8(rw0, v0 + k * STEP, 0);
+            B1[k] = bload8(rw1, v1 + k * STEP, 0);
+        }
     }
     __syncthreads();
 
@@ -176,14 +204,26 @@ __device__ __forceinline__ void gemm_tile(const Fwd& f, uint4 (*As)[4][GM], cons
             if (Ag && c + GDEP < NC) A0[k] = Ag[(c + GDEP) * 4];
             // codes of step c; refill the slot with step c + GDEP (a load
             // past the row's last chunk returns zeros)
-            const uint2 w0 = B0[k], w1 = B1[k];
-            B0[k] = bload8(rw0, v0 + (c + GDEP) * 1024, 0);
-            B1[k] = bload8(rw1, v1 + (c + GDEP) * 1024, 0);
+            const BT w0 = B0[k], w1 = B1[k];
             // the K order inside a chunk is free as long as A and B agree:
             // lane half h takes inputs 16h..16h+7 in the first MFMA and
-            // 16h+8..16h+15 in the second (dwords 2h, 2h+1; LDS pieces 2h, 2h+1)
-            const half8 b00 = b_operand(w0.x, mv), b01 = b_operand(w0.y, mv);
-            const half8 b10 = b_operand(w1.x, mv), b11 = b_operand(w1.y, mv);
+            // 16h+8..16h+15 in the second (LDS pieces 2h, 2h+1)
+            half8 b00, b01, b10, b11;
+            if constexpr (S8) {
+                B0[k] = bload16(rw0, v0 + (c + GDEP) * STEP, 0);
+                B1[k] = bload16(rw1, v1 + (c + GDEP) * STEP, 0);
+                b00 = b_operand8(w0.x, w0.y);
+                b01 = b_operand8(w0.z, w0.w);
+                b10 = b_operand8(w1.x, w1.y);
+                b11 = b_operand8(w1.z, w1.w);
+            } else {
+                B0[k] = bload8(rw0, v0 + (c + GDEP) * STEP, 0);
+                B1[k] = bload8(rw1, v1 + (c + GDEP) * STEP, 0);
+                b00 = b_operand(w0.x, mv);
+                b01 = b_operand(w0.y, mv);
+                b10 = b_operand(w1.x, mv);
+                b11 = b_operand(w1.y, mv);
+            }
             const uint4(*Ab)[GM] = As[c & 1];
             half8 a0[4], a1[4];
 #pragma unroll
@@ -207,7 +247,10 @@ __device__ __forceinline__ void gemm_tile(const Fwd& f, uint4 (*As)[4][GM], cons
         }
     }
 
-    // epilogue: lane holds column o of each block, rows (j/4)*8 + half*4 + j%4
+    // epilogue: lane holds column o of each block, rows (j/4)*8 + half*4 + j%4;
+    // int4 (stored c + 8, 1024 + 16 n): sum c x = acc/16 - 72 S; int8
+    // (stored q + 128, 1024 + n): sum q x = acc - 1152 S
+    constexpr float CA = S8 ? 1.0f : 0.0625f, CB = S8 ? -1152.f : -72.f;
     if (MODE == GEMM_GU) {
         const float sg = ((const float*)tab)[o0], su = ((const float*)tab)[I + o0];
 #pragma unroll
@@ -217,8 +260,8 @@ __device__ __forceinline__ void gemm_tile(const Fwd& f, uint4 (*As)[4][GM], cons
                 const int i = 32 * mb + (j >> 2) * 8 + half * 4 + (j & 3);
                 if (i < rows) {
                     const float sc = s_inv[i] * s_rs[i];
-                    const float g = fmaf(acc[mb][0][j], 0.0625f, -72.f * s_sum[i]) * sc * sg;
-                    const float u = fmaf(acc[mb][1][j], 0.0625f, -72.f * s_sum[i]) * sc * su;
+                    const float g = fmaf(acc[mb][0][j], CA, CB * s_sum[i]) * sc * sg;
+                    const float u = fmaf(acc[mb][1][j], CA, CB * s_sum[i]) * sc * su;
                     f.hbuf[(size_t)s_out[i] * I + o0] = g / (1.0f + expf(-g)) * u;
                 }
             }
@@ -232,8 +275,8 @@ __device__ __forceinline__ void gemm_tile(const Fwd& f, uint4 (*As)[4][GM], cons
                 if (i < rows) {
                     const float sc = s_inv[i];
                     float* y = f.ypart + (size_t)s_out[i] * H;
-                    y[o0] = fmaf(acc[mb][0][j], 0.0625f, -72.f * s_sum[i]) * sc * sd0;
-                    y[o1] = fmaf(acc[mb][1][j], 0.0625f, -72.f * s_sum[i]) * sc * sd1;
+                    y[o0] = fmaf(acc[mb][0][j], CA, CB * s_sum[i]) * sc * sd0;
+                    y[o1] = fmaf(acc[mb][1][j], CA, CB * s_sum[i]) * sc * sd1;
                 }
             }
     }
@@ -314,11 +357,21 @@ __global__ void __launch_bounds__(64 * GW, 1) k_gemm(Fwd f)
         }
         return;
     }
+    if (grp.kind == 1 && f.shared_fmt == MOE_W_INT8_ROW) {
+        // per-row int8 shared expert (the same tile, int8 B operands)
+        switch ((rows + 31) >> 5) {
+        case 1: gemm_tile<MODE, 1, true>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
+        case 2: gemm_tile<MODE, 2, true>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
+        case 3: gemm_tile<MODE, 3, true>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
+        default: gemm_tile<MODE, 4, true>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
+        }
+        return;
+    }
     switch ((rows + 31) >> 5) {
-    case 1: gemm_tile<MODE, 1>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
-    case 2: gemm_tile<MODE, 2>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
-    case 3: gemm_tile<MODE, 3>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
-    default: gemm_tile<MODE, 4>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
+    case 1: gemm_tile<MODE, 1, false>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
+    case 2: gemm_tile<MODE, 2, false>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
+    case 3: gemm_tile<MODE, 3, false>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
+    default: gemm_tile<MODE, 4, false>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
     }
 }
 

@@ -252,8 +252,7 @@ int run_router(moe_ctx* c, const Fwd& f)
 bool uses_gemm(const moe_ctx* c, int T)
 {
     return c->hbuf != nullptr && T > ROUTER_SMALL_MAX_T && T >= c->gemm_min_tokens &&
-           gemm_shape_ok(c->cfg.hidden, c->cfg.inter) &&
-           !(c->cfg.n_shared > 0 && c->shared_fmt == MOE_W_INT8_ROW);
+           gemm_shape_ok(c->cfg.hidden, c->cfg.inter);
 }
 
 int run_forward_gemm(moe_ctx* c, Fwd& f)

@@ -98,3 +98,6 @@ CONFIGS["glm_decode_int8_shared"] = CONFIGS["glm_decode"].with_(name="glm_decode
 # the same decode layer scored by a softmax over all experts (renormalised top-8)
 CONFIGS["glm_decode_softmax"] = CONFIGS["glm_decode"].with_(name="glm_decode_softmax", scoring=1,
                                                             n_layers=4, seed=601)
+# GLM-5.2 shape prefill with the shared expert in per-row int8
+CONFIGS["glm_prefill_int8_shared"] = CONFIGS["glm_prefill"].with_(name="glm_prefill_int8_shared",
+                                                                  shared_fmt=3, seed=303)

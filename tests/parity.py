@@ -13,6 +13,7 @@ against the oracle):
 """
 from __future__ import annotations
 
+import os
 import sys
 from concurrent.futures import ThreadPoolExecutor
 
@@ -146,3 +147,27 @@ def check_residual(x, got_next, ref_next, keep=None, what=""):
     assert e_next <= REL_TOL, f"{what}: new x max|d|/max|ref| = {e_next:.3e}"
     assert e_term <= REL_TOL, f"{what}: moe term max|d|/max|ref| = {e_term:.3e}"
     return e_next, e_term
+
+
+WORKERS = min(16, os.cpu_count() or 1)
+
+
+def block_sample(ids, E, excluded, block=32):
+    """Tokens that put a compared row in every occupied 32-row block of the
+    grouped GEMM: an expert's rows are its tokens in ascending order (the
+    stable bucketing), the shared expert's rows are all tokens.  Each block
+    contributes its last unflagged token; a block of near-tie tokens only
+    (a rarely chosen expert whose few tokens all sit on a tie, where either
+    side may route differently) is left out and counted."""
+    T, _ = ids.shape
+    picks, uncovered = set(), 0
+    groups = [np.flatnonzero((ids == e).any(axis=1)) for e in range(E)] + [np.arange(T)]
+    for toks in groups:
+        for b0 in range(0, len(toks), block):
+            blk = toks[b0:b0 + block]
+            ok = blk[~excluded[blk]]
+            if len(ok):
+                picks.add(int(ok[-1]))
+            else:
+                uncovered += 1
+    return np.array(sorted(picks)), uncovered

@@ -7,13 +7,12 @@ shared expert) through the C ABI, in the layouts the benchmark times:
     that cover every occupied 32-row block of every grouped-GEMM tile.
 The oracle generates only the experts the tokens select; the GPU slots of
 those experts must hold exactly the oracle's packed bytes."""
-import os
-
 import numpy as np
 import pytest
 
 import synth
-from parity import OracleLayer, check_ids, flags, log, oracle_blob, rel_err, REL_TOL, check_residual
+from parity import (OracleLayer, WORKERS, block_sample, check_ids, check_residual, flags, log,
+                    oracle_blob, rel_err, REL_TOL)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -98,30 +97,6 @@ def test_glm_verify_chained_teacher_forced():
     finally:
         ml.close()
         torch.cuda.empty_cache()
-
-
-WORKERS = min(16, os.cpu_count() or 1)
-
-
-def block_sample(ids, E, excluded, block=32):
-    """Tokens that put a compared row in every occupied 32-row block of the
-    grouped GEMM: an expert's rows are its tokens in ascending order (the
-    stable bucketing), the shared expert's rows are all tokens.  Each block
-    contributes its last unflagged token; a block of near-tie tokens only
-    (a rarely chosen expert whose few tokens all sit on a tie, where either
-    side may route differently) is left out and counted."""
-    T, _ = ids.shape
-    picks, uncovered = set(), 0
-    groups = [np.flatnonzero((ids == e).any(axis=1)) for e in range(E)] + [np.arange(T)]
-    for toks in groups:
-        for b0 in range(0, len(toks), block):
-            blk = toks[b0:b0 + block]
-            ok = blk[~excluded[blk]]
-            if len(ok):
-                picks.add(int(ok[-1]))
-            else:
-                uncovered += 1
-    return np.array(sorted(picks)), uncovered
 
 
 def test_glm_prefill_2048():

@@ -7,8 +7,8 @@ import pytest
 
 import oracle
 import synth
-from parity import (OracleLayer, check_ids, check_residual, flags, log, oracle_blob, rel_err,
-                    REL_TOL)
+from parity import (OracleLayer, WORKERS, block_sample, check_ids, check_residual, flags, log,
+                    oracle_blob, rel_err, REL_TOL)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -184,24 +184,58 @@ def test_requant_shared_int8(kind):
         ml.close()
 
 
-def test_many_tokens_stay_on_gemv():
-    """T = 300 (past the k-slice partial buffers' 16 and 64 tokens, so the
-    plan drops to fewer slices): int8 shared experts keep every T on the
-    GEMV path."""
+@pytest.mark.parametrize("path", ["gemm", "gemv"])
+def test_many_tokens(path):
+    """T = 300 with an int8 shared expert: through the grouped GEMM (the
+    shared expert's tiles take int8 B operands) and, with the GEMM threshold
+    raised, through the GEMVs (past their k-slice partial buffers' 16 and 64
+    tokens, so the plan drops to fewer slices)."""
     cfg = synth.CONFIGS["int8_shared"]
     ml = workload.build_layer(cfg, max_tokens=300)
     ref = OracleLayer(cfg, 0)
     try:
+        if path == "gemv":
+            M._check("moe_set_gemm_min_tokens", M.moe_set_gemm_min_tokens(ml.ctx, 1 << 20))
         x = synth.tokens(cfg, T=300, stream=9)
         got = ml.forward(torch.from_numpy(x).cuda(), 0).cpu().numpy()
         assert ml.status()[0] == 0
         r_out, _, _, gk, gi = ref.forward(x)
         excluded, _ = flags(gk, gi)
         err = rel_err(got, r_out, ~excluded)
-        log(f"int8_shared T=300: max|d|/max|ref| = {err:.2e}, {int(excluded.sum())} flagged")
+        log(f"int8_shared T=300 ({path}): max|d|/max|ref| = {err:.2e}, {int(excluded.sum())} flagged")
         assert err <= REL_TOL
     finally:
         ml.close()
+
+
+def test_glm_prefill_int8_shared():
+    """GLM-shape prefill (T = 2048) with the shared expert in per-row int8
+    through the grouped GEMM: routing of every token, and the outputs of
+    tokens covering every occupied 32-row block of every expert's rows and of
+    the shared expert's (whose tiles run the int8 operand path)."""
+    cfg = synth.CONFIGS["glm_prefill_int8_shared"]
+    log("building glm_prefill_int8_shared: 1 layer x 256 experts, T=2048")
+    ml = workload.build_layer(cfg)
+    try:
+        x = synth.tokens(cfg, T=cfg.T)
+        xd = torch.from_numpy(x).cuda()
+        out = ml.forward(xd, 0).cpu().numpy()
+        ids, w = ml.route(xd, 0)
+        assert ml.status()[0] == 0
+        ref = OracleLayer(cfg, 0)
+        r_ids, r_w, _, _, gk, gi = ref.route(x)
+        check_ids(ids.cpu().numpy(), r_ids, w.cpu().numpy(), r_w, gk, gi, "prefill int8 shared")
+        excluded, _ = flags(gk, gi)
+        sample, uncovered = block_sample(r_ids, cfg.E, excluded)
+        assert uncovered <= 4
+        r_out, _, _, _, _ = ref.forward(x[sample], workers=WORKERS)
+        err = rel_err(out[sample], r_out)
+        log(f"glm prefill, int8 shared: {len(sample)} tokens, max|d|/max|ref| = {err:.3e}")
+        assert err <= REL_TOL
+        assert np.isfinite(out).all()
+    finally:
+        ml.close()
+        torch.cuda.empty_cache()
 
 
 def test_graph_replay_int8_shared():
