@@ -172,7 +172,8 @@ def bench_decode(torch, args, result):
             "bound": "hbm", "achieved": alg_gateup / t_gu / 1e9, "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": alg_gateup / t_gu / 1e9 / HBM_PEAK_GBS,
             "traffic": measured_traffic(),
-            "kernel": "k_gu (int4 gate/up GEMV, one wavefront per (expert, 64-row block, k-slice))",
+            "kernel": "k_gu8 (one-token int4 gate/up: a workgroup per (expert, 8 rows), "
+                      "4 wavefronts splitting H, h written directly)",
             "algorithmic_bytes_per_launch": alg_gateup,
             "avg_launch_ms": kt["gateup_gemv"],
         },
@@ -556,19 +557,20 @@ def stream_ceiling(torch, result, unit_bytes: int):
 
 
 def measured_traffic():
-    """HBM bytes per launch of the gate/up kernel from the committed counter
-    runs, if they were taken on the current kernel source (else None)."""
+    """HBM bytes per launch of the one-token gate/up kernel from the
+    committed counter runs, if they were taken on the current kernel source
+    (else None)."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
-    src = os.path.join(ROOT, "int4_weight_expert_amd", "csrc", "k_gemv.hip")
+    src = os.path.join(ROOT, "int4_weight_expert_amd", "csrc", "k_tok1.hip")
     try:
         rec = json.load(open(path))
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     except (OSError, ValueError):
         return None
-    if rec.get("k_gemv_sha256") != sha:
+    if rec.get("k_tok1_sha256") != sha:
         return None
-    return rec.get("k_gu_bytes_per_launch")
+    return rec.get("gateup_bytes_per_launch")
 
 
 def _oracle_rate(jobs, threads: int):
@@ -730,6 +732,8 @@ def main():
         "extra": {},
     }
     if args.only and args.only != "decode":
+        if args.copy_probe:
+            copy_probe(torch, result)
         {"verify": lambda: bench_chain(torch, "glm_verify", 64, result),
          "edge0": lambda: bench_chain(torch, "edge0_decode", 200, result),
          "edge0_k8": lambda: bench_chain(torch, "edge0_decode_k8", 200, result),
