@@ -16,7 +16,7 @@ LIB = os.path.join(HERE, "libmoe_int4.so")
 PROBE_SRC = "hbm_probe.hip"
 PROBE_LIB = os.path.join(HERE, "libhbm_probe.so")
 
-SOURCES = ["moe_api.hip", "moe_stage.hip", "k_pack.hip", "k_small.hip", "k_large.hip", "k_gemv.hip", "k_gemm.hip", "k_tok1.hip"]
+SOURCES = ["moe_api.hip", "moe_stage.hip", "k_pack.hip", "k_small.hip", "k_large.hip", "k_gemv.hip", "k_gemm.hip", "k_tok1.hip", "k_midt.hip"]
 
 # -packed-fp32-ops: keep hipcc from forming v_pk_{add,mul,fma}_f32 out of
 # ordinary float code (the host pass warns that it does not know the

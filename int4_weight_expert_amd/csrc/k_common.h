@@ -144,6 +144,20 @@ __device__ __forceinline__ void nib_pairs(uint32_t w, uint32_t mv, uint32_t& p0,
     p3 = bfi(NIB_MASK, w >> 8, mv);
 }
 
+// The same pairs in plain code, for matrix-core operands: the compiler
+// inserts the wait states a matrix instruction needs after the vector ALU
+// writes its source registers only for instructions it can see, not for
+// the results of inline assembly (with nib_pairs feeding v_mfma directly,
+// the few-token kernels read stale operands).
+__device__ __forceinline__ void nib_pairs_mfma(uint32_t w, uint32_t& p0, uint32_t& p1,
+                                               uint32_t& p2, uint32_t& p3)
+{
+    p0 = ((w << 4) & NIB_MASK) | 0x64006400u;
+    p1 = (w & NIB_MASK) | 0x64006400u;
+    p2 = ((w >> 4) & NIB_MASK) | 0x64006400u;
+    p3 = ((w >> 8) & NIB_MASK) | 0x64006400u;
+}
+
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
 {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, a), __builtin_bit_cast(h2_t, b), c,

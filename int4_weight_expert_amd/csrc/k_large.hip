@@ -25,8 +25,10 @@ __device__ __forceinline__ uint32_t ordf(float c)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Per-token sum, RMSNorm factor and sums of 64-column groups; one
-// wavefront per token.  H must be a multiple of 256.
+// Per-token sum and RMSNorm factor, and x staged for the grouped GEMM: the
+// whole row as fp16 with one power-of-two scale (largest magnitude in
+// [2^13, 2^14)), in pair order, and its sum; one wavefront per token.  H
+// must be a multiple of 256.
 template <int NG>
 __global__ void __launch_bounds__(256) k_tokstats(Fwd f)
 {
@@ -36,22 +38,7 @@ __global__ void __launch_bounds__(256) k_tokstats(Fwd f)
     const int H = f.H;
     const float* xt = f.x + (size_t)t * H;
     float sum = 0.f, ss = 0.f;
-    if constexpr (NG > 0) {
-        // grouped GEMM: the whole row as fp16 with one power-of-two scale
-        // (largest magnitude in [2^13, 2^14)), in pair order, and its sum
-        stage_row<NG>(xt, H, lane, f.xq + (size_t)t * (H / 8), f.xrow + t, sum, ss);
-    } else {
-        // expert GEMVs: fp16 spans of 64
-        for (int s = 0; s < H / 64; ++s) {
-            const float v = xt[s * 64 + lane];
-            sum += v;
-            ss = fmaf(v, v, ss);
-            stage_span64(v, lane, (uint16_t*)(f.xq + (size_t)t * (H / 8) + s * 8),
-                         f.xsc + (size_t)t * (H / 64) + s);
-        }
-        sum = wsum(sum);
-        ss = wsum(ss);
-    }
+    stage_row<NG>(xt, H, lane, f.xq + (size_t)t * (H / 8), f.xrow + t, sum, ss);
     if (lane == 0) {
         f.tok[t].xsum = sum;
         f.tok[t].rscale = f.residual ? 1.0f / sqrtf(ss / (float)H + f.eps) : 1.0f;
@@ -59,10 +46,55 @@ __global__ void __launch_bounds__(256) k_tokstats(Fwd f)
     }
 }
 
+// Per-token sum and RMSNorm factor, and x staged for the expert GEMVs as
+// fp16 spans of 64 (each with its own power-of-two scale), by a 256-thread
+// workgroup: wavefront w takes spans w NS .. (w + 1) NS - 1 (NS = H / 256)
+// with eight loads in flight at a time, the four wavefronts' sums added in
+// wavefront order.
+__device__ void stage_token_spans(const Fwd& f, int t)
+{
+    __shared__ float s_ts[4][2];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int H = f.H, NS = H / 256;
+    const float* xt = f.x + (size_t)t * H;
+    float sum = 0.f, ss = 0.f;
+    for (int s0 = 0; s0 < NS; s0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = xt[(size_t)(w * NS + min(s0 + i, NS - 1)) * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (s0 + i < NS) {
+                const int s = w * NS + s0 + i;
+                sum += v[i];
+                ss = fmaf(v[i], v[i], ss);
+                stage_span64(v[i], lane, (uint16_t*)(f.xq + (size_t)t * (H / 8) + s * 8),
+                             f.xsc + (size_t)t * (H / 64) + s);
+            }
+    }
+    sum = wsum(sum);
+    ss = wsum(ss);
+    if (lane == 0) {
+        s_ts[w][0] = sum;
+        s_ts[w][1] = ss;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        sum = (s_ts[0][0] + s_ts[1][0]) + (s_ts[2][0] + s_ts[3][0]);
+        ss = (s_ts[0][1] + s_ts[1][1]) + (s_ts[2][1] + s_ts[3][1]);
+        f.tok[t].xsum = sum;
+        f.tok[t].rscale = f.residual ? 1.0f / sqrtf(ss / (float)H + f.eps) : 1.0f;
+        flag_range(f, ss);
+    }
+}
+
+// one workgroup per token
+__global__ void __launch_bounds__(256) k_tokspans(Fwd f) { stage_token_spans(f, blockIdx.x); }
+
 // Router logits for many tokens on the fp32 matrix cores
 // (v_mfma_f32_32x32x2_f32: fp32 products, fp32 accumulation).  Workgroup =
-// 64 tokens x every expert x one of ROUTER_SLICES slices of the H inputs, so
-// x is read once and each router weight once per 64 tokens.  x goes through
+// 64 tokens x every expert x one of rslices slices of the H inputs, so x is
+// read once and each router weight once per 64 tokens.  x goes through
 // LDS in chunks of 32 inputs (double-buffered, input-major so that the
 // operand reads are conflict-free); wavefront w takes experts 32w..32w+31
 // for both 32-token blocks, its router weights straight from memory.  Per
@@ -83,7 +115,7 @@ __global__ void __launch_bounds__(512) k_router_mfma(Fwd f)
     const int h = lane >> 5, m = lane & 31;
     // expert e = 32w + m: interleaved block e / 64, lane e % 64
     const float4* wb = (const float4*)f.wr + (size_t)(w >> 1) * (H / 4) * 64 + (w & 1) * 32 + m;
-    const int KC = H / ROUTER_SLICES;  // inputs per slice (H is a multiple of 256)
+    const int KC = H / f.rslices;  // inputs per slice, a multiple of 32
     const int kb = slice * KC, NCH = KC / 32;
     // x loader: threads cover (token, float4) pairs of a chunk, 512 in all
     auto load_x = [&](int ch, float4 (&v)[4]) {
@@ -152,6 +184,77 @@ __global__ void __launch_bounds__(512) k_router_mfma(Fwd f)
         }
 }
 
+// Router logits for a few tokens (2 .. 16): workgroup e holds expert e's
+// row of the row-major router copy in registers (thread l: float4 columns
+// l, l + 256, ...) and takes the tokens TT at a time, every token's loads in
+// flight together; the 4 wavefronts' sums meet in LDS in wavefront order
+// and go to logit plane 0.  Workgroup t < T also forms token t's statistics
+// (sum, RMSNorm factor, range check) and stages its x for the expert
+// kernels: the whole row with one power-of-two scale (ROWS, the
+// matrix-core path) or in spans of 64.
+constexpr int RT_TT = 4;
+
+template <int Q, int NG, bool ROWS>
+__global__ void __launch_bounds__(256) k_router_t(Fwd f)
+{
+    __shared__ float s_red[RT_TT][4];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, e = blockIdx.x;
+    const int H = f.H, H4 = H / 4, T = f.T;
+    if (e < f.E) {
+        const float4* wr = (const float4*)(f.wr_rows + (size_t)e * H);
+        float4 wv[Q];
+#pragma unroll
+        for (int k = 0; k < Q; ++k) {
+            const int c = tid + 256 * k;
+            wv[k] = c < H4 ? wr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        for (int t0 = 0; t0 < T; t0 += RT_TT) {
+            float acc[RT_TT];
+#pragma unroll
+            for (int j = 0; j < RT_TT; ++j) {
+                const float4* xr = (const float4*)(f.x + (size_t)min(t0 + j, T - 1) * H);
+                float4 xv[Q];
+#pragma unroll
+                for (int k = 0; k < Q; ++k) xv[k] = xr[min(tid + 256 * k, H4 - 1)];
+                float a = 0.f;
+#pragma unroll
+                for (int k = 0; k < Q; ++k)
+                    if (tid + 256 * k < H4) {
+                        a = fmaf(wv[k].x, xv[k].x, a);
+                        a = fmaf(wv[k].y, xv[k].y, a);
+                        a = fmaf(wv[k].z, xv[k].z, a);
+                        a = fmaf(wv[k].w, xv[k].w, a);
+                    }
+                acc[j] = wave_sum(a);
+            }
+            if (lane == 0)
+#pragma unroll
+                for (int j = 0; j < RT_TT; ++j) s_red[j][w] = acc[j];
+            __syncthreads();
+            if (tid < RT_TT && t0 + tid < T)
+                f.logits[(size_t)(t0 + tid) * f.Epad + e] =
+                    (s_red[tid][0] + s_red[tid][1]) + (s_red[tid][2] + s_red[tid][3]);
+            __syncthreads();
+        }
+    }
+    if (e < T) {
+        if (ROWS) {
+            if (w == 0) {
+                float sum, ss;
+                stage_row<NG>(f.x + (size_t)e * H, H, lane, f.xq + (size_t)e * (H / 8), f.xrow + e,
+                              sum, ss);
+                if (lane == 0) {
+                    f.tok[e].xsum = sum;
+                    f.tok[e].rscale = f.residual ? 1.0f / sqrtf(ss / (float)H + f.eps) : 1.0f;
+                    flag_range(f, ss);
+                }
+            }
+        } else {
+            stage_token_spans(f, e);
+        }
+    }
+}
+
 __global__ void __launch_bounds__(256) k_topk(Fwd f)
 {
     const int lane = threadIdx.x & 63;
@@ -159,6 +262,25 @@ __global__ void __launch_bounds__(256) k_topk(Fwd f)
     if (t >= f.T) return;
     const int E = f.E, K = f.K, Epad = f.Epad;
     const float rs = f.tok[t].rscale;
+    // the router's slice partials of the lane's 4 experts, summed in slice
+    // order, 8 slices (32 loads) in flight at a time (plane indices clamped,
+    // the clamped ones then zeroed); expert slots past E (padding of Epad)
+    // are read but not used
+    float lg[4] = {0.f, 0.f, 0.f, 0.f};
+    const int R = f.rslices;
+    for (int s0 = 0; s0 < R; s0 += 8) {
+        float v[4][8];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int e = min(lane + 64 * m, Epad - 1);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[m][i] = f.logits[((size_t)min(s0 + i, R - 1) * f.T + t) * Epad + e];
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) lg[m] += s0 + i < R ? v[m][i] : 0.f;
+    }
     float c[4], sg[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -166,12 +288,7 @@ __global__ void __launch_bounds__(256) k_topk(Fwd f)
         c[m] = -INFINITY;
         sg[m] = 0.f;
         if (e < E) {
-            // the router's slice partials, summed in slice order
-            float l = 0.f;
-#pragma unroll
-            for (int sl = 0; sl < ROUTER_SLICES; ++sl)
-                l += f.logits[((size_t)sl * f.T + t) * Epad + e];
-            l *= rs;
+            const float l = lg[m] * rs;
             if (f.scoring == MOE_SCORE_SOFTMAX) {
                 sg[m] = l;  // the probability follows below
             } else {
@@ -415,12 +532,47 @@ __global__ void __launch_bounds__(1024) k_bucket(const int32_t* __restrict__ ids
     }
 }
 
+// up to 16 tokens (each workgroup takes the tokens 4 at a time; beyond 16
+// the matrix-core router with more H slices measured faster)
+bool router_t_ok(int T, int H, const float* wr_rows)
+{
+    return T >= 2 && T <= 16 && wr_rows != nullptr && H <= 8192;
+}
+
+template <int Q>
+static hipError_t router_t_go(const Fwd& f, hipStream_t st)
+{
+    const dim3 grid((unsigned)std::max(f.E, f.T)), block(256);
+    if (!f.row_staging) return launch_k(k_router_t<Q, 1, false>, grid, block, 0, st, f);
+    const int ng = (f.H + 511) / 512;
+    if (ng <= 1) return launch_k(k_router_t<Q, 1, true>, grid, block, 0, st, f);
+    if (ng <= 2) return launch_k(k_router_t<Q, 2, true>, grid, block, 0, st, f);
+    if (ng <= 4) return launch_k(k_router_t<Q, 4, true>, grid, block, 0, st, f);
+    if (ng <= 8) return launch_k(k_router_t<Q, 8, true>, grid, block, 0, st, f);
+    if (ng <= 12) return launch_k(k_router_t<Q, 12, true>, grid, block, 0, st, f);
+    return launch_k(k_router_t<Q, 16, true>, grid, block, 0, st, f);
+}
+
 hipError_t launch_router_large(const Fwd& f, hipStream_t st, int stage)
 {
+    if (f.rslices == 1) {  // a few tokens: the row router (logits and staging), then top-K
+        switch (stage) {
+        case 0: {
+            const int q = (f.H + 1023) / 1024;
+            if (q <= 1) return router_t_go<1>(f, st);
+            if (q <= 2) return router_t_go<2>(f, st);
+            if (q <= 4) return router_t_go<4>(f, st);
+            if (q <= 6) return router_t_go<6>(f, st);
+            return router_t_go<8>(f, st);
+        }
+        case 1: return hipSuccess;
+        default: break;
+        }
+    }
     switch (stage) {
     case 0: {
         const dim3 grid((f.T + 3) / 4), block(256);
-        if (!f.row_staging) return launch_k(k_tokstats<0>, grid, block, 0, st, f);
+        if (!f.row_staging) return launch_k(k_tokspans, dim3((unsigned)f.T), block, 0, st, f);
         const int ng = (f.H + 511) / 512;  // 8-value groups per lane (H <= 8192 here)
         if (ng <= 1) return launch_k(k_tokstats<1>, grid, block, 0, st, f);
         if (ng <= 2) return launch_k(k_tokstats<2>, grid, block, 0, st, f);
@@ -430,13 +582,30 @@ hipError_t launch_router_large(const Fwd& f, hipStream_t st, int stage)
         return launch_k(k_tokstats<16>, grid, block, 0, st, f);
     }
     case 1:
-        return launch_k(k_router_mfma, dim3((f.T + 63) / 64, ROUTER_SLICES), dim3(64 * (f.Epad / 32)), 0,
-                        st, f);
+        return launch_k(k_router_mfma, dim3((f.T + 63) / 64, (unsigned)f.rslices), dim3(64 * (f.Epad / 32)),
+                        0, st, f);
     case 2: return launch_k(k_topk, dim3((f.T + 3) / 4), dim3(256), 0, st, f);
     default:
         return launch_k(k_bucket, dim3(1), dim3(1024), 0, st, (const int32_t*)f.ids, f.T * f.K,
                         f.E, f.cnt, f.off, f.perm, f.active, f.n_active, f, 1);
     }
+}
+
+int router_slices(int T, int H)
+{
+    const int tiles = (T + 63) / 64;
+    int s = ROUTER_SLICES;
+    while (s < ROUTER_SLICES_MAX && tiles * s < 256 && (H / 32) % (2 * s) == 0) s *= 2;
+    return s;
+}
+
+// rslices * T: at most ROUTER_SLICES * T; with more slices the grid had
+// fewer than 256 workgroups before the last doubling, so rslices * T <
+// 64 * 512.
+size_t router_logit_rows(int Tmax)
+{
+    return std::max<size_t>((size_t)ROUTER_SLICES * Tmax,
+                            std::min<size_t>((size_t)ROUTER_SLICES_MAX * Tmax, 32768));
 }
 
 hipError_t launch_bucket(const int32_t* ids, int T, int K, int E, int32_t* cnt, int32_t* off,

@@ -659,6 +659,7 @@ __global__ void __launch_bounds__(RT_THREADS) k_router1(Fwd f, const float* __re
             st_agent(&f.tpart[1], sq);
             f.tok[0].xsum = gs;
             f.tok[0].rscale = f.residual ? 1.0f / sqrtf(sq / (float)H + f.eps) : 1.0f;
+            flag_range(f, sq);
         }
     }
     // the descriptors that do not depend on the selection (which the
@@ -674,7 +675,8 @@ __global__ void __launch_bounds__(RT_THREADS) k_router1(Fwd f, const float* __re
     }
     if (e == 0 && threadIdx.x == 0) {
         f.n_groups[0] = f.n_shared + f.K;
-        *f.sel_flag = 0u;  // the gate/up kernel publishes its selection anew
+        // the gate/up kernel publishes its selection anew
+        for (int i = 0; i < 8; ++i) f.sel_base[i] = 0ull;
     }
 }
 

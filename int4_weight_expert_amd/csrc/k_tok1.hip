@@ -185,7 +185,7 @@ __device__ void select1(const Fwd& f, Sel1& s)
 // taking H / W inputs in NST steps of 16 chunks, every load issued at once
 // ---------------------------------------------------------------------------
 
-constexpr int SEL_POLLS = 4096;  // flag polls (with a short sleep each) before selecting locally
+constexpr int SEL_POLLS = 4096;  // polls (with a short sleep each) before selecting locally
 
 template <int FMT, int W, int NST, bool SEL>
 __global__ void __launch_bounds__(64 * W) k_gu8(Fwd f)
@@ -194,7 +194,13 @@ __global__ void __launch_bounds__(64 * W) k_gu8(Fwd f)
     __shared__ float s_red[W][16];
     const int lane = threadIdx.x & 63, w = uni((int)(threadIdx.x >> 6));
     const int H = f.H, I = f.I, C = H / 32, G = H / 64, NSB = I / 8;
-    const int sb = blockIdx.x % NSB, gi = blockIdx.x / NSB;
+    // Workgroup p runs on XCD p mod 8.  Within each run of 64 workgroups
+    // the order is transposed, so that the 8 row blocks of one 64-row slot
+    // block (whose 16-byte pieces share each 1 KiB chunk) run on one XCD.
+    // The grid is a multiple of 64 (I % 512 == 0), and each run stays in
+    // one expert group (NSB = I / 8 is a multiple of 64).
+    const int p = blockIdx.x, q = (p & ~63) + ((p & 7) << 3) + ((p >> 3) & 7);
+    const int sb = q % NSB, gi = q / NSB;
     int t = 0, r;
     const uint8_t* base;
     if (SEL) {
@@ -202,11 +208,14 @@ __global__ void __launch_bounds__(64 * W) k_gu8(Fwd f)
         // Small layers: every routed workgroup selects for itself.  Large
         // layers (sel_leader): the first routed workgroup (group ns, row
         // block 0; dispatched before the others) selects and publishes each
-        // rank's slot with an agent-scope flag; the other routed workgroups
-        // poll the flag a bounded number of times and, if it has not come,
-        // select for themselves (same steps, same result), so no workgroup
-        // ever waits unboundedly.  The first routed workgroup also writes
-        // the selection out for the later kernels.
+        // rank's slot base with an agent-scope store of base | 1 (bases are
+        // 256-byte aligned; the router cleared the words to 0); the other
+        // routed workgroups poll their rank's word a bounded number of
+        // times and, if it has not come, select for themselves (same steps,
+        // same result), so no workgroup ever waits unboundedly.  The word
+        // carries everything a poller needs, so no ordering between stores
+        // is involved.  The first routed workgroup also writes the
+        // selection out for the later kernels.
         const int ns = f.n_shared;
         if (gi < ns) {
             base = f.shared + (size_t)gi * f.shared_bytes;
@@ -233,21 +242,13 @@ __global__ void __launch_bounds__(64 * W) k_gu8(Fwd f)
                     g.kind = 0;
                     g.expert = ek;
                     f.groups[ns + kk] = g;
-                    __hip_atomic_store(&f.sel_base[kk], (uint64_t)(uintptr_t)bk, __ATOMIC_RELAXED,
+                    __hip_atomic_store(&f.sel_base[kk], (uint64_t)(uintptr_t)bk | 1ull, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
                     if (sk < 0) {
                         atomicOr(&f.status[0], (uint32_t)STATUS_NOT_RESIDENT);
                         const int code = f.layer * f.E + ek;
                         atomicOr(&f.status[1 + code / 32], 1u << (code % 32));
                     }
-                }
-                if (f.sel_leader) {
-                    // the bases reach agent coherence before the flag does
-                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-                    __builtin_amdgcn_s_waitcnt(0);
-                    __syncthreads();
-                    if (threadIdx.x == 0)
-                        __hip_atomic_store(f.sel_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 }
                 if (threadIdx.x == 0) {
                     const int slot = sel.slot[sel.ids[k]];
@@ -258,17 +259,16 @@ __global__ void __launch_bounds__(64 * W) k_gu8(Fwd f)
             } else {
                 if (threadIdx.x == 0) {
                     int ok = 0;
+                    uint64_t word = 0;
                     for (int i = 0; i < SEL_POLLS; ++i) {
-                        if (__hip_atomic_load(f.sel_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 1u) {
+                        word = __hip_atomic_load(&f.sel_base[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        if (word & 1ull) {
                             ok = 1;
                             break;
                         }
                         __builtin_amdgcn_s_sleep(8);
                     }
-                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-                    if (ok)
-                        s_base = __hip_atomic_load(&f.sel_base[k], __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
+                    s_base = word & ~1ull;
                     s_ok = ok;
                 }
                 __syncthreads();

@@ -168,6 +168,7 @@ Fwd make_fwd(moe_ctx* c, const float* x, float* out, int T, int layer, int resid
     f.x = x;
     f.out = out;
     f.T = T;
+    f.rslices = router_t_ok(T, g.hidden, c->wr_rows) ? 1 : router_slices(T, g.hidden);
     f.H = g.hidden;
     f.I = g.inter;
     f.E = g.n_experts;
@@ -216,7 +217,6 @@ Fwd make_fwd(moe_ctx* c, const float* x, float* out, int T, int layer, int resid
     f.tiles = c->tiles;
     f.n_tiles = c->n_tiles;
     f.counters = c->counters;
-    f.sel_flag = c->sel_flag;
     f.sel_base = c->sel_base;
     f.n_group = g.n_group;
     f.scoring = g.scoring;
@@ -235,7 +235,7 @@ int run_router(moe_ctx* c, const Fwd& f)
         mark(c, "router_logits");
         return hip_rc(c, launch_router1(f, c->stream));
     }
-    if (f.T <= ROUTER_SMALL_MAX_T) {
+    if (f.T <= ROUTER_SMALL_MAX_T && !f.row_staging) {
         mark(c, "router_topk_bucket");
         return hip_rc(c, launch_router_small(f, c->stream));
     }
@@ -281,6 +281,31 @@ int run_forward_gemm(moe_ctx* c, Fwd& f)
     return MOE_OK;
 }
 
+// A few tokens, row format: the large-T router (it stages x per row), the
+// matrix-core gate/up units, the h rows (slices summed, SiLU * up, staged
+// per row), the matrix-core down units and the combine.
+int run_forward_midt(moe_ctx* c, Fwd& f)
+{
+    f.row_staging = 1;
+    midt_plan(f, c->gpart_bytes, c->ypart_bytes);
+    int rc = run_router(c, f);
+    if (rc) return rc;
+    mark(c, "gateup_mfma");
+    rc = hip_rc(c, launch_midt_gateup(f, c->stream));
+    if (rc) return rc;
+    mark(c, "h_rows");
+    rc = hip_rc(c, launch_midt_hrows(f, c->stream));
+    if (rc) return rc;
+    mark(c, "down_mfma");
+    rc = hip_rc(c, launch_midt_down(f, c->stream));
+    if (rc) return rc;
+    mark(c, "combine");
+    rc = hip_rc(c, launch_combine(f, c->stream));
+    if (rc) return rc;
+    mark(c, nullptr);
+    return MOE_OK;
+}
+
 int run_forward(moe_ctx* c, const float* x, int T, int layer, float* out, int residual)
 {
     if (!c || !x || !out) return MOE_E_ARG;
@@ -290,6 +315,7 @@ int run_forward(moe_ctx* c, const float* x, int T, int layer, float* out, int re
     if (!residual && overlaps(x, nb, out, nb)) return MOE_E_ARG;
     Fwd f = make_fwd(c, x, out, T, layer, residual);
     if (uses_gemm(c, T)) return run_forward_gemm(c, f);
+    if (midt_ok(f)) return run_forward_midt(c, f);
     plan_gemv(c, f);
     if (c->tok1 && router1_ok(f) && tok1_sel_ok(f)) {
         f.sel_in_gateup = 1;
@@ -521,7 +547,7 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
     rc = rc ? rc : dalloc(c, &c->staging, std::max(c->slot_bytes, c->shared_bytes));
     rc = rc ? rc : dalloc(c, &c->part, (H / 64) * ROUTER_SMALL_MAX_T * c->Epad * 4);
     rc = rc ? rc : dalloc(c, &c->tpart, (H / 64) * ROUTER_SMALL_MAX_T * 2 * 4);
-    rc = rc ? rc : dalloc(c, &c->logits, (size_t)ROUTER_SLICES * Tm * c->Epad * 4);
+    rc = rc ? rc : dalloc(c, &c->logits, router_logit_rows((int)Tm) * c->Epad * 4);
     rc = rc ? rc : dalloc(c, &c->ids, Tm * K * 4);
     rc = rc ? rc : dalloc(c, &c->wts, Tm * K * 4);
     rc = rc ? rc : dalloc(c, &c->tok, Tm * sizeof(TokStat));
@@ -549,7 +575,8 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
     rc = rc ? rc : dalloc(c, &c->gpart, c->gpart_bytes);
     rc = rc ? rc : dalloc(c, &c->ypart, c->ypart_bytes);
     if (g.wfmt == MOE_W_INT4_ROW && Tm > ROUTER_SMALL_MAX_T) {
-        // grouped-GEMM path workspace
+        // per-row staging (the few-token matrix-core path and the grouped
+        // GEMM) and the grouped-GEMM workspace
         rc = rc ? rc : dalloc(c, &c->xrow, Tm * 8);
         rc = rc ? rc : dalloc(c, &c->hrow, rows * 8);
         rc = rc ? rc : dalloc(c, &c->hbuf, rows * I * 4);
@@ -557,7 +584,6 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
         rc = rc ? rc : dalloc(c, &c->n_tiles, 4);
     }
     rc = rc ? rc : dalloc(c, &c->counters, (1 + H / 64) * 4);
-    rc = rc ? rc : dalloc(c, &c->sel_flag, 4);
     rc = rc ? rc : dalloc(c, &c->sel_base, 8 * 8);
     c->status_words = 1 + (L * E + 31) / 32;
     rc = rc ? rc : dalloc(c, &c->status, c->status_words * 4);

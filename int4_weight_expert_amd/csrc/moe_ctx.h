@@ -50,7 +50,6 @@ struct moe_ctx {
     int2* tiles = nullptr;
     int32_t* n_tiles = nullptr;
     uint32_t* counters = nullptr;
-    uint32_t* sel_flag = nullptr;
     uint64_t* sel_base = nullptr;
     uint32_t* status = nullptr;
     size_t status_words = 0;

@@ -66,7 +66,7 @@ struct Fwd {
     float* part;          // small-T router partial logits [S][T][Epad]
     float* tpart;         // small-T router partial token sums [S][T][2] (sum, sum of squares)
     int S;                // router K-slices of 64 columns (S = H/64)
-    float* logits;        // [ROUTER_SLICES][T][Epad] partial logits (large-T router)
+    float* logits;        // [rslices][T][Epad] partial logits (large-T router)
     int32_t* ids;         // [T][K]
     float* wts;           // [T][K]
     TokStat* tok;         // [T]
@@ -93,6 +93,7 @@ struct Fwd {
     float* ypart;         // [rows][H/64][dn_ks][64] down partials ([rows][H] when dn_ks = 1)
     // grouped-GEMM path (many tokens): x and h staged per row in xq / hq
     int row_staging;      // 1: stage x per row (grouped GEMM), 0: in spans of 64 (GEMVs)
+    int rslices;          // H slices (partial logit planes) of the large-T router
     float2* xrow;         // [T] per token (2^-k, sum of its fp16 values)
     float2* hrow;         // [rows]
     float* hbuf;          // [rows][I] h in fp32 (gate/up GEMM output)
@@ -100,8 +101,8 @@ struct Fwd {
     int h_f32;            // 1: the down GEMV stages its h slices from hf (one token)
     int sel_in_gateup;    // 1: the one-token gate/up kernel selects the experts itself
     int sel_leader;       // 1: one gate/up workgroup selects and publishes to the others
-    uint32_t* sel_flag;   // [1] the gate/up kernel's selection published (reset by the router)
-    uint64_t* sel_base;   // [8] slot base of each rank, published with sel_flag
+    uint64_t* sel_base;   // [8] slot base | 1 of each rank once the gate/up kernel's selection is
+                          // published (0 = not yet: cleared by the router)
     int2* tiles;          // [max tiles] (group index, first row) of each 128-row tile
     int32_t* n_tiles;     // [1]
 };
@@ -166,6 +167,14 @@ bool tok1_sel_ok(const Fwd& f);
 bool tok1_sel_leader(const Fwd& f);
 hipError_t launch_tok1_gateup(const Fwd& f, hipStream_t st);
 hipError_t launch_tok1_down(const Fwd& f, hipStream_t st);
+// few tokens (MIDT_MIN_T .. the grouped GEMM's threshold), row format,
+// matrix cores; below MIDT_MIN_T the GEMVs (as fast at 8 tokens, measured)
+constexpr int MIDT_MIN_T = 9;
+bool midt_ok(const Fwd& f);
+void midt_plan(Fwd& f, size_t gpart_bytes, size_t ypart_bytes);
+hipError_t launch_midt_gateup(const Fwd& f, hipStream_t st);
+hipError_t launch_midt_hrows(const Fwd& f, hipStream_t st);
+hipError_t launch_midt_down(const Fwd& f, hipStream_t st);
 bool down_combine1_ok(const Fwd& f);
 hipError_t launch_down_combine1(const Fwd& f, hipStream_t st);
 size_t gemv_lds_bytes(int chunks_per_slice, int T);
@@ -173,6 +182,15 @@ int gemv_step_chunks(int which);
 int gemv_max_dn_ks();
 
 constexpr int ROUTER_SMALL_MAX_T = 8;
-constexpr int ROUTER_SLICES = 8;  // H slices of the large-T router (partial logit planes)
+constexpr int ROUTER_SLICES = 8;      // H slices of the large-T router at its largest T
+constexpr int ROUTER_SLICES_MAX = 64;  // ... and at its smallest (one 64-token tile)
+// H slices of the large-T router for T tokens: 8, doubled while the grid
+// has fewer than 256 workgroups (up to 64, and while each slice keeps a
+// whole number of 32-input chunks), so that a few tokens do not read the
+// whole router through a handful of workgroups.
+int router_slices(int T, int H);
+// the few-token row router (2 .. 16 tokens; rslices = 1)
+bool router_t_ok(int T, int H, const float* wr_rows);
+size_t router_logit_rows(int Tmax);  // rslices * T at most, over T <= Tmax
 
 }  // namespace moe

@@ -84,3 +84,25 @@ def test_deterministic_and_missing_expert(case):
         assert err <= REL_TOL
     finally:
         ml.map(0, victim, victim)
+
+
+def test_non_finite_input_is_reported(case):
+    """A NaN or an infinity in the token sets MOE_E_RANGE on the one-token
+    router too (its first workgroup forms the token's sum of squares); the
+    status clears, and the next finite forward is clean and matches."""
+    cfg, ml, ref = case
+    x = synth.tokens(cfg, T=1, stream=30)
+    for bad in (np.nan, np.inf):
+        xb = x.copy()
+        xb[0, cfg.H // 3] = bad
+        ml.forward(torch.from_numpy(xb).cuda(), 0)
+        rc, missing = ml.status()
+        assert rc == M.MOE_E_RANGE and missing == [], (bad, rc)
+        assert ml.status()[0] == M.MOE_OK
+    out = ml.forward(torch.from_numpy(x).cuda(), 0).cpu().numpy()
+    assert ml.status()[0] == M.MOE_OK
+    r_out, _, _, gk, gi = ref.forward(x)
+    excluded, _ = flags(gk, gi)
+    err = rel_err(out, r_out, ~excluded)
+    log(f"{cfg.name} after the non-finite inputs: max|d|/max|ref| = {err:.2e}")
+    assert err <= REL_TOL
