@@ -149,13 +149,15 @@ __device__ __forceinline__ void nib_pairs(uint32_t w, uint32_t mv, uint32_t& p0,
 // writes its source registers only for instructions it can see, not for
 // the results of inline assembly (with nib_pairs feeding v_mfma directly,
 // the few-token kernels read stale operands).
-__device__ __forceinline__ void nib_pairs_mfma(uint32_t w, uint32_t& p0, uint32_t& p1,
+// mv holds 0x64006400 in a form the compiler cannot fold (Fwd::magic), so
+// that each pair is one v_bfi_b32 it forms itself.
+__device__ __forceinline__ void nib_pairs_mfma(uint32_t w, uint32_t mv, uint32_t& p0, uint32_t& p1,
                                                uint32_t& p2, uint32_t& p3)
 {
-    p0 = ((w << 4) & NIB_MASK) | 0x64006400u;
-    p1 = (w & NIB_MASK) | 0x64006400u;
-    p2 = ((w >> 4) & NIB_MASK) | 0x64006400u;
-    p3 = ((w >> 8) & NIB_MASK) | 0x64006400u;
+    p0 = ((w << 4) & NIB_MASK) | (mv & ~NIB_MASK);
+    p1 = (w & NIB_MASK) | (mv & ~NIB_MASK);
+    p2 = ((w >> 4) & NIB_MASK) | (mv & ~NIB_MASK);
+    p3 = ((w >> 8) & NIB_MASK) | (mv & ~NIB_MASK);
 }
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)

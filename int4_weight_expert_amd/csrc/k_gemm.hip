@@ -69,10 +69,10 @@ __device__ __forceinline__ half8 as_half8(uint32_t a, uint32_t b, uint32_t c, ui
 }
 
 // B operand of one 16-input half of a chunk: dword `d` of a row's 16 bytes
-__device__ __forceinline__ half8 b_operand(uint32_t dword)
+__device__ __forceinline__ half8 b_operand(uint32_t dword, uint32_t mv)
 {
     uint32_t p0, p1, p2, p3;
-    nib_pairs_mfma(dword, p0, p1, p2, p3);
+    nib_pairs_mfma(dword, mv, p0, p1, p2, p3);
     return as_half8(p0, p1, p2, p3);
 }
 
@@ -129,6 +129,7 @@ __device__ __forceinline__ void gemm_tile(const Fwd& f, uint4 (*As)[4][GM], cons
     // fp32 row scales after the three matrices
     const uint8_t* tab = base + (S8 ? (size_t)3 * H * I : (size_t)3 * H * I / 2);
 
+    const uint32_t mv = f.magic;
     // weight streams: the wavefront's rows lie in one 64-row block (a
     // wave-uniform resource); the lane's row within it is the offset.  A
     // 16-byte chunk holds 32 int4 codes or 16 int8 codes: a K step of 32
@@ -218,10 +219,10 @@ __device__ __forceinline__ void gemm_tile(const Fwd& f, uint4 (*As)[4][GM], cons
             } else {
                 B0[k] = bload8(rw0, v0 + (c + GDEP) * STEP, 0);
                 B1[k] = bload8(rw1, v1 + (c + GDEP) * STEP, 0);
-                b00 = b_operand(w0.x);
-                b01 = b_operand(w0.y);
-                b10 = b_operand(w1.x);
-                b11 = b_operand(w1.y);
+                b00 = b_operand(w0.x, mv);
+                b01 = b_operand(w0.y, mv);
+                b10 = b_operand(w1.x, mv);
+                b11 = b_operand(w1.y, mv);
             }
             const uint4(*Ab)[GM] = As[c & 1];
             half8 a0[4], a1[4];

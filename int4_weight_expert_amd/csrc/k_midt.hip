@@ -57,10 +57,10 @@ __device__ __forceinline__ uint32_t dwq(const uint4& v, int d)
 __device__ __forceinline__ half8 as_h8(const uint4& v) { return __builtin_bit_cast(half8, v); }
 
 // Dword j of a 16-byte code piece as the fp16 A operand (1024 + 16 n, pair order).
-__device__ __forceinline__ half8 codes_h8(const uint4& w, int j)
+__device__ __forceinline__ half8 codes_h8(const uint4& w, int j, uint32_t mv)
 {
     uint32_t p0, p1, p2, p3;
-    nib_pairs_mfma(dwq(w, j), p0, p1, p2, p3);
+    nib_pairs_mfma(dwq(w, j), mv, p0, p1, p2, p3);
     return as_h8(make_uint4(p0, p1, p2, p3));
 }
 
@@ -113,6 +113,7 @@ __global__ void __launch_bounds__(64) k_gum(Fwd f)
     const float* tab = (const float*)(base ? base + (size_t)3 * H * I / 2 : anchor);
     const float sgl = base ? tab[b * 64 + lane] : 0.f, sul = base ? tab[I + b * 64 + lane] : 0.f;
     const half8 ones = as_h8(make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u));
+    const uint32_t mv = f.magic;
     // row-group s: row 16 s + i of chunk 4 step + g
     uint32_t voff[4];
 #pragma unroll
@@ -159,8 +160,8 @@ __global__ void __launch_bounds__(64) k_gum(Fwd f)
                     ds = mfma16(ones, xb, ds);
 #pragma unroll
                     for (int s = 0; s < 4; ++s) {
-                        dg[s] = mfma16(codes_h8(a[s], j), xb, dg[s]);
-                        du[s] = mfma16(codes_h8(bb[s], j), xb, du[s]);
+                        dg[s] = mfma16(codes_h8(a[s], j, mv), xb, dg[s]);
+                        du[s] = mfma16(codes_h8(bb[s], j, mv), xb, du[s]);
                     }
                 }
             }
@@ -217,6 +218,7 @@ __global__ void __launch_bounds__(64) k_dnm(Fwd f)
     const float sdl =
         base ? ((const float*)(base + (size_t)3 * H * I / 2))[2 * I + b * 64 + lane] : 0.f;
     const half8 ones = as_h8(make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u));
+    const uint32_t mv = f.magic;
     uint32_t voff[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) voff[s] = (uint32_t)((g * 64 + 16 * s + i) * 16);
@@ -254,7 +256,7 @@ __global__ void __launch_bounds__(64) k_dnm(Fwd f)
                     const half8 xb = as_h8(x[j]);
                     ds = mfma16(ones, xb, ds);
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) dy[s] = mfma16(codes_h8(w[s], j), xb, dy[s]);
+                    for (int s = 0; s < 4; ++s) dy[s] = mfma16(codes_h8(w[s], j, mv), xb, dy[s]);
                 }
             }
         }

@@ -586,6 +586,100 @@ __global__ void __launch_bounds__(RT_THREADS) k_router_small(Fwd f, const float*
 }
 
 // ---------------------------------------------------------------------------
+// Router for 2..8 tokens from the row-major router copy.  Workgroups e < E
+// (512 threads) hold expert e's row in registers (thread l: float4 columns
+// l, l + 512, ...) and form its logits for all tokens at once (every
+// token's loads in flight together, the 8 wavefronts' sums added in
+// wavefront order), stored whole (part_logits: no partials, no per-block
+// sums).  Workgroups E, E + 1, ... stage x meanwhile: slice u = (token, 8
+// spans of 64), wavefront w taking span 8 q' + w, the slice's sum and sum of
+// squares into tpart as two of the tail's 4-span slices (added there in
+// order).  The last workgroup to arrive runs router_tail (its first 256
+// threads), as the split-K router's does.
+// ---------------------------------------------------------------------------
+
+constexpr int R8_THREADS = 512;
+
+template <int NT, int Q>  // Q float4 loads per thread per row (H <= 2048 Q)
+__global__ void __launch_bounds__(R8_THREADS) k_router8(Fwd f)
+{
+    constexpr int RW = R8_THREADS / 64;
+    __shared__ float s_red[RW][NT];
+    __shared__ float s_st[RW][2];
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int e = blockIdx.x, H = f.H, H4 = H / 4, T = f.T, E = f.E, Epad = f.Epad;
+    float bias_e = 0.f;
+    int slot_e = -1;
+    if (tid < E) {
+        bias_e = f.bias[tid];
+        slot_e = f.tbl[tid];
+    }
+    if (e < E) {
+        const float4* wr = (const float4*)(f.wr_rows + (size_t)e * H);
+        float4 wv[Q], xv[NT][Q];
+#pragma unroll
+        for (int k = 0; k < Q; ++k) {
+            const int c = tid + R8_THREADS * k;
+            wv[k] = c < H4 ? wr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            const float4* xr = (const float4*)(f.x + (size_t)min(j, T - 1) * H);
+#pragma unroll
+            for (int k = 0; k < Q; ++k) xv[j][k] = xr[min(tid + R8_THREADS * k, H4 - 1)];
+        }
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            float a = 0.f;
+#pragma unroll
+            for (int k = 0; k < Q; ++k)
+                if (tid + R8_THREADS * k < H4) {
+                    a = fmaf(wv[k].x, xv[j][k].x, a);
+                    a = fmaf(wv[k].y, xv[j][k].y, a);
+                    a = fmaf(wv[k].z, xv[j][k].z, a);
+                    a = fmaf(wv[k].w, xv[j][k].w, a);
+                }
+            a = wave_sum(a);
+            if (lane == 0) s_red[w][j] = a;
+        }
+        __syncthreads();
+        if (tid < T) {
+            float l = 0.f;
+#pragma unroll
+            for (int v = 0; v < RW; ++v) l += s_red[v][tid];
+            st_agent(&part_logits(f)[(size_t)tid * Epad + e], l);
+        }
+    } else {
+        // x staged as fp16 spans; per slice of 8 spans the sums of spans
+        // 8 q' .. 8 q' + 3 and 8 q' + 4 .. 8 q' + 7 (the tail's 4-span slices
+        // 2 q' and 2 q' + 1)
+        const int S = f.S, S2p = router_s2p(S), S8 = S / 2;
+        for (int u = e - E; u < T * S8; u += gridDim.x - E) {
+            const int t = u / S8, q = u - t * S8, sp = 8 * q + w;
+            const float xv = f.x[(size_t)t * H + sp * 64 + lane];
+            const float gs = wave_sum(xv), ss = wave_sum(xv * xv);
+            stage_span64(xv, lane, (uint16_t*)(f.xq + (size_t)t * (H / 8) + sp * 8),
+                         f.xsc + (size_t)t * (H / 64) + sp);
+            if (lane == 0) {
+                s_st[w][0] = gs;
+                s_st[w][1] = ss;
+            }
+            __syncthreads();
+            if (tid < 4) {
+                const int hh = tid >> 1, c = tid & 1;  // half hh of the slice, sum or squares
+                const float v = (s_st[4 * hh + 0][c] + s_st[4 * hh + 1][c]) +
+                                (s_st[4 * hh + 2][c] + s_st[4 * hh + 3][c]);
+                st_agent(&f.tpart[(size_t)t * S2p + 2 * (2 * q + hh) + c], v);
+            }
+            __syncthreads();
+        }
+    }
+    if (!arrive_block(&f.counters[0], gridDim.x)) return;
+    if (tid >= RT_THREADS) return;  // the tail is written for RT_THREADS threads
+    router_tail<NT>(f, bias_e, slot_e);
+}
+
+// ---------------------------------------------------------------------------
 // One-token router, logits only: workgroup e computes expert e's whole raw
 // logit x . Wr[e] from the row-major copy of the router weights (4
 // wavefronts, each a quarter of the H inputs, all loads in flight at once,
@@ -706,8 +800,24 @@ hipError_t launch_router1(const Fwd& f, hipStream_t st)
 
 int router_small_slices(int H) { return (H / 64) / (RT_THREADS / 64); }
 
+template <int NT>
+static hipError_t router8_go(const Fwd& f, hipStream_t st)
+{
+    // experts, then staging workgroups: a slice of 8 spans each, up to 256
+    const int stage = std::min(f.T * (f.S / 2), 256);
+    const dim3 grid((unsigned)(f.E + stage)), block(R8_THREADS);
+    switch ((f.H + 2047) / 2048) {
+    case 1: return launch_k(k_router8<NT, 1>, grid, block, 0, st, f);
+    case 2: return launch_k(k_router8<NT, 2>, grid, block, 0, st, f);
+    case 3: return launch_k(k_router8<NT, 3>, grid, block, 0, st, f);
+    default: return launch_k(k_router8<NT, 4>, grid, block, 0, st, f);
+    }
+}
+
 hipError_t launch_router_small(const Fwd& f, hipStream_t st)
 {
+    if (f.T >= 2 && f.wr_rows != nullptr && f.H <= 8192 && f.H % 512 == 0)  // the row router
+        return f.T <= 2 ? router8_go<2>(f, st) : f.T <= 4 ? router8_go<4>(f, st) : router8_go<8>(f, st);
     const dim3 grid(f.Epad / 64, router_small_slices(f.H)), block(RT_THREADS);
     if (f.T <= 1) return launch_k(k_router_small<1>, grid, block, 0, st, f, f.x);
     if (f.T <= 2) return launch_k(k_router_small<2>, grid, block, 0, st, f, f.x);

@@ -169,6 +169,7 @@ Fwd make_fwd(moe_ctx* c, const float* x, float* out, int T, int layer, int resid
     f.out = out;
     f.T = T;
     f.rslices = router_t_ok(T, g.hidden, c->wr_rows) ? 1 : router_slices(T, g.hidden);
+    f.magic = 0x64006400u;
     f.H = g.hidden;
     f.I = g.inter;
     f.E = g.n_experts;

@@ -94,6 +94,7 @@ struct Fwd {
     // grouped-GEMM path (many tokens): x and h staged per row in xq / hq
     int row_staging;      // 1: stage x per row (grouped GEMM), 0: in spans of 64 (GEMVs)
     int rslices;          // H slices (partial logit planes) of the large-T router
+    uint32_t magic;       // 0x64006400 (fp16 pair 1024, 1024), opaque to the compiler
     float2* xrow;         // [T] per token (2^-k, sum of its fp16 values)
     float2* hrow;         // [rows]
     float* hbuf;          // [rows][I] h in fp32 (gate/up GEMM output)
