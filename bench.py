@@ -389,6 +389,38 @@ def bench_staged(torch, result, n_layers: int = 8, per_layer: int = 16, n_tokens
     torch.cuda.empty_cache()
 
 
+def bench_batch(torch, name, steps, result):
+    """A batch of a few tokens per forward (fresh tokens for each of the
+    resident layers, taken in turn), graph-replayed: per-layer time and the
+    HBM rate over the distinct experts the layers read."""
+    import numpy as np
+    import synth
+    from int4_weight_expert_amd import workload
+    cfg = synth.CONFIGS[name]
+    log(f"[bench] building {name}: {cfg.n_layers} layers x {cfg.E} experts, T={cfg.T}")
+    ml = workload.build_layer(cfg, max_tokens=cfg.T)
+    L = cfg.n_layers
+    xs = [workload.tokens_device(cfg, T=cfg.T, stream=l) for l in range(L)]
+    outs = [torch.empty_like(x) for x in xs]
+    distinct = [len(np.unique(ml.route(xs[l], l)[0].cpu().numpy())) for l in range(L)]
+    fns = [(lambda l=l: ml.forward(xs[l], l, outs[l])) for l in range(L)]
+    for fn in fns:
+        fn()
+    g, t, pct = time_graph(torch, ml, fns, steps, 8)
+    bytes_layer = float(np.mean([glm_bytes(cfg, u, cfg.T) for u in distinct]))
+    result["extra"][name] = {
+        "T": cfg.T, "layers": L, "us_per_layer": t * 1e6, "graph_replay_percentiles": pct,
+        "tokens_per_s": cfg.T / t, "distinct_experts_per_layer": distinct,
+        "layer_algorithmic_bytes_mean": bytes_layer, "layer_gbps": bytes_layer / t / 1e9,
+        "layer_frac_hbm_peak": bytes_layer / t / 1e9 / HBM_PEAK_GBS,
+    }
+    log(f"[bench] {name}: {t * 1e6:.1f} us/layer, {bytes_layer / t / 1e9:.0f} GB/s over "
+        f"{np.mean(distinct):.0f} distinct experts")
+    ml.close()
+    del ml, xs, outs
+    torch.cuda.empty_cache()
+
+
 def bench_chain(torch, name, steps, result):
     """Chained residual layers (x <- x + moe(rmsnorm(x))): per-layer time."""
     import numpy as np
@@ -545,12 +577,36 @@ def stream_ceiling(torch, result, unit_bytes: int):
                          "nontemporal": bool(nt), "gbps": gbs, "median_ms": ms})
     best = max(rows, key=lambda r: r["gbps"])
     gbs_all, ms_all = run(total, best["blocks"], int(best["nontemporal"]), n=8, rotate=False)
+    # the one-token gate/up kernel's access pattern against contiguous reads,
+    # same workgroups and bytes (9 GLM experts' gate and up codes), rotated
+    # over 12 disjoint sets of 9 slots
+    lib.hbm_probe_pattern.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]
+    lib.hbm_probe_pattern.restype = ctypes.c_int
+    exp_bytes, n_exp = 18915328, 9
+    pat = {}
+    for pattern, name in ((0, "gateup_pattern"), (1, "contiguous")):
+        evs = []
+        for i in range(48):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            rc = lib.hbm_probe_pattern(buf.data_ptr() + (i % 12) * n_exp * exp_bytes, exp_bytes,
+                                       n_exp, pattern, sink.data_ptr(), 0xDEADBEEF, st.cuda_stream)
+            b.record(st)
+            if rc != 0:
+                raise RuntimeError(f"hbm_probe_pattern: hip error {rc}")
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+        pat[name] = {"gbps": n_exp * 256 * 49152 / (ms * 1e-3) / 1e9, "median_ms": ms}
     out = {"unit_reads": rows, "best_unit_gbps": best["gbps"],
            "whole_2gib_gbps": gbs_all, "whole_2gib_ms": ms_all,
-           "ceiling_gbps": max(best["gbps"], gbs_all)}
+           "ceiling_gbps": max(best["gbps"], gbs_all), "access_pattern": pat}
     result["extra"]["hbm_stream_probe"] = out
     log(f"[bench] streaming-read ceiling: {best['gbps']:.0f} GB/s for {unit} B reads "
-        f"({best['blocks']} blocks, nt={best['nontemporal']}), {gbs_all:.0f} GB/s whole 2 GiB")
+        f"({best['blocks']} blocks, nt={best['nontemporal']}), {gbs_all:.0f} GB/s whole 2 GiB; "
+        f"gate/up access pattern {pat['gateup_pattern']['gbps']:.0f} GB/s, contiguous "
+        f"{pat['contiguous']['gbps']:.0f} GB/s")
     del buf, sink
     torch.cuda.empty_cache()
     return out["ceiling_gbps"]
@@ -703,7 +759,7 @@ def main():
     ap.add_argument("--no-probe", action="store_true", help="skip the streaming-read ceiling")
     ap.add_argument("--only", choices=["decode", "verify", "edge0", "edge0_k8", "prefill", "grouped",
                                        "softmax", "int8_shared", "requant", "staged",
-                                       "prefill_int8_shared"],
+                                       "prefill_int8_shared", "batch"],
                     help="run one workload only (for profiling); the JSON line then "
                          "carries that workload in extra")
     ap.add_argument("--copy-probe", action="store_true",
@@ -742,6 +798,8 @@ def main():
          "grouped": lambda: bench_rotated(torch, "glm_decode_grouped", 200, result),
          "softmax": lambda: bench_rotated(torch, "glm_decode_softmax", 200, result),
          "int8_shared": lambda: bench_rotated(torch, "glm_decode_int8_shared", 200, result),
+         "batch": lambda: (bench_batch(torch, "glm_batch16", 64, result),
+                           bench_batch(torch, "glm_batch32", 64, result)),
          "requant": lambda: bench_requant(torch, result),
          "staged": lambda: bench_staged(torch, result)}[args.only]()
         print(json.dumps(result), flush=True)
@@ -763,6 +821,8 @@ def main():
         bench_rotated(torch, "glm_decode_grouped", 200, result)
         bench_rotated(torch, "glm_decode_softmax", 200, result)
         bench_rotated(torch, "glm_decode_int8_shared", 200, result)
+        bench_batch(torch, "glm_batch16", 64, result)
+        bench_batch(torch, "glm_batch32", 64, result)
         bench_requant(torch, result)
         bench_staged(torch, result)
         bench_prefill(torch, 20, result)

@@ -1,7 +1,8 @@
 // hbm_probe.hip -- a plain streaming-read kernel that measures the HBM read
 // rate this part reaches, the ceiling the byte-bound MoE kernels are held
-// against.  Not part of the MoE path: a separate library (libhbm_probe.so)
-// that only the benchmark loads.
+// against, and a read of the one-token gate/up kernel's bytes in its own
+// access pattern beside a contiguous one.  Not part of the MoE path: a
+// separate library (libhbm_probe.so) that only the benchmark loads.
 //
 // Each thread reads 16-byte pieces with a grid stride, eight loads in
 // flight, and folds them into one word so that the loads cannot be removed;
@@ -42,6 +43,46 @@ __global__ void __launch_bounds__(kThreads) k_stream_read(const u32x4* __restric
     if (acc == never) sink[blockIdx.x] = acc;
 }
 
+// The one-token gate/up launch's bytes read in two access patterns by the
+// same workgroups (n_exp x 256 of 256 threads, 48 KB each as 12 16-byte
+// loads per lane, all in flight at once), with the GLM expert shape (gate and
+// up [2048][6144] int4 in the slot layout: 64-row blocks of 1 KiB chunks):
+// PATTERN 0 as that kernel reads them (a workgroup owns 8 rows: their 16-byte
+// pieces of every chunk, 128 bytes out of each 1 KiB, the other rows read by
+// other workgroups), PATTERN 1 each workgroup's 48 KB contiguous.
+constexpr int kPH = 6144, kPI = 2048, kPC = kPH / 32;
+
+template <int PATTERN>
+__global__ void __launch_bounds__(kThreads) k_pattern_read(const uint8_t* __restrict__ buf,
+                                                           size_t exp_bytes, uint32_t* __restrict__ sink,
+                                                           uint32_t never)
+{
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int sb = blockIdx.x % (kPI / 8), gi = blockIdx.x / (kPI / 8);
+    const uint8_t* base = buf + (size_t)gi * exp_bytes;
+    u32x4 v[12];
+    if (PATTERN == 0) {
+        const int b = sb >> 3, s8 = sb & 7, rr = lane & 7, j = lane >> 3, c0 = w * 48;
+        const size_t off = (size_t)(s8 * 8 + rr) * 16 + (size_t)(2 * j) * 1024;
+#pragma unroll
+        for (int st = 0; st < 3; ++st)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const size_t so = (size_t)(c0 + st * 16 + h) * 1024;
+                v[2 * st + h] = *(const u32x4*)(base + (size_t)b * kPC * 1024 + off + so);
+                v[6 + 2 * st + h] = *(const u32x4*)(base + (size_t)kPI * kPH / 2 + (size_t)b * kPC * 1024 + off + so);
+            }
+    } else {
+        const uint8_t* p = base + (size_t)sb * 49152 + (size_t)w * 12288;
+#pragma unroll
+        for (int i = 0; i < 12; ++i) v[i] = *(const u32x4*)(p + (size_t)i * 1024 + lane * 16);
+    }
+    uint32_t acc = 0;
+#pragma unroll
+    for (int i = 0; i < 12; ++i) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+    if (acc == never) sink[blockIdx.x] = acc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -60,6 +101,24 @@ int hbm_probe_read(const void* buf, size_t bytes, int blocks, int nt, uint32_t* 
     else
         hipLaunchKernelGGL(k_stream_read<false>, dim3(blocks), dim3(kThreads), 0,
                            (hipStream_t)stream, (const u32x4*)buf, bytes / 16, sink, never);
+    return (int)hipGetLastError();
+}
+
+// Reads n_exp GLM-shape experts' gate and up codes (exp_bytes apart from buf,
+// at least 12.6 MB each) in `pattern` 0 (the one-token gate/up kernel's) or
+// 1 (contiguous per workgroup); sink needs n_exp x 256 words.  Returns a
+// hipError_t value (0 = success).
+int hbm_probe_pattern(const void* buf, size_t exp_bytes, int n_exp, int pattern, uint32_t* sink,
+                      uint32_t never, void* stream)
+{
+    if (!buf || !sink || n_exp <= 0 || exp_bytes < (size_t)kPI * kPH) return (int)hipErrorInvalidValue;
+    const dim3 grid((unsigned)(n_exp * (kPI / 8))), block(kThreads);
+    if (pattern == 0)
+        hipLaunchKernelGGL(k_pattern_read<0>, grid, block, 0, (hipStream_t)stream, (const uint8_t*)buf,
+                           exp_bytes, sink, never);
+    else
+        hipLaunchKernelGGL(k_pattern_read<1>, grid, block, 0, (hipStream_t)stream, (const uint8_t*)buf,
+                           exp_bytes, sink, never);
     return (int)hipGetLastError();
 }
 

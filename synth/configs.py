@@ -101,3 +101,6 @@ CONFIGS["glm_decode_softmax"] = CONFIGS["glm_decode"].with_(name="glm_decode_sof
 # GLM-5.2 shape prefill with the shared expert in per-row int8
 CONFIGS["glm_prefill_int8_shared"] = CONFIGS["glm_prefill"].with_(name="glm_prefill_int8_shared",
                                                                   shared_fmt=3, seed=303)
+# GLM-5.2 shape batches of a few tokens (fresh tokens per layer), 4 layers rotated
+CONFIGS["glm_batch16"] = CONFIGS["glm_decode"].with_(name="glm_batch16", T=16, n_layers=4, seed=610)
+CONFIGS["glm_batch32"] = CONFIGS["glm_decode"].with_(name="glm_batch32", T=32, n_layers=4, seed=611)
