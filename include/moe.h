@@ -63,6 +63,9 @@ typedef struct moe_ctx moe_ctx;
 #define MOE_E_RANGE (-8)        /* an input row was not finite (moe_status) */
 #define MOE_E_BUSY (-9)         /* slot still named by the slot table (asynchronous loads) */
 
+/* slot-table value of an expert held by another GPU (see moe_map_expert) */
+#define MOE_SLOT_REMOTE (-2)
+
 /* expert weight formats (layout of an expert blob, see moe_load_expert) */
 #define MOE_W_INT4_ROW 1        /* symmetric int4, one fp32 scale per output row */
 #define MOE_W_INT4_AFFINE_G64 2 /* affine int4, bf16 scale and min per 64 inputs */
@@ -211,7 +214,11 @@ int moe_import_shared(moe_ctx *ctx, int layer, int s, const uint8_t *qg, const u
 
 /* Points (layer, expert_id) at a slot, or unmaps it with slot = -1
  * ([COLI] §2.2 ESlot, [EDGE0] §十四 slot table).  Several layers or ids may
- * share a slot.  Errors: MOE_E_ARG, MOE_E_SLOT. */
+ * share a slot.  slot = MOE_SLOT_REMOTE marks an expert that lives on
+ * another GPU (expert parallelism): a token that selects it gets no
+ * contribution from it here and no status is raised (its partial sum comes
+ * from the GPU that holds it), where an unmapped (-1) expert is skipped and
+ * reported as MOE_E_NOT_RESIDENT.  Errors: MOE_E_ARG, MOE_E_SLOT. */
 int moe_map_expert(moe_ctx *ctx, int layer, int expert_id, int slot);
 
 /* --- residency: asynchronous loads, staged (sticky) slots, whole layers ---
@@ -235,7 +242,8 @@ int moe_map_expert(moe_ctx *ctx, int layer, int expert_id, int slot);
  * follows the map). */
 
 /* Table updates, in stream order on the context's stream, without a sync:
- * (layer, expert_ids[i]) -> slots[i] (-1 unmaps).  Later entries for the
+ * (layer, expert_ids[i]) -> slots[i] (-1 unmaps, MOE_SLOT_REMOTE marks an
+ * expert held by another GPU).  Later entries for the
  * same id win.  Errors: MOE_E_ARG, MOE_E_SLOT, MOE_E_HIP. */
 int moe_map_experts_async(moe_ctx *ctx, int layer, int n, const int *expert_ids,
                           const int *slots);

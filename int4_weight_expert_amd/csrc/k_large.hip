@@ -512,7 +512,7 @@ __global__ void __launch_bounds__(1024) k_bucket(const int32_t* __restrict__ ids
         g.kind = 0;
         g.expert = tid;
         f.groups[f.n_shared + s_act[tid]] = g;
-        if (slot < 0) {
+        if (slot == -1) {  // missing (a remote expert, -2, is skipped quietly)
             atomicOr(&f.status[0], (uint32_t)STATUS_NOT_RESIDENT);
             const int code = f.layer * E + tid;
             atomicOr(&f.status[1 + code / 32], 1u << (code % 32));

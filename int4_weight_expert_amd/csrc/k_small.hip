@@ -426,7 +426,7 @@ __device__ void router_tail(const Fwd& f, float bias_e, int slot_e)
             g.kind = 0;
             g.expert = tid;
             f.groups[f.n_shared + idx_e] = g;
-            if (slot_e < 0) {
+            if (slot_e == -1) {  // missing (a remote expert, -2, is skipped quietly)
                 atomicOr(&f.status[0], (uint32_t)STATUS_NOT_RESIDENT);
                 const int code = f.layer * E + tid;
                 atomicOr(&f.status[1 + code / 32], 1u << (code % 32));

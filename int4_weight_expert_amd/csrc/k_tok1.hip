@@ -244,7 +244,7 @@ __global__ void __launch_bounds__(64 * W) k_gu8(Fwd f)
                     f.groups[ns + kk] = g;
                     __hip_atomic_store(&f.sel_base[kk], (uint64_t)(uintptr_t)bk | 1ull, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
-                    if (sk < 0) {
+                    if (sk == -1) {  // missing (a remote expert, -2, is skipped quietly)
                         atomicOr(&f.status[0], (uint32_t)STATUS_NOT_RESIDENT);
                         const int code = f.layer * f.E + ek;
                         atomicOr(&f.status[1 + code / 32], 1u << (code % 32));

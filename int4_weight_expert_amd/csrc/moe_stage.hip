@@ -286,7 +286,7 @@ int moe_map_expert(moe_ctx* c, int layer, int expert_id, int slot)
     if (!c || layer < 0 || layer >= c->cfg.n_layers || expert_id < 0 ||
         expert_id >= c->cfg.n_experts)
         return MOE_E_ARG;
-    if (slot < -1 || slot >= c->cfg.n_slots) return MOE_E_SLOT;
+    if (slot < MOE_SLOT_REMOTE || slot >= c->cfg.n_slots) return MOE_E_SLOT;
     const int rc = apply_updates(c, {{layer * c->cfg.n_experts + expert_id, slot}});
     if (rc) return rc;
     return hip_rc(c, hipStreamSynchronize(c->stream));
@@ -299,7 +299,7 @@ int moe_map_experts_async(moe_ctx* c, int layer, int n, const int* expert_ids, c
     std::vector<std::pair<int, int>> ups;
     for (int i = 0; i < n; ++i) {
         if (expert_ids[i] < 0 || expert_ids[i] >= c->cfg.n_experts) return MOE_E_ARG;
-        if (slots[i] < -1 || slots[i] >= c->cfg.n_slots) return MOE_E_SLOT;
+        if (slots[i] < MOE_SLOT_REMOTE || slots[i] >= c->cfg.n_slots) return MOE_E_SLOT;
         ups.push_back({layer * c->cfg.n_experts + expert_ids[i], slots[i]});
     }
     return apply_updates(c, ups);

@@ -23,6 +23,7 @@ MOE_E_HIP = -6
 MOE_E_UNSUPPORTED = -7
 MOE_E_RANGE = -8
 MOE_E_BUSY = -9
+MOE_SLOT_REMOTE = -2
 MOE_W_INT4_ROW = 1
 MOE_SCORE_SIGMOID, MOE_SCORE_SOFTMAX = 0, 1
 MOE_W_INT4_AFFINE_G64 = 2
