@@ -29,12 +29,13 @@
 // N tiles let one staged activation tile feed many output columns: the
 // activations (2 bytes per input) are the larger share of operand traffic.  Each
 // wavefront covers the 128 rows as four 32-row blocks: 8 accumulator tiles.
-// Per K step of 32 inputs (one 16-byte chunk of codes per output row): the
-// activation tile (128 x 32 fp16) is double-buffered in LDS, piece-major so
-// the A-operand reads are conflict-free; every wavefront loads its own codes
-// straight into registers (8 bytes per lane: lanes l and l+32 read the two
-// halves of a row's chunk, each half feeding one MFMA per step).
-// Activations and codes are fetched GDEP steps ahead.
+// Per K step of 64 inputs (two 16-byte chunks of int4 codes per output row):
+// the activation tile (128 x 64 fp16) is double-buffered in LDS, piece-major
+// so the A-operand reads are conflict-free; every wavefront loads its own
+// codes straight into registers with one 16-byte load per lane (lanes l and
+// l+32 read the step's two chunks of a row, each feeding four MFMAs).
+// Activations and codes are fetched 4 steps ahead.  (Per-row int8 codes, a
+// shared expert: 32-input steps of two 16-byte chunks.)
 #include <type_traits>
 
 #include "k_common.h"
@@ -111,9 +112,11 @@ __device__ __forceinline__ half8 b_operand8(uint32_t lo, uint32_t hi)
 // The tile's prologue, K loop and epilogue, specialised on the number MB of
 // 32-row blocks that hold rows of the group: a partial tile issues only its
 // blocks' LDS reads and MFMAs.  Each specialisation is self-contained, so no
-// register array lives across the dispatch.
-template <int MODE, int MB, bool S8>
-__device__ __forceinline__ void gemm_tile(const Fwd& f, uint4 (*As)[4][GM], const int* s_src,
+// register array lives across the dispatch.  This one: per-row int8 codes
+// (a shared expert), K step of 32 inputs = two 16-byte chunks, lane half h
+// loading chunk 2 step + h whole.
+template <int MODE, int MB>
+__device__ __forceinline__ void gemm_tile8(const Fwd& f, uint4 (*As)[8][GM], const int* s_src,
                                           const int* s_out, const float* s_inv,
                                           const float* s_sum, const float* s_rs,
                                           const uint8_t* base, int ntile, int rows)
@@ -125,25 +128,23 @@ __device__ __forceinline__ void gemm_tile(const Fwd& f, uint4 (*As)[4][GM], cons
     const int NC = K / 32;                  // K steps (chunks)
     int o0, o1;
     size_t mat0, mat1;
-    gemm_out_rows<MODE, S8>(ntile, w, n, H, I, o0, o1, mat0, mat1);
+    gemm_out_rows<MODE, true>(ntile, w, n, H, I, o0, o1, mat0, mat1);
     // fp32 row scales after the three matrices
-    const uint8_t* tab = base + (S8 ? (size_t)3 * H * I : (size_t)3 * H * I / 2);
+    const uint8_t* tab = base + (size_t)3 * H * I;
 
-    const uint32_t mv = f.magic;
     // weight streams: the wavefront's rows lie in one 64-row block (a
     // wave-uniform resource); the lane's row within it is the offset.  A
-    // 16-byte chunk holds 32 int4 codes or 16 int8 codes: a K step of 32
-    // inputs is one int4 chunk (lane half h reads its bytes 8h..8h+7) or two
-    // int8 chunks (lane half h reads chunk 2 step + h whole).
-    const int C = S8 ? 2 * NC : NC;  // chunks per weight row
+    // 16-byte chunk holds 16 int8 codes: a K step of 32 inputs is two chunks
+    // (lane half h reads chunk 2 step + h whole).
+    const int C = 2 * NC;  // chunks per weight row
     const int blk = MODE == GEMM_GU ? ntile * 4 + (w >> 1) : ntile * 8 + w;
     const __amdgpu_buffer_rsrc_t rw0 =
         make_rsrc(base + mat0 + (size_t)blk * C * 1024, (uint32_t)C * 1024);
     const __amdgpu_buffer_rsrc_t rw1 =
         make_rsrc(base + mat1 + (size_t)blk * C * 1024, (uint32_t)C * 1024);
-    const uint32_t v0 = S8 ? (uint32_t)(o0 & 63) * 16 + half * 1024 : (uint32_t)(o0 & 63) * 16 + half * 8;
-    const uint32_t v1 = S8 ? (uint32_t)(o1 & 63) * 16 + half * 1024 : (uint32_t)(o1 & 63) * 16 + half * 8;
-    constexpr uint32_t STEP = S8 ? 2048 : 1024;  // code bytes per K step and 64-row block
+    const uint32_t v0 = (uint32_t)(o0 & 63) * 16 + half * 1024;
+    const uint32_t v1 = (uint32_t)(o1 & 63) * 16 + half * 1024;
+    constexpr uint32_t STEP = 2048;  // code bytes per K step and 64-row block
 
     // activation loader: thread -> row tid & 127, piece tid >> 7 (a
     // wavefront writes 64 consecutive rows of one piece: no bank conflict)
@@ -175,19 +176,12 @@ __device__ __forceinline__ void gemm_tile(const Fwd& f, uint4 (*As)[4][GM], cons
         A0[k] = z4;
         if (Ag) A0[k] = Ag[k * 4];
     }
-    // codes: int4 8 bytes per lane and step, int8 16 bytes (GDEP steps
-    // either way)
-    typedef typename std::conditional<S8, uint4, uint2>::type BT;
-    BT B0[GDEP], B1[GDEP];
+    // codes: 16 bytes per lane and step, GDEP steps in flight
+    uint4 B0[GDEP], B1[GDEP];
 #pragma unroll
     for (int k = 0; k < GDEP; ++k) {
-        if constexpr (S8) {
-            B0[k] = bload16(rw0, v0 + k * STEP, 0);
-            B1[k] = bload16(rw1, v1 + k * STEP, 0);
-        } else {
-            B0[k] = bload8(rw0, v0 + k * STEP, 0);
-            B1[k] = bload8(rw1, v1 + k * STEP, 0);
-        }
+        B0[k] = bload16(rw0, v0 + k * STEP, 0);
+        B1[k] = bload16(rw1, v1 + k * STEP, 0);
     }
     __syncthreads();
 
@@ -204,26 +198,14 @@ __device__ __forceinline__ void gemm_tile(const Fwd& f, uint4 (*As)[4][GM], cons
             if (Ag && c + GDEP < NC) A0[k] = Ag[(c + GDEP) * 4];
             // codes of step c; refill the slot with step c + GDEP (a load
             // past the row's last chunk returns zeros)
-            const BT w0 = B0[k], w1 = B1[k];
-            // the K order inside a chunk is free as long as A and B agree:
+            const uint4 w0 = B0[k], w1 = B1[k];
+            // the K order inside a step is free as long as A and B agree:
             // lane half h takes inputs 16h..16h+7 in the first MFMA and
             // 16h+8..16h+15 in the second (LDS pieces 2h, 2h+1)
-            half8 b00, b01, b10, b11;
-            if constexpr (S8) {
-                B0[k] = bload16(rw0, v0 + (c + GDEP) * STEP, 0);
-                B1[k] = bload16(rw1, v1 + (c + GDEP) * STEP, 0);
-                b00 = b_operand8(w0.x, w0.y);
-                b01 = b_operand8(w0.z, w0.w);
-                b10 = b_operand8(w1.x, w1.y);
-                b11 = b_operand8(w1.z, w1.w);
-            } else {
-                B0[k] = bload8(rw0, v0 + (c + GDEP) * STEP, 0);
-                B1[k] = bload8(rw1, v1 + (c + GDEP) * STEP, 0);
-                b00 = b_operand(w0.x, mv);
-                b01 = b_operand(w0.y, mv);
-                b10 = b_operand(w1.x, mv);
-                b11 = b_operand(w1.y, mv);
-            }
+            B0[k] = bload16(rw0, v0 + (c + GDEP) * STEP, 0);
+            B1[k] = bload16(rw1, v1 + (c + GDEP) * STEP, 0);
+            const half8 b00 = b_operand8(w0.x, w0.y), b01 = b_operand8(w0.z, w0.w);
+            const half8 b10 = b_operand8(w1.x, w1.y), b11 = b_operand8(w1.z, w1.w);
             const uint4(*Ab)[GM] = As[c & 1];
             half8 a0[4], a1[4];
 #pragma unroll
@@ -248,9 +230,8 @@ __device__ __forceinline__ void gemm_tile(const Fwd& f, uint4 (*As)[4][GM], cons
     }
 
     // epilogue: lane holds column o of each block, rows (j/4)*8 + half*4 + j%4;
-    // int4 (stored c + 8, 1024 + 16 n): sum c x = acc/16 - 72 S; int8
-    // (stored q + 128, 1024 + n): sum q x = acc - 1152 S
-    constexpr float CA = S8 ? 1.0f : 0.0625f, CB = S8 ? -1152.f : -72.f;
+    // int8 (stored q + 128, 1024 + n): sum q x = acc - 1152 S
+    constexpr float CA = 1.0f, CB = -1152.f;
     if (MODE == GEMM_GU) {
         const float sg = ((const float*)tab)[o0], su = ((const float*)tab)[I + o0];
 #pragma unroll
@@ -282,10 +263,153 @@ __device__ __forceinline__ void gemm_tile(const Fwd& f, uint4 (*As)[4][GM], cons
     }
 }
 
+// int4 codes with a K step of 64 inputs: lane half h loads chunk 2s + h of
+// its row whole (one 16-byte load), and dword d of it (inputs 8d..8d+7 of
+// the chunk, pair order) meets LDS piece 4h + d in MFMA round d; the
+// activation tile of a step is 128 rows x 64 fp16 (8 pieces), double
+// buffered, so a step has 4 rounds of MFMAs behind one barrier.
+template <int MODE, int MB>
+__device__ __forceinline__ void gemm_tile64(const Fwd& f, uint4 (*As)[8][GM], const int* s_src,
+                                            const int* s_out, const float* s_inv,
+                                            const float* s_sum, const float* s_rs,
+                                            const uint8_t* base, int ntile, int rows)
+{
+    constexpr int D = GDEP / 2;  // K steps in flight (the same bytes as GDEP 32-input steps)
+    const int tid = threadIdx.x, lane = tid & 63, w = uni(tid >> 6);
+    const int n = lane & 31, half = lane >> 5;
+    const int H = f.H, I = f.I;
+    const int K = MODE == GEMM_GU ? H : I;  // reduction length
+    const int NC = K / 32, NS = K / 64;     // chunks, K steps
+    int o0, o1;
+    size_t mat0, mat1;
+    gemm_out_rows<MODE, false>(ntile, w, n, H, I, o0, o1, mat0, mat1);
+    const uint8_t* tab = base + (size_t)3 * H * I / 2;  // fp32 row scales
+    const uint32_t mv = f.magic;
+    const int blk = MODE == GEMM_GU ? ntile * 4 + (w >> 1) : ntile * 8 + w;
+    const __amdgpu_buffer_rsrc_t rw0 =
+        make_rsrc(base + mat0 + (size_t)blk * NC * 1024, (uint32_t)NC * 1024);
+    const __amdgpu_buffer_rsrc_t rw1 =
+        make_rsrc(base + mat1 + (size_t)blk * NC * 1024, (uint32_t)NC * 1024);
+    const uint32_t v0 = (uint32_t)(o0 & 63) * 16 + half * 1024;
+    const uint32_t v1 = (uint32_t)(o1 & 63) * 16 + half * 1024;
+    constexpr uint32_t STEP = 2048;  // code bytes per K step and 64-row block
+
+    // activation loader: thread -> row tid & 127, pieces p and 4 + p of the
+    // step (p = tid >> 7: piece p of each of the step's two chunks)
+    const int arow = tid & (GM - 1), apc = tid >> 7;
+    const int asrc = s_src[arow];
+    const uint4* Ag = nullptr;
+    if (asrc >= 0)
+        Ag = (MODE == GEMM_GU ? f.xq + (size_t)asrc * (H / 8) : f.hq + (size_t)asrc * (I / 8)) +
+             apc;
+    const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+
+    float16 acc[4][2];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        acc[mb][0] = (float16){};
+        acc[mb][1] = (float16){};
+    }
+
+    uint4 A0[D], A1[D];  // step j's two chunks in slot j % D
+    A0[0] = A1[0] = z4;
+    if (Ag) {
+        A0[0] = Ag[0];
+        A1[0] = Ag[4];
+    }
+    As[0][apc][arow] = A0[0];
+    As[0][4 + apc][arow] = A1[0];
+#pragma unroll
+    for (int k = 1; k < D; ++k) {
+        A0[k] = A1[k] = z4;
+        if (Ag) {
+            A0[k] = Ag[k * 8];
+            A1[k] = Ag[k * 8 + 4];
+        }
+    }
+    uint4 B0[D], B1[D];
+#pragma unroll
+    for (int k = 0; k < D; ++k) {
+        B0[k] = bload16(rw0, v0 + k * STEP, 0);
+        B1[k] = bload16(rw1, v1 + k * STEP, 0);
+    }
+    __syncthreads();
+
+#pragma unroll 1
+    for (int s0 = 0; s0 < NS; s0 += D) {
+#pragma unroll
+        for (int k = 0; k < D; ++k) {
+            const int s = s0 + k;
+            // step s + 1 (slot (s + 1) % D) into the other LDS buffer; slot
+            // s % D (step s, already in LDS) fetches step s + D
+            const int s1 = (k + 1) % D;
+            if (s + 1 < NS) {
+                As[(s + 1) & 1][apc][arow] = A0[s1];
+                As[(s + 1) & 1][4 + apc][arow] = A1[s1];
+            }
+            if (Ag && s + D < NS) {
+                A0[k] = Ag[(s + D) * 8];
+                A1[k] = Ag[(s + D) * 8 + 4];
+            }
+            // codes of step s; refill with step s + D (past the row's last
+            // chunk the loads return zeros)
+            const uint4 w0 = B0[k], w1 = B1[k];
+            B0[k] = bload16(rw0, v0 + (s + D) * STEP, 0);
+            B1[k] = bload16(rw1, v1 + (s + D) * STEP, 0);
+            const uint4(*Ab)[GM] = As[s & 1];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const half8 bd0 = b_operand(d == 0 ? w0.x : d == 1 ? w0.y : d == 2 ? w0.z : w0.w, mv);
+                const half8 bd1 = b_operand(d == 0 ? w1.x : d == 1 ? w1.y : d == 2 ? w1.z : w1.w, mv);
+                half8 a[4];
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) a[mb] = __builtin_bit_cast(half8, Ab[4 * half + d][32 * mb + n]);
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mb], bd0, acc[mb][0], 0, 0, 0);
+                    acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mb], bd1, acc[mb][1], 0, 0, 0);
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // epilogue (int4 stored c + 8, 1024 + 16 n): sum c x = acc/16 - 72 S
+    if (MODE == GEMM_GU) {
+        const float sg = ((const float*)tab)[o0], su = ((const float*)tab)[I + o0];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int i = 32 * mb + (j >> 2) * 8 + half * 4 + (j & 3);
+                if (i < rows) {
+                    const float sc = s_inv[i] * s_rs[i];
+                    const float g = fmaf(acc[mb][0][j], 0.0625f, -72.f * s_sum[i]) * sc * sg;
+                    const float u = fmaf(acc[mb][1][j], 0.0625f, -72.f * s_sum[i]) * sc * su;
+                    f.hbuf[(size_t)s_out[i] * I + o0] = g / (1.0f + expf(-g)) * u;
+                }
+            }
+    } else {
+        const float sd0 = ((const float*)tab)[2 * I + o0], sd1 = ((const float*)tab)[2 * I + o1];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int i = 32 * mb + (j >> 2) * 8 + half * 4 + (j & 3);
+                if (i < rows) {
+                    const float sc = s_inv[i];
+                    float* y = f.ypart + (size_t)s_out[i] * H;
+                    y[o0] = fmaf(acc[mb][0][j], 0.0625f, -72.f * s_sum[i]) * sc * sd0;
+                    y[o1] = fmaf(acc[mb][1][j], 0.0625f, -72.f * s_sum[i]) * sc * sd1;
+                }
+            }
+    }
+}
+
 template <int MODE>
 __global__ void __launch_bounds__(64 * GW, 1) k_gemm(Fwd f)
 {
-    __shared__ uint4 As[2][4][GM];  // [buffer][16-byte piece][row]
+    __shared__ uint4 As[2][8][GM];  // [buffer][16-byte piece][row]
     __shared__ int s_src[GM], s_out[GM];
     __shared__ float s_inv[GM], s_sum[GM], s_rs[GM];
 
@@ -360,18 +484,18 @@ __global__ void __launch_bounds__(64 * GW, 1) k_gemm(Fwd f)
     if (grp.kind == 1 && f.shared_fmt == MOE_W_INT8_ROW) {
         // per-row int8 shared expert (the same tile, int8 B operands)
         switch ((rows + 31) >> 5) {
-        case 1: gemm_tile<MODE, 1, true>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
-        case 2: gemm_tile<MODE, 2, true>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
-        case 3: gemm_tile<MODE, 3, true>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
-        default: gemm_tile<MODE, 4, true>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
+        case 1: gemm_tile8<MODE, 1>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
+        case 2: gemm_tile8<MODE, 2>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
+        case 3: gemm_tile8<MODE, 3>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
+        default: gemm_tile8<MODE, 4>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
         }
         return;
     }
     switch ((rows + 31) >> 5) {
-    case 1: gemm_tile<MODE, 1, false>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
-    case 2: gemm_tile<MODE, 2, false>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
-    case 3: gemm_tile<MODE, 3, false>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
-    default: gemm_tile<MODE, 4, false>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
+    case 1: gemm_tile64<MODE, 1>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
+    case 2: gemm_tile64<MODE, 2>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
+    case 3: gemm_tile64<MODE, 3>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
+    default: gemm_tile64<MODE, 4>(f, As, s_src, s_out, s_inv, s_sum, s_rs, base, ntile, rows); break;
     }
 }
 
