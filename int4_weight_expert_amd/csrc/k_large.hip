@@ -402,97 +402,118 @@ __global__ void __launch_bounds__(256) k_topk(Fwd f)
 }
 
 // Stable counting sort of the T*K assignments by expert (one workgroup of
-// 1024 threads).  Within a 1024-assignment chunk, each wavefront finds the
-// lanes holding the same expert id with 8 ballots over the id's bits; a
-// per-expert running prefix over wavefronts and chunks keeps the order of
-// assignment indices.  If `groups` is set, also builds the forward's expert
-// groups (shared experts first, then active experts ascending) and flags
-// selected experts without a slot.
+// 1024 threads).  Wavefront w owns the w-th of 16 contiguous segments of the
+// assignments and walks it 64 at a time: the lanes holding the same expert
+// id are found with 8 ballots over the id's bits, and the lowest of them
+// keeps the wavefront's running count of that expert in its own LDS row.
+// Pass 1 counts; a prefix over the 16 wavefronts per expert and a scan over
+// the experts give every (wavefront, expert) its first position; pass 2
+// repeats the walk and writes each assignment at its expert's offset plus
+// the number of earlier assignments of that expert, so the order of
+// assignment indices is kept.  If `groups` is set, also builds the forward's
+// expert groups (shared experts first, then active experts ascending) and
+// flags selected experts without a slot.
+__device__ __forceinline__ unsigned long long same_expert(int e, bool valid)
+{
+    unsigned long long same = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+        const bool on = (e >> bit) & 1;
+        const unsigned long long bb = __ballot(on);
+        same &= on ? bb : ~bb;
+    }
+    return same;
+}
+
 __global__ void __launch_bounds__(1024) k_bucket(const int32_t* __restrict__ ids, int n, int E,
                                                  int32_t* cnt, int32_t* off, int32_t* perm,
                                                  int32_t* active, int32_t* n_active, Fwd f,
                                                  int build_groups)
 {
+    constexpr int BU = 8;  // rounds whose ids are loaded together
     __shared__ int s_cnt[256];
     __shared__ int s_off[257];
     __shared__ int s_act[256];
-    __shared__ int s_run[256];
     __shared__ int s_nact;
     __shared__ int wcnt[16][256];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    if (tid < 256) {
-        s_cnt[tid] = 0;
-        s_run[tid] = 0;
-    }
+    for (int i = tid; i < 16 * 256; i += 1024) (&wcnt[0][0])[i] = 0;
     __syncthreads();
-    for (int a = tid; a < n; a += 1024) {
-        const int e = ids[a];
-        if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
-    }
-    __syncthreads();
-    if (w == 0) {
-        int c4[4], a4[4], sc = 0, sa = 0;
+    const int seg = ((n + 15) / 16 + 63) / 64 * 64;  // assignments per wavefront
+    const int a0 = w * seg, a1 = min(n, a0 + seg);
+    const int rounds = a1 > a0 ? (a1 - a0 + 63) / 64 : 0;
+    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int pass = 0; pass < 2; ++pass) {
+        for (int r0 = 0; r0 < rounds; r0 += BU) {
+            int ev[BU];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            c4[m] = s_cnt[lane * 4 + m];
-            a4[m] = c4[m] > 0;
-            sc += c4[m];
-            sa += a4[m];
-        }
-        int ic = sc, ia = sa;
+            for (int u = 0; u < BU; ++u) {
+                const int a = a0 + (r0 + u) * 64 + lane;
+                ev[u] = a < a1 ? ids[a] : -1;
+            }
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int pc = __shfl_up(ic, o), pa = __shfl_up(ia, o);
-            if (lane >= o) {
-                ic += pc;
-                ia += pa;
+            for (int u = 0; u < BU; ++u) {
+                if (r0 + u >= rounds) break;
+                const int a = a0 + (r0 + u) * 64 + lane;
+                int e = ev[u];
+                const bool valid = e >= 0 && e < E;
+                if (!valid) e = 0;
+                const unsigned long long same = same_expert(e, valid);
+                const int rank = __popcll(same & below);
+                // every lane reads the running count before its lowest lane
+                // (rank 0) advances it
+                const int before = wcnt[w][e];
+                if (pass == 1 && valid) perm[s_off[e] + before + rank] = a;
+                if (valid && rank == 0) wcnt[w][e] = before + __popcll(same);
             }
         }
-        int rc = ic - sc, ra = ia - sa;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            s_off[lane * 4 + m] = rc;
-            s_act[lane * 4 + m] = a4[m] ? ra : -1;
-            rc += c4[m];
-            ra += a4[m];
-        }
-        if (lane == 63) {
-            s_off[256] = rc;
-            s_nact = ra;
-        }
-    }
-    __syncthreads();
-    for (int base = 0; base < n; base += 1024) {
-        for (int i = tid; i < 16 * 256; i += 1024) (&wcnt[0][0])[i] = 0;
+        if (pass == 1) break;
         __syncthreads();
-        const int a = base + tid;
-        int e = a < n ? ids[a] : -1;
-        const bool valid = e >= 0 && e < E;
-        if (!valid) e = 0;
-        unsigned long long same = __ballot(valid);
-#pragma unroll
-        for (int bit = 0; bit < 8; ++bit) {
-            const bool on = (e >> bit) & 1;
-            const unsigned long long bb = __ballot(on);
-            same &= on ? bb : ~bb;
-        }
-        const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-        const int rank = __popcll(same & below);
-        if (valid && rank == 0) wcnt[w][e] = __popcll(same);
-        __syncthreads();
+        // per expert: the wavefronts' first positions and the total
         if (tid < 256) {
-            int run = s_run[tid];
+            int run = 0;
             for (int v = 0; v < 16; ++v) {
                 const int c = wcnt[v][tid];
                 wcnt[v][tid] = run;
                 run += c;
             }
-            s_run[tid] = run;
+            s_cnt[tid] = run;
         }
         __syncthreads();
-        if (valid) perm[s_off[e] + wcnt[w][e] + rank] = a;
+        if (w == 0) {
+            int c4[4], a4[4], sc = 0, sa = 0;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                c4[m] = s_cnt[lane * 4 + m];
+                a4[m] = c4[m] > 0;
+                sc += c4[m];
+                sa += a4[m];
+            }
+            int ic = sc, ia = sa;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int pc = __shfl_up(ic, o), pa = __shfl_up(ia, o);
+                if (lane >= o) {
+                    ic += pc;
+                    ia += pa;
+                }
+            }
+            int rc = ic - sc, ra = ia - sa;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                s_off[lane * 4 + m] = rc;
+                s_act[lane * 4 + m] = a4[m] ? ra : -1;
+                rc += c4[m];
+                ra += a4[m];
+            }
+            if (lane == 63) {
+                s_off[256] = rc;
+                s_nact = ra;
+            }
+        }
         __syncthreads();
     }
+    __syncthreads();
     if (tid < E) {
         cnt[tid] = s_cnt[tid];
         off[tid] = s_off[tid];
