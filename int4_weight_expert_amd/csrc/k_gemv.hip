@@ -685,9 +685,14 @@ __global__ void __launch_bounds__(256) k_gu_fin(Fwd f, int n_rows)
 
 // ---------------------------------------------------------------------------
 // down unit: partial sd (Wd h_r)_row of one k-slice -> ypart[r][b][q][64].
+// CMB (one token): the partials go out agent-coherent and each unit arrives
+// on its output block's counter; the unit that completes a block (every
+// group's every k-slice) sums it as the combine kernel would (shared experts,
+// then the routed ones in rank order, each the sum of its k-slices in order)
+// and writes the block's outputs, so no combine launch follows.
 // ---------------------------------------------------------------------------
 
-template <int FMT, int NT, bool S8, bool HF = false>
+template <int FMT, int NT, bool S8, bool HF = false, bool CMB = false>
 __global__ void __launch_bounds__(64) k_dn(Fwd f)
 {
     extern __shared__ uint4 lds4[];
@@ -770,8 +775,42 @@ __global__ void __launch_bounds__(64) k_dn(Fwd f)
         }
 #pragma unroll
         for (int j = 0; j < NT; ++j)
-            if (j < nj) f.ypart[(((size_t)rr[j] * NB + b) * KS + q) * 64 + lane] = Yt[j] * sdr;
+            if (j < nj) {
+                float* yp = f.ypart + (((size_t)rr[j] * NB + b) * KS + q) * 64 + lane;
+                if (CMB)
+                    st_agent(yp, Yt[j] * sdr);
+                else
+                    *yp = Yt[j] * sdr;
+            }
         lds_wave_sync();
+    }
+    if constexpr (CMB) {
+        // one token (T = 1): routed rank k is row k, shared expert s row K + s
+        if (!arrive_wave(f.dn_cnt + (size_t)b * 64, (uint32_t)(uni(f.n_groups[0]) * KS))) return;
+        const int K = f.K, ns = f.n_shared;
+        float v[9][4];
+#pragma unroll
+        for (int e = 0; e < 9; ++e) {
+            int r = -1;
+            if (e < ns) r = K + e;
+            else if (e - ns < K) r = e - ns;
+            const float* p = f.ypart + ((size_t)(r < 0 ? 0 : r) * NB + b) * KS * 64 + lane;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) v[e][s] = ld_agent(p + min(s, KS - 1) * 64);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                if (r < 0 || s >= KS) v[e][s] = 0.f;
+        }
+        float m = 0.f;
+#pragma unroll
+        for (int e = 0; e < 9; ++e) {
+            const float y = (v[e][0] + v[e][1]) + (v[e][2] + v[e][3]);
+            if (e < ns) m += y;
+            else if (e - ns < K) m = fmaf(f.wts[e - ns], y, m);
+        }
+        const int d = b * 64 + lane;
+        if (f.residual) m = f.x[d] + m;
+        f.out[d] = m;
     }
 }
 
@@ -1094,16 +1133,16 @@ static hipError_t gu_launch(const Fwd& f, hipStream_t st)
     return launch_k(k_gu<FMT, NT, S8>, dim3(units), dim3(64), lds, st, f);
 }
 
-template <int FMT, int NT, bool S8, bool HF = false>
+template <int FMT, int NT, bool S8, bool HF = false, bool CMB = false>
 static hipError_t dn_launch(const Fwd& f, hipStream_t st)
 {
     const int KS = f.dn_ks, CPU = f.I / 32 / KS;
     const unsigned units = (unsigned)(max_groups(f) * (f.H / 64) * KS);
     const size_t lds = gemv_lds_bytes(CPU, f.T);
     static bool big = false;
-    hipError_t e0 = allow_lds(k_dn<FMT, NT, S8, HF>, lds, big);
+    hipError_t e0 = allow_lds(k_dn<FMT, NT, S8, HF, CMB>, lds, big);
     if (e0 != hipSuccess) return e0;
-    return launch_k(k_dn<FMT, NT, S8, HF>, dim3(units), dim3(64), lds, st, f);
+    return launch_k(k_dn<FMT, NT, S8, HF, CMB>, dim3(units), dim3(64), lds, st, f);
 }
 
 template <int FMT, bool S8>
@@ -1172,6 +1211,9 @@ hipError_t launch_gateup_gemv(const Fwd& f, hipStream_t st)
 
 hipError_t launch_down_gemv(const Fwd& f, hipStream_t st)
 {
+    if (f.h_f32 && f.dn_fused)  // one token, the combine in the last unit of each block
+        return f.fmt == MOE_W_INT4_ROW ? dn_launch<MOE_W_INT4_ROW, 1, false, true, true>(f, st)
+                                       : dn_launch<MOE_W_INT4_AFFINE_G64, 1, false, true, true>(f, st);
     if (f.h_f32)  // one token after the one-token gate/up kernel (int4 shared experts)
         return f.fmt == MOE_W_INT4_ROW ? dn_launch<MOE_W_INT4_ROW, 1, false, true>(f, st)
                                        : dn_launch<MOE_W_INT4_AFFINE_G64, 1, false, true>(f, st);

@@ -218,6 +218,7 @@ Fwd make_fwd(moe_ctx* c, const float* x, float* out, int T, int layer, int resid
     f.tiles = c->tiles;
     f.n_tiles = c->n_tiles;
     f.counters = c->counters;
+    f.dn_cnt = c->dn_cnt;
     f.sel_base = c->sel_base;
     f.n_group = g.n_group;
     f.scoring = g.scoring;
@@ -340,9 +341,14 @@ int run_forward(moe_ctx* c, const float* x, int T, int layer, float* out, int re
             return MOE_OK;
         }
         f.h_f32 = 1;
-        mark(c, "down_gemv");
+        f.dn_fused = c->dn_fused;
+        mark(c, f.dn_fused ? "down_combine" : "down_gemv");
         rc = hip_rc(c, launch_down_gemv(f, c->stream));
         if (rc) return rc;
+        if (f.dn_fused) {
+            mark(c, nullptr);
+            return MOE_OK;
+        }
         mark(c, "combine");
         rc = hip_rc(c, launch_combine(f, c->stream));
         if (rc) return rc;
@@ -585,6 +591,7 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
         rc = rc ? rc : dalloc(c, &c->n_tiles, 4);
     }
     rc = rc ? rc : dalloc(c, &c->counters, (1 + H / 64) * 4);
+    rc = rc ? rc : dalloc(c, &c->dn_cnt, (size_t)(H / 64) * 256);
     rc = rc ? rc : dalloc(c, &c->sel_base, 8 * 8);
     c->status_words = 1 + (L * E + 31) / 32;
     rc = rc ? rc : dalloc(c, &c->status, c->status_words * 4);
@@ -592,6 +599,7 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
         c->tbl_host.assign(L * E, -1);
         hipError_t e = hipMemcpy(c->tbl, c->tbl_host.data(), L * E * 4, hipMemcpyHostToDevice);
         if (e == hipSuccess) e = hipMemset(c->counters, 0, (1 + H / 64) * 4);
+        if (e == hipSuccess) e = hipMemset(c->dn_cnt, 0, (size_t)(H / 64) * 256);
         if (e == hipSuccess) e = hipMemset(c->status, 0, c->status_words * 4);
         if (e == hipSuccess) e = hipMemset(c->bias, 0, L * E * 4);
         if (e == hipSuccess) e = hipMemset(c->wr, 0, L * c->Epad * H * 4);

@@ -50,11 +50,13 @@ struct moe_ctx {
     int2* tiles = nullptr;
     int32_t* n_tiles = nullptr;
     uint32_t* counters = nullptr;
+    uint32_t* dn_cnt = nullptr;  // [H/64][64]: one counter per 256-byte line
     uint64_t* sel_base = nullptr;
     uint32_t* status = nullptr;
     size_t status_words = 0;
     int gemm_min_tokens = 64;
     bool tok1 = true;          // one token: the k_tok1 kernels where the shape allows
+    bool dn_fused = true;      // one token: the down GEMV's last unit per block combines
     int lds_max = 65536;
     hipError_t last_err = hipSuccess;
     // timing

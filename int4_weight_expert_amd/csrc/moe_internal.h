@@ -82,6 +82,7 @@ struct Fwd {
     uint4* hq;            // [rows][I/8] h = silu(g) * u staged as fp16 spans
     float2* hsc;          // [rows][I/64]
     uint32_t* counters;   // [0]: router arrivals
+    uint32_t* dn_cnt;     // one-token down GEMV: per 64-output block arrival counters, 256 bytes apart
     uint32_t* status;     // [0] flags, [1..] missing bitmap over layer*E+id
     int n_layers;
     int lds_max;          // device LDS bytes per workgroup
@@ -102,6 +103,7 @@ struct Fwd {
     int h_f32;            // 1: the down GEMV stages its h slices from hf (one token)
     int sel_in_gateup;    // 1: the one-token gate/up kernel selects the experts itself
     int sel_leader;       // 1: one gate/up workgroup selects and publishes to the others
+    int dn_fused;         // 1: the one-token down GEMV combines each output block in its last unit
     uint64_t* sel_base;   // [8] slot base | 1 of each rank once the gate/up kernel's selection is
                           // published (0 = not yet: cleared by the router)
     int2* tiles;          // [max tiles] (group index, first row) of each 128-row tile
