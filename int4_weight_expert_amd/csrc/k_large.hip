@@ -406,10 +406,10 @@ __global__ void __launch_bounds__(256) k_topk(Fwd f)
 // assignments and walks it 64 at a time: the lanes holding the same expert
 // id are found with 8 ballots over the id's bits, and the lowest of them
 // keeps the wavefront's running count of that expert in its own LDS row.
-// Pass 1 counts; a prefix over the 16 wavefronts per expert and a scan over
-// the experts give every (wavefront, expert) its first position; pass 2
-// repeats the walk and writes each assignment at its expert's offset plus
-// the number of earlier assignments of that expert, so the order of
+// Pass 1 counts (LDS atomics); a prefix over the 16 wavefronts per expert and
+// a scan over the experts give every (wavefront, expert) its first position;
+// pass 2 repeats the walk and writes each assignment at its expert's offset
+// plus the number of earlier assignments of that expert, so the order of
 // assignment indices is kept.  If `groups` is set, also builds the forward's
 // expert groups (shared experts first, then active experts ascending) and
 // flags selected experts without a slot.
@@ -457,13 +457,17 @@ __global__ void __launch_bounds__(1024) k_bucket(const int32_t* __restrict__ ids
                 const int a = a0 + (r0 + u) * 64 + lane;
                 int e = ev[u];
                 const bool valid = e >= 0 && e < E;
+                if (pass == 0) {  // counts only: order does not matter
+                    if (valid) atomicAdd(&wcnt[w][e], 1);
+                    continue;
+                }
                 if (!valid) e = 0;
                 const unsigned long long same = same_expert(e, valid);
                 const int rank = __popcll(same & below);
                 // every lane reads the running count before its lowest lane
                 // (rank 0) advances it
                 const int before = wcnt[w][e];
-                if (pass == 1 && valid) perm[s_off[e] + before + rank] = a;
+                if (valid) perm[s_off[e] + before + rank] = a;
                 if (valid && rank == 0) wcnt[w][e] = before + __popcll(same);
             }
         }
