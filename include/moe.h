@@ -160,7 +160,7 @@ int moe_set_router_noalloc(moe_ctx *ctx, int layer, const float *W, const float 
  *   MOE_W_INT4_AFFINE_G64: Qg Qu Qd (as above, unsigned codes 0..15), then
  *     Ag[I][H/64][2] Au[I][H/64][2] Ad[H][I/64][2] bf16 pairs (scale, min);
  *     weight = code * scale + min for the group of 64 inputs it falls in.
- * The slot keeps the bytes in the library's own order (64-row interleave);
+ * The slot keeps the bytes in the library's own order (8-row interleave);
  * moe_read_slot gives the blob back.  Synchronous.  Does not map the slot.
  * Errors: MOE_E_SLOT, MOE_E_SIZE, MOE_E_ARG, MOE_E_HIP. */
 int moe_load_expert(moe_ctx *ctx, int slot, const void *blob, size_t nbytes);
@@ -292,7 +292,7 @@ int moe_sticky_plan(const int *held, const int64_t *last_used, int n_slots, cons
                     int n_want, int *slot_of, int *load);
 
 /* The slot image of an expert blob, on the host (no context, no GPU): the
- * blob's bytes in the slot's own order (64-row interleave, row-format codes
+ * blob's bytes in the slot's own order (8-row interleave, row-format codes
  * offset binary, affine pairs interleaved).  hidden and inter multiples of
  * 64.  Returns MOE_OK, MOE_E_ARG or MOE_E_SIZE. */
 size_t moe_image_bytes(int wfmt, int hidden, int inter);

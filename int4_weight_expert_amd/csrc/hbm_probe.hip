@@ -49,7 +49,10 @@ __global__ void __launch_bounds__(kThreads) k_stream_read(const u32x4* __restric
 // up [2048][6144] int4 in the slot layout: 64-row blocks of 1 KiB chunks):
 // PATTERN 0 as that kernel reads them (a workgroup owns 8 rows: their 16-byte
 // pieces of every chunk, 128 bytes out of each 1 KiB, the other rows read by
-// other workgroups), PATTERN 1 each workgroup's 48 KB contiguous.
+// other workgroups), PATTERN 1 each workgroup's 48 KB contiguous, PATTERN 2
+// as PATTERN 0 with that kernel's workgroup order (within each run of 64
+// workgroups the order is transposed, so that the 8 workgroups sharing a
+// 64-row block run on one XCD).
 constexpr int kPH = 6144, kPI = 2048, kPC = kPH / 32;
 
 template <int PATTERN>
@@ -58,10 +61,11 @@ __global__ void __launch_bounds__(kThreads) k_pattern_read(const uint8_t* __rest
                                                            uint32_t never)
 {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int sb = blockIdx.x % (kPI / 8), gi = blockIdx.x / (kPI / 8);
+    const int p = blockIdx.x, q = PATTERN == 2 ? (p & ~63) + ((p & 7) << 3) + ((p >> 3) & 7) : p;
+    const int sb = q % (kPI / 8), gi = q / (kPI / 8);
     const uint8_t* base = buf + (size_t)gi * exp_bytes;
     u32x4 v[12];
-    if (PATTERN == 0) {
+    if (PATTERN != 1) {
         const int b = sb >> 3, s8 = sb & 7, rr = lane & 7, j = lane >> 3, c0 = w * 48;
         const size_t off = (size_t)(s8 * 8 + rr) * 16 + (size_t)(2 * j) * 1024;
 #pragma unroll
@@ -105,8 +109,9 @@ int hbm_probe_read(const void* buf, size_t bytes, int blocks, int nt, uint32_t* 
 }
 
 // Reads n_exp GLM-shape experts' gate and up codes (exp_bytes apart from buf,
-// at least 12.6 MB each) in `pattern` 0 (the one-token gate/up kernel's) or
-// 1 (contiguous per workgroup); sink needs n_exp x 256 words.  Returns a
+// at least 12.6 MB each) in `pattern` 0 (the one-token gate/up kernel's), 1
+// (contiguous per workgroup) or 2 (0 in that kernel's workgroup order); sink
+// needs n_exp x 256 words.  Returns a
 // hipError_t value (0 = success).
 int hbm_probe_pattern(const void* buf, size_t exp_bytes, int n_exp, int pattern, uint32_t* sink,
                       uint32_t never, void* stream)
@@ -115,6 +120,9 @@ int hbm_probe_pattern(const void* buf, size_t exp_bytes, int n_exp, int pattern,
     const dim3 grid((unsigned)(n_exp * (kPI / 8))), block(kThreads);
     if (pattern == 0)
         hipLaunchKernelGGL(k_pattern_read<0>, grid, block, 0, (hipStream_t)stream, (const uint8_t*)buf,
+                           exp_bytes, sink, never);
+    else if (pattern == 2)
+        hipLaunchKernelGGL(k_pattern_read<2>, grid, block, 0, (hipStream_t)stream, (const uint8_t*)buf,
                            exp_bytes, sink, never);
     else
         hipLaunchKernelGGL(k_pattern_read<1>, grid, block, 0, (hipStream_t)stream, (const uint8_t*)buf,

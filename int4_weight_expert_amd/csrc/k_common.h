@@ -64,6 +64,23 @@ __device__ __forceinline__ uint2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff,
     return make_uint2(v.x, v.y);
 }
 
+// Slot layout of an int4 matrix [O][In] (row and affine formats): 8-row
+// groups.  Within group o / 8 the 16-byte pieces of its 8 rows for chunk c
+// (32 inputs) are 128 contiguous bytes, chunk after chunk, so a group's
+// codes are one run of C * 128 bytes (C = In / 32) and a 64-row block (8
+// groups) is C * 1024 bytes.  Byte offset of row r's piece of chunk c,
+// counted from the start of r's 64-row block (r < 64) or of the matrix:
+__device__ __forceinline__ uint32_t blk_off(int r, int C, int c)
+{
+    return (uint32_t)(((r >> 3) * C + c) * 128 + (r & 7) * 16);
+}
+// Affine (scale, min) pairs, 4 bytes each, grouped the same way: row r's
+// pair of input group g (64 inputs) at ((r / 8) * G + g) * 32 + (r % 8) * 4.
+__device__ __forceinline__ uint32_t tab_off(int r, int G, int g)
+{
+    return (uint32_t)(((r >> 3) * G + g) * 32 + (r & 7) * 4);
+}
+
 __device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
 {
     return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);

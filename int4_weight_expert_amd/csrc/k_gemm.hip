@@ -264,7 +264,8 @@ __device__ __forceinline__ void gemm_tile8(const Fwd& f, uint4 (*As)[8][GM], con
 }
 
 // int4 codes with a K step of 64 inputs: lane half h loads chunk 2s + h of
-// its row whole (one 16-byte load), and dword d of it (inputs 8d..8d+7 of
+// its row whole (one 16-byte load; a wavefront's 32 rows are four 8-row
+// groups of the slot layout), and dword d of it (inputs 8d..8d+7 of
 // the chunk, pair order) meets LDS piece 4h + d in MFMA round d; the
 // activation tile of a step is 128 rows x 64 fp16 (8 pieces), double
 // buffered, so a step has 4 rounds of MFMAs behind one barrier.
@@ -290,9 +291,10 @@ __device__ __forceinline__ void gemm_tile64(const Fwd& f, uint4 (*As)[8][GM], co
         make_rsrc(base + mat0 + (size_t)blk * NC * 1024, (uint32_t)NC * 1024);
     const __amdgpu_buffer_rsrc_t rw1 =
         make_rsrc(base + mat1 + (size_t)blk * NC * 1024, (uint32_t)NC * 1024);
-    const uint32_t v0 = (uint32_t)(o0 & 63) * 16 + half * 1024;
-    const uint32_t v1 = (uint32_t)(o1 & 63) * 16 + half * 1024;
-    constexpr uint32_t STEP = 2048;  // code bytes per K step and 64-row block
+    // the lane's row in its 64-row block, chunk `half` of the first step
+    const uint32_t v0 = blk_off(o0 & 63, NC, half);
+    const uint32_t v1 = blk_off(o1 & 63, NC, half);
+    constexpr uint32_t STEP = 256;  // code bytes per K step and row (two chunks of an 8-row group)
 
     // activation loader: thread -> row tid & 127, pieces p and 4 + p of the
     // step (p = tid >> 7: piece p of each of the step's two chunks)

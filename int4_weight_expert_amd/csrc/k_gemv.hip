@@ -429,14 +429,14 @@ __global__ void __launch_bounds__(64) k_gu(Fwd f)
     uint4* xq = lds4;
     float2* xs = (float2*)(lds4 + NT * CPU * 4);
     const uint8_t* base = grp.base;
-    const uint32_t voff = (uint32_t)lane * 16, toff = (uint32_t)lane * 4;
+    // the lane's row in the block: its piece of chunk c0 + j at voff + 128 j
+    const uint32_t voff = blk_off(lane, C, c0), toff = tab_off(lane, G, 0);
     const uint32_t mv = magic_vgpr();
-    const __amdgpu_buffer_rsrc_t rg =
-        make_rsrc(base + ((size_t)b * C + c0) * 1024, (uint32_t)CPU * 1024);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(base + (size_t)b * C * 1024, (uint32_t)C * 1024);
     const __amdgpu_buffer_rsrc_t ru =
-        make_rsrc(base + (size_t)I * H / 2 + ((size_t)b * C + c0) * 1024, (uint32_t)CPU * 1024);
+        make_rsrc(base + (size_t)I * H / 2 + (size_t)b * C * 1024, (uint32_t)C * 1024);
     // row format: fp32 row scales after the codes; affine: (scale, min) bf16
-    // pair per row and 64-input group, [row block][group][64] per matrix
+    // pair per row and 64-input group, in 8-row groups per matrix
     const uint8_t* tab = base + (size_t)3 * H * I / 2;
     const __amdgpu_buffer_rsrc_t rtg = make_rsrc(tab + (size_t)b * G * 256, (uint32_t)G * 256);
     const __amdgpu_buffer_rsrc_t rtu =
@@ -465,12 +465,12 @@ __global__ void __launch_bounds__(64) k_gu(Fwd f)
             uint32_t PA = 0, PB = 0;
 #pragma unroll
             for (int k = 0; k < UG; ++k) {
-                A[k] = bload16(rg, voff + k * 1024, 0);
-                B[k] = bload16(ru, voff + k * 1024, 0);
+                A[k] = bload16(rg, voff + k * 128, 0);
+                B[k] = bload16(ru, voff + k * 128, 0);
             }
             if (FMT != MOE_W_INT4_ROW) {
-                PA = bload4(rtg, toff, (uint32_t)(c0 / 2) * 256);
-                PB = bload4(rtu, toff, (uint32_t)(c0 / 2) * 256);
+                PA = bload4(rtg, toff, (uint32_t)(c0 / 2) * 32);
+                PB = bload4(rtu, toff, (uint32_t)(c0 / 2) * 32);
             }
             copy_slice<NT>(f.xq, f.xsc, tt, nj, H / 8, H / 64, c0, CPU, lane, xq, xs);
             // one rolling step = one span (2 chunks); the last step loads nothing
@@ -481,14 +481,14 @@ __global__ void __launch_bounds__(64) k_gu(Fwd f)
         {                                                                                \
             const uint4 wa = A[k], wb = B[k];                                            \
             if (LOAD_) {                                                                 \
-                A[k] = bload16(rg, voff + k * 1024, ((I_) + 1) * UG * 1024);             \
-                B[k] = bload16(ru, voff + k * 1024, ((I_) + 1) * UG * 1024);             \
+                A[k] = bload16(rg, voff + k * 128, ((I_) + 1) * UG * 128);             \
+                B[k] = bload16(ru, voff + k * 128, ((I_) + 1) * UG * 128);             \
             }                                                                            \
             chunk2<NT>(wa, wb, xq, CPU * 4, (I_) * UG + k, nj, mv, ag, au);               \
         }                                                                                \
         if (FMT != MOE_W_INT4_ROW && (LOAD_)) {                                          \
-            PA = bload4(rtg, toff, (uint32_t)(c0 / 2 + (I_) + 1) * 256);                 \
-            PB = bload4(rtu, toff, (uint32_t)(c0 / 2 + (I_) + 1) * 256);                 \
+            PA = bload4(rtg, toff, (uint32_t)(c0 / 2 + (I_) + 1) * 32);                 \
+            PB = bload4(rtu, toff, (uint32_t)(c0 / 2 + (I_) + 1) * 32);                 \
         }                                                                                \
         _Pragma("unroll") for (int j = 0; j < NT; ++j) if (j < nj)                       \
         {                                                                                \
@@ -546,14 +546,14 @@ __global__ void __launch_bounds__(1024) k_gu_wg(Fwd f)
     float2* xs = (float2*)(xq + NT * CPU * 4);
     float* red = (float*)(lds4 + KS * wl);  // [KS][NT][2][64]
     const uint8_t* base = grp.base;
-    const uint32_t voff = (uint32_t)lane * 16, toff = (uint32_t)lane * 4;
+    // the lane's row in the block: its piece of chunk c0 + j at voff + 128 j
+    const uint32_t voff = blk_off(lane, C, c0), toff = tab_off(lane, G, 0);
     const uint32_t mv = magic_vgpr();
-    const __amdgpu_buffer_rsrc_t rg =
-        make_rsrc(base + ((size_t)b * C + c0) * 1024, (uint32_t)CPU * 1024);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(base + (size_t)b * C * 1024, (uint32_t)C * 1024);
     const __amdgpu_buffer_rsrc_t ru =
-        make_rsrc(base + (size_t)I * H / 2 + ((size_t)b * C + c0) * 1024, (uint32_t)CPU * 1024);
+        make_rsrc(base + (size_t)I * H / 2 + (size_t)b * C * 1024, (uint32_t)C * 1024);
     // row format: fp32 row scales after the codes; affine: (scale, min) bf16
-    // pair per row and 64-input group, [row block][group][64] per matrix
+    // pair per row and 64-input group, in 8-row groups per matrix
     const uint8_t* tab = base + (size_t)3 * H * I / 2;
     const __amdgpu_buffer_rsrc_t rtg = make_rsrc(tab + (size_t)b * G * 256, (uint32_t)G * 256);
     const __amdgpu_buffer_rsrc_t rtu =
@@ -582,12 +582,12 @@ __global__ void __launch_bounds__(1024) k_gu_wg(Fwd f)
             uint32_t PA = 0, PB = 0;
 #pragma unroll
             for (int k = 0; k < UG; ++k) {
-                A[k] = bload16(rg, voff + k * 1024, 0);
-                B[k] = bload16(ru, voff + k * 1024, 0);
+                A[k] = bload16(rg, voff + k * 128, 0);
+                B[k] = bload16(ru, voff + k * 128, 0);
             }
             if (FMT != MOE_W_INT4_ROW) {
-                PA = bload4(rtg, toff, (uint32_t)(c0 / 2) * 256);
-                PB = bload4(rtu, toff, (uint32_t)(c0 / 2) * 256);
+                PA = bload4(rtg, toff, (uint32_t)(c0 / 2) * 32);
+                PB = bload4(rtu, toff, (uint32_t)(c0 / 2) * 32);
             }
             copy_slice<NT>(f.xq, f.xsc, tt, nj, H / 8, H / 64, c0, CPU, lane, xq, xs);
             // one rolling step = one span (2 chunks); the last step loads nothing
@@ -598,14 +598,14 @@ __global__ void __launch_bounds__(1024) k_gu_wg(Fwd f)
         {                                                                                \
             const uint4 wa = A[k], wb = B[k];                                            \
             if (LOAD_) {                                                                 \
-                A[k] = bload16(rg, voff + k * 1024, ((I_) + 1) * UG * 1024);             \
-                B[k] = bload16(ru, voff + k * 1024, ((I_) + 1) * UG * 1024);             \
+                A[k] = bload16(rg, voff + k * 128, ((I_) + 1) * UG * 128);             \
+                B[k] = bload16(ru, voff + k * 128, ((I_) + 1) * UG * 128);             \
             }                                                                            \
             chunk2<NT>(wa, wb, xq, CPU * 4, (I_) * UG + k, nj, mv, ag, au);               \
         }                                                                                \
         if (FMT != MOE_W_INT4_ROW && (LOAD_)) {                                          \
-            PA = bload4(rtg, toff, (uint32_t)(c0 / 2 + (I_) + 1) * 256);                 \
-            PB = bload4(rtu, toff, (uint32_t)(c0 / 2 + (I_) + 1) * 256);                 \
+            PA = bload4(rtg, toff, (uint32_t)(c0 / 2 + (I_) + 1) * 32);                 \
+            PB = bload4(rtu, toff, (uint32_t)(c0 / 2 + (I_) + 1) * 32);                 \
         }                                                                                \
         _Pragma("unroll") for (int j = 0; j < NT; ++j) if (j < nj)                       \
         {                                                                                \
@@ -710,10 +710,11 @@ __global__ void __launch_bounds__(64) k_dn(Fwd f)
     uint4* xq = lds4;
     float2* xs = (float2*)(lds4 + NT * CPU * 4);
     const uint8_t* base = grp.base;
-    const uint32_t voff = (uint32_t)lane * 16, toff = (uint32_t)lane * 4;
+    // the lane's row in the block: its piece of chunk c0 + j at voff + 128 j
+    const uint32_t voff = blk_off(lane, C, c0), toff = tab_off(lane, GI, 0);
     const uint32_t mv = magic_vgpr();
     const __amdgpu_buffer_rsrc_t rd =
-        make_rsrc(base + (size_t)I * H + ((size_t)b * C + c0) * 1024, (uint32_t)CPU * 1024);
+        make_rsrc(base + (size_t)I * H + (size_t)b * C * 1024, (uint32_t)C * 1024);
     const uint8_t* tab = base + (size_t)3 * H * I / 2;
     const __amdgpu_buffer_rsrc_t rtd = make_rsrc(
         tab + ((size_t)2 * I * (H / 64) + (size_t)b * GI * 64) * 4, (uint32_t)GI * 256);
@@ -737,10 +738,10 @@ __global__ void __launch_bounds__(64) k_dn(Fwd f)
             uint4 D[UD];
             uint32_t P0 = 0, P1 = 0;
 #pragma unroll
-            for (int k = 0; k < UD; ++k) D[k] = bload16(rd, voff + k * 1024, 0);
+            for (int k = 0; k < UD; ++k) D[k] = bload16(rd, voff + k * 128, 0);
             if (FMT != MOE_W_INT4_ROW) {
-                P0 = bload4(rtd, toff, (uint32_t)(c0 / 2) * 256);
-                P1 = bload4(rtd, toff, (uint32_t)(c0 / 2 + 1) * 256);
+                P0 = bload4(rtd, toff, (uint32_t)(c0 / 2) * 32);
+                P1 = bload4(rtd, toff, (uint32_t)(c0 / 2 + 1) * 32);
             }
             if (HF)  // one token, h in fp32 from the one-token gate/up kernel
                 stage_slice_f32(f.hf + (size_t)rr[0] * I, c0, CPU, lane, xq, xs);
@@ -753,13 +754,13 @@ __global__ void __launch_bounds__(64) k_dn(Fwd f)
         _Pragma("unroll") for (int k = 0; k < UD; ++k)                                    \
         {                                                                                \
             const uint4 wd = D[k];                                                       \
-            if (LOAD_) D[k] = bload16(rd, voff + k * 1024, ((I_) + 1) * UD * 1024);      \
+            if (LOAD_) D[k] = bload16(rd, voff + k * 128, ((I_) + 1) * UD * 128);      \
             if (k < 2) chunk1<NT>(wd, xq, CPU * 4, (I_) * UD + k, nj, mv, a0);            \
             else chunk1<NT>(wd, xq, CPU * 4, (I_) * UD + k, nj, mv, a1);                  \
         }                                                                                \
         if (FMT != MOE_W_INT4_ROW && (LOAD_)) {                                          \
-            P0 = bload4(rtd, toff, (uint32_t)(c0 / 2 + 2 * (I_) + 2) * 256);             \
-            P1 = bload4(rtd, toff, (uint32_t)(c0 / 2 + 2 * (I_) + 3) * 256);             \
+            P0 = bload4(rtd, toff, (uint32_t)(c0 / 2 + 2 * (I_) + 2) * 32);             \
+            P1 = bload4(rtd, toff, (uint32_t)(c0 / 2 + 2 * (I_) + 3) * 32);             \
         }                                                                                \
         _Pragma("unroll") for (int j = 0; j < NT; ++j) if (j < nj)                       \
         {                                                                                \
@@ -957,8 +958,8 @@ __global__ void __launch_bounds__(512) k_dn2(Fwd f)
 #pragma unroll
     for (int g = 0; g < RG; ++g) {
         const int rg = blockIdx.x * RG + g, blk = rg >> 3, row64 = (rg & 7) * 8 + r8;
-        coff[g] = (uint32_t)blk * C * 1024 + (uint32_t)chunk * 1024 + (uint32_t)row64 * 16;
-        toff[g] = (uint32_t)blk * NP * 256 + (uint32_t)(chunk >> 1) * 256 + (uint32_t)row64 * 4;
+        coff[g] = (uint32_t)blk * C * 1024 + blk_off(row64, C, chunk);
+        toff[g] = (uint32_t)blk * NP * 256 + tab_off(row64, NP, chunk >> 1);
     }
     const uint32_t mv = magic_vgpr();
     constexpr int NS = DC_NE * RG;  // steps (slot e, row group g), e outer

@@ -22,7 +22,7 @@
 // a one-step rolling prefetch.  Lane l = (i = l % 16, g = l / 16): for
 // row-group s (rows 16 s .. 16 s + 15 of the block) the lane loads the
 // 16-byte piece of row 16 s + i in chunk 4 step + g (the slot layout keeps
-// the 16 rows' pieces of a chunk in 256 contiguous bytes), and as the B
+// each 8-row group's pieces of a chunk in 128 contiguous bytes), and as the B
 // operand the staged activations of token i of the pass in the same chunk
 // (64 contiguous bytes).  Dword j of the piece (8 codes) with quad j of the
 // activations is the lane's K-group of MFMA (s, j): K = 32 inputs per MFMA,
@@ -103,11 +103,10 @@ __global__ void __launch_bounds__(64) k_gum(Fwd f)
     const int CPU = C / KS, c0 = q * CPU, nst = CPU / MT_STEP;
     const uint8_t* base = grp.base;
     const uint8_t* anchor = (const uint8_t*)f.x;  // any valid address (empty resources)
-    const uint32_t mbytes = base ? (uint32_t)CPU * 1024 : 0u;
-    const __amdgpu_buffer_rsrc_t rg =
-        make_rsrc(base ? base + ((size_t)b * C + c0) * 1024 : anchor, mbytes);
+    const uint32_t mbytes = base ? (uint32_t)C * 1024 : 0u;
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(base ? base + (size_t)b * C * 1024 : anchor, mbytes);
     const __amdgpu_buffer_rsrc_t ru =
-        make_rsrc(base ? base + (size_t)I * H / 2 + ((size_t)b * C + c0) * 1024 : anchor, mbytes);
+        make_rsrc(base ? base + (size_t)I * H / 2 + (size_t)b * C * 1024 : anchor, mbytes);
     // the block's row scales, in registers until the first epilogue puts
     // them in LDS (each lane then needs 16 rows of them)
     const float* tab = (const float*)(base ? base + (size_t)3 * H * I / 2 : anchor);
@@ -117,7 +116,7 @@ __global__ void __launch_bounds__(64) k_gum(Fwd f)
     // row-group s: row 16 s + i of chunk 4 step + g
     uint32_t voff[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) voff[s] = (uint32_t)((g * 64 + 16 * s + i) * 16);
+    for (int s = 0; s < 4; ++s) voff[s] = blk_off(16 * s + i, C, c0 + g);
 #pragma unroll 1
     for (int p0 = 0; p0 < grp.cnt; p0 += MT_N) {
         const int nj = min(MT_N, grp.cnt - p0);
@@ -146,8 +145,8 @@ __global__ void __launch_bounds__(64) k_gum(Fwd f)
                 for (int s = 0; s < 4; ++s) {
                     a[s] = A[s];
                     bb[s] = B[s];
-                    A[s] = bload16(rg, voff[s], (uint32_t)(sn * MT_STEP) * 1024);
-                    B[s] = bload16(ru, voff[s], (uint32_t)(sn * MT_STEP) * 1024);
+                    A[s] = bload16(rg, voff[s], (uint32_t)(sn * MT_STEP) * 128);
+                    B[s] = bload16(ru, voff[s], (uint32_t)(sn * MT_STEP) * 128);
                 }
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -213,15 +212,15 @@ __global__ void __launch_bounds__(64) k_dnm(Fwd f)
     const uint8_t* base = grp.base;
     const uint8_t* anchor = (const uint8_t*)f.x;
     const __amdgpu_buffer_rsrc_t rd =
-        make_rsrc(base ? base + (size_t)I * H + ((size_t)b * C + c0) * 1024 : anchor,
-                  base ? (uint32_t)CPU * 1024 : 0u);
+        make_rsrc(base ? base + (size_t)I * H + (size_t)b * C * 1024 : anchor,
+                  base ? (uint32_t)C * 1024 : 0u);
     const float sdl =
         base ? ((const float*)(base + (size_t)3 * H * I / 2))[2 * I + b * 64 + lane] : 0.f;
     const half8 ones = as_h8(make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u));
     const uint32_t mv = f.magic;
     uint32_t voff[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) voff[s] = (uint32_t)((g * 64 + 16 * s + i) * 16);
+    for (int s = 0; s < 4; ++s) voff[s] = blk_off(16 * s + i, C, c0 + g);
 #pragma unroll 1
     for (int p0 = 0; p0 < grp.cnt; p0 += MT_N) {
         const int nj = min(MT_N, grp.cnt - p0);
@@ -244,7 +243,7 @@ __global__ void __launch_bounds__(64) k_dnm(Fwd f)
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
                     w[s] = D[s];
-                    D[s] = bload16(rd, voff[s], (uint32_t)(sn * MT_STEP) * 1024);
+                    D[s] = bload16(rd, voff[s], (uint32_t)(sn * MT_STEP) * 128);
                 }
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {

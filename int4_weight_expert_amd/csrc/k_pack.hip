@@ -298,11 +298,13 @@ __global__ void __launch_bounds__(RQ_ROWS * 32) k_requant_rows(RqArgs a)
         }
     }
     if (SLOT) {  // every matrix's O is a multiple of 64, so the tile is full
+        // the tile's 8 rows are one 8-row group of the slot layout: C * 128
+        // contiguous bytes
         __syncthreads();
-        const int b = o0 >> 6, rb = o0 & 63;
+        uint8_t* gq = m.q + (size_t)(o0 >> 3) * C * 128;
         for (int i = threadIdx.x; i < C * RQ_ROWS; i += RQ_ROWS * 32) {
             const int c = i / RQ_ROWS, r = i % RQ_ROWS;
-            *(uint4*)(m.q + (((size_t)b * C + c) * 64 + rb + r) * 16) =
+            *(uint4*)(gq + ((size_t)c * RQ_ROWS + r) * 16) =
                 *(const uint4*)(rq_tile + c * RQ_TSTRIDE + r * 16);
         }
     }
@@ -373,8 +375,12 @@ __global__ void __launch_bounds__(256) k_pack_affine_g64(const void* __restrict_
     }
 }
 
-// Blob matrix [O][In/2] bytes <-> slot interleave (see moe_internal.h).
-// One thread per 16-byte chunk; `flip` = 0x88888888 for the row format.
+// Blob matrix [O][In/2] bytes <-> slot interleave (see moe_internal.h):
+// groups of R rows, the 16-byte pieces of a group's rows for one chunk of 32
+// inputs contiguous, chunk after chunk (R = 8 for the int4 formats; R = 64
+// for int8 matrices, passed as int4 matrices of twice the width).  One
+// thread per 16-byte chunk; `flip` = 0x88888888 for the row format.
+template <int R>
 __global__ void __launch_bounds__(256) k_interleave(const uint8_t* __restrict__ src,
                                                     uint8_t* __restrict__ dst, int64_t O,
                                                     int64_t In, uint32_t flip, int to_slot)
@@ -383,8 +389,8 @@ __global__ void __launch_bounds__(256) k_interleave(const uint8_t* __restrict__ 
     const int64_t total = O * C;
     for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
          idx += (int64_t)gridDim.x * 256) {
-        const int64_t lane = idx & 63, c = (idx >> 6) % C, b = (idx >> 6) / C;
-        const int64_t canon = (b * 64 + lane) * (In / 2) + c * 16;
+        const int64_t r = idx % R, c = (idx / R) % C, grp = (idx / R) / C;
+        const int64_t canon = (grp * R + r) * (In / 2) + c * 16;
         const int64_t inter = idx * 16;
         uint4 v = *(const uint4*)(src + (to_slot ? canon : inter));
         v.x ^= flip;
@@ -395,7 +401,7 @@ __global__ void __launch_bounds__(256) k_interleave(const uint8_t* __restrict__ 
     }
 }
 
-// Affine (scale, min) pairs: blob [O][G] <-> slot [O/64][G][64], 4 B each.
+// Affine (scale, min) pairs: blob [O][G] <-> slot [O/8][G][8], 4 B each.
 __global__ void __launch_bounds__(256) k_interleave_pairs(const uint32_t* __restrict__ src,
                                                           uint32_t* __restrict__ dst, int64_t O,
                                                           int64_t G, int to_slot)
@@ -403,8 +409,8 @@ __global__ void __launch_bounds__(256) k_interleave_pairs(const uint32_t* __rest
     const int64_t total = O * G;
     for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
          idx += (int64_t)gridDim.x * 256) {
-        const int64_t lane = idx & 63, g = (idx >> 6) % G, b = (idx >> 6) / G;
-        const int64_t canon = (b * 64 + lane) * G + g;
+        const int64_t r = idx & 7, g = (idx >> 3) % G, grp = (idx >> 3) / G;
+        const int64_t canon = (grp * 8 + r) * G + g;
         if (to_slot) dst[idx] = src[canon];
         else dst[canon] = src[idx];
     }
@@ -575,7 +581,7 @@ static hipError_t convert(const uint8_t* src, uint8_t* dst, int fmt, int H, int 
         const int64_t m8 = (int64_t)I * H;
         const int64_t mats[3][3] = {{0, I, H}, {m8, I, H}, {2 * m8, H, I}};
         for (auto& m : mats)
-            hipLaunchKernelGGL(k_interleave, dim3(grid_for(m[1] * (m[2] / 16), 256)), dim3(256), 0,
+            hipLaunchKernelGGL(k_interleave<64>, dim3(grid_for(m[1] * (m[2] / 16), 256)), dim3(256), 0,
                                st, src + m[0], dst + m[0], m[1], 2 * m[2], 0x80808080u, to_slot);
         const hipError_t e = hipMemcpyAsync(dst + 3 * m8, src + 3 * m8, (size_t)(2 * I + H) * 4,
                                             hipMemcpyDeviceToDevice, st);
@@ -584,7 +590,7 @@ static hipError_t convert(const uint8_t* src, uint8_t* dst, int fmt, int H, int 
     const int64_t gq = (int64_t)I * (H / 2), dq = (int64_t)H * (I / 2);
     const int64_t mats[3][3] = {{0, I, H}, {gq, I, H}, {2 * gq, H, I}};  // offset, O, In
     for (auto& m : mats) {
-        hipLaunchKernelGGL(k_interleave, dim3(grid_for(m[1] * (m[2] / 32), 256)), dim3(256), 0,
+        hipLaunchKernelGGL(k_interleave<8>, dim3(grid_for(m[1] * (m[2] / 32), 256)), dim3(256), 0,
                            st, src + m[0], dst + m[0], m[1], m[2], flip, to_slot);
     }
     const int64_t sb = 2 * gq + dq;

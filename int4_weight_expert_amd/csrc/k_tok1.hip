@@ -15,10 +15,10 @@
 // matrix and reduces them completely, so no k-slice partials and no
 // finalize or combine launch are needed; there are enough such workgroups
 // (GLM shape: 9 x 256 for gate/up, 768 for down, a few per CU) to spread
-// the stream over every CU evenly.  In the slot layout the 8 rows' 16-byte
-// pieces of one 32-input chunk are 128 contiguous bytes, so a wavefront
-// load, lane (row r of 8, span lane j of 8), covers 8 rows x 8 chunks in
-// 128-byte runs.  Each step a lane takes two consecutive chunks (one span of
+// the stream over every CU evenly.  The 8 rows are one 8-row group of the
+// slot layout, whose codes are one contiguous run per matrix (128 bytes per
+// 32-input chunk), so a workgroup streams contiguous memory; a wavefront
+// load, lane (row r of 8, span lane j of 8), covers 8 rows x 8 chunks.  Each step a lane takes two consecutive chunks (one span of
 // 64 inputs, whose staged activation scale and sum it folds in itself).
 // The lanes of one row are summed with a fixed butterfly, the wavefronts in
 // LDS in wavefront order: results are bitwise reproducible.
@@ -194,13 +194,8 @@ __global__ void __launch_bounds__(64 * W) k_gu8(Fwd f)
     __shared__ float s_red[W][16];
     const int lane = threadIdx.x & 63, w = uni((int)(threadIdx.x >> 6));
     const int H = f.H, I = f.I, C = H / 32, G = H / 64, NSB = I / 8;
-    // Workgroup p runs on XCD p mod 8.  Within each run of 64 workgroups
-    // the order is transposed, so that the 8 row blocks of one 64-row slot
-    // block (whose 16-byte pieces share each 1 KiB chunk) run on one XCD.
-    // The grid is a multiple of 64 (I % 512 == 0), and each run stays in
-    // one expert group (NSB = I / 8 is a multiple of 64).
-    const int p = blockIdx.x, q = (p & ~63) + ((p & 7) << 3) + ((p >> 3) & 7);
-    const int sb = q % NSB, gi = q / NSB;
+    // workgroup -> (8-row group sb of I, expert group gi)
+    const int sb = blockIdx.x % NSB, gi = blockIdx.x / NSB;
     int t = 0, r;
     const uint8_t* base;
     if (SEL) {
@@ -290,34 +285,36 @@ __global__ void __launch_bounds__(64 * W) k_gu8(Fwd f)
         tok_rows(f, f.perm, grp, 0, t, r);
         base = grp.base;
     }
-    const int b = sb >> 3, s8 = sb & 7, rr = lane & 7, j = lane >> 3;
+    const int rr = lane & 7, j = lane >> 3;
     constexpr int CW = 16 * NST, NSP = CW / 2;  // chunks and spans of the wave
     const int c0 = w * CW;
     const uint8_t* anchor = (const uint8_t*)f.x;  // any valid address (empty resources)
-    const uint32_t mbytes = base ? (uint32_t)C * 1024 : 0u;
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc(base ? base + (size_t)b * C * 1024 : anchor, mbytes);
+    // the workgroup's 8 rows are one 8-row group of the slot layout: C * 128
+    // contiguous bytes per matrix, 128 per chunk
+    const uint32_t mbytes = base ? (uint32_t)C * 128 : 0u;
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(base ? base + (size_t)sb * C * 128 : anchor, mbytes);
     const __amdgpu_buffer_rsrc_t ru =
-        make_rsrc(base ? base + (size_t)I * H / 2 + (size_t)b * C * 1024 : anchor, mbytes);
-    const uint32_t voff = (uint32_t)(s8 * 8 + rr) * 16 + (uint32_t)(2 * j) * 1024;
+        make_rsrc(base ? base + (size_t)I * H / 2 + (size_t)sb * C * 128 : anchor, mbytes);
+    const uint32_t voff = (uint32_t)rr * 16 + (uint32_t)(2 * j) * 128;
     uint4 A[2 * NST], B[2 * NST];
 #pragma unroll
     for (int st = 0; st < NST; ++st)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const uint32_t so = (uint32_t)(c0 + st * 16 + h) * 1024;
+            const uint32_t so = (uint32_t)(c0 + st * 16 + h) * 128;
             A[2 * st + h] = bload16(rg, voff, so);
             B[2 * st + h] = bload16(ru, voff, so);
         }
     const uint8_t* tab = base ? base + (size_t)3 * H * I / 2 : anchor;
     uint32_t PA[NST], PB[NST];
     if (FMT != MOE_W_INT4_ROW) {
-        const uint32_t tb = base ? (uint32_t)G * 256 : 0u;
-        const __amdgpu_buffer_rsrc_t rtg = make_rsrc(tab + (size_t)b * G * 256, tb);
-        const __amdgpu_buffer_rsrc_t rtu = make_rsrc(tab + ((size_t)I * G + (size_t)b * G * 64) * 4, tb);
-        const uint32_t toff = (uint32_t)(s8 * 8 + rr) * 4 + (uint32_t)j * 256;
+        const uint32_t tb = base ? (uint32_t)G * 32 : 0u;
+        const __amdgpu_buffer_rsrc_t rtg = make_rsrc(tab + (size_t)sb * G * 32, tb);
+        const __amdgpu_buffer_rsrc_t rtu = make_rsrc(tab + (size_t)I * G * 4 + (size_t)sb * G * 32, tb);
+        const uint32_t toff = (uint32_t)rr * 4 + (uint32_t)j * 32;
 #pragma unroll
         for (int st = 0; st < NST; ++st) {
-            const uint32_t so = (uint32_t)(c0 / 2 + st * 8) * 256;
+            const uint32_t so = (uint32_t)(c0 / 2 + st * 8) * 32;
             PA[st] = bload4(rtg, toff, so);
             PB[st] = bload4(rtu, toff, so);
         }
@@ -389,7 +386,7 @@ __global__ void __launch_bounds__(64 * D8_NE) k_dn8(Fwd f)
     __shared__ float s_w[D8_NE];
     const int lane = threadIdx.x & 63, e = uni((int)(threadIdx.x >> 6));
     const int H = f.H, I = f.I, C = I / 32, NP = I / 64, K = f.K, ns = f.n_shared, NST = C / 16;
-    const int ob = blockIdx.x, b = ob >> 3, s8 = ob & 7, rr = lane & 7, j = lane >> 3;
+    const int ob = blockIdx.x, rr = lane & 7, j = lane >> 3;
     // this slot's h row (T = 1): routed rank k is row k, shared expert s row K + s
     const int hrow = e < ns ? K + e : e - ns;
     // its h first (lane c: chunk c of 32 inputs, I <= 2048), so that the
@@ -412,22 +409,24 @@ __global__ void __launch_bounds__(64 * D8_NE) k_dn8(Fwd f)
                           ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(gbase >> 32), src) << 32);
     const uint8_t* base = m ? (const uint8_t*)(uintptr_t)bsel : nullptr;
     const uint8_t* anchor = (const uint8_t*)f.x;
+    // the workgroup's 8 rows are one 8-row group of the slot layout (C * 128
+    // contiguous bytes, 128 per chunk; 32 bytes of affine pairs per input group)
     const __amdgpu_buffer_rsrc_t rd =
-        make_rsrc(base ? base + (size_t)I * H + (size_t)b * C * 1024 : anchor,
-                  base ? (uint32_t)C * 1024 : 0u);
-    const uint32_t voff = (uint32_t)(s8 * 8 + rr) * 16 + (uint32_t)(2 * j) * 1024;
+        make_rsrc(base ? base + (size_t)I * H + (size_t)ob * C * 128 : anchor,
+                  base ? (uint32_t)C * 128 : 0u);
+    const uint32_t voff = (uint32_t)rr * 16 + (uint32_t)(2 * j) * 128;
     const uint8_t* tab = base ? base + (size_t)3 * H * I / 2 : anchor;
     const __amdgpu_buffer_rsrc_t rt =
-        make_rsrc(tab + ((size_t)2 * I * (H / 64) + (size_t)b * NP * 64) * 4,
-                  (FMT != MOE_W_INT4_ROW && base) ? (uint32_t)NP * 256 : 0u);
-    const uint32_t toff = (uint32_t)(s8 * 8 + rr) * 4 + (uint32_t)j * 256;
+        make_rsrc(tab + (size_t)2 * I * (H / 64) * 4 + (size_t)ob * NP * 32,
+                  (FMT != MOE_W_INT4_ROW && base) ? (uint32_t)NP * 32 : 0u);
+    const uint32_t toff = (uint32_t)rr * 4 + (uint32_t)j * 32;
     uint4 D[2 * PD];
     uint32_t P[PD];
 #pragma unroll
     for (int k = 0; k < PD; ++k) {
-        D[2 * k] = bload16(rd, voff, (uint32_t)(k * 16) * 1024);
-        D[2 * k + 1] = bload16(rd, voff, (uint32_t)(k * 16 + 1) * 1024);
-        if (FMT != MOE_W_INT4_ROW) P[k] = bload4(rt, toff, (uint32_t)(k * 8) * 256);
+        D[2 * k] = bload16(rd, voff, (uint32_t)(k * 16) * 128);
+        D[2 * k + 1] = bload16(rd, voff, (uint32_t)(k * 16 + 1) * 128);
+        if (FMT != MOE_W_INT4_ROW) P[k] = bload4(rt, toff, (uint32_t)(k * 8) * 32);
     }
     const int row = ob * 8 + rr;
     float sd = 1.f;
@@ -480,10 +479,10 @@ __global__ void __launch_bounds__(64 * D8_NE) k_dn8(Fwd f)
             const uint4* xv = hq + sp * 8;
             const uint4 d0 = D[2 * k], d1 = D[2 * k + 1];
             const uint32_t pv2 = P[k];
-            const uint32_t so = (uint32_t)((st0 + k + PD) * 16) * 1024;
+            const uint32_t so = (uint32_t)((st0 + k + PD) * 16) * 128;
             D[2 * k] = bload16(rd, voff, so);
-            D[2 * k + 1] = bload16(rd, voff, so + 1024);
-            if (FMT != MOE_W_INT4_ROW) P[k] = bload4(rt, toff, (uint32_t)((st0 + k + PD) * 8) * 256);
+            D[2 * k + 1] = bload16(rd, voff, so + 128);
+            if (FMT != MOE_W_INT4_ROW) P[k] = bload4(rt, toff, (uint32_t)((st0 + k + PD) * 8) * 32);
             float a = dot_chunk(d0, xv, mv, 0.f);
             a = dot_chunk(d1, xv + 4, mv, a);
             Yt = fold_span<FMT>(Yt, a, hs[sp], FMT == MOE_W_INT4_ROW ? 0u : pv2);

@@ -14,18 +14,19 @@ namespace moe {
 // ---------------------------------------------------------------------------
 // Slot layout (the library's own order of an expert's bytes in HBM).
 //
-// Every int4 matrix [O][In] is stored as 64-row blocks: block b, 16-byte
-// chunk c (32 consecutive inputs) of its 64 rows are 1 KiB contiguous,
-//   byte offset ((b * (In/32) + c) * 64 + lane) * 16  holds row 64b+lane,
-//   inputs 32c .. 32c+31.
-// A wavefront reading chunk c of block b therefore issues one fully
-// coalesced 1 KiB load (16 B per lane, lane = output row), and every lane
-// needs the same 32 activations, which arrive as scalar (SGPR) operands.
+// Every int4 matrix [O][In] is stored as 8-row groups: group q, 16-byte
+// chunk c (32 consecutive inputs) of its 8 rows are 128 bytes contiguous,
+//   byte offset ((q * (In/32) + c) * 8 + r) * 16  holds row 8q+r,
+//   inputs 32c .. 32c+31,
+// so a group's codes are one run of In/2 * 8 bytes and a 64-row block (8
+// groups) is In/2 * 64 bytes.  A workgroup that owns 8 rows over all inputs
+// (the one-token kernels) reads one contiguous run per matrix; a wavefront
+// whose lanes are 64 rows of a block reads eight 128-byte runs per chunk.
 // Row format codes are stored offset-binary (code + 8, i.e. blob byte ^ 0x88)
 // so that unsigned byte conversion gives code + 8 directly.
 // Scales follow the three matrices: row format keeps fp32 sg[I] su[I] sd[H]
-// unchanged; affine format stores the (scale, min) bf16 pair of row 64b+lane,
-// group g at ((b * (In/64) + g) * 64 + lane) * 4.
+// unchanged; affine format stores the (scale, min) bf16 pair of row 8q+r,
+// group g at ((q * (In/64) + g) * 8 + r) * 4.
 // Sizes equal the blob sizes, so a slot is moe_expert_bytes() long.
 // ---------------------------------------------------------------------------
 

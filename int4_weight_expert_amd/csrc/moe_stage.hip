@@ -470,12 +470,12 @@ int moe_blob_to_image(int wfmt, int hidden, int inter, const void* blob, size_t 
     const uint8_t flip = wfmt == MOE_W_INT4_ROW ? 0x88 : 0x00;
     const int64_t mats[3][3] = {{0, I, H}, {gq, I, H}, {2 * gq, H, I}};  // offset, O, In
     for (const auto& m : mats) {
-        const int64_t C = m[2] / 32;
-        for (int64_t b = 0; b < m[1] / 64; ++b)
+        const int64_t C = m[2] / 32;  // 8-row groups, 128 bytes per chunk
+        for (int64_t q = 0; q < m[1] / 8; ++q)
             for (int64_t c = 0; c < C; ++c)
-                for (int64_t lane = 0; lane < 64; ++lane) {
-                    const uint8_t* s = src + m[0] + (b * 64 + lane) * (m[2] / 2) + c * 16;
-                    uint8_t* d = dst + m[0] + ((b * C + c) * 64 + lane) * 16;
+                for (int64_t r = 0; r < 8; ++r) {
+                    const uint8_t* s = src + m[0] + (q * 8 + r) * (m[2] / 2) + c * 16;
+                    uint8_t* d = dst + m[0] + ((q * C + c) * 8 + r) * 16;
                     for (int k = 0; k < 16; ++k) d[k] = s[k] ^ flip;
                 }
     }
@@ -486,11 +486,11 @@ int moe_blob_to_image(int wfmt, int hidden, int inter, const void* blob, size_t 
         const int64_t ga = I * (H / 64) * 4;
         const int64_t pm[3][3] = {{sb, I, H / 64}, {sb + ga, I, H / 64}, {sb + 2 * ga, H, I / 64}};
         for (const auto& m : pm)
-            for (int64_t b = 0; b < m[1] / 64; ++b)
+            for (int64_t q = 0; q < m[1] / 8; ++q)
                 for (int64_t g = 0; g < m[2]; ++g)
-                    for (int64_t lane = 0; lane < 64; ++lane)
-                        memcpy(dst + m[0] + ((b * m[2] + g) * 64 + lane) * 4,
-                               src + m[0] + ((b * 64 + lane) * m[2] + g) * 4, 4);
+                    for (int64_t r = 0; r < 8; ++r)
+                        memcpy(dst + m[0] + ((q * m[2] + g) * 8 + r) * 4,
+                               src + m[0] + ((q * 8 + r) * m[2] + g) * 4, 4);
     }
     return MOE_OK;
 }

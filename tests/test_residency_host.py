@@ -65,15 +65,15 @@ def test_sticky_plan_matches_rule_on_random_steps():
 
 
 def ref_image(fmt, H, I, blob):
-    """The slot order as documented: matrix [O][In/2] in 64-row blocks, block
-    b chunk c (16 bytes, 32 inputs) of row 64b+lane at ((b*In/32+c)*64+lane)*16,
+    """The slot order as documented: matrix [O][In/2] in 8-row groups, group
+    q chunk c (16 bytes, 32 inputs) of row 8q+r at ((q*In/32+c)*8+r)*16,
     row-format codes offset binary (byte ^ 0x88); row scales as they are;
-    affine (scale, min) pairs of (row, group) at ((b*In/64+g)*64+lane)*4."""
+    affine (scale, min) pairs of (row, group) at ((q*In/64+g)*8+r)*4."""
     out = np.empty_like(blob)
     gq, dq = I * H // 2, H * I // 2
     flip = 0x88 if fmt == ROW else 0
     for off, O, In in [(0, I, H), (gq, I, H), (2 * gq, H, I)]:
-        m = blob[off:off + O * In // 2].reshape(O // 64, 64, In // 32, 16)
+        m = blob[off:off + O * In // 2].reshape(O // 8, 8, In // 32, 16)
         out[off:off + O * In // 2] = (m.transpose(0, 2, 1, 3) ^ flip).reshape(-1)
     sb = 2 * gq + dq
     if fmt == ROW:
@@ -81,7 +81,7 @@ def ref_image(fmt, H, I, blob):
     else:
         ga = I * (H // 64) * 4
         for off, O, G in [(sb, I, H // 64), (sb + ga, I, H // 64), (sb + 2 * ga, H, I // 64)]:
-            m = blob[off:off + O * G * 4].reshape(O // 64, 64, G, 4)
+            m = blob[off:off + O * G * 4].reshape(O // 8, 8, G, 4)
             out[off:off + O * G * 4] = m.transpose(0, 2, 1, 3).reshape(-1)
     return out
 
