@@ -577,15 +577,17 @@ def stream_ceiling(torch, result, unit_bytes: int):
                          "nontemporal": bool(nt), "gbps": gbs, "median_ms": ms})
     best = max(rows, key=lambda r: r["gbps"])
     gbs_all, ms_all = run(total, best["blocks"], int(best["nontemporal"]), n=8, rotate=False)
-    # the one-token gate/up kernel's access pattern against contiguous reads,
-    # same workgroups and bytes (9 GLM experts' gate and up codes), rotated
-    # over 12 disjoint sets of 9 slots
+    # the one-token gate/up kernel's workgroups (8 rows each) reading 9 GLM
+    # experts' gate and up codes in 64-row blocks (a slot layout where their
+    # pieces interleave) and in 8-row groups (contiguous per workgroup, the
+    # slot layout used), rotated over 12 disjoint sets of 9 slots
     lib.hbm_probe_pattern.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_void_p, ctypes.c_uint32, ctypes.c_void_p]
     lib.hbm_probe_pattern.restype = ctypes.c_int
     exp_bytes, n_exp = 18915328, 9
     pat = {}
-    for pattern, name in ((0, "gateup_pattern"), (1, "contiguous")):
+    for pattern, name in ((0, "rows8_of_64row_blocks"), (2, "rows8_of_64row_blocks_xcd_order"),
+                          (1, "rows8_groups_contiguous")):
         evs = []
         for i in range(48):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -605,8 +607,9 @@ def stream_ceiling(torch, result, unit_bytes: int):
     result["extra"]["hbm_stream_probe"] = out
     log(f"[bench] streaming-read ceiling: {best['gbps']:.0f} GB/s for {unit} B reads "
         f"({best['blocks']} blocks, nt={best['nontemporal']}), {gbs_all:.0f} GB/s whole 2 GiB; "
-        f"gate/up access pattern {pat['gateup_pattern']['gbps']:.0f} GB/s, contiguous "
-        f"{pat['contiguous']['gbps']:.0f} GB/s")
+        f"8 rows of 64-row blocks {pat['rows8_of_64row_blocks']['gbps']:.0f} GB/s "
+        f"({pat['rows8_of_64row_blocks_xcd_order']['gbps']:.0f} XCD-grouped), 8-row groups (contiguous) "
+        f"{pat['rows8_groups_contiguous']['gbps']:.0f} GB/s")
     del buf, sink
     torch.cuda.empty_cache()
     return out["ceiling_gbps"]

@@ -1,7 +1,7 @@
 // hbm_probe.hip -- a plain streaming-read kernel that measures the HBM read
 // rate this part reaches, the ceiling the byte-bound MoE kernels are held
-// against, and a read of the one-token gate/up kernel's bytes in its own
-// access pattern beside a contiguous one.  Not part of the MoE path: a
+// against, and a read of the one-token gate/up kernel's bytes in the access
+// patterns of two slot layouts.  Not part of the MoE path: a
 // separate library (libhbm_probe.so) that only the benchmark loads.
 //
 // Each thread reads 16-byte pieces with a grid stride, eight loads in
@@ -43,16 +43,16 @@ __global__ void __launch_bounds__(kThreads) k_stream_read(const u32x4* __restric
     if (acc == never) sink[blockIdx.x] = acc;
 }
 
-// The one-token gate/up launch's bytes read in two access patterns by the
+// The one-token gate/up launch's bytes read in three access patterns by the
 // same workgroups (n_exp x 256 of 256 threads, 48 KB each as 12 16-byte
 // loads per lane, all in flight at once), with the GLM expert shape (gate and
-// up [2048][6144] int4 in the slot layout: 64-row blocks of 1 KiB chunks):
-// PATTERN 0 as that kernel reads them (a workgroup owns 8 rows: their 16-byte
-// pieces of every chunk, 128 bytes out of each 1 KiB, the other rows read by
-// other workgroups), PATTERN 1 each workgroup's 48 KB contiguous, PATTERN 2
-// as PATTERN 0 with that kernel's workgroup order (within each run of 64
-// workgroups the order is transposed, so that the 8 workgroups sharing a
-// 64-row block run on one XCD).
+// up [2048][6144] int4): PATTERN 0 as a workgroup that owns 8 rows reads them
+// from 64-row blocks of 1 KiB chunks (their 16-byte pieces of every chunk,
+// 128 bytes out of each 1 KiB, the other rows read by other workgroups),
+// PATTERN 2 the same in an order that puts the 8 workgroups sharing a 64-row
+// block on one XCD (within each run of 64 workgroups the order transposed),
+// PATTERN 1 each workgroup's 48 KB contiguous, as in the slot layout's 8-row
+// groups.
 constexpr int kPH = 6144, kPI = 2048, kPC = kPH / 32;
 
 template <int PATTERN>
@@ -109,9 +109,9 @@ int hbm_probe_read(const void* buf, size_t bytes, int blocks, int nt, uint32_t* 
 }
 
 // Reads n_exp GLM-shape experts' gate and up codes (exp_bytes apart from buf,
-// at least 12.6 MB each) in `pattern` 0 (the one-token gate/up kernel's), 1
-// (contiguous per workgroup) or 2 (0 in that kernel's workgroup order); sink
-// needs n_exp x 256 words.  Returns a
+// at least 12.6 MB each) in `pattern` 0 (8 rows' pieces of 64-row blocks),
+// 1 (contiguous per workgroup: the 8-row groups) or 2 (0 with the workgroups
+// sharing a block on one XCD); sink needs n_exp x 256 words.  Returns a
 // hipError_t value (0 = success).
 int hbm_probe_pattern(const void* buf, size_t exp_bytes, int n_exp, int pattern, uint32_t* sink,
                       uint32_t never, void* stream)
