@@ -686,12 +686,84 @@ __global__ void __launch_bounds__(R8_THREADS) k_router8(Fwd f)
 // reduced in LDS in wavefront order) and stores it (part[4 e]); workgroup 0
 // also forms the token's sum and sum of squares (tpart, and the RMSNorm
 // factor), workgroup e stages x spans e, e + E, ... as fp16 for the expert
-// kernels.  The selection (sigmoid, bias, top-K, weights) runs in the
-// one-token gate/up kernel, after this launch, instead of in a last
-// workgroup behind a cross-workgroup arrival.
+// kernels.  The selection (sigmoid, bias, top-K, weights) runs either in
+// the one-token gate/up kernel, after this launch (SEL false), or in the
+// router's last workgroup behind a cross-workgroup arrival (SEL).
 // ---------------------------------------------------------------------------
 
-template <int Q>  // float4 loads per lane and wavefront (H = 1024 Q)
+// The one-token selection in the router's last workgroup (sigmoid scoring,
+// one group, E <= 256): the same steps and arithmetic as the gate/up
+// kernel's selection, the logits and the token's statistics read
+// agent-coherent from the other workgroups; writes ids, weights, perm and
+// the routed groups' descriptors (missing experts flagged), so that the
+// gate/up kernel reads its expert's slot from its group.
+__device__ void router1_select(const Fwd& f)
+{
+    __shared__ unsigned long long s_key[256];
+    __shared__ unsigned long long s_cand[32];
+    __shared__ float s_sig[256];
+    __shared__ int s_slot[256];
+    __shared__ int s_ids[8];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, E = f.E, K = f.K, ns = f.n_shared;
+    const float l = tid < E ? ld_agent(&f.part[(size_t)tid * 4]) : 0.f;
+    const float bias = tid < E ? f.bias[tid] : 0.f;
+    const int slot = tid < E ? f.tbl[tid] : -1;
+    const float ss = ld_agent(&f.tpart[1]);
+    const float rs = f.residual ? 1.0f / sqrtf(ss / (float)f.H + f.eps) : 1.0f;
+    unsigned long long key = 0ull;
+    float sig = 0.f;
+    if (tid < E) {
+        sig = 1.0f / (1.0f + expf(-(l * rs)));
+        key = ((unsigned long long)ord_float(sig + bias) << 32) | (uint32_t)(0xFFFFu - tid);
+    }
+    s_key[tid] = key;
+    s_sig[tid] = sig;
+    s_slot[tid] = slot;
+    if (tid < 32) s_cand[tid] = 0ull;
+    __syncthreads();
+    {
+        const unsigned long long* kb = &s_key[w * 64];
+        const unsigned long long mine = kb[lane];
+        int rank = 0;
+#pragma unroll
+        for (int e = 0; e < 64; e += 2) {
+            const ulonglong2 kk = *(const ulonglong2*)&kb[e];
+            rank += (kk.x > mine) + (kk.y > mine);
+        }
+        if (rank < K) s_cand[w * K + rank] = mine;
+    }
+    __syncthreads();
+    if (tid < 4 * K) {
+        const unsigned long long mine = s_cand[tid];
+        int rank = 0;
+        for (int j = 0; j < 4 * K; ++j) rank += s_cand[j] > mine;
+        if (rank < K) s_ids[rank] = (int)(0xFFFFu - (uint32_t)(mine & 0xFFFFu));
+    }
+    __syncthreads();
+    if (tid < K) {
+        float sum = 0.f;
+        for (int k = 0; k < K; ++k) sum += s_sig[s_ids[k]];
+        const int ek = s_ids[tid], sk = s_slot[ek];
+        const float sg = s_sig[ek];
+        f.ids[tid] = ek;
+        f.wts[tid] = f.norm_topk ? f.routed_scale * (sg / (sum + 1e-20f)) : f.routed_scale * sg;
+        f.perm[tid] = tid;
+        Group g;
+        g.base = sk >= 0 ? f.pool + (size_t)sk * f.slot_bytes : nullptr;
+        g.cnt = 1;
+        g.off = tid;
+        g.kind = 0;
+        g.expert = ek;
+        f.groups[ns + tid] = g;
+        if (sk == -1) {  // missing (a remote expert, -2, is skipped quietly)
+            atomicOr(&f.status[0], (uint32_t)STATUS_NOT_RESIDENT);
+            const int code = f.layer * f.E + ek;
+            atomicOr(&f.status[1 + code / 32], 1u << (code % 32));
+        }
+    }
+}
+
+template <int Q, bool SEL>  // Q: float4 loads per lane and wavefront (H = 1024 Q)
 __global__ void __launch_bounds__(RT_THREADS) k_router1(Fwd f, const float* __restrict__ X)
 {
     constexpr int NW = RT_THREADS / 64;
@@ -767,10 +839,12 @@ __global__ void __launch_bounds__(RT_THREADS) k_router1(Fwd f, const float* __re
         g.expert = -1;
         f.groups[threadIdx.x] = g;
     }
-    if (e == 0 && threadIdx.x == 0) {
-        f.n_groups[0] = f.n_shared + f.K;
-        // the gate/up kernel publishes its selection anew
-        for (int i = 0; i < 8; ++i) f.sel_base[i] = 0ull;
+    if (e == 0 && threadIdx.x == 0) f.n_groups[0] = f.n_shared + f.K;
+    if (SEL) {
+        // the last workgroup to arrive selects (arrivals spread over 16
+        // counters on lines of their own, then one top counter)
+        if (!arrive_block_h(f.rt_cnt, gridDim.x)) return;
+        router1_select(f);
     }
 }
 
@@ -779,19 +853,25 @@ bool router1_ok(const Fwd& f)
     return f.T == 1 && f.wr_rows != nullptr && f.H % 1024 == 0 && f.H / 1024 <= 8;
 }
 
-hipError_t launch_router1(const Fwd& f, hipStream_t st)
+template <bool SEL>
+static hipError_t router1_go(const Fwd& f, hipStream_t st)
 {
     const dim3 grid((unsigned)f.E), block(RT_THREADS);
     switch (f.H / 1024) {
-    case 1: return launch_k(k_router1<1>, grid, block, 0, st, f, f.x);
-    case 2: return launch_k(k_router1<2>, grid, block, 0, st, f, f.x);
-    case 3: return launch_k(k_router1<3>, grid, block, 0, st, f, f.x);
-    case 4: return launch_k(k_router1<4>, grid, block, 0, st, f, f.x);
-    case 5: return launch_k(k_router1<5>, grid, block, 0, st, f, f.x);
-    case 6: return launch_k(k_router1<6>, grid, block, 0, st, f, f.x);
-    case 7: return launch_k(k_router1<7>, grid, block, 0, st, f, f.x);
-    default: return launch_k(k_router1<8>, grid, block, 0, st, f, f.x);
+    case 1: return launch_k(k_router1<1, SEL>, grid, block, 0, st, f, f.x);
+    case 2: return launch_k(k_router1<2, SEL>, grid, block, 0, st, f, f.x);
+    case 3: return launch_k(k_router1<3, SEL>, grid, block, 0, st, f, f.x);
+    case 4: return launch_k(k_router1<4, SEL>, grid, block, 0, st, f, f.x);
+    case 5: return launch_k(k_router1<5, SEL>, grid, block, 0, st, f, f.x);
+    case 6: return launch_k(k_router1<6, SEL>, grid, block, 0, st, f, f.x);
+    case 7: return launch_k(k_router1<7, SEL>, grid, block, 0, st, f, f.x);
+    default: return launch_k(k_router1<8, SEL>, grid, block, 0, st, f, f.x);
     }
+}
+
+hipError_t launch_router1(const Fwd& f, hipStream_t st)
+{
+    return f.sel_in_router ? router1_go<true>(f, st) : router1_go<false>(f, st);
 }
 
 // ---------------------------------------------------------------------------

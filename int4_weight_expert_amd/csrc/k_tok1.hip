@@ -185,8 +185,6 @@ __device__ void select1(const Fwd& f, Sel1& s)
 // taking H / W inputs in NST steps of 16 chunks, every load issued at once
 // ---------------------------------------------------------------------------
 
-constexpr int SEL_POLLS = 4096;  // polls (with a short sleep each) before selecting locally
-
 template <int FMT, int W, int NST, bool SEL>
 __global__ void __launch_bounds__(64 * W) k_gu8(Fwd f)
 {
@@ -199,82 +197,44 @@ __global__ void __launch_bounds__(64 * W) k_gu8(Fwd f)
     int t = 0, r;
     const uint8_t* base;
     if (SEL) {
-        // the router left raw logits.  Group ns + k is the expert of rank k.
-        // Small layers: every routed workgroup selects for itself.  Large
-        // layers (sel_leader): the first routed workgroup (group ns, row
-        // block 0; dispatched before the others) selects and publishes each
-        // rank's slot base with an agent-scope store of base | 1 (bases are
-        // 256-byte aligned; the router cleared the words to 0); the other
-        // routed workgroups poll their rank's word a bounded number of
-        // times and, if it has not come, select for themselves (same steps,
-        // same result), so no workgroup ever waits unboundedly.  The word
-        // carries everything a poller needs, so no ordering between stores
-        // is involved.  The first routed workgroup also writes the
-        // selection out for the later kernels.
+        // the router left raw logits (small layers; large ones select in the
+        // router's last workgroup and take the other branch).  Group ns + k
+        // is the expert of rank k; every routed workgroup selects for itself
+        // (same steps, same result), and the first (group ns, row group 0)
+        // also writes the selection out for the later kernels.
         const int ns = f.n_shared;
         if (gi < ns) {
             base = f.shared + (size_t)gi * f.shared_bytes;
             r = f.K + gi;
         } else {
             __shared__ Sel1 sel;
-            __shared__ int s_ok;
             __shared__ uint64_t s_base;
             const int k = gi - ns;
             r = k;
-            if (!f.sel_leader || (k == 0 && sb == 0)) {
-                // the leader (or, on small layers, every routed workgroup)
-                select1(f, sel);
-                if (k == 0 && sb == 0 && (int)threadIdx.x < f.K) {
-                    const int kk = threadIdx.x, ek = sel.ids[kk], sk = sel.slot[ek];
-                    const uint8_t* bk = sk >= 0 ? f.pool + (size_t)sk * f.slot_bytes : nullptr;
-                    f.ids[kk] = ek;
-                    f.wts[kk] = sel.wts[kk];
-                    f.perm[kk] = kk;
-                    Group g;
-                    g.base = bk;
-                    g.cnt = 1;
-                    g.off = kk;
-                    g.kind = 0;
-                    g.expert = ek;
-                    f.groups[ns + kk] = g;
-                    __hip_atomic_store(&f.sel_base[kk], (uint64_t)(uintptr_t)bk | 1ull, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                    if (sk == -1) {  // missing (a remote expert, -2, is skipped quietly)
-                        atomicOr(&f.status[0], (uint32_t)STATUS_NOT_RESIDENT);
-                        const int code = f.layer * f.E + ek;
-                        atomicOr(&f.status[1 + code / 32], 1u << (code % 32));
-                    }
-                }
-                if (threadIdx.x == 0) {
-                    const int slot = sel.slot[sel.ids[k]];
-                    s_base = (uint64_t)(uintptr_t)(slot >= 0 ? f.pool + (size_t)slot * f.slot_bytes
-                                                             : nullptr);
-                }
-                __syncthreads();
-            } else {
-                if (threadIdx.x == 0) {
-                    int ok = 0;
-                    uint64_t word = 0;
-                    for (int i = 0; i < SEL_POLLS; ++i) {
-                        word = __hip_atomic_load(&f.sel_base[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        if (word & 1ull) {
-                            ok = 1;
-                            break;
-                        }
-                        __builtin_amdgcn_s_sleep(8);
-                    }
-                    s_base = word & ~1ull;
-                    s_ok = ok;
-                }
-                __syncthreads();
-                if (!s_ok) {  // not published in time: select here
-                    select1(f, sel);
-                    const int slot = sel.slot[sel.ids[k]];
-                    if (threadIdx.x == 0)
-                        s_base = (uint64_t)(uintptr_t)(slot >= 0 ? f.pool + (size_t)slot * f.slot_bytes : nullptr);
-                    __syncthreads();
+            select1(f, sel);
+            if (k == 0 && sb == 0 && (int)threadIdx.x < f.K) {
+                const int kk = threadIdx.x, ek = sel.ids[kk], sk = sel.slot[ek];
+                f.ids[kk] = ek;
+                f.wts[kk] = sel.wts[kk];
+                f.perm[kk] = kk;
+                Group g;
+                g.base = sk >= 0 ? f.pool + (size_t)sk * f.slot_bytes : nullptr;
+                g.cnt = 1;
+                g.off = kk;
+                g.kind = 0;
+                g.expert = ek;
+                f.groups[ns + kk] = g;
+                if (sk == -1) {  // missing (a remote expert, -2, is skipped quietly)
+                    atomicOr(&f.status[0], (uint32_t)STATUS_NOT_RESIDENT);
+                    const int code = f.layer * f.E + ek;
+                    atomicOr(&f.status[1 + code / 32], 1u << (code % 32));
                 }
             }
+            if (threadIdx.x == 0) {
+                const int slot = sel.slot[sel.ids[k]];
+                s_base = (uint64_t)(uintptr_t)(slot >= 0 ? f.pool + (size_t)slot * f.slot_bytes : nullptr);
+            }
+            __syncthreads();
             base = (const uint8_t*)(uintptr_t)s_base;
         }
         base = (const uint8_t*)(uintptr_t)(((uint64_t)(uint32_t)uni((int)(uint32_t)(uintptr_t)base)) |
@@ -625,12 +585,11 @@ bool tok1_sel_ok(const Fwd& f)
            f.scoring == MOE_SCORE_SIGMOID && f.n_group == 1;
 }
 
-// The selection runs in the gate/up kernel: by its first routed workgroup,
-// published to the others, on large layers (where selecting in all 2,048
-// routed workgroups of the GLM shape would hold their loads back); by every
-// routed workgroup on small ones (at most 512 gate/up workgroups), where
-// waiting for the publication costs more.
-bool tok1_sel_leader(const Fwd& f) { return (f.n_shared + f.K) * (f.I / 8) > 512; }
+// Where the one-token selection runs: on large layers (more than 512
+// gate/up workgroups) in the router's last workgroup, behind an arrival;
+// on small ones in every routed gate/up workgroup (the arrival and the
+// extra launch tail would cost more than the redundant selections).
+bool tok1_sel_in_router(const Fwd& f) { return (f.n_shared + f.K) * (f.I / 8) > 512; }
 
 hipError_t launch_tok1_gateup(const Fwd& f, hipStream_t st)
 {

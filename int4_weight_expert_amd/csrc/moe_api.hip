@@ -219,7 +219,7 @@ Fwd make_fwd(moe_ctx* c, const float* x, float* out, int T, int layer, int resid
     f.n_tiles = c->n_tiles;
     f.counters = c->counters;
     f.dn_cnt = c->dn_cnt;
-    f.sel_base = c->sel_base;
+    f.rt_cnt = c->rt_cnt;
     f.n_group = g.n_group;
     f.scoring = g.scoring;
     f.topk_group = g.topk_group;
@@ -233,7 +233,7 @@ Fwd make_fwd(moe_ctx* c, const float* x, float* out, int T, int layer, int resid
 int run_router(moe_ctx* c, const Fwd& f)
 {
     hipError_t e;
-    if (f.sel_in_gateup) {  // logits only: the one-token gate/up kernel selects
+    if (f.sel_in_gateup || f.sel_in_router) {  // the one-token router (logits, or logits and selection)
         mark(c, "router_logits");
         return hip_rc(c, launch_router1(f, c->stream));
     }
@@ -320,8 +320,10 @@ int run_forward(moe_ctx* c, const float* x, int T, int layer, float* out, int re
     if (midt_ok(f)) return run_forward_midt(c, f);
     plan_gemv(c, f);
     if (c->tok1 && router1_ok(f) && tok1_sel_ok(f)) {
-        f.sel_in_gateup = 1;
-        f.sel_leader = tok1_sel_leader(f);
+        // the selection in the router's last workgroup (large layers) or in
+        // every routed gate/up workgroup (small ones)
+        if (tok1_sel_in_router(f)) f.sel_in_router = 1;
+        else f.sel_in_gateup = 1;
     }
     int rc = run_router(c, f);
     if (rc) return rc;
@@ -592,7 +594,7 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
     }
     rc = rc ? rc : dalloc(c, &c->counters, (1 + H / 64) * 4);
     rc = rc ? rc : dalloc(c, &c->dn_cnt, (size_t)(H / 64) * 256);
-    rc = rc ? rc : dalloc(c, &c->sel_base, 8 * 8);
+    rc = rc ? rc : dalloc(c, &c->rt_cnt, (size_t)17 * 256);
     c->status_words = 1 + (L * E + 31) / 32;
     rc = rc ? rc : dalloc(c, &c->status, c->status_words * 4);
     if (rc == MOE_OK) {
@@ -600,6 +602,7 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
         hipError_t e = hipMemcpy(c->tbl, c->tbl_host.data(), L * E * 4, hipMemcpyHostToDevice);
         if (e == hipSuccess) e = hipMemset(c->counters, 0, (1 + H / 64) * 4);
         if (e == hipSuccess) e = hipMemset(c->dn_cnt, 0, (size_t)(H / 64) * 256);
+        if (e == hipSuccess) e = hipMemset(c->rt_cnt, 0, (size_t)17 * 256);
         if (e == hipSuccess) e = hipMemset(c->status, 0, c->status_words * 4);
         if (e == hipSuccess) e = hipMemset(c->bias, 0, L * E * 4);
         if (e == hipSuccess) e = hipMemset(c->wr, 0, L * c->Epad * H * 4);

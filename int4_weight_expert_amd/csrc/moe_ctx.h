@@ -51,7 +51,7 @@ struct moe_ctx {
     int32_t* n_tiles = nullptr;
     uint32_t* counters = nullptr;
     uint32_t* dn_cnt = nullptr;  // [H/64][64]: one counter per 256-byte line
-    uint64_t* sel_base = nullptr;
+    uint32_t* rt_cnt = nullptr;  // [17][64]: the one-token router's arrival counters
     uint32_t* status = nullptr;
     size_t status_words = 0;
     int gemm_min_tokens = 64;

@@ -84,6 +84,7 @@ struct Fwd {
     float2* hsc;          // [rows][I/64]
     uint32_t* counters;   // [0]: router arrivals
     uint32_t* dn_cnt;     // one-token down GEMV: per 64-output block arrival counters, 256 bytes apart
+    uint32_t* rt_cnt;     // one-token router: 16 arrival sub-counters and a top counter, 256 bytes apart
     uint32_t* status;     // [0] flags, [1..] missing bitmap over layer*E+id
     int n_layers;
     int lds_max;          // device LDS bytes per workgroup
@@ -103,10 +104,8 @@ struct Fwd {
     float* hf;            // [K + n_shared][I] h in fp32 of the one-token kernels
     int h_f32;            // 1: the down GEMV stages its h slices from hf (one token)
     int sel_in_gateup;    // 1: the one-token gate/up kernel selects the experts itself
-    int sel_leader;       // 1: one gate/up workgroup selects and publishes to the others
+    int sel_in_router;    // 1: the one-token router's last workgroup selects
     int dn_fused;         // 1: the one-token down GEMV combines each output block in its last unit
-    uint64_t* sel_base;   // [8] slot base | 1 of each rank once the gate/up kernel's selection is
-                          // published (0 = not yet: cleared by the router)
     int2* tiles;          // [max tiles] (group index, first row) of each 128-row tile
     int32_t* n_tiles;     // [1]
 };
@@ -168,7 +167,7 @@ hipError_t launch_combine(const Fwd& f, hipStream_t st);
 bool tok1_ok(const Fwd& f);
 bool tok1_down_ok(const Fwd& f);
 bool tok1_sel_ok(const Fwd& f);
-bool tok1_sel_leader(const Fwd& f);
+bool tok1_sel_in_router(const Fwd& f);
 hipError_t launch_tok1_gateup(const Fwd& f, hipStream_t st);
 hipError_t launch_tok1_down(const Fwd& f, hipStream_t st);
 // few tokens (MIDT_MIN_T .. the grouped GEMM's threshold), row format,
