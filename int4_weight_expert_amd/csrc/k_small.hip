@@ -674,7 +674,7 @@ __global__ void __launch_bounds__(R8_THREADS) k_router8(Fwd f)
             __syncthreads();
         }
     }
-    if (!arrive_block(&f.counters[0], gridDim.x)) return;
+    if (!arrive_block_h(f.rt_cnt, gridDim.x)) return;
     if (tid >= RT_THREADS) return;  // the tail is written for RT_THREADS threads
     router_tail<NT>(f, bias_e, slot_e);
 }

@@ -84,7 +84,7 @@ struct Fwd {
     float2* hsc;          // [rows][I/64]
     uint32_t* counters;   // [0]: router arrivals
     uint32_t* dn_cnt;     // one-token down GEMV: per 64-output block arrival counters, 256 bytes apart
-    uint32_t* rt_cnt;     // one-token router: 16 arrival sub-counters and a top counter, 256 bytes apart
+    uint32_t* rt_cnt;     // one- and few-token routers: 16 arrival sub-counters and a top counter, 256 bytes apart
     uint32_t* status;     // [0] flags, [1..] missing bitmap over layer*E+id
     int n_layers;
     int lds_max;          // device LDS bytes per workgroup
