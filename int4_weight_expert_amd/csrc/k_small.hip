@@ -145,30 +145,40 @@ __device__ void router_tail(const Fwd& f, float bias_e, int slot_e)
         // workgroup) and, for thread t < T, token t's statistics; every
         // thread loads (indices clamped), so that no branch separates them
         const float* lg = part_logits(f);
-        const int ec = min(tid, Epad - 1), tc = min(tid, T - 1);
-        float lv[NT], st[64];
+        const int ec = min(tid, Epad - 1);
+        float lv[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) lv[t] = ld_agent(&lg[(size_t)min(t, T - 1) * Epad + ec]);
-        load64(rt, (uint32_t)tc * S2p * 4, 0, min(2 * S, 64), st);
+        // token ts = tid / 32 (T <= 8): its 32 threads each sum every 32nd
+        // slice's (sum, sum of squares), all loads of a round of 4 slices in
+        // flight, then a fixed butterfly over the 32
+        const int ts = tid >> 5, sub = tid & 31, tsc = min(ts, T - 1);
+        const float* tp = f.tpart + (size_t)tsc * S2p;
         float sum = 0.f, ss = 0.f;
+        for (int i0 = 0; i0 < S; i0 += 128) {
+            float2 v[4];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            sum += st[2 * i];
-            ss += st[2 * i + 1];
-        }
-        for (int c0 = 64; c0 < 2 * S; c0 += 64) {  // H > 8192
-            load64(rt, (uint32_t)tc * S2p * 4, c0, 2 * S - c0, st);
-#pragma unroll
-            for (int i = 0; i < 32; ++i) {
-                sum += st[2 * i];
-                ss += st[2 * i + 1];
+            for (int q = 0; q < 4; ++q) {
+                const int i = min(i0 + sub + 32 * q, S - 1);
+                v[q] = make_float2(ld_agent(&tp[2 * i]), ld_agent(&tp[2 * i + 1]));
             }
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (i0 + sub + 32 * q < S) {
+                    sum += v[q].x;
+                    ss += v[q].y;
+                }
         }
-        if (tid < T) {
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) {
+            sum += __shfl_xor(sum, o);
+            ss += __shfl_xor(ss, o);
+        }
+        if (sub == 0 && ts < T) {
             const float rs = f.residual ? 1.0f / sqrtf(ss / (float)H + f.eps) : 1.0f;
-            f.tok[tid].xsum = sum;
-            f.tok[tid].rscale = rs;
-            s_rs[tid] = rs;
+            f.tok[ts].xsum = sum;
+            f.tok[ts].rscale = rs;
+            s_rs[ts] = rs;
             flag_range(f, ss);
         }
 #pragma unroll
@@ -397,11 +407,20 @@ __device__ void router_tail(const Fwd& f, float bias_e, int slot_e)
             }
         }
         __syncthreads();
-        for (int a = tid; a < n; a += RT_THREADS) {
-            const int e = s_ids[a];
-            int rank = 0;
-            for (int b2 = 0; b2 < a; ++b2) rank += s_ids[b2] == e;
-            f.perm[s_off[e] + rank] = a;
+        // each assignment's place in its group (n = T K <= 64: wavefront 0,
+        // the lanes holding the same id found with 8 ballots over its bits)
+        if (w == 0) {
+            const bool valid = lane < n;
+            const int e = valid ? s_ids[lane] : 0;
+            unsigned long long same = __ballot(valid);
+#pragma unroll
+            for (int bit = 0; bit < 8; ++bit) {
+                const bool on = (e >> bit) & 1;
+                const unsigned long long bb = __ballot(on);
+                same &= on ? bb : ~bb;
+            }
+            const unsigned long long below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+            if (valid) f.perm[s_off[e] + __popcll(same & below)] = lane;
         }
         if (tid < E) {
             cnt_e = s_cnt[tid];
