@@ -706,8 +706,10 @@ __global__ void __launch_bounds__(R8_THREADS) k_router8(Fwd f)
 // also forms the token's sum and sum of squares (tpart, and the RMSNorm
 // factor), workgroup e stages x spans e, e + E, ... as fp16 for the expert
 // kernels.  The selection (sigmoid, bias, top-K, weights) runs either in
-// the one-token gate/up kernel, after this launch (SEL false), or in the
-// router's last workgroup behind a cross-workgroup arrival (SEL).
+// the one-token gate/up kernel, after this launch (SEL 0), or in the
+// router's last workgroup behind a cross-workgroup arrival: the plain
+// sigmoid top-K (SEL 1, router1_select) or the general tail with softmax
+// scoring and group-limited selection (SEL 2, router_tail with one slice).
 // ---------------------------------------------------------------------------
 
 // The one-token selection in the router's last workgroup (sigmoid scoring,
@@ -782,7 +784,7 @@ __device__ void router1_select(const Fwd& f)
     }
 }
 
-template <int Q, bool SEL>  // Q: float4 loads per lane and wavefront (H = 1024 Q)
+template <int Q, int SEL>  // Q: float4 loads per lane and wavefront (H = 1024 Q)
 __global__ void __launch_bounds__(RT_THREADS) k_router1(Fwd f, const float* __restrict__ X)
 {
     constexpr int NW = RT_THREADS / 64;
@@ -862,8 +864,12 @@ __global__ void __launch_bounds__(RT_THREADS) k_router1(Fwd f, const float* __re
     if (SEL) {
         // the last workgroup to arrive selects (arrivals spread over 16
         // counters on lines of their own, then one top counter)
+        const int tid = threadIdx.x;
+        const float bias_e = SEL == 2 && tid < f.E ? f.bias[tid] : 0.f;
+        const int slot_e = SEL == 2 && tid < f.E ? f.tbl[tid] : -1;
         if (!arrive_block_h(f.rt_cnt, gridDim.x)) return;
-        router1_select(f);
+        if (SEL == 1) router1_select(f);
+        else router_tail<1>(f, bias_e, slot_e);  // f.S = 1: one partial per expert (part[4 e])
     }
 }
 
@@ -872,7 +878,7 @@ bool router1_ok(const Fwd& f)
     return f.T == 1 && f.wr_rows != nullptr && f.H % 1024 == 0 && f.H / 1024 <= 8;
 }
 
-template <bool SEL>
+template <int SEL>
 static hipError_t router1_go(const Fwd& f, hipStream_t st)
 {
     const dim3 grid((unsigned)f.E), block(RT_THREADS);
@@ -890,7 +896,8 @@ static hipError_t router1_go(const Fwd& f, hipStream_t st)
 
 hipError_t launch_router1(const Fwd& f, hipStream_t st)
 {
-    return f.sel_in_router ? router1_go<true>(f, st) : router1_go<false>(f, st);
+    return f.sel_in_router == 2 ? router1_go<2>(f, st)
+                                : f.sel_in_router ? router1_go<1>(f, st) : router1_go<0>(f, st);
 }
 
 // ---------------------------------------------------------------------------

@@ -324,6 +324,12 @@ int run_forward(moe_ctx* c, const float* x, int T, int layer, float* out, int re
         // every routed gate/up workgroup (small ones)
         if (tok1_sel_in_router(f)) f.sel_in_router = 1;
         else f.sel_in_gateup = 1;
+    } else if (c->tok1 && router1_ok(f) && tok1_ok(f) && f.E <= 256) {
+        // softmax scoring or group-limited selection: the general router
+        // tail in the one-token router's last workgroup, its logits one
+        // partial per expert
+        f.sel_in_router = 2;
+        f.S = 1;
     }
     int rc = run_router(c, f);
     if (rc) return rc;

@@ -104,7 +104,7 @@ struct Fwd {
     float* hf;            // [K + n_shared][I] h in fp32 of the one-token kernels
     int h_f32;            // 1: the down GEMV stages its h slices from hf (one token)
     int sel_in_gateup;    // 1: the one-token gate/up kernel selects the experts itself
-    int sel_in_router;    // 1: the one-token router's last workgroup selects
+    int sel_in_router;    // the one-token router's last workgroup selects: 1 plain sigmoid top-K, 2 the general tail
     int dn_fused;         // 1: the one-token down GEMV combines each output block in its last unit
     int2* tiles;          // [max tiles] (group index, first row) of each 128-row tile
     int32_t* n_tiles;     // [1]
