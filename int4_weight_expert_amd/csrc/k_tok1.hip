@@ -14,7 +14,7 @@
 // Work decomposition.  A workgroup owns 8 consecutive output rows of one
 // matrix and reduces them completely, so no k-slice partials and no
 // finalize or combine launch are needed; there are enough such workgroups
-// (GLM shape: 9 x 256 for gate/up, 768 for down, a few per CU) to spread
+// (GLM shape: 9 x 256 for gate/up, 9 x 192 for down, a few per CU) to spread
 // the stream over every CU evenly.  The 8 rows are one 8-row group of the
 // slot layout, whose codes are one contiguous run per matrix (128 bytes per
 // 32-input chunk), so a workgroup streams contiguous memory; a wavefront
@@ -30,6 +30,10 @@
 // rank order), each over all I inputs of its expert; the wavefront stages its
 // expert's h as fp16 spans in LDS first (power-of-two scale per span); the
 // slots are weighted and added in slot order (+ x for the residual form).
+// That suits small layers; on large ones each workgroup would read all
+// slots' h, so there the down workgroup is (expert group, 32 rows of H),
+// one wavefront per 8-row group over all I inputs with the group's h staged
+// once, and the last of a 64-row block's workgroups sums the slots.
 //
 // Roofline: HBM (the expert codes; the rest is a few hundred KB).
 #include <algorithm>
@@ -464,6 +468,116 @@ __global__ void __launch_bounds__(64 * D8_NE) k_dn8(Fwd f)
 }
 
 // ---------------------------------------------------------------------------
+// down + combine, one token, large layers: workgroup (expert group gi, 8W
+// rows of H), wave v the 8-row group of its rows over all I inputs (NST steps
+// of 16 chunks, every load issued at once, one contiguous run of the slot
+// layout per wave and 8W * I/2 bytes per workgroup); the group's h is staged
+// once per workgroup as fp16 spans.  Each workgroup writes its rows' results;
+// the last of the 64-row block's workgroups to arrive sums them (shared
+// experts, then the routed ones in rank order) and writes the block's
+// outputs (+ x for the residual form).
+// ---------------------------------------------------------------------------
+
+template <int FMT, int W, int NST>
+__global__ void __launch_bounds__(64 * W) k_dnb(Fwd f)
+{
+    extern __shared__ uint4 lds4[];
+    const int lane = threadIdx.x & 63, w = uni((int)(threadIdx.x >> 6));
+    const int H = f.H, I = f.I, C = I / 32, NP = I / 64, NB = H / 64, PB = 8 / W;
+    // workgroup -> (part hb of 64-row block b, expert group gi)
+    const int hb = blockIdx.x % PB, b = (blockIdx.x / PB) % NB, gi = blockIdx.x / (PB * NB);
+    const int ng = uni(f.n_groups[0]);
+    if (gi >= ng) return;
+    const Group grp = uni_group(f.groups, gi);
+    int t = 0, r = 0;
+    tok_rows(f, f.perm, grp, 0, t, r);
+    const uint8_t* base = grp.base;
+    const uint8_t* anchor = (const uint8_t*)f.x;  // any valid address (empty resources)
+    const int sb = b * 8 + hb * W + w, rr = lane & 7, j = lane >> 3;
+    const __amdgpu_buffer_rsrc_t rd =
+        make_rsrc(base ? base + (size_t)I * H + (size_t)sb * C * 128 : anchor,
+                  base ? (uint32_t)C * 128 : 0u);
+    const uint32_t voff = (uint32_t)rr * 16 + (uint32_t)(2 * j) * 128;
+    const uint8_t* tab = base ? base + (size_t)3 * H * I / 2 : anchor;
+    const __amdgpu_buffer_rsrc_t rt =
+        make_rsrc(tab + (size_t)2 * I * (H / 64) * 4 + (size_t)sb * NP * 32,
+                  (FMT != MOE_W_INT4_ROW && base) ? (uint32_t)NP * 32 : 0u);
+    const uint32_t toff = (uint32_t)rr * 4 + (uint32_t)j * 32;
+    uint4 D[2 * NST];
+    uint32_t P[NST];
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+        D[2 * st] = bload16(rd, voff, (uint32_t)(st * 16) * 128);
+        D[2 * st + 1] = bload16(rd, voff, (uint32_t)(st * 16 + 1) * 128);
+        P[st] = FMT != MOE_W_INT4_ROW ? bload4(rt, toff, (uint32_t)(st * 8) * 32) : 0u;
+    }
+    const int row = sb * 8 + rr;
+    float sd = 1.f;
+    if (FMT == MOE_W_INT4_ROW && base != nullptr && lane < 8) sd = ((const float*)tab)[2 * I + row];
+
+    // the group's h as fp16 spans: thread g takes inputs 8g .. 8g+7, the 8
+    // threads of a span agree on its power-of-two scale and sum its values
+    uint4* hq = lds4;
+    float2* hs = (float2*)(hq + C * 4);
+    {
+        const float4* hr = (const float4*)(f.hf + (size_t)r * I);
+        const int n8 = I / 8;  // a multiple of 64: whole wavefronts in or out
+        for (int g = threadIdx.x; g - lane < n8; g += 64 * W) {
+            const float4 lo = hr[2 * g], hi = hr[2 * g + 1];
+            float mx = fmaxf(fmaxf(fmaxf(fabsf(lo.x), fabsf(lo.y)), fmaxf(fabsf(lo.z), fabsf(lo.w))),
+                             fmaxf(fmaxf(fabsf(hi.x), fabsf(hi.y)), fmaxf(fabsf(hi.z), fabsf(hi.w))));
+            mx = fmaxf(mx, __shfl_xor(mx, 1));
+            mx = fmaxf(mx, __shfl_xor(mx, 2));
+            mx = fmaxf(mx, __shfl_xor(mx, 4));
+            int ex;
+            frexpf(mx, &ex);
+            ex = max(ex, -100);
+            const float sc = ldexpf(1.0f, 14 - ex);
+            const _Float16 a0 = (_Float16)(lo.x * sc), a1 = (_Float16)(lo.y * sc);
+            const _Float16 a2 = (_Float16)(lo.z * sc), a3 = (_Float16)(lo.w * sc);
+            const _Float16 a4 = (_Float16)(hi.x * sc), a5 = (_Float16)(hi.y * sc);
+            const _Float16 a6 = (_Float16)(hi.z * sc), a7 = (_Float16)(hi.w * sc);
+            hq[g] = make_uint4(h2pack(a0, a4), h2pack(a1, a5), h2pack(a2, a6), h2pack(a3, a7));
+            float sum = (((float)a0 + (float)a1) + ((float)a2 + (float)a3)) +
+                        (((float)a4 + (float)a5) + ((float)a6 + (float)a7));
+            sum += __shfl_xor(sum, 1);
+            sum += __shfl_xor(sum, 2);
+            sum += __shfl_xor(sum, 4);
+            if ((g & 7) == 0) hs[g >> 3] = make_float2(ldexpf(1.0f, ex - 14), sum);
+        }
+    }
+    __syncthreads();
+    const uint32_t mv = magic_vgpr();
+    float Yt = 0.f;
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+        const int sp = st * 8 + j;
+        const uint4* xv = hq + sp * 8;
+        float a = dot_chunk(D[2 * st], xv, mv, 0.f);
+        a = dot_chunk(D[2 * st + 1], xv + 4, mv, a);
+        Yt = fold_span<FMT>(Yt, a, hs[sp], P[st]);
+    }
+    Yt = row_sum8(Yt);
+    if (lane < 8) st_agent(f.ypart + (size_t)r * H + row, base ? Yt * sd : 0.f);
+    if (!arrive_block(f.dn_cnt + (size_t)b * 64, (uint32_t)(ng * PB))) return;
+    if (w != 0) return;
+    // one token: routed rank k is h row k, shared expert s row K + s
+    const int K = f.K, ns = f.n_shared, d = b * 64 + lane;
+    float v[D8_NE];
+#pragma unroll
+    for (int e = 0; e < D8_NE; ++e) {
+        const int re = e < ns ? K + e : e - ns;
+        v[e] = e < ng ? ld_agent(f.ypart + (size_t)re * H + d) : 0.f;
+    }
+    float m = 0.f;
+#pragma unroll
+    for (int e = 0; e < D8_NE; ++e)
+        if (e < ng) m = e < ns ? m + v[e] : fmaf(f.wts[e - ns], v[e], m);
+    if (f.residual) m = f.x[d] + m;
+    f.out[d] = m;
+}
+
+// ---------------------------------------------------------------------------
 // launch
 // ---------------------------------------------------------------------------
 
@@ -544,6 +658,30 @@ hipError_t dn8_go(const Fwd& f, hipStream_t st)
     return launch_k(k_dn8<FMT, PD>, dim3((unsigned)(f.H / 8)), dim3(64 * ne), lds, st, f);
 }
 
+// waves per block-down workgroup (8 rows each; 8 / DNB_W workgroups per
+// 64-row block)
+constexpr int DNB_W = 4;
+
+size_t dnb_lds(int I) { return (size_t)(I / 8) * 16 + (size_t)(I / 64) * 8; }
+
+template <int FMT, int NST>
+hipError_t dnb_go(const Fwd& f, hipStream_t st)
+{
+    const unsigned wgs = (unsigned)((f.n_shared + f.K) * (f.H / 64) * (8 / DNB_W));
+    return launch_k(k_dnb<FMT, DNB_W, NST>, dim3(wgs), dim3(64 * DNB_W), dnb_lds(f.I), st, f);
+}
+
+template <int FMT>
+hipError_t dnb_fmt(const Fwd& f, hipStream_t st)
+{
+    switch (f.I / 512) {
+    case 1: return dnb_go<FMT, 1>(f, st);
+    case 2: return dnb_go<FMT, 2>(f, st);
+    case 3: return dnb_go<FMT, 3>(f, st);
+    default: return dnb_go<FMT, 4>(f, st);
+    }
+}
+
 template <int FMT>
 hipError_t dn8_fmt(const Fwd& f, hipStream_t st)
 {
@@ -576,6 +714,13 @@ bool tok1_down_ok(const Fwd& f)
            dn8_lds(f.I, ne) <= (size_t)f.lds_max;
 }
 
+// The block down + combine kernel: I up to 2048 (all of a wave's codes in
+// flight at once), at most 9 expert slots, the block arrival counters.
+bool tok1_dnb_ok(const Fwd& f)
+{
+    return tok1_ok(f) && f.I <= 2048 && f.n_shared + f.K <= D8_NE && f.dn_cnt != nullptr;
+}
+
 // The selection can move into the gate/up kernel (256-thread workgroups,
 // one thread per expert) for the plain sigmoid top-K.
 bool tok1_sel_ok(const Fwd& f)
@@ -595,6 +740,12 @@ hipError_t launch_tok1_gateup(const Fwd& f, hipStream_t st)
 {
     return f.fmt == MOE_W_INT4_ROW ? gu8_fmt<MOE_W_INT4_ROW>(f, st)
                                    : gu8_fmt<MOE_W_INT4_AFFINE_G64>(f, st);
+}
+
+hipError_t launch_tok1_down_blocks(const Fwd& f, hipStream_t st)
+{
+    return f.fmt == MOE_W_INT4_ROW ? dnb_fmt<MOE_W_INT4_ROW>(f, st)
+                                   : dnb_fmt<MOE_W_INT4_AFFINE_G64>(f, st);
 }
 
 hipError_t launch_tok1_down(const Fwd& f, hipStream_t st)

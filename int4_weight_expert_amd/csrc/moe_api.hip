@@ -348,6 +348,13 @@ int run_forward(moe_ctx* c, const float* x, int T, int layer, float* out, int re
             mark(c, nullptr);
             return MOE_OK;
         }
+        if (c->dn_fused && tok1_dnb_ok(f)) {
+            mark(c, "down_combine");
+            rc = hip_rc(c, launch_tok1_down_blocks(f, c->stream));
+            if (rc) return rc;
+            mark(c, nullptr);
+            return MOE_OK;
+        }
         f.h_f32 = 1;
         f.dn_fused = c->dn_fused;
         mark(c, f.dn_fused ? "down_combine" : "down_gemv");

@@ -170,6 +170,8 @@ bool tok1_sel_ok(const Fwd& f);
 bool tok1_sel_in_router(const Fwd& f);
 hipError_t launch_tok1_gateup(const Fwd& f, hipStream_t st);
 hipError_t launch_tok1_down(const Fwd& f, hipStream_t st);
+bool tok1_dnb_ok(const Fwd& f);
+hipError_t launch_tok1_down_blocks(const Fwd& f, hipStream_t st);
 // few tokens (MIDT_MIN_T .. the grouped GEMM's threshold), row format,
 // matrix cores; below MIDT_MIN_T the GEMVs (as fast at 8 tokens, measured)
 constexpr int MIDT_MIN_T = 9;
