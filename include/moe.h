@@ -62,6 +62,7 @@ typedef struct moe_ctx moe_ctx;
 #define MOE_E_UNSUPPORTED (-7)  /* configuration outside what the kernels do */
 #define MOE_E_RANGE (-8)        /* an input row was not finite (moe_status) */
 #define MOE_E_BUSY (-9)         /* slot still named by the slot table (asynchronous loads) */
+#define MOE_E_WAIT (-10)        /* a kernel's bounded wait for other workgroups gave up (moe_status) */
 
 /* slot-table value of an expert held by another GPU (see moe_map_expert) */
 #define MOE_SLOT_REMOTE (-2)
@@ -335,7 +336,10 @@ int moe_route(moe_ctx *ctx, const float *x, int T, int layer, int32_t *ids, floa
  * no slot; up to cap missing (layer*E + id) codes go to missing_ids,
  * *n_missing = their count), MOE_E_RANGE (a row of x held a NaN or an
  * infinity, or values whose squares overflow fp32; those rows' outputs are
- * unspecified), or MOE_OK.  Clears the device status on the same stream.
+ * unspecified), MOE_E_WAIT (the one-token router's selecting workgroup gave
+ * up its bounded wait for the other workgroups' logits; that forward's
+ * output is unspecified; not expected in practice), or MOE_OK.  Clears the
+ * device status on the same stream.
  * missing_ids/n_missing may be null.  Errors: MOE_E_ARG, MOE_E_HIP. */
 int moe_status(moe_ctx *ctx, int32_t *missing_ids, int cap, int *n_missing);
 

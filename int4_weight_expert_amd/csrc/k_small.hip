@@ -706,19 +706,31 @@ __global__ void __launch_bounds__(R8_THREADS) k_router8(Fwd f)
 // also forms the token's sum and sum of squares (tpart, and the RMSNorm
 // factor), workgroup e stages x spans e, e + E, ... as fp16 for the expert
 // kernels.  The selection (sigmoid, bias, top-K, weights) runs either in
-// the one-token gate/up kernel, after this launch (SEL 0), or in the
-// router's last workgroup behind a cross-workgroup arrival: the plain
-// sigmoid top-K (SEL 1, router1_select) or the general tail with softmax
-// scoring and group-limited selection (SEL 2, router_tail with one slice).
+// the one-token gate/up kernel, after this launch (SEL 0), or in this
+// launch: the plain sigmoid top-K in workgroup 0 (SEL 1, router1_select),
+// which waits for the other workgroups' tagged logits, or the general tail
+// with softmax scoring and group-limited selection in the last workgroup to
+// arrive (SEL 2, router_tail with one slice).
 // ---------------------------------------------------------------------------
 
-// The one-token selection in the router's last workgroup (sigmoid scoring,
-// one group, E <= 256): the same steps and arithmetic as the gate/up
-// kernel's selection, the logits and the token's statistics read
-// agent-coherent from the other workgroups; writes ids, weights, perm and
-// the routed groups' descriptors (missing experts flagged), so that the
-// gate/up kernel reads its expert's slot from its group.
-__device__ void router1_select(const Fwd& f)
+// bounded wait of the selecting workgroup (polls of the tagged logits,
+// each after a short sleep): far beyond any launch's duration
+constexpr uint32_t RT_SPIN_MAX = 1u << 18;
+
+// The one-token selection in the router's workgroup 0 (sigmoid scoring, one
+// group, E <= 256): the same steps and arithmetic as the gate/up kernel's
+// selection.  Workgroup e stores expert e's logit with this call's tag in
+// one 64-bit word (rt_tag[e], a single store, agent scope); thread e here
+// polls word e until it carries the tag (the tag is one more than the last
+// selection's, rt_epoch, so a word from an earlier call never matches), up
+// to RT_SPIN_MAX rounds (then it flags STATUS_WAIT and goes on).  rs_lds
+// holds the token's RMSNorm factor, which this workgroup's thread 0 formed
+// (read after the polls' barriers).  Writes ids,
+// weights, perm and the routed groups' descriptors (missing experts
+// flagged), so that the gate/up kernel reads its expert's slot from its
+// group, and then the tag as the last selection's.  Every workgroup is
+// resident at once (one per expert, a few per CU), so the wait ends.
+__device__ void router1_select(const Fwd& f, uint32_t tag, const float* rs_lds)
 {
     __shared__ unsigned long long s_key[256];
     __shared__ unsigned long long s_cand[32];
@@ -726,11 +738,24 @@ __device__ void router1_select(const Fwd& f)
     __shared__ int s_slot[256];
     __shared__ int s_ids[8];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, E = f.E, K = f.K, ns = f.n_shared;
-    const float l = tid < E ? ld_agent(&f.part[(size_t)tid * 4]) : 0.f;
     const float bias = tid < E ? f.bias[tid] : 0.f;
     const int slot = tid < E ? f.tbl[tid] : -1;
-    const float ss = ld_agent(&f.tpart[1]);
-    const float rs = f.residual ? 1.0f / sqrtf(ss / (float)f.H + f.eps) : 1.0f;
+    uint64_t tv = 0;
+    int ok = tid >= E;
+    for (uint32_t n = 0;; ++n) {
+        if (!ok) {
+            tv = __hip_atomic_load(&f.rt_tag[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ok = (uint32_t)(tv >> 32) == tag;
+        }
+        if (__syncthreads_and(ok)) break;
+        if (n == RT_SPIN_MAX) {
+            if (tid == 0) atomicOr(&f.status[0], (uint32_t)STATUS_WAIT);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    const float l = tid < E ? __uint_as_float((uint32_t)tv) : 0.f;
+    const float rs = *rs_lds;
     unsigned long long key = 0ull;
     float sig = 0.f;
     if (tid < E) {
@@ -782,6 +807,7 @@ __device__ void router1_select(const Fwd& f)
             atomicOr(&f.status[1 + code / 32], 1u << (code % 32));
         }
     }
+    if (tid == 0) f.rt_epoch[0] = tag;
 }
 
 template <int Q, int SEL>  // Q: float4 loads per lane and wavefront (H = 1024 Q)
@@ -789,8 +815,11 @@ __global__ void __launch_bounds__(RT_THREADS) k_router1(Fwd f, const float* __re
 {
     constexpr int NW = RT_THREADS / 64;
     __shared__ float s_red[NW][3];
+    __shared__ float s_rs;
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int e = blockIdx.x, H = f.H;
+    // SEL 1: this call's tag for the logits
+    const uint32_t tag = SEL == 1 ? f.rt_epoch[0] + 1u : 0u;
     const float4* wr = (const float4*)(f.wr_rows + (size_t)e * H) + (size_t)w * (H / 16);
     const float4* x4 = (const float4*)X + (size_t)w * (H / 16);
     float4 a[Q], v[Q];
@@ -840,12 +869,18 @@ __global__ void __launch_bounds__(RT_THREADS) k_router1(Fwd f, const float* __re
             gs += s_red[v2][1];
             sq += s_red[v2][2];
         }
-        st_agent(&f.part[(size_t)e * 4], l);  // one slice per expert (row stride 4)
-        if (e == 0) {                         // one slice of token statistics
+        if (SEL == 1)
+            __hip_atomic_store(&f.rt_tag[e], ((uint64_t)tag << 32) | __float_as_uint(l),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+            st_agent(&f.part[(size_t)e * 4], l);  // one slice per expert (row stride 4)
+        if (e == 0) {                             // one slice of token statistics
             st_agent(&f.tpart[0], gs);
             st_agent(&f.tpart[1], sq);
+            const float rs = f.residual ? 1.0f / sqrtf(sq / (float)H + f.eps) : 1.0f;
             f.tok[0].xsum = gs;
-            f.tok[0].rscale = f.residual ? 1.0f / sqrtf(sq / (float)H + f.eps) : 1.0f;
+            f.tok[0].rscale = rs;
+            s_rs = rs;
             flag_range(f, sq);
         }
     }
@@ -861,15 +896,15 @@ __global__ void __launch_bounds__(RT_THREADS) k_router1(Fwd f, const float* __re
         f.groups[threadIdx.x] = g;
     }
     if (e == 0 && threadIdx.x == 0) f.n_groups[0] = f.n_shared + f.K;
-    if (SEL) {
+    if (SEL == 1 && e == 0) router1_select(f, tag, &s_rs);
+    if (SEL == 2) {
         // the last workgroup to arrive selects (arrivals spread over 16
         // counters on lines of their own, then one top counter)
         const int tid = threadIdx.x;
-        const float bias_e = SEL == 2 && tid < f.E ? f.bias[tid] : 0.f;
-        const int slot_e = SEL == 2 && tid < f.E ? f.tbl[tid] : -1;
+        const float bias_e = tid < f.E ? f.bias[tid] : 0.f;
+        const int slot_e = tid < f.E ? f.tbl[tid] : -1;
         if (!arrive_block_h(f.rt_cnt, gridDim.x)) return;
-        if (SEL == 1) router1_select(f);
-        else router_tail<1>(f, bias_e, slot_e);  // f.S = 1: one partial per expert (part[4 e])
+        router_tail<1>(f, bias_e, slot_e);  // f.S = 1: one partial per expert (part[4 e])
     }
 }
 

@@ -220,6 +220,8 @@ Fwd make_fwd(moe_ctx* c, const float* x, float* out, int T, int layer, int resid
     f.counters = c->counters;
     f.dn_cnt = c->dn_cnt;
     f.rt_cnt = c->rt_cnt;
+    f.rt_tag = c->rt_tag;
+    f.rt_epoch = c->rt_epoch;
     f.n_group = g.n_group;
     f.scoring = g.scoring;
     f.topk_group = g.topk_group;
@@ -608,6 +610,8 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
     rc = rc ? rc : dalloc(c, &c->counters, (1 + H / 64) * 4);
     rc = rc ? rc : dalloc(c, &c->dn_cnt, (size_t)(H / 64) * 256);
     rc = rc ? rc : dalloc(c, &c->rt_cnt, (size_t)17 * 256);
+    rc = rc ? rc : dalloc(c, &c->rt_tag, (size_t)256 * 8);
+    rc = rc ? rc : dalloc(c, &c->rt_epoch, 256);
     c->status_words = 1 + (L * E + 31) / 32;
     rc = rc ? rc : dalloc(c, &c->status, c->status_words * 4);
     if (rc == MOE_OK) {
@@ -616,6 +620,8 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
         if (e == hipSuccess) e = hipMemset(c->counters, 0, (1 + H / 64) * 4);
         if (e == hipSuccess) e = hipMemset(c->dn_cnt, 0, (size_t)(H / 64) * 256);
         if (e == hipSuccess) e = hipMemset(c->rt_cnt, 0, (size_t)17 * 256);
+        if (e == hipSuccess) e = hipMemset(c->rt_tag, 0, (size_t)256 * 8);
+        if (e == hipSuccess) e = hipMemset(c->rt_epoch, 0, 256);
         if (e == hipSuccess) e = hipMemset(c->status, 0, c->status_words * 4);
         if (e == hipSuccess) e = hipMemset(c->bias, 0, L * E * 4);
         if (e == hipSuccess) e = hipMemset(c->wr, 0, L * c->Epad * H * 4);
@@ -826,6 +832,7 @@ int moe_status(moe_ctx* c, int32_t* missing, int cap, int* n_missing)
                 ++n;
             }
     if (n_missing) *n_missing = n;
+    if (st[0] & STATUS_WAIT) return MOE_E_WAIT;
     if (st[0] & STATUS_NOT_RESIDENT) return MOE_E_NOT_RESIDENT;
     if (st[0] & STATUS_RANGE) return MOE_E_RANGE;
     return MOE_OK;

@@ -52,6 +52,8 @@ struct moe_ctx {
     uint32_t* counters = nullptr;
     uint32_t* dn_cnt = nullptr;  // [H/64][64]: one counter per 256-byte line
     uint32_t* rt_cnt = nullptr;  // [17][64]: the one-token router's arrival counters
+    uint64_t* rt_tag = nullptr;  // [256]: the one-token router's tagged logits
+    uint32_t* rt_epoch = nullptr;  // [1]: tag of its last selection
     uint32_t* status = nullptr;
     size_t status_words = 0;
     int gemm_min_tokens = 64;

@@ -85,6 +85,8 @@ struct Fwd {
     uint32_t* counters;   // [0]: router arrivals
     uint32_t* dn_cnt;     // one-token down GEMV: per 64-output block arrival counters, 256 bytes apart
     uint32_t* rt_cnt;     // one- and few-token routers: 16 arrival sub-counters and a top counter, 256 bytes apart
+    uint64_t* rt_tag;     // one-token router: per expert (call tag << 32) | logit bits [256]
+    uint32_t* rt_epoch;   // one-token router: tag of the last selection [1]
     uint32_t* status;     // [0] flags, [1..] missing bitmap over layer*E+id
     int n_layers;
     int lds_max;          // device LDS bytes per workgroup
@@ -110,7 +112,7 @@ struct Fwd {
     int32_t* n_tiles;     // [1]
 };
 
-enum { STATUS_NOT_RESIDENT = 1u, STATUS_RANGE = 2u };
+enum { STATUS_NOT_RESIDENT = 1u, STATUS_RANGE = 2u, STATUS_WAIT = 4u };
 
 // launchers (return hipError_t)
 hipError_t launch_requant_rows(const void* w, int src, const float* sinv, int64_t O, int64_t I,

@@ -23,6 +23,7 @@ MOE_E_HIP = -6
 MOE_E_UNSUPPORTED = -7
 MOE_E_RANGE = -8
 MOE_E_BUSY = -9
+MOE_E_WAIT = -10
 MOE_SLOT_REMOTE = -2
 MOE_W_INT4_ROW = 1
 MOE_SCORE_SIGMOID, MOE_SCORE_SOFTMAX = 0, 1
@@ -32,7 +33,8 @@ MOE_SRC_F32, MOE_SRC_BF16, MOE_SRC_FP8_E4M3 = 0, 1, 2
 
 ERROR_NAMES = {0: "MOE_OK", -1: "MOE_E_ARG", -2: "MOE_E_NOMEM", -3: "MOE_E_SIZE",
                -4: "MOE_E_SLOT", -5: "MOE_E_NOT_RESIDENT", -6: "MOE_E_HIP",
-               -7: "MOE_E_UNSUPPORTED", -8: "MOE_E_RANGE", -9: "MOE_E_BUSY"}
+               -7: "MOE_E_UNSUPPORTED", -8: "MOE_E_RANGE", -9: "MOE_E_BUSY",
+               -10: "MOE_E_WAIT"}
 
 EXPORTS = ["moe_layer_create", "moe_destroy", "moe_set_stream", "moe_expert_bytes",
            "moe_set_router", "moe_load_expert", "moe_pack_expert", "moe_set_shared",
