@@ -89,8 +89,12 @@ __device__ __forceinline__ void load64(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
     }
 }
 
-template <int NT>
-__device__ void router_tail(const Fwd& f, float bias_e, int slot_e)
+// PRE (one token): the expert's logit and the token's sum of squares come
+// from the caller (which also wrote the token's statistics) instead of the
+// partial buffers.
+template <int NT, bool PRE = false>
+__device__ void router_tail(const Fwd& f, float bias_e, int slot_e, float pre_l = 0.f,
+                            float pre_ss = 0.f)
 {
     __shared__ unsigned long long s_key[NT][256];
     __shared__ unsigned long long s_cand[NT][32];
@@ -114,7 +118,10 @@ __device__ void router_tail(const Fwd& f, float bias_e, int slot_e)
     for (int t = 0; t < NT; ++t) lsum[t] = 0.f;
     float rs0 = 1.f;
     // (the loads of a step are issued together, before any of them is used)
-    if (NT == 1) {
+    if (NT == 1 && PRE) {
+        lsum[0] = pre_l;
+        rs0 = f.residual ? 1.0f / sqrtf(pre_ss / (float)H + f.eps) : 1.0f;
+    } else if (NT == 1) {
         float a[64], st[64];
         load64(rp, (uint32_t)tid * Sp * 4, 0, S, a);  // S <= 64
         load64(rt, 0, 0, min(2 * S, 64), st);
@@ -707,10 +714,9 @@ __global__ void __launch_bounds__(R8_THREADS) k_router8(Fwd f)
 // factor), workgroup e stages x spans e, e + E, ... as fp16 for the expert
 // kernels.  The selection (sigmoid, bias, top-K, weights) runs either in
 // the one-token gate/up kernel, after this launch (SEL 0), or in this
-// launch: the plain sigmoid top-K in workgroup 0 (SEL 1, router1_select),
-// which waits for the other workgroups' tagged logits, or the general tail
-// with softmax scoring and group-limited selection in the last workgroup to
-// arrive (SEL 2, router_tail with one slice).
+// launch's workgroup 0, once the other workgroups' tagged logits are in:
+// the plain sigmoid top-K (SEL 1, router1_select) or the general tail with
+// softmax scoring and group-limited selection (SEL 2, router_tail).
 // ---------------------------------------------------------------------------
 
 // bounded wait of the selecting workgroup (polls of the tagged logits,
@@ -730,18 +736,13 @@ constexpr uint32_t RT_SPIN_MAX = 1u << 18;
 // flagged), so that the gate/up kernel reads its expert's slot from its
 // group, and then the tag as the last selection's.  Every workgroup is
 // resident at once (one per expert, a few per CU), so the wait ends.
-__device__ void router1_select(const Fwd& f, uint32_t tag, const float* rs_lds)
+// Thread e < E of workgroup 0: expert e's logit once its word carries the
+// tag (the polls end together: a barrier per round).
+__device__ float poll_logit(const Fwd& f, uint32_t tag)
 {
-    __shared__ unsigned long long s_key[256];
-    __shared__ unsigned long long s_cand[32];
-    __shared__ float s_sig[256];
-    __shared__ int s_slot[256];
-    __shared__ int s_ids[8];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, E = f.E, K = f.K, ns = f.n_shared;
-    const float bias = tid < E ? f.bias[tid] : 0.f;
-    const int slot = tid < E ? f.tbl[tid] : -1;
+    const int tid = threadIdx.x;
     uint64_t tv = 0;
-    int ok = tid >= E;
+    int ok = tid >= f.E;
     for (uint32_t n = 0;; ++n) {
         if (!ok) {
             tv = __hip_atomic_load(&f.rt_tag[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -754,7 +755,20 @@ __device__ void router1_select(const Fwd& f, uint32_t tag, const float* rs_lds)
         }
         __builtin_amdgcn_s_sleep(1);
     }
-    const float l = tid < E ? __uint_as_float((uint32_t)tv) : 0.f;
+    return tid < f.E ? __uint_as_float((uint32_t)tv) : 0.f;
+}
+
+__device__ void router1_select(const Fwd& f, uint32_t tag, const float* rs_lds)
+{
+    __shared__ unsigned long long s_key[256];
+    __shared__ unsigned long long s_cand[32];
+    __shared__ float s_sig[256];
+    __shared__ int s_slot[256];
+    __shared__ int s_ids[8];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, E = f.E, K = f.K, ns = f.n_shared;
+    const float bias = tid < E ? f.bias[tid] : 0.f;
+    const int slot = tid < E ? f.tbl[tid] : -1;
+    const float l = poll_logit(f, tag);
     const float rs = *rs_lds;
     unsigned long long key = 0ull;
     float sig = 0.f;
@@ -815,11 +829,11 @@ __global__ void __launch_bounds__(RT_THREADS) k_router1(Fwd f, const float* __re
 {
     constexpr int NW = RT_THREADS / 64;
     __shared__ float s_red[NW][3];
-    __shared__ float s_rs;
+    __shared__ float s_rs, s_ss;
     const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int e = blockIdx.x, H = f.H;
-    // SEL 1: this call's tag for the logits
-    const uint32_t tag = SEL == 1 ? f.rt_epoch[0] + 1u : 0u;
+    // SEL 1, 2: this call's tag for the logits
+    const uint32_t tag = SEL != 0 ? f.rt_epoch[0] + 1u : 0u;
     const float4* wr = (const float4*)(f.wr_rows + (size_t)e * H) + (size_t)w * (H / 16);
     const float4* x4 = (const float4*)X + (size_t)w * (H / 16);
     float4 a[Q], v[Q];
@@ -869,7 +883,7 @@ __global__ void __launch_bounds__(RT_THREADS) k_router1(Fwd f, const float* __re
             gs += s_red[v2][1];
             sq += s_red[v2][2];
         }
-        if (SEL == 1)
+        if (SEL != 0)
             __hip_atomic_store(&f.rt_tag[e], ((uint64_t)tag << 32) | __float_as_uint(l),
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         else
@@ -881,6 +895,7 @@ __global__ void __launch_bounds__(RT_THREADS) k_router1(Fwd f, const float* __re
             f.tok[0].xsum = gs;
             f.tok[0].rscale = rs;
             s_rs = rs;
+            s_ss = sq;
             flag_range(f, sq);
         }
     }
@@ -897,14 +912,14 @@ __global__ void __launch_bounds__(RT_THREADS) k_router1(Fwd f, const float* __re
     }
     if (e == 0 && threadIdx.x == 0) f.n_groups[0] = f.n_shared + f.K;
     if (SEL == 1 && e == 0) router1_select(f, tag, &s_rs);
-    if (SEL == 2) {
-        // the last workgroup to arrive selects (arrivals spread over 16
-        // counters on lines of their own, then one top counter)
+    if (SEL == 2 && e == 0) {
+        // the general tail in workgroup 0 once every tagged logit is in
         const int tid = threadIdx.x;
         const float bias_e = tid < f.E ? f.bias[tid] : 0.f;
         const int slot_e = tid < f.E ? f.tbl[tid] : -1;
-        if (!arrive_block_h(f.rt_cnt, gridDim.x)) return;
-        router_tail<1>(f, bias_e, slot_e);  // f.S = 1: one partial per expert (part[4 e])
+        const float l = poll_logit(f, tag);  // (s_ss: read after its barriers)
+        router_tail<1, true>(f, bias_e, slot_e, l, s_ss);
+        if (tid == 0) f.rt_epoch[0] = tag;
     }
 }
 
