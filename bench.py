@@ -629,7 +629,7 @@ def measured_traffic():
         return None
     if rec.get("k_tok1_sha256") != sha:
         return None
-    return rec.get("gateup_bytes_per_launch")
+    return rec.get("bytes_per_launch")
 
 
 def _oracle_rate(jobs, threads: int):
