@@ -416,10 +416,9 @@ __global__ void __launch_bounds__(64 * GW, 1) k_gemm(Fwd f)
     __shared__ float s_inv[GM], s_sum[GM], s_rs[GM];
 
     // Workgroup -> (tile, N tile), XCD-aware: workgroup p runs on XCD p % 8;
-    // tile i (the list is longest first) goes to XCD i % 8 with its N tiles
-    // innermost, so the workgroups sharing a tile's activations run together
-    // behind one L2 and every XCD gets an even share of the work, longest
-    // tiles first (little imbalance at the end of the launch).
+    // tile i goes to XCD i % 8 with its N tiles innermost, so the
+    // workgroups sharing a tile's activations run together behind one L2 and
+    // every XCD gets an even share of the list's mix of tiles.
     const int n_tiles = uni(f.n_tiles[0]);
     const int NT = gridDim.y;  // N tiles
     const int p = blockIdx.y * gridDim.x + blockIdx.x;
@@ -538,19 +537,34 @@ __device__ __forceinline__ int block_scan512(int v, int* s_w, int* total)
     return before + v;
 }
 
-// Tile list, longest first: every group's full 128-row tiles (groups in
+// Tile list.  Sorted first: every group's full 128-row tiles (groups in
 // order), then the partial tiles by descending number of occupied 32-row
-// blocks (groups in order within a class).  k_gemm runs tile i on XCD i mod 8,
-// so every XCD gets an even share of each class, longest first.
+// blocks (groups in order within a class).  Full tiles are matrix-core
+// heavy and read their codes once per 128 rows; partial tiles read the same
+// codes per tile for fewer rows, so a run of them asks more of HBM than it
+// can give while the full tiles leave it half idle.  The list therefore
+// spreads the full tiles evenly among the partial ones, except for the last
+// 32 tiles (one wave of workgroups at 8 N tiles each), which are the
+// smallest partial tiles, so that the launch still ends on short work.
+// k_gemm runs tile i on XCD i mod 8.
+constexpr int TILE_LIST_LDS = 2048;  // tiles reordered in LDS (beyond: sorted order)
+
 __global__ void __launch_bounds__(512) k_tiles(Fwd f)
 {
     __shared__ int s_w[8];
+    __shared__ int2 s_t[TILE_LIST_LDS];
     const int tid = threadIdx.x;
     const int ng = f.n_groups[0];
     int cnt = 0;
     if (tid < ng) cnt = f.groups[tid].cnt;
     const int nfull = cnt / GM, rem = cnt - nfull * GM;
     const int cls = rem ? (rem + 31) >> 5 : 0;  // occupied blocks of the partial tile
+    // the sorted list's length first, to know where it can be built
+    int nF, nPart;
+    block_scan512(nfull, s_w, &nF);
+    block_scan512(rem ? 1 : 0, s_w, &nPart);
+    const int L = nF + nPart;
+    int2* dst = L <= TILE_LIST_LDS ? s_t : f.tiles;
     int base = 0;
     // pass 0: full tiles; passes 1..4: partial tiles with 4, 3, 2, 1 blocks
     for (int pass = 0; pass < 5; ++pass) {
@@ -558,10 +572,24 @@ __global__ void __launch_bounds__(512) k_tiles(Fwd f)
         int total;
         const int excl = block_scan512(v, s_w, &total) - v;
         for (int i = 0; i < v; ++i)
-            f.tiles[base + excl + i] = make_int2(tid, pass == 0 ? i * GM : nfull * GM);
+            dst[base + excl + i] = make_int2(tid, pass == 0 ? i * GM : nfull * GM);
         base += total;
     }
     if (tid == 0) f.n_tiles[0] = base;
+    if (dst == f.tiles) return;
+    __syncthreads();
+    // position x < M holds full tile c if x = floor(c M / nF), else the next
+    // partial tile; positions from M on hold the last `tail` partial tiles
+    const int tail = min(nPart, 32), M = L - tail;
+    for (int x = tid; x < L; x += 512) {
+        int src = x;  // from M on (or with no full tiles): partial tile x - nF
+        if (x < M && nF > 0) {
+            const int c = (int)(((int64_t)x * nF + M - 1) / M);         // first full tile at or after x
+            const int cF = (int)(((int64_t)(x + 1) * nF + M - 1) / M);  // full tiles at positions <= x
+            src = (c < nF && (int)((int64_t)c * M / nF) == x) ? c : nF + (x - cF);
+        }
+        f.tiles[x] = s_t[src];
+    }
 }
 
 // ---------------------------------------------------------------------------

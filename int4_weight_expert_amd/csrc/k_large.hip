@@ -25,6 +25,20 @@ __device__ __forceinline__ uint32_t ordf(float c)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The large-T router's power of two for a token's x: 2^k with sqrt(ss) 2^k
+// in [2^11, 2^12), so every scaled |x| stays below 2^12 (1 when ss is 0 or
+// not finite).
+__device__ __forceinline__ float router_xscale(float ss)
+{
+    const float u = sqrtf(ss);
+    if (!(u > 0.f && u <= 3.402823466e38f)) return 1.f;
+    int ex = 0;
+    (void)frexpf(u, &ex);  // u in [2^(ex-1), 2^ex)
+    int k = 12 - ex;
+    k = k > 100 ? 100 : k < -100 ? -100 : k;
+    return ldexpf(1.f, k);
+}
+
 // Per-token sum and RMSNorm factor, and x staged for the grouped GEMM: the
 // whole row as fp16 with one power-of-two scale (largest magnitude in
 // [2^13, 2^14)), in pair order, and its sum; one wavefront per token.  H
@@ -42,6 +56,7 @@ __global__ void __launch_bounds__(256) k_tokstats(Fwd f)
     if (lane == 0) {
         f.tok[t].xsum = sum;
         f.tok[t].rscale = f.residual ? 1.0f / sqrtf(ss / (float)H + f.eps) : 1.0f;
+        f.tok[t].xscale = router_xscale(ss);
         flag_range(f, ss);
     }
 }
@@ -84,6 +99,7 @@ __device__ void stage_token_spans(const Fwd& f, int t)
         ss = (s_ts[0][1] + s_ts[1][1]) + (s_ts[2][1] + s_ts[3][1]);
         f.tok[t].xsum = sum;
         f.tok[t].rscale = f.residual ? 1.0f / sqrtf(ss / (float)H + f.eps) : 1.0f;
+        f.tok[t].xscale = router_xscale(ss);
         flag_range(f, ss);
     }
 }
@@ -91,96 +107,158 @@ __device__ void stage_token_spans(const Fwd& f, int t)
 // one workgroup per token
 __global__ void __launch_bounds__(256) k_tokspans(Fwd f) { stage_token_spans(f, blockIdx.x); }
 
-// Router logits for many tokens on the fp32 matrix cores
-// (v_mfma_f32_32x32x2_f32: fp32 products, fp32 accumulation).  Workgroup =
-// 64 tokens x every expert x one of rslices slices of the H inputs, so x is
-// read once and each router weight once per 64 tokens.  x goes through
-// LDS in chunks of 32 inputs (double-buffered, input-major so that the
-// operand reads are conflict-free); wavefront w takes experts 32w..32w+31
-// for both 32-token blocks, its router weights straight from memory.  Per
-// step of 8 inputs the lanes of the lower half take inputs k..k+3, the upper
-// half k+4..k+7, so MFMA step j pairs inputs k+j and k+4+j in both operands;
-// two accumulator pairs (even and odd steps) per token block.  Each slice's
-// partial logits go to a plane of their own; k_topk sums the planes in slice
-// order.
+// Router logits for many tokens on the fp16 matrix cores.  Each fp32
+// operand v is carried as two fp16 parts, hi = fp16(v) and lo = fp16(v - hi)
+// (22 significant bits together), after an exact power-of-two scale: x per
+// token (its statistics' xscale), the weights per expert (the split copy
+// made when the router is set).  A 32 x 32 x 16 step takes three products
+// into one fp32 accumulator, hi.hi, hi.lo and lo.hi (lo.lo, about 2^-22 of
+// the product, is left out); the partial logit is the sum times both
+// inverse scales.
+// Workgroup = 128 tokens x every expert x one of rslices slices of the H
+// inputs.  Workgroup p (on XCD p mod 8) takes slice p mod rslices, so with
+// 8 or more slices the workgroups of an XCD read only their own slices'
+// weights, which stay in that XCD's L2.  x goes through LDS already split
+// (double-buffered chunks of 32 inputs, token-minor so the operand reads are
+// conflict-free); wavefront w takes experts 32w..32w+31 for the four
+// 32-token blocks, its weight operands straight from the split copy.  x and the
+// weights are fetched four chunks ahead.  Each slice's partial logits go to a plane of their own; k_topk
+// sums the planes in slice order.
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+constexpr int RTILE = 128;  // tokens per workgroup of the large-T router
+typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
 
-__global__ void __launch_bounds__(512) k_router_mfma(Fwd f)
+template <int NW>
+__global__ void __launch_bounds__(64 * NW) k_router_h16(Fwd f)
 {
-    __shared__ float4 xs[2][8][64];  // [buffer][float4 of the chunk][token]
+    constexpr int TT = RTILE, TB = TT / 32;  // tokens per workgroup, 32-token blocks
+    // [buffer][step of 16 inputs][input half][token] of 4 fp16 pairs: hi, lo
+    __shared__ uint4 xh[2][2][2][TT], xl[2][2][2][TT];
+    __shared__ float s_xs[TT];
+    constexpr int NTHR = 64 * NW, NX = TT * 8;  // x float4 per chunk
+    constexpr int NR = (NX + NTHR - 1) / NTHR;  // ... per thread
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int nthr = blockDim.x;
-    const int H = f.H, T = f.T, Epad = f.Epad;
-    const int t0 = blockIdx.x * 64, slice = blockIdx.y;
+    const int H = f.H, T = f.T, Epad = f.Epad, R = f.rslices;
+    const int p = blockIdx.y * gridDim.x + blockIdx.x;
+    const int slice = p % R, t0 = (p / R) * TT;
     const int h = lane >> 5, m = lane & 31;
-    // expert e = 32w + m: interleaved block e / 64, lane e % 64
-    const float4* wb = (const float4*)f.wr + (size_t)(w >> 1) * (H / 4) * 64 + (w & 1) * 32 + m;
-    const int KC = H / f.rslices;  // inputs per slice, a multiple of 32
+    const int KC = H / R;  // inputs per slice, a multiple of 32
     const int kb = slice * KC, NCH = KC / 32;
-    // x loader: threads cover (token, float4) pairs of a chunk, 512 in all
-    auto load_x = [&](int ch, float4 (&v)[4]) {
+    // the lane's (hi, lo) operand pair of step s: wb[s * 128]
+    const uint4* wb = f.wr16 + ((size_t)w * (H / 16) + kb / 16) * 128 + lane * 2;
+    for (int i = tid; i < TT; i += NTHR) s_xs[i] = t0 + i < T ? f.tok[t0 + i].xscale : 1.f;
+    // x loader: pair i = tid + r NTHR -> token i >> 3, float4 i & 7 of the
+    // chunk; token and pair indices clamped (a padded token's row is read
+    // but its logits are not stored), so the loads carry no branch
+    const float4* xr[NR];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = tid + r * nthr;  // pair index
-            const int tok = i >> 3, j = i & 7;
-            v[r] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (i < 512 && t0 + tok < T)
-                v[r] = ((const float4*)(f.x + (size_t)(t0 + tok) * H + kb + ch * 32))[j];
-        }
-    };
-    auto store_x = [&](int buf, const float4 (&v)[4]) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = tid + r * nthr;
-            if (i < 512) xs[buf][i & 7][i >> 3] = v[r];
-        }
-    };
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) acc[b][0] = acc[b][1] = (f32x16){};
-    float4 xv[4];
-    load_x(0, xv);
-    store_x(0, xv);
-    // weights one chunk ahead in registers (the next chunk's index clamped,
-    // so the loads carry no branch)
-    float4 bw[4];
-#pragma unroll
-    for (int st = 0; st < 4; ++st) bw[st] = wb[(size_t)((kb + st * 8) / 4 + h) * 64];
+    for (int r = 0; r < NR; ++r) {
+        const int i = min(tid + r * NTHR, NX - 1);
+        xr[r] = (const float4*)(f.x + (size_t)min(t0 + (i >> 3), T - 1) * H + kb) + (i & 7);
+    }
     __syncthreads();
-    for (int ch = 0; ch < NCH; ++ch) {
-        const int buf = ch & 1;
-        const int cn = min(ch + 1, NCH - 1);
-        if (ch + 1 < NCH) load_x(ch + 1, xv);
-        float4 bn[4];
+    auto load_x = [&](int ch, float4 (&v)[NR]) {
 #pragma unroll
-        for (int st = 0; st < 4; ++st) bn[st] = wb[(size_t)((kb + cn * 32 + st * 8) / 4 + h) * 64];
+        for (int r = 0; r < NR; ++r) v[r] = xr[r][ch * 8];
+    };
+    // inputs 4j..4j+3 of the chunk: step j >> 2, half (j >> 1) & 1, pairs
+    // 2 (j & 1) and 2 (j & 1) + 1 of that half's 8 inputs
+    auto store_x = [&](int buf, const float4 (&v)[NR]) {
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const float4 a0 = xs[buf][2 * st + h][m], a1 = xs[buf][2 * st + h][32 + m];
-            const float4 b = bw[st];
-            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.x, b.x, acc[0][0], 0, 0, 0);
-            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.x, b.x, acc[1][0], 0, 0, 0);
-            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.y, b.y, acc[0][1], 0, 0, 0);
-            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.y, b.y, acc[1][1], 0, 0, 0);
-            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.z, b.z, acc[0][0], 0, 0, 0);
-            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.z, b.z, acc[1][0], 0, 0, 0);
-            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0.w, b.w, acc[0][1], 0, 0, 0);
-            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1.w, b.w, acc[1][1], 0, 0, 0);
+        for (int r = 0; r < NR; ++r) {
+            const int i = tid + r * NTHR;
+            if (NR * NTHR == NX || i < NX) {
+                const int tok = i >> 3, j = i & 7;
+                const float sc = s_xs[tok];
+                const float a0 = v[r].x * sc, a1 = v[r].y * sc, a2 = v[r].z * sc, a3 = v[r].w * sc;
+                const _Float16 h0 = (_Float16)a0, h1 = (_Float16)a1, h2 = (_Float16)a2,
+                               h3 = (_Float16)a3;
+                const _Float16 l0 = (_Float16)(a0 - (float)h0), l1 = (_Float16)(a1 - (float)h1),
+                               l2 = (_Float16)(a2 - (float)h2), l3 = (_Float16)(a3 - (float)h3);
+                uint2* dh = (uint2*)&xh[buf][j >> 2][(j >> 1) & 1][tok] + (j & 1);
+                uint2* dl = (uint2*)&xl[buf][j >> 2][(j >> 1) & 1][tok] + (j & 1);
+                *dh = make_uint2(pack_h2(h0, h1), pack_h2(h2, h3));
+                *dl = make_uint2(pack_h2(l0, l1), pack_h2(l2, l3));
+            }
         }
-        if (ch + 1 < NCH) store_x(buf ^ 1, xv);
-        __syncthreads();
+    };
+    f32x16 acc[TB];
 #pragma unroll
-        for (int st = 0; st < 4; ++st) bw[st] = bn[st];
+    for (int b = 0; b < TB; ++b) acc[b] = (f32x16){};
+    // x and weights of chunks ch .. ch + RP - 1 in flight, in slot ch % RP
+    // (chunk indices clamped past the end, so the loads carry no branch)
+    constexpr int RP = 4;
+    float4 xv[RP][NR];
+    uint4 bw[RP][2][2];  // [slot][step][hi, lo]
+#pragma unroll
+    for (int k = 0; k < RP; ++k) {
+        const int c = min(k, NCH - 1);
+        load_x(c, xv[k]);
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            bw[k][st][0] = wb[(2 * c + st) * 128];
+            bw[k][st][1] = wb[(2 * c + st) * 128 + 1];
+        }
+    }
+    store_x(0, xv[0]);
+    load_x(min(RP, NCH - 1), xv[0]);
+    __syncthreads();
+#pragma unroll 1
+    for (int ch0 = 0; ch0 < NCH; ch0 += RP) {
+#pragma unroll
+        for (int k = 0; k < RP; ++k) {
+            const int ch = ch0 + k;
+            const int k1 = (k + 1) % RP;
+            // chunk ch + 1 into the other buffer (free since the last barrier),
+            // then its slot refetches chunk ch + 1 + RP
+            if (ch + 1 < NCH) store_x((ch + 1) & 1, xv[k1]);
+            load_x(min(ch + 1 + RP, NCH - 1), xv[k1]);
+            if (ch < NCH) {
+                const int buf = ch & 1;
+#pragma unroll
+                for (int st = 0; st < 2; ++st) {
+                    const h16x8 bh = __builtin_bit_cast(h16x8, bw[k][st][0]);
+                    const h16x8 bl = __builtin_bit_cast(h16x8, bw[k][st][1]);
+                    // hi.hi, then hi.lo, then lo.hi, each over the token
+                    // blocks (no accumulator is used twice in a row)
+#pragma unroll
+                    for (int tb = 0; tb < TB; ++tb) {
+                        const h16x8 ah = __builtin_bit_cast(h16x8, xh[buf][st][h][32 * tb + m]);
+                        acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bh, acc[tb], 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int tb = 0; tb < TB; ++tb) {
+                        const h16x8 ah = __builtin_bit_cast(h16x8, xh[buf][st][h][32 * tb + m]);
+                        acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, bl, acc[tb], 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int tb = 0; tb < TB; ++tb) {
+                        const h16x8 al = __builtin_bit_cast(h16x8, xl[buf][st][h][32 * tb + m]);
+                        acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, bh, acc[tb], 0, 0, 0);
+                    }
+                }
+            }
+            const int cn = min(ch + RP, NCH - 1);
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                bw[k][st][0] = wb[(2 * cn + st) * 128];
+                bw[k][st][1] = wb[(2 * cn + st) * 128 + 1];
+            }
+            __syncthreads();
+        }
     }
     // entry (reg j, lane l) of a 32 x 32 tile: token (j/4)*8 + (l/32)*4 + j%4,
     // expert l%32
+    const int e = 32 * w + m;
+    const float winv = f.wr16s[e].y;
     float* plane = f.logits + (size_t)slice * T * Epad;
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
+    for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            const int t = t0 + 32 * tb + (j >> 2) * 8 + h * 4 + (j & 3);
-            if (t < T) plane[(size_t)t * Epad + 32 * w + m] = acc[tb][0][j] + acc[tb][1][j];
+            const int tl = 32 * tb + (j >> 2) * 8 + h * 4 + (j & 3);
+            const int t = t0 + tl;
+            if (t < T) plane[(size_t)t * Epad + e] = acc[tb][j] * (winv / s_xs[tl]);
         }
 }
 
@@ -607,8 +685,17 @@ hipError_t launch_router_large(const Fwd& f, hipStream_t st, int stage)
         return launch_k(k_tokstats<16>, grid, block, 0, st, f);
     }
     case 1:
-        return launch_k(k_router_mfma, dim3((f.T + 63) / 64, (unsigned)f.rslices), dim3(64 * (f.Epad / 32)),
-                        0, st, f);
+        if (f.wr16 == nullptr || f.wr16s == nullptr) return hipErrorInvalidValue;
+    {
+        const dim3 grid((f.T + RTILE - 1) / RTILE, (unsigned)f.rslices), block(64 * (f.Epad / 32));
+        switch (f.Epad / 32) {
+        case 2: return launch_k(k_router_h16<2>, grid, block, 0, st, f);
+        case 4: return launch_k(k_router_h16<4>, grid, block, 0, st, f);
+        case 6: return launch_k(k_router_h16<6>, grid, block, 0, st, f);
+        case 8: return launch_k(k_router_h16<8>, grid, block, 0, st, f);
+        default: return hipErrorInvalidValue;
+        }
+    }
     case 2: return launch_k(k_topk, dim3((f.T + 3) / 4), dim3(256), 0, st, f);
     default:
         return launch_k(k_bucket, dim3(1), dim3(1024), 0, st, (const int32_t*)f.ids, f.T * f.K,
@@ -618,15 +705,14 @@ hipError_t launch_router_large(const Fwd& f, hipStream_t st, int stage)
 
 int router_slices(int T, int H)
 {
-    const int tiles = (T + 63) / 64;
+    const int tiles = (T + RTILE - 1) / RTILE;
     int s = ROUTER_SLICES;
-    while (s < ROUTER_SLICES_MAX && tiles * s < 256 && (H / 32) % (2 * s) == 0) s *= 2;
+    while (s < ROUTER_SLICES_MAX && tiles * 2 * s <= 256 && (H / 32) % (2 * s) == 0) s *= 2;
     return s;
 }
 
-// rslices * T: at most ROUTER_SLICES * T; with more slices the grid had
-// fewer than 256 workgroups before the last doubling, so rslices * T <
-// 64 * 512.
+// rslices * T: at most ROUTER_SLICES * T; with more slices the grid has at
+// most 256 workgroups of RTILE tokens, so rslices * T <= 128 * 256.
 size_t router_logit_rows(int Tmax)
 {
     return std::max<size_t>((size_t)ROUTER_SLICES * Tmax,

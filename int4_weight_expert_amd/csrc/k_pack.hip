@@ -433,6 +433,74 @@ __global__ void __launch_bounds__(256) k_router_layout(const float* __restrict__
     }
 }
 
+// Router W [E][H] -> the large-T router's split fp16 copy.  Each expert row
+// is scaled by 2^k (its largest magnitude then in [2^13, 2^14), exact) and
+// each scaled weight v is held as hi = fp16(v) and lo = fp16(v - hi), 22
+// significant bits together.  Layout [Epad/32][H/16][64][2] uint4: lane
+// l = 32 h + m of expert block b holds expert 32 b + m, inputs 16 s + 8 h ..
+// 16 s + 8 h + 7 in order, hi then lo (the B operands of a 32 x 32 x 16
+// fp16 matrix-core step).  Rows >= E are zero; s16[e] = (2^k, 2^-k).
+__global__ void __launch_bounds__(256) k_router_rowscale(const float* __restrict__ W, int E,
+                                                         int H, float2* __restrict__ s16)
+{
+    __shared__ float s_m[4];
+    const int e = blockIdx.x, tid = threadIdx.x;
+    float m = 0.f;
+    if (e < E)
+        for (int k = tid; k < H; k += 256) m = fmaxf(m, fabsf(W[(size_t)e * H + k]));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if ((tid & 63) == 0) s_m[tid >> 6] = m;
+    __syncthreads();
+    if (tid == 0) {
+        m = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+        int ex = 0;
+        int k = 0;
+        if (m > 0.f && m <= 3.402823466e38f) {
+            (void)frexpf(m, &ex);  // m in [2^(ex-1), 2^ex)
+            k = 14 - ex;
+            k = k > 100 ? 100 : k < -100 ? -100 : k;
+        }
+        s16[e] = make_float2(ldexpf(1.f, k), ldexpf(1.f, -k));
+    }
+}
+
+__global__ void __launch_bounds__(256) k_router_split(const float* __restrict__ W,
+                                                      const float2* __restrict__ s16,
+                                                      uint4* __restrict__ w16, int E, int Epad,
+                                                      int H)
+{
+    const int64_t S = H / 16;
+    const int64_t total = (int64_t)(Epad / 32) * S * 64;
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * 256) {
+        const int l = (int)(idx & 63);
+        const int64_t s = (idx >> 6) % S, b = (idx >> 6) / S;
+        const int64_t e = b * 32 + (l & 31);
+        uint32_t hi[4] = {0u, 0u, 0u, 0u}, lo[4] = {0u, 0u, 0u, 0u};
+        if (e < E) {
+            const float sc = s16[e].x;
+            const float* src = W + e * H + s * 16 + (l >> 5) * 8;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t hp = 0u, lp = 0u;
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const float v = src[2 * i + j] * sc;
+                    const _Float16 a = (_Float16)v;
+                    const _Float16 r = (_Float16)(v - (float)a);
+                    hp |= (uint32_t)__builtin_bit_cast(uint16_t, a) << (16 * j);
+                    lp |= (uint32_t)__builtin_bit_cast(uint16_t, r) << (16 * j);
+                }
+                hi[i] = hp;
+                lo[i] = lp;
+            }
+        }
+        w16[2 * idx] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        w16[2 * idx + 1] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    }
+}
+
 static unsigned grid_for(int64_t items, int64_t per_block)
 {
     int64_t g = (items + per_block - 1) / per_block;
@@ -639,6 +707,15 @@ hipError_t launch_router_to_internal(const float* W, float* wr, int E, int Epad,
 {
     hipLaunchKernelGGL(k_router_layout, dim3(grid_for((int64_t)Epad * (H / 4), 256)), dim3(256),
                        0, st, W, (float4*)wr, E, Epad, H);
+    return hipGetLastError();
+}
+
+hipError_t launch_router_split(const float* W, uint4* w16, float2* w16s, int E, int Epad, int H,
+                               hipStream_t st)
+{
+    hipLaunchKernelGGL(k_router_rowscale, dim3(Epad), dim3(256), 0, st, W, E, H, w16s);
+    hipLaunchKernelGGL(k_router_split, dim3(grid_for((int64_t)(Epad / 32) * (H / 16) * 64, 256)),
+                       dim3(256), 0, st, W, (const float2*)w16s, w16, E, Epad, H);
     return hipGetLastError();
 }
 

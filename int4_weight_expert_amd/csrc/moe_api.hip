@@ -184,6 +184,8 @@ Fwd make_fwd(moe_ctx* c, const float* x, float* out, int T, int layer, int resid
     f.layer = layer;
     f.wr = c->wr + (size_t)layer * c->Epad * g.hidden;
     f.wr_rows = c->wr_rows ? c->wr_rows + (size_t)layer * g.n_experts * g.hidden : nullptr;
+    f.wr16 = c->wr16 ? c->wr16 + (size_t)layer * c->Epad * g.hidden / 4 : nullptr;
+    f.wr16s = c->wr16s ? c->wr16s + (size_t)layer * c->Epad : nullptr;
     f.bias = c->bias + (size_t)layer * g.n_experts;
     f.tbl = c->tbl + (size_t)layer * g.n_experts;
     f.pool = c->pool;
@@ -565,6 +567,10 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
     rc = rc ? rc : dalloc(c, &c->pool, (size_t)g.n_slots * c->slot_bytes);
     rc = rc ? rc : dalloc(c, &c->wr, L * c->Epad * H * 4);
     rc = rc ? rc : dalloc(c, &c->wr_rows, L * E * H * 4);
+    if (Tm > ROUTER_SMALL_MAX_T) {  // the large-T router's split fp16 copy
+        rc = rc ? rc : dalloc(c, &c->wr16, L * c->Epad * H * 4);
+        rc = rc ? rc : dalloc(c, &c->wr16s, L * c->Epad * 8);
+    }
     rc = rc ? rc : dalloc(c, &c->bias, L * E * 4);
     rc = rc ? rc : dalloc(c, &c->tbl, L * E * 4);
     rc = rc ? rc : dalloc(c, &c->shared, L * g.n_shared * c->shared_bytes);
@@ -626,6 +632,8 @@ int moe_layer_create(const moe_config* cfg, void* stream, moe_ctx** out)
         if (e == hipSuccess) e = hipMemset(c->bias, 0, L * E * 4);
         if (e == hipSuccess) e = hipMemset(c->wr, 0, L * c->Epad * H * 4);
         if (e == hipSuccess) e = hipMemset(c->wr_rows, 0, L * E * H * 4);
+        if (e == hipSuccess && c->wr16) e = hipMemset(c->wr16, 0, L * c->Epad * H * 4);
+        if (e == hipSuccess && c->wr16s) e = hipMemset(c->wr16s, 0, L * c->Epad * 8);
         if (e == hipSuccess && g.n_shared) e = hipMemset(c->shared, 0, L * g.n_shared * c->shared_bytes);
         if (e == hipSuccess) e = hipDeviceSynchronize();
         if (e != hipSuccess) rc = MOE_E_HIP;
@@ -675,6 +683,10 @@ int moe_set_router(moe_ctx* c, int layer, const float* W, const float* bias)
     if (e == hipSuccess)
         e = hipMemcpyAsync(c->wr_rows + (size_t)layer * E * H, tmp, E * H * 4,
                            hipMemcpyDeviceToDevice, c->stream);
+    if (e == hipSuccess && c->wr16)
+        e = launch_router_split(tmp, c->wr16 + (size_t)layer * c->Epad * H / 4,
+                                c->wr16s + (size_t)layer * c->Epad, (int)E, c->Epad, (int)H,
+                                c->stream);
     if (e == hipSuccess)
         e = hipMemcpyAsync(c->bias + (size_t)layer * E, bias, E * 4, hipMemcpyDefault, c->stream);
     if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
@@ -696,6 +708,10 @@ int moe_set_router_noalloc(moe_ctx* c, int layer, const float* W, const float* b
     if (e == hipSuccess)
         e = hipMemcpyAsync(c->wr_rows + (size_t)layer * E * H, tmp, E * H * 4,
                            hipMemcpyDeviceToDevice, c->stream);
+    if (e == hipSuccess && c->wr16)
+        e = launch_router_split(tmp, c->wr16 + (size_t)layer * c->Epad * H / 4,
+                                c->wr16s + (size_t)layer * c->Epad, (int)E, c->Epad, (int)H,
+                                c->stream);
     if (e == hipSuccess)
         e = hipMemcpyAsync(c->bias + (size_t)layer * E, bias, E * 4, hipMemcpyDefault, c->stream);
     if (e == hipSuccess) e = hipStreamSynchronize(c->stream);

@@ -16,6 +16,8 @@ struct moe_ctx {
     uint8_t* pool = nullptr;
     float* wr = nullptr;
     float* wr_rows = nullptr;  // the router weights again, row-major [L][E][H]
+    uint4* wr16 = nullptr;     // and as split fp16 operands [L][Epad/32][H/16][64][2] (large T)
+    float2* wr16s = nullptr;   // [L][Epad] their per-expert scales
     float* bias = nullptr;
     int* tbl = nullptr;
     std::vector<int> tbl_host;

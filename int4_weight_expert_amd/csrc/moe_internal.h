@@ -41,6 +41,7 @@ struct Group {
 struct TokStat {
     float xsum;    // sum of x over the row (offset correction of int4 codes)
     float rscale;  // RMSNorm factor (1 when the forward does not normalise)
+    float xscale;  // 2^k with sqrt(sum of squares) * 2^k in [2^11, 2^12): the large-T router's x scale
 };
 
 // Launch-time description of one forward (all device pointers).
@@ -58,6 +59,8 @@ struct Fwd {
     int layer;
     const float* wr;      // router, interleaved [Epad/64][H/4][64] float4
     const float* wr_rows; // router, row-major [E][H] (the one-token router)
+    const uint4* wr16;    // router as split fp16 (hi, lo) operands [Epad/32][H/16][64][2] (large-T router)
+    const float2* wr16s;  // [Epad] per expert (2^k its weights were scaled by, 2^-k)
     const float* bias;    // [E]
     const int* tbl;       // [E] slot table row of this layer
     const uint8_t* pool;  // slot pool base
@@ -135,6 +138,8 @@ hipError_t launch_slot_to_blob(const uint8_t* slot, uint8_t* blob, int fmt, int 
                                hipStream_t st);
 hipError_t launch_router_to_internal(const float* W, float* wr, int E, int Epad, int H,
                                      hipStream_t st);
+hipError_t launch_router_split(const float* W, uint4* w16, float2* w16s, int E, int Epad, int H,
+                               hipStream_t st);
 hipError_t launch_bucket(const int32_t* ids, int T, int K, int E, int32_t* cnt, int32_t* off,
                          int32_t* perm, int32_t* active, int32_t* n_active, hipStream_t st);
 
