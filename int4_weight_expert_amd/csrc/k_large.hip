@@ -121,9 +121,9 @@ __global__ void __launch_bounds__(256) k_tokspans(Fwd f) { stage_token_spans(f, 
 // weights, which stay in that XCD's L2.  x goes through LDS already split
 // (double-buffered chunks of 32 inputs, token-minor so the operand reads are
 // conflict-free); wavefront w takes experts 32w..32w+31 for the four
-// 32-token blocks, its weight operands straight from the split copy.  x and the
-// weights are fetched four chunks ahead.  Each slice's partial logits go to a plane of their own; k_topk
-// sums the planes in slice order.
+// 32-token blocks, its weight operands straight from the split copy.  x and
+// the weights are fetched four chunks ahead.  Each slice's partial logits go
+// to a plane of their own; k_topk sums the planes in slice order.
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int RTILE = 128;  // tokens per workgroup of the large-T router
 typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
