@@ -758,7 +758,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--no-extra", action="store_true", help="only the decode workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-tokens", type=int, default=16)
+    ap.add_argument("--cpu-tokens", type=int, default=40)
     ap.add_argument("--no-probe", action="store_true", help="skip the streaming-read ceiling")
     ap.add_argument("--only", choices=["decode", "verify", "edge0", "edge0_k8", "prefill", "grouped",
                                        "softmax", "int8_shared", "requant", "staged",
